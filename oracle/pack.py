@@ -1,0 +1,112 @@
+"""Oracle: offline weight packing (smoothing, SVD split, residual quantization) and
+the LoRA fold.
+
+Test infrastructure: see the package docstring for who may import this.
+
+Sources:
+* weight side of smoothing, W_hat = diag(s) W: ch3chohch3.github.io "从 Smooth Quant
+  到 SVD Quant", section "Smooth Quant（W8A8）", first displayed equation;
+* SVD split W_hat = L1 L2 + R with L1 = U Sigma_r, L2 = V_r^T, rank 32 by default,
+  L1 [hidden x r], L2 [r x hidden], low-rank branch kept in 16 bit and only R
+  quantized to 4 bit: jeonghoonpark.com "SVDQuant" review, section 4.2, the bullet
+  list defining L1, L2, R and the decomposition equation; the same post on
+  ch3chohch3.github.io, section "量化方案", the truncation equation;
+* static artifacts (weight scales, smoothing factor, low-rank branch) fixed offline:
+  ch3chohch3.github.io post, section "量化方案", item 1;
+* LoRA adapters used without re-quantizing R: SVDQuant abstract (chatpaper.ai).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .numerics import bf16_to_f64, round_f64_to_bf16, bf16_value_to_bits
+from . import quant
+
+
+def smoothed_weight(W_bits: np.ndarray, s32: np.ndarray) -> np.ndarray:
+    """W_hat = diag(s) W in fp64 (a bf16 times an fp32 value is exact in fp64)."""
+    return np.asarray(s32, dtype=np.float64)[:, None] * bf16_to_f64(W_bits)
+
+
+def svd_split(W_hat: np.ndarray, rank: int):
+    """Truncated SVD split of the smoothed weight.
+
+    L1 = U_r Sigma_r (the page writes U Sigma_r; U_r, the first r columns, is the
+    reading), L2 = V_r^T.  Both factors are rounded to bf16 (RNE, one rounding from
+    fp64), and R absorbs that rounding: R = W_hat - L1b L2b in fp64, so
+    W_hat = L1b L2b + R holds with the stored factors.  Sigma goes entirely into L1.
+    The SVD is LAPACK's (numpy.linalg.svd), a library step.
+    Returns dict(L1, L2 unrounded; L1b, L2b bf16 values; R fp64; sigma).
+    """
+    U, S, Vt = np.linalg.svd(W_hat, full_matrices=False)
+    L1 = U[:, :rank] * S[:rank]
+    L2 = Vt[:rank, :]
+    L1b = round_f64_to_bf16(L1)
+    L2b = round_f64_to_bf16(L2)
+    R = W_hat - L1b @ L2b
+    return dict(L1=L1, L2=L2, L1b=L1b, L2b=L2b, R=R, sigma=S)
+
+
+def quantize_residual(R32: np.ndarray, fmt: str):
+    """Quantize R [K x N] per output column n, in groups along K.
+
+    Returns (codes [N][K], scales [K/G][N]): INT4 codes int8 with fp16 scale bits, or
+    E2M1 codes uint8 with E8M0 bytes.
+    """
+    Rt = np.ascontiguousarray(np.asarray(R32, dtype=np.float32).T)  # [N][K]
+    if fmt == "int4":
+        codes, sc = quant.quantize_int4(Rt, quant.INT4_GROUP)
+    elif fmt == "mxfp4":
+        codes, sc = quant.quantize_mxfp4(Rt, quant.FP4_GROUP)
+    else:
+        raise ValueError(fmt)
+    return codes, np.ascontiguousarray(sc.T)
+
+
+def pack_weights(W_bits: np.ndarray, act_absmax, alpha: float, rank: int, fmt: str):
+    """Offline pack of one layer: s, W_hat, SVD split, R quantization.
+
+    act_absmax None means no smoothing (s = 1).  Returns a dict with
+      s64, s32, inv_s32   smoothing factor (fp64, stored fp32, reciprocal fp32)
+      L1b [K][r], L2b [r][N] bf16 values (fp64), and their bit patterns L1_bits, L2_bits
+      R (fp64), R32 (fp32) the residual
+      codesW [N][K], qW [N][K/2] packed nibbles, sW [K/G][N] (fp16 bits or E8M0)
+      sigma   singular values of W_hat; L1, L2 unrounded factors
+    """
+    K, N = W_bits.shape
+    if act_absmax is None:
+        s64 = np.ones(K)
+        s32 = s64.astype(np.float32)
+        inv_s32 = s32.copy()
+    else:
+        w_absmax = quant.channel_absmax_rows(W_bits)
+        s64, s32, inv_s32 = quant.smoothing_factors(act_absmax, w_absmax, alpha)
+    W_hat = smoothed_weight(W_bits, s32)
+    sp = svd_split(W_hat, rank)
+    R32 = sp["R"].astype(np.float32)
+    codesW, sW = quantize_residual(R32, fmt)
+    return dict(
+        fmt=fmt, K=K, N=N, rank=rank, s64=s64, s32=s32, inv_s32=inv_s32, W_hat=W_hat,
+        L1=sp["L1"], L2=sp["L2"], L1b=sp["L1b"], L2b=sp["L2b"],
+        L1_bits=bf16_value_to_bits(sp["L1b"]), L2_bits=bf16_value_to_bits(sp["L2b"]),
+        R=sp["R"], R32=R32, sigma=sp["sigma"],
+        codesW=codesW, qW=quant.pack_nibbles(codesW), sW=sW,
+    )
+
+
+def fold_lora(packed: dict, A_bits: np.ndarray, B_bits: np.ndarray, scale: float = 1.0):
+    """Concatenate an off-the-shelf LoRA (X A B, acting on unsmoothed X) into the
+    low-rank branch, leaving the quantized residual untouched.
+
+    X A B = (X diag(s)^-1)(diag(s) A) B, so the smoothing factor is folded into A:
+    L1' = [L1b | bf16(scale * diag(s32) A)], L2' = [L2b ; B].  LoRA scale 1.0 unless
+    given (the pages fix none).
+    """
+    sA = round_f64_to_bf16(float(scale) * np.asarray(packed["s32"], dtype=np.float64)[:, None]
+                           * bf16_to_f64(A_bits))
+    L1n = np.concatenate([packed["L1b"], sA], axis=1)
+    L2n = np.concatenate([packed["L2b"], bf16_to_f64(B_bits)], axis=0)
+    out = dict(packed)
+    out.update(rank=L1n.shape[1], L1b=L1n, L2b=L2n, L1_bits=bf16_value_to_bits(L1n),
+               L2_bits=bf16_value_to_bits(L2n))
+    return out
