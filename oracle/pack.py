@@ -63,6 +63,13 @@ def quantize_residual(R32: np.ndarray, fmt: str):
     return codes, np.ascontiguousarray(sc.T)
 
 
+def pack_codes(codes: np.ndarray, fmt: str) -> np.ndarray:
+    """Nibble-pack 4-bit codes along the last axis (INT4 as sign-magnitude nibbles)."""
+    if fmt == "int4":
+        return quant.pack_nibbles(quant.int4_to_nibble(codes))
+    return quant.pack_nibbles(codes)
+
+
 def pack_weights(W_bits: np.ndarray, act_absmax, alpha: float, rank: int, fmt: str):
     """Offline pack of one layer: s, W_hat, SVD split, R quantization.
 
@@ -90,7 +97,7 @@ def pack_weights(W_bits: np.ndarray, act_absmax, alpha: float, rank: int, fmt: s
         L1=sp["L1"], L2=sp["L2"], L1b=sp["L1b"], L2b=sp["L2b"],
         L1_bits=bf16_value_to_bits(sp["L1b"]), L2_bits=bf16_value_to_bits(sp["L2b"]),
         R=sp["R"], R32=R32, sigma=sp["sigma"],
-        codesW=codesW, qW=quant.pack_nibbles(codesW), sW=sW,
+        codesW=codesW, qW=pack_codes(codesW, fmt), sW=sW,
     )
 
 

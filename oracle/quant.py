@@ -189,22 +189,32 @@ def dequant_mxfp4(codes: np.ndarray, e8m0: np.ndarray, G: int = FP4_GROUP) -> np
     return g.reshape(codes.shape)
 
 
-def pack_nibbles(codes: np.ndarray) -> np.ndarray:
-    """Two 4-bit codes per byte along the last axis: byte j = c[2j] | c[2j+1] << 4.
+def int4_to_nibble(q: np.ndarray) -> np.ndarray:
+    """INT4 code q in [-7, 7] -> 4-bit sign-magnitude nibble (bit 3 sign, bits 0-2 |q|).
 
-    INT4 codes are stored as their 4-bit two's complement (q & 0xF).
+    Reading: the pages fix no bit encoding.  Sign-magnitude is the layout E2M1 codes
+    already use (sign in bit 3), and zero is always 0x0.
     """
-    c = (np.asarray(codes).astype(np.int16) & 0xF).astype(np.uint8)
+    q = np.asarray(q).astype(np.int16)
+    return (((q < 0).astype(np.uint8) << 3) | np.abs(q).astype(np.uint8)).astype(np.uint8)
+
+
+def nibble_to_int4(n: np.ndarray) -> np.ndarray:
+    n = np.asarray(n, dtype=np.uint8)
+    mag = (n & 7).astype(np.int8)
+    return np.where(n & 8, -mag, mag).astype(np.int8)
+
+
+def pack_nibbles(nibbles: np.ndarray) -> np.ndarray:
+    """Two 4-bit codes per byte along the last axis: byte j = n[2j] | n[2j+1] << 4."""
+    c = (np.asarray(nibbles).astype(np.uint16) & 0xF).astype(np.uint8)
     return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
 
 
-def unpack_nibbles(packed: np.ndarray, signed: bool) -> np.ndarray:
+def unpack_nibbles(packed: np.ndarray) -> np.ndarray:
+    """Inverse of pack_nibbles: 4-bit codes (uint8, 0..15)."""
     p = np.asarray(packed, dtype=np.uint8)
-    lo = p & 0xF
-    hi = p >> 4
-    out = np.empty(p.shape[:-1] + (2 * p.shape[-1],), dtype=np.int16)
-    out[..., 0::2] = lo
-    out[..., 1::2] = hi
-    if signed:
-        out = np.where(out >= 8, out - 16, out)
-    return out.astype(np.int8 if signed else np.uint8)
+    out = np.empty(p.shape[:-1] + (2 * p.shape[-1],), dtype=np.uint8)
+    out[..., 0::2] = p & 0xF
+    out[..., 1::2] = p >> 4
+    return out

@@ -45,9 +45,14 @@ def test_int4_golden_cases():
         assert codes[0, : len(c["codes"])].tolist() == c["codes"], c["why"]
         assert not codes[0, len(c["codes"]):].any()
     nb = d["nibble_packing"]
-    assert quant.pack_nibbles(np.array(nb["codes"], dtype=np.int8)).tolist() == nb["bytes"]
-    back = quant.unpack_nibbles(np.array(nb["bytes"], dtype=np.uint8), signed=True)
+    nib = quant.int4_to_nibble(np.array(nb["codes"], dtype=np.int8))
+    assert quant.pack_nibbles(nib).tolist() == nb["bytes"]
+    back = quant.nibble_to_int4(quant.unpack_nibbles(np.array(nb["bytes"], dtype=np.uint8)))
     assert back.tolist() == nb["codes"]
+    # every code round-trips, and zero is never the negative-zero nibble
+    q = np.arange(-7, 8, dtype=np.int8)
+    assert np.array_equal(quant.nibble_to_int4(quant.int4_to_nibble(q)), q)
+    assert quant.int4_to_nibble(np.int8(0)) == 0
 
 
 def _check_int4_group_properties(vals32, codes, sbits):
