@@ -1,0 +1,162 @@
+// C ABI: argument validation, error reporting and kernel launches for the device
+// entry points declared in include/svdq.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/svdq.h"
+#include "internal.hpp"
+#include "kernels.hpp"
+
+namespace svdq {
+
+static thread_local std::string g_err;
+
+svdq_status fail(svdq_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+svdq_status ok() {
+  g_err.clear();
+  return SVDQ_OK;
+}
+
+static bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int group_of(int fmt) { return fmt == SVDQ_INT4_G64 ? 64 : 32; }
+
+svdq_status check_dims(int64_t K, int64_t N, int32_t fmt) {
+  if (fmt != SVDQ_INT4_G64 && fmt != SVDQ_MXFP4_G32)
+    return fail(SVDQ_EUNSUPPORTED, "unsupported format %d", (int)fmt);
+  if (K < 128 || K % 128 != 0) return fail(SVDQ_EINVAL, "K must be a positive multiple of 128 (got %lld)", (long long)K);
+  if (N < 1) return fail(SVDQ_EINVAL, "N must be >= 1 (got %lld)", (long long)N);
+  return SVDQ_OK;
+}
+
+static svdq_status check_layer(const svdq_layer* L, KernelLayer& kl) {
+  if (!L) return fail(SVDQ_EINVAL, "layer is NULL");
+  svdq_status st = check_dims(L->K, L->N, L->fmt);
+  if (st != SVDQ_OK) return st;
+  if (L->rank < 0 || L->rank > SVDQ_MAX_RANK)
+    return fail(SVDQ_EUNSUPPORTED, "rank must be in [0, %d] (got %d)", SVDQ_MAX_RANK, (int)L->rank);
+  if (!L->inv_s || !L->qW || !L->sW) return fail(SVDQ_EINVAL, "layer inv_s, qW and sW must be non-NULL");
+  if (L->rank > 0 && (!L->Ld_hi || !L->Ld_lo || !L->L2))
+    return fail(SVDQ_EINVAL, "layer Ld_hi, Ld_lo and L2 must be non-NULL when rank > 0");
+  if (!aligned(L->inv_s, 16) || !aligned(L->qW, 16) || (L->rank > 0 && (!aligned(L->Ld_hi, 16) || !aligned(L->Ld_lo, 16))))
+    return fail(SVDQ_EINVAL, "layer inv_s, qW, Ld_hi and Ld_lo must be 16-byte aligned");
+  if (L->rank > 0 && !aligned(L->L2, 2)) return fail(SVDQ_EINVAL, "layer L2 must be 2-byte aligned");
+  kl = KernelLayer{L->K, L->N, L->rank, L->fmt, L->inv_s, L->Ld_hi, L->Ld_lo, L->L2, L->qW, L->sW};
+  return SVDQ_OK;
+}
+
+static size_t rup(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct WsLayout {
+  size_t qx, sx, la, total;
+};
+static WsLayout ws_layout(const svdq_layer* L, int64_t M) {
+  WsLayout w;
+  w.qx = 0;
+  const size_t qb = rup((size_t)M * (size_t)(L->K / 2));
+  w.sx = qb;
+  const size_t sb = rup((size_t)(L->K / group_of(L->fmt)) * (size_t)M * (L->fmt == SVDQ_INT4_G64 ? 2 : 1));
+  w.la = w.sx + sb;
+  w.total = w.la + rup((size_t)M * (size_t)L->rank * 4);
+  return w;
+}
+
+}  // namespace svdq
+
+using namespace svdq;
+
+extern "C" {
+
+const char* svdq_last_error(void) { return g_err.c_str(); }
+
+size_t svdq_workspace_bytes(const svdq_layer* layer, int64_t M) {
+  if (!layer || M < 0 || layer->K < 0) return 0;
+  return ws_layout(layer, M).total;
+}
+
+svdq_status svdq_quantize_act_lora_down(const svdq_layer* layer, int64_t M, const uint16_t* X,
+                                        int64_t ldx, uint8_t* qX, void* sX, float* lora_act,
+                                        void* stream) {
+  KernelLayer kl;
+  svdq_status st = check_layer(layer, kl);
+  if (st != SVDQ_OK) return st;
+  if (M < 0) return fail(SVDQ_EINVAL, "M must be >= 0");
+  if (M == 0) return ok();
+  if (!X || !qX || !sX) return fail(SVDQ_EINVAL, "X, qX and sX must be non-NULL");
+  if (kl.rank > 0 && !lora_act) return fail(SVDQ_EINVAL, "lora_act must be non-NULL when rank > 0");
+  if (ldx < kl.K || ldx % 8 != 0) return fail(SVDQ_EINVAL, "ldx must be >= K and a multiple of 8");
+  if (!aligned(X, 16) || !aligned(qX, 16) || !aligned(sX, 2) || (lora_act && !aligned(lora_act, 4)))
+    return fail(SVDQ_EINVAL, "X and qX must be 16-byte aligned");
+  hipError_t e = launch_k1(kl, M, X, ldx, qX, sX, lora_act, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(SVDQ_EHIP, "kernel 1 launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+svdq_status svdq_gemm_w4a4_lora_up(const svdq_layer* layer, int64_t M, const uint8_t* qX,
+                                   const void* sX, const float* lora_act, void* Y, int64_t ldy,
+                                   int32_t ydtype, void* stream) {
+  KernelLayer kl;
+  svdq_status st = check_layer(layer, kl);
+  if (st != SVDQ_OK) return st;
+  if (M < 0) return fail(SVDQ_EINVAL, "M must be >= 0");
+  if (M == 0) return ok();
+  if (ydtype != SVDQ_F32 && ydtype != SVDQ_BF16) return fail(SVDQ_EUNSUPPORTED, "unsupported output dtype %d", (int)ydtype);
+  if (!qX || !sX || !Y) return fail(SVDQ_EINVAL, "qX, sX and Y must be non-NULL");
+  if (kl.rank > 0 && !lora_act) return fail(SVDQ_EINVAL, "lora_act must be non-NULL when rank > 0");
+  if (ldy < kl.N) return fail(SVDQ_EINVAL, "ldy must be >= N");
+  if (!aligned(qX, 16) || !aligned(Y, ydtype == SVDQ_F32 ? 4 : 2) || !aligned(sX, 2))
+    return fail(SVDQ_EINVAL, "qX must be 16-byte aligned and Y aligned to its element size");
+  hipError_t e = launch_k2(kl, M, qX, sX, lora_act, Y, ldy, ydtype, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(SVDQ_EHIP, "kernel 2 launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+svdq_status svdq_linear_forward(const svdq_layer* layer, int64_t M, const uint16_t* X, int64_t ldx,
+                                void* Y, int64_t ldy, int32_t ydtype, void* workspace,
+                                size_t ws_bytes, void* stream) {
+  KernelLayer kl;
+  svdq_status st = check_layer(layer, kl);
+  if (st != SVDQ_OK) return st;
+  if (M < 0) return fail(SVDQ_EINVAL, "M must be >= 0");
+  if (M == 0) return ok();
+  const WsLayout w = ws_layout(layer, M);
+  if (!workspace || ws_bytes < w.total) return fail(SVDQ_EINVAL, "workspace too small: need %zu bytes", w.total);
+  if (!aligned(workspace, 256)) return fail(SVDQ_EINVAL, "workspace must be 256-byte aligned");
+  uint8_t* base = static_cast<uint8_t*>(workspace);
+  uint8_t* qX = base + w.qx;
+  void* sX = base + w.sx;
+  float* la = kl.rank > 0 ? reinterpret_cast<float*>(base + w.la) : nullptr;
+  st = svdq_quantize_act_lora_down(layer, M, X, ldx, qX, sX, la, stream);
+  if (st != SVDQ_OK) return st;
+  return svdq_gemm_w4a4_lora_up(layer, M, qX, sX, la, Y, ldy, ydtype, stream);
+}
+
+svdq_status svdq_debug_group_sums(const svdq_layer* layer, int64_t M, const uint8_t* qX, int64_t m0,
+                                  int64_t n0, int64_t mt, int64_t nt, int32_t* out, void* stream) {
+  KernelLayer kl;
+  svdq_status st = check_layer(layer, kl);
+  if (st != SVDQ_OK) return st;
+  if (kl.fmt != SVDQ_INT4_G64) return fail(SVDQ_EUNSUPPORTED, "group sums are defined for INT4 only");
+  if (!qX || !out) return fail(SVDQ_EINVAL, "qX and out must be non-NULL");
+  if (m0 < 0 || n0 < 0 || mt < 1 || nt < 1 || m0 + mt > M || n0 + nt > kl.N)
+    return fail(SVDQ_EINVAL, "window out of range");
+  if (!aligned(qX, 16)) return fail(SVDQ_EINVAL, "qX must be 16-byte aligned");
+  hipError_t e = launch_k2_debug(kl, M, qX, m0, n0, mt, nt, out, (hipStream_t)stream);
+  if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess) return fail(SVDQ_EHIP, "group-sum kernel: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,17 @@
+// Internal helpers shared by the C ABI translation units (host code only).
+#pragma once
+#include <stdint.h>
+
+#include "../../include/svdq.h"
+
+namespace svdq {
+
+// Record a failure message (thread-local) and return st.
+svdq_status fail(svdq_status st, const char* fmt, ...);
+// Clear the message and return SVDQ_OK.
+svdq_status ok();
+// Validate K, N, fmt (K a positive multiple of 128, N >= 1, known format).
+svdq_status check_dims(int64_t K, int64_t N, int32_t fmt);
+int group_of(int fmt);
+
+}  // namespace svdq

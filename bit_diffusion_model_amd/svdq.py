@@ -1,0 +1,283 @@
+"""ctypes binding over libsvdq.so (include/svdq.h).
+
+Argument marshalling only: every step of the layer runs in the library (HIP kernels
+on the device, C++ on the host).  torch provides device memory and the current HIP
+stream; no torch op touches the data on the hot path.  If the library is missing the
+import fails loudly: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsvdq.so")
+
+INT4_G64, MXFP4_G32 = 0, 1
+F32, BF16 = 0, 1
+FMT = {"int4": INT4_G64, "mxfp4": MXFP4_G32}
+GROUP = {INT4_G64: 64, MXFP4_G32: 32}
+MAX_RANK = 128
+
+
+class SvdqError(RuntimeError):
+    pass
+
+
+class _Layer(ctypes.Structure):
+    _fields_ = [
+        ("K", ctypes.c_int64), ("N", ctypes.c_int64), ("rank", ctypes.c_int32), ("fmt", ctypes.c_int32),
+        ("inv_s", ctypes.c_void_p), ("Ld_hi", ctypes.c_void_p), ("Ld_lo", ctypes.c_void_p),
+        ("L2", ctypes.c_void_p), ("qW", ctypes.c_void_p), ("sW", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+EXPORTS = [
+    "svdq_last_error", "svdq_act_absmax", "svdq_weight_sizes", "svdq_pack_weights",
+    "svdq_quantize_weights", "svdq_concat_lora", "svdq_lowrank_down_factors",
+    "svdq_quantize_act_lora_down", "svdq_gemm_w4a4_lora_up", "svdq_workspace_bytes",
+    "svdq_linear_forward", "svdq_debug_group_sums",
+]
+
+
+def lib():
+    """Load libsvdq.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise SvdqError(f"{LIB_PATH} is missing: build it with bit_diffusion_model_amd.build.build()")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I64, I32, F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
+    sig = {
+        "svdq_last_error": (ctypes.c_char_p, []),
+        "svdq_act_absmax": (I32, [I64, I64, P, I64, P]),
+        "svdq_weight_sizes": (I32, [I64, I64, I32, P, P]),
+        "svdq_pack_weights": (I32, [I64, I64, P, P, F, I32, I32, P, P, P, P, P, P, P]),
+        "svdq_quantize_weights": (I32, [I64, I64, P, I32, P, P]),
+        "svdq_concat_lora": (I32, [I64, I64, P, I32, P, P, I32, P, P, F, P, P]),
+        "svdq_lowrank_down_factors": (I32, [I64, I32, P, P, P, P]),
+        "svdq_quantize_act_lora_down": (I32, [P, I64, P, I64, P, P, P, P]),
+        "svdq_gemm_w4a4_lora_up": (I32, [P, I64, P, P, P, P, I64, I32, P]),
+        "svdq_workspace_bytes": (ctypes.c_size_t, [P, I64]),
+        "svdq_linear_forward": (I32, [P, I64, P, I64, P, I64, I32, P, ctypes.c_size_t, P]),
+        "svdq_debug_group_sums": (I32, [P, I64, P, I64, I64, I64, I64, P, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = L
+    return L
+
+
+def _check(status: int):
+    if status != 0:
+        raise SvdqError(f"svdq status {status}: {lib().svdq_last_error().decode()}")
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+# ------------------------------------------------------------------ host functions
+
+def act_absmax(X_bits: np.ndarray) -> np.ndarray:
+    X = np.ascontiguousarray(X_bits, dtype=np.uint16)
+    out = np.empty(X.shape[1], np.float32)
+    _check(lib().svdq_act_absmax(X.shape[0], X.shape[1], _ptr(X), X.shape[1], _ptr(out)))
+    return out
+
+
+def weight_sizes(K: int, N: int, fmt: int):
+    q = ctypes.c_size_t()
+    s = ctypes.c_size_t()
+    _check(lib().svdq_weight_sizes(K, N, fmt, ctypes.byref(q), ctypes.byref(s)))
+    return q.value, s.value
+
+
+@dataclass
+class HostPack:
+    """Offline pack artifacts (host numpy arrays)."""
+    K: int
+    N: int
+    rank: int
+    fmt: int
+    s: np.ndarray       # fp32 [K]
+    inv_s: np.ndarray   # fp32 [K]
+    L1t: np.ndarray     # bf16 bits [rank][K]
+    L2: np.ndarray      # bf16 bits [rank][N]
+    qW: np.ndarray      # u8 [N][K/2]
+    sW: np.ndarray      # fp16 bits u16 or E8M0 u8 [K/G][N]
+    R: Optional[np.ndarray] = None
+
+
+def pack_weights(W_bits: np.ndarray, act_absmax_: Optional[np.ndarray], alpha: float, rank: int,
+                 fmt: int, want_R: bool = False) -> HostPack:
+    W = np.ascontiguousarray(W_bits, dtype=np.uint16)
+    K, N = W.shape
+    s = np.empty(K, np.float32)
+    inv = np.empty(K, np.float32)
+    L1t = np.zeros((rank, K), np.uint16)
+    L2 = np.zeros((rank, N), np.uint16)
+    qW = np.empty((N, K // 2), np.uint8)
+    G = GROUP.get(fmt, 64)
+    sW = np.empty((K // G, N), np.uint16 if fmt == INT4_G64 else np.uint8)
+    R = np.empty((K, N), np.float32) if want_R else None
+    a = None if act_absmax_ is None else np.ascontiguousarray(act_absmax_, dtype=np.float32)
+    _check(lib().svdq_pack_weights(K, N, _ptr(W), _ptr(a), float(alpha), rank, fmt, _ptr(s), _ptr(inv),
+                                   _ptr(L1t), _ptr(L2), _ptr(qW), _ptr(sW), _ptr(R)))
+    return HostPack(K, N, rank, fmt, s, inv, L1t, L2, qW, sW, R)
+
+
+def quantize_weights(R: np.ndarray, fmt: int):
+    R = np.ascontiguousarray(R, dtype=np.float32)
+    K, N = R.shape
+    qW = np.empty((N, K // 2), np.uint8)
+    G = GROUP.get(fmt, 64)
+    sW = np.empty((K // G, N), np.uint16 if fmt == INT4_G64 else np.uint8)
+    _check(lib().svdq_quantize_weights(K, N, _ptr(R), fmt, _ptr(qW), _ptr(sW)))
+    return qW, sW
+
+
+def concat_lora(p: HostPack, A_bits: np.ndarray, B_bits: np.ndarray, scale: float = 1.0) -> HostPack:
+    A = np.ascontiguousarray(A_bits, dtype=np.uint16)
+    B = np.ascontiguousarray(B_bits, dtype=np.uint16)
+    lr = A.shape[1]
+    r = p.rank + lr
+    L1t = np.empty((r, p.K), np.uint16)
+    L2 = np.empty((r, p.N), np.uint16)
+    _check(lib().svdq_concat_lora(p.K, p.N, _ptr(p.s), p.rank, _ptr(np.ascontiguousarray(p.L1t)),
+                                  _ptr(np.ascontiguousarray(p.L2)), lr, _ptr(A), _ptr(B), float(scale),
+                                  _ptr(L1t), _ptr(L2)))
+    return HostPack(p.K, p.N, r, p.fmt, p.s, p.inv_s, L1t, L2, p.qW, p.sW, p.R)
+
+
+def lowrank_down_factors(inv_s: np.ndarray, L1t: np.ndarray):
+    inv = np.ascontiguousarray(inv_s, dtype=np.float32)
+    L1t = np.ascontiguousarray(L1t, dtype=np.uint16)
+    r, K = L1t.shape
+    hi = np.zeros((r, K), np.uint16)
+    lo = np.zeros((r, K), np.uint16)
+    _check(lib().svdq_lowrank_down_factors(K, r, _ptr(inv), _ptr(L1t), _ptr(hi), _ptr(lo)))
+    return hi, lo
+
+
+# ------------------------------------------------------------------ device side
+
+def _torch():
+    import torch
+
+    if not torch.cuda.is_available():
+        raise SvdqError("no HIP device visible to torch")
+    return torch
+
+
+def _dptr(t) -> Optional[int]:
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream)
+
+
+def _upload(a: np.ndarray, device):
+    torch = _torch()
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        t = torch.from_numpy(a.view(np.int16))
+    elif a.dtype == np.uint8:
+        t = torch.from_numpy(a)
+    else:
+        t = torch.from_numpy(a)
+    return t.to(device)
+
+
+class PackedLinear:
+    """A packed layer resident on the GPU, callable through the library's kernels."""
+
+    def __init__(self, K: int, N: int, rank: int, fmt: int, inv_s: np.ndarray, L1t: np.ndarray,
+                 L2: np.ndarray, qW: np.ndarray, sW: np.ndarray, device="cuda:0"):
+        self.K, self.N, self.rank, self.fmt = int(K), int(N), int(rank), int(fmt)
+        self.device = device
+        self.inv_s = _upload(np.asarray(inv_s, np.float32), device)
+        if rank > 0:
+            hi, lo = lowrank_down_factors(inv_s, L1t)
+            self.Ld_hi = _upload(hi, device)
+            self.Ld_lo = _upload(lo, device)
+            self.L2 = _upload(np.asarray(L2, np.uint16), device)
+        else:
+            self.Ld_hi = self.Ld_lo = self.L2 = None
+        self.qW = _upload(np.asarray(qW, np.uint8), device)
+        self.sW = _upload(sW, device)
+        self._c = _Layer(self.K, self.N, self.rank, self.fmt, _dptr(self.inv_s), _dptr(self.Ld_hi),
+                         _dptr(self.Ld_lo), _dptr(self.L2), _dptr(self.qW), _dptr(self.sW))
+
+    @classmethod
+    def from_host_pack(cls, p: HostPack, device="cuda:0"):
+        return cls(p.K, p.N, p.rank, p.fmt, p.inv_s, p.L1t, p.L2, p.qW, p.sW, device)
+
+    @property
+    def group(self) -> int:
+        return GROUP[self.fmt]
+
+    def c_layer(self):
+        return ctypes.byref(self._c)
+
+    def alloc_act(self, M: int):
+        torch = _torch()
+        qX = torch.empty((M, self.K // 2), dtype=torch.uint8, device=self.device)
+        sdt = torch.int16 if self.fmt == INT4_G64 else torch.uint8
+        sX = torch.empty((self.K // self.group, M), dtype=sdt, device=self.device)
+        la = torch.empty((M, self.rank), dtype=torch.float32, device=self.device) if self.rank else None
+        return qX, sX, la
+
+    def quantize_act(self, X, out=None):
+        """Kernel 1 on bf16 X [M][K] (torch tensor on the device)."""
+        M = X.shape[0]
+        qX, sX, la = out if out is not None else self.alloc_act(M)
+        _check(lib().svdq_quantize_act_lora_down(self.c_layer(), M, _dptr(X), X.stride(0), _dptr(qX),
+                                                 _dptr(sX), _dptr(la), _stream()))
+        return qX, sX, la
+
+    def gemm(self, qX, sX, la, ydtype: int = F32, out=None):
+        """Kernel 2: Y [M][N] from kernel 1's outputs."""
+        torch = _torch()
+        M = qX.shape[0]
+        if out is None:
+            out = torch.empty((M, self.N), dtype=torch.float32 if ydtype == F32 else torch.bfloat16,
+                              device=self.device)
+        _check(lib().svdq_gemm_w4a4_lora_up(self.c_layer(), M, _dptr(qX), _dptr(sX), _dptr(la), _dptr(out),
+                                            out.stride(0), ydtype, _stream()))
+        return out
+
+    def workspace(self, M: int):
+        torch = _torch()
+        n = lib().svdq_workspace_bytes(self.c_layer(), M)
+        return torch.empty(max(n, 256), dtype=torch.uint8, device=self.device)
+
+    def forward(self, X, ydtype: int = F32, out=None, workspace=None):
+        """The public layer: svdq_linear_forward (kernel 1 then kernel 2)."""
+        torch = _torch()
+        M = X.shape[0]
+        if out is None:
+            out = torch.empty((M, self.N), dtype=torch.float32 if ydtype == F32 else torch.bfloat16,
+                              device=self.device)
+        ws = workspace if workspace is not None else self.workspace(M)
+        _check(lib().svdq_linear_forward(self.c_layer(), M, _dptr(X), X.stride(0), _dptr(out), out.stride(0),
+                                         ydtype, _dptr(ws), ws.numel(), _stream()))
+        return out
+
+    def group_sums(self, qX, m0: int, n0: int, mt: int, nt: int):
+        """Exact INT4 group sums I[g][m][n] for a window (diagnostic)."""
+        torch = _torch()
+        out = torch.empty((self.K // 64, mt, nt), dtype=torch.int32, device=self.device)
+        _check(lib().svdq_debug_group_sums(self.c_layer(), qX.shape[0], _dptr(qX), m0, n0, mt, nt, _dptr(out),
+                                           _stream()))
+        return out

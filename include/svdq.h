@@ -1,0 +1,186 @@
+/*
+ * svdq.h - C ABI of the MI355X (gfx950) SVDQuant W4A4 + low-rank linear layer.
+ *
+ *   Y = Q(X diag(s)^-1) Q(R) + (X diag(s)^-1 L1) L2
+ *
+ * The layer equation and the split W_hat = L1 L2 + R (16-bit low-rank branch, 4-bit
+ * residual) are those of the jeonghoonpark.com "SVDQuant" review, section 4.2, and of
+ * the ch3chohch3.github.io post "从 Smooth Quant 到 SVD Quant", section "量化方案".
+ * The two device entry points follow the two fused kernels of the review's section
+ * 4.3 ("Nunchaku"): the low-rank down projection fused into activation quantization,
+ * the low-rank up projection fused into the 4-bit GEMM.
+ *
+ * Conventions for every function below:
+ *  - Row-major storage everywhere.  bf16 and fp16 values travel as uint16_t bit
+ *    patterns.  Sizes are int64_t element counts.
+ *  - "host" pointers are CPU memory; "device" pointers are GPU memory on the current
+ *    HIP device.  The caller owns and allocates every buffer; the library allocates no
+ *    device memory, keeps no global state besides a thread-local error message, and
+ *    never synchronizes the device.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Device
+ *    entry points only enqueue work on it and return; stream order is the only
+ *    synchronization between them.
+ *  - Every function returns an svdq_status; on failure svdq_last_error() describes
+ *    it.  Nothing throws or aborts across this boundary.
+ *
+ * Formats (svdq_format):
+ *  - SVDQ_INT4_G64: symmetric INT4, q in [-7, 7], one fp16 scale per 64 consecutive
+ *    values along K, q = round-half-even(v / s), s = fp16(fp32(max|v| / 7)).  Codes
+ *    are 4-bit sign-magnitude nibbles (bit 3 sign, bits 0-2 |q|).
+ *  - SVDQ_MXFP4_G32: E2M1 codes (bit 3 sign, bits 0-2 index into
+ *    {0, 0.5, 1, 1.5, 2, 3, 4, 6}) with one E8M0 byte (2^(byte - 127)) per 32 values,
+ *    the exponent being the smallest e with 6 * 2^e >= max|v|; round half to even on
+ *    the E2M1 grid, sign bit kept.
+ *  Two codes per byte: byte j of a row holds element 2j in the low nibble and
+ *  element 2j+1 in the high nibble.  The quantizer formula is the review's section 3
+ *  equation Q_X = round(X / s_X), s_X = max|X| / q_max (q_max 7 for INT4, 6 for FP4).
+ */
+#ifndef SVDQ_H
+#define SVDQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SVDQ_OK = 0,
+  SVDQ_EINVAL = 1,       /* bad argument: NULL pointer, size, alignment, range */
+  SVDQ_EUNSUPPORTED = 2, /* valid but not supported (format, rank limit) */
+  SVDQ_ENUMERIC = 3,     /* non-finite input where finite values are required */
+  SVDQ_EHIP = 4          /* HIP runtime error reported at launch */
+} svdq_status;
+
+typedef enum { SVDQ_INT4_G64 = 0, SVDQ_MXFP4_G32 = 1 } svdq_format;
+typedef enum { SVDQ_F32 = 0, SVDQ_BF16 = 1 } svdq_dtype;
+
+#define SVDQ_MAX_RANK 128
+
+/* Device-resident description of one packed layer (all pointers device memory,
+ * owned by the caller, produced by svdq_pack_weights + svdq_lowrank_down_factors):
+ *   inv_s  [K]        fp32  reciprocal smoothing factor, fp32(1 / fp32(s))
+ *   Ld_hi  [rank][K]  bf16  high part of (diag(inv_s) L1)^T
+ *   Ld_lo  [rank][K]  bf16  low part, so Ld_hi + Ld_lo = diag(inv_s) L1 to ~2^-17
+ *   L2     [rank][N]  bf16  up projection
+ *   qW     [N][K/2]   u8    residual codes, row n = output channel n along K
+ *   sW     [K/G][N]   fp16 bits (INT4) or E8M0 bytes (MXFP4), group-major
+ * Ld_hi/Ld_lo/L2 may be NULL iff rank == 0. */
+typedef struct svdq_layer {
+  int64_t K, N;
+  int32_t rank;
+  int32_t fmt; /* svdq_format */
+  const float* inv_s;
+  const uint16_t* Ld_hi;
+  const uint16_t* Ld_lo;
+  const uint16_t* L2;
+  const uint8_t* qW;
+  const void* sW;
+} svdq_layer;
+
+/* Thread-local description of the last failure in this thread ("" after success). */
+const char* svdq_last_error(void);
+
+/* ----------------------------------------------------------------- host side ---- */
+
+/* Calibration statistic max over rows m of |X[m][k]| for each input channel k
+ * (the max|X_j| of the smoothing-factor formula, ch3chohch3.github.io post, section
+ * "Smooth Quant（W8A8）").  X: host bf16 [M][ldx]; out: host fp32 [K].
+ * EINVAL on NULL / M < 1 / K < 1 / ldx < K. */
+svdq_status svdq_act_absmax(int64_t M, int64_t K, const uint16_t* X, int64_t ldx, float* out);
+
+/* Sizes in bytes of the packed residual buffers for a K x N layer. */
+svdq_status svdq_weight_sizes(int64_t K, int64_t N, int32_t fmt, size_t* qW_bytes,
+                              size_t* sW_bytes);
+
+/* Offline pack (host only, fp64 internally; multi-threaded).
+ *   s_j = max(a_j,1e-5)^alpha / max(w_j,1e-5)^(1-alpha), w_j = max_n |W[j][n]|
+ *     (ch3chohch3.github.io post, "Smooth Quant（W8A8）", smoothing-factor equation);
+ *   W_hat = diag(fp32(s)) W;  truncated SVD W_hat ~ U_r Sigma_r V_r^T computed from the
+ *     Gram matrix of W_hat with the library's own symmetric eigensolver;
+ *   L1 = U_r Sigma_r, L2 = V_r^T, both rounded to bf16 (review, section 4.2);
+ *   R = W_hat - L1 L2 with the rounded factors; R quantized per output column n in
+ *     groups along K (format fmt).
+ * Inputs: W host bf16 [K][N]; act_absmax host fp32 [K] or NULL for no smoothing
+ * (s = 1); alpha in [0,1]; 0 <= rank <= min(K, N, SVDQ_MAX_RANK).
+ * Outputs (host, caller-allocated): s_out, inv_s_out [K] fp32; L1t_out [rank][K] bf16
+ * (L1 transposed: row j = sigma_j u_j); L2_out [rank][N] bf16; qW_out [N][K/2];
+ * sW_out [K/G][N]; R_out optional fp32 [K][N] (NULL to skip).
+ * Errors: EINVAL (NULL, K % 128 != 0, N < 1, alpha out of range, bad rank),
+ * ENUMERIC (non-finite W or act_absmax), EUNSUPPORTED (fmt). */
+svdq_status svdq_pack_weights(int64_t K, int64_t N, const uint16_t* W, const float* act_absmax,
+                              float alpha, int32_t rank, int32_t fmt, float* s_out,
+                              float* inv_s_out, uint16_t* L1t_out, uint16_t* L2_out,
+                              uint8_t* qW_out, void* sW_out, float* R_out);
+
+/* Quantize a given fp32 residual R [K][N] (host) per output column in groups along K:
+ * the last step of svdq_pack_weights on its own.  Outputs as in svdq_pack_weights. */
+svdq_status svdq_quantize_weights(int64_t K, int64_t N, const float* R, int32_t fmt,
+                                  uint8_t* qW_out, void* sW_out);
+
+/* Fold an off-the-shelf LoRA (X A B on unsmoothed X) into the low-rank branch without
+ * touching the quantized residual (SVDQuant abstract, chatpaper.ai: adapters run
+ * without re-quantization).  X A B = (X diag(s)^-1)(diag(s) A) B, so
+ *   L1t_out = [L1t ; bf16(lora_scale * diag(s) A)^T]   ([rank+lr][K])
+ *   L2_out  = [L2 ; B]                                  ([rank+lr][N])
+ * Host pointers: s [K] fp32; L1t [rank][K]; L2 [rank][N]; A [K][lr]; B [lr][N] bf16.
+ * EINVAL / EUNSUPPORTED when rank + lr exceeds SVDQ_MAX_RANK. */
+svdq_status svdq_concat_lora(int64_t K, int64_t N, const float* s, int32_t rank,
+                             const uint16_t* L1t, const uint16_t* L2, int32_t lora_rank,
+                             const uint16_t* A, const uint16_t* B, float lora_scale,
+                             uint16_t* L1t_out, uint16_t* L2_out);
+
+/* Offline fold of the runtime smoothing into the down projection:
+ * (X diag(s)^-1) L1 = X (diag(inv_s) L1).  For each j < rank, k < K:
+ *   v = inv_s[k] * L1t[j][k] (fp32), hi = bf16_rne(v), lo = bf16_rne(v - hi).
+ * Host pointers; outputs hi_out, lo_out [rank][K] bf16. */
+svdq_status svdq_lowrank_down_factors(int64_t K, int32_t rank, const float* inv_s,
+                                      const uint16_t* L1t, uint16_t* hi_out, uint16_t* lo_out);
+
+/* ---------------------------------------------------------------- device side ---- */
+
+/* Kernel 1: smooth, quantize and down-project the activations in one pass over X
+ * (review section 4.3: down projection fused with the quantization kernel, sharing
+ * the activation read).
+ *   X        device bf16 [M][ldx], 16-byte aligned rows (ldx % 8 == 0)
+ *   qX       device u8 [M][K/2]           4-bit codes of X_hat = X diag(inv_s)
+ *   sX       device [K/G][M]              fp16 bits (INT4) or E8M0 bytes (MXFP4)
+ *   lora_act device fp32 [M][rank]        X_hat L1 (unused when rank == 0)
+ * M == 0 is a no-op.  EINVAL on NULL / misalignment / ldx < K; EHIP on launch error. */
+svdq_status svdq_quantize_act_lora_down(const svdq_layer* layer, int64_t M, const uint16_t* X,
+                                        int64_t ldx, uint8_t* qX, void* sX, float* lora_act,
+                                        void* stream);
+
+/* Kernel 2: W4A4 GEMM on the codes with per-group rescaling by s_X s_W and the
+ * low-rank up projection (lora_act L2) added in the epilogue (review section 4.3: up
+ * projection fused with the 4-bit kernel).
+ *   qX, sX, lora_act  as written by kernel 1 (device)
+ *   Y                 device [M][ldy], fp32 or bf16 (ydtype), 16-byte aligned rows
+ * Y is overwritten (no accumulation into existing contents). */
+svdq_status svdq_gemm_w4a4_lora_up(const svdq_layer* layer, int64_t M, const uint8_t* qX,
+                                   const void* sX, const float* lora_act, void* Y, int64_t ldy,
+                                   int32_t ydtype, void* stream);
+
+/* Bytes of device workspace svdq_linear_forward needs for M rows (qX, sX, lora_act,
+ * each 256-byte aligned). */
+size_t svdq_workspace_bytes(const svdq_layer* layer, int64_t M);
+
+/* The public layer: kernel 1 then kernel 2 on `stream`, intermediates in `workspace`
+ * (device, >= svdq_workspace_bytes, 256-byte aligned). */
+svdq_status svdq_linear_forward(const svdq_layer* layer, int64_t M, const uint16_t* X,
+                                int64_t ldx, void* Y, int64_t ldy, int32_t ydtype,
+                                void* workspace, size_t ws_bytes, void* stream);
+
+/* Diagnostic, same main loop as kernel 2 with an epilogue that stores the exact
+ * integer group sums I[g][m][n] = sum_{k in group g} qX[m][k] qW[n][k] (INT4 only) for
+ * the window rows [m0, m0+mt) x cols [n0, n0+nt).  out: device int32 [K/64][mt][nt].
+ * Synchronous (waits for the stream) so it can be used from tests directly. */
+svdq_status svdq_debug_group_sums(const svdq_layer* layer, int64_t M, const uint8_t* qX,
+                                  int64_t m0, int64_t n0, int64_t mt, int64_t nt, int32_t* out,
+                                  void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SVDQ_H */

@@ -1,0 +1,141 @@
+"""GPU parity of the HIP path against the oracle on small and ragged shapes.
+
+Bar: bit-exact 4-bit codes, scales and INT4 integer group sums; lora_act within the
+arithmetic's error budget; Y within 2e-2 x RMS of the oracle output (fp32 output).
+Shapes span several 256 x 256 output tiles and 16-token kernel-1 tiles with ragged
+tails, K from 128 (the minimum) upward, ranks 0 / 1 / 8 / 48 / 128.
+"""
+import numpy as np
+import pytest
+
+from gpu_helpers import TOL_Y, layer_from_oracle, log, lora_bound, oracle_k1, oracle_pack, rel_err, to_dev_bf16
+
+from bit_diffusion_model_amd import svdq
+from bit_diffusion_model_amd.workloads import make, random_layer
+from oracle import forward as oforward
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [  # M, K, N, rank, fmt
+    (64, 256, 256, 8, "int4"),
+    (1, 128, 1, 0, "int4"),
+    (17, 128, 33, 1, "int4"),
+    (300, 384, 520, 8, "int4"),
+    (530, 256, 257, 48, "int4"),
+    (33, 128, 160, 128, "int4"),
+    (64, 256, 256, 8, "mxfp4"),
+    (17, 128, 33, 1, "mxfp4"),
+    (300, 384, 520, 16, "mxfp4"),
+]
+
+
+def _ids(s):
+    return "M{}_K{}_N{}_r{}_{}".format(*s)
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=_ids)
+def test_kernel1_codes_scales_lora(shape):
+    M, K, N, r, fmt = shape
+    log(f"k1 {_ids(shape)}")
+    wl = random_layer(M, K, N, r, 7000 + M + K + N, fmt=fmt, x_out=3, w_out=2)
+    p = oracle_pack(wl)
+    lay = layer_from_oracle(p)
+    X = to_dev_bf16(wl.X)
+    qX, sX, la = lay.quantize_act(X)
+    import torch
+
+    torch.cuda.synchronize()
+    Xh, codes, sc, qX_ref, sX_ref, la_ref = oracle_k1(wl.X, p)
+    np.testing.assert_array_equal(qX.cpu().numpy(), qX_ref)
+    np.testing.assert_array_equal(sX.cpu().numpy().view(sX_ref.dtype), sX_ref)
+    if r:
+        la_g = la.cpu().numpy().astype(np.float64)
+        assert np.all(np.abs(la_g - la_ref) <= lora_bound(Xh, p["L1b"]))
+
+
+@pytest.mark.parametrize("shape", [s for s in SHAPES if s[4] == "int4"], ids=_ids)
+def test_kernel2_group_sums_exact(shape):
+    M, K, N, r, fmt = shape
+    log(f"groupsums {_ids(shape)}")
+    wl = random_layer(M, K, N, r, 7000 + M + K + N, fmt=fmt, x_out=3, w_out=2)
+    p = oracle_pack(wl)
+    lay = layer_from_oracle(p)
+    qX, sX, la = lay.quantize_act(to_dev_bf16(wl.X))
+    _, codes, _, _, _, _ = oracle_k1(wl.X, p)
+    I_ref = oforward.group_sums(codes, p["codesW"], 64)
+    I = lay.group_sums(qX, 0, 0, M, N).cpu().numpy()
+    np.testing.assert_array_equal(I, I_ref)
+    if M > 2 and N > 3:  # an interior window
+        I2 = lay.group_sums(qX, M // 3, N // 4, M - M // 3, N - N // 4).cpu().numpy()
+        np.testing.assert_array_equal(I2, I_ref[:, M // 3:, N // 4:])
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=_ids)
+def test_forward_matches_oracle(shape):
+    M, K, N, r, fmt = shape
+    log(f"forward {_ids(shape)}")
+    wl = random_layer(M, K, N, r, 7000 + M + K + N, fmt=fmt, x_out=3, w_out=2)
+    p = oracle_pack(wl)
+    lay = layer_from_oracle(p)
+    Y = lay.forward(to_dev_bf16(wl.X)).cpu().numpy().astype(np.float64)
+    Yref = oforward.forward(wl.X, p)["Y"]
+    e = rel_err(Y, Yref)
+    log(f"  max|err|/RMS = {e:.3e}")
+    assert e <= TOL_Y
+    # the two kernels called separately give the same bits as the public entry point
+    qX, sX, la = lay.quantize_act(to_dev_bf16(wl.X))
+    Y2 = lay.gemm(qX, sX, la).cpu().numpy()
+    np.testing.assert_array_equal(Y2, Y.astype(np.float32))
+
+
+def test_tiny_config_c0():
+    wl = make("C0")
+    p = oracle_pack(wl)
+    lay = layer_from_oracle(p)
+    X = to_dev_bf16(wl.X)
+    Y = lay.forward(X).cpu().numpy().astype(np.float64)
+    Yref = oforward.forward(wl.X, p)["Y"]
+    e = rel_err(Y, Yref)
+    log(f"C0 max|err|/RMS = {e:.3e}")
+    assert e <= TOL_Y
+
+
+def test_rank0_and_zero_residual():
+    wl = random_layer(200, 256, 300, 8, 99, x_out=3)
+    p0 = oracle_pack(wl, rank=0)
+    Y = layer_from_oracle(p0).forward(to_dev_bf16(wl.X)).cpu().numpy().astype(np.float64)
+    assert rel_err(Y, oforward.forward(wl.X, p0)["Y"]) <= TOL_Y
+    p = dict(oracle_pack(wl))
+    p["codesW"] = np.zeros_like(p["codesW"])
+    p["qW"] = np.zeros_like(p["qW"])
+    Y = layer_from_oracle(p).forward(to_dev_bf16(wl.X)).cpu().numpy().astype(np.float64)
+    ref = oforward.forward(wl.X, p)["Y"]
+    assert rel_err(Y, ref) <= 1e-3  # only the low-rank branch remains: fp32-accurate
+
+
+def test_bf16_output_and_determinism():
+    wl = random_layer(257, 256, 300, 8, 5, x_out=3)
+    p = oracle_pack(wl)
+    lay = layer_from_oracle(p)
+    X = to_dev_bf16(wl.X)
+    Y32 = lay.forward(X)
+    Yb = lay.forward(X, ydtype=svdq.BF16).float().cpu().numpy().astype(np.float64)
+    ref = oforward.forward(wl.X, p)["Y"]
+    rms = np.sqrt(np.mean(ref ** 2))
+    assert np.all(np.abs(Yb - ref) <= 2.0 ** -8 * np.abs(ref) + TOL_Y * rms)
+    for _ in range(5):
+        assert np.array_equal(lay.forward(X).cpu().numpy(), Y32.cpu().numpy())
+
+
+def test_strided_activation_rows():
+    import torch
+
+    wl = random_layer(40, 256, 96, 8, 12, x_out=2)
+    p = oracle_pack(wl)
+    lay = layer_from_oracle(p)
+    Xp = np.zeros((40, 256 + 64), np.uint16)
+    Xp[:, :256] = wl.X
+    Xd = to_dev_bf16(Xp)[:, :256]
+    assert Xd.stride(0) == 320
+    Y = lay.forward(Xd).cpu().numpy().astype(np.float64)
+    assert rel_err(Y, oforward.forward(wl.X, p)["Y"]) <= TOL_Y
