@@ -8,8 +8,9 @@
 // fused into the quantization kernel so both share one read of X (review, section 4.3,
 // Figure 6(b)).  Activation scales are computed online (ch3chohch3 post, "量化方案").
 //
-// Work split: a block of 4 waves owns 16 consecutive tokens.  The K dimension is cut
-// into 64-wide chunks; wave w takes chunks w, w+4, ...  Inside a chunk, lane l holds
+// Work split: a block of 8 waves owns 16 consecutive tokens.  The K dimension is cut
+// into 64-wide chunks; wave w takes chunks w, w+8, ..., with the next chunk's X and
+// inv_s loads issued before the current chunk is processed.  Inside a chunk, lane l holds
 // token (l & 15) and the 16 consecutive channels 16 * (l >> 4) .. +15 (two 16-byte
 // loads of X).  One INT4 group (64) is therefore spread over the 4 lanes l, l^16,
 // l^32, l^48; one FP4 group (32) over lanes l, l^16.
@@ -19,14 +20,17 @@
 // MFMA A operand with no conversion.  v_mfma_f32_16x16x32_bf16: lane l supplies row
 // l & 15 and k-block l >> 4; we feed the lane's first 8 channels to one MFMA and the
 // next 8 to a second, and the B operand (Ld rows, contiguous along K) uses the same
-// channel order.  Partial sums of the 4 waves are added through LDS at the end.
+// channel order.  Partial sums of the 8 waves are added through LDS at the end, in a
+// fixed order.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace svdq {
 
+constexpr int K1_WAVES = 8;
+
 template <int FMT, int NT>
-__global__ __launch_bounds__(256) void k1_quant_lora_down(
+__global__ __launch_bounds__(64 * K1_WAVES) void k1_quant_lora_down(
     const uint16_t* __restrict__ X, int64_t ldx, int64_t M, int64_t K,
     const float* __restrict__ inv_s, const uint16_t* __restrict__ Ldh,
     const uint16_t* __restrict__ Ldl, int rank, uint8_t* __restrict__ qX,
@@ -35,32 +39,59 @@ __global__ __launch_bounds__(256) void k1_quant_lora_down(
   const int wave = threadIdx.x >> 6;
   const int r16 = lane & 15;
   const int sub = lane >> 4;
-  const int64_t row = (int64_t)blockIdx.x * 16 + r16;
+  const int64_t m0 = (int64_t)blockIdx.x * 16;
+  const int64_t row = m0 + r16;
   const bool row_ok = row < M;
   const int nchunks = (int)(K >> 6);
+  // rows past M read as zeros through the range check
+  const int64_t nrows = M - m0 < 16 ? M - m0 : 16;
+  const __amdgpu_buffer_rsrc_t rX = make_rsrc(X + m0 * ldx, (uint32_t)(((nrows - 1) * ldx + K) * 2));
+  const __amdgpu_buffer_rsrc_t rS = make_rsrc(inv_s, (uint32_t)(K * 4));
+  const uint32_t xoff = (uint32_t)(r16 * ldx + sub * 16) * 2;
 
   v4f acc[NT > 0 ? NT : 1];
 #pragma unroll
   for (int t = 0; t < (NT > 0 ? NT : 1); ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  for (int c = wave; c < nchunks; c += 4) {
+  uint4 xa, xb, s0, s1, s2, s3;  // the current chunk's X and inv_s, loaded one chunk ahead
+  auto fetch = [&](int c) {
+    const uint32_t kx = xoff + (uint32_t)c * 128;
+    xa = buf_load16(rX, kx);
+    xb = buf_load16(rX, kx + 16);
+    const uint32_t ks = (uint32_t)(c * 64 + sub * 16) * 4;
+    s0 = buf_load16(rS, ks);
+    s1 = buf_load16(rS, ks + 16);
+    s2 = buf_load16(rS, ks + 32);
+    s3 = buf_load16(rS, ks + 48);
+  };
+  if (wave < nchunks) fetch(wave);
+
+  for (int c = wave; c < nchunks; c += K1_WAVES) {
     const int64_t k0 = (int64_t)c * 64 + sub * 16;
-    uint4 xa = make_uint4(0, 0, 0, 0), xb = make_uint4(0, 0, 0, 0);
-    if (row_ok) {
-      const uint4* px = reinterpret_cast<const uint4*>(X + row * ldx + k0);
-      xa = px[0];
-      xb = px[1];
-    }
-    const float4* ps = reinterpret_cast<const float4*>(inv_s + k0);
-    float4 s0 = ps[0], s1 = ps[1], s2 = ps[2], s3 = ps[3];
     const uint32_t xw[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
-    const float sv[16] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w,
-                          s2.x, s2.y, s2.z, s2.w, s3.x, s3.y, s3.z, s3.w};
+    const uint32_t sw[16] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w,
+                             s2.x, s2.y, s2.z, s2.w, s3.x, s3.y, s3.z, s3.w};
+    const uint4 cxa = xa, cxb = xb;
+    if (c + K1_WAVES < nchunks) fetch(c + K1_WAVES);
+
+    // low-rank down projection operands for this chunk (issued early)
+    uint4 hA[NT > 0 ? NT : 1], hB[NT > 0 ? NT : 1], lA[NT > 0 ? NT : 1], lB[NT > 0 ? NT : 1];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int n = t * 16 + r16;
+      hA[t] = hB[t] = lA[t] = lB[t] = make_uint4(0, 0, 0, 0);
+      if (n < rank) {
+        const uint4* ph = reinterpret_cast<const uint4*>(Ldh + (int64_t)n * K + k0);
+        const uint4* pl = reinterpret_cast<const uint4*>(Ldl + (int64_t)n * K + k0);
+        hA[t] = ph[0]; hB[t] = ph[1]; lA[t] = pl[0]; lB[t] = pl[1];
+      }
+    }
+
     float xh[16];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      xh[2 * i] = bf16_lo_to_f32(xw[i]) * sv[2 * i];
-      xh[2 * i + 1] = bf16_hi_to_f32(xw[i]) * sv[2 * i + 1];
+      xh[2 * i] = bf16_lo_to_f32(xw[i]) * __uint_as_float(sw[2 * i]);
+      xh[2 * i + 1] = bf16_hi_to_f32(xw[i]) * __uint_as_float(sw[2 * i + 1]);
     }
     float a = 0.f;
 #pragma unroll
@@ -78,8 +109,8 @@ __global__ __launch_bounds__(256) void k1_quant_lora_down(
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float q0 = rintf(xh[i] * rcp);
-        // x - q0 * s is exact whenever it is near s / 2 (see the oracle's argument),
-        // so this decides the exact quotient's rounding, ties to even.
+        // x - q0 * s is exact whenever it is near s / 2, so this decides the exact
+        // quotient's rounding, ties to even.
         const float e = fmaf(-q0, sf, xh[i]);
         const float ae = fabsf(e);
         const bool odd = (((int)q0) & 1) != 0;
@@ -123,38 +154,34 @@ __global__ __launch_bounds__(256) void k1_quant_lora_down(
     }
 
     if constexpr (NT > 0) {
-      const v8bf a0 = __builtin_bit_cast(v8bf, xa);
-      const v8bf a1 = __builtin_bit_cast(v8bf, xb);
+      const v8bf a0 = __builtin_bit_cast(v8bf, cxa);
+      const v8bf a1 = __builtin_bit_cast(v8bf, cxb);
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        const int n = t * 16 + r16;
-        uint4 h0 = make_uint4(0, 0, 0, 0), h1 = h0, l0 = h0, l1 = h0;
-        if (n < rank) {
-          const uint4* ph = reinterpret_cast<const uint4*>(Ldh + (int64_t)n * K + k0);
-          const uint4* pl = reinterpret_cast<const uint4*>(Ldl + (int64_t)n * K + k0);
-          h0 = ph[0]; h1 = ph[1]; l0 = pl[0]; l1 = pl[1];
-        }
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, __builtin_bit_cast(v8bf, h0), acc[t], 0, 0, 0);
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, __builtin_bit_cast(v8bf, h1), acc[t], 0, 0, 0);
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, __builtin_bit_cast(v8bf, l0), acc[t], 0, 0, 0);
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, __builtin_bit_cast(v8bf, l1), acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, __builtin_bit_cast(v8bf, hA[t]), acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, __builtin_bit_cast(v8bf, hB[t]), acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, __builtin_bit_cast(v8bf, lA[t]), acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, __builtin_bit_cast(v8bf, lB[t]), acc[t], 0, 0, 0);
       }
     }
   }
 
   if constexpr (NT > 0) {
     // D layout of the 16x16 MFMA: lane l holds column l & 15, rows 4 * (l >> 4) + i.
-    __shared__ float red[4][16][NT * 16];
+    __shared__ float red[K1_WAVES][16][NT * 16];
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) red[wave][4 * sub + i][t * 16 + r16] = acc[t][i];
     __syncthreads();
-    const int64_t m0 = (int64_t)blockIdx.x * 16;
-    for (int idx = threadIdx.x; idx < 16 * rank; idx += 256) {
+    for (int idx = threadIdx.x; idx < 16 * rank; idx += 64 * K1_WAVES) {
       const int rr = idx / rank, cc = idx - rr * rank;
-      if (m0 + rr < M)
-        lora_act[(m0 + rr) * rank + cc] = red[0][rr][cc] + red[1][rr][cc] + red[2][rr][cc] + red[3][rr][cc];
+      if (m0 + rr < M) {
+        float v = 0.f;
+#pragma unroll
+        for (int w = 0; w < K1_WAVES; ++w) v += red[w][rr][cc];
+        lora_act[(m0 + rr) * rank + cc] = v;
+      }
     }
   }
 }
@@ -162,7 +189,7 @@ __global__ __launch_bounds__(256) void k1_quant_lora_down(
 template <int FMT>
 static hipError_t launch_k1_fmt(const KernelLayer& L, int64_t M, const uint16_t* X, int64_t ldx,
                                 uint8_t* qX, void* sX, float* lora_act, hipStream_t st) {
-  const dim3 grid((unsigned)((M + 15) / 16)), block(256);
+  const dim3 grid((unsigned)((M + 15) / 16)), block(64 * K1_WAVES);
   const int nt = (L.rank + 15) / 16;
 #define K1_CASE(NTV)                                                                          \
   case NTV:                                                                                   \

@@ -17,10 +17,13 @@
 //    With per-group scales on both sides this per-element rescale is the VALU cost
 //    that bounds the INT4 path; moving the powers of two into the MFMA halves it.
 //
-// Tiling: a 512-thread block (8 waves) owns a 256 x 256 output tile; wave w owns rows
-// 128*(w/4) .. +127 and columns 64*(w%4) .. +63, i.e. 4 x 2 MFMA tiles of 32 x 32.  Per
+// Tiling: a 512-thread block (8 waves) owns a 256 x 128 output tile; wave w owns rows
+// 64*(w/2) .. +63 and columns 64*(w%2) .. +63, i.e. 2 x 2 MFMA tiles of 32 x 32.  Per
 // 64-wide K step the block stages both operand panels through LDS (double buffered,
-// rows padded to avoid bank conflicts); the codes are expanded once per block there.
+// rows padded so that 8 consecutive rows of 16-byte accesses hit distinct banks); the
+// codes are expanded once per block there.  Global loads run two K steps ahead of the
+// MFMAs through a two-deep register ring and use buffer resources, whose range check
+// returns zeros for the rows past the end of the matrix.
 //
 // 32x32x64 operand layout (measured): lane l supplies row/column l & 31; for FP4 it
 // holds the 32 consecutive K values 32*(l>>5).. with the block scale of that half; for
@@ -34,8 +37,8 @@ namespace svdq {
 
 namespace {
 
-constexpr int BM = 256, BN = 256, NWAVES = 8, NTHREADS = 512;
-constexpr int WM = 128, WN = 64;  // wave tile
+constexpr int BM = 256, BN = 128, NTHREADS = 512;
+constexpr int WM = 64, WN = 64;  // wave tile; waves form a 4 x 2 grid
 constexpr int TI = WM / 32, TJ = WN / 32;
 
 template <int FMT>
@@ -43,30 +46,34 @@ struct Smem {
   // operand row pitch in bytes: INT4 expands 32 code bytes to 64 FP8 bytes
   static constexpr int kRow = FMT == 0 ? 64 : 32;
   static constexpr int kPitch = kRow + 16;
-  uint8_t A[2][BM * kPitch];
-  uint8_t B[2][BN * kPitch];
-  _Float16 mX[2][BM];
-  _Float16 mW[2][BN];
-  uint32_t eX[2][BM];  // MXFP4: two E8M0 bytes (groups 2s, 2s+1); INT4: one byte
-  uint32_t eW[2][BN];
+  // one K step's panels and scales; each stage spans < 64 KB so every access in it is
+  // a per-lane base register plus an immediate offset
+  struct Stage {
+    _Float16 mX[BM];
+    _Float16 mW[BN];
+    uint32_t eX[BM];  // MXFP4: two E8M0 bytes (groups 2s, 2s+1); INT4: one byte
+    uint32_t eW[BN];
+    uint8_t A[BM * kPitch];
+    uint8_t B[BN * kPitch];
+  } st[2];
 };
 
 // fp16 scale -> (fp16 mantissa in [1,2) or 0, E8M0 byte for 2^(e+9))
-__device__ __forceinline__ void split_scale(uint16_t bits, _Float16& m, uint32_t& ebyte) {
-  const float f = (float)__builtin_bit_cast(_Float16, bits);
-  if (f == 0.0f) {
-    m = (_Float16)0.0f;
-    ebyte = 127;
-    return;
-  }
+__device__ __forceinline__ void split_scale(uint32_t bits, _Float16& m, uint32_t& ebyte) {
+  const float f = (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
   const uint32_t u = __float_as_uint(f);
   const int e = (int)((u >> 23) & 0xFF) - 127;
-  m = (_Float16)__uint_as_float((u & 0x807FFFFFu) | (127u << 23));
-  ebyte = (uint32_t)(e + 9 + 127);
+  m = f == 0.0f ? (_Float16)0.0f : (_Float16)__uint_as_float((u & 0x807FFFFFu) | (127u << 23));
+  ebyte = f == 0.0f ? 127u : (uint32_t)(e + 9 + 127);
 }
 
+struct Stage {
+  uint4 a, b;
+  uint32_t s;
+};
+
 template <int FMT, bool DEBUG>
-__global__ __launch_bounds__(NTHREADS) void k2_gemm(
+__global__ __launch_bounds__(NTHREADS, 1) void k2_gemm(
     const uint8_t* __restrict__ qX, const void* __restrict__ sXv, int64_t M,
     const uint8_t* __restrict__ qW, const void* __restrict__ sWv, int64_t N, int64_t K,
     const float* __restrict__ lora_act, const uint16_t* __restrict__ L2, int rank,
@@ -76,72 +83,90 @@ __global__ __launch_bounds__(NTHREADS) void k2_gemm(
   __shared__ S sm;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar
   const int l32 = lane & 31;
   const int kh = lane >> 5;
-  const int wm = (wave >> 2) * WM;
-  const int wn = (wave & 3) * WN;
+  const int wm = (wave >> 1) * WM;
+  const int wn = (wave & 1) * WN;
   const int64_t m0 = mbase + (int64_t)blockIdx.y * BM;
   const int64_t n0 = nbase + (int64_t)blockIdx.x * BN;
-  const int64_t Kb = K >> 1;            // bytes per code row
-  const int nsteps = (int)(K >> 6);     // 64-wide K steps
+  const uint32_t Kb = (uint32_t)(K >> 1);  // bytes per code row
+  const int nsteps = (int)(K >> 6);         // 64-wide K steps
 
-  // ---- global -> register staging (one 16-byte piece of A and of B per thread) ----
-  const int ldrow = tid >> 1, ldhalf = tid & 1;
-  const int64_t arow = m0 + ldrow, brow = n0 + ldrow;
-  const bool a_ok = arow < mlim, b_ok = brow < nlim;
-  const uint8_t* pa = qX + arow * Kb + ldhalf * 16;
-  const uint8_t* pb = qW + brow * Kb + ldhalf * 16;
-  uint4 ra, rb;
-  uint32_t rs;  // scale bits for row/col tid (tid < 256: X row, else W column)
-  auto gload = [&](int s) {
-    ra = a_ok ? *reinterpret_cast<const uint4*>(pa + (int64_t)s * 32) : make_uint4(0, 0, 0, 0);
-    rb = b_ok ? *reinterpret_cast<const uint4*>(pb + (int64_t)s * 32) : make_uint4(0, 0, 0, 0);
+  // ---- buffer resources (range-checked loads) -------------------------------------
+  const int64_t rowsA = mlim - m0 < BM ? mlim - m0 : BM;
+  const int64_t rowsB = nlim - n0 < BN ? nlim - n0 : BN;
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(qX + m0 * Kb, (uint32_t)rowsA * Kb);
+  const __amdgpu_buffer_rsrc_t rB = make_rsrc(qW + n0 * Kb, (uint32_t)rowsB * Kb);
+  const int ng = FMT == 0 ? nsteps : 2 * nsteps;  // scale groups along K
+  const int esz = FMT == 0 ? 2 : 1;
+  const __amdgpu_buffer_rsrc_t rSX = make_rsrc(sXv, DEBUG ? 0u : (uint32_t)(ng * M * esz));
+  const __amdgpu_buffer_rsrc_t rSW = make_rsrc(sWv, DEBUG ? 0u : (uint32_t)(ng * N * esz));
+
+  // staging: every thread moves one 16-byte piece of the A panel (row t & 255, half
+  // t >> 8); waves 0-3 also move one piece of the B panel (row t & 127, half t >> 7)
+  // and one X-row scale (row t), waves 4-5 one W-column scale (column t - 256).  All
+  // the role tests are wave-uniform, so the buffer resources stay scalar.
+  const int ldrow = tid & 255, ldhalf = tid >> 8;
+  const int brow = tid & 127, bhalf = (tid >> 7) & 1;
+  const uint32_t offA = (uint32_t)ldrow * Kb + ldhalf * 16;
+  const uint32_t offB = (uint32_t)brow * Kb + bhalf * 16;
+  const bool doB = wave < 4;
+  const bool xs = wave < 4;
+  const bool ws = wave >= 4 && wave < 6;
+  const uint32_t sidx = xs ? (uint32_t)(m0 + tid) : (uint32_t)(n0 + tid - 256);
+  const uint32_t sstride = xs ? (uint32_t)M : (uint32_t)N;
+
+  auto gload = [&](Stage& st, int s) {
+    st.a = buf_load16(rA, offA + (uint32_t)s * 32);
+    st.b = doB ? buf_load16(rB, offB + (uint32_t)s * 32) : make_uint4(0, 0, 0, 0);
+    st.s = 0;
     if (DEBUG) {
-      rs = 0x3C00u;  // unit scale; the debug epilogue forces its own scale bytes
-    } else if (tid < BM) {
-      const int64_t r = m0 + tid;
-      if (FMT == 0) rs = r < mlim ? reinterpret_cast<const uint16_t*>(sXv)[(int64_t)s * M + r] : 0;
-      else rs = r < mlim ? (uint32_t)reinterpret_cast<const uint8_t*>(sXv)[(int64_t)(2 * s) * M + r] |
-                               ((uint32_t)reinterpret_cast<const uint8_t*>(sXv)[(int64_t)(2 * s + 1) * M + r] << 8)
-                         : 0x7F7Fu;
+    } else if (FMT == 0) {
+      const uint32_t o = ((uint32_t)s * sstride + sidx) * 2;
+      if (xs) st.s = buf_load2(rSX, o);
+      else if (ws) st.s = buf_load2(rSW, o);
     } else {
-      const int64_t c = n0 + tid - BM;
-      if (FMT == 0) rs = c < nlim ? reinterpret_cast<const uint16_t*>(sWv)[(int64_t)s * N + c] : 0;
-      else rs = c < nlim ? (uint32_t)reinterpret_cast<const uint8_t*>(sWv)[(int64_t)(2 * s) * N + c] |
-                               ((uint32_t)reinterpret_cast<const uint8_t*>(sWv)[(int64_t)(2 * s + 1) * N + c] << 8)
-                         : 0x7F7Fu;
+      const uint32_t o0 = (uint32_t)(2 * s) * sstride + sidx, o1 = o0 + sstride;
+      if (xs) st.s = buf_load1(rSX, o0) | (buf_load1(rSX, o1) << 8);
+      else if (ws) st.s = buf_load1(rSW, o0) | (buf_load1(rSW, o1) << 8);
     }
   };
-  auto sstore = [&](int buf) {
+  auto sstore = [&](const Stage& st, int buf) {
     if (FMT == 0) {
-      uint32_t a8[8], b8[8];
-      const uint32_t aw[4] = {ra.x, ra.y, ra.z, ra.w}, bw[4] = {rb.x, rb.y, rb.z, rb.w};
+      uint32_t a8[8];
+      const uint32_t aw[4] = {st.a.x, st.a.y, st.a.z, st.a.w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        nib8_to_fp8(aw[i], a8[2 * i], a8[2 * i + 1]);
-        nib8_to_fp8(bw[i], b8[2 * i], b8[2 * i + 1]);
-      }
-      uint4* da = reinterpret_cast<uint4*>(&sm.A[buf][ldrow * S::kPitch + ldhalf * 32]);
-      uint4* db = reinterpret_cast<uint4*>(&sm.B[buf][ldrow * S::kPitch + ldhalf * 32]);
+      for (int i = 0; i < 4; ++i) nib8_to_fp8(aw[i], a8[2 * i], a8[2 * i + 1]);
+      uint4* da = reinterpret_cast<uint4*>(&sm.st[buf].A[ldrow * S::kPitch + ldhalf * 32]);
       da[0] = make_uint4(a8[0], a8[1], a8[2], a8[3]);
       da[1] = make_uint4(a8[4], a8[5], a8[6], a8[7]);
-      db[0] = make_uint4(b8[0], b8[1], b8[2], b8[3]);
-      db[1] = make_uint4(b8[4], b8[5], b8[6], b8[7]);
-      _Float16 m;
-      uint32_t eb;
-      split_scale((uint16_t)rs, m, eb);
-      if (DEBUG) {
-        m = (_Float16)1.0f;
-        eb = 127 + 9;
+      if (doB) {
+        uint32_t b8[8];
+        const uint32_t bw[4] = {st.b.x, st.b.y, st.b.z, st.b.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) nib8_to_fp8(bw[i], b8[2 * i], b8[2 * i + 1]);
+        uint4* db = reinterpret_cast<uint4*>(&sm.st[buf].B[brow * S::kPitch + bhalf * 32]);
+        db[0] = make_uint4(b8[0], b8[1], b8[2], b8[3]);
+        db[1] = make_uint4(b8[4], b8[5], b8[6], b8[7]);
       }
-      if (tid < BM) { sm.mX[buf][tid] = m; sm.eX[buf][tid] = eb; }
-      else { sm.mW[buf][tid - BM] = m; sm.eW[buf][tid - BM] = eb; }
+      if (xs || ws) {
+        _Float16 m;
+        uint32_t eb;
+        if (DEBUG) {
+          m = (_Float16)1.0f;
+          eb = 127 + 9;
+        } else {
+          split_scale(st.s, m, eb);
+        }
+        if (xs) { sm.st[buf].mX[tid] = m; sm.st[buf].eX[tid] = eb; }
+        else { sm.st[buf].mW[tid - 256] = m; sm.st[buf].eW[tid - 256] = eb; }
+      }
     } else {
-      *reinterpret_cast<uint4*>(&sm.A[buf][ldrow * S::kPitch + ldhalf * 16]) = ra;
-      *reinterpret_cast<uint4*>(&sm.B[buf][ldrow * S::kPitch + ldhalf * 16]) = rb;
-      if (tid < BM) sm.eX[buf][tid] = rs;
-      else sm.eW[buf][tid - BM] = rs;
+      *reinterpret_cast<uint4*>(&sm.st[buf].A[ldrow * S::kPitch + ldhalf * 16]) = st.a;
+      if (doB) *reinterpret_cast<uint4*>(&sm.st[buf].B[brow * S::kPitch + bhalf * 16]) = st.b;
+      if (xs) sm.st[buf].eX[tid] = st.s;
+      else if (ws) sm.st[buf].eW[tid - 256] = st.s;
     }
   };
 
@@ -151,15 +176,7 @@ __global__ __launch_bounds__(NTHREADS) void k2_gemm(
 #pragma unroll
     for (int j = 0; j < TJ; ++j) acc[i][j] = v16f{};
 
-  gload(0);
-  sstore(0);
-  __syncthreads();
-
-  for (int s = 0; s < nsteps; ++s) {
-    const int buf = s & 1;
-    if (s + 1 < nsteps) gload(s + 1);
-
-    // B fragments and column scales of this wave
+  auto compute = [&](int buf, int s) {
     v8i bf[TJ];
     uint32_t sb[TJ];
     _Float16 mw[TJ];
@@ -167,39 +184,34 @@ __global__ __launch_bounds__(NTHREADS) void k2_gemm(
     for (int j = 0; j < TJ; ++j) {
       const int col = wn + j * 32 + l32;
       if (FMT == 0) {
-        const uint4* p = reinterpret_cast<const uint4*>(&sm.B[buf][col * S::kPitch + kh * 32]);
+        const uint4* p = reinterpret_cast<const uint4*>(&sm.st[buf].B[col * S::kPitch + kh * 32]);
         const uint4 x0 = p[0], x1 = p[1];
         bf[j] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-        sb[j] = sm.eW[buf][col];
-        mw[j] = sm.mW[buf][col];
+        sb[j] = sm.st[buf].eW[col];
+        mw[j] = sm.st[buf].mW[col];
       } else {
-        const uint4 x0 = *reinterpret_cast<const uint4*>(&sm.B[buf][col * S::kPitch + kh * 16]);
+        const uint4 x0 = *reinterpret_cast<const uint4*>(&sm.st[buf].B[col * S::kPitch + kh * 16]);
         bf[j] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, 0, 0, 0, 0};
-        sb[j] = (sm.eW[buf][col] >> (8 * kh)) & 0xFF;
+        sb[j] = (sm.st[buf].eW[col] >> (8 * kh)) & 0xFF;
       }
     }
 #pragma unroll
     for (int i = 0; i < TI; ++i) {
+      // keep each row tile's fragment reads next to its MFMAs (bounds live registers)
+      __asm__ volatile("" ::: "memory");
       const int row = wm + i * 32 + l32;
       v8i af;
       uint32_t sa;
       if (FMT == 0) {
-        const uint4* p = reinterpret_cast<const uint4*>(&sm.A[buf][row * S::kPitch + kh * 32]);
+        const uint4* p = reinterpret_cast<const uint4*>(&sm.st[buf].A[row * S::kPitch + kh * 32]);
         const uint4 x0 = p[0], x1 = p[1];
         af = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-        sa = sm.eX[buf][row];
-      } else {
-        const uint4 x0 = *reinterpret_cast<const uint4*>(&sm.A[buf][row * S::kPitch + kh * 16]);
-        af = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, 0, 0, 0, 0};
-        sa = (sm.eX[buf][row] >> (8 * kh)) & 0xFF;
-      }
-      if (FMT == 0) {
+        sa = sm.st[buf].eX[row];
         // mantissas of the 16 accumulator rows: rows 8*(a>>2) + 4*kh + (a&3)
         h2 mx[8];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int rb0 = wm + i * 32 + 8 * q + 4 * kh;
-          const uint2 w = *reinterpret_cast<const uint2*>(&sm.mX[buf][rb0]);
+          const uint2 w = *reinterpret_cast<const uint2*>(&sm.st[buf].mX[wm + i * 32 + 8 * q + 4 * kh]);
           mx[2 * q] = __builtin_bit_cast(h2, w.x);
           mx[2 * q + 1] = __builtin_bit_cast(h2, w.y);
         }
@@ -226,13 +238,34 @@ __global__ __launch_bounds__(NTHREADS) void k2_gemm(
           }
         }
       } else {
+        const uint4 x0 = *reinterpret_cast<const uint4*>(&sm.st[buf].A[row * S::kPitch + kh * 16]);
+        af = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, 0, 0, 0, 0};
+        sa = (sm.st[buf].eX[row] >> (8 * kh)) & 0xFF;
 #pragma unroll
         for (int j = 0; j < TJ; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf[j], acc[i][j], 4, 4, 0,
                                                                      (int)sa, 0, (int)sb[j]);
       }
     }
-    if (s + 1 < nsteps) sstore(buf ^ 1);
+  };
+
+  // ---- main loop: loads two steps ahead, LDS double buffer, one barrier per step ----
+  Stage r0, r1;
+  gload(r0, 0);
+  if (nsteps > 1) gload(r1, 1);
+  sstore(r0, 0);
+  __syncthreads();
+  for (int s = 0; s < nsteps; s += 2) {
+    // even step s: r0 is free (stored), r1 holds step s+1
+    if (s + 2 < nsteps) gload(r0, s + 2);
+    compute(0, s);
+    if (s + 1 < nsteps) sstore(r1, 1);
+    __syncthreads();
+    if (s + 1 >= nsteps) break;
+    // odd step s+1: r1 is free, r0 holds step s+2
+    if (s + 3 < nsteps) gload(r1, s + 3);
+    compute(1, s + 1);
+    if (s + 2 < nsteps) sstore(r0, 0);
     __syncthreads();
   }
   if (DEBUG) return;
