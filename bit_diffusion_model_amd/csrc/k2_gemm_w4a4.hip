@@ -17,8 +17,9 @@
 //    With per-group scales on both sides this per-element rescale is the VALU cost
 //    that bounds the INT4 path; moving the powers of two into the MFMA halves it.
 //
-// Tiling: a 512-thread block (8 waves) owns a 256 x 128 output tile; wave w owns rows
-// 64*(w/2) .. +63 and columns 64*(w%2) .. +63, i.e. 2 x 2 MFMA tiles of 32 x 32.  Per
+// Tiling: a 256-thread block (4 waves) owns a 128 x 128 output tile; wave w owns rows
+// 64*(w/2) .. +63 and columns 64*(w%2) .. +63, i.e. 2 x 2 MFMA tiles of 32 x 32; two
+// blocks share a CU, so one block's barrier and staging overlap the other's math.  Per
 // 64-wide K step the block stages both operand panels through LDS (double buffered,
 // rows padded so that 8 consecutive rows of 16-byte accesses hit distinct banks); the
 // codes are expanded once per block there.  Global loads run two K steps ahead of the
@@ -37,8 +38,8 @@ namespace svdq {
 
 namespace {
 
-constexpr int BM = 256, BN = 128, NTHREADS = 512;
-constexpr int WM = 64, WN = 64;  // wave tile; waves form a 4 x 2 grid
+constexpr int BM = 128, BN = 128, NTHREADS = 256;
+constexpr int WM = 64, WN = 64;  // wave tile; waves form a 2 x 2 grid
 constexpr int TI = WM / 32, TJ = WN / 32;
 
 template <int FMT>
@@ -46,13 +47,10 @@ struct Smem {
   // operand row pitch in bytes: INT4 expands 32 code bytes to 64 FP8 bytes
   static constexpr int kRow = FMT == 0 ? 64 : 32;
   static constexpr int kPitch = kRow + 16;
-  // one K step's panels and scales; each stage spans < 64 KB so every access in it is
-  // a per-lane base register plus an immediate offset
+  // one K step's panels and scales
   struct Stage {
-    _Float16 mX[BM];
-    _Float16 mW[BN];
-    uint32_t eX[BM];  // MXFP4: two E8M0 bytes (groups 2s, 2s+1); INT4: one byte
-    uint32_t eW[BN];
+    _Float16 m[BM + BN];  // INT4 scale mantissas: X rows, then W columns
+    uint32_t e[BM + BN];  // E8M0 bytes (MXFP4: groups 2s and 2s+1 in bytes 0 and 1)
     uint8_t A[BM * kPitch];
     uint8_t B[BN * kPitch];
   } st[2];
@@ -73,7 +71,7 @@ struct Stage {
 };
 
 template <int FMT, bool DEBUG>
-__global__ __launch_bounds__(NTHREADS, 1) void k2_gemm(
+__global__ __launch_bounds__(NTHREADS, 2) void k2_gemm(
     const uint8_t* __restrict__ qX, const void* __restrict__ sXv, int64_t M,
     const uint8_t* __restrict__ qW, const void* __restrict__ sWv, int64_t N, int64_t K,
     const float* __restrict__ lora_act, const uint16_t* __restrict__ L2, int rank,
@@ -91,7 +89,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void k2_gemm(
   const int64_t m0 = mbase + (int64_t)blockIdx.y * BM;
   const int64_t n0 = nbase + (int64_t)blockIdx.x * BN;
   const uint32_t Kb = (uint32_t)(K >> 1);  // bytes per code row
-  const int nsteps = (int)(K >> 6);         // 64-wide K steps
+  const int nsteps = (int)(K >> 6);         // 64-wide K steps; even because K % 128 == 0
 
   // ---- buffer resources (range-checked loads) -------------------------------------
   const int64_t rowsA = mlim - m0 < BM ? mlim - m0 : BM;
@@ -100,73 +98,59 @@ __global__ __launch_bounds__(NTHREADS, 1) void k2_gemm(
   const __amdgpu_buffer_rsrc_t rB = make_rsrc(qW + n0 * Kb, (uint32_t)rowsB * Kb);
   const int ng = FMT == 0 ? nsteps : 2 * nsteps;  // scale groups along K
   const int esz = FMT == 0 ? 2 : 1;
-  const __amdgpu_buffer_rsrc_t rSX = make_rsrc(sXv, DEBUG ? 0u : (uint32_t)(ng * M * esz));
-  const __amdgpu_buffer_rsrc_t rSW = make_rsrc(sWv, DEBUG ? 0u : (uint32_t)(ng * N * esz));
-
-  // staging: every thread moves one 16-byte piece of the A panel (row t & 255, half
-  // t >> 8); waves 0-3 also move one piece of the B panel (row t & 127, half t >> 7)
-  // and one X-row scale (row t), waves 4-5 one W-column scale (column t - 256).  All
-  // the role tests are wave-uniform, so the buffer resources stay scalar.
-  const int ldrow = tid & 255, ldhalf = tid >> 8;
-  const int brow = tid & 127, bhalf = (tid >> 7) & 1;
-  const uint32_t offA = (uint32_t)ldrow * Kb + ldhalf * 16;
-  const uint32_t offB = (uint32_t)brow * Kb + bhalf * 16;
-  const bool doB = wave < 4;
-  const bool xs = wave < 4;
-  const bool ws = wave >= 4 && wave < 6;
-  const uint32_t sidx = xs ? (uint32_t)(m0 + tid) : (uint32_t)(n0 + tid - 256);
+  // staging roles: thread t moves one 16-byte piece of the A panel and one of the B
+  // panel (row t & 127, half t >> 7) and one scale: waves 0-1 the X row t, waves 2-3
+  // the W column t - 128.  The choice is wave-uniform, so it is made once, here.
+  const bool xs = wave < 2;
+  const __amdgpu_buffer_rsrc_t rS = make_rsrc(xs ? sXv : sWv, DEBUG ? 0u : (uint32_t)(ng * (xs ? M : N) * esz));
+  const uint32_t sidx = xs ? (uint32_t)(m0 + tid) : (uint32_t)(n0 + tid - BM);
   const uint32_t sstride = xs ? (uint32_t)M : (uint32_t)N;
+  const int ldrow = tid & 127, ldhalf = tid >> 7;
+  const uint32_t offAB = (uint32_t)ldrow * Kb + ldhalf * 16;
 
+  // Loads for steps past the end are harmless: they read zeros (range check) or codes
+  // of another row into a buffer that is never consumed.
   auto gload = [&](Stage& st, int s) {
-    st.a = buf_load16(rA, offA + (uint32_t)s * 32);
-    st.b = doB ? buf_load16(rB, offB + (uint32_t)s * 32) : make_uint4(0, 0, 0, 0);
-    st.s = 0;
+    st.a = buf_load16(rA, offAB + (uint32_t)s * 32);
+    st.b = buf_load16(rB, offAB + (uint32_t)s * 32);
     if (DEBUG) {
+      st.s = 0;
     } else if (FMT == 0) {
-      const uint32_t o = ((uint32_t)s * sstride + sidx) * 2;
-      if (xs) st.s = buf_load2(rSX, o);
-      else if (ws) st.s = buf_load2(rSW, o);
+      st.s = buf_load2(rS, ((uint32_t)s * sstride + sidx) * 2);
     } else {
-      const uint32_t o0 = (uint32_t)(2 * s) * sstride + sidx, o1 = o0 + sstride;
-      if (xs) st.s = buf_load1(rSX, o0) | (buf_load1(rSX, o1) << 8);
-      else if (ws) st.s = buf_load1(rSW, o0) | (buf_load1(rSW, o1) << 8);
+      const uint32_t o0 = (uint32_t)(2 * s) * sstride + sidx;
+      st.s = buf_load1(rS, o0) | (buf_load1(rS, o0 + sstride) << 8);
     }
   };
   auto sstore = [&](const Stage& st, int buf) {
     if (FMT == 0) {
-      uint32_t a8[8];
-      const uint32_t aw[4] = {st.a.x, st.a.y, st.a.z, st.a.w};
+      uint32_t a8[8], b8[8];
+      const uint32_t aw[4] = {st.a.x, st.a.y, st.a.z, st.a.w}, bw[4] = {st.b.x, st.b.y, st.b.z, st.b.w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) nib8_to_fp8(aw[i], a8[2 * i], a8[2 * i + 1]);
+      for (int i = 0; i < 4; ++i) {
+        nib8_to_fp8(aw[i], a8[2 * i], a8[2 * i + 1]);
+        nib8_to_fp8(bw[i], b8[2 * i], b8[2 * i + 1]);
+      }
       uint4* da = reinterpret_cast<uint4*>(&sm.st[buf].A[ldrow * S::kPitch + ldhalf * 32]);
+      uint4* db = reinterpret_cast<uint4*>(&sm.st[buf].B[ldrow * S::kPitch + ldhalf * 32]);
       da[0] = make_uint4(a8[0], a8[1], a8[2], a8[3]);
       da[1] = make_uint4(a8[4], a8[5], a8[6], a8[7]);
-      if (doB) {
-        uint32_t b8[8];
-        const uint32_t bw[4] = {st.b.x, st.b.y, st.b.z, st.b.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) nib8_to_fp8(bw[i], b8[2 * i], b8[2 * i + 1]);
-        uint4* db = reinterpret_cast<uint4*>(&sm.st[buf].B[brow * S::kPitch + bhalf * 32]);
-        db[0] = make_uint4(b8[0], b8[1], b8[2], b8[3]);
-        db[1] = make_uint4(b8[4], b8[5], b8[6], b8[7]);
+      db[0] = make_uint4(b8[0], b8[1], b8[2], b8[3]);
+      db[1] = make_uint4(b8[4], b8[5], b8[6], b8[7]);
+      _Float16 m;
+      uint32_t eb;
+      if (DEBUG) {
+        m = (_Float16)1.0f;
+        eb = 127 + 9;
+      } else {
+        split_scale(st.s, m, eb);
       }
-      if (xs || ws) {
-        _Float16 m;
-        uint32_t eb;
-        if (DEBUG) {
-          m = (_Float16)1.0f;
-          eb = 127 + 9;
-        } else {
-          split_scale(st.s, m, eb);
-        }
-        if (xs) { sm.st[buf].mX[tid] = m; sm.st[buf].eX[tid] = eb; }
-        else { sm.st[buf].mW[tid - 256] = m; sm.st[buf].eW[tid - 256] = eb; }
-      }
+      sm.st[buf].m[tid] = m;
+      sm.st[buf].e[tid] = eb;
     } else {
       *reinterpret_cast<uint4*>(&sm.st[buf].A[ldrow * S::kPitch + ldhalf * 16]) = st.a;
-      if (doB) *reinterpret_cast<uint4*>(&sm.st[buf].B[brow * S::kPitch + bhalf * 16]) = st.b;
-      if (xs) sm.st[buf].eX[tid] = st.s;
-      else if (ws) sm.st[buf].eW[tid - 256] = st.s;
+      *reinterpret_cast<uint4*>(&sm.st[buf].B[ldrow * S::kPitch + ldhalf * 16]) = st.b;
+      sm.st[buf].e[tid] = st.s;
     }
   };
 
@@ -187,12 +171,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void k2_gemm(
         const uint4* p = reinterpret_cast<const uint4*>(&sm.st[buf].B[col * S::kPitch + kh * 32]);
         const uint4 x0 = p[0], x1 = p[1];
         bf[j] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-        sb[j] = sm.st[buf].eW[col];
-        mw[j] = sm.st[buf].mW[col];
+        sb[j] = sm.st[buf].e[BM + col];
+        mw[j] = sm.st[buf].m[BM + col];
       } else {
         const uint4 x0 = *reinterpret_cast<const uint4*>(&sm.st[buf].B[col * S::kPitch + kh * 16]);
         bf[j] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, 0, 0, 0, 0};
-        sb[j] = (sm.st[buf].eW[col] >> (8 * kh)) & 0xFF;
+        sb[j] = (sm.st[buf].e[BM + col] >> (8 * kh)) & 0xFF;
       }
     }
 #pragma unroll
@@ -206,12 +190,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void k2_gemm(
         const uint4* p = reinterpret_cast<const uint4*>(&sm.st[buf].A[row * S::kPitch + kh * 32]);
         const uint4 x0 = p[0], x1 = p[1];
         af = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-        sa = sm.st[buf].eX[row];
+        sa = sm.st[buf].e[row];
         // mantissas of the 16 accumulator rows: rows 8*(a>>2) + 4*kh + (a&3)
         h2 mx[8];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const uint2 w = *reinterpret_cast<const uint2*>(&sm.st[buf].mX[wm + i * 32 + 8 * q + 4 * kh]);
+          const uint2 w = *reinterpret_cast<const uint2*>(&sm.st[buf].m[wm + i * 32 + 8 * q + 4 * kh]);
           mx[2 * q] = __builtin_bit_cast(h2, w.x);
           mx[2 * q + 1] = __builtin_bit_cast(h2, w.y);
         }
@@ -240,7 +224,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void k2_gemm(
       } else {
         const uint4 x0 = *reinterpret_cast<const uint4*>(&sm.st[buf].A[row * S::kPitch + kh * 16]);
         af = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, 0, 0, 0, 0};
-        sa = (sm.st[buf].eX[row] >> (8 * kh)) & 0xFF;
+        sa = (sm.st[buf].e[row] >> (8 * kh)) & 0xFF;
 #pragma unroll
         for (int j = 0; j < TJ; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf[j], acc[i][j], 4, 4, 0,
@@ -252,20 +236,19 @@ __global__ __launch_bounds__(NTHREADS, 1) void k2_gemm(
   // ---- main loop: loads two steps ahead, LDS double buffer, one barrier per step ----
   Stage r0, r1;
   gload(r0, 0);
-  if (nsteps > 1) gload(r1, 1);
+  gload(r1, 1);
   sstore(r0, 0);
   __syncthreads();
   for (int s = 0; s < nsteps; s += 2) {
     // even step s: r0 is free (stored), r1 holds step s+1
-    if (s + 2 < nsteps) gload(r0, s + 2);
+    gload(r0, s + 2);
     compute(0, s);
-    if (s + 1 < nsteps) sstore(r1, 1);
+    sstore(r1, 1);
     __syncthreads();
-    if (s + 1 >= nsteps) break;
     // odd step s+1: r1 is free, r0 holds step s+2
-    if (s + 3 < nsteps) gload(r1, s + 3);
+    gload(r1, s + 3);
     compute(1, s + 1);
-    if (s + 2 < nsteps) sstore(r0, 0);
+    sstore(r0, 0);
     __syncthreads();
   }
   if (DEBUG) return;
