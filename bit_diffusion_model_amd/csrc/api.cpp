@@ -48,12 +48,12 @@ static svdq_status check_layer(const svdq_layer* L, KernelLayer& kl) {
   if (L->rank < 0 || L->rank > SVDQ_MAX_RANK)
     return fail(SVDQ_EUNSUPPORTED, "rank must be in [0, %d] (got %d)", SVDQ_MAX_RANK, (int)L->rank);
   if (!L->inv_s || !L->qW || !L->sW) return fail(SVDQ_EINVAL, "layer inv_s, qW and sW must be non-NULL");
-  if (L->rank > 0 && (!L->Ld_hi || !L->Ld_lo || !L->L2))
-    return fail(SVDQ_EINVAL, "layer Ld_hi, Ld_lo and L2 must be non-NULL when rank > 0");
-  if (!aligned(L->inv_s, 16) || !aligned(L->qW, 16) || (L->rank > 0 && (!aligned(L->Ld_hi, 16) || !aligned(L->Ld_lo, 16))))
-    return fail(SVDQ_EINVAL, "layer inv_s, qW, Ld_hi and Ld_lo must be 16-byte aligned");
-  if (L->rank > 0 && !aligned(L->L2, 2)) return fail(SVDQ_EINVAL, "layer L2 must be 2-byte aligned");
-  kl = KernelLayer{L->K, L->N, L->rank, L->fmt, L->inv_s, L->Ld_hi, L->Ld_lo, L->L2, L->qW, L->sW};
+  if (L->rank > 0 && (!L->Ld_hi || !L->Ld_lo || !L->L2t))
+    return fail(SVDQ_EINVAL, "layer Ld_hi, Ld_lo and L2t must be non-NULL when rank > 0");
+  if (!aligned(L->inv_s, 16) || !aligned(L->qW, 16) ||
+      (L->rank > 0 && (!aligned(L->Ld_hi, 16) || !aligned(L->Ld_lo, 16) || !aligned(L->L2t, 16))))
+    return fail(SVDQ_EINVAL, "layer inv_s, qW, Ld_hi, Ld_lo and L2t must be 16-byte aligned");
+  kl = KernelLayer{L->K, L->N, L->rank, L->fmt, L->inv_s, L->Ld_hi, L->Ld_lo, L->L2t, L->qW, L->sW};
   return SVDQ_OK;
 }
 
@@ -69,7 +69,7 @@ static WsLayout ws_layout(const svdq_layer* L, int64_t M) {
   w.sx = qb;
   const size_t sb = rup((size_t)(L->K / group_of(L->fmt)) * (size_t)M * (L->fmt == SVDQ_INT4_G64 ? 2 : 1));
   w.la = w.sx + sb;
-  w.total = w.la + rup((size_t)M * (size_t)L->rank * 4);
+  w.total = w.la + rup((size_t)M * (size_t)((L->rank + 15) / 16 * 16) * 4);
   return w;
 }
 
@@ -97,8 +97,8 @@ svdq_status svdq_quantize_act_lora_down(const svdq_layer* layer, int64_t M, cons
   if (!X || !qX || !sX) return fail(SVDQ_EINVAL, "X, qX and sX must be non-NULL");
   if (kl.rank > 0 && !lora_act) return fail(SVDQ_EINVAL, "lora_act must be non-NULL when rank > 0");
   if (ldx < kl.K || ldx % 8 != 0) return fail(SVDQ_EINVAL, "ldx must be >= K and a multiple of 8");
-  if (!aligned(X, 16) || !aligned(qX, 16) || !aligned(sX, 2) || (lora_act && !aligned(lora_act, 4)))
-    return fail(SVDQ_EINVAL, "X and qX must be 16-byte aligned");
+  if (!aligned(X, 16) || !aligned(qX, 16) || !aligned(sX, 2) || (lora_act && !aligned(lora_act, 16)))
+    return fail(SVDQ_EINVAL, "X, qX and lora_act must be 16-byte aligned");
   hipError_t e = launch_k1(kl, M, X, ldx, qX, sX, lora_act, (hipStream_t)stream);
   if (e != hipSuccess) return fail(SVDQ_EHIP, "kernel 1 launch: %s", hipGetErrorString(e));
   return ok();
@@ -116,8 +116,9 @@ svdq_status svdq_gemm_w4a4_lora_up(const svdq_layer* layer, int64_t M, const uin
   if (!qX || !sX || !Y) return fail(SVDQ_EINVAL, "qX, sX and Y must be non-NULL");
   if (kl.rank > 0 && !lora_act) return fail(SVDQ_EINVAL, "lora_act must be non-NULL when rank > 0");
   if (ldy < kl.N) return fail(SVDQ_EINVAL, "ldy must be >= N");
-  if (!aligned(qX, 16) || !aligned(Y, ydtype == SVDQ_F32 ? 4 : 2) || !aligned(sX, 2))
-    return fail(SVDQ_EINVAL, "qX must be 16-byte aligned and Y aligned to its element size");
+  if (!aligned(qX, 16) || !aligned(Y, ydtype == SVDQ_F32 ? 4 : 2) || !aligned(sX, 2) ||
+      (lora_act && !aligned(lora_act, 16)))
+    return fail(SVDQ_EINVAL, "qX and lora_act must be 16-byte aligned and Y aligned to its element size");
   hipError_t e = launch_k2(kl, M, qX, sX, lora_act, Y, ldy, ydtype, (hipStream_t)stream);
   if (e != hipSuccess) return fail(SVDQ_EHIP, "kernel 2 launch: %s", hipGetErrorString(e));
   return ok();

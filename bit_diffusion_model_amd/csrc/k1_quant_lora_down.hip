@@ -48,6 +48,8 @@ __global__ __launch_bounds__(64 * K1_WAVES) void k1_quant_lora_down(
   const __amdgpu_buffer_rsrc_t rX = make_rsrc(X + m0 * ldx, (uint32_t)(((nrows - 1) * ldx + K) * 2));
   const __amdgpu_buffer_rsrc_t rS = make_rsrc(inv_s, (uint32_t)(K * 4));
   const uint32_t xoff = (uint32_t)(r16 * ldx + sub * 16) * 2;
+  const __amdgpu_buffer_rsrc_t rLh = make_rsrc(Ldh, (uint32_t)(rank * K * 2));
+  const __amdgpu_buffer_rsrc_t rLl = make_rsrc(Ldl, (uint32_t)(rank * K * 2));
 
   v4f acc[NT > 0 ? NT : 1];
 #pragma unroll
@@ -74,17 +76,16 @@ __global__ __launch_bounds__(64 * K1_WAVES) void k1_quant_lora_down(
     const uint4 cxa = xa, cxb = xb;
     if (c + K1_WAVES < nchunks) fetch(c + K1_WAVES);
 
-    // low-rank down projection operands for this chunk (issued early)
+    // low-rank down projection operands for this chunk (issued early); rows past the
+    // rank read as zeros through the range check
     uint4 hA[NT > 0 ? NT : 1], hB[NT > 0 ? NT : 1], lA[NT > 0 ? NT : 1], lB[NT > 0 ? NT : 1];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const int n = t * 16 + r16;
-      hA[t] = hB[t] = lA[t] = lB[t] = make_uint4(0, 0, 0, 0);
-      if (n < rank) {
-        const uint4* ph = reinterpret_cast<const uint4*>(Ldh + (int64_t)n * K + k0);
-        const uint4* pl = reinterpret_cast<const uint4*>(Ldl + (int64_t)n * K + k0);
-        hA[t] = ph[0]; hB[t] = ph[1]; lA[t] = pl[0]; lB[t] = pl[1];
-      }
+      const uint32_t o = (uint32_t)((t * 16 + r16) * K + k0) * 2;
+      hA[t] = buf_load16(rLh, o);
+      hB[t] = buf_load16(rLh, o + 16);
+      lA[t] = buf_load16(rLl, o);
+      lB[t] = buf_load16(rLl, o + 16);
     }
 
     float xh[16];
@@ -106,19 +107,35 @@ __global__ __launch_bounds__(64 * K1_WAVES) void k1_quant_lora_down(
       const float sf = (float)sh;
       const float rcp = 1.0f / sf;
       const float hs = 0.5f * sf;
+      // Common path: q0 = rint(x * rcp).  x * rcp differs from x / s by at most
+      // |x / s| * 2^-23 < 2^-19 (|x / s| < 16 even for subnormal fp16 scales), so q0 is
+      // the correctly rounded quotient unless x / s lies within 2^-17 of a half
+      // integer.  Such lanes are flagged and, if any lane of the wave has one, the
+      // chunk takes the exact correction: x - q0 * s is exact near s / 2, so comparing
+      // its magnitude with s / 2 decides the rounding, ties to even.
+      float q[16];
+      bool near = false;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float q0 = rintf(xh[i] * rcp);
-        // x - q0 * s is exact whenever it is near s / 2, so this decides the exact
-        // quotient's rounding, ties to even.
-        const float e = fmaf(-q0, sf, xh[i]);
-        const float ae = fabsf(e);
-        const bool odd = (((int)q0) & 1) != 0;
-        const bool away = (ae > hs) || (ae == hs && odd);
-        float q = away ? q0 + copysignf(1.0f, e) : q0;
-        q = fminf(fmaxf(q, -7.0f), 7.0f);
-        const int qi = (sf == 0.0f) ? 0 : (int)q;
-        nib[i] = (uint32_t)((qi < 0 ? 8 : 0) | (qi < 0 ? -qi : qi));
+        const float t = xh[i] * rcp;
+        q[i] = rintf(t);
+        near |= fabsf(t - q[i]) > 0.49999237f;  // 0.5 - 2^-17
+      }
+      if (__builtin_amdgcn_ballot_w64(near) != 0) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float e = fmaf(-q[i], sf, xh[i]);
+          const float ae = fabsf(e);
+          const int odd = ((int)q[i]) & 1;
+          const int away = (int)(ae > hs) | ((int)(ae == hs) & odd);
+          q[i] = q[i] + (float)away * copysignf(1.0f, e);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float qc = __builtin_amdgcn_fmed3f(q[i], -7.0f, 7.0f);
+        const uint32_t mag = (uint32_t)fabsf(qc);
+        nib[i] = (sf == 0.0f) ? 0u : (mag | (qc < 0.0f ? 8u : 0u));
       }
       if (row_ok && sub == 0)
         reinterpret_cast<uint16_t*>(sXv)[(int64_t)c * M + row] = __builtin_bit_cast(uint16_t, sh);
@@ -174,13 +191,16 @@ __global__ __launch_bounds__(64 * K1_WAVES) void k1_quant_lora_down(
 #pragma unroll
       for (int i = 0; i < 4; ++i) red[wave][4 * sub + i][t * 16 + r16] = acc[t][i];
     __syncthreads();
-    for (int idx = threadIdx.x; idx < 16 * rank; idx += 64 * K1_WAVES) {
-      const int rr = idx / rank, cc = idx - rr * rank;
+    // all NT * 16 columns are written; those past the rank are zero (their factor
+    // rows read as zeros)
+    constexpr int R16 = NT * 16;
+    for (int idx = threadIdx.x; idx < 16 * R16; idx += 64 * K1_WAVES) {
+      const int rr = idx / R16, cc = idx - rr * R16;
       if (m0 + rr < M) {
         float v = 0.f;
 #pragma unroll
         for (int w = 0; w < K1_WAVES; ++w) v += red[w][rr][cc];
-        lora_act[(m0 + rr) * rank + cc] = v;
+        lora_act[(m0 + rr) * R16 + cc] = v;
       }
     }
   }

@@ -255,31 +255,30 @@ __global__ __launch_bounds__(NTHREADS, 2) void k2_gemm(
 
   // ---- low-rank up projection: acc += lora_act[rows, :] L2[:, cols] -------------------
   // v_mfma_f32_32x32x16_bf16 with a bf16 hi/lo split of lora_act (L2 is bf16 already).
+  // Both operands are rows of 16-padded arrays (lora_act [M][R16] fp32, L2t [N][R16]
+  // bf16): lane (row or column l & 31, kh) reads the 8 consecutive ranks 16 t + 8 kh..,
+  // and rows past M / columns past N read as zeros through the range check.
   if (rank > 0) {
-    for (int k0 = 0; k0 < rank; k0 += 16) {
+    const int R16 = (rank + 15) & ~15;
+    const __amdgpu_buffer_rsrc_t rL = make_rsrc(lora_act + m0 * R16, (uint32_t)(rowsA * R16 * 4));
+    const __amdgpu_buffer_rsrc_t rU = make_rsrc(L2 + n0 * R16, (uint32_t)(rowsB * R16 * 2));
+    for (int k0 = 0; k0 < R16; k0 += 16) {
       v8bf bl[TJ];
 #pragma unroll
-      for (int j = 0; j < TJ; ++j) {
-        const int64_t c = n0 + wn + j * 32 + l32;
-        uint16_t t[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int k = k0 + 8 * kh + u;
-          t[u] = (k < rank && c < nlim) ? L2[(int64_t)k * N + c] : (uint16_t)0;
-        }
-        bl[j] = __builtin_bit_cast(v8bf, t);
-      }
+      for (int j = 0; j < TJ; ++j)
+        bl[j] = __builtin_bit_cast(v8bf, buf_load16(rU, (uint32_t)((wn + j * 32 + l32) * R16 + k0 + 8 * kh) * 2));
 #pragma unroll
       for (int i = 0; i < TI; ++i) {
-        const int64_t r = m0 + wm + i * 32 + l32;
+        const uint32_t o = (uint32_t)((wm + i * 32 + l32) * R16 + k0 + 8 * kh) * 4;
+        const uint4 v0 = buf_load16(rL, o), v1 = buf_load16(rL, o + 16);
+        const float v[8] = {__uint_as_float(v0.x), __uint_as_float(v0.y), __uint_as_float(v0.z), __uint_as_float(v0.w),
+                            __uint_as_float(v1.x), __uint_as_float(v1.y), __uint_as_float(v1.z), __uint_as_float(v1.w)};
         uint16_t hi[8], lo[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          const int k = k0 + 8 * kh + u;
-          const float v = (k < rank && r < mlim) ? lora_act[r * rank + k] : 0.0f;
-          const uint32_t hb = f32_to_bf16_rne(v);
+          const uint32_t hb = f32_to_bf16_rne(v[u]);
           hi[u] = (uint16_t)hb;
-          lo[u] = (uint16_t)f32_to_bf16_rne(v - __uint_as_float(hb << 16));
+          lo[u] = (uint16_t)f32_to_bf16_rne(v[u] - __uint_as_float(hb << 16));
         }
         const v8bf ah = __builtin_bit_cast(v8bf, hi), al = __builtin_bit_cast(v8bf, lo);
 #pragma unroll
@@ -316,11 +315,11 @@ hipError_t launch_k2(const KernelLayer& L, int64_t M, const uint8_t* qX, const v
   const dim3 grid((unsigned)((L.N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM)), block(NTHREADS);
   if (L.fmt == 0)
     hipLaunchKernelGGL((k2_gemm<0, false>), grid, block, 0, st, qX, sX, M, L.qW, L.sW, L.N, L.K,
-                       lora_act, L.L2, L.rank, Y, ldy, ydtype, (int64_t)0, (int64_t)0, M, L.N,
+                       lora_act, L.L2t, L.rank, Y, ldy, ydtype, (int64_t)0, (int64_t)0, M, L.N,
                        (int32_t*)nullptr);
   else
     hipLaunchKernelGGL((k2_gemm<1, false>), grid, block, 0, st, qX, sX, M, L.qW, L.sW, L.N, L.K,
-                       lora_act, L.L2, L.rank, Y, ldy, ydtype, (int64_t)0, (int64_t)0, M, L.N,
+                       lora_act, L.L2t, L.rank, Y, ldy, ydtype, (int64_t)0, (int64_t)0, M, L.N,
                        (int32_t*)nullptr);
   return hipGetLastError();
 }

@@ -12,7 +12,7 @@ struct KernelLayer {
   const float* inv_s;
   const uint16_t* Ld_hi;
   const uint16_t* Ld_lo;
-  const uint16_t* L2;
+  const uint16_t* L2t;
   const uint8_t* qW;
   const void* sW;
 };

@@ -32,7 +32,7 @@ class _Layer(ctypes.Structure):
     _fields_ = [
         ("K", ctypes.c_int64), ("N", ctypes.c_int64), ("rank", ctypes.c_int32), ("fmt", ctypes.c_int32),
         ("inv_s", ctypes.c_void_p), ("Ld_hi", ctypes.c_void_p), ("Ld_lo", ctypes.c_void_p),
-        ("L2", ctypes.c_void_p), ("qW", ctypes.c_void_p), ("sW", ctypes.c_void_p),
+        ("L2t", ctypes.c_void_p), ("qW", ctypes.c_void_p), ("sW", ctypes.c_void_p),
     ]
 
 
@@ -40,7 +40,7 @@ _lib = None
 
 EXPORTS = [
     "svdq_last_error", "svdq_act_absmax", "svdq_weight_sizes", "svdq_pack_weights",
-    "svdq_quantize_weights", "svdq_concat_lora", "svdq_lowrank_down_factors",
+    "svdq_quantize_weights", "svdq_concat_lora", "svdq_prepare_lowrank",
     "svdq_quantize_act_lora_down", "svdq_gemm_w4a4_lora_up", "svdq_workspace_bytes",
     "svdq_linear_forward", "svdq_debug_group_sums",
 ]
@@ -62,7 +62,7 @@ def lib():
         "svdq_pack_weights": (I32, [I64, I64, P, P, F, I32, I32, P, P, P, P, P, P, P]),
         "svdq_quantize_weights": (I32, [I64, I64, P, I32, P, P]),
         "svdq_concat_lora": (I32, [I64, I64, P, I32, P, P, I32, P, P, F, P, P]),
-        "svdq_lowrank_down_factors": (I32, [I64, I32, P, P, P, P]),
+        "svdq_prepare_lowrank": (I32, [I64, I64, I32, P, P, P, P, P, P]),
         "svdq_quantize_act_lora_down": (I32, [P, I64, P, I64, P, P, P, P]),
         "svdq_gemm_w4a4_lora_up": (I32, [P, I64, P, P, P, P, I64, I32, P]),
         "svdq_workspace_bytes": (ctypes.c_size_t, [P, I64]),
@@ -159,14 +159,23 @@ def concat_lora(p: HostPack, A_bits: np.ndarray, B_bits: np.ndarray, scale: floa
     return HostPack(p.K, p.N, r, p.fmt, p.s, p.inv_s, L1t, L2, p.qW, p.sW, p.R)
 
 
-def lowrank_down_factors(inv_s: np.ndarray, L1t: np.ndarray):
+def r16(rank: int) -> int:
+    """rank rounded up to a multiple of 16 (padded width of lora_act and L2t)."""
+    return (rank + 15) // 16 * 16
+
+
+def prepare_lowrank(inv_s: np.ndarray, L1t: np.ndarray, L2: np.ndarray):
+    """Device layouts of the low-rank branch: (Ld_hi, Ld_lo [rank][K], L2t [N][R16])."""
     inv = np.ascontiguousarray(inv_s, dtype=np.float32)
     L1t = np.ascontiguousarray(L1t, dtype=np.uint16)
+    L2 = np.ascontiguousarray(L2, dtype=np.uint16)
     r, K = L1t.shape
+    N = L2.shape[1]
     hi = np.zeros((r, K), np.uint16)
     lo = np.zeros((r, K), np.uint16)
-    _check(lib().svdq_lowrank_down_factors(K, r, _ptr(inv), _ptr(L1t), _ptr(hi), _ptr(lo)))
-    return hi, lo
+    L2t = np.zeros((N, r16(r)), np.uint16)
+    _check(lib().svdq_prepare_lowrank(K, N, r, _ptr(inv), _ptr(L1t), _ptr(L2), _ptr(hi), _ptr(lo), _ptr(L2t)))
+    return hi, lo, L2t
 
 
 # ------------------------------------------------------------------ device side
@@ -208,16 +217,16 @@ class PackedLinear:
         self.device = device
         self.inv_s = _upload(np.asarray(inv_s, np.float32), device)
         if rank > 0:
-            hi, lo = lowrank_down_factors(inv_s, L1t)
+            hi, lo, L2t = prepare_lowrank(inv_s, L1t, L2)
             self.Ld_hi = _upload(hi, device)
             self.Ld_lo = _upload(lo, device)
-            self.L2 = _upload(np.asarray(L2, np.uint16), device)
+            self.L2t = _upload(L2t, device)
         else:
-            self.Ld_hi = self.Ld_lo = self.L2 = None
+            self.Ld_hi = self.Ld_lo = self.L2t = None
         self.qW = _upload(np.asarray(qW, np.uint8), device)
         self.sW = _upload(sW, device)
         self._c = _Layer(self.K, self.N, self.rank, self.fmt, _dptr(self.inv_s), _dptr(self.Ld_hi),
-                         _dptr(self.Ld_lo), _dptr(self.L2), _dptr(self.qW), _dptr(self.sW))
+                         _dptr(self.Ld_lo), _dptr(self.L2t), _dptr(self.qW), _dptr(self.sW))
 
     @classmethod
     def from_host_pack(cls, p: HostPack, device="cuda:0"):
@@ -235,7 +244,7 @@ class PackedLinear:
         qX = torch.empty((M, self.K // 2), dtype=torch.uint8, device=self.device)
         sdt = torch.int16 if self.fmt == INT4_G64 else torch.uint8
         sX = torch.empty((self.K // self.group, M), dtype=sdt, device=self.device)
-        la = torch.empty((M, self.rank), dtype=torch.float32, device=self.device) if self.rank else None
+        la = torch.empty((M, r16(self.rank)), dtype=torch.float32, device=self.device) if self.rank else None
         return qX, sX, la
 
     def quantize_act(self, X, out=None):

@@ -59,14 +59,15 @@ typedef enum { SVDQ_F32 = 0, SVDQ_BF16 = 1 } svdq_dtype;
 #define SVDQ_MAX_RANK 128
 
 /* Device-resident description of one packed layer (all pointers device memory,
- * owned by the caller, produced by svdq_pack_weights + svdq_lowrank_down_factors):
+ * owned by the caller, produced by svdq_pack_weights + svdq_prepare_lowrank).
+ * R16 below is rank rounded up to a multiple of 16.
  *   inv_s  [K]        fp32  reciprocal smoothing factor, fp32(1 / fp32(s))
  *   Ld_hi  [rank][K]  bf16  high part of (diag(inv_s) L1)^T
  *   Ld_lo  [rank][K]  bf16  low part, so Ld_hi + Ld_lo = diag(inv_s) L1 to ~2^-17
- *   L2     [rank][N]  bf16  up projection
+ *   L2t    [N][R16]   bf16  up projection transposed (L2^T), columns >= rank zero
  *   qW     [N][K/2]   u8    residual codes, row n = output channel n along K
  *   sW     [K/G][N]   fp16 bits (INT4) or E8M0 bytes (MXFP4), group-major
- * Ld_hi/Ld_lo/L2 may be NULL iff rank == 0. */
+ * Ld_hi/Ld_lo/L2t may be NULL iff rank == 0. */
 typedef struct svdq_layer {
   int64_t K, N;
   int32_t rank;
@@ -74,7 +75,7 @@ typedef struct svdq_layer {
   const float* inv_s;
   const uint16_t* Ld_hi;
   const uint16_t* Ld_lo;
-  const uint16_t* L2;
+  const uint16_t* L2t;
   const uint8_t* qW;
   const void* sW;
 } svdq_layer;
@@ -131,12 +132,15 @@ svdq_status svdq_concat_lora(int64_t K, int64_t N, const float* s, int32_t rank,
                              const uint16_t* A, const uint16_t* B, float lora_scale,
                              uint16_t* L1t_out, uint16_t* L2_out);
 
-/* Offline fold of the runtime smoothing into the down projection:
- * (X diag(s)^-1) L1 = X (diag(inv_s) L1).  For each j < rank, k < K:
- *   v = inv_s[k] * L1t[j][k] (fp32), hi = bf16_rne(v), lo = bf16_rne(v - hi).
- * Host pointers; outputs hi_out, lo_out [rank][K] bf16. */
-svdq_status svdq_lowrank_down_factors(int64_t K, int32_t rank, const float* inv_s,
-                                      const uint16_t* L1t, uint16_t* hi_out, uint16_t* lo_out);
+/* Offline device layouts of the low-rank branch.  The runtime smoothing is folded into
+ * the down projection, (X diag(s)^-1) L1 = X (diag(inv_s) L1): for j < rank, k < K,
+ *   v = inv_s[k] * L1t[j][k] (fp32), hi = bf16_rne(v), lo = bf16_rne(v - hi);
+ * and the up projection is transposed and zero-padded: L2t[n][j] = L2[j][n] (j < rank),
+ * 0 (rank <= j < R16).  Host pointers; outputs hi_out, lo_out [rank][K], L2t_out
+ * [N][R16] bf16. */
+svdq_status svdq_prepare_lowrank(int64_t K, int64_t N, int32_t rank, const float* inv_s,
+                                 const uint16_t* L1t, const uint16_t* L2, uint16_t* hi_out,
+                                 uint16_t* lo_out, uint16_t* L2t_out);
 
 /* ---------------------------------------------------------------- device side ---- */
 
@@ -146,7 +150,8 @@ svdq_status svdq_lowrank_down_factors(int64_t K, int32_t rank, const float* inv_
  *   X        device bf16 [M][ldx], 16-byte aligned rows (ldx % 8 == 0)
  *   qX       device u8 [M][K/2]           4-bit codes of X_hat = X diag(inv_s)
  *   sX       device [K/G][M]              fp16 bits (INT4) or E8M0 bytes (MXFP4)
- *   lora_act device fp32 [M][rank]        X_hat L1 (unused when rank == 0)
+ *   lora_act device fp32 [M][R16]         X_hat L1, columns >= rank written as zero
+ *                                         (unused when rank == 0)
  * M == 0 is a no-op.  EINVAL on NULL / misalignment / ldx < K; EHIP on launch error. */
 svdq_status svdq_quantize_act_lora_down(const svdq_layer* layer, int64_t M, const uint16_t* X,
                                         int64_t ldx, uint8_t* qX, void* sX, float* lora_act,

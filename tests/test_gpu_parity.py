@@ -50,7 +50,8 @@ def test_kernel1_codes_scales_lora(shape):
     np.testing.assert_array_equal(sX.cpu().numpy().view(sX_ref.dtype), sX_ref)
     if r:
         la_g = la.cpu().numpy().astype(np.float64)
-        assert np.all(np.abs(la_g - la_ref) <= lora_bound(Xh, p["L1b"]))
+        assert la_g.shape[1] == svdq.r16(r) and not la_g[:, r:].any()
+        assert np.all(np.abs(la_g[:, :r] - la_ref) <= lora_bound(Xh, p["L1b"]))
 
 
 @pytest.mark.parametrize("shape", [s for s in SHAPES if s[4] == "int4"], ids=_ids)

@@ -133,15 +133,19 @@ def test_concat_lora_bit_exact():
         np.testing.assert_array_equal(f.L2, o["L2_bits"])
 
 
-def test_lowrank_down_factors_split():
+def test_prepare_lowrank_layouts():
     rng = np.random.default_rng(2)
     from bit_diffusion_model_amd.workloads import bf16_bits_from_f64
     L1t = bf16_bits_from_f64(rng.standard_normal((5, 256)))
+    L2 = bf16_bits_from_f64(rng.standard_normal((5, 40)))
     inv = rng.uniform(0.05, 20, 256).astype(np.float32)
-    hi, lo = svdq.lowrank_down_factors(inv, L1t)
+    hi, lo, L2t = svdq.prepare_lowrank(inv, L1t, L2)
     v = inv.astype(np.float64)[None, :] * bf16_to_f64(L1t)
     rec = bf16_to_f64(hi) + bf16_to_f64(lo)
     assert np.all(np.abs(rec - v) <= 2.0 ** -16 * np.abs(v))
+    assert L2t.shape == (40, 16)
+    np.testing.assert_array_equal(L2t[:, :5], L2.T)
+    assert not L2t[:, 5:].any()
 
 
 # ------------------------------------------------------------------ error paths
@@ -185,4 +189,4 @@ def test_device_entry_points_validate_on_host():
     assert L.svdq_gemm_w4a4_lora_up(ref, 4, 16, 16, 16, 16, 64, 5, None) == 2
     assert L.svdq_linear_forward(ref, 4, 16, 256, 16, 64, 0, 256, 10, None) == 1 and "workspace" in _err()
     assert L.svdq_debug_group_sums(ref, 4, 16, 0, 0, 5, 4, 16, None) == 1 and "window" in _err()
-    assert L.svdq_workspace_bytes(ref, 100) >= 100 * 128 + 4 * 100 * 2 + 100 * 8 * 4
+    assert L.svdq_workspace_bytes(ref, 100) >= 100 * 128 + 4 * 100 * 2 + 100 * 16 * 4
