@@ -71,7 +71,7 @@ struct Stage {
 };
 
 template <int FMT, bool DEBUG>
-__global__ __launch_bounds__(NTHREADS, 2) void k2_gemm(
+__global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void k2_gemm(
     const uint8_t* __restrict__ qX, const void* __restrict__ sXv, int64_t M,
     const uint8_t* __restrict__ qW, const void* __restrict__ sWv, int64_t N, int64_t K,
     const float* __restrict__ lora_act, const uint16_t* __restrict__ L2, int rank,
@@ -161,8 +161,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void k2_gemm(
     for (int j = 0; j < TJ; ++j) acc[i][j] = v16f{};
 
   auto compute = [&](int buf, int s) {
-    v8i bf[TJ];
-    uint32_t sb[TJ];
+    v8i bf[TJ], af[TI];
+    uint32_t sb[TJ], sa[TI];
     _Float16 mw[TJ];
 #pragma unroll
     for (int j = 0; j < TJ; ++j) {
@@ -181,16 +181,30 @@ __global__ __launch_bounds__(NTHREADS, 2) void k2_gemm(
     }
 #pragma unroll
     for (int i = 0; i < TI; ++i) {
-      // keep each row tile's fragment reads next to its MFMAs (bounds live registers)
-      __asm__ volatile("" ::: "memory");
       const int row = wm + i * 32 + l32;
-      v8i af;
-      uint32_t sa;
       if (FMT == 0) {
         const uint4* p = reinterpret_cast<const uint4*>(&sm.st[buf].A[row * S::kPitch + kh * 32]);
         const uint4 x0 = p[0], x1 = p[1];
-        af = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-        sa = sm.st[buf].e[row];
+        af[i] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+        sa[i] = sm.st[buf].e[row];
+      } else {
+        const uint4 x0 = *reinterpret_cast<const uint4*>(&sm.st[buf].A[row * S::kPitch + kh * 16]);
+        af[i] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, 0, 0, 0, 0};
+        sa[i] = (sm.st[buf].e[row] >> (8 * kh)) & 0xFF;
+      }
+    }
+    if (FMT == 0) {
+      // all four group-sum MFMAs first (separate result registers), then the rescale
+      // epilogues, so each epilogue overlaps the MFMAs still in flight
+      v16f p[TI][TJ];
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+          p[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], v16f{}, 0, 0, 0, (int)sa[i], 0,
+                                                                   (int)sb[j]);
+#pragma unroll
+      for (int i = 0; i < TI; ++i) {
         // mantissas of the 16 accumulator rows: rows 8*(a>>2) + 4*kh + (a&3)
         h2 mx[8];
 #pragma unroll
@@ -201,35 +215,40 @@ __global__ __launch_bounds__(NTHREADS, 2) void k2_gemm(
         }
 #pragma unroll
         for (int j = 0; j < TJ; ++j) {
-          const v16f p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf[j], v16f{}, 0, 0, 0,
-                                                                        (int)sa, 0, (int)sb[j]);
           if (DEBUG) {
 #pragma unroll
             for (int a = 0; a < 16; ++a) {
               const int64_t r = m0 + wm + i * 32 + 8 * (a >> 2) + 4 * kh + (a & 3);
               const int64_t c = n0 + wn + j * 32 + l32;
               if (r < mlim && c < nlim)
-                dbg[((int64_t)s * (mlim - mbase) + (r - mbase)) * (nlim - nbase) + (c - nbase)] = (int32_t)p[a];
+                dbg[((int64_t)s * (mlim - mbase) + (r - mbase)) * (nlim - nbase) + (c - nbase)] = (int32_t)p[i][j][a];
             }
           } else {
             const h2 mw2 = h2{mw[j], mw[j]};
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
               const h2 sc = mx[q] * mw2;
-              acc[i][j][2 * q] = fmaf(p[2 * q], (float)sc.x, acc[i][j][2 * q]);
-              acc[i][j][2 * q + 1] = fmaf(p[2 * q + 1], (float)sc.y, acc[i][j][2 * q + 1]);
+              acc[i][j][2 * q] = fmaf(p[i][j][2 * q], (float)sc.x, acc[i][j][2 * q]);
+              acc[i][j][2 * q + 1] = fmaf(p[i][j][2 * q + 1], (float)sc.y, acc[i][j][2 * q + 1]);
             }
           }
         }
-      } else {
-        const uint4 x0 = *reinterpret_cast<const uint4*>(&sm.st[buf].A[row * S::kPitch + kh * 16]);
-        af = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, 0, 0, 0, 0};
-        sa = (sm.st[buf].e[row] >> (8 * kh)) & 0xFF;
+      }
+      if (!DEBUG) {
+        // schedule: MFMA t+1 is issued ahead of epilogue t (24 VALU ops each)
+#pragma unroll
+        for (int t = 0; t < TI * TJ; ++t) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 24, 0);  // then VALU
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
 #pragma unroll
         for (int j = 0; j < TJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf[j], acc[i][j], 4, 4, 0,
-                                                                     (int)sa, 0, (int)sb[j]);
-      }
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], 4, 4, 0, (int)sa[i], 0,
+                                                                     (int)sb[j]);
     }
   };
 
