@@ -63,6 +63,46 @@ def traffic_entry():
     return d.get("bytes_per_launch")
 
 
+CALIB_BYTES = 512 << 20
+
+
+def _pmc_means(path):
+    """Mean counter value per kernel-name prefix from a rocprofv3 counter CSV."""
+    import csv
+    import collections
+
+    acc = collections.defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        name = r["Kernel_Name"]
+        key = "k2" if "k2_gemm<0, false>" in name else ("copy" if "copyBuffer" in name or "copy" in name.lower() else None)
+        if key:
+            acc[key].append(float(r["Counter_Value"]))
+    # the calibration copy is the largest copy dispatch (uploads may also use copy kernels)
+    return {k: ((max(v) if k == "copy" else sum(v) / len(v)), len(v)) for k, v in acc.items()}
+
+
+def write_traffic(fetch_csv, write_csv):
+    """Kernel 2's HBM traffic per launch: FETCH_SIZE and WRITE_SIZE (KiB per dispatch)
+    of kernel 2, each divided by the same counter's reading per byte for a plain copy of
+    CALIB_BYTES (read and written once each)."""
+    f = _pmc_means(fetch_csv)
+    w = _pmc_means(write_csv)
+    ffac = f["copy"][0] * 1024.0 / CALIB_BYTES
+    wfac = w["copy"][0] * 1024.0 / CALIB_BYTES
+    fetch_b = f["k2"][0] * 1024.0 / ffac
+    write_b = w["k2"][0] * 1024.0 / wfac
+    d = {"kernel": "k2_gemm<INT4>", "workload": "FLUX.1 QKV projection M=4608 K=3072 N=9216 r=32, fp32 Y",
+         "k2_source_hash": source_hash(K2_SOURCES), "fetch_kib_raw": f["k2"][0], "write_kib_raw": w["k2"][0],
+         "copy_fetch_factor": ffac, "copy_write_factor": wfac, "fetch_bytes": fetch_b, "write_bytes": write_b,
+         "bytes_per_launch": fetch_b + write_b, "dispatches": f["k2"][1],
+         "command": "rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -- "
+                    "python bench.py --steps 3 --warmup 1 --no-cpu-baseline --calib-copy"}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(d, fh, indent=1)
+    print(json.dumps(d))
+
+
 def cpu_baseline(wl_name, rows):
     """The oracle forward (unchanged, numpy fp64 / exact integers) on a bounded sample:
     `rows` tokens of the workload against all output columns.  Pack artifacts are
@@ -107,7 +147,16 @@ def main():
     ap.add_argument("--ydtype", default="f32", choices=["f32", "bf16"])
     ap.add_argument("--cpu-rows", type=int, default=4608)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="after timing, run one plain device copy of 512 MiB (counter calibration)")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="compute kernel 2's HBM bytes per launch from two rocprofv3 --pmc CSVs "
+                         "(FETCH_SIZE, WRITE_SIZE) of runs made with --calib-copy, write the "
+                         "summary JSON, and exit")
     args = ap.parse_args()
+    if args.write_traffic:
+        write_traffic(*args.write_traffic)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "this build measures one GPU: the layer shards along tokens with no "
@@ -208,6 +257,11 @@ def main():
                     "k2_TOPS": round(k2_tops, 2), "rank0_ms": round(ms0, 5),
                     "lowrank_overhead": round(ms / ms0 - 1.0, 4)},
     }
+    if args.calib_copy:
+        src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline: oracle on {args.cpu_rows} tokens")
         out["cpu_baseline"] = cpu_baseline(args.workload, min(args.cpu_rows, M))
