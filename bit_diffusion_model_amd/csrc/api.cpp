@@ -62,10 +62,14 @@ static size_t rup(size_t x) { return (x + 255) & ~size_t(255); }
 struct WsLayout {
   size_t qx, sx, la, total;
 };
+// The forward path keeps INT4 activation codes as FP8 bytes (one per code, [M][K]) so
+// that kernel 2 copies them to LDS without expanding; MXFP4 codes stay packed.
+static bool fwd_fp8_codes(const svdq_layer* L) { return L->fmt == SVDQ_INT4_G64; }
+
 static WsLayout ws_layout(const svdq_layer* L, int64_t M) {
   WsLayout w;
   w.qx = 0;
-  const size_t qb = rup((size_t)M * (size_t)(L->K / 2));
+  const size_t qb = rup((size_t)M * (size_t)(fwd_fp8_codes(L) ? L->K : L->K / 2));
   w.sx = qb;
   const size_t sb = rup((size_t)(L->K / group_of(L->fmt)) * (size_t)M * (L->fmt == SVDQ_INT4_G64 ? 2 : 1));
   w.la = w.sx + sb;
@@ -86,9 +90,12 @@ size_t svdq_workspace_bytes(const svdq_layer* layer, int64_t M) {
   return ws_layout(layer, M).total;
 }
 
-svdq_status svdq_quantize_act_lora_down(const svdq_layer* layer, int64_t M, const uint16_t* X,
-                                        int64_t ldx, uint8_t* qX, void* sX, float* lora_act,
-                                        void* stream) {
+}  // extern "C"
+
+namespace svdq {
+
+static svdq_status run_k1(const svdq_layer* layer, int64_t M, const uint16_t* X, int64_t ldx,
+                          uint8_t* qX, void* sX, float* lora_act, bool fp8_codes, void* stream) {
   KernelLayer kl;
   svdq_status st = check_layer(layer, kl);
   if (st != SVDQ_OK) return st;
@@ -99,14 +106,14 @@ svdq_status svdq_quantize_act_lora_down(const svdq_layer* layer, int64_t M, cons
   if (ldx < kl.K || ldx % 8 != 0) return fail(SVDQ_EINVAL, "ldx must be >= K and a multiple of 8");
   if (!aligned(X, 16) || !aligned(qX, 16) || !aligned(sX, 2) || (lora_act && !aligned(lora_act, 16)))
     return fail(SVDQ_EINVAL, "X, qX and lora_act must be 16-byte aligned");
-  hipError_t e = launch_k1(kl, M, X, ldx, qX, sX, lora_act, (hipStream_t)stream);
+  hipError_t e = launch_k1(kl, M, X, ldx, qX, sX, lora_act, fp8_codes, (hipStream_t)stream);
   if (e != hipSuccess) return fail(SVDQ_EHIP, "kernel 1 launch: %s", hipGetErrorString(e));
   return ok();
 }
 
-svdq_status svdq_gemm_w4a4_lora_up(const svdq_layer* layer, int64_t M, const uint8_t* qX,
-                                   const void* sX, const float* lora_act, void* Y, int64_t ldy,
-                                   int32_t ydtype, void* stream) {
+static svdq_status run_k2(const svdq_layer* layer, int64_t M, const uint8_t* qX, const void* sX,
+                          const float* lora_act, void* Y, int64_t ldy, int32_t ydtype,
+                          bool fp8_codes, void* stream) {
   KernelLayer kl;
   svdq_status st = check_layer(layer, kl);
   if (st != SVDQ_OK) return st;
@@ -119,9 +126,25 @@ svdq_status svdq_gemm_w4a4_lora_up(const svdq_layer* layer, int64_t M, const uin
   if (!aligned(qX, 16) || !aligned(Y, ydtype == SVDQ_F32 ? 4 : 2) || !aligned(sX, 2) ||
       (lora_act && !aligned(lora_act, 16)))
     return fail(SVDQ_EINVAL, "qX and lora_act must be 16-byte aligned and Y aligned to its element size");
-  hipError_t e = launch_k2(kl, M, qX, sX, lora_act, Y, ldy, ydtype, (hipStream_t)stream);
+  hipError_t e = launch_k2(kl, M, qX, sX, lora_act, Y, ldy, ydtype, fp8_codes, (hipStream_t)stream);
   if (e != hipSuccess) return fail(SVDQ_EHIP, "kernel 2 launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace svdq
+
+extern "C" {
+
+svdq_status svdq_quantize_act_lora_down(const svdq_layer* layer, int64_t M, const uint16_t* X,
+                                        int64_t ldx, uint8_t* qX, void* sX, float* lora_act,
+                                        void* stream) {
+  return run_k1(layer, M, X, ldx, qX, sX, lora_act, false, stream);
+}
+
+svdq_status svdq_gemm_w4a4_lora_up(const svdq_layer* layer, int64_t M, const uint8_t* qX,
+                                   const void* sX, const float* lora_act, void* Y, int64_t ldy,
+                                   int32_t ydtype, void* stream) {
+  return run_k2(layer, M, qX, sX, lora_act, Y, ldy, ydtype, false, stream);
 }
 
 svdq_status svdq_linear_forward(const svdq_layer* layer, int64_t M, const uint16_t* X, int64_t ldx,
@@ -139,9 +162,10 @@ svdq_status svdq_linear_forward(const svdq_layer* layer, int64_t M, const uint16
   uint8_t* qX = base + w.qx;
   void* sX = base + w.sx;
   float* la = kl.rank > 0 ? reinterpret_cast<float*>(base + w.la) : nullptr;
-  st = svdq_quantize_act_lora_down(layer, M, X, ldx, qX, sX, la, stream);
+  const bool f8 = fwd_fp8_codes(layer);
+  st = run_k1(layer, M, X, ldx, qX, sX, la, f8, stream);
   if (st != SVDQ_OK) return st;
-  return svdq_gemm_w4a4_lora_up(layer, M, qX, sX, la, Y, ldy, ydtype, stream);
+  return run_k2(layer, M, qX, sX, la, Y, ldy, ydtype, f8, stream);
 }
 
 svdq_status svdq_debug_group_sums(const svdq_layer* layer, int64_t M, const uint8_t* qX, int64_t m0,

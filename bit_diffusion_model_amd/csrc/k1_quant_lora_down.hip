@@ -29,7 +29,7 @@ namespace svdq {
 
 constexpr int K1_WAVES = 8;
 
-template <int FMT, int NT>
+template <int FMT, int NT, bool FP8OUT>
 __global__ __launch_bounds__(64 * K1_WAVES) void k1_quant_lora_down(
     const uint16_t* __restrict__ X, int64_t ldx, int64_t M, int64_t K,
     const float* __restrict__ inv_s, const uint16_t* __restrict__ Ldh,
@@ -161,13 +161,27 @@ __global__ __launch_bounds__(64 * K1_WAVES) void k1_quant_lora_down(
         reinterpret_cast<uint8_t*>(sXv)[(int64_t)(2 * c + (sub >> 1)) * M + row] = (uint8_t)(e + 127);
     }
     if (row_ok) {
-      uint32_t w0 = 0, w1 = 0;
+      if constexpr (FP8OUT) {
+        // one FP8 E4M3 byte per code (sign, exponent 0, mantissa |q|: value q * 2^-9),
+        // the operand form the GEMM consumes; [M][K] bytes, each 8-element block stored
+        // as its even elements then its odd ones (the order of the GEMM's own nibble
+        // expansion of the weights, which the two operands must share)
+        uint32_t b[4] = {0, 0, 0, 0};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        w0 |= (nib[2 * j] | (nib[2 * j + 1] << 4)) << (8 * j);
-        w1 |= (nib[8 + 2 * j] | (nib[8 + 2 * j + 1] << 4)) << (8 * j);
+        for (int i = 0; i < 16; ++i) {
+          const int d = (i >> 3) * 2 + (i & 1), pos = (i & 7) >> 1;
+          b[d] |= ((nib[i] & 7u) | ((nib[i] & 8u) << 4)) << (8 * pos);
+        }
+        *reinterpret_cast<uint4*>(qX + row * K + k0) = make_uint4(b[0], b[1], b[2], b[3]);
+      } else {
+        uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          w0 |= (nib[2 * j] | (nib[2 * j + 1] << 4)) << (8 * j);
+          w1 |= (nib[8 + 2 * j] | (nib[8 + 2 * j + 1] << 4)) << (8 * j);
+        }
+        *reinterpret_cast<uint2*>(qX + row * (K >> 1) + (k0 >> 1)) = make_uint2(w0, w1);
       }
-      *reinterpret_cast<uint2*>(qX + row * (K >> 1) + (k0 >> 1)) = make_uint2(w0, w1);
     }
 
     if constexpr (NT > 0) {
@@ -206,15 +220,15 @@ __global__ __launch_bounds__(64 * K1_WAVES) void k1_quant_lora_down(
   }
 }
 
-template <int FMT>
+template <int FMT, bool FP8OUT>
 static hipError_t launch_k1_fmt(const KernelLayer& L, int64_t M, const uint16_t* X, int64_t ldx,
                                 uint8_t* qX, void* sX, float* lora_act, hipStream_t st) {
   const dim3 grid((unsigned)((M + 15) / 16)), block(64 * K1_WAVES);
   const int nt = (L.rank + 15) / 16;
-#define K1_CASE(NTV)                                                                          \
-  case NTV:                                                                                   \
-    hipLaunchKernelGGL((k1_quant_lora_down<FMT, NTV>), grid, block, 0, st, X, ldx, M, L.K,    \
-                       L.inv_s, L.Ld_hi, L.Ld_lo, L.rank, qX, sX, lora_act);                  \
+#define K1_CASE(NTV)                                                                            \
+  case NTV:                                                                                     \
+    hipLaunchKernelGGL((k1_quant_lora_down<FMT, NTV, FP8OUT>), grid, block, 0, st, X, ldx, M, L.K, \
+                       L.inv_s, L.Ld_hi, L.Ld_lo, L.rank, qX, sX, lora_act);                    \
     break;
   switch (nt) {
     K1_CASE(0) K1_CASE(1) K1_CASE(2) K1_CASE(3) K1_CASE(4)
@@ -226,9 +240,11 @@ static hipError_t launch_k1_fmt(const KernelLayer& L, int64_t M, const uint16_t*
 }
 
 hipError_t launch_k1(const KernelLayer& L, int64_t M, const uint16_t* X, int64_t ldx, uint8_t* qX,
-                     void* sX, float* lora_act, hipStream_t st) {
-  if (L.fmt == 0) return launch_k1_fmt<0>(L, M, X, ldx, qX, sX, lora_act, st);
-  return launch_k1_fmt<1>(L, M, X, ldx, qX, sX, lora_act, st);
+                     void* sX, float* lora_act, bool fp8_codes, hipStream_t st) {
+  if (L.fmt == 0)
+    return fp8_codes ? launch_k1_fmt<0, true>(L, M, X, ldx, qX, sX, lora_act, st)
+                     : launch_k1_fmt<0, false>(L, M, X, ldx, qX, sX, lora_act, st);
+  return launch_k1_fmt<1, false>(L, M, X, ldx, qX, sX, lora_act, st);
 }
 
 }  // namespace svdq

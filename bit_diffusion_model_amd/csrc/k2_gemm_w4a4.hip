@@ -66,11 +66,14 @@ __device__ __forceinline__ void split_scale(uint32_t bits, _Float16& m, uint32_t
 }
 
 struct Stage {
-  uint4 a, b;
+  uint4 a, a1, b;  // a1: second half of a 32-byte A piece (pre-expanded FP8 codes)
   uint32_t s;
 };
 
-template <int FMT, bool DEBUG>
+// AF8 (INT4 only): the activation codes arrive already as FP8 bytes, [M][K], each
+// 8-element block in the order kernel 2's nibble expansion produces (even elements,
+// then odd ones), so the A panel is copied to LDS without conversion.
+template <int FMT, bool DEBUG, bool AF8>
 __global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void k2_gemm(
     const uint8_t* __restrict__ qX, const void* __restrict__ sXv, int64_t M,
     const uint8_t* __restrict__ qW, const void* __restrict__ sWv, int64_t N, int64_t K,
@@ -89,12 +92,13 @@ __global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 
   const int64_t m0 = mbase + (int64_t)blockIdx.y * BM;
   const int64_t n0 = nbase + (int64_t)blockIdx.x * BN;
   const uint32_t Kb = (uint32_t)(K >> 1);  // bytes per code row
+  const uint32_t Ka = AF8 ? (uint32_t)K : Kb;  // bytes per A row
   const int nsteps = (int)(K >> 6);         // 64-wide K steps; even because K % 128 == 0
 
   // ---- buffer resources (range-checked loads) -------------------------------------
   const int64_t rowsA = mlim - m0 < BM ? mlim - m0 : BM;
   const int64_t rowsB = nlim - n0 < BN ? nlim - n0 : BN;
-  const __amdgpu_buffer_rsrc_t rA = make_rsrc(qX + m0 * Kb, (uint32_t)rowsA * Kb);
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(qX + m0 * Ka, (uint32_t)rowsA * Ka);
   const __amdgpu_buffer_rsrc_t rB = make_rsrc(qW + n0 * Kb, (uint32_t)rowsB * Kb);
   const int ng = FMT == 0 ? nsteps : 2 * nsteps;  // scale groups along K
   const int esz = FMT == 0 ? 2 : 1;
@@ -107,11 +111,17 @@ __global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 
   const uint32_t sstride = xs ? (uint32_t)M : (uint32_t)N;
   const int ldrow = tid & 127, ldhalf = tid >> 7;
   const uint32_t offAB = (uint32_t)ldrow * Kb + ldhalf * 16;
+  const uint32_t offA8 = (uint32_t)ldrow * Ka + ldhalf * 32;
 
   // Loads for steps past the end are harmless: they read zeros (range check) or codes
   // of another row into a buffer that is never consumed.
   auto gload = [&](Stage& st, int s) {
-    st.a = buf_load16(rA, offAB + (uint32_t)s * 32);
+    if (AF8) {
+      st.a = buf_load16(rA, offA8 + (uint32_t)s * 64);
+      st.a1 = buf_load16(rA, offA8 + (uint32_t)s * 64 + 16);
+    } else {
+      st.a = buf_load16(rA, offAB + (uint32_t)s * 32);
+    }
     st.b = buf_load16(rB, offAB + (uint32_t)s * 32);
     if (DEBUG) {
       st.s = 0;
@@ -128,13 +138,18 @@ __global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 
       const uint32_t aw[4] = {st.a.x, st.a.y, st.a.z, st.a.w}, bw[4] = {st.b.x, st.b.y, st.b.z, st.b.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        nib8_to_fp8(aw[i], a8[2 * i], a8[2 * i + 1]);
+        if (!AF8) nib8_to_fp8(aw[i], a8[2 * i], a8[2 * i + 1]);
         nib8_to_fp8(bw[i], b8[2 * i], b8[2 * i + 1]);
       }
       uint4* da = reinterpret_cast<uint4*>(&sm.st[buf].A[ldrow * S::kPitch + ldhalf * 32]);
       uint4* db = reinterpret_cast<uint4*>(&sm.st[buf].B[ldrow * S::kPitch + ldhalf * 32]);
-      da[0] = make_uint4(a8[0], a8[1], a8[2], a8[3]);
-      da[1] = make_uint4(a8[4], a8[5], a8[6], a8[7]);
+      if (AF8) {
+        da[0] = st.a;
+        da[1] = st.a1;
+      } else {
+        da[0] = make_uint4(a8[0], a8[1], a8[2], a8[3]);
+        da[1] = make_uint4(a8[4], a8[5], a8[6], a8[7]);
+      }
       db[0] = make_uint4(b8[0], b8[1], b8[2], b8[3]);
       db[1] = make_uint4(b8[4], b8[5], b8[6], b8[7]);
       _Float16 m;
@@ -329,24 +344,32 @@ __global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 
 
 }  // namespace
 
-hipError_t launch_k2(const KernelLayer& L, int64_t M, const uint8_t* qX, const void* sX,
-                     const float* lora_act, void* Y, int64_t ldy, int ydtype, hipStream_t st) {
+template <int FMT, bool AF8>
+static void launch_k2_t(const KernelLayer& L, int64_t M, const uint8_t* qX, const void* sX,
+                        const float* lora_act, void* Y, int64_t ldy, int ydtype, hipStream_t st) {
   const dim3 grid((unsigned)((L.N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM)), block(NTHREADS);
-  if (L.fmt == 0)
-    hipLaunchKernelGGL((k2_gemm<0, false>), grid, block, 0, st, qX, sX, M, L.qW, L.sW, L.N, L.K,
-                       lora_act, L.L2t, L.rank, Y, ldy, ydtype, (int64_t)0, (int64_t)0, M, L.N,
-                       (int32_t*)nullptr);
-  else
-    hipLaunchKernelGGL((k2_gemm<1, false>), grid, block, 0, st, qX, sX, M, L.qW, L.sW, L.N, L.K,
-                       lora_act, L.L2t, L.rank, Y, ldy, ydtype, (int64_t)0, (int64_t)0, M, L.N,
-                       (int32_t*)nullptr);
+  hipLaunchKernelGGL((k2_gemm<FMT, false, AF8>), grid, block, 0, st, qX, sX, M, L.qW, L.sW, L.N, L.K,
+                     lora_act, L.L2t, L.rank, Y, ldy, ydtype, (int64_t)0, (int64_t)0, M, L.N,
+                     (int32_t*)nullptr);
+}
+
+hipError_t launch_k2(const KernelLayer& L, int64_t M, const uint8_t* qX, const void* sX,
+                     const float* lora_act, void* Y, int64_t ldy, int ydtype, bool fp8_codes,
+                     hipStream_t st) {
+  if (L.fmt == 0) {
+    if (fp8_codes) launch_k2_t<0, true>(L, M, qX, sX, lora_act, Y, ldy, ydtype, st);
+    else launch_k2_t<0, false>(L, M, qX, sX, lora_act, Y, ldy, ydtype, st);
+  } else {
+    if (fp8_codes) return hipErrorInvalidValue;
+    launch_k2_t<1, false>(L, M, qX, sX, lora_act, Y, ldy, ydtype, st);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_k2_debug(const KernelLayer& L, int64_t M, const uint8_t* qX, int64_t m0,
                            int64_t n0, int64_t mt, int64_t nt, int32_t* out, hipStream_t st) {
   const dim3 grid((unsigned)((nt + BN - 1) / BN), (unsigned)((mt + BM - 1) / BM)), block(NTHREADS);
-  hipLaunchKernelGGL((k2_gemm<0, true>), grid, block, 0, st, qX, (const void*)nullptr, M, L.qW,
+  hipLaunchKernelGGL((k2_gemm<0, true, false>), grid, block, 0, st, qX, (const void*)nullptr, M, L.qW,
                      (const void*)nullptr, L.N, L.K, (const float*)nullptr, (const uint16_t*)nullptr,
                      0, (void*)nullptr, (int64_t)0, 0, m0, n0, m0 + mt, n0 + nt, out);
   return hipGetLastError();

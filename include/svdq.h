@@ -167,12 +167,15 @@ svdq_status svdq_gemm_w4a4_lora_up(const svdq_layer* layer, int64_t M, const uin
                                    const void* sX, const float* lora_act, void* Y, int64_t ldy,
                                    int32_t ydtype, void* stream);
 
-/* Bytes of device workspace svdq_linear_forward needs for M rows (qX, sX, lora_act,
- * each 256-byte aligned). */
+/* Bytes of device workspace svdq_linear_forward needs for M rows (activation codes,
+ * sX, lora_act, each 256-byte aligned).  For INT4 the forward path holds the
+ * activation codes as one byte each (M*K bytes, the operand form of kernel 2's matrix
+ * cores), for MXFP4 packed (M*K/2 bytes). */
 size_t svdq_workspace_bytes(const svdq_layer* layer, int64_t M);
 
 /* The public layer: kernel 1 then kernel 2 on `stream`, intermediates in `workspace`
- * (device, >= svdq_workspace_bytes, 256-byte aligned). */
+ * (device, >= svdq_workspace_bytes, 256-byte aligned).  Same arithmetic as the two
+ * calls above in sequence: the results are identical bit for bit. */
 svdq_status svdq_linear_forward(const svdq_layer* layer, int64_t M, const uint16_t* X,
                                 int64_t ldx, void* Y, int64_t ldy, int32_t ydtype,
                                 void* workspace, size_t ws_bytes, void* stream);

@@ -78,11 +78,21 @@ def test_forward_matches_oracle(shape):
     wl = random_layer(M, K, N, r, 7000 + M + K + N, fmt=fmt, x_out=3, w_out=2)
     p = oracle_pack(wl)
     lay = layer_from_oracle(p)
-    Y = lay.forward(to_dev_bf16(wl.X)).cpu().numpy().astype(np.float64)
+    ws = lay.workspace(M)
+    Y = lay.forward(to_dev_bf16(wl.X), workspace=ws).cpu().numpy().astype(np.float64)
     Yref = oforward.forward(wl.X, p)["Y"]
     e = rel_err(Y, Yref)
     log(f"  max|err|/RMS = {e:.3e}")
     assert e <= TOL_Y
+    if fmt == "int4":
+        # the forward path keeps the activation codes as FP8 E4M3 bytes (sign bit 7,
+        # magnitude in the mantissa bits), each 8-element block as even then odd elements
+        b = ws[:M * K].cpu().numpy().reshape(M, K // 8, 8)
+        q = (b & 7).astype(np.int64) * np.where(b & 0x80, -1, 1)
+        assert not (b & 0x78).any()
+        codes = np.empty_like(q)
+        codes[:, :, 0::2], codes[:, :, 1::2] = q[:, :, :4], q[:, :, 4:]
+        np.testing.assert_array_equal(codes.reshape(M, K), oforward.quantize_activations(wl.X, p["inv_s32"], fmt)[1])
     # the two kernels called separately give the same bits as the public entry point
     qX, sX, la = lay.quantize_act(to_dev_bf16(wl.X))
     Y2 = lay.gemm(qX, sX, la).cpu().numpy()
