@@ -212,16 +212,16 @@ def main():
     tops = ops / (ms * 1e-3) / 1e12
     log(f"[bench] {ms:.4f} ms/step (wall {wall / args.steps * 1e3:.4f}), {tops:.1f} TOPS")
 
-    # per-kernel durations, launched exactly as inside svdq_linear_forward, on the
-    # same (torch current) stream the events are recorded on
-    qX, sX, la = lay.alloc_act(M)
+    # per-kernel durations, launched exactly as inside svdq_linear_forward (activation
+    # side in MMA form), on the same (torch current) stream the events are recorded on
+    qX, sX, la = lay.alloc_act(M, svdq.ACT_MMA)
     nrep = max(args.steps, 10)
     e = [torch.cuda.Event(enable_timing=True) for _ in range(3 * nrep)]
     for i in range(nrep):
         e[3 * i].record()
-        lay.quantize_act(X, (qX, sX, la))
+        lay.quantize_act(X, (qX, sX, la), form=svdq.ACT_MMA)
         e[3 * i + 1].record()
-        lay.gemm(qX, sX, la, ydt, Y)
+        lay.gemm(qX, sX, la, ydt, Y, form=svdq.ACT_MMA)
         e[3 * i + 2].record()
     torch.cuda.synchronize()
     t_k1 = float(np.mean([e[3 * i].elapsed_time(e[3 * i + 1]) for i in range(nrep)])) * 1e-3
@@ -239,7 +239,13 @@ def main():
 
     G = lay.group
     k2_ops = float(M) * N * (2.0 * K + 2.0 * r)
-    k1_bytes = float(M) * (2 * K + K // 2 + (K // G) * (2 if fmt == svdq.INT4_G64 else 1) + 4 * r)
+    # kernel 1's HBM bytes in MMA form: X (bf16), codes (INT4 FP8 bytes / MXFP4 nibbles),
+    # scales (INT4 4-byte words / E8M0 bytes), lora_act (R16 x 4 bytes); the factor
+    # rows are re-read from L2 and not counted
+    if fmt == svdq.INT4_G64:
+        k1_bytes = float(M) * (2 * K + K + (K // G) * 4 + 4 * svdq.r16(r))
+    else:
+        k1_bytes = float(M) * (2 * K + K // 2 + (K // G) + 4 * svdq.r16(r))
     peak = PEAK_MFMA_TOPS if fmt == svdq.INT4_G64 else PEAK_MFMA_FP4_TOPS
     k2_tops = k2_ops / t_k2 / 1e12
     traffic = traffic_entry() if args.workload == "C1" and ydt == svdq.F32 else None

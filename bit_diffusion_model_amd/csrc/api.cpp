@@ -50,6 +50,7 @@ static svdq_status check_layer(const svdq_layer* L, KernelLayer& kl) {
   if (!L->inv_s || !L->qW || !L->sW) return fail(SVDQ_EINVAL, "layer inv_s, qW and sW must be non-NULL");
   if (L->rank > 0 && (!L->Ld_hi || !L->Ld_lo || !L->L2t))
     return fail(SVDQ_EINVAL, "layer Ld_hi, Ld_lo and L2t must be non-NULL when rank > 0");
+  if (L->fmt == SVDQ_INT4_G64 && !aligned(L->sW, 4)) return fail(SVDQ_EINVAL, "INT4 layer sW must be 4-byte aligned");
   if (!aligned(L->inv_s, 16) || !aligned(L->qW, 16) ||
       (L->rank > 0 && (!aligned(L->Ld_hi, 16) || !aligned(L->Ld_lo, 16) || !aligned(L->L2t, 16))))
     return fail(SVDQ_EINVAL, "layer inv_s, qW, Ld_hi, Ld_lo and L2t must be 16-byte aligned");
@@ -62,17 +63,16 @@ static size_t rup(size_t x) { return (x + 255) & ~size_t(255); }
 struct WsLayout {
   size_t qx, sx, la, total;
 };
-// The forward path keeps INT4 activation codes as FP8 bytes (one per code, [M][K]) so
-// that kernel 2 copies them to LDS without expanding; MXFP4 codes stay packed.
-static bool fwd_fp8_codes(const svdq_layer* L) { return L->fmt == SVDQ_INT4_G64; }
-
+// The forward path's workspace: the activation side in MMA form (INT4 codes as FP8
+// bytes [M][K] and split 32-bit scale words; MXFP4 packed codes and E8M0 bytes;
+// lora_act as bf16 hi/lo rows, the bytes of fp32 [M][R16]).
 static WsLayout ws_layout(const svdq_layer* L, int64_t M) {
+  const bool f8 = L->fmt == SVDQ_INT4_G64;
   WsLayout w;
   w.qx = 0;
-  const size_t qb = rup((size_t)M * (size_t)(fwd_fp8_codes(L) ? L->K : L->K / 2));
-  w.sx = qb;
-  const size_t sb = rup((size_t)(L->K / group_of(L->fmt)) * (size_t)M * (L->fmt == SVDQ_INT4_G64 ? 2 : 1));
-  w.la = w.sx + sb;
+  w.sx = rup((size_t)M * (size_t)(f8 ? L->K : L->K / 2));
+  const size_t ssz = f8 ? 4 : 1;
+  w.la = w.sx + rup((size_t)(L->K / group_of(L->fmt)) * (size_t)M * ssz);
   w.total = w.la + rup((size_t)M * (size_t)((L->rank + 15) / 16 * 16) * 4);
   return w;
 }
@@ -94,11 +94,17 @@ size_t svdq_workspace_bytes(const svdq_layer* layer, int64_t M) {
 
 namespace svdq {
 
+static svdq_status check_form(int32_t form) {
+  if (form != SVDQ_ACT_PACKED && form != SVDQ_ACT_MMA) return fail(SVDQ_EUNSUPPORTED, "unknown activation form %d", (int)form);
+  return SVDQ_OK;
+}
+
 static svdq_status run_k1(const svdq_layer* layer, int64_t M, const uint16_t* X, int64_t ldx,
-                          uint8_t* qX, void* sX, float* lora_act, bool fp8_codes, void* stream) {
+                          int32_t form, uint8_t* qX, void* sX, void* lora_act, void* stream) {
   KernelLayer kl;
   svdq_status st = check_layer(layer, kl);
   if (st != SVDQ_OK) return st;
+  if ((st = check_form(form)) != SVDQ_OK) return st;
   if (M < 0) return fail(SVDQ_EINVAL, "M must be >= 0");
   if (M == 0) return ok();
   if (!X || !qX || !sX) return fail(SVDQ_EINVAL, "X, qX and sX must be non-NULL");
@@ -106,27 +112,29 @@ static svdq_status run_k1(const svdq_layer* layer, int64_t M, const uint16_t* X,
   if (ldx < kl.K || ldx % 8 != 0) return fail(SVDQ_EINVAL, "ldx must be >= K and a multiple of 8");
   if (!aligned(X, 16) || !aligned(qX, 16) || !aligned(sX, 2) || (lora_act && !aligned(lora_act, 16)))
     return fail(SVDQ_EINVAL, "X, qX and lora_act must be 16-byte aligned");
-  hipError_t e = launch_k1(kl, M, X, ldx, qX, sX, lora_act, fp8_codes, (hipStream_t)stream);
+  hipError_t e = launch_k1(kl, M, X, ldx, qX, sX, lora_act, form == SVDQ_ACT_MMA, (hipStream_t)stream);
   if (e != hipSuccess) return fail(SVDQ_EHIP, "kernel 1 launch: %s", hipGetErrorString(e));
   return ok();
 }
 
-static svdq_status run_k2(const svdq_layer* layer, int64_t M, const uint8_t* qX, const void* sX,
-                          const float* lora_act, void* Y, int64_t ldy, int32_t ydtype,
-                          bool fp8_codes, void* stream) {
+static svdq_status run_k2(const svdq_layer* layer, int64_t M, int32_t form, const uint8_t* qX,
+                          const void* sX, const void* lora_act, void* Y, int64_t ldy,
+                          int32_t ydtype, void* stream) {
   KernelLayer kl;
   svdq_status st = check_layer(layer, kl);
   if (st != SVDQ_OK) return st;
+  if ((st = check_form(form)) != SVDQ_OK) return st;
   if (M < 0) return fail(SVDQ_EINVAL, "M must be >= 0");
   if (M == 0) return ok();
   if (ydtype != SVDQ_F32 && ydtype != SVDQ_BF16) return fail(SVDQ_EUNSUPPORTED, "unsupported output dtype %d", (int)ydtype);
   if (!qX || !sX || !Y) return fail(SVDQ_EINVAL, "qX, sX and Y must be non-NULL");
   if (kl.rank > 0 && !lora_act) return fail(SVDQ_EINVAL, "lora_act must be non-NULL when rank > 0");
   if (ldy < kl.N) return fail(SVDQ_EINVAL, "ldy must be >= N");
+  if (ldy >= (int64_t(1) << 23)) return fail(SVDQ_EUNSUPPORTED, "ldy must be < 2^23 elements");
   if (!aligned(qX, 16) || !aligned(Y, ydtype == SVDQ_F32 ? 4 : 2) || !aligned(sX, 2) ||
       (lora_act && !aligned(lora_act, 16)))
     return fail(SVDQ_EINVAL, "qX and lora_act must be 16-byte aligned and Y aligned to its element size");
-  hipError_t e = launch_k2(kl, M, qX, sX, lora_act, Y, ldy, ydtype, fp8_codes, (hipStream_t)stream);
+  hipError_t e = launch_k2(kl, M, qX, sX, lora_act, Y, ldy, ydtype, form == SVDQ_ACT_MMA, (hipStream_t)stream);
   if (e != hipSuccess) return fail(SVDQ_EHIP, "kernel 2 launch: %s", hipGetErrorString(e));
   return ok();
 }
@@ -136,15 +144,15 @@ static svdq_status run_k2(const svdq_layer* layer, int64_t M, const uint8_t* qX,
 extern "C" {
 
 svdq_status svdq_quantize_act_lora_down(const svdq_layer* layer, int64_t M, const uint16_t* X,
-                                        int64_t ldx, uint8_t* qX, void* sX, float* lora_act,
-                                        void* stream) {
-  return run_k1(layer, M, X, ldx, qX, sX, lora_act, false, stream);
+                                        int64_t ldx, int32_t form, uint8_t* qX, void* sX,
+                                        void* lora_act, void* stream) {
+  return run_k1(layer, M, X, ldx, form, qX, sX, lora_act, stream);
 }
 
-svdq_status svdq_gemm_w4a4_lora_up(const svdq_layer* layer, int64_t M, const uint8_t* qX,
-                                   const void* sX, const float* lora_act, void* Y, int64_t ldy,
-                                   int32_t ydtype, void* stream) {
-  return run_k2(layer, M, qX, sX, lora_act, Y, ldy, ydtype, false, stream);
+svdq_status svdq_gemm_w4a4_lora_up(const svdq_layer* layer, int64_t M, int32_t form,
+                                   const uint8_t* qX, const void* sX, const void* lora_act,
+                                   void* Y, int64_t ldy, int32_t ydtype, void* stream) {
+  return run_k2(layer, M, form, qX, sX, lora_act, Y, ldy, ydtype, stream);
 }
 
 svdq_status svdq_linear_forward(const svdq_layer* layer, int64_t M, const uint16_t* X, int64_t ldx,
@@ -161,11 +169,10 @@ svdq_status svdq_linear_forward(const svdq_layer* layer, int64_t M, const uint16
   uint8_t* base = static_cast<uint8_t*>(workspace);
   uint8_t* qX = base + w.qx;
   void* sX = base + w.sx;
-  float* la = kl.rank > 0 ? reinterpret_cast<float*>(base + w.la) : nullptr;
-  const bool f8 = fwd_fp8_codes(layer);
-  st = run_k1(layer, M, X, ldx, qX, sX, la, f8, stream);
+  void* la = kl.rank > 0 ? base + w.la : nullptr;
+  st = run_k1(layer, M, X, ldx, SVDQ_ACT_MMA, qX, sX, la, stream);
   if (st != SVDQ_OK) return st;
-  return run_k2(layer, M, qX, sX, la, Y, ldy, ydtype, f8, stream);
+  return run_k2(layer, M, SVDQ_ACT_MMA, qX, sX, la, Y, ldy, ydtype, stream);
 }
 
 svdq_status svdq_debug_group_sums(const svdq_layer* layer, int64_t M, const uint8_t* qX, int64_t m0,

@@ -32,6 +32,27 @@ __device__ __forceinline__ void nib8_to_fp8(uint32_t d, uint32_t& lo, uint32_t& 
   hi = ((d >> 4) & 0x07070707u) | (d & 0x80808080u);
 }
 
+// The same expansion for the kernel's weight layout, in which each byte j of the word
+// holds element 2j in bits 0-2 (magnitude) and 7 (sign), the magnitude of element 2j+1
+// in bits 4-6, and in bit 3 the sign of element 2j-1 (cyclically, of byte j-1's odd
+// element).  Then lo is a mask, and hi is the word rotated by 4 bits and masked.
+__device__ __forceinline__ void nib8p_to_fp8(uint32_t d, uint32_t& lo, uint32_t& hi) {
+  lo = d & 0x87878787u;
+  hi = __builtin_amdgcn_alignbit(d, d, 4) & 0x87878787u;
+}
+
+// An fp16 INT4 group scale s = m * 2^e (m in [1, 2)) as one word: bits 0-15 the fp16 m
+// (0 for s = 0), bits 16-23 the E8M0 byte of 2^(e + 9) (127 for s = 0).  2^-9 is the
+// value of FP8 code 1, so an MFMA with these block scales on both sides returns the
+// exact integer group sum times 2^(eX + eW).
+__device__ __forceinline__ uint32_t split_scale_word(uint32_t bits) {
+  const float f = (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t m = f == 0.0f ? 0u : __builtin_bit_cast(uint16_t, (_Float16)__uint_as_float((u & 0x807FFFFFu) | (127u << 23)));
+  const uint32_t eb = f == 0.0f ? 127u : ((u >> 23) & 0xFFu) + 9u;
+  return m | (eb << 16);
+}
+
 // Raw buffer resource over `bytes` bytes at p: loads beyond the range return zeros.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
@@ -47,6 +68,14 @@ __device__ __forceinline__ uint32_t buf_load2(__amdgpu_buffer_rsrc_t r, uint32_t
 }
 __device__ __forceinline__ uint32_t buf_load1(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
+}
+// Stores through a buffer resource: a store whose offset is outside the range is
+// dropped (the offset is checked in full; nothing goes through the scalar offset).
+__device__ __forceinline__ void buf_store4(uint32_t v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_store2(uint16_t v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b16(v, r, off, 0, 0);
 }
 
 __device__ __forceinline__ float wave_max_xor(float v, int mask) {

@@ -29,7 +29,7 @@ namespace svdq {
 
 constexpr int K1_WAVES = 8;
 
-template <int FMT, int NT, bool FP8OUT>
+template <int FMT, int NT, bool MMA>
 __global__ __launch_bounds__(64 * K1_WAVES) void k1_quant_lora_down(
     const uint16_t* __restrict__ X, int64_t ldx, int64_t M, int64_t K,
     const float* __restrict__ inv_s, const uint16_t* __restrict__ Ldh,
@@ -137,8 +137,12 @@ __global__ __launch_bounds__(64 * K1_WAVES) void k1_quant_lora_down(
         const uint32_t mag = (uint32_t)fabsf(qc);
         nib[i] = (sf == 0.0f) ? 0u : (mag | (qc < 0.0f ? 8u : 0u));
       }
-      if (row_ok && sub == 0)
-        reinterpret_cast<uint16_t*>(sXv)[(int64_t)c * M + row] = __builtin_bit_cast(uint16_t, sh);
+      if (row_ok && sub == 0) {
+        if constexpr (MMA)  // the split form kernel 2 consumes: [K/64][M] words
+          reinterpret_cast<uint32_t*>(sXv)[(int64_t)c * M + row] = split_scale_word(__builtin_bit_cast(uint16_t, sh));
+        else
+          reinterpret_cast<uint16_t*>(sXv)[(int64_t)c * M + row] = __builtin_bit_cast(uint16_t, sh);
+      }
     } else {
       // MXFP4: e = smallest exponent with 6 * 2^e >= a (clamped to [-127, 127]);
       // codes = E2M1 round-half-even of x * 2^-e (hardware convert, scale 1).
@@ -161,7 +165,7 @@ __global__ __launch_bounds__(64 * K1_WAVES) void k1_quant_lora_down(
         reinterpret_cast<uint8_t*>(sXv)[(int64_t)(2 * c + (sub >> 1)) * M + row] = (uint8_t)(e + 127);
     }
     if (row_ok) {
-      if constexpr (FP8OUT) {
+      if constexpr (MMA && FMT == 0) {
         // one FP8 E4M3 byte per code (sign, exponent 0, mantissa |q|: value q * 2^-9),
         // the operand form the GEMM consumes; [M][K] bytes, each 8-element block stored
         // as its even elements then its odd ones (the order of the GEMM's own nibble
@@ -214,21 +218,31 @@ __global__ __launch_bounds__(64 * K1_WAVES) void k1_quant_lora_down(
         float v = 0.f;
 #pragma unroll
         for (int w = 0; w < K1_WAVES; ++w) v += red[w][rr][cc];
-        lora_act[(m0 + rr) * R16 + cc] = v;
+        if constexpr (MMA) {
+          // the bf16 pair kernel 2's up-projection MFMA consumes, v = hi + lo to ~2^-17
+          // relative; row layout [R16 hi][R16 lo] (the same bytes as R16 fp32)
+          const uint32_t hb = f32_to_bf16_rne(v);
+          const uint32_t lb = f32_to_bf16_rne(v - __uint_as_float(hb << 16));
+          uint16_t* la = reinterpret_cast<uint16_t*>(lora_act) + (m0 + rr) * 2 * R16;
+          la[cc] = (uint16_t)hb;
+          la[R16 + cc] = (uint16_t)lb;
+        } else {
+          lora_act[(m0 + rr) * R16 + cc] = v;
+        }
       }
     }
   }
 }
 
-template <int FMT, bool FP8OUT>
+template <int FMT, bool MMA>
 static hipError_t launch_k1_fmt(const KernelLayer& L, int64_t M, const uint16_t* X, int64_t ldx,
-                                uint8_t* qX, void* sX, float* lora_act, hipStream_t st) {
+                                uint8_t* qX, void* sX, void* lora_act, hipStream_t st) {
   const dim3 grid((unsigned)((M + 15) / 16)), block(64 * K1_WAVES);
   const int nt = (L.rank + 15) / 16;
 #define K1_CASE(NTV)                                                                            \
   case NTV:                                                                                     \
-    hipLaunchKernelGGL((k1_quant_lora_down<FMT, NTV, FP8OUT>), grid, block, 0, st, X, ldx, M, L.K, \
-                       L.inv_s, L.Ld_hi, L.Ld_lo, L.rank, qX, sX, lora_act);                    \
+    hipLaunchKernelGGL((k1_quant_lora_down<FMT, NTV, MMA>), grid, block, 0, st, X, ldx, M, L.K, \
+                       L.inv_s, L.Ld_hi, L.Ld_lo, L.rank, qX, sX, static_cast<float*>(lora_act));                    \
     break;
   switch (nt) {
     K1_CASE(0) K1_CASE(1) K1_CASE(2) K1_CASE(3) K1_CASE(4)
@@ -240,11 +254,12 @@ static hipError_t launch_k1_fmt(const KernelLayer& L, int64_t M, const uint16_t*
 }
 
 hipError_t launch_k1(const KernelLayer& L, int64_t M, const uint16_t* X, int64_t ldx, uint8_t* qX,
-                     void* sX, float* lora_act, bool fp8_codes, hipStream_t st) {
+                     void* sX, void* lora_act, bool mma, hipStream_t st) {
   if (L.fmt == 0)
-    return fp8_codes ? launch_k1_fmt<0, true>(L, M, X, ldx, qX, sX, lora_act, st)
-                     : launch_k1_fmt<0, false>(L, M, X, ldx, qX, sX, lora_act, st);
-  return launch_k1_fmt<1, false>(L, M, X, ldx, qX, sX, lora_act, st);
+    return mma ? launch_k1_fmt<0, true>(L, M, X, ldx, qX, sX, lora_act, st)
+               : launch_k1_fmt<0, false>(L, M, X, ldx, qX, sX, lora_act, st);
+  return mma ? launch_k1_fmt<1, true>(L, M, X, ldx, qX, sX, lora_act, st)
+             : launch_k1_fmt<1, false>(L, M, X, ldx, qX, sX, lora_act, st);
 }
 
 }  // namespace svdq

@@ -16,6 +16,11 @@
 //    epilogue adds it times the fp16 product mX*mW (v_pk_mul_f16 + v_fma_mix_f32).
 //    With per-group scales on both sides this per-element rescale is the VALU cost
 //    that bounds the INT4 path; moving the powers of two into the MFMA halves it.
+//    The weight scales arrive already split (one word: fp16 m, E8M0 byte), and the
+//    weight codes in a bit order that expands to FP8 with a mask and a rotate (both
+//    prepared once, offline).  In the fused forward path the activation side comes
+//    the same way from kernel 1: FP8 code bytes, split scales, and the low-rank
+//    activations as bf16 hi/lo pairs, so the main loop converts only the weights.
 //
 // Tiling: a 256-thread block (4 waves) owns a 128 x 128 output tile; wave w owns rows
 // 64*(w/2) .. +63 and columns 64*(w%2) .. +63, i.e. 2 x 2 MFMA tiles of 32 x 32; two
@@ -56,32 +61,25 @@ struct Smem {
   } st[2];
 };
 
-// fp16 scale -> (fp16 mantissa in [1,2) or 0, E8M0 byte for 2^(e+9))
-__device__ __forceinline__ void split_scale(uint32_t bits, _Float16& m, uint32_t& ebyte) {
-  const float f = (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
-  const uint32_t u = __float_as_uint(f);
-  const int e = (int)((u >> 23) & 0xFF) - 127;
-  m = f == 0.0f ? (_Float16)0.0f : (_Float16)__uint_as_float((u & 0x807FFFFFu) | (127u << 23));
-  ebyte = f == 0.0f ? 127u : (uint32_t)(e + 9 + 127);
-}
-
 struct Stage {
   uint4 a, a1, b;  // a1: second half of a 32-byte A piece (pre-expanded FP8 codes)
   uint32_t s;
 };
 
-// AF8 (INT4 only): the activation codes arrive already as FP8 bytes, [M][K], each
-// 8-element block in the order kernel 2's nibble expansion produces (even elements,
-// then odd ones), so the A panel is copied to LDS without conversion.
-template <int FMT, bool DEBUG, bool AF8>
+// MMA: the activation side arrives in kernel 1's operand form: INT4 codes as FP8 bytes
+// [M][K], each 8-element block in the order of the weights' expansion (even elements,
+// then odd ones), so the A panel is copied to LDS without conversion, and INT4 scales
+// as split words [K/64][M]; lora_act as bf16 rows [R16 hi][R16 lo] (both formats).
+template <int FMT, bool DEBUG, bool MMA>
 __global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void k2_gemm(
     const uint8_t* __restrict__ qX, const void* __restrict__ sXv, int64_t M,
     const uint8_t* __restrict__ qW, const void* __restrict__ sWv, int64_t N, int64_t K,
-    const float* __restrict__ lora_act, const uint16_t* __restrict__ L2, int rank,
+    const void* __restrict__ lora_act, const uint16_t* __restrict__ L2, int rank,
     void* __restrict__ Y, int64_t ldy, int ydtype,
     int64_t mbase, int64_t nbase, int64_t mlim, int64_t nlim, int32_t* __restrict__ dbg) {
   using S = Smem<FMT>;
   __shared__ S sm;
+  constexpr bool AF8 = MMA && FMT == 0;  // activation codes as FP8 bytes
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar
@@ -101,7 +99,9 @@ __global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 
   const __amdgpu_buffer_rsrc_t rA = make_rsrc(qX + m0 * Ka, (uint32_t)rowsA * Ka);
   const __amdgpu_buffer_rsrc_t rB = make_rsrc(qW + n0 * Kb, (uint32_t)rowsB * Kb);
   const int ng = FMT == 0 ? nsteps : 2 * nsteps;  // scale groups along K
-  const int esz = FMT == 0 ? 2 : 1;
+  // INT4 scale words are 4 bytes, except the public path's fp16 activation scales
+  const bool xs16 = FMT == 0 && !AF8 && wave < 2;
+  const int esz = FMT == 0 ? (xs16 ? 2 : 4) : 1;
   // staging roles: thread t moves one 16-byte piece of the A panel and one of the B
   // panel (row t & 127, half t >> 7) and one scale: waves 0-1 the X row t, waves 2-3
   // the W column t - 128.  The choice is wave-uniform, so it is made once, here.
@@ -126,7 +126,8 @@ __global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 
     if (DEBUG) {
       st.s = 0;
     } else if (FMT == 0) {
-      st.s = buf_load2(rS, ((uint32_t)s * sstride + sidx) * 2);
+      if (xs16) st.s = buf_load2(rS, ((uint32_t)s * sstride + sidx) * 2);
+      else st.s = buf_load4(rS, ((uint32_t)s * sstride + sidx) * 4);
     } else {
       const uint32_t o0 = (uint32_t)(2 * s) * sstride + sidx;
       st.s = buf_load1(rS, o0) | (buf_load1(rS, o0 + sstride) << 8);
@@ -139,7 +140,7 @@ __global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if (!AF8) nib8_to_fp8(aw[i], a8[2 * i], a8[2 * i + 1]);
-        nib8_to_fp8(bw[i], b8[2 * i], b8[2 * i + 1]);
+        nib8p_to_fp8(bw[i], b8[2 * i], b8[2 * i + 1]);
       }
       uint4* da = reinterpret_cast<uint4*>(&sm.st[buf].A[ldrow * S::kPitch + ldhalf * 32]);
       uint4* db = reinterpret_cast<uint4*>(&sm.st[buf].B[ldrow * S::kPitch + ldhalf * 32]);
@@ -152,16 +153,11 @@ __global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 
       }
       db[0] = make_uint4(b8[0], b8[1], b8[2], b8[3]);
       db[1] = make_uint4(b8[4], b8[5], b8[6], b8[7]);
-      _Float16 m;
-      uint32_t eb;
-      if (DEBUG) {
-        m = (_Float16)1.0f;
-        eb = 127 + 9;
-      } else {
-        split_scale(st.s, m, eb);
-      }
-      sm.st[buf].m[tid] = m;
-      sm.st[buf].e[tid] = eb;
+      uint32_t w;
+      if (DEBUG) w = 0x3C00u | ((127u + 9u) << 16);  // m = 1, 2^9
+      else w = xs16 ? split_scale_word(st.s) : st.s;
+      sm.st[buf].m[tid] = __builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+      sm.st[buf].e[tid] = w >> 16;
     } else {
       *reinterpret_cast<uint4*>(&sm.st[buf].A[ldrow * S::kPitch + ldhalf * 16]) = st.a;
       *reinterpret_cast<uint4*>(&sm.st[buf].B[ldrow * S::kPitch + ldhalf * 16]) = st.b;
@@ -294,7 +290,7 @@ __global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 
   // and rows past M / columns past N read as zeros through the range check.
   if (rank > 0) {
     const int R16 = (rank + 15) & ~15;
-    const __amdgpu_buffer_rsrc_t rL = make_rsrc(lora_act + m0 * R16, (uint32_t)(rowsA * R16 * 4));
+    const __amdgpu_buffer_rsrc_t rL = make_rsrc(static_cast<const uint8_t*>(lora_act) + m0 * R16 * 4, (uint32_t)(rowsA * R16 * 4));
     const __amdgpu_buffer_rsrc_t rU = make_rsrc(L2 + n0 * R16, (uint32_t)(rowsB * R16 * 2));
     for (int k0 = 0; k0 < R16; k0 += 16) {
       v8bf bl[TJ];
@@ -303,18 +299,26 @@ __global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 
         bl[j] = __builtin_bit_cast(v8bf, buf_load16(rU, (uint32_t)((wn + j * 32 + l32) * R16 + k0 + 8 * kh) * 2));
 #pragma unroll
       for (int i = 0; i < TI; ++i) {
-        const uint32_t o = (uint32_t)((wm + i * 32 + l32) * R16 + k0 + 8 * kh) * 4;
-        const uint4 v0 = buf_load16(rL, o), v1 = buf_load16(rL, o + 16);
-        const float v[8] = {__uint_as_float(v0.x), __uint_as_float(v0.y), __uint_as_float(v0.z), __uint_as_float(v0.w),
-                            __uint_as_float(v1.x), __uint_as_float(v1.y), __uint_as_float(v1.z), __uint_as_float(v1.w)};
-        uint16_t hi[8], lo[8];
+        v8bf ah, al;
+        if (MMA) {  // bf16 rows [R16 hi][R16 lo]
+          const uint32_t o = (uint32_t)((wm + i * 32 + l32) * 2 * R16 + k0 + 8 * kh) * 2;
+          ah = __builtin_bit_cast(v8bf, buf_load16(rL, o));
+          al = __builtin_bit_cast(v8bf, buf_load16(rL, o + R16 * 2));
+        } else {
+          const uint32_t o = (uint32_t)((wm + i * 32 + l32) * R16 + k0 + 8 * kh) * 4;
+          const uint4 v0 = buf_load16(rL, o), v1 = buf_load16(rL, o + 16);
+          const float v[8] = {__uint_as_float(v0.x), __uint_as_float(v0.y), __uint_as_float(v0.z), __uint_as_float(v0.w),
+                              __uint_as_float(v1.x), __uint_as_float(v1.y), __uint_as_float(v1.z), __uint_as_float(v1.w)};
+          uint16_t hi[8], lo[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const uint32_t hb = f32_to_bf16_rne(v[u]);
-          hi[u] = (uint16_t)hb;
-          lo[u] = (uint16_t)f32_to_bf16_rne(v[u] - __uint_as_float(hb << 16));
+          for (int u = 0; u < 8; ++u) {
+            const uint32_t hb = f32_to_bf16_rne(v[u]);
+            hi[u] = (uint16_t)hb;
+            lo[u] = (uint16_t)f32_to_bf16_rne(v[u] - __uint_as_float(hb << 16));
+          }
+          ah = __builtin_bit_cast(v8bf, hi);
+          al = __builtin_bit_cast(v8bf, lo);
         }
-        const v8bf ah = __builtin_bit_cast(v8bf, hi), al = __builtin_bit_cast(v8bf, lo);
 #pragma unroll
         for (int j = 0; j < TJ; ++j) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl[j], acc[i][j], 0, 0, 0);
@@ -325,43 +329,61 @@ __global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 
   }
 
   // ---- store -------------------------------------------------------------------------
-#pragma unroll
-  for (int i = 0; i < TI; ++i)
+  // Through a resource over this tile's rows of Y: rows past M fall outside its range
+  // and are dropped; columns past N are masked per 32-column tile (they may be the
+  // caller's row padding).  The host guarantees 128 * ldy * 4 < 2^32.
+  const uint32_t ysz = ydtype == 0 ? 4u : 2u;
+  const uint32_t ystep = (uint32_t)ldy * ysz;
+  // base: element (m0, n0); range: to the end of row m0 + rowsA - 1
+  const __amdgpu_buffer_rsrc_t rY = make_rsrc(static_cast<uint8_t*>(Y) + (m0 * ldy + n0) * ysz,
+                                              (uint32_t)rowsA * ystep - (uint32_t)n0 * ysz);
+  if (ydtype == 0) {
 #pragma unroll
     for (int j = 0; j < TJ; ++j) {
-      const int64_t c = n0 + wn + j * 32 + l32;
-      if (c >= nlim) continue;
+      if (n0 + wn + j * 32 + l32 >= nlim) continue;
 #pragma unroll
-      for (int a = 0; a < 16; ++a) {
-        const int64_t r = m0 + wm + i * 32 + 8 * (a >> 2) + 4 * kh + (a & 3);
-        if (r < mlim) {
-          if (ydtype == 0) reinterpret_cast<float*>(Y)[r * ldy + c] = acc[i][j][a];
-          else reinterpret_cast<uint16_t*>(Y)[r * ldy + c] = (uint16_t)f32_to_bf16_rne(acc[i][j][a]);
-        }
+      for (int i = 0; i < TI; ++i) {
+        const uint32_t o = (uint32_t)(wm + i * 32 + 4 * kh) * ystep + (uint32_t)(wn + j * 32 + l32) * 4u;
+#pragma unroll
+        for (int a = 0; a < 16; ++a)
+          buf_store4(__float_as_uint(acc[i][j][a]), rY, o + (uint32_t)(8 * (a >> 2) + (a & 3)) * ystep);
       }
     }
+  } else {
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      if (n0 + wn + j * 32 + l32 >= nlim) continue;
+#pragma unroll
+      for (int i = 0; i < TI; ++i) {
+        const uint32_t o = (uint32_t)(wm + i * 32 + 4 * kh) * ystep + (uint32_t)(wn + j * 32 + l32) * 2u;
+#pragma unroll
+        for (int a = 0; a < 16; ++a)
+          buf_store2((uint16_t)f32_to_bf16_rne(acc[i][j][a]), rY, o + (uint32_t)(8 * (a >> 2) + (a & 3)) * ystep);
+      }
+    }
+  }
 }
 
 }  // namespace
 
-template <int FMT, bool AF8>
+template <int FMT, bool MMA>
 static void launch_k2_t(const KernelLayer& L, int64_t M, const uint8_t* qX, const void* sX,
-                        const float* lora_act, void* Y, int64_t ldy, int ydtype, hipStream_t st) {
+                        const void* lora_act, void* Y, int64_t ldy, int ydtype, hipStream_t st) {
   const dim3 grid((unsigned)((L.N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM)), block(NTHREADS);
-  hipLaunchKernelGGL((k2_gemm<FMT, false, AF8>), grid, block, 0, st, qX, sX, M, L.qW, L.sW, L.N, L.K,
+  hipLaunchKernelGGL((k2_gemm<FMT, false, MMA>), grid, block, 0, st, qX, sX, M, L.qW, L.sW, L.N, L.K,
                      lora_act, L.L2t, L.rank, Y, ldy, ydtype, (int64_t)0, (int64_t)0, M, L.N,
                      (int32_t*)nullptr);
 }
 
 hipError_t launch_k2(const KernelLayer& L, int64_t M, const uint8_t* qX, const void* sX,
-                     const float* lora_act, void* Y, int64_t ldy, int ydtype, bool fp8_codes,
+                     const void* lora_act, void* Y, int64_t ldy, int ydtype, bool mma,
                      hipStream_t st) {
   if (L.fmt == 0) {
-    if (fp8_codes) launch_k2_t<0, true>(L, M, qX, sX, lora_act, Y, ldy, ydtype, st);
+    if (mma) launch_k2_t<0, true>(L, M, qX, sX, lora_act, Y, ldy, ydtype, st);
     else launch_k2_t<0, false>(L, M, qX, sX, lora_act, Y, ldy, ydtype, st);
   } else {
-    if (fp8_codes) return hipErrorInvalidValue;
-    launch_k2_t<1, false>(L, M, qX, sX, lora_act, Y, ldy, ydtype, st);
+    if (mma) launch_k2_t<1, true>(L, M, qX, sX, lora_act, Y, ldy, ydtype, st);
+    else launch_k2_t<1, false>(L, M, qX, sX, lora_act, Y, ldy, ydtype, st);
   }
   return hipGetLastError();
 }
@@ -370,7 +392,7 @@ hipError_t launch_k2_debug(const KernelLayer& L, int64_t M, const uint8_t* qX, i
                            int64_t n0, int64_t mt, int64_t nt, int32_t* out, hipStream_t st) {
   const dim3 grid((unsigned)((nt + BN - 1) / BN), (unsigned)((mt + BM - 1) / BM)), block(NTHREADS);
   hipLaunchKernelGGL((k2_gemm<0, true, false>), grid, block, 0, st, qX, (const void*)nullptr, M, L.qW,
-                     (const void*)nullptr, L.N, L.K, (const float*)nullptr, (const uint16_t*)nullptr,
+                     (const void*)nullptr, L.N, L.K, (const void*)nullptr, (const uint16_t*)nullptr,
                      0, (void*)nullptr, (int64_t)0, 0, m0, n0, m0 + mt, n0 + nt, out);
   return hipGetLastError();
 }

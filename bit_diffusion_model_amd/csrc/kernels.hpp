@@ -17,14 +17,15 @@ struct KernelLayer {
   const void* sW;
 };
 
-// fp8_codes (INT4 only): write the activation codes as one FP8 E4M3 byte each, [M][K],
-// instead of nibble pairs [M][K/2] (the form kernel 2 consumes without expanding).
+// mma: the activation side in the matrix-core operand form (INT4 codes as FP8 bytes
+// [M][K] and split scale words; lora_act as bf16 hi/lo rows) instead of the packed
+// storage form (4-bit codes [M][K/2], fp16 / E8M0 scales, fp32 lora_act).
 hipError_t launch_k1(const KernelLayer& L, int64_t M, const uint16_t* X, int64_t ldx, uint8_t* qX,
-                     void* sX, float* lora_act, bool fp8_codes, hipStream_t st);
+                     void* sX, void* lora_act, bool mma, hipStream_t st);
 
-// ydtype: 0 fp32, 1 bf16.  fp8_codes: qX holds FP8 bytes [M][K] (INT4 only).
+// ydtype: 0 fp32, 1 bf16.  mma: as for launch_k1.
 hipError_t launch_k2(const KernelLayer& L, int64_t M, const uint8_t* qX, const void* sX,
-                     const float* lora_act, void* Y, int64_t ldy, int ydtype, bool fp8_codes,
+                     const void* lora_act, void* Y, int64_t ldy, int ydtype, bool mma,
                      hipStream_t st);
 
 hipError_t launch_k2_debug(const KernelLayer& L, int64_t M, const uint8_t* qX, int64_t m0,

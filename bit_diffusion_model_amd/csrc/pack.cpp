@@ -647,4 +647,64 @@ svdq_status svdq_prepare_lowrank(int64_t K, int64_t N, int32_t rank, const float
   return ok();
 }
 
+svdq_status svdq_prepare_weights(int64_t K, int64_t N, int32_t fmt, const uint8_t* qW, const void* sW,
+                                 uint8_t* qW_out, void* sW_out) {
+  svdq_status st = check_dims(K, N, fmt);
+  if (st != SVDQ_OK) return st;
+  if (!qW || !sW || !qW_out || !sW_out) return fail(SVDQ_EINVAL, "required pointer is NULL");
+  const int64_t words = N * (K / 8);
+  const int64_t groups = K / group_of(fmt);
+  if (fmt == SVDQ_MXFP4_G32) {
+    std::memcpy(qW_out, qW, (size_t)(N * (K / 2)));
+    std::memcpy(sW_out, sW, (size_t)(groups * N));
+    return ok();
+  }
+  // codes: per 32-bit word (8 codes, code 2j in the low nibble of byte j), byte j of the
+  // output holds code 2j's magnitude in bits 0-2 and sign in bit 7, code 2j+1's
+  // magnitude in bits 4-6, and in bit 3 the sign of code 2j-1 (mod 8)
+  for (int64_t w = 0; w < words; ++w) {
+    uint32_t d;
+    std::memcpy(&d, qW + 4 * w, 4);
+    uint32_t o = 0;
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t lo = (d >> (8 * j)) & 0xF, hi = (d >> (8 * j + 4)) & 0xF;
+      const uint32_t hi_prev = (d >> (8 * ((j + 3) & 3) + 4)) & 0xF;
+      const uint32_t b = (lo & 7) | ((lo & 8) << 4) | ((hi & 7) << 4) | (hi_prev & 8);
+      o |= b << (8 * j);
+    }
+    std::memcpy(qW_out + 4 * w, &o, 4);
+  }
+  // scales: fp16 s = m * 2^e, m in [1, 2) -> word (fp16 bits of m) | (e + 9 + 127) << 16;
+  // s = 0 -> m = 0, byte 127
+  const uint16_t* s16 = static_cast<const uint16_t*>(sW);
+  uint32_t* o32 = static_cast<uint32_t*>(sW_out);
+  for (int64_t i = 0; i < groups * N; ++i) {
+    const uint16_t h = s16[i];
+    if (h & 0x8000u) return fail(SVDQ_ENUMERIC, "negative weight scale");
+    const uint32_t ex = (h >> 10) & 0x1F, mant = h & 0x3FF;
+    if (ex == 0x1F) return fail(SVDQ_ENUMERIC, "non-finite weight scale");
+    if (ex == 0 && mant == 0) {
+      o32[i] = 127u << 16;
+      continue;
+    }
+    int e;
+    uint32_t m10;
+    if (ex != 0) {
+      e = (int)ex - 15;
+      m10 = mant;
+    } else {  // subnormal: mant * 2^-24, normalise
+      int sh = 0;
+      uint32_t mm = mant;
+      while (!(mm & 0x400u)) {
+        mm <<= 1;
+        ++sh;
+      }
+      e = -14 - sh;
+      m10 = mm & 0x3FF;
+    }
+    o32[i] = ((15u << 10) | m10) | ((uint32_t)(e + 9 + 127) << 16);
+  }
+  return ok();
+}
+
 }  // extern "C"

@@ -18,6 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsvdq.so")
 
 INT4_G64, MXFP4_G32 = 0, 1
+ACT_PACKED, ACT_MMA = 0, 1  # svdq_act_form
 F32, BF16 = 0, 1
 FMT = {"int4": INT4_G64, "mxfp4": MXFP4_G32}
 GROUP = {INT4_G64: 64, MXFP4_G32: 32}
@@ -40,7 +41,7 @@ _lib = None
 
 EXPORTS = [
     "svdq_last_error", "svdq_act_absmax", "svdq_weight_sizes", "svdq_pack_weights",
-    "svdq_quantize_weights", "svdq_concat_lora", "svdq_prepare_lowrank",
+    "svdq_quantize_weights", "svdq_concat_lora", "svdq_prepare_lowrank", "svdq_prepare_weights",
     "svdq_quantize_act_lora_down", "svdq_gemm_w4a4_lora_up", "svdq_workspace_bytes",
     "svdq_linear_forward", "svdq_debug_group_sums",
 ]
@@ -63,8 +64,9 @@ def lib():
         "svdq_quantize_weights": (I32, [I64, I64, P, I32, P, P]),
         "svdq_concat_lora": (I32, [I64, I64, P, I32, P, P, I32, P, P, F, P, P]),
         "svdq_prepare_lowrank": (I32, [I64, I64, I32, P, P, P, P, P, P]),
-        "svdq_quantize_act_lora_down": (I32, [P, I64, P, I64, P, P, P, P]),
-        "svdq_gemm_w4a4_lora_up": (I32, [P, I64, P, P, P, P, I64, I32, P]),
+        "svdq_prepare_weights": (I32, [I64, I64, I32, P, P, P, P]),
+        "svdq_quantize_act_lora_down": (I32, [P, I64, P, I64, I32, P, P, P, P]),
+        "svdq_gemm_w4a4_lora_up": (I32, [P, I64, I32, P, P, P, P, I64, I32, P]),
         "svdq_workspace_bytes": (ctypes.c_size_t, [P, I64]),
         "svdq_linear_forward": (I32, [P, I64, P, I64, P, I64, I32, P, ctypes.c_size_t, P]),
         "svdq_debug_group_sums": (I32, [P, I64, P, I64, I64, I64, I64, P, P]),
@@ -178,6 +180,17 @@ def prepare_lowrank(inv_s: np.ndarray, L1t: np.ndarray, L2: np.ndarray):
     return hi, lo, L2t
 
 
+def prepare_weights(K: int, N: int, fmt: int, qW: np.ndarray, sW: np.ndarray):
+    """Kernel layout of the residual weights: (qW [N][K/2] u8, sW [K/G][N] u32 for INT4 /
+    u8 E8M0 for MXFP4)."""
+    qW = np.ascontiguousarray(qW, dtype=np.uint8)
+    sW = np.ascontiguousarray(sW)
+    qo = np.empty_like(qW)
+    so = np.empty((K // GROUP[fmt], N), np.uint32 if fmt == INT4_G64 else np.uint8)
+    _check(lib().svdq_prepare_weights(K, N, fmt, _ptr(qW), _ptr(sW), _ptr(qo), _ptr(so)))
+    return qo, so
+
+
 # ------------------------------------------------------------------ device side
 
 def _torch():
@@ -201,8 +214,8 @@ def _upload(a: np.ndarray, device):
     a = np.ascontiguousarray(a)
     if a.dtype == np.uint16:
         t = torch.from_numpy(a.view(np.int16))
-    elif a.dtype == np.uint8:
-        t = torch.from_numpy(a)
+    elif a.dtype == np.uint32:
+        t = torch.from_numpy(a.view(np.int32))
     else:
         t = torch.from_numpy(a)
     return t.to(device)
@@ -223,8 +236,9 @@ class PackedLinear:
             self.L2t = _upload(L2t, device)
         else:
             self.Ld_hi = self.Ld_lo = self.L2t = None
-        self.qW = _upload(np.asarray(qW, np.uint8), device)
-        self.sW = _upload(sW, device)
+        qk, sk = prepare_weights(self.K, self.N, self.fmt, qW, sW)
+        self.qW = _upload(qk, device)
+        self.sW = _upload(sk, device)
         self._c = _Layer(self.K, self.N, self.rank, self.fmt, _dptr(self.inv_s), _dptr(self.Ld_hi),
                          _dptr(self.Ld_lo), _dptr(self.L2t), _dptr(self.qW), _dptr(self.sW))
 
@@ -239,31 +253,41 @@ class PackedLinear:
     def c_layer(self):
         return ctypes.byref(self._c)
 
-    def alloc_act(self, M: int):
+    def alloc_act(self, M: int, form: int = ACT_PACKED):
+        """Device buffers for kernel 1's outputs in the given activation form."""
         torch = _torch()
-        qX = torch.empty((M, self.K // 2), dtype=torch.uint8, device=self.device)
-        sdt = torch.int16 if self.fmt == INT4_G64 else torch.uint8
+        mma8 = form == ACT_MMA and self.fmt == INT4_G64
+        qX = torch.empty((M, self.K if mma8 else self.K // 2), dtype=torch.uint8, device=self.device)
+        if self.fmt == INT4_G64:
+            sdt = torch.int32 if mma8 else torch.int16
+        else:
+            sdt = torch.uint8
         sX = torch.empty((self.K // self.group, M), dtype=sdt, device=self.device)
-        la = torch.empty((M, r16(self.rank)), dtype=torch.float32, device=self.device) if self.rank else None
+        la = None
+        if self.rank:
+            if form == ACT_MMA:
+                la = torch.empty((M, 2 * r16(self.rank)), dtype=torch.int16, device=self.device)
+            else:
+                la = torch.empty((M, r16(self.rank)), dtype=torch.float32, device=self.device)
         return qX, sX, la
 
-    def quantize_act(self, X, out=None):
+    def quantize_act(self, X, out=None, form: int = ACT_PACKED):
         """Kernel 1 on bf16 X [M][K] (torch tensor on the device)."""
         M = X.shape[0]
-        qX, sX, la = out if out is not None else self.alloc_act(M)
-        _check(lib().svdq_quantize_act_lora_down(self.c_layer(), M, _dptr(X), X.stride(0), _dptr(qX),
+        qX, sX, la = out if out is not None else self.alloc_act(M, form)
+        _check(lib().svdq_quantize_act_lora_down(self.c_layer(), M, _dptr(X), X.stride(0), form, _dptr(qX),
                                                  _dptr(sX), _dptr(la), _stream()))
         return qX, sX, la
 
-    def gemm(self, qX, sX, la, ydtype: int = F32, out=None):
-        """Kernel 2: Y [M][N] from kernel 1's outputs."""
+    def gemm(self, qX, sX, la, ydtype: int = F32, out=None, form: int = ACT_PACKED):
+        """Kernel 2: Y [M][N] from kernel 1's outputs (same activation form)."""
         torch = _torch()
         M = qX.shape[0]
         if out is None:
             out = torch.empty((M, self.N), dtype=torch.float32 if ydtype == F32 else torch.bfloat16,
                               device=self.device)
-        _check(lib().svdq_gemm_w4a4_lora_up(self.c_layer(), M, _dptr(qX), _dptr(sX), _dptr(la), _dptr(out),
-                                            out.stride(0), ydtype, _stream()))
+        _check(lib().svdq_gemm_w4a4_lora_up(self.c_layer(), M, form, _dptr(qX), _dptr(sX), _dptr(la),
+                                            _dptr(out), out.stride(0), ydtype, _stream()))
         return out
 
     def workspace(self, M: int):

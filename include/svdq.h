@@ -56,17 +56,33 @@ typedef enum {
 typedef enum { SVDQ_INT4_G64 = 0, SVDQ_MXFP4_G32 = 1 } svdq_format;
 typedef enum { SVDQ_F32 = 0, SVDQ_BF16 = 1 } svdq_dtype;
 
+/* How kernel 1 hands the activation side to kernel 2 (both calls must agree).
+ *   PACKED: the format's storage form: qX [M][K/2] 4-bit codes (INT4 sign-magnitude
+ *           nibbles, MXFP4 E2M1), sX [K/G][M] fp16 bits (INT4) or E8M0 bytes (MXFP4),
+ *           lora_act [M][R16] fp32.
+ *   MMA:    the matrix-core operand form, which kernel 2 uses without converting.
+ *           INT4: qX [M][K] one FP8 E4M3 byte per code (sign bit 7, magnitude in the
+ *           mantissa bits: value q * 2^-9), each 8-code block stored as codes
+ *           0,2,4,6,1,3,5,7; sX [K/64][M] u32 words (fp16 bits of m) | (e+9+127) << 16
+ *           for the fp16 scale s = m * 2^e, m in [1, 2) (s = 0: m = 0, byte 127).
+ *           MXFP4: qX and sX as PACKED.  Both: lora_act rows of 2*R16 bf16, [R16 hi]
+ *           [R16 lo] with hi = bf16(v), lo = bf16(v - hi) of the fp32 value v. */
+typedef enum { SVDQ_ACT_PACKED = 0, SVDQ_ACT_MMA = 1 } svdq_act_form;
+
 #define SVDQ_MAX_RANK 128
 
 /* Device-resident description of one packed layer (all pointers device memory,
- * owned by the caller, produced by svdq_pack_weights + svdq_prepare_lowrank).
+ * owned by the caller, produced by svdq_pack_weights, then svdq_prepare_lowrank and
+ * svdq_prepare_weights for the kernels' layouts).
  * R16 below is rank rounded up to a multiple of 16.
  *   inv_s  [K]        fp32  reciprocal smoothing factor, fp32(1 / fp32(s))
  *   Ld_hi  [rank][K]  bf16  high part of (diag(inv_s) L1)^T
  *   Ld_lo  [rank][K]  bf16  low part, so Ld_hi + Ld_lo = diag(inv_s) L1 to ~2^-17
  *   L2t    [N][R16]   bf16  up projection transposed (L2^T), columns >= rank zero
- *   qW     [N][K/2]   u8    residual codes, row n = output channel n along K
- *   sW     [K/G][N]   fp16 bits (INT4) or E8M0 bytes (MXFP4), group-major
+ *   qW     [N][K/2]   u8    residual codes, row n = output channel n along K, in the
+ *                           kernel bit order of svdq_prepare_weights
+ *   sW     [K/G][N]   group-major scales as svdq_prepare_weights writes them: split
+ *                           32-bit words (INT4, 4-byte aligned) or E8M0 bytes (MXFP4)
  * Ld_hi/Ld_lo/L2t may be NULL iff rank == 0. */
 typedef struct svdq_layer {
   int64_t K, N;
@@ -142,40 +158,55 @@ svdq_status svdq_prepare_lowrank(int64_t K, int64_t N, int32_t rank, const float
                                  const uint16_t* L1t, const uint16_t* L2, uint16_t* hi_out,
                                  uint16_t* lo_out, uint16_t* L2t_out);
 
+/* Offline device layout of the residual weights (host pointers).  The values are those
+ * of svdq_pack_weights / svdq_quantize_weights; only their encoding changes.
+ *   MXFP4: qW_out = qW, sW_out = sW (E8M0 bytes), copied.
+ *   INT4:  qW_out [N][K/2]: each 32-bit word of 8 sign-magnitude codes (code 2j in the
+ *          low nibble of byte j) is re-encoded so that byte j holds code 2j's magnitude
+ *          in bits 0-2 and sign in bit 7, code 2j+1's magnitude in bits 4-6, and in bit 3
+ *          the sign of code 2j-1 (indices mod 8): a mask then yields the even codes and
+ *          a 4-bit rotate plus the same mask the odd ones, as FP8 E4M3 bytes q * 2^-9.
+ *          sW_out [K/64][N] u32: the fp16 scale s = m * 2^e (m in [1, 2)) as
+ *          (fp16 bits of m) | (e + 9 + 127) << 16; s = 0 gives m = 0, byte 127.
+ * EINVAL on bad sizes, ENUMERIC on a negative or non-finite scale. */
+svdq_status svdq_prepare_weights(int64_t K, int64_t N, int32_t fmt, const uint8_t* qW,
+                                 const void* sW, uint8_t* qW_out, void* sW_out);
+
 /* ---------------------------------------------------------------- device side ---- */
 
 /* Kernel 1: smooth, quantize and down-project the activations in one pass over X
  * (review section 4.3: down projection fused with the quantization kernel, sharing
  * the activation read).
  *   X        device bf16 [M][ldx], 16-byte aligned rows (ldx % 8 == 0)
- *   qX       device u8 [M][K/2]           4-bit codes of X_hat = X diag(inv_s)
- *   sX       device [K/G][M]              fp16 bits (INT4) or E8M0 bytes (MXFP4)
- *   lora_act device fp32 [M][R16]         X_hat L1, columns >= rank written as zero
+ *   form     svdq_act_form of the outputs:
+ *   qX       device                       codes of X_hat = X diag(inv_s)
+ *   sX       device                       their group scales
+ *   lora_act device                       X_hat L1, columns >= rank written as zero
  *                                         (unused when rank == 0)
  * M == 0 is a no-op.  EINVAL on NULL / misalignment / ldx < K; EHIP on launch error. */
 svdq_status svdq_quantize_act_lora_down(const svdq_layer* layer, int64_t M, const uint16_t* X,
-                                        int64_t ldx, uint8_t* qX, void* sX, float* lora_act,
-                                        void* stream);
+                                        int64_t ldx, int32_t form, uint8_t* qX, void* sX,
+                                        void* lora_act, void* stream);
 
 /* Kernel 2: W4A4 GEMM on the codes with per-group rescaling by s_X s_W and the
  * low-rank up projection (lora_act L2) added in the epilogue (review section 4.3: up
  * projection fused with the 4-bit kernel).
- *   qX, sX, lora_act  as written by kernel 1 (device)
- *   Y                 device [M][ldy], fp32 or bf16 (ydtype), 16-byte aligned rows
+ *   form, qX, sX, lora_act  as written by kernel 1 (device)
+ *   Y                 device [M][ldy], fp32 or bf16 (ydtype); 128 * ldy * 4 < 2^32
  * Y is overwritten (no accumulation into existing contents). */
-svdq_status svdq_gemm_w4a4_lora_up(const svdq_layer* layer, int64_t M, const uint8_t* qX,
-                                   const void* sX, const float* lora_act, void* Y, int64_t ldy,
-                                   int32_t ydtype, void* stream);
+svdq_status svdq_gemm_w4a4_lora_up(const svdq_layer* layer, int64_t M, int32_t form,
+                                   const uint8_t* qX, const void* sX, const void* lora_act,
+                                   void* Y, int64_t ldy, int32_t ydtype, void* stream);
 
-/* Bytes of device workspace svdq_linear_forward needs for M rows (activation codes,
- * sX, lora_act, each 256-byte aligned).  For INT4 the forward path holds the
- * activation codes as one byte each (M*K bytes, the operand form of kernel 2's matrix
- * cores), for MXFP4 packed (M*K/2 bytes). */
+/* Bytes of device workspace svdq_linear_forward needs for M rows: the MMA-form qX,
+ * sX and lora_act, each 256-byte aligned. */
 size_t svdq_workspace_bytes(const svdq_layer* layer, int64_t M);
 
-/* The public layer: kernel 1 then kernel 2 on `stream`, intermediates in `workspace`
- * (device, >= svdq_workspace_bytes, 256-byte aligned).  Same arithmetic as the two
- * calls above in sequence: the results are identical bit for bit. */
+/* The public layer: kernel 1 then kernel 2 on `stream` with the activation side in
+ * MMA form, intermediates in `workspace` (device, >= svdq_workspace_bytes, 256-byte
+ * aligned).  The same launches as the two calls above with form = SVDQ_ACT_MMA: the
+ * results are identical bit for bit (PACKED gives the same values up to the rounding of
+ * the up projection's hi/lo split, which PACKED does in kernel 2). */
 svdq_status svdq_linear_forward(const svdq_layer* layer, int64_t M, const uint16_t* X,
                                 int64_t ldx, void* Y, int64_t ldy, int32_t ydtype,
                                 void* workspace, size_t ws_bytes, void* stream);

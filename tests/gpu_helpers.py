@@ -60,3 +60,39 @@ def lora_bound(Xh, L1b):
 def rel_err(Y, Yref):
     rms = np.sqrt(np.mean(Yref ** 2))
     return np.abs(Y - Yref).max() / rms
+
+
+def bf16_rne_bits(v32):
+    """fp32 array -> bf16 bits, round to nearest even (finite inputs)."""
+    u = np.ascontiguousarray(v32, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def decode_mma(qX, sX, la, fmt, K, rank):
+    """Kernel 1's MMA-form outputs (device tensors) decoded per the header's description:
+    INT4 codes from FP8 bytes (sign bit 7, magnitude bits 0-2; 8-code blocks stored as
+    codes 0,2,4,6,1,3,5,7) and scale values m * 2^(byte - 136); MXFP4 codes and E8M0 bytes
+    as stored; lora_act rows [R16 hi][R16 lo] bf16.  Returns (codes or packed bytes,
+    scales (float64 values for INT4, bytes for MXFP4), hi bits, lo bits)."""
+    q = qX.cpu().numpy()
+    M = q.shape[0]
+    if fmt == "int4":
+        b = q.reshape(M, K // 8, 8).astype(np.int64)
+        v = (b & 7) * np.where(b & 0x80, -1, 1)
+        assert not (b & 0x78).any()
+        codes = np.empty_like(v)
+        codes[:, :, 0::2], codes[:, :, 1::2] = v[:, :, :4], v[:, :, 4:]
+        w = sX.cpu().numpy().view(np.uint32)
+        m = (w & 0xFFFF).astype(np.uint16).view(np.float16).astype(np.float64)
+        e = ((w >> 16) & 0xFF).astype(np.int64) - 136
+        assert not (w >> 24).any()
+        sc = m * 2.0 ** e
+        out = codes.reshape(M, K), sc
+    else:
+        out = q, sX.cpu().numpy()
+    hi = lo = None
+    if rank:
+        R16 = (rank + 15) // 16 * 16
+        l = la.cpu().numpy().view(np.uint16).reshape(M, 2, R16)
+        hi, lo = l[:, 0, :], l[:, 1, :]
+    return out[0], out[1], hi, lo

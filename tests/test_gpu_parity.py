@@ -8,7 +8,8 @@ tails, K from 128 (the minimum) upward, ranks 0 / 1 / 8 / 48 / 128.
 import numpy as np
 import pytest
 
-from gpu_helpers import TOL_Y, layer_from_oracle, log, lora_bound, oracle_k1, oracle_pack, rel_err, to_dev_bf16
+from gpu_helpers import (TOL_Y, bf16_rne_bits, decode_mma, layer_from_oracle, log, lora_bound, oracle_k1,
+                         oracle_pack, rel_err, to_dev_bf16)
 
 from bit_diffusion_model_amd import svdq
 from bit_diffusion_model_amd.workloads import make, random_layer
@@ -52,6 +53,21 @@ def test_kernel1_codes_scales_lora(shape):
         la_g = la.cpu().numpy().astype(np.float64)
         assert la_g.shape[1] == svdq.r16(r) and not la_g[:, r:].any()
         assert np.all(np.abs(la_g[:, :r] - la_ref) <= lora_bound(Xh, p["L1b"]))
+    # the MMA form: the same codes and scales re-encoded, lora_act as the bf16 hi/lo
+    # split of the very fp32 values above
+    qm, sm, lam = lay.quantize_act(X, form=svdq.ACT_MMA)
+    c_m, s_m, hi, lo = decode_mma(qm, sm, lam, fmt, K, r)
+    if fmt == "int4":
+        np.testing.assert_array_equal(c_m, codes)
+        np.testing.assert_array_equal(s_m, sX_ref.view(np.float16).astype(np.float64))
+    else:
+        np.testing.assert_array_equal(c_m, qX_ref)
+        np.testing.assert_array_equal(s_m, sX_ref)
+    if r:
+        v = la.cpu().numpy()
+        np.testing.assert_array_equal(hi, bf16_rne_bits(v))
+        rem = v - (hi.astype(np.uint32) << 16).view(np.float32)
+        np.testing.assert_array_equal(lo, bf16_rne_bits(rem))
 
 
 @pytest.mark.parametrize("shape", [s for s in SHAPES if s[4] == "int4"], ids=_ids)
@@ -93,10 +109,17 @@ def test_forward_matches_oracle(shape):
         codes = np.empty_like(q)
         codes[:, :, 0::2], codes[:, :, 1::2] = q[:, :, :4], q[:, :, 4:]
         np.testing.assert_array_equal(codes.reshape(M, K), oforward.quantize_activations(wl.X, p["inv_s32"], fmt)[1])
-    # the two kernels called separately give the same bits as the public entry point
-    qX, sX, la = lay.quantize_act(to_dev_bf16(wl.X))
-    Y2 = lay.gemm(qX, sX, la).cpu().numpy()
+    # the two kernels called separately in MMA form give the same bits as the forward
+    X = to_dev_bf16(wl.X)
+    qX, sX, la = lay.quantize_act(X, form=svdq.ACT_MMA)
+    Y2 = lay.gemm(qX, sX, la, form=svdq.ACT_MMA).cpu().numpy()
     np.testing.assert_array_equal(Y2, Y.astype(np.float32))
+    # the packed form meets the same bar
+    qX, sX, la = lay.quantize_act(X)
+    Yp = lay.gemm(qX, sX, la).cpu().numpy().astype(np.float64)
+    ep = rel_err(Yp, Yref)
+    log(f"  packed form max|err|/RMS = {ep:.3e}")
+    assert ep <= TOL_Y
 
 
 def test_tiny_config_c0():

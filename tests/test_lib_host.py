@@ -148,6 +148,39 @@ def test_prepare_lowrank_layouts():
     assert not L2t[:, 5:].any()
 
 
+def test_prepare_weights_kernel_layout():
+    """The kernel layout decodes back to the oracle's codes and scales: even codes by the
+    mask 0x87, odd codes by a 4-bit rotate of the word and the same mask (FP8 E4M3 bytes
+    with zero exponent: magnitude in bits 0-2, sign in bit 7); each scale word is
+    m * 2^(byte - 127 - 9) with m the fp16 in its low half, m in [1, 2) or 0."""
+    rng = np.random.default_rng(11)
+    K, N = 256, 40
+    R = (rng.standard_normal((K, N)) * 10.0 ** rng.uniform(-9, 2, (1, N))).astype(np.float32)
+    R[:, 5] = 0.0
+    R[64:128, 6] = 0.0
+    codes, sc = opack.quantize_residual(R, "int4")
+    qW = opack.pack_codes(codes, "int4")
+    assert (sc.view(np.uint16) & 0x7C00 == 0).any(), "want subnormal fp16 scales in the case"
+    qk, sk = svdq.prepare_weights(K, N, svdq.INT4_G64, qW, sc)
+    words = qk.view("<u4").astype(np.uint64)
+    rot = ((words >> 4) | (words << 28)) & 0xFFFFFFFF
+    dec = np.empty((N, K // 8, 8), np.int64)
+    for src, off in ((words, 0), (rot, 1)):
+        for j in range(4):
+            b = (src >> (8 * j)) & 0x87
+            dec[:, :, 2 * j + off] = ((b & 7) * np.where(b & 0x80, -1, 1)).reshape(N, K // 8)
+    np.testing.assert_array_equal(dec.reshape(N, K), codes)
+    m = sk.astype(np.uint32)
+    mant = (m & 0xFFFF).astype(np.uint16).view(np.float16).astype(np.float64)
+    e = ((m >> 16) & 0xFF).astype(np.int64) - 127 - 9
+    assert np.all((mant == 0) | ((mant >= 1) & (mant < 2)))
+    np.testing.assert_array_equal(mant * 2.0 ** e, sc.view(np.float16).astype(np.float64))
+    c4, s4 = opack.quantize_residual(R, "mxfp4")
+    qf, sf = svdq.prepare_weights(K, N, svdq.MXFP4_G32, opack.pack_codes(c4, "mxfp4"), s4)
+    np.testing.assert_array_equal(qf, opack.pack_codes(c4, "mxfp4"))
+    np.testing.assert_array_equal(sf, s4)
+
+
 # ------------------------------------------------------------------ error paths
 
 def _err():
@@ -176,17 +209,23 @@ def test_device_entry_points_validate_on_host():
     lay = svdq._Layer(256, 64, 8, 0, 16, 16, 16, 16, 16, 16)  # fake aligned non-NULL pointers
     ref = ctypes.byref(lay)
     # M == 0 is a no-op that never touches the device
-    assert L.svdq_quantize_act_lora_down(ref, 0, None, 256, None, None, None, None) == 0
-    assert L.svdq_gemm_w4a4_lora_up(ref, 0, None, None, None, None, 64, 0, None) == 0
-    assert L.svdq_quantize_act_lora_down(None, 4, None, 256, None, None, None, None) == 1
+    assert L.svdq_quantize_act_lora_down(ref, 0, None, 256, 0, None, None, None, None) == 0
+    assert L.svdq_gemm_w4a4_lora_up(ref, 0, 0, None, None, None, None, 64, 0, None) == 0
+    assert L.svdq_quantize_act_lora_down(None, 4, None, 256, 0, None, None, None, None) == 1
     bad = svdq._Layer(200, 64, 8, 0, 16, 16, 16, 16, 16, 16)
-    assert L.svdq_quantize_act_lora_down(ctypes.byref(bad), 4, 16, 256, 16, 16, 16, None) == 1
+    assert L.svdq_quantize_act_lora_down(ctypes.byref(bad), 4, 16, 256, 0, 16, 16, 16, None) == 1
     big = svdq._Layer(256, 64, 129, 0, 16, 16, 16, 16, 16, 16)
-    assert L.svdq_gemm_w4a4_lora_up(ctypes.byref(big), 4, 16, 16, 16, 16, 64, 0, None) == 2
-    assert L.svdq_quantize_act_lora_down(ref, 4, 16, 100, 16, 16, 16, None) == 1 and "ldx" in _err()
-    assert L.svdq_quantize_act_lora_down(ref, 4, 18, 256, 16, 16, 16, None) == 1 and "aligned" in _err()
-    assert L.svdq_gemm_w4a4_lora_up(ref, 4, 16, 16, 16, 16, 32, 0, None) == 1 and "ldy" in _err()
-    assert L.svdq_gemm_w4a4_lora_up(ref, 4, 16, 16, 16, 16, 64, 5, None) == 2
+    assert L.svdq_gemm_w4a4_lora_up(ctypes.byref(big), 4, 0, 16, 16, 16, 16, 64, 0, None) == 2
+    assert L.svdq_quantize_act_lora_down(ref, 4, 16, 100, 0, 16, 16, 16, None) == 1 and "ldx" in _err()
+    assert L.svdq_quantize_act_lora_down(ref, 4, 18, 256, 0, 16, 16, 16, None) == 1 and "aligned" in _err()
+    assert L.svdq_quantize_act_lora_down(ref, 4, 16, 256, 2, 16, 16, 16, None) == 2 and "form" in _err()
+    assert L.svdq_gemm_w4a4_lora_up(ref, 4, 0, 16, 16, 16, 16, 32, 0, None) == 1 and "ldy" in _err()
+    assert L.svdq_gemm_w4a4_lora_up(ref, 4, 0, 16, 16, 16, 16, 1 << 23, 0, None) == 2 and "ldy" in _err()
+    assert L.svdq_gemm_w4a4_lora_up(ref, 4, 0, 16, 16, 16, 16, 64, 5, None) == 2
+    assert L.svdq_gemm_w4a4_lora_up(ref, 4, 7, 16, 16, 16, 16, 64, 0, None) == 2 and "form" in _err()
+    unal = svdq._Layer(256, 64, 8, 0, 16, 16, 16, 16, 16, 18)
+    assert L.svdq_gemm_w4a4_lora_up(ctypes.byref(unal), 4, 0, 16, 16, 16, 16, 64, 0, None) == 1 and "sW" in _err()
     assert L.svdq_linear_forward(ref, 4, 16, 256, 16, 64, 0, 256, 10, None) == 1 and "workspace" in _err()
     assert L.svdq_debug_group_sums(ref, 4, 16, 0, 0, 5, 4, 16, None) == 1 and "window" in _err()
-    assert L.svdq_workspace_bytes(ref, 100) >= 100 * 128 + 4 * 100 * 2 + 100 * 16 * 4
+    # MMA form: FP8 codes (M*K bytes), 4-byte scale words, 2*R16 bf16 per row
+    assert L.svdq_workspace_bytes(ref, 100) >= 100 * 256 + 4 * 100 * 4 + 100 * 16 * 4
