@@ -215,13 +215,14 @@ def main():
     # per-kernel durations, launched exactly as inside svdq_linear_forward (activation
     # side in MMA form), on the same (torch current) stream the events are recorded on
     qX, sX, la = lay.alloc_act(M, svdq.ACT_MMA)
+    gws = lay.gemm_workspace(M, svdq.ACT_MMA)
     nrep = max(args.steps, 10)
     e = [torch.cuda.Event(enable_timing=True) for _ in range(3 * nrep)]
     for i in range(nrep):
         e[3 * i].record()
         lay.quantize_act(X, (qX, sX, la), form=svdq.ACT_MMA)
         e[3 * i + 1].record()
-        lay.gemm(qX, sX, la, ydt, Y, form=svdq.ACT_MMA)
+        lay.gemm(qX, sX, la, ydt, Y, form=svdq.ACT_MMA, workspace=gws)
         e[3 * i + 2].record()
     torch.cuda.synchronize()
     t_k1 = float(np.mean([e[3 * i].elapsed_time(e[3 * i + 1]) for i in range(nrep)])) * 1e-3

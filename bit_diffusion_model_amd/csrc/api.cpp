@@ -61,7 +61,7 @@ static svdq_status check_layer(const svdq_layer* L, KernelLayer& kl) {
 static size_t rup(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct WsLayout {
-  size_t qx, sx, la, total;
+  size_t qx, sx, la, part, total;
 };
 // The forward path's workspace: the activation side in MMA form (INT4 codes as FP8
 // bytes [M][K] and split 32-bit scale words; MXFP4 packed codes and E8M0 bytes;
@@ -73,7 +73,9 @@ static WsLayout ws_layout(const svdq_layer* L, int64_t M) {
   w.sx = rup((size_t)M * (size_t)(f8 ? L->K : L->K / 2));
   const size_t ssz = f8 ? 4 : 1;
   w.la = w.sx + rup((size_t)(L->K / group_of(L->fmt)) * (size_t)M * ssz);
-  w.total = w.la + rup((size_t)M * (size_t)((L->rank + 15) / 16 * 16) * 4);
+  w.part = w.la + rup((size_t)M * (size_t)((L->rank + 15) / 16 * 16) * 4);
+  KernelLayer kl{L->K, L->N, L->rank, L->fmt, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+  w.total = w.part + rup(plan_k2(kl, M, true).bytes);
   return w;
 }
 
@@ -86,8 +88,14 @@ extern "C" {
 const char* svdq_last_error(void) { return g_err.c_str(); }
 
 size_t svdq_workspace_bytes(const svdq_layer* layer, int64_t M) {
-  if (!layer || M < 0 || layer->K < 0) return 0;
+  if (!layer || M < 0 || check_dims(layer->K, layer->N, layer->fmt) != SVDQ_OK) return 0;
   return ws_layout(layer, M).total;
+}
+
+size_t svdq_gemm_workspace_bytes(const svdq_layer* layer, int64_t M, int32_t form) {
+  if (!layer || M < 1 || check_dims(layer->K, layer->N, layer->fmt) != SVDQ_OK) return 0;
+  KernelLayer kl{layer->K, layer->N, layer->rank, layer->fmt, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+  return plan_k2(kl, M, form == SVDQ_ACT_MMA).bytes;
 }
 
 }  // extern "C"
@@ -119,7 +127,7 @@ static svdq_status run_k1(const svdq_layer* layer, int64_t M, const uint16_t* X,
 
 static svdq_status run_k2(const svdq_layer* layer, int64_t M, int32_t form, const uint8_t* qX,
                           const void* sX, const void* lora_act, void* Y, int64_t ldy,
-                          int32_t ydtype, void* stream) {
+                          int32_t ydtype, void* workspace, size_t ws_bytes, void* stream) {
   KernelLayer kl;
   svdq_status st = check_layer(layer, kl);
   if (st != SVDQ_OK) return st;
@@ -134,7 +142,9 @@ static svdq_status run_k2(const svdq_layer* layer, int64_t M, int32_t form, cons
   if (!aligned(qX, 16) || !aligned(Y, ydtype == SVDQ_F32 ? 4 : 2) || !aligned(sX, 2) ||
       (lora_act && !aligned(lora_act, 16)))
     return fail(SVDQ_EINVAL, "qX and lora_act must be 16-byte aligned and Y aligned to its element size");
-  hipError_t e = launch_k2(kl, M, qX, sX, lora_act, Y, ldy, ydtype, form == SVDQ_ACT_MMA, (hipStream_t)stream);
+  if (workspace && !aligned(workspace, 256)) return fail(SVDQ_EINVAL, "workspace must be 256-byte aligned");
+  hipError_t e = launch_k2(kl, M, qX, sX, lora_act, Y, ldy, ydtype, form == SVDQ_ACT_MMA, workspace,
+                           workspace ? ws_bytes : 0, (hipStream_t)stream);
   if (e != hipSuccess) return fail(SVDQ_EHIP, "kernel 2 launch: %s", hipGetErrorString(e));
   return ok();
 }
@@ -151,8 +161,9 @@ svdq_status svdq_quantize_act_lora_down(const svdq_layer* layer, int64_t M, cons
 
 svdq_status svdq_gemm_w4a4_lora_up(const svdq_layer* layer, int64_t M, int32_t form,
                                    const uint8_t* qX, const void* sX, const void* lora_act,
-                                   void* Y, int64_t ldy, int32_t ydtype, void* stream) {
-  return run_k2(layer, M, form, qX, sX, lora_act, Y, ldy, ydtype, stream);
+                                   void* Y, int64_t ldy, int32_t ydtype, void* workspace,
+                                   size_t ws_bytes, void* stream) {
+  return run_k2(layer, M, form, qX, sX, lora_act, Y, ldy, ydtype, workspace, ws_bytes, stream);
 }
 
 svdq_status svdq_linear_forward(const svdq_layer* layer, int64_t M, const uint16_t* X, int64_t ldx,
@@ -172,7 +183,7 @@ svdq_status svdq_linear_forward(const svdq_layer* layer, int64_t M, const uint16
   void* la = kl.rank > 0 ? base + w.la : nullptr;
   st = run_k1(layer, M, X, ldx, SVDQ_ACT_MMA, qX, sX, la, stream);
   if (st != SVDQ_OK) return st;
-  return run_k2(layer, M, SVDQ_ACT_MMA, qX, sX, la, Y, ldy, ydtype, stream);
+  return run_k2(layer, M, SVDQ_ACT_MMA, qX, sX, la, Y, ldy, ydtype, base + w.part, w.total - w.part, stream);
 }
 
 svdq_status svdq_debug_group_sums(const svdq_layer* layer, int64_t M, const uint8_t* qX, int64_t m0,

@@ -61,6 +61,43 @@ struct Smem {
   } st[2];
 };
 
+// Store one 32 x 32 accumulator (rows r_off.., columns c_off.. of the tile at m0, n0)
+// to Y through a resource over the tile's rows: rows past the end fall outside the range
+// and are dropped; columns past N are masked (they may be the caller's row padding).
+// The host guarantees 128 * ldy * 4 < 2^32.
+__device__ __forceinline__ void store_sub(const v16f& acc, void* Y, int64_t ldy, int ydtype, int64_t m0,
+                                          int64_t n0, int64_t rowsA, int64_t nlim, int r_off, int c_off,
+                                          int l32, int kh) {
+  if (n0 + c_off + l32 >= nlim) return;
+  const uint32_t ysz = ydtype == 0 ? 4u : 2u;
+  const uint32_t ystep = (uint32_t)ldy * ysz;
+  // base: element (m0, n0); range: to the end of row m0 + rowsA - 1
+  const __amdgpu_buffer_rsrc_t rY = make_rsrc(static_cast<uint8_t*>(Y) + (m0 * ldy + n0) * ysz,
+                                              (uint32_t)rowsA * ystep - (uint32_t)n0 * ysz);
+  const uint32_t o = (uint32_t)(r_off + 4 * kh) * ystep + (uint32_t)(c_off + l32) * ysz;
+  if (ydtype == 0) {
+#pragma unroll
+    for (int a = 0; a < 16; ++a)
+      buf_store4(__float_as_uint(acc[a]), rY, o + (uint32_t)(8 * (a >> 2) + (a & 3)) * ystep);
+  } else {
+#pragma unroll
+    for (int a = 0; a < 16; ++a)
+      buf_store2((uint16_t)f32_to_bf16_rne(acc[a]), rY, o + (uint32_t)(8 * (a >> 2) + (a & 3)) * ystep);
+  }
+}
+
+// Work split of one launch (see launch_k2): blocks [0, full) compute tiles 0 .. full-1
+// over the whole K; the remaining tiles full .. are each cut into `split` parts along K,
+// one block per part, which write fp32 partial tiles that k2_fixup adds up.
+struct K2Sched {
+  uint32_t tiles_n;  // tiles along N
+  uint32_t full;     // tiles computed whole
+  uint32_t split;    // parts per remaining tile (1: none remain)
+  float* partials;   // [remaining * split][4 waves][TI][TJ][16][64] fp32
+};
+constexpr int PART_FLOATS = 4 * TI * TJ * 16 * 64;  // one partial tile
+static_assert(TI == 2 && TJ == 2, "k2_fixup decodes (wave, i, j) for a 2 x 2 wave tile");
+
 struct Stage {
   uint4 a, a1, b;  // a1: second half of a 32-byte A piece (pre-expanded FP8 codes)
   uint32_t s;
@@ -76,7 +113,7 @@ __global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 
     const uint8_t* __restrict__ qW, const void* __restrict__ sWv, int64_t N, int64_t K,
     const void* __restrict__ lora_act, const uint16_t* __restrict__ L2, int rank,
     void* __restrict__ Y, int64_t ldy, int ydtype,
-    int64_t mbase, int64_t nbase, int64_t mlim, int64_t nlim, int32_t* __restrict__ dbg) {
+    int64_t mbase, int64_t nbase, int64_t mlim, int64_t nlim, K2Sched sch, int32_t* __restrict__ dbg) {
   using S = Smem<FMT>;
   __shared__ S sm;
   constexpr bool AF8 = MMA && FMT == 0;  // activation codes as FP8 bytes
@@ -87,11 +124,22 @@ __global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 
   const int kh = lane >> 5;
   const int wm = (wave >> 1) * WM;
   const int wn = (wave & 1) * WN;
-  const int64_t m0 = mbase + (int64_t)blockIdx.y * BM;
-  const int64_t n0 = nbase + (int64_t)blockIdx.x * BN;
   const uint32_t Kb = (uint32_t)(K >> 1);  // bytes per code row
   const uint32_t Ka = AF8 ? (uint32_t)K : Kb;  // bytes per A row
   const int nsteps = (int)(K >> 6);         // 64-wide K steps; even because K % 128 == 0
+  // tile and K range of this block; part < 0: the whole K
+  uint32_t t = blockIdx.x;
+  int part = -1, kbeg = 0, kend = nsteps;
+  if (t >= sch.full) {
+    const uint32_t u = t - sch.full;
+    t = sch.full + u / sch.split;
+    part = (int)(u % sch.split);
+    const int pairs = nsteps >> 1;  // parts start and end on even steps
+    kbeg = 2 * (int)(((uint32_t)part * pairs) / sch.split);
+    kend = 2 * (int)(((uint32_t)(part + 1) * pairs) / sch.split);
+  }
+  const int64_t m0 = mbase + (int64_t)(t / sch.tiles_n) * BM;
+  const int64_t n0 = nbase + (int64_t)(t % sch.tiles_n) * BN;
 
   // ---- buffer resources (range-checked loads) -------------------------------------
   const int64_t rowsA = mlim - m0 < BM ? mlim - m0 : BM;
@@ -265,11 +313,11 @@ __global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 
 
   // ---- main loop: loads two steps ahead, LDS double buffer, one barrier per step ----
   Stage r0, r1;
-  gload(r0, 0);
-  gload(r1, 1);
+  gload(r0, kbeg);
+  gload(r1, kbeg + 1);
   sstore(r0, 0);
   __syncthreads();
-  for (int s = 0; s < nsteps; s += 2) {
+  for (int s = kbeg; s < kend; s += 2) {
     // even step s: r0 is free (stored), r1 holds step s+1
     gload(r0, s + 2);
     compute(0, s);
@@ -288,7 +336,7 @@ __global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 
   // Both operands are rows of 16-padded arrays (lora_act [M][R16] fp32, L2t [N][R16]
   // bf16): lane (row or column l & 31, kh) reads the 8 consecutive ranks 16 t + 8 kh..,
   // and rows past M / columns past N read as zeros through the range check.
-  if (rank > 0) {
+  if (rank > 0 && part <= 0) {  // once per tile: whole, or the first part
     const int R16 = (rank + 15) & ~15;
     const __amdgpu_buffer_rsrc_t rL = make_rsrc(static_cast<const uint8_t*>(lora_act) + m0 * R16 * 4, (uint32_t)(rowsA * R16 * 4));
     const __amdgpu_buffer_rsrc_t rU = make_rsrc(L2 + n0 * R16, (uint32_t)(rowsB * R16 * 2));
@@ -328,72 +376,129 @@ __global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 
     }
   }
 
-  // ---- store -------------------------------------------------------------------------
-  // Through a resource over this tile's rows of Y: rows past M fall outside its range
-  // and are dropped; columns past N are masked per 32-column tile (they may be the
-  // caller's row padding).  The host guarantees 128 * ldy * 4 < 2^32.
-  const uint32_t ysz = ydtype == 0 ? 4u : 2u;
-  const uint32_t ystep = (uint32_t)ldy * ysz;
-  // base: element (m0, n0); range: to the end of row m0 + rowsA - 1
-  const __amdgpu_buffer_rsrc_t rY = make_rsrc(static_cast<uint8_t*>(Y) + (m0 * ldy + n0) * ysz,
-                                              (uint32_t)rowsA * ystep - (uint32_t)n0 * ysz);
-  if (ydtype == 0) {
+  // ---- store (or the partial tile) ------------------------------------------------------
+  if (part < 0) {
 #pragma unroll
-    for (int j = 0; j < TJ; ++j) {
-      if (n0 + wn + j * 32 + l32 >= nlim) continue;
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
-      for (int i = 0; i < TI; ++i) {
-        const uint32_t o = (uint32_t)(wm + i * 32 + 4 * kh) * ystep + (uint32_t)(wn + j * 32 + l32) * 4u;
-#pragma unroll
-        for (int a = 0; a < 16; ++a)
-          buf_store4(__float_as_uint(acc[i][j][a]), rY, o + (uint32_t)(8 * (a >> 2) + (a & 3)) * ystep);
-      }
-    }
+      for (int j = 0; j < TJ; ++j) store_sub(acc[i][j], Y, ldy, ydtype, m0, n0, rowsA, nlim, wm + i * 32, wn + j * 32, l32, kh);
   } else {
+    // partial tile, laid out per (wave, i, j): 16 x 64 floats, lane-contiguous
+    float* P = sch.partials + (size_t)(blockIdx.x - sch.full) * PART_FLOATS;
 #pragma unroll
-    for (int j = 0; j < TJ; ++j) {
-      if (n0 + wn + j * 32 + l32 >= nlim) continue;
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
-      for (int i = 0; i < TI; ++i) {
-        const uint32_t o = (uint32_t)(wm + i * 32 + 4 * kh) * ystep + (uint32_t)(wn + j * 32 + l32) * 2u;
+      for (int j = 0; j < TJ; ++j)
 #pragma unroll
-        for (int a = 0; a < 16; ++a)
-          buf_store2((uint16_t)f32_to_bf16_rne(acc[i][j][a]), rY, o + (uint32_t)(8 * (a >> 2) + (a & 3)) * ystep);
-      }
-    }
+        for (int a = 0; a < 16; ++a) P[(((wave * TI + i) * TJ + j) * 16 + a) * 64 + lane] = acc[i][j][a];
   }
+}
+
+// Sum of the `split` partial tiles of one remaining tile, in part order (the result does
+// not depend on which part finished first), stored like a whole tile.  One 64-thread
+// block per 32 x 32 sub-tile: blockIdx.x = remaining tile * 16 + (wave, i, j).
+__global__ __launch_bounds__(64) void k2_fixup(const float* __restrict__ partials, K2Sched sch, int64_t M,
+                                               int64_t N, void* __restrict__ Y, int64_t ldy, int ydtype) {
+  const int lane = threadIdx.x;
+  const uint32_t r = blockIdx.x >> 4, sub = blockIdx.x & 15;  // sub = (wave * TI + i) * TJ + j
+  const int w = (int)(sub >> 2), i = (int)((sub >> 1) & 1), j = (int)(sub & 1);
+  const uint32_t t = sch.full + r;
+  const int64_t m0 = (int64_t)(t / sch.tiles_n) * BM, n0 = (int64_t)(t % sch.tiles_n) * BN;
+  const float* P = partials + (size_t)r * sch.split * PART_FLOATS + (size_t)sub * 16 * 64 + lane;
+  v16f acc;
+#pragma unroll
+  for (int a = 0; a < 16; ++a) acc[a] = P[a * 64];
+  for (uint32_t p = 1; p < sch.split; ++p) {
+    const float* Q = P + (size_t)p * PART_FLOATS;
+#pragma unroll
+    for (int a = 0; a < 16; ++a) acc[a] += Q[a * 64];
+  }
+  const int64_t rowsA = M - m0 < BM ? M - m0 : BM;
+  store_sub(acc, Y, ldy, ydtype, m0, n0, rowsA, N, (w >> 1) * WM + i * 32, (w & 1) * WN + j * 32, lane & 31, lane >> 5);
 }
 
 }  // namespace
 
 template <int FMT, bool MMA>
 static void launch_k2_t(const KernelLayer& L, int64_t M, const uint8_t* qX, const void* sX,
-                        const void* lora_act, void* Y, int64_t ldy, int ydtype, hipStream_t st) {
-  const dim3 grid((unsigned)((L.N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM)), block(NTHREADS);
-  hipLaunchKernelGGL((k2_gemm<FMT, false, MMA>), grid, block, 0, st, qX, sX, M, L.qW, L.sW, L.N, L.K,
-                     lora_act, L.L2t, L.rank, Y, ldy, ydtype, (int64_t)0, (int64_t)0, M, L.N,
+                        const void* lora_act, void* Y, int64_t ldy, int ydtype, const K2Sched& sch,
+                        uint32_t nblocks, hipStream_t st) {
+  hipLaunchKernelGGL((k2_gemm<FMT, false, MMA>), dim3(nblocks), dim3(NTHREADS), 0, st, qX, sX, M, L.qW, L.sW,
+                     L.N, L.K, lora_act, L.L2t, L.rank, Y, ldy, ydtype, (int64_t)0, (int64_t)0, M, L.N, sch,
                      (int32_t*)nullptr);
+}
+
+template <int FMT, bool MMA>
+static int blocks_per_cu() {
+  static int n = 0;  // per kernel instance; the same on every MI355X device
+  if (n == 0) {
+    int v = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, k2_gemm<FMT, false, MMA>, NTHREADS, 0) != hipSuccess || v < 1) v = 1;
+    n = v;
+  }
+  return n;
+}
+
+static int blocks_per_cu(int fmt, bool mma) {
+  if (fmt == 0) return mma ? blocks_per_cu<0, true>() : blocks_per_cu<0, false>();
+  return mma ? blocks_per_cu<1, true>() : blocks_per_cu<1, false>();
+}
+
+K2Plan plan_k2(const KernelLayer& L, int64_t M, bool mma) {
+  K2Plan p{};
+  p.tiles_m = (uint32_t)((M + BM - 1) / BM);
+  p.tiles_n = (uint32_t)((L.N + BN - 1) / BN);
+  const uint32_t T = p.tiles_m * p.tiles_n;
+  p.full = T;
+  p.split = 1;
+  p.bytes = 0;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    return p;
+  const uint32_t G = (uint32_t)cus * (uint32_t)blocks_per_cu(L.fmt, mma);  // blocks resident at once
+  const uint32_t R = T % G;  // tiles of the last, partly filled round
+  const uint32_t nsteps = (uint32_t)(L.K >> 6);
+  uint32_t S = R ? G / R : 1;
+  if (S > nsteps / 4) S = nsteps / 4;  // parts of at least 4 K steps
+  if (S > 16) S = 16;
+  if (R == 0 || S < 2) return p;
+  p.full = T - R;
+  p.split = S;
+  p.bytes = (size_t)R * S * PART_FLOATS * sizeof(float);
+  return p;
 }
 
 hipError_t launch_k2(const KernelLayer& L, int64_t M, const uint8_t* qX, const void* sX,
                      const void* lora_act, void* Y, int64_t ldy, int ydtype, bool mma,
-                     hipStream_t st) {
-  if (L.fmt == 0) {
-    if (mma) launch_k2_t<0, true>(L, M, qX, sX, lora_act, Y, ldy, ydtype, st);
-    else launch_k2_t<0, false>(L, M, qX, sX, lora_act, Y, ldy, ydtype, st);
-  } else {
-    if (mma) launch_k2_t<1, true>(L, M, qX, sX, lora_act, Y, ldy, ydtype, st);
-    else launch_k2_t<1, false>(L, M, qX, sX, lora_act, Y, ldy, ydtype, st);
+                     void* workspace, size_t ws_bytes, hipStream_t st) {
+  K2Plan p = plan_k2(L, M, mma);
+  if (!workspace || ws_bytes < p.bytes || p.split < 2) {  // no split: every tile whole
+    p.full = p.tiles_m * p.tiles_n;
+    p.split = 1;
   }
+  const uint32_t T = p.tiles_m * p.tiles_n, rem = T - p.full;
+  const K2Sched sch{p.tiles_n, p.full, p.split, static_cast<float*>(workspace)};
+  const uint32_t nblocks = p.full + rem * p.split;
+  if (L.fmt == 0) {
+    if (mma) launch_k2_t<0, true>(L, M, qX, sX, lora_act, Y, ldy, ydtype, sch, nblocks, st);
+    else launch_k2_t<0, false>(L, M, qX, sX, lora_act, Y, ldy, ydtype, sch, nblocks, st);
+  } else {
+    if (mma) launch_k2_t<1, true>(L, M, qX, sX, lora_act, Y, ldy, ydtype, sch, nblocks, st);
+    else launch_k2_t<1, false>(L, M, qX, sX, lora_act, Y, ldy, ydtype, sch, nblocks, st);
+  }
+  if (rem > 0)
+    hipLaunchKernelGGL(k2_fixup, dim3(rem * 16), dim3(64), 0, st, static_cast<const float*>(workspace), sch, M,
+                       L.N, Y, ldy, ydtype);
   return hipGetLastError();
 }
 
 hipError_t launch_k2_debug(const KernelLayer& L, int64_t M, const uint8_t* qX, int64_t m0,
                            int64_t n0, int64_t mt, int64_t nt, int32_t* out, hipStream_t st) {
-  const dim3 grid((unsigned)((nt + BN - 1) / BN), (unsigned)((mt + BM - 1) / BM)), block(NTHREADS);
-  hipLaunchKernelGGL((k2_gemm<0, true, false>), grid, block, 0, st, qX, (const void*)nullptr, M, L.qW,
-                     (const void*)nullptr, L.N, L.K, (const void*)nullptr, (const uint16_t*)nullptr,
-                     0, (void*)nullptr, (int64_t)0, 0, m0, n0, m0 + mt, n0 + nt, out);
+  const uint32_t tn = (uint32_t)((nt + BN - 1) / BN), tm = (uint32_t)((mt + BM - 1) / BM);
+  const K2Sched sch{tn, tm * tn, 1, nullptr};
+  hipLaunchKernelGGL((k2_gemm<0, true, false>), dim3(tm * tn), dim3(NTHREADS), 0, st, qX, (const void*)nullptr, M,
+                     L.qW, (const void*)nullptr, L.N, L.K, (const void*)nullptr, (const uint16_t*)nullptr, 0,
+                     (void*)nullptr, (int64_t)0, 0, m0, n0, m0 + mt, n0 + nt, sch, out);
   return hipGetLastError();
 }
 

@@ -23,10 +23,20 @@ struct KernelLayer {
 hipError_t launch_k1(const KernelLayer& L, int64_t M, const uint16_t* X, int64_t ldx, uint8_t* qX,
                      void* sX, void* lora_act, bool mma, hipStream_t st);
 
-// ydtype: 0 fp32, 1 bf16.  mma: as for launch_k1.
+// Work split of kernel 2 on the current device: tiles [0, full) whole, the remaining
+// tiles (those of a last, partly filled round of resident blocks) cut into `split` parts
+// along K whose fp32 partial tiles take `bytes` of workspace.
+struct K2Plan {
+  uint32_t tiles_m, tiles_n, full, split;
+  size_t bytes;
+};
+K2Plan plan_k2(const KernelLayer& L, int64_t M, bool mma);
+
+// ydtype: 0 fp32, 1 bf16.  mma: as for launch_k1.  workspace (device, may be NULL): used
+// for the split when it holds plan_k2's bytes; otherwise every tile is computed whole.
 hipError_t launch_k2(const KernelLayer& L, int64_t M, const uint8_t* qX, const void* sX,
                      const void* lora_act, void* Y, int64_t ldy, int ydtype, bool mma,
-                     hipStream_t st);
+                     void* workspace, size_t ws_bytes, hipStream_t st);
 
 hipError_t launch_k2_debug(const KernelLayer& L, int64_t M, const uint8_t* qX, int64_t m0,
                            int64_t n0, int64_t mt, int64_t nt, int32_t* out, hipStream_t st);

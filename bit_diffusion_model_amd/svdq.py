@@ -42,7 +42,7 @@ _lib = None
 EXPORTS = [
     "svdq_last_error", "svdq_act_absmax", "svdq_weight_sizes", "svdq_pack_weights",
     "svdq_quantize_weights", "svdq_concat_lora", "svdq_prepare_lowrank", "svdq_prepare_weights",
-    "svdq_quantize_act_lora_down", "svdq_gemm_w4a4_lora_up", "svdq_workspace_bytes",
+    "svdq_quantize_act_lora_down", "svdq_gemm_w4a4_lora_up", "svdq_gemm_workspace_bytes", "svdq_workspace_bytes",
     "svdq_linear_forward", "svdq_debug_group_sums",
 ]
 
@@ -66,7 +66,8 @@ def lib():
         "svdq_prepare_lowrank": (I32, [I64, I64, I32, P, P, P, P, P, P]),
         "svdq_prepare_weights": (I32, [I64, I64, I32, P, P, P, P]),
         "svdq_quantize_act_lora_down": (I32, [P, I64, P, I64, I32, P, P, P, P]),
-        "svdq_gemm_w4a4_lora_up": (I32, [P, I64, I32, P, P, P, P, I64, I32, P]),
+        "svdq_gemm_w4a4_lora_up": (I32, [P, I64, I32, P, P, P, P, I64, I32, P, ctypes.c_size_t, P]),
+        "svdq_gemm_workspace_bytes": (ctypes.c_size_t, [P, I64, I32]),
         "svdq_workspace_bytes": (ctypes.c_size_t, [P, I64]),
         "svdq_linear_forward": (I32, [P, I64, P, I64, P, I64, I32, P, ctypes.c_size_t, P]),
         "svdq_debug_group_sums": (I32, [P, I64, P, I64, I64, I64, I64, P, P]),
@@ -209,6 +210,10 @@ def _stream():
     return ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream)
 
 
+def torch_uint8():
+    return _torch().uint8
+
+
 def _upload(a: np.ndarray, device):
     torch = _torch()
     a = np.ascontiguousarray(a)
@@ -279,15 +284,21 @@ class PackedLinear:
                                                  _dptr(sX), _dptr(la), _stream()))
         return qX, sX, la
 
-    def gemm(self, qX, sX, la, ydtype: int = F32, out=None, form: int = ACT_PACKED):
+    def gemm_workspace(self, M: int, form: int = ACT_PACKED):
+        """Device scratch for kernel 2's split of its last round (None when unused)."""
+        n = lib().svdq_gemm_workspace_bytes(self.c_layer(), M, form)
+        return _torch().empty(n, dtype=torch_uint8(), device=self.device) if n else None
+
+    def gemm(self, qX, sX, la, ydtype: int = F32, out=None, form: int = ACT_PACKED, workspace=None):
         """Kernel 2: Y [M][N] from kernel 1's outputs (same activation form)."""
         torch = _torch()
         M = qX.shape[0]
         if out is None:
             out = torch.empty((M, self.N), dtype=torch.float32 if ydtype == F32 else torch.bfloat16,
                               device=self.device)
+        nws = 0 if workspace is None else workspace.numel() * workspace.element_size()
         _check(lib().svdq_gemm_w4a4_lora_up(self.c_layer(), M, form, _dptr(qX), _dptr(sX), _dptr(la),
-                                            _dptr(out), out.stride(0), ydtype, _stream()))
+                                            _dptr(out), out.stride(0), ydtype, _dptr(workspace), nws, _stream()))
         return out
 
     def workspace(self, M: int):

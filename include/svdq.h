@@ -193,20 +193,30 @@ svdq_status svdq_quantize_act_lora_down(const svdq_layer* layer, int64_t M, cons
  * projection fused with the 4-bit kernel).
  *   form, qX, sX, lora_act  as written by kernel 1 (device)
  *   Y                 device [M][ldy], fp32 or bf16 (ydtype); 128 * ldy * 4 < 2^32
+ *   workspace         optional device scratch (NULL / ws_bytes 0: none), 256-byte
+ *                     aligned.  With at least svdq_gemm_workspace_bytes bytes, the
+ *                     128 x 128 output tiles that would form a last, partly filled round
+ *                     of resident blocks are split along K, their fp32 partial tiles
+ *                     kept there and added in a fixed order by a second kernel; the
+ *                     result is deterministic for a given device and workspace choice.
  * Y is overwritten (no accumulation into existing contents). */
 svdq_status svdq_gemm_w4a4_lora_up(const svdq_layer* layer, int64_t M, int32_t form,
                                    const uint8_t* qX, const void* sX, const void* lora_act,
-                                   void* Y, int64_t ldy, int32_t ydtype, void* stream);
+                                   void* Y, int64_t ldy, int32_t ydtype, void* workspace,
+                                   size_t ws_bytes, void* stream);
 
-/* Bytes of device workspace svdq_linear_forward needs for M rows: the MMA-form qX,
- * sX and lora_act, each 256-byte aligned. */
+/* Workspace bytes kernel 2 uses for its split on the current device (0: no split). */
+size_t svdq_gemm_workspace_bytes(const svdq_layer* layer, int64_t M, int32_t form);
+
+/* Bytes of device workspace svdq_linear_forward needs for M rows on the current device:
+ * the MMA-form qX, sX and lora_act and kernel 2's split workspace, each 256-byte
+ * aligned. */
 size_t svdq_workspace_bytes(const svdq_layer* layer, int64_t M);
 
 /* The public layer: kernel 1 then kernel 2 on `stream` with the activation side in
  * MMA form, intermediates in `workspace` (device, >= svdq_workspace_bytes, 256-byte
- * aligned).  The same launches as the two calls above with form = SVDQ_ACT_MMA: the
- * results are identical bit for bit (PACKED gives the same values up to the rounding of
- * the up projection's hi/lo split, which PACKED does in kernel 2). */
+ * aligned).  The same launches as the two calls above with form = SVDQ_ACT_MMA and
+ * kernel 2 given its split workspace: the results are identical bit for bit. */
 svdq_status svdq_linear_forward(const svdq_layer* layer, int64_t M, const uint16_t* X,
                                 int64_t ldx, void* Y, int64_t ldy, int32_t ydtype,
                                 void* workspace, size_t ws_bytes, void* stream);

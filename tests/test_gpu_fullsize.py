@@ -80,8 +80,12 @@ def test_full_size_layer(name):
             np.testing.assert_array_equal(I, I_ref)
         log("  group sums exact")
     rng = np.random.default_rng(7)
-    rows = np.unique(np.concatenate([rng.choice(wl.M, 48, replace=False), [0, wl.M - 1]]))
-    cols = np.unique(np.concatenate([rng.choice(wl.N, 48, replace=False), [0, wl.N - 1]]))
+    # random rows and columns, plus some from the last tile row and column (the tiles
+    # kernel 2 may split along K)
+    rows = np.unique(np.concatenate([rng.choice(wl.M, 48, replace=False), [0, wl.M - 1],
+                                     rng.choice(np.arange((wl.M - 1) // 128 * 128, wl.M), 8)]))
+    cols = np.unique(np.concatenate([rng.choice(wl.N, 48, replace=False), [0, wl.N - 1],
+                                     rng.choice(np.arange(wl.N // 2, wl.N), 8)]))
     Yg = Y.cpu().numpy()[np.ix_(rows, cols)].astype(np.float64)
     out = oforward.forward(wl.X, p, rows=rows, cols=cols)
     e = rel_err(Yg, out["Y"])

@@ -27,6 +27,9 @@ SHAPES = [  # M, K, N, rank, fmt
     (64, 256, 256, 8, "mxfp4"),
     (17, 128, 33, 1, "mxfp4"),
     (300, 384, 520, 16, "mxfp4"),
+    # K long enough that kernel 2 splits its tiles along K (few tiles, >= 8 K steps)
+    (200, 1024, 300, 8, "int4"),
+    (130, 768, 260, 16, "mxfp4"),
 ]
 
 
@@ -109,11 +112,19 @@ def test_forward_matches_oracle(shape):
         codes = np.empty_like(q)
         codes[:, :, 0::2], codes[:, :, 1::2] = q[:, :, :4], q[:, :, 4:]
         np.testing.assert_array_equal(codes.reshape(M, K), oforward.quantize_activations(wl.X, p["inv_s32"], fmt)[1])
-    # the two kernels called separately in MMA form give the same bits as the forward
+    # the two kernels called separately in MMA form, kernel 2 with its split workspace,
+    # give the same bits as the forward; without the workspace (no split) the same bar
     X = to_dev_bf16(wl.X)
     qX, sX, la = lay.quantize_act(X, form=svdq.ACT_MMA)
-    Y2 = lay.gemm(qX, sX, la, form=svdq.ACT_MMA).cpu().numpy()
+    gws = lay.gemm_workspace(M, svdq.ACT_MMA)
+    Y2 = lay.gemm(qX, sX, la, form=svdq.ACT_MMA, workspace=gws).cpu().numpy()
     np.testing.assert_array_equal(Y2, Y.astype(np.float32))
+    Yn = lay.gemm(qX, sX, la, form=svdq.ACT_MMA).cpu().numpy().astype(np.float64)
+    en = rel_err(Yn, Yref)
+    log(f"  unsplit kernel 2 max|err|/RMS = {en:.3e} (split workspace {0 if gws is None else gws.numel()} B)")
+    assert en <= TOL_Y
+    if K >= 768:
+        assert gws is not None, "expected kernel 2 to split this shape"
     # the packed form meets the same bar
     qX, sX, la = lay.quantize_act(X)
     Yp = lay.gemm(qX, sX, la).cpu().numpy().astype(np.float64)

@@ -210,21 +210,22 @@ def test_device_entry_points_validate_on_host():
     ref = ctypes.byref(lay)
     # M == 0 is a no-op that never touches the device
     assert L.svdq_quantize_act_lora_down(ref, 0, None, 256, 0, None, None, None, None) == 0
-    assert L.svdq_gemm_w4a4_lora_up(ref, 0, 0, None, None, None, None, 64, 0, None) == 0
+    assert L.svdq_gemm_w4a4_lora_up(ref, 0, 0, None, None, None, None, 64, 0, None, 0, None) == 0
     assert L.svdq_quantize_act_lora_down(None, 4, None, 256, 0, None, None, None, None) == 1
     bad = svdq._Layer(200, 64, 8, 0, 16, 16, 16, 16, 16, 16)
     assert L.svdq_quantize_act_lora_down(ctypes.byref(bad), 4, 16, 256, 0, 16, 16, 16, None) == 1
     big = svdq._Layer(256, 64, 129, 0, 16, 16, 16, 16, 16, 16)
-    assert L.svdq_gemm_w4a4_lora_up(ctypes.byref(big), 4, 0, 16, 16, 16, 16, 64, 0, None) == 2
+    assert L.svdq_gemm_w4a4_lora_up(ctypes.byref(big), 4, 0, 16, 16, 16, 16, 64, 0, None, 0, None) == 2
     assert L.svdq_quantize_act_lora_down(ref, 4, 16, 100, 0, 16, 16, 16, None) == 1 and "ldx" in _err()
     assert L.svdq_quantize_act_lora_down(ref, 4, 18, 256, 0, 16, 16, 16, None) == 1 and "aligned" in _err()
     assert L.svdq_quantize_act_lora_down(ref, 4, 16, 256, 2, 16, 16, 16, None) == 2 and "form" in _err()
-    assert L.svdq_gemm_w4a4_lora_up(ref, 4, 0, 16, 16, 16, 16, 32, 0, None) == 1 and "ldy" in _err()
-    assert L.svdq_gemm_w4a4_lora_up(ref, 4, 0, 16, 16, 16, 16, 1 << 23, 0, None) == 2 and "ldy" in _err()
-    assert L.svdq_gemm_w4a4_lora_up(ref, 4, 0, 16, 16, 16, 16, 64, 5, None) == 2
-    assert L.svdq_gemm_w4a4_lora_up(ref, 4, 7, 16, 16, 16, 16, 64, 0, None) == 2 and "form" in _err()
+    assert L.svdq_gemm_w4a4_lora_up(ref, 4, 0, 16, 16, 16, 16, 32, 0, None, 0, None) == 1 and "ldy" in _err()
+    assert L.svdq_gemm_w4a4_lora_up(ref, 4, 0, 16, 16, 16, 16, 1 << 23, 0, None, 0, None) == 2 and "ldy" in _err()
+    assert L.svdq_gemm_w4a4_lora_up(ref, 4, 0, 16, 16, 16, 16, 64, 5, None, 0, None) == 2
+    assert L.svdq_gemm_w4a4_lora_up(ref, 4, 7, 16, 16, 16, 16, 64, 0, None, 0, None) == 2 and "form" in _err()
     unal = svdq._Layer(256, 64, 8, 0, 16, 16, 16, 16, 16, 18)
-    assert L.svdq_gemm_w4a4_lora_up(ctypes.byref(unal), 4, 0, 16, 16, 16, 16, 64, 0, None) == 1 and "sW" in _err()
+    assert L.svdq_gemm_w4a4_lora_up(ctypes.byref(unal), 4, 0, 16, 16, 16, 16, 64, 0, None, 0, None) == 1 and "sW" in _err()
+    assert L.svdq_gemm_w4a4_lora_up(ref, 4, 0, 16, 16, 16, 16, 64, 0, 8, 1 << 20, None) == 1 and "workspace" in _err()
     assert L.svdq_linear_forward(ref, 4, 16, 256, 16, 64, 0, 256, 10, None) == 1 and "workspace" in _err()
     assert L.svdq_debug_group_sums(ref, 4, 16, 0, 0, 5, 4, 16, None) == 1 and "window" in _err()
     # MMA form: FP8 codes (M*K bytes), 4-byte scale words, 2*R16 bf16 per row
