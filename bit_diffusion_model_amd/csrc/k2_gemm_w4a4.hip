@@ -23,13 +23,14 @@
 //    activations as bf16 hi/lo pairs, so the main loop converts only the weights.
 //
 // Tiling: a 256-thread block (4 waves) owns a 128 x 128 output tile; wave w owns rows
-// 64*(w/2) .. +63 and columns 64*(w%2) .. +63, i.e. 2 x 2 MFMA tiles of 32 x 32; two
-// blocks share a CU, so one block's barrier and staging overlap the other's math.  Per
-// 64-wide K step the block stages both operand panels through LDS (double buffered,
-// rows padded so that 8 consecutive rows of 16-byte accesses hit distinct banks); the
-// codes are expanded once per block there.  Global loads run two K steps ahead of the
-// MFMAs through a two-deep register ring and use buffer resources, whose range check
-// returns zeros for the rows past the end of the matrix.
+// 64*(w/2) .. +63 and columns 64*(w%2) .. +63, i.e. 2 x 2 MFMA tiles of 32 x 32; two or
+// more blocks share a CU, so one block's barrier and staging overlap another's math.
+// K advances in stages of SUB 64-wide sub-steps (one INT4 group, two FP4 groups each):
+// per stage the block stages both operand panels through LDS (double buffered, rows
+// padded so that 8 consecutive rows of 16-byte accesses hit distinct banks), the codes
+// are expanded once per block there, and one barrier covers SUB sub-steps of MFMAs and
+// rescales.  The next stage's global loads are issued before the current stage's math,
+// through buffer resources whose range check returns zeros past the end of the matrix.
 //
 // 32x32x64 operand layout (measured): lane l supplies row/column l & 31; for FP4 it
 // holds the 32 consecutive K values 32*(l>>5).. with the block scale of that half; for
@@ -47,15 +48,15 @@ constexpr int BM = 128, BN = 128, NTHREADS = 256;
 constexpr int WM = 64, WN = 64;  // wave tile; waves form a 2 x 2 grid
 constexpr int TI = WM / 32, TJ = WN / 32;
 
-template <int FMT>
+template <int FMT, int SUB>
 struct Smem {
-  // operand row pitch in bytes: INT4 expands 32 code bytes to 64 FP8 bytes
-  static constexpr int kRow = FMT == 0 ? 64 : 32;
-  static constexpr int kPitch = kRow + 16;
-  // one K step's panels and scales
+  // operand bytes per row and 64-wide sub-step: INT4 expands 32 code bytes to 64 FP8
+  static constexpr int kSub = FMT == 0 ? 64 : 32;
+  static constexpr int kPitch = SUB * kSub + 16;
+  // one stage's panels and scales
   struct Stage {
-    _Float16 m[BM + BN];  // INT4 scale mantissas: X rows, then W columns
-    uint32_t e[BM + BN];  // E8M0 bytes (MXFP4: groups 2s and 2s+1 in bytes 0 and 1)
+    _Float16 m[FMT == 0 ? SUB : 1][BM + BN];  // INT4 scale mantissas: X rows, then W columns
+    uint32_t e[SUB][BM + BN];  // E8M0 bytes (MXFP4: the sub-step's two groups in bytes 0, 1)
     uint8_t A[BM * kPitch];
     uint8_t B[BN * kPitch];
   } st[2];
@@ -96,25 +97,28 @@ struct K2Sched {
   float* partials;   // [remaining * split][4 waves][TI][TJ][16][64] fp32
 };
 constexpr int PART_FLOATS = 4 * TI * TJ * 16 * 64;  // one partial tile
-static_assert(TI == 2 && TJ == 2, "k2_fixup decodes (wave, i, j) for a 2 x 2 wave tile");
+static_assert(TI == 2 && TJ == 2, "k2_fixup and the rescale schedule assume a 2 x 2 wave tile");
 
+// One stage's global loads of one thread: INT4 activation codes as FP8 bytes take two
+// 16-byte pieces per sub-step, 4-bit codes one.
+template <int SUB>
 struct Stage {
-  uint4 a, a1, b;  // a1: second half of a 32-byte A piece (pre-expanded FP8 codes)
-  uint32_t s;
+  uint4 a[2 * SUB], b[SUB];
+  uint32_t s[SUB];
 };
 
 // MMA: the activation side arrives in kernel 1's operand form: INT4 codes as FP8 bytes
 // [M][K], each 8-element block in the order of the weights' expansion (even elements,
 // then odd ones), so the A panel is copied to LDS without conversion, and INT4 scales
 // as split words [K/64][M]; lora_act as bf16 rows [R16 hi][R16 lo] (both formats).
-template <int FMT, bool DEBUG, bool MMA>
+template <int FMT, bool DEBUG, bool MMA, int SUB>
 __global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void k2_gemm(
     const uint8_t* __restrict__ qX, const void* __restrict__ sXv, int64_t M,
     const uint8_t* __restrict__ qW, const void* __restrict__ sWv, int64_t N, int64_t K,
     const void* __restrict__ lora_act, const uint16_t* __restrict__ L2, int rank,
     void* __restrict__ Y, int64_t ldy, int ydtype,
     int64_t mbase, int64_t nbase, int64_t mlim, int64_t nlim, K2Sched sch, int32_t* __restrict__ dbg) {
-  using S = Smem<FMT>;
+  using S = Smem<FMT, SUB>;
   __shared__ S sm;
   constexpr bool AF8 = MMA && FMT == 0;  // activation codes as FP8 bytes
   const int tid = threadIdx.x;
@@ -124,19 +128,18 @@ __global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 
   const int kh = lane >> 5;
   const int wm = (wave >> 1) * WM;
   const int wn = (wave & 1) * WN;
-  const uint32_t Kb = (uint32_t)(K >> 1);  // bytes per code row
+  const uint32_t Kb = (uint32_t)(K >> 1);      // bytes per 4-bit code row
   const uint32_t Ka = AF8 ? (uint32_t)K : Kb;  // bytes per A row
-  const int nsteps = (int)(K >> 6);         // 64-wide K steps; even because K % 128 == 0
-  // tile and K range of this block; part < 0: the whole K
+  const int nstages = (int)(K >> 6) / SUB;     // the host picks SUB dividing K / 64
+  // tile and stage range of this block; part < 0: the whole K
   uint32_t t = blockIdx.x;
-  int part = -1, kbeg = 0, kend = nsteps;
+  int part = -1, kbeg = 0, kend = nstages;
   if (t >= sch.full) {
     const uint32_t u = t - sch.full;
     t = sch.full + u / sch.split;
     part = (int)(u % sch.split);
-    const int pairs = nsteps >> 1;  // parts start and end on even steps
-    kbeg = 2 * (int)(((uint32_t)part * pairs) / sch.split);
-    kend = 2 * (int)(((uint32_t)(part + 1) * pairs) / sch.split);
+    kbeg = (int)(((uint32_t)part * nstages) / sch.split);
+    kend = (int)(((uint32_t)(part + 1) * nstages) / sch.split);
   }
   const int64_t m0 = mbase + (int64_t)(t / sch.tiles_n) * BM;
   const int64_t n0 = nbase + (int64_t)(t % sch.tiles_n) * BN;
@@ -146,70 +149,93 @@ __global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 
   const int64_t rowsB = nlim - n0 < BN ? nlim - n0 : BN;
   const __amdgpu_buffer_rsrc_t rA = make_rsrc(qX + m0 * Ka, (uint32_t)rowsA * Ka);
   const __amdgpu_buffer_rsrc_t rB = make_rsrc(qW + n0 * Kb, (uint32_t)rowsB * Kb);
-  const int ng = FMT == 0 ? nsteps : 2 * nsteps;  // scale groups along K
+  const int ng = FMT == 0 ? (int)(K >> 6) : (int)(K >> 5);  // scale groups along K
   // INT4 scale words are 4 bytes, except the public path's fp16 activation scales
   const bool xs16 = FMT == 0 && !AF8 && wave < 2;
   const int esz = FMT == 0 ? (xs16 ? 2 : 4) : 1;
-  // staging roles: thread t moves one 16-byte piece of the A panel and one of the B
-  // panel (row t & 127, half t >> 7) and one scale: waves 0-1 the X row t, waves 2-3
-  // the W column t - 128.  The choice is wave-uniform, so it is made once, here.
+  // staging roles: thread t moves the pieces of row t & 127, half t >> 7, of the A and
+  // the B panel, and one scale per sub-step: waves 0-1 of the X row t, waves 2-3 of the
+  // W column t - 128.  The choice is wave-uniform, so it is made once, here.
   const bool xs = wave < 2;
   const __amdgpu_buffer_rsrc_t rS = make_rsrc(xs ? sXv : sWv, DEBUG ? 0u : (uint32_t)(ng * (xs ? M : N) * esz));
   const uint32_t sidx = xs ? (uint32_t)(m0 + tid) : (uint32_t)(n0 + tid - BM);
   const uint32_t sstride = xs ? (uint32_t)M : (uint32_t)N;
   const int ldrow = tid & 127, ldhalf = tid >> 7;
-  const uint32_t offAB = (uint32_t)ldrow * Kb + ldhalf * 16;
-  const uint32_t offA8 = (uint32_t)ldrow * Ka + ldhalf * 32;
+  // this thread's part of a stage row: 4-bit code bytes [SUB*16*half, +SUB*16) (INT4
+  // FP8 activation bytes [SUB*32*half, +SUB*32)); in LDS, INT4 stores every code as a byte
+  const uint32_t offB = (uint32_t)ldrow * Kb + ldhalf * SUB * 16;
+  const uint32_t offA = (uint32_t)ldrow * Ka + ldhalf * SUB * (AF8 ? 32 : 16);
+  const int ldsAB = ldrow * S::kPitch + ldhalf * SUB * (FMT == 0 ? 32 : 16);
 
-  // Loads for steps past the end are harmless: they read zeros (range check) or codes
-  // of another row into a buffer that is never consumed.
-  auto gload = [&](Stage& st, int s) {
-    if (AF8) {
-      st.a = buf_load16(rA, offA8 + (uint32_t)s * 64);
-      st.a1 = buf_load16(rA, offA8 + (uint32_t)s * 64 + 16);
-    } else {
-      st.a = buf_load16(rA, offAB + (uint32_t)s * 32);
+  // Loads for stages past the end are harmless: they read zeros (range check) or codes
+  // of another row into registers that are never stored.
+  auto gload = [&](Stage<SUB>& st, int k) {
+    const uint32_t kb = (uint32_t)k * SUB * 32;  // 4-bit code bytes before stage k
+#pragma unroll
+    for (int v = 0; v < SUB; ++v) {
+      if (AF8) {
+        st.a[2 * v] = buf_load16(rA, offA + 2 * kb + v * 32);
+        st.a[2 * v + 1] = buf_load16(rA, offA + 2 * kb + v * 32 + 16);
+      } else {
+        st.a[v] = buf_load16(rA, offA + kb + v * 16);
+      }
+      st.b[v] = buf_load16(rB, offB + kb + v * 16);
     }
-    st.b = buf_load16(rB, offAB + (uint32_t)s * 32);
-    if (DEBUG) {
-      st.s = 0;
-    } else if (FMT == 0) {
-      if (xs16) st.s = buf_load2(rS, ((uint32_t)s * sstride + sidx) * 2);
-      else st.s = buf_load4(rS, ((uint32_t)s * sstride + sidx) * 4);
-    } else {
-      const uint32_t o0 = (uint32_t)(2 * s) * sstride + sidx;
-      st.s = buf_load1(rS, o0) | (buf_load1(rS, o0 + sstride) << 8);
+#pragma unroll
+    for (int u = 0; u < SUB; ++u) {
+      const uint32_t g = (uint32_t)(k * SUB + u);  // 64-wide sub-step
+      if (DEBUG) {
+        st.s[u] = 0;
+      } else if (FMT == 0) {
+        if (xs16) st.s[u] = buf_load2(rS, (g * sstride + sidx) * 2);
+        else st.s[u] = buf_load4(rS, (g * sstride + sidx) * 4);
+      } else {
+        const uint32_t o0 = 2 * g * sstride + sidx;
+        st.s[u] = buf_load1(rS, o0) | (buf_load1(rS, o0 + sstride) << 8);
+      }
     }
   };
-  auto sstore = [&](const Stage& st, int buf) {
-    if (FMT == 0) {
-      uint32_t a8[8], b8[8];
-      const uint32_t aw[4] = {st.a.x, st.a.y, st.a.z, st.a.w}, bw[4] = {st.b.x, st.b.y, st.b.z, st.b.w};
+  auto sstore = [&](const Stage<SUB>& st, int buf) {
+    uint8_t* A = &sm.st[buf].A[ldsAB];
+    uint8_t* B = &sm.st[buf].B[ldsAB];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (!AF8) nib8_to_fp8(aw[i], a8[2 * i], a8[2 * i + 1]);
-        nib8p_to_fp8(bw[i], b8[2 * i], b8[2 * i + 1]);
-      }
-      uint4* da = reinterpret_cast<uint4*>(&sm.st[buf].A[ldrow * S::kPitch + ldhalf * 32]);
-      uint4* db = reinterpret_cast<uint4*>(&sm.st[buf].B[ldrow * S::kPitch + ldhalf * 32]);
-      if (AF8) {
-        da[0] = st.a;
-        da[1] = st.a1;
+    for (int v = 0; v < SUB; ++v) {
+      if (FMT == 0) {
+        uint32_t a8[8], b8[8];
+        const uint32_t aw[4] = {st.a[v].x, st.a[v].y, st.a[v].z, st.a[v].w};
+        const uint32_t bw[4] = {st.b[v].x, st.b[v].y, st.b[v].z, st.b[v].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (!AF8) nib8_to_fp8(aw[i], a8[2 * i], a8[2 * i + 1]);
+          nib8p_to_fp8(bw[i], b8[2 * i], b8[2 * i + 1]);
+        }
+        uint4* da = reinterpret_cast<uint4*>(A + v * 32);
+        uint4* db = reinterpret_cast<uint4*>(B + v * 32);
+        if (AF8) {
+          da[0] = st.a[2 * v];
+          da[1] = st.a[2 * v + 1];
+        } else {
+          da[0] = make_uint4(a8[0], a8[1], a8[2], a8[3]);
+          da[1] = make_uint4(a8[4], a8[5], a8[6], a8[7]);
+        }
+        db[0] = make_uint4(b8[0], b8[1], b8[2], b8[3]);
+        db[1] = make_uint4(b8[4], b8[5], b8[6], b8[7]);
       } else {
-        da[0] = make_uint4(a8[0], a8[1], a8[2], a8[3]);
-        da[1] = make_uint4(a8[4], a8[5], a8[6], a8[7]);
+        *reinterpret_cast<uint4*>(A + v * 16) = st.a[v];
+        *reinterpret_cast<uint4*>(B + v * 16) = st.b[v];
       }
-      db[0] = make_uint4(b8[0], b8[1], b8[2], b8[3]);
-      db[1] = make_uint4(b8[4], b8[5], b8[6], b8[7]);
-      uint32_t w;
-      if (DEBUG) w = 0x3C00u | ((127u + 9u) << 16);  // m = 1, 2^9
-      else w = xs16 ? split_scale_word(st.s) : st.s;
-      sm.st[buf].m[tid] = __builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
-      sm.st[buf].e[tid] = w >> 16;
-    } else {
-      *reinterpret_cast<uint4*>(&sm.st[buf].A[ldrow * S::kPitch + ldhalf * 16]) = st.a;
-      *reinterpret_cast<uint4*>(&sm.st[buf].B[ldrow * S::kPitch + ldhalf * 16]) = st.b;
-      sm.st[buf].e[tid] = st.s;
+    }
+#pragma unroll
+    for (int u = 0; u < SUB; ++u) {
+      if (FMT == 0) {
+        uint32_t w;
+        if (DEBUG) w = 0x3C00u | ((127u + 9u) << 16);  // m = 1, 2^9
+        else w = xs16 ? split_scale_word(st.s[u]) : st.s[u];
+        sm.st[buf].m[u][tid] = __builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+        sm.st[buf].e[u][tid] = w >> 16;
+      } else {
+        sm.st[buf].e[u][tid] = st.s[u];
+      }
     }
   };
 
@@ -219,7 +245,9 @@ __global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
     for (int j = 0; j < TJ; ++j) acc[i][j] = v16f{};
 
-  auto compute = [&](int buf, int s) {
+  // one 64-wide sub-step u of the stage in LDS buffer buf (global index g for the debug
+  // output)
+  auto compute = [&](int buf, int u, int g) {
     v8i bf[TJ], af[TI];
     uint32_t sb[TJ], sa[TI];
     _Float16 mw[TJ];
@@ -227,29 +255,29 @@ __global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 
     for (int j = 0; j < TJ; ++j) {
       const int col = wn + j * 32 + l32;
       if (FMT == 0) {
-        const uint4* p = reinterpret_cast<const uint4*>(&sm.st[buf].B[col * S::kPitch + kh * 32]);
+        const uint4* p = reinterpret_cast<const uint4*>(&sm.st[buf].B[col * S::kPitch + u * 64 + kh * 32]);
         const uint4 x0 = p[0], x1 = p[1];
         bf[j] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-        sb[j] = sm.st[buf].e[BM + col];
-        mw[j] = sm.st[buf].m[BM + col];
+        sb[j] = sm.st[buf].e[u][BM + col];
+        mw[j] = sm.st[buf].m[u][BM + col];
       } else {
-        const uint4 x0 = *reinterpret_cast<const uint4*>(&sm.st[buf].B[col * S::kPitch + kh * 16]);
+        const uint4 x0 = *reinterpret_cast<const uint4*>(&sm.st[buf].B[col * S::kPitch + u * 32 + kh * 16]);
         bf[j] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, 0, 0, 0, 0};
-        sb[j] = (sm.st[buf].e[BM + col] >> (8 * kh)) & 0xFF;
+        sb[j] = (sm.st[buf].e[u][BM + col] >> (8 * kh)) & 0xFF;
       }
     }
 #pragma unroll
     for (int i = 0; i < TI; ++i) {
       const int row = wm + i * 32 + l32;
       if (FMT == 0) {
-        const uint4* p = reinterpret_cast<const uint4*>(&sm.st[buf].A[row * S::kPitch + kh * 32]);
+        const uint4* p = reinterpret_cast<const uint4*>(&sm.st[buf].A[row * S::kPitch + u * 64 + kh * 32]);
         const uint4 x0 = p[0], x1 = p[1];
         af[i] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-        sa[i] = sm.st[buf].e[row];
+        sa[i] = sm.st[buf].e[u][row];
       } else {
-        const uint4 x0 = *reinterpret_cast<const uint4*>(&sm.st[buf].A[row * S::kPitch + kh * 16]);
+        const uint4 x0 = *reinterpret_cast<const uint4*>(&sm.st[buf].A[row * S::kPitch + u * 32 + kh * 16]);
         af[i] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, 0, 0, 0, 0};
-        sa[i] = (sm.st[buf].e[row] >> (8 * kh)) & 0xFF;
+        sa[i] = (sm.st[buf].e[u][row] >> (8 * kh)) & 0xFF;
       }
     }
     if (FMT == 0) {
@@ -268,7 +296,7 @@ __global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 
         h2 mx[8];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const uint2 w = *reinterpret_cast<const uint2*>(&sm.st[buf].m[wm + i * 32 + 8 * q + 4 * kh]);
+          const uint2 w = *reinterpret_cast<const uint2*>(&sm.st[buf].m[u][wm + i * 32 + 8 * q + 4 * kh]);
           mx[2 * q] = __builtin_bit_cast(h2, w.x);
           mx[2 * q + 1] = __builtin_bit_cast(h2, w.y);
         }
@@ -280,7 +308,7 @@ __global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 
               const int64_t r = m0 + wm + i * 32 + 8 * (a >> 2) + 4 * kh + (a & 3);
               const int64_t c = n0 + wn + j * 32 + l32;
               if (r < mlim && c < nlim)
-                dbg[((int64_t)s * (mlim - mbase) + (r - mbase)) * (nlim - nbase) + (c - nbase)] = (int32_t)p[i][j][a];
+                dbg[((int64_t)g * (mlim - mbase) + (r - mbase)) * (nlim - nbase) + (c - nbase)] = (int32_t)p[i][j][a];
             }
           } else {
             const h2 mw2 = h2{mw[j], mw[j]};
@@ -311,22 +339,18 @@ __global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 
     }
   };
 
-  // ---- main loop: loads two steps ahead, LDS double buffer, one barrier per step ----
-  Stage r0, r1;
-  gload(r0, kbeg);
-  gload(r1, kbeg + 1);
-  sstore(r0, 0);
+  // ---- main loop: the next stage's loads are issued first, LDS double buffer, one
+  // barrier per stage ------------------------------------------------------------------
+  Stage<SUB> r;
+  gload(r, kbeg);
+  sstore(r, 0);
   __syncthreads();
-  for (int s = kbeg; s < kend; s += 2) {
-    // even step s: r0 is free (stored), r1 holds step s+1
-    gload(r0, s + 2);
-    compute(0, s);
-    sstore(r1, 1);
-    __syncthreads();
-    // odd step s+1: r1 is free, r0 holds step s+2
-    gload(r1, s + 3);
-    compute(1, s + 1);
-    sstore(r0, 0);
+  for (int k = kbeg; k < kend; ++k) {
+    const int buf = (k - kbeg) & 1;
+    gload(r, k + 1);
+#pragma unroll
+    for (int u = 0; u < SUB; ++u) compute(buf, u, k * SUB + u);
+    sstore(r, buf ^ 1);
     __syncthreads();
   }
   if (DEBUG) return;
@@ -419,29 +443,38 @@ __global__ __launch_bounds__(64) void k2_fixup(const float* __restrict__ partial
 
 }  // namespace
 
-template <int FMT, bool MMA>
+// Sub-steps per stage: the largest of 2, 1 that divides K / 64.
+static int sub_of(int64_t K) { return (K >> 6) % 2 == 0 ? 2 : 1; }
+
+template <int FMT, bool MMA, int SUB>
 static void launch_k2_t(const KernelLayer& L, int64_t M, const uint8_t* qX, const void* sX,
                         const void* lora_act, void* Y, int64_t ldy, int ydtype, const K2Sched& sch,
                         uint32_t nblocks, hipStream_t st) {
-  hipLaunchKernelGGL((k2_gemm<FMT, false, MMA>), dim3(nblocks), dim3(NTHREADS), 0, st, qX, sX, M, L.qW, L.sW,
-                     L.N, L.K, lora_act, L.L2t, L.rank, Y, ldy, ydtype, (int64_t)0, (int64_t)0, M, L.N, sch,
+  hipLaunchKernelGGL((k2_gemm<FMT, false, MMA, SUB>), dim3(nblocks), dim3(NTHREADS), 0, st, qX, sX, M, L.qW,
+                     L.sW, L.N, L.K, lora_act, L.L2t, L.rank, Y, ldy, ydtype, (int64_t)0, (int64_t)0, M, L.N, sch,
                      (int32_t*)nullptr);
 }
 
-template <int FMT, bool MMA>
+template <int FMT, bool MMA, int SUB>
 static int blocks_per_cu() {
   static int n = 0;  // per kernel instance; the same on every MI355X device
   if (n == 0) {
     int v = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, k2_gemm<FMT, false, MMA>, NTHREADS, 0) != hipSuccess || v < 1) v = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, k2_gemm<FMT, false, MMA, SUB>, NTHREADS, 0) != hipSuccess ||
+        v < 1)
+      v = 1;
     n = v;
   }
   return n;
 }
 
-static int blocks_per_cu(int fmt, bool mma) {
-  if (fmt == 0) return mma ? blocks_per_cu<0, true>() : blocks_per_cu<0, false>();
-  return mma ? blocks_per_cu<1, true>() : blocks_per_cu<1, false>();
+static int blocks_per_cu(int fmt, bool mma, int sub) {
+  if (fmt == 0) {
+    if (sub == 2) return mma ? blocks_per_cu<0, true, 2>() : blocks_per_cu<0, false, 2>();
+    return mma ? blocks_per_cu<0, true, 1>() : blocks_per_cu<0, false, 1>();
+  }
+  if (sub == 2) return mma ? blocks_per_cu<1, true, 2>() : blocks_per_cu<1, false, 2>();
+  return mma ? blocks_per_cu<1, true, 1>() : blocks_per_cu<1, false, 1>();
 }
 
 K2Plan plan_k2(const KernelLayer& L, int64_t M, bool mma) {
@@ -455,11 +488,13 @@ K2Plan plan_k2(const KernelLayer& L, int64_t M, bool mma) {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
     return p;
-  const uint32_t G = (uint32_t)cus * (uint32_t)blocks_per_cu(L.fmt, mma);  // blocks resident at once
+  const int sub = sub_of(L.K);
+  const uint32_t G = (uint32_t)cus * (uint32_t)blocks_per_cu(L.fmt, mma, sub);  // blocks resident at once
   const uint32_t R = T % G;  // tiles of the last, partly filled round
-  const uint32_t nsteps = (uint32_t)(L.K >> 6);
+  const uint32_t nst = (uint32_t)(L.K >> 6) / (uint32_t)sub;  // stages
   uint32_t S = R ? G / R : 1;
-  if (S > nsteps / 4) S = nsteps / 4;  // parts of at least 4 K steps
+  if (S * 4 > nst * sub) S = nst * sub / 4;  // parts of at least 4 sub-steps
+  if (S > nst) S = nst;
   if (S > 16) S = 16;
   if (R == 0 || S < 2) return p;
   p.full = T - R;
@@ -479,13 +514,16 @@ hipError_t launch_k2(const KernelLayer& L, int64_t M, const uint8_t* qX, const v
   const uint32_t T = p.tiles_m * p.tiles_n, rem = T - p.full;
   const K2Sched sch{p.tiles_n, p.full, p.split, static_cast<float*>(workspace)};
   const uint32_t nblocks = p.full + rem * p.split;
+#define K2_LAUNCH(F, MM, SB) launch_k2_t<F, MM, SB>(L, M, qX, sX, lora_act, Y, ldy, ydtype, sch, nblocks, st)
+  const int sub = sub_of(L.K);
   if (L.fmt == 0) {
-    if (mma) launch_k2_t<0, true>(L, M, qX, sX, lora_act, Y, ldy, ydtype, sch, nblocks, st);
-    else launch_k2_t<0, false>(L, M, qX, sX, lora_act, Y, ldy, ydtype, sch, nblocks, st);
+    if (sub == 2) mma ? K2_LAUNCH(0, true, 2) : K2_LAUNCH(0, false, 2);
+    else mma ? K2_LAUNCH(0, true, 1) : K2_LAUNCH(0, false, 1);
   } else {
-    if (mma) launch_k2_t<1, true>(L, M, qX, sX, lora_act, Y, ldy, ydtype, sch, nblocks, st);
-    else launch_k2_t<1, false>(L, M, qX, sX, lora_act, Y, ldy, ydtype, sch, nblocks, st);
+    if (sub == 2) mma ? K2_LAUNCH(1, true, 2) : K2_LAUNCH(1, false, 2);
+    else mma ? K2_LAUNCH(1, true, 1) : K2_LAUNCH(1, false, 1);
   }
+#undef K2_LAUNCH
   if (rem > 0)
     hipLaunchKernelGGL(k2_fixup, dim3(rem * 16), dim3(64), 0, st, static_cast<const float*>(workspace), sch, M,
                        L.N, Y, ldy, ydtype);
@@ -496,7 +534,7 @@ hipError_t launch_k2_debug(const KernelLayer& L, int64_t M, const uint8_t* qX, i
                            int64_t n0, int64_t mt, int64_t nt, int32_t* out, hipStream_t st) {
   const uint32_t tn = (uint32_t)((nt + BN - 1) / BN), tm = (uint32_t)((mt + BM - 1) / BM);
   const K2Sched sch{tn, tm * tn, 1, nullptr};
-  hipLaunchKernelGGL((k2_gemm<0, true, false>), dim3(tm * tn), dim3(NTHREADS), 0, st, qX, (const void*)nullptr, M,
+  hipLaunchKernelGGL((k2_gemm<0, true, false, 1>), dim3(tm * tn), dim3(NTHREADS), 0, st, qX, (const void*)nullptr, M,
                      L.qW, (const void*)nullptr, L.N, L.K, (const void*)nullptr, (const uint16_t*)nullptr, 0,
                      (void*)nullptr, (int64_t)0, 0, m0, n0, m0 + mt, n0 + nt, sch, out);
   return hipGetLastError();
