@@ -281,53 +281,54 @@ __global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 
       }
     }
     if (FMT == 0) {
-      // all four group-sum MFMAs first (separate result registers), then the rescale
-      // epilogues, so each epilogue overlaps the MFMAs still in flight
-      v16f p[TI][TJ];
+      // two group-sum MFMAs in flight: tile t+1's MFMA is issued ahead of tile t's rescale
+      auto gs = [&](int i, int j) {
+        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], v16f{}, 0, 0, 0, (int)sa[i], 0,
+                                                               (int)sb[j]);
+      };
+      h2 mx[TI][8];
 #pragma unroll
       for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int j = 0; j < TJ; ++j)
-          p[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], v16f{}, 0, 0, 0, (int)sa[i], 0,
-                                                                   (int)sb[j]);
-#pragma unroll
-      for (int i = 0; i < TI; ++i) {
-        // mantissas of the 16 accumulator rows: rows 8*(a>>2) + 4*kh + (a&3)
-        h2 mx[8];
-#pragma unroll
         for (int q = 0; q < 4; ++q) {
           const uint2 w = *reinterpret_cast<const uint2*>(&sm.st[buf].m[u][wm + i * 32 + 8 * q + 4 * kh]);
-          mx[2 * q] = __builtin_bit_cast(h2, w.x);
-          mx[2 * q + 1] = __builtin_bit_cast(h2, w.y);
+          mx[i][2 * q] = __builtin_bit_cast(h2, w.x);
+          mx[i][2 * q + 1] = __builtin_bit_cast(h2, w.y);
         }
+      auto epi = [&](int i, int j, const v16f& p) {
+        if (DEBUG) {
 #pragma unroll
-        for (int j = 0; j < TJ; ++j) {
-          if (DEBUG) {
+          for (int a = 0; a < 16; ++a) {
+            const int64_t r = m0 + wm + i * 32 + 8 * (a >> 2) + 4 * kh + (a & 3);
+            const int64_t c = n0 + wn + j * 32 + l32;
+            if (r < mlim && c < nlim)
+              dbg[((int64_t)g * (mlim - mbase) + (r - mbase)) * (nlim - nbase) + (c - nbase)] = (int32_t)p[a];
+          }
+        } else {
+          const h2 mw2 = h2{mw[j], mw[j]};
 #pragma unroll
-            for (int a = 0; a < 16; ++a) {
-              const int64_t r = m0 + wm + i * 32 + 8 * (a >> 2) + 4 * kh + (a & 3);
-              const int64_t c = n0 + wn + j * 32 + l32;
-              if (r < mlim && c < nlim)
-                dbg[((int64_t)g * (mlim - mbase) + (r - mbase)) * (nlim - nbase) + (c - nbase)] = (int32_t)p[i][j][a];
-            }
-          } else {
-            const h2 mw2 = h2{mw[j], mw[j]};
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-              const h2 sc = mx[q] * mw2;
-              acc[i][j][2 * q] = fmaf(p[i][j][2 * q], (float)sc.x, acc[i][j][2 * q]);
-              acc[i][j][2 * q + 1] = fmaf(p[i][j][2 * q + 1], (float)sc.y, acc[i][j][2 * q + 1]);
-            }
+          for (int q = 0; q < 8; ++q) {
+            const h2 sc = mx[i][q] * mw2;
+            acc[i][j][2 * q] = fmaf(p[2 * q], (float)sc.x, acc[i][j][2 * q]);
+            acc[i][j][2 * q + 1] = fmaf(p[2 * q + 1], (float)sc.y, acc[i][j][2 * q + 1]);
           }
         }
-      }
+      };
+      v16f p0 = gs(0, 0);
+      v16f p1 = gs(0, 1);
+      epi(0, 0, p0);
+      p0 = gs(1, 0);
+      epi(0, 1, p1);
+      p1 = gs(1, 1);
+      epi(1, 0, p0);
+      epi(1, 1, p1);
       if (!DEBUG) {
-        // schedule: MFMA t+1 is issued ahead of epilogue t (24 VALU ops each)
-#pragma unroll
-        for (int t = 0; t < TI * TJ; ++t) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-          __builtin_amdgcn_sched_group_barrier(0x002, 24, 0);  // then VALU
-        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 24, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 24, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 48, 0);
       }
     } else {
 #pragma unroll
