@@ -74,7 +74,14 @@ def _pmc_means(path):
     acc = collections.defaultdict(list)
     for r in csv.DictReader(open(path)):
         name = r["Kernel_Name"]
-        key = "k2" if "k2_gemm<0, false>" in name else ("copy" if "copyBuffer" in name or "copy" in name.lower() else None)
+        # kernel 2 of the timed forward: INT4, MMA activation form (the fixup launch is
+        # counted with it)
+        if "k2_gemm<0, false, true" in name or "k2_fixup" in name:
+            key = "k2" if "k2_gemm" in name else "fixup"
+        elif "copyBuffer" in name or "copy" in name.lower():
+            key = "copy"
+        else:
+            key = None
         if key:
             acc[key].append(float(r["Counter_Value"]))
     # the calibration copy is the largest copy dispatch (uploads may also use copy kernels)
@@ -89,9 +96,10 @@ def write_traffic(fetch_csv, write_csv):
     w = _pmc_means(write_csv)
     ffac = f["copy"][0] * 1024.0 / CALIB_BYTES
     wfac = w["copy"][0] * 1024.0 / CALIB_BYTES
-    fetch_b = f["k2"][0] * 1024.0 / ffac
-    write_b = w["k2"][0] * 1024.0 / wfac
-    d = {"kernel": "k2_gemm<INT4>", "workload": "FLUX.1 QKV projection M=4608 K=3072 N=9216 r=32, fp32 Y",
+    # the fixup launch runs once per kernel-2 launch
+    fetch_b = (f["k2"][0] + f.get("fixup", (0.0, 0))[0]) * 1024.0 / ffac
+    write_b = (w["k2"][0] + w.get("fixup", (0.0, 0))[0]) * 1024.0 / wfac
+    d = {"kernel": "k2_gemm<INT4, MMA form> + k2_fixup", "workload": "FLUX.1 QKV projection M=4608 K=3072 N=9216 r=32, fp32 Y",
          "k2_source_hash": source_hash(K2_SOURCES), "fetch_kib_raw": f["k2"][0], "write_kib_raw": w["k2"][0],
          "copy_fetch_factor": ffac, "copy_write_factor": wfac, "fetch_bytes": fetch_b, "write_bytes": write_b,
          "bytes_per_launch": fetch_b + write_b, "dispatches": f["k2"][1],
@@ -141,8 +149,10 @@ def cpu_baseline(wl_name, rows):
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # defaults: ~60 ms of warm-up (the clocks settle within a few tens of ms) and of
+    # timed work at C1
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="C1", choices=list(WORKLOADS))
     ap.add_argument("--ydtype", default="f32", choices=["f32", "bf16"])
     ap.add_argument("--cpu-rows", type=int, default=4608)
@@ -227,16 +237,19 @@ def main():
     torch.cuda.synchronize()
     t_k1 = float(np.mean([e[3 * i].elapsed_time(e[3 * i + 1]) for i in range(nrep)])) * 1e-3
     t_k2 = float(np.mean([e[3 * i + 1].elapsed_time(e[3 * i + 2]) for i in range(nrep)])) * 1e-3
-    # rank-0 layer (same codes, no low-rank branch) for the low-rank overhead
-    for _ in range(3):
-        lay0.forward(X, ydt, Y, ws0)
-    torch.cuda.synchronize()
-    ev0.record()
-    for _ in range(nrep):
-        lay0.forward(X, ydt, Y, ws0)
-    ev1.record()
-    torch.cuda.synchronize()
-    ms0 = ev0.elapsed_time(ev1) / nrep
+    # low-rank overhead: the layer against a rank-0 layer with the same codes, timed in
+    # alternating blocks of 20 forwards (medians of 5), so both see the same clocks
+    fr, f0 = [], []
+    for _ in range(5):
+        for lyr, wsp, out in ((lay, ws, fr), (lay0, ws0, f0)):
+            lyr.forward(X, ydt, Y, wsp)
+            ev0.record()
+            for _ in range(20):
+                lyr.forward(X, ydt, Y, wsp)
+            ev1.record()
+            torch.cuda.synchronize()
+            out.append(ev0.elapsed_time(ev1) / 20)
+    ms_r, ms0 = float(np.median(fr)), float(np.median(f0))
 
     G = lay.group
     k2_ops = float(M) * N * (2.0 * K + 2.0 * r)
@@ -262,7 +275,7 @@ def main():
         "kernels": {"k1_us": round(t_k1 * 1e6, 2), "k2_us": round(t_k2 * 1e6, 2),
                     "k1_GBps": round(k1_bytes / t_k1 / 1e9, 1), "k1_hbm_frac": round(k1_bytes / t_k1 / 1e9 / PEAK_HBM_GBS, 4),
                     "k2_TOPS": round(k2_tops, 2), "rank0_ms": round(ms0, 5),
-                    "lowrank_overhead": round(ms / ms0 - 1.0, 4)},
+                    "fwd_ms_paired": round(ms_r, 5), "lowrank_overhead": round(ms_r / ms0 - 1.0, 4)},
     }
     if args.calib_copy:
         src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device=dev)
