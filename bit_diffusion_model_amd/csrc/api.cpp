@@ -50,7 +50,7 @@ static svdq_status check_layer(const svdq_layer* L, KernelLayer& kl) {
   if (!L->inv_s || !L->qW || !L->sW) return fail(SVDQ_EINVAL, "layer inv_s, qW and sW must be non-NULL");
   if (L->rank > 0 && (!L->Ld_hi || !L->Ld_lo || !L->L2t))
     return fail(SVDQ_EINVAL, "layer Ld_hi, Ld_lo and L2t must be non-NULL when rank > 0");
-  if (L->fmt == SVDQ_INT4_G64 && !aligned(L->sW, 4)) return fail(SVDQ_EINVAL, "INT4 layer sW must be 4-byte aligned");
+  if (!aligned(L->sW, 16)) return fail(SVDQ_EINVAL, "layer sW must be 16-byte aligned");
   if (!aligned(L->inv_s, 16) || !aligned(L->qW, 16) ||
       (L->rank > 0 && (!aligned(L->Ld_hi, 16) || !aligned(L->Ld_lo, 16) || !aligned(L->L2t, 16))))
     return fail(SVDQ_EINVAL, "layer inv_s, qW, Ld_hi, Ld_lo and L2t must be 16-byte aligned");
@@ -64,15 +64,17 @@ struct WsLayout {
   size_t qx, sx, la, part, total;
 };
 // The forward path's workspace: the activation side in MMA form (INT4 codes as FP8
-// bytes [M][K] and split 32-bit scale words; MXFP4 packed codes and E8M0 bytes;
-// lora_act as bf16 hi/lo rows, the bytes of fp32 [M][R16]).
+// bytes [M][K] and split scale planes; MXFP4 packed codes and E8M0 bytes; lora_act as
+// bf16 hi/lo rows, the bytes of fp32 [M][R16]), then kernel 2's partial tiles.
 static WsLayout ws_layout(const svdq_layer* L, int64_t M) {
   const bool f8 = L->fmt == SVDQ_INT4_G64;
   WsLayout w;
   w.qx = 0;
   w.sx = rup((size_t)M * (size_t)(f8 ? L->K : L->K / 2));
-  const size_t ssz = f8 ? 4 : 1;
-  w.la = w.sx + rup((size_t)(L->K / group_of(L->fmt)) * (size_t)M * ssz);
+  // MMA-form scales: rows padded to Mp = M rounded up to 4; INT4 as an fp16 plane and
+  // an E8M0 plane (3 bytes per group and row), MXFP4 E8M0 bytes
+  const size_t Mp = ((size_t)M + 3) / 4 * 4;
+  w.la = w.sx + rup((size_t)(L->K / group_of(L->fmt)) * Mp * (f8 ? 3 : 1));
   w.part = w.la + rup((size_t)M * (size_t)((L->rank + 15) / 16 * 16) * 4);
   KernelLayer kl{L->K, L->N, L->rank, L->fmt, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
   w.total = w.part + rup(plan_k2(kl, M, true).bytes);

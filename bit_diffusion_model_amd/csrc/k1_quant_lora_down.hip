@@ -138,10 +138,14 @@ __global__ __launch_bounds__(64 * K1_WAVES) void k1_quant_lora_down(
         nib[i] = (sf == 0.0f) ? 0u : (mag | (qc < 0.0f ? 8u : 0u));
       }
       if (row_ok && sub == 0) {
-        if constexpr (MMA)  // the split form kernel 2 consumes: [K/64][M] words
-          reinterpret_cast<uint32_t*>(sXv)[(int64_t)c * M + row] = split_scale_word(__builtin_bit_cast(uint16_t, sh));
-        else
+        if constexpr (MMA) {  // the split planes kernel 2 consumes: fp16 m, then E8M0 bytes
+          const int64_t Mp = (M + 3) & ~int64_t(3);
+          const uint32_t w = split_scale_word(__builtin_bit_cast(uint16_t, sh));
+          reinterpret_cast<uint16_t*>(sXv)[(int64_t)c * Mp + row] = (uint16_t)(w & 0xFFFFu);
+          reinterpret_cast<uint8_t*>(sXv)[(K >> 6) * Mp * 2 + (int64_t)c * Mp + row] = (uint8_t)(w >> 16);
+        } else {
           reinterpret_cast<uint16_t*>(sXv)[(int64_t)c * M + row] = __builtin_bit_cast(uint16_t, sh);
+        }
       }
     } else {
       // MXFP4: e = smallest exponent with 6 * 2^e >= a (clamped to [-127, 127]);
@@ -161,8 +165,10 @@ __global__ __launch_bounds__(64 * K1_WAVES) void k1_quant_lora_down(
         nib[i] = p & 0xF;
         nib[i + 1] = (p >> 4) & 0xF;
       }
-      if (row_ok && (sub & 1) == 0)
-        reinterpret_cast<uint8_t*>(sXv)[(int64_t)(2 * c + (sub >> 1)) * M + row] = (uint8_t)(e + 127);
+      if (row_ok && (sub & 1) == 0) {
+        const int64_t ld = MMA ? (M + 3) & ~int64_t(3) : M;  // MMA form: rows padded to 4
+        reinterpret_cast<uint8_t*>(sXv)[(int64_t)(2 * c + (sub >> 1)) * ld + row] = (uint8_t)(e + 127);
+      }
     }
     if (row_ok) {
       if constexpr (MMA && FMT == 0) {

@@ -152,14 +152,18 @@ __global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 
   const int ng = FMT == 0 ? (int)(K >> 6) : (int)(K >> 5);  // scale groups along K
   // INT4 scale words are 4 bytes, except the public path's fp16 activation scales
   const bool xs16 = FMT == 0 && !AF8 && wave < 2;
-  const int esz = FMT == 0 ? (xs16 ? 2 : 4) : 1;
   // staging roles: thread t moves the pieces of row t & 127, half t >> 7, of the A and
   // the B panel, and one scale per sub-step: waves 0-1 of the X row t, waves 2-3 of the
   // W column t - 128.  The choice is wave-uniform, so it is made once, here.
   const bool xs = wave < 2;
-  const __amdgpu_buffer_rsrc_t rS = make_rsrc(xs ? sXv : sWv, DEBUG ? 0u : (uint32_t)(ng * (xs ? M : N) * esz));
+  // scale rows: the packed activation scales have stride M; the MMA-form activation
+  // scales and the prepared weight scales are padded to a multiple of 4, and INT4 ones
+  // are split into a plane of fp16 mantissas followed by a plane of E8M0 bytes
+  const uint32_t sstride = xs ? (uint32_t)(MMA ? (M + 3) & ~int64_t(3) : M) : (uint32_t)((N + 3) & ~int64_t(3));
+  const uint32_t sbytes = (uint32_t)ng * sstride * (FMT == 0 ? (xs16 ? 2 : 3) : 1);
+  const __amdgpu_buffer_rsrc_t rS = make_rsrc(xs ? sXv : sWv, DEBUG ? 0u : sbytes);
+  const uint32_t eplane = (uint32_t)ng * sstride * 2;  // INT4 E8M0 plane offset
   const uint32_t sidx = xs ? (uint32_t)(m0 + tid) : (uint32_t)(n0 + tid - BM);
-  const uint32_t sstride = xs ? (uint32_t)M : (uint32_t)N;
   const int ldrow = tid & 127, ldhalf = tid >> 7;
   // this thread's part of a stage row: 4-bit code bytes [SUB*16*half, +SUB*16) (INT4
   // FP8 activation bytes [SUB*32*half, +SUB*32)); in LDS, INT4 stores every code as a byte
@@ -188,7 +192,7 @@ __global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 
         st.s[u] = 0;
       } else if (FMT == 0) {
         if (xs16) st.s[u] = buf_load2(rS, (g * sstride + sidx) * 2);
-        else st.s[u] = buf_load4(rS, (g * sstride + sidx) * 4);
+        else st.s[u] = buf_load2(rS, (g * sstride + sidx) * 2) | (buf_load1(rS, eplane + g * sstride + sidx) << 16);
       } else {
         const uint32_t o0 = 2 * g * sstride + sidx;
         st.s[u] = buf_load1(rS, o0) | (buf_load1(rS, o0 + sstride) << 8);
@@ -419,6 +423,308 @@ __global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// Kernel 2, streamed (MMA activation form): codes and scales go from global memory
+// straight into LDS with buffer loads that write LDS (each lane's 16 or 4 bytes land at
+// the instruction's LDS base + lane * size), so no register staging, no LDS store
+// instructions and no wait for a stage's data until it is needed.  DNB LDS buffers: the
+// loads of stage k+2 are issued while stage k is computed; one barrier per stage.
+// 16-byte slots of each operand row are XOR-swizzled with the row (rows are not padded:
+// a load instruction fills 1 KB contiguously), so that the 8 rows an MFMA operand read
+// takes at once fall on 8 different bank groups.  The weight codes stay 4-bit in LDS and
+// are expanded to FP8 after the read, per wave.
+constexpr int DNB = 3;
+
+template <int FMT, int SUB>
+struct DLay {
+  static constexpr int RA = SUB * (FMT == 0 ? 64 : 32);  // A bytes per row and stage
+  static constexpr int RB = SUB * 32;                     // B (4-bit) bytes per row and stage
+  static constexpr int B_OFF = BM * RA;
+  static constexpr int S_OFF = B_OFF + BN * RB;
+  // scales of one sub-step: INT4 X m [BM] fp16 | W m [BN] fp16 | X e (256 B) | W e (256 B);
+  // MXFP4 X e [2][BM] | W e [2][BN] (the sub-step's two 32-groups)
+  static constexpr int S_SUB = FMT == 0 ? 2 * BM + 2 * BN + 512 : 2 * BM + 2 * BN;
+  static constexpr int BUF = S_OFF + SUB * S_SUB;
+  // load instructions per wave and stage
+  static constexpr int NA = BM * RA / 1024 / 4;
+  static constexpr int NBW = BN * RB / 1024 / 4;
+  static constexpr int NS = 2;  // scale loads per wave: one activation-side, one weight-side
+  static constexpr int NDW = NA + NBW + NS;
+  static_assert(BM * RA % 4096 == 0 && BN * RB % 4096 == 0, "whole 1 KB load chunks per wave");
+};
+
+// XOR swizzle of the 16-byte slot within a row of `slots` slots
+__device__ __forceinline__ int swz(int row, int slots) {
+  return slots == 8 ? (row & 7) : (slots == 4 ? ((row >> 1) & 3) : ((row >> 2) & 1));
+}
+
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, off, 0, 0, 0);
+}
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, off, 0, 0, 0);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {  // s_waitcnt vmcnt(N), other counters untouched
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int FMT, int SUB>
+__global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void k2_stream(
+    const uint8_t* __restrict__ qX, const uint8_t* __restrict__ sX, int64_t M,
+    const uint8_t* __restrict__ qW, const uint8_t* __restrict__ sW, int64_t N, int64_t K,
+    const uint16_t* __restrict__ lora_act, const uint16_t* __restrict__ L2, int rank,
+    void* __restrict__ Y, int64_t ldy, int ydtype, K2Sched sch) {
+  using D = DLay<FMT, SUB>;
+  // three separate arrays, always addressed statically (the main loop is unrolled by
+  // three), so the compiler can tell a buffer's pending loads from reads of another
+  __shared__ __attribute__((aligned(1024))) uint8_t lds0[D::BUF];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds1[D::BUF];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds2[D::BUF];
+  static_assert(DNB == 3, "three LDS buffers");
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int kh = lane >> 5;
+  const int wm = (wave >> 1) * WM;
+  const int wn = (wave & 1) * WN;
+  const uint32_t Kb = (uint32_t)(K >> 1);                  // 4-bit code bytes per row
+  const uint32_t Ka = FMT == 0 ? (uint32_t)K : Kb;         // A bytes per row
+  const int nstages = (int)(K >> 6) / SUB;
+  uint32_t t = blockIdx.x;
+  int part = -1, kbeg = 0, kend = nstages;
+  if (t >= sch.full) {
+    const uint32_t u = t - sch.full;
+    t = sch.full + u / sch.split;
+    part = (int)(u % sch.split);
+    kbeg = (int)(((uint32_t)part * nstages) / sch.split);
+    kend = (int)(((uint32_t)(part + 1) * nstages) / sch.split);
+  }
+  const int64_t m0 = (int64_t)(t / sch.tiles_n) * BM;
+  const int64_t n0 = (int64_t)(t % sch.tiles_n) * BN;
+  const int64_t rowsA = M - m0 < BM ? M - m0 : BM;
+  const int64_t rowsB = N - n0 < BN ? N - n0 : BN;
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(qX + m0 * Ka, (uint32_t)rowsA * Ka);
+  const __amdgpu_buffer_rsrc_t rB = make_rsrc(qW + n0 * Kb, (uint32_t)rowsB * Kb);
+  const uint32_t ng = FMT == 0 ? (uint32_t)(K >> 6) : (uint32_t)(K >> 5);
+  const uint32_t Mp = (uint32_t)((M + 3) & ~int64_t(3)), Np = (uint32_t)((N + 3) & ~int64_t(3));
+  const __amdgpu_buffer_rsrc_t rSX = make_rsrc(sX, ng * Mp * (FMT == 0 ? 3 : 1));
+  const __amdgpu_buffer_rsrc_t rSW = make_rsrc(sW, ng * Np * (FMT == 0 ? 3 : 1));
+
+  // ---- loads of stage k into LDS buffer b (every wave issues D::NDW instructions) -------
+  auto issue = [&](int k, uint8_t* base) {
+#pragma unroll
+    for (int q = 0; q < D::NA; ++q) {  // A: chunk n covers rows n * 1024 / RA ..
+      const int n = wave + 4 * q;
+      const int pos = n * 1024 + lane * 16;
+      const int row = pos / D::RA, ps = (pos % D::RA) / 16;
+      const int ls = ps ^ swz(row, D::RA / 16);
+      dma16(rA, base + n * 1024, (uint32_t)row * Ka + (uint32_t)k * D::RA + ls * 16);
+    }
+#pragma unroll
+    for (int q = 0; q < D::NBW; ++q) {
+      const int n = wave + 4 * q;
+      const int pos = n * 1024 + lane * 16;
+      const int row = pos / D::RB, ps = (pos % D::RB) / 16;
+      const int ls = ps ^ swz(row, D::RB / 16);
+      dma16(rB, base + D::B_OFF + n * 1024, (uint32_t)row * Kb + (uint32_t)k * D::RB + ls * 16);
+    }
+    // scale loads: every wave issues one activation-side and one weight-side load; the
+    // wave number picks the sub-step (w & 1) and, for INT4, the plane (m for waves 0-1,
+    // E8M0 for waves 2-3), arithmetically (no branches, so the compiler keeps tracking
+    // which buffer has loads pending).  Sub-steps past SUB repeat the last (same data).
+    {
+      const int u = SUB == 1 ? 0 : (wave & 1);
+      uint8_t* sb = base + D::S_OFF + u * D::S_SUB;
+      if (FMT == 0) {
+        const uint32_t g = (uint32_t)(k * SUB + u);
+        const uint32_t ep = (uint32_t)wave >> 1;  // 0: m planes, 1: E8M0 planes
+        const uint32_t mx_ = (g * Mp + (uint32_t)m0) * 2, ex_ = ng * Mp * 2 + g * Mp + (uint32_t)m0;
+        const uint32_t mw_ = (g * Np + (uint32_t)n0) * 2, ew_ = ng * Np * 2 + g * Np + (uint32_t)n0;
+        dma4(rSX, sb + ep * (2 * BM + 2 * BN), mx_ + ep * (ex_ - mx_) + lane * 4);
+        dma4(rSW, sb + 2 * BM + ep * (2 * BN + 256), mw_ + ep * (ew_ - mw_) + lane * 4);
+      } else {  // lanes 0-31 group 2g, lanes 32-63 group 2g+1
+        const uint32_t g2 = 2 * (uint32_t)(k * SUB + u) + (uint32_t)kh;
+        dma4(rSX, sb, g2 * Mp + (uint32_t)m0 + l32 * 4);
+        dma4(rSW, sb + 2 * BM, g2 * Np + (uint32_t)n0 + l32 * 4);
+      }
+    }
+  };
+
+  v16f acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) acc[i][j] = v16f{};
+
+  // ---- one 64-wide sub-step u of the stage in LDS buffer b ------------------------------
+  auto compute = [&](const uint8_t* base, int u) {
+    const uint8_t* sb = base + D::S_OFF + u * D::S_SUB;
+    v8i af[TI], bf[TJ];
+    uint32_t sa[TI], sbv[TJ];
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const int col = wn + j * 32 + l32;
+      const int ls = u * 2 + kh;  // 4-bit bytes u*32 + kh*16
+      const uint4 x = *reinterpret_cast<const uint4*>(base + D::B_OFF + col * D::RB + ((ls ^ swz(col, D::RB / 16)) * 16));
+      if (FMT == 0) {
+        uint32_t w8[8];
+        const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) nib8p_to_fp8(xw[e], w8[2 * e], w8[2 * e + 1]);
+        bf[j] = v8i{(int)w8[0], (int)w8[1], (int)w8[2], (int)w8[3], (int)w8[4], (int)w8[5], (int)w8[6], (int)w8[7]};
+        sbv[j] = sb[2 * BM + 2 * BN + 256 + col];
+      } else {
+        bf[j] = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
+        sbv[j] = sb[2 * BM + kh * BN + col];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      const int row = wm + i * 32 + l32;
+      if (FMT == 0) {
+        const int ls0 = u * 4 + kh * 2;  // FP8 bytes u*64 + kh*32, two slots
+        const int sw = swz(row, D::RA / 16);
+        const uint4 x0 = *reinterpret_cast<const uint4*>(base + row * D::RA + ((ls0 ^ sw) * 16));
+        const uint4 x1 = *reinterpret_cast<const uint4*>(base + row * D::RA + (((ls0 + 1) ^ sw) * 16));
+        af[i] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+        sa[i] = sb[2 * BM + 2 * BN + row];
+      } else {
+        const int ls = u * 2 + kh;
+        const uint4 x = *reinterpret_cast<const uint4*>(base + row * D::RA + ((ls ^ swz(row, D::RA / 16)) * 16));
+        af[i] = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
+        sa[i] = sb[kh * BM + row];
+      }
+    }
+    if (FMT == 0) {
+      const _Float16* xm = reinterpret_cast<const _Float16*>(sb);
+      const _Float16* wmn = reinterpret_cast<const _Float16*>(sb + 2 * BM);
+      h2 mw[TJ];
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const _Float16 m = wmn[wn + j * 32 + l32];
+        mw[j] = h2{m, m};
+      }
+      h2 mx[TI][8];
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint2 w = *reinterpret_cast<const uint2*>(&xm[wm + i * 32 + 8 * q + 4 * kh]);
+          mx[i][2 * q] = __builtin_bit_cast(h2, w.x);
+          mx[i][2 * q + 1] = __builtin_bit_cast(h2, w.y);
+        }
+      auto gs = [&](int i, int j) {
+        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], v16f{}, 0, 0, 0, (int)sa[i], 0,
+                                                               (int)sbv[j]);
+      };
+      auto epi = [&](int i, int j, const v16f& p) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const h2 sc = mx[i][q] * mw[j];
+          acc[i][j][2 * q] = fmaf(p[2 * q], (float)sc.x, acc[i][j][2 * q]);
+          acc[i][j][2 * q + 1] = fmaf(p[2 * q + 1], (float)sc.y, acc[i][j][2 * q + 1]);
+        }
+      };
+      // two group-sum MFMAs in flight: tile t+1's MFMA is issued ahead of tile t's rescale
+      v16f p0 = gs(0, 0);
+      v16f p1 = gs(0, 1);
+      epi(0, 0, p0);
+      p0 = gs(1, 0);
+      epi(0, 1, p1);
+      p1 = gs(1, 1);
+      epi(1, 0, p0);
+      epi(1, 1, p1);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 24, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 24, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 48, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], 4, 4, 0, (int)sa[i], 0,
+                                                                     (int)sbv[j]);
+    }
+  };
+
+  // ---- main loop ------------------------------------------------------------------------
+  // Stage k's loads were issued two stages earlier into buffer (k - kbeg) % DNB.  A wave
+  // waits for its own loads of stage k (vmcnt: the loads of stage k+1 may stay in
+  // flight), the barrier makes every wave's loads visible and frees the buffer read
+  // during stage k-1, which then receives stage k+2.
+  // Every step issues a stage's loads: past the end, the last stage again (harmless,
+  // never read), so the count in flight is the same at every wait and the loop body has
+  // no branches.
+  auto kstep = [&](int k, const uint8_t* cur, uint8_t* nxt) {
+    wait_vm<D::NDW>();  // this wave's loads of stage k are in; stage k+1's may be in flight
+    __builtin_amdgcn_s_barrier();
+    issue(k + 2 < kend ? k + 2 : kend - 1, nxt);
+#pragma unroll
+    for (int u = 0; u < SUB; ++u) compute(cur, u);
+  };
+  const int nk = kend - kbeg;
+  issue(kbeg, lds0);
+  issue(kbeg + 1 < kend ? kbeg + 1 : kend - 1, lds1);
+  int k = kbeg;
+  for (; k + 3 <= kend; k += 3) {
+    kstep(k, lds0, lds2);
+    kstep(k + 1, lds1, lds0);
+    kstep(k + 2, lds2, lds1);
+  }
+  if (nk % 3 >= 1) kstep(k, lds0, lds2);
+  if (nk % 3 == 2) kstep(k + 1, lds1, lds0);
+  wait_vm<0>();
+
+  // ---- low-rank up projection: acc += lora_act[rows, :] L2[:, cols] ----------------------
+  // v_mfma_f32_32x32x16_bf16 on lora_act's bf16 hi/lo rows ([M][R16 hi | R16 lo]) and L2t
+  // [N][R16]; rows past M / columns past N read zeros through the range check.
+  if (rank > 0 && part <= 0) {
+    const int R16 = (rank + 15) & ~15;
+    const __amdgpu_buffer_rsrc_t rL = make_rsrc(lora_act + m0 * 2 * R16, (uint32_t)(rowsA * R16 * 4));
+    const __amdgpu_buffer_rsrc_t rU = make_rsrc(L2 + n0 * R16, (uint32_t)(rowsB * R16 * 2));
+    for (int k0 = 0; k0 < R16; k0 += 16) {
+      v8bf bl[TJ];
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+        bl[j] = __builtin_bit_cast(v8bf, buf_load16(rU, (uint32_t)((wn + j * 32 + l32) * R16 + k0 + 8 * kh) * 2));
+#pragma unroll
+      for (int i = 0; i < TI; ++i) {
+        const uint32_t o = (uint32_t)((wm + i * 32 + l32) * 2 * R16 + k0 + 8 * kh) * 2;
+        const v8bf ah = __builtin_bit_cast(v8bf, buf_load16(rL, o));
+        const v8bf al = __builtin_bit_cast(v8bf, buf_load16(rL, o + R16 * 2));
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bl[j], acc[i][j], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // ---- store (or the partial tile) ------------------------------------------------------
+  if (part < 0) {
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) store_sub(acc[i][j], Y, ldy, ydtype, m0, n0, rowsA, N, wm + i * 32, wn + j * 32, l32, kh);
+  } else {
+    float* P = sch.partials + (size_t)(blockIdx.x - sch.full) * PART_FLOATS;
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+#pragma unroll
+        for (int a = 0; a < 16; ++a) P[(((wave * TI + i) * TJ + j) * 16 + a) * 64 + lane] = acc[i][j][a];
+  }
+}
+
 // Sum of the `split` partial tiles of one remaining tile, in part order (the result does
 // not depend on which part finished first), stored like a whole tile.  One 64-thread
 // block per 32 x 32 sub-tile: blockIdx.x = remaining tile * 16 + (wave, i, j).
@@ -469,13 +775,24 @@ static int blocks_per_cu() {
   return n;
 }
 
-static int blocks_per_cu(int fmt, bool mma, int sub) {
-  if (fmt == 0) {
-    if (sub == 2) return mma ? blocks_per_cu<0, true, 2>() : blocks_per_cu<0, false, 2>();
-    return mma ? blocks_per_cu<0, true, 1>() : blocks_per_cu<0, false, 1>();
+template <int FMT, int SUB>
+static int stream_blocks_per_cu() {
+  static int n = 0;
+  if (n == 0) {
+    int v = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, k2_stream<FMT, SUB>, NTHREADS, 0) != hipSuccess || v < 1) v = 1;
+    n = v;
   }
-  if (sub == 2) return mma ? blocks_per_cu<1, true, 2>() : blocks_per_cu<1, false, 2>();
-  return mma ? blocks_per_cu<1, true, 1>() : blocks_per_cu<1, false, 1>();
+  return n;
+}
+
+static int blocks_per_cu(int fmt, bool mma, int sub) {
+  if (mma) {
+    if (fmt == 0) return sub == 2 ? stream_blocks_per_cu<0, 2>() : stream_blocks_per_cu<0, 1>();
+    return sub == 2 ? stream_blocks_per_cu<1, 2>() : stream_blocks_per_cu<1, 1>();
+  }
+  if (fmt == 0) return sub == 2 ? blocks_per_cu<0, false, 2>() : blocks_per_cu<0, false, 1>();
+  return sub == 2 ? blocks_per_cu<1, false, 2>() : blocks_per_cu<1, false, 1>();
 }
 
 K2Plan plan_k2(const KernelLayer& L, int64_t M, bool mma) {
@@ -515,16 +832,29 @@ hipError_t launch_k2(const KernelLayer& L, int64_t M, const uint8_t* qX, const v
   const uint32_t T = p.tiles_m * p.tiles_n, rem = T - p.full;
   const K2Sched sch{p.tiles_n, p.full, p.split, static_cast<float*>(workspace)};
   const uint32_t nblocks = p.full + rem * p.split;
-#define K2_LAUNCH(F, MM, SB) launch_k2_t<F, MM, SB>(L, M, qX, sX, lora_act, Y, ldy, ydtype, sch, nblocks, st)
+#define K2_LAUNCH(F, SB) launch_k2_t<F, false, SB>(L, M, qX, sX, lora_act, Y, ldy, ydtype, sch, nblocks, st)
+#define K2_STREAM(F, SB)                                                                                   \
+  hipLaunchKernelGGL((k2_stream<F, SB>), dim3(nblocks), dim3(NTHREADS), 0, st, qX,                        \
+                     static_cast<const uint8_t*>(sX), M, L.qW, static_cast<const uint8_t*>(L.sW), L.N, L.K, \
+                     static_cast<const uint16_t*>(lora_act), L.L2t, L.rank, Y, ldy, ydtype, sch)
   const int sub = sub_of(L.K);
-  if (L.fmt == 0) {
-    if (sub == 2) mma ? K2_LAUNCH(0, true, 2) : K2_LAUNCH(0, false, 2);
-    else mma ? K2_LAUNCH(0, true, 1) : K2_LAUNCH(0, false, 1);
+  if (mma) {  // the activation side in MMA form: streamed kernel
+    if (L.fmt == 0) {
+      if (sub == 2) K2_STREAM(0, 2);
+      else K2_STREAM(0, 1);
+    } else {
+      if (sub == 2) K2_STREAM(1, 2);
+      else K2_STREAM(1, 1);
+    }
+  } else if (L.fmt == 0) {
+    if (sub == 2) K2_LAUNCH(0, 2);
+    else K2_LAUNCH(0, 1);
   } else {
-    if (sub == 2) mma ? K2_LAUNCH(1, true, 2) : K2_LAUNCH(1, false, 2);
-    else mma ? K2_LAUNCH(1, true, 1) : K2_LAUNCH(1, false, 1);
+    if (sub == 2) K2_LAUNCH(1, 2);
+    else K2_LAUNCH(1, 1);
   }
 #undef K2_LAUNCH
+#undef K2_STREAM
   if (rem > 0)
     hipLaunchKernelGGL(k2_fixup, dim3(rem * 16), dim3(64), 0, st, static_cast<const float*>(workspace), sch, M,
                        L.N, Y, ldy, ydtype);

@@ -654,9 +654,13 @@ svdq_status svdq_prepare_weights(int64_t K, int64_t N, int32_t fmt, const uint8_
   if (!qW || !sW || !qW_out || !sW_out) return fail(SVDQ_EINVAL, "required pointer is NULL");
   const int64_t words = N * (K / 8);
   const int64_t groups = K / group_of(fmt);
+  const int64_t Np = (N + 3) / 4 * 4;  // scale rows padded to 4 bytes (fp16 rows: 8)
   if (fmt == SVDQ_MXFP4_G32) {
     std::memcpy(qW_out, qW, (size_t)(N * (K / 2)));
-    std::memcpy(sW_out, sW, (size_t)(groups * N));
+    const uint8_t* s8 = static_cast<const uint8_t*>(sW);
+    uint8_t* o8 = static_cast<uint8_t*>(sW_out);
+    for (int64_t g = 0; g < groups; ++g)
+      for (int64_t n = 0; n < Np; ++n) o8[g * Np + n] = n < N ? s8[g * N + n] : (uint8_t)127;
     return ok();
   }
   // codes: per 32-bit word (8 codes, code 2j in the low nibble of byte j), byte j of the
@@ -674,36 +678,41 @@ svdq_status svdq_prepare_weights(int64_t K, int64_t N, int32_t fmt, const uint8_
     }
     std::memcpy(qW_out + 4 * w, &o, 4);
   }
-  // scales: fp16 s = m * 2^e, m in [1, 2) -> word (fp16 bits of m) | (e + 9 + 127) << 16;
-  // s = 0 -> m = 0, byte 127
+  // scales: fp16 s = m * 2^e, m in [1, 2) -> plane of fp16 m [groups][Np], then plane of
+  // E8M0 bytes e + 9 + 127 [groups][Np]; s = 0 (and padding) -> m = 0, byte 127
   const uint16_t* s16 = static_cast<const uint16_t*>(sW);
-  uint32_t* o32 = static_cast<uint32_t*>(sW_out);
-  for (int64_t i = 0; i < groups * N; ++i) {
-    const uint16_t h = s16[i];
-    if (h & 0x8000u) return fail(SVDQ_ENUMERIC, "negative weight scale");
-    const uint32_t ex = (h >> 10) & 0x1F, mant = h & 0x3FF;
-    if (ex == 0x1F) return fail(SVDQ_ENUMERIC, "non-finite weight scale");
-    if (ex == 0 && mant == 0) {
-      o32[i] = 127u << 16;
-      continue;
-    }
-    int e;
-    uint32_t m10;
-    if (ex != 0) {
-      e = (int)ex - 15;
-      m10 = mant;
-    } else {  // subnormal: mant * 2^-24, normalise
-      int sh = 0;
-      uint32_t mm = mant;
-      while (!(mm & 0x400u)) {
-        mm <<= 1;
-        ++sh;
+  uint16_t* om = static_cast<uint16_t*>(sW_out);
+  uint8_t* oe = static_cast<uint8_t*>(sW_out) + groups * Np * 2;
+  for (int64_t g = 0; g < groups; ++g)
+    for (int64_t n = 0; n < Np; ++n) {
+      const int64_t o = g * Np + n;
+      const uint16_t h = n < N ? s16[g * N + n] : (uint16_t)0;
+      if (h & 0x8000u) return fail(SVDQ_ENUMERIC, "negative weight scale");
+      const uint32_t ex = (h >> 10) & 0x1F, mant = h & 0x3FF;
+      if (ex == 0x1F) return fail(SVDQ_ENUMERIC, "non-finite weight scale");
+      if (ex == 0 && mant == 0) {
+        om[o] = 0;
+        oe[o] = 127;
+        continue;
       }
-      e = -14 - sh;
-      m10 = mm & 0x3FF;
+      int e;
+      uint32_t m10;
+      if (ex != 0) {
+        e = (int)ex - 15;
+        m10 = mant;
+      } else {  // subnormal: mant * 2^-24, normalise
+        int sh = 0;
+        uint32_t mm = mant;
+        while (!(mm & 0x400u)) {
+          mm <<= 1;
+          ++sh;
+        }
+        e = -14 - sh;
+        m10 = mm & 0x3FF;
+      }
+      om[o] = (uint16_t)((15u << 10) | m10);
+      oe[o] = (uint8_t)(e + 9 + 127);
     }
-    o32[i] = ((15u << 10) | m10) | ((uint32_t)(e + 9 + 127) << 16);
-  }
   return ok();
 }
 

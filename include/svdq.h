@@ -60,13 +60,16 @@ typedef enum { SVDQ_F32 = 0, SVDQ_BF16 = 1 } svdq_dtype;
  *   PACKED: the format's storage form: qX [M][K/2] 4-bit codes (INT4 sign-magnitude
  *           nibbles, MXFP4 E2M1), sX [K/G][M] fp16 bits (INT4) or E8M0 bytes (MXFP4),
  *           lora_act [M][R16] fp32.
- *   MMA:    the matrix-core operand form, which kernel 2 uses without converting.
+ *   MMA:    the matrix-core operand form, which kernel 2 streams into LDS without
+ *           converting.  Mp = M rounded up to a multiple of 4.
  *           INT4: qX [M][K] one FP8 E4M3 byte per code (sign bit 7, magnitude in the
  *           mantissa bits: value q * 2^-9), each 8-code block stored as codes
- *           0,2,4,6,1,3,5,7; sX [K/64][M] u32 words (fp16 bits of m) | (e+9+127) << 16
- *           for the fp16 scale s = m * 2^e, m in [1, 2) (s = 0: m = 0, byte 127).
- *           MXFP4: qX and sX as PACKED.  Both: lora_act rows of 2*R16 bf16, [R16 hi]
- *           [R16 lo] with hi = bf16(v), lo = bf16(v - hi) of the fp32 value v. */
+ *           0,2,4,6,1,3,5,7; sX: for the fp16 scale s = m * 2^e (m in [1, 2)) the
+ *           plane fp16 m [K/64][Mp] then the plane of E8M0 bytes of 2^(e+9)
+ *           [K/64][Mp] (s = 0: m = 0, byte 127).
+ *           MXFP4: qX as PACKED; sX [K/32][Mp] E8M0 bytes.
+ *           Both: lora_act rows of 2*R16 bf16, [R16 hi][R16 lo] with hi = bf16(v),
+ *           lo = bf16(v - hi) of the fp32 value v. */
 typedef enum { SVDQ_ACT_PACKED = 0, SVDQ_ACT_MMA = 1 } svdq_act_form;
 
 #define SVDQ_MAX_RANK 128
@@ -81,8 +84,9 @@ typedef enum { SVDQ_ACT_PACKED = 0, SVDQ_ACT_MMA = 1 } svdq_act_form;
  *   L2t    [N][R16]   bf16  up projection transposed (L2^T), columns >= rank zero
  *   qW     [N][K/2]   u8    residual codes, row n = output channel n along K, in the
  *                           kernel bit order of svdq_prepare_weights
- *   sW     [K/G][N]   group-major scales as svdq_prepare_weights writes them: split
- *                           32-bit words (INT4, 4-byte aligned) or E8M0 bytes (MXFP4)
+ *   sW                group-major scales as svdq_prepare_weights writes them: INT4 the
+ *                           fp16 mantissa and E8M0 planes, MXFP4 E8M0 bytes, rows
+ *                           padded to Np (16-byte aligned)
  * Ld_hi/Ld_lo/L2t may be NULL iff rank == 0. */
 typedef struct svdq_layer {
   int64_t K, N;
@@ -159,15 +163,17 @@ svdq_status svdq_prepare_lowrank(int64_t K, int64_t N, int32_t rank, const float
                                  uint16_t* lo_out, uint16_t* L2t_out);
 
 /* Offline device layout of the residual weights (host pointers).  The values are those
- * of svdq_pack_weights / svdq_quantize_weights; only their encoding changes.
- *   MXFP4: qW_out = qW, sW_out = sW (E8M0 bytes), copied.
+ * of svdq_pack_weights / svdq_quantize_weights; only their encoding changes.  Np = N
+ * rounded up to a multiple of 4; scale rows are padded to it.
+ *   MXFP4: qW_out = qW; sW_out [K/32][Np] E8M0 bytes (padding 127).
  *   INT4:  qW_out [N][K/2]: each 32-bit word of 8 sign-magnitude codes (code 2j in the
  *          low nibble of byte j) is re-encoded so that byte j holds code 2j's magnitude
  *          in bits 0-2 and sign in bit 7, code 2j+1's magnitude in bits 4-6, and in bit 3
  *          the sign of code 2j-1 (indices mod 8): a mask then yields the even codes and
  *          a 4-bit rotate plus the same mask the odd ones, as FP8 E4M3 bytes q * 2^-9.
- *          sW_out [K/64][N] u32: the fp16 scale s = m * 2^e (m in [1, 2)) as
- *          (fp16 bits of m) | (e + 9 + 127) << 16; s = 0 gives m = 0, byte 127.
+ *          sW_out: the fp16 scale s = m * 2^e (m in [1, 2)) as two planes, fp16 m
+ *          [K/64][Np] then E8M0 bytes of 2^(e+9) [K/64][Np] ((K/64) * Np * 3 bytes);
+ *          s = 0 and padding give m = 0, byte 127.
  * EINVAL on bad sizes, ENUMERIC on a negative or non-finite scale. */
 svdq_status svdq_prepare_weights(int64_t K, int64_t N, int32_t fmt, const uint8_t* qW,
                                  const void* sW, uint8_t* qW_out, void* sW_out);

@@ -151,10 +151,11 @@ def test_prepare_lowrank_layouts():
 def test_prepare_weights_kernel_layout():
     """The kernel layout decodes back to the oracle's codes and scales: even codes by the
     mask 0x87, odd codes by a 4-bit rotate of the word and the same mask (FP8 E4M3 bytes
-    with zero exponent: magnitude in bits 0-2, sign in bit 7); each scale word is
-    m * 2^(byte - 127 - 9) with m the fp16 in its low half, m in [1, 2) or 0."""
+    with zero exponent: magnitude in bits 0-2, sign in bit 7); each scale is
+    m * 2^(byte - 127 - 9) with m from the fp16 plane and the byte from the E8M0 plane,
+    m in [1, 2) or 0; padded rows hold m = 0, byte 127."""
     rng = np.random.default_rng(11)
-    K, N = 256, 40
+    K, N = 256, 39  # N not a multiple of 4: padded scale rows
     R = (rng.standard_normal((K, N)) * 10.0 ** rng.uniform(-9, 2, (1, N))).astype(np.float32)
     R[:, 5] = 0.0
     R[64:128, 6] = 0.0
@@ -170,15 +171,20 @@ def test_prepare_weights_kernel_layout():
             b = (src >> (8 * j)) & 0x87
             dec[:, :, 2 * j + off] = ((b & 7) * np.where(b & 0x80, -1, 1)).reshape(N, K // 8)
     np.testing.assert_array_equal(dec.reshape(N, K), codes)
-    m = sk.astype(np.uint32)
-    mant = (m & 0xFFFF).astype(np.uint16).view(np.float16).astype(np.float64)
-    e = ((m >> 16) & 0xFF).astype(np.int64) - 127 - 9
+    Np = (N + 3) // 4 * 4
+    G = K // 64
+    assert sk.size == G * Np * 3
+    mant = sk[:G * Np * 2].view(np.float16).reshape(G, Np).astype(np.float64)
+    e = sk[G * Np * 2:].reshape(G, Np).astype(np.int64) - 127 - 9
     assert np.all((mant == 0) | ((mant >= 1) & (mant < 2)))
-    np.testing.assert_array_equal(mant * 2.0 ** e, sc.view(np.float16).astype(np.float64))
+    np.testing.assert_array_equal((mant * 2.0 ** e)[:, :N], sc.view(np.float16).astype(np.float64))
+    assert not mant[:, N:].any() and np.all(e[:, N:] == -9)
     c4, s4 = opack.quantize_residual(R, "mxfp4")
     qf, sf = svdq.prepare_weights(K, N, svdq.MXFP4_G32, opack.pack_codes(c4, "mxfp4"), s4)
     np.testing.assert_array_equal(qf, opack.pack_codes(c4, "mxfp4"))
-    np.testing.assert_array_equal(sf, s4)
+    sf = sf.reshape(K // 32, Np)
+    np.testing.assert_array_equal(sf[:, :N], s4)
+    assert np.all(sf[:, N:] == 127)
 
 
 # ------------------------------------------------------------------ error paths
@@ -228,5 +234,6 @@ def test_device_entry_points_validate_on_host():
     assert L.svdq_gemm_w4a4_lora_up(ref, 4, 0, 16, 16, 16, 16, 64, 0, 8, 1 << 20, None) == 1 and "workspace" in _err()
     assert L.svdq_linear_forward(ref, 4, 16, 256, 16, 64, 0, 256, 10, None) == 1 and "workspace" in _err()
     assert L.svdq_debug_group_sums(ref, 4, 16, 0, 0, 5, 4, 16, None) == 1 and "window" in _err()
-    # MMA form: FP8 codes (M*K bytes), 4-byte scale words, 2*R16 bf16 per row
-    assert L.svdq_workspace_bytes(ref, 100) >= 100 * 256 + 4 * 100 * 4 + 100 * 16 * 4
+    # MMA form: FP8 codes (M*K bytes), fp16 + E8M0 scale planes (3 bytes per group and
+    # row), 2*R16 bf16 per row
+    assert L.svdq_workspace_bytes(ref, 100) >= 100 * 256 + 4 * 100 * 3 + 100 * 16 * 4
