@@ -74,10 +74,10 @@ def _pmc_means(path):
     acc = collections.defaultdict(list)
     for r in csv.DictReader(open(path)):
         name = r["Kernel_Name"]
-        # kernel 2 of the timed forward: INT4, MMA activation form (the fixup launch is
-        # counted with it)
-        if "k2_gemm<0, false, true" in name or "k2_fixup" in name:
-            key = "k2" if "k2_gemm" in name else "fixup"
+        # kernel 2 of the timed forward: the INT4 streamed kernel on the MMA activation
+        # form (the fixup launch is counted with it)
+        if "k2_stream<0," in name or "k2_fixup" in name:
+            key = "k2" if "k2_stream" in name else "fixup"
         elif "copyBuffer" in name or "copy" in name.lower():
             key = "copy"
         else:
@@ -99,7 +99,7 @@ def write_traffic(fetch_csv, write_csv):
     # the fixup launch runs once per kernel-2 launch
     fetch_b = (f["k2"][0] + f.get("fixup", (0.0, 0))[0]) * 1024.0 / ffac
     write_b = (w["k2"][0] + w.get("fixup", (0.0, 0))[0]) * 1024.0 / wfac
-    d = {"kernel": "k2_gemm<INT4, MMA form> + k2_fixup", "workload": "FLUX.1 QKV projection M=4608 K=3072 N=9216 r=32, fp32 Y",
+    d = {"kernel": "k2_stream<INT4> + k2_fixup", "workload": "FLUX.1 QKV projection M=4608 K=3072 N=9216 r=32, fp32 Y",
          "k2_source_hash": source_hash(K2_SOURCES), "fetch_kib_raw": f["k2"][0], "write_kib_raw": w["k2"][0],
          "copy_fetch_factor": ffac, "copy_write_factor": wfac, "fetch_bytes": fetch_b, "write_bytes": write_b,
          "bytes_per_launch": fetch_b + write_b, "dispatches": f["k2"][1],

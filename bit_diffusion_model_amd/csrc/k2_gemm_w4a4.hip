@@ -427,13 +427,13 @@ __global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 
 // Kernel 2, streamed (MMA activation form): codes and scales go from global memory
 // straight into LDS with buffer loads that write LDS (each lane's 16 or 4 bytes land at
 // the instruction's LDS base + lane * size), so no register staging, no LDS store
-// instructions and no wait for a stage's data until it is needed.  DNB LDS buffers: the
-// loads of stage k+2 are issued while stage k is computed; one barrier per stage.
+// instructions and no wait for a stage's data until it is needed.  NB = 3 LDS buffers:
+// the loads of stage k+2 are issued while stage k is computed; NB = 2: stage k+1's (less
+// LDS, for more blocks per CU).  One barrier per stage.
 // 16-byte slots of each operand row are XOR-swizzled with the row (rows are not padded:
 // a load instruction fills 1 KB contiguously), so that the 8 rows an MFMA operand read
 // takes at once fall on 8 different bank groups.  The weight codes stay 4-bit in LDS and
 // are expanded to FP8 after the read, per wave.
-constexpr int DNB = 3;
 
 template <int FMT, int SUB>
 struct DLay {
@@ -471,19 +471,19 @@ __device__ __forceinline__ void wait_vm() {  // s_waitcnt vmcnt(N), other counte
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int FMT, int SUB>
-__global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void k2_stream(
+template <int FMT, int SUB, int NB, int WPE>
+__global__ __launch_bounds__(NTHREADS, WPE) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void k2_stream(
     const uint8_t* __restrict__ qX, const uint8_t* __restrict__ sX, int64_t M,
     const uint8_t* __restrict__ qW, const uint8_t* __restrict__ sW, int64_t N, int64_t K,
     const uint16_t* __restrict__ lora_act, const uint16_t* __restrict__ L2, int rank,
     void* __restrict__ Y, int64_t ldy, int ydtype, K2Sched sch) {
   using D = DLay<FMT, SUB>;
-  // three separate arrays, always addressed statically (the main loop is unrolled by
-  // three), so the compiler can tell a buffer's pending loads from reads of another
+  // separate arrays, always addressed statically (the main loop is unrolled by NB), so
+  // the compiler can tell a buffer's pending loads from reads of another
+  static_assert(NB == 2 || NB == 3, "two or three LDS buffers");
   __shared__ __attribute__((aligned(1024))) uint8_t lds0[D::BUF];
   __shared__ __attribute__((aligned(1024))) uint8_t lds1[D::BUF];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds2[D::BUF];
-  static_assert(DNB == 3, "three LDS buffers");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds2[NB == 3 ? D::BUF : 16];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -655,31 +655,46 @@ __global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 
   };
 
   // ---- main loop ------------------------------------------------------------------------
-  // Stage k's loads were issued two stages earlier into buffer (k - kbeg) % DNB.  A wave
-  // waits for its own loads of stage k (vmcnt: the loads of stage k+1 may stay in
+  // Stage k's loads were issued NB-1 stages earlier into buffer (k - kbeg) % NB.  A wave
+  // waits for its own loads of stage k (with NB = 3 the loads of stage k+1 may stay in
   // flight), the barrier makes every wave's loads visible and frees the buffer read
-  // during stage k-1, which then receives stage k+2.
-  // Every step issues a stage's loads: past the end, the last stage again (harmless,
-  // never read), so the count in flight is the same at every wait and the loop body has
-  // no branches.
-  auto kstep = [&](int k, const uint8_t* cur, uint8_t* nxt) {
-    wait_vm<D::NDW>();  // this wave's loads of stage k are in; stage k+1's may be in flight
-    __builtin_amdgcn_s_barrier();
-    issue(k + 2 < kend ? k + 2 : kend - 1, nxt);
-#pragma unroll
-    for (int u = 0; u < SUB; ++u) compute(cur, u);
-  };
+  // during stage k-1, which then receives stage k+NB-1.  Every step issues a stage's
+  // loads: past the end, the last stage again (harmless, never read), so the count in
+  // flight is the same at every wait and the loop body has no branches.
   const int nk = kend - kbeg;
-  issue(kbeg, lds0);
-  issue(kbeg + 1 < kend ? kbeg + 1 : kend - 1, lds1);
   int k = kbeg;
-  for (; k + 3 <= kend; k += 3) {
-    kstep(k, lds0, lds2);
-    kstep(k + 1, lds1, lds0);
-    kstep(k + 2, lds2, lds1);
+  if constexpr (NB == 3) {
+    auto kstep = [&](int kk, const uint8_t* cur, uint8_t* nxt) {
+      wait_vm<D::NDW>();
+      __builtin_amdgcn_s_barrier();
+      issue(kk + 2 < kend ? kk + 2 : kend - 1, nxt);
+#pragma unroll
+      for (int u = 0; u < SUB; ++u) compute(cur, u);
+    };
+    issue(kbeg, lds0);
+    issue(kbeg + 1 < kend ? kbeg + 1 : kend - 1, lds1);
+    for (; k + 3 <= kend; k += 3) {
+      kstep(k, lds0, lds2);
+      kstep(k + 1, lds1, lds0);
+      kstep(k + 2, lds2, lds1);
+    }
+    if (nk % 3 >= 1) kstep(k, lds0, lds2);
+    if (nk % 3 == 2) kstep(k + 1, lds1, lds0);
+  } else {
+    auto kstep = [&](int kk, const uint8_t* cur, uint8_t* nxt) {
+      wait_vm<0>();
+      __builtin_amdgcn_s_barrier();
+      issue(kk + 1 < kend ? kk + 1 : kend - 1, nxt);
+#pragma unroll
+      for (int u = 0; u < SUB; ++u) compute(cur, u);
+    };
+    issue(kbeg, lds0);
+    for (; k + 2 <= kend; k += 2) {
+      kstep(k, lds0, lds1);
+      kstep(k + 1, lds1, lds0);
+    }
+    if (nk % 2) kstep(k, lds0, lds1);
   }
-  if (nk % 3 >= 1) kstep(k, lds0, lds2);
-  if (nk % 3 == 2) kstep(k + 1, lds1, lds0);
   wait_vm<0>();
 
   // ---- low-rank up projection: acc += lora_act[rows, :] L2[:, cols] ----------------------
@@ -775,12 +790,21 @@ static int blocks_per_cu() {
   return n;
 }
 
+// Streamed-kernel configuration per format: LDS buffers and waves per SIMD.
+template <int FMT>
+struct SCfg {
+  static constexpr int NB = 3, WPE = 2;
+};
+
 template <int FMT, int SUB>
 static int stream_blocks_per_cu() {
   static int n = 0;
   if (n == 0) {
     int v = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, k2_stream<FMT, SUB>, NTHREADS, 0) != hipSuccess || v < 1) v = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, k2_stream<FMT, SUB, SCfg<FMT>::NB, SCfg<FMT>::WPE>,
+                                                     NTHREADS, 0) != hipSuccess ||
+        v < 1)
+      v = 1;
     n = v;
   }
   return n;
@@ -834,7 +858,7 @@ hipError_t launch_k2(const KernelLayer& L, int64_t M, const uint8_t* qX, const v
   const uint32_t nblocks = p.full + rem * p.split;
 #define K2_LAUNCH(F, SB) launch_k2_t<F, false, SB>(L, M, qX, sX, lora_act, Y, ldy, ydtype, sch, nblocks, st)
 #define K2_STREAM(F, SB)                                                                                   \
-  hipLaunchKernelGGL((k2_stream<F, SB>), dim3(nblocks), dim3(NTHREADS), 0, st, qX,                        \
+  hipLaunchKernelGGL((k2_stream<F, SB, SCfg<F>::NB, SCfg<F>::WPE>), dim3(nblocks), dim3(NTHREADS), 0, st, qX, \
                      static_cast<const uint8_t*>(sX), M, L.qW, static_cast<const uint8_t*>(L.sW), L.N, L.K, \
                      static_cast<const uint16_t*>(lora_act), L.L2t, L.rank, Y, ldy, ydtype, sch)
   const int sub = sub_of(L.K);
