@@ -48,13 +48,13 @@ static svdq_status check_layer(const svdq_layer* L, KernelLayer& kl) {
   if (L->rank < 0 || L->rank > SVDQ_MAX_RANK)
     return fail(SVDQ_EUNSUPPORTED, "rank must be in [0, %d] (got %d)", SVDQ_MAX_RANK, (int)L->rank);
   if (!L->inv_s || !L->qW || !L->sW) return fail(SVDQ_EINVAL, "layer inv_s, qW and sW must be non-NULL");
-  if (L->rank > 0 && (!L->Ld_hi || !L->Ld_lo || !L->L2t))
-    return fail(SVDQ_EINVAL, "layer Ld_hi, Ld_lo and L2t must be non-NULL when rank > 0");
+  if (L->rank > 0 && (!L->L1t || !L->L2t))
+    return fail(SVDQ_EINVAL, "layer L1t and L2t must be non-NULL when rank > 0");
   if (!aligned(L->sW, 16)) return fail(SVDQ_EINVAL, "layer sW must be 16-byte aligned");
   if (!aligned(L->inv_s, 16) || !aligned(L->qW, 16) ||
-      (L->rank > 0 && (!aligned(L->Ld_hi, 16) || !aligned(L->Ld_lo, 16) || !aligned(L->L2t, 16))))
-    return fail(SVDQ_EINVAL, "layer inv_s, qW, Ld_hi, Ld_lo and L2t must be 16-byte aligned");
-  kl = KernelLayer{L->K, L->N, L->rank, L->fmt, L->inv_s, L->Ld_hi, L->Ld_lo, L->L2t, L->qW, L->sW};
+      (L->rank > 0 && (!aligned(L->L1t, 16) || !aligned(L->L2t, 16))))
+    return fail(SVDQ_EINVAL, "layer inv_s, qW, L1t and L2t must be 16-byte aligned");
+  kl = KernelLayer{L->K, L->N, L->rank, L->fmt, L->inv_s, L->L1t, L->L2t, L->qW, L->sW};
   return SVDQ_OK;
 }
 
@@ -76,7 +76,7 @@ static WsLayout ws_layout(const svdq_layer* L, int64_t M) {
   const size_t Mp = ((size_t)M + 3) / 4 * 4;
   w.la = w.sx + rup((size_t)(L->K / group_of(L->fmt)) * Mp * (f8 ? 3 : 1));
   w.part = w.la + rup((size_t)M * (size_t)((L->rank + 15) / 16 * 16) * 4);
-  KernelLayer kl{L->K, L->N, L->rank, L->fmt, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+  KernelLayer kl{L->K, L->N, L->rank, L->fmt, nullptr, nullptr, nullptr, nullptr, nullptr};
   w.total = w.part + rup(plan_k2(kl, M, true).bytes);
   return w;
 }
@@ -96,7 +96,7 @@ size_t svdq_workspace_bytes(const svdq_layer* layer, int64_t M) {
 
 size_t svdq_gemm_workspace_bytes(const svdq_layer* layer, int64_t M, int32_t form) {
   if (!layer || M < 1 || check_dims(layer->K, layer->N, layer->fmt) != SVDQ_OK) return 0;
-  KernelLayer kl{layer->K, layer->N, layer->rank, layer->fmt, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+  KernelLayer kl{layer->K, layer->N, layer->rank, layer->fmt, nullptr, nullptr, nullptr, nullptr, nullptr};
   return plan_k2(kl, M, form == SVDQ_ACT_MMA).bytes;
 }
 

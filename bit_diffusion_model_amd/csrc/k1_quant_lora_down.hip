@@ -15,13 +15,23 @@
 // loads of X).  One INT4 group (64) is therefore spread over the 4 lanes l, l^16,
 // l^32, l^48; one FP4 group (32) over lanes l, l^16.
 //
-// Down projection: X_hat L1 = X (diag(inv_s) L1).  The fold of inv_s into L1 is done
-// offline and stored as a bf16 hi/lo pair (Ld_hi + Ld_lo), so the raw bf16 X is the
-// MFMA A operand with no conversion.  v_mfma_f32_16x16x32_bf16: lane l supplies row
-// l & 15 and k-block l >> 4; we feed the lane's first 8 channels to one MFMA and the
-// next 8 to a second, and the B operand (Ld rows, contiguous along K) uses the same
+// Down projection: X_hat L1 with L1 as the pack stores it (bf16, transposed to
+// [rank][K]).  The smoothed activations exist only in fp32 registers, so each is split
+// into a bf16 pair hi + lo (hi = bf16(x), lo = bf16(x - hi): x to ~2^-17) and the
+// pair feeds two v_mfma_f32_16x16x32_bf16 against the same L1 fragment, which keeps
+// the low-rank branch fp32-accurate with one read of L1 per chunk.  Lane l supplies
+// MFMA row l & 15 and k-block l >> 4: the lane's first 8 channels go to one MFMA and
+// the next 8 to a second, and the B operand (L1 rows, contiguous along K) uses the same
 // channel order.  Partial sums of the 8 waves are added through LDS at the end, in a
 // fixed order.
+//
+// INT4 rounding: t = x * (1 / s) is within |x / s| * 2^-23 of the quotient x / s, so
+// round(t) is the correctly rounded code unless x / s lies within 2^-17 of a half
+// integer.  Such lanes are flagged and, if any lane of the wave has one, the chunk takes
+// the exact correction (x - q * s is exact near s / 2, and ties go to even).  The MMA
+// form then converts t * 2^-9 with the hardware FP8 conversion (round to nearest even
+// on the E4M3 subnormal grid, whose step is 2^-9): the byte of code q, with no integer
+// conversion or bit packing.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -29,12 +39,20 @@ namespace svdq {
 
 constexpr int K1_WAVES = 8;
 
+typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+
+// fp32 pair -> bf16 pair bits, round to nearest even (element a in the low half)
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+  const bf2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Rank tiles 1 and 2 fit in 128 VGPRs, so two 8-wave blocks share a CU.
 template <int FMT, int NT, bool MMA>
-__global__ __launch_bounds__(64 * K1_WAVES) void k1_quant_lora_down(
-    const uint16_t* __restrict__ X, int64_t ldx, int64_t M, int64_t K,
-    const float* __restrict__ inv_s, const uint16_t* __restrict__ Ldh,
-    const uint16_t* __restrict__ Ldl, int rank, uint8_t* __restrict__ qX,
-    void* __restrict__ sXv, float* __restrict__ lora_act) {
+__global__ __launch_bounds__(64 * K1_WAVES) __attribute__((amdgpu_waves_per_eu(NT == 1 || NT == 2 ? 4 : 2))) void
+k1_quant_lora_down(const uint16_t* __restrict__ X, int64_t ldx, int64_t M, int64_t K,
+                   const float* __restrict__ inv_s, const uint16_t* __restrict__ L1t, int rank,
+                   uint8_t* __restrict__ qX, void* __restrict__ sXv, float* __restrict__ lora_act) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int r16 = lane & 15;
@@ -48,8 +66,7 @@ __global__ __launch_bounds__(64 * K1_WAVES) void k1_quant_lora_down(
   const __amdgpu_buffer_rsrc_t rX = make_rsrc(X + m0 * ldx, (uint32_t)(((nrows - 1) * ldx + K) * 2));
   const __amdgpu_buffer_rsrc_t rS = make_rsrc(inv_s, (uint32_t)(K * 4));
   const uint32_t xoff = (uint32_t)(r16 * ldx + sub * 16) * 2;
-  const __amdgpu_buffer_rsrc_t rLh = make_rsrc(Ldh, (uint32_t)(rank * K * 2));
-  const __amdgpu_buffer_rsrc_t rLl = make_rsrc(Ldl, (uint32_t)(rank * K * 2));
+  const __amdgpu_buffer_rsrc_t rL = make_rsrc(L1t, (uint32_t)(rank * K * 2));
 
   v4f acc[NT > 0 ? NT : 1];
 #pragma unroll
@@ -73,19 +90,15 @@ __global__ __launch_bounds__(64 * K1_WAVES) void k1_quant_lora_down(
     const uint32_t xw[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
     const uint32_t sw[16] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w,
                              s2.x, s2.y, s2.z, s2.w, s3.x, s3.y, s3.z, s3.w};
-    const uint4 cxa = xa, cxb = xb;
     if (c + K1_WAVES < nchunks) fetch(c + K1_WAVES);
 
-    // low-rank down projection operands for this chunk (issued early); rows past the
-    // rank read as zeros through the range check
-    uint4 hA[NT > 0 ? NT : 1], hB[NT > 0 ? NT : 1], lA[NT > 0 ? NT : 1], lB[NT > 0 ? NT : 1];
+    // L1 fragments for this chunk (issued early); rows past the rank read as zeros
+    uint4 LA[NT > 0 ? NT : 1], LB[NT > 0 ? NT : 1];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const uint32_t o = (uint32_t)((t * 16 + r16) * K + k0) * 2;
-      hA[t] = buf_load16(rLh, o);
-      hB[t] = buf_load16(rLh, o + 16);
-      lA[t] = buf_load16(rLl, o);
-      lB[t] = buf_load16(rLl, o + 16);
+      LA[t] = buf_load16(rL, o);
+      LB[t] = buf_load16(rL, o + 16);
     }
 
     float xh[16];
@@ -99,57 +112,77 @@ __global__ __launch_bounds__(64 * K1_WAVES) void k1_quant_lora_down(
     for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(xh[i]));
     a = wave_max_xor(a, 16);
 
-    uint32_t nib[16];
     if constexpr (FMT == 0) {
-      // INT4: s = fp16(fp32(a / 7)), saturating; q = round-half-even(x / s) exactly.
+      // INT4: s = fp16(fp32(a / 7)), saturating; q = round-half-even(x / s) exactly
       a = wave_max_xor(a, 32);
       const _Float16 sh = (_Float16)fminf(a / 7.0f, 65504.0f);
       const float sf = (float)sh;
-      const float rcp = 1.0f / sf;
-      const float hs = 0.5f * sf;
-      // Common path: q0 = rint(x * rcp).  x * rcp differs from x / s by at most
-      // |x / s| * 2^-23 < 2^-19 (|x / s| < 16 even for subnormal fp16 scales), so q0 is
-      // the correctly rounded quotient unless x / s lies within 2^-17 of a half
-      // integer.  Such lanes are flagged and, if any lane of the wave has one, the
-      // chunk takes the exact correction: x - q0 * s is exact near s / 2, so comparing
-      // its magnitude with s / 2 decides the rounding, ties to even.
-      float q[16];
-      bool near = false;
+      const float rcp = sf > 0.0f ? 1.0f / sf : 0.0f;  // s = 0: every x is 0, every code 0
+      float t[16];
+      float dev = 0.f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float t = xh[i] * rcp;
-        q[i] = rintf(t);
-        near |= fabsf(t - q[i]) > 0.49999237f;  // 0.5 - 2^-17
+        t[i] = xh[i] * rcp;
+        dev = fmaxf(dev, fabsf(t[i] - rintf(t[i])));
       }
-      if (__builtin_amdgcn_ballot_w64(near) != 0) {
+      if (__builtin_amdgcn_ballot_w64(dev > 0.49999237f) != 0) {  // 0.5 - 2^-17
+        const float hs = 0.5f * sf;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float e = fmaf(-q[i], sf, xh[i]);
+          const float q = rintf(t[i]);
+          const float e = fmaf(-q, sf, xh[i]);
           const float ae = fabsf(e);
-          const int odd = ((int)q[i]) & 1;
+          const int odd = ((int)q) & 1;
           const int away = (int)(ae > hs) | ((int)(ae == hs) & odd);
-          q[i] = q[i] + (float)away * copysignf(1.0f, e);
+          t[i] = q + (float)away * copysignf(1.0f, e);
         }
       }
+      if (row_ok) {
+        if constexpr (MMA) {
+          // one FP8 E4M3 byte per code (sign, exponent 0, mantissa |q|: value q * 2^-9),
+          // [M][K] bytes, each 8-element block stored as its even elements then its odd
+          // ones (the order of the GEMM's own nibble expansion of the weights, which the
+          // two operands must share).  The clamp to +-7 only acts for subnormal fp16
+          // scales; code 0 may carry either sign bit.
+          uint32_t b[4];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float qc = __builtin_amdgcn_fmed3f(q[i], -7.0f, 7.0f);
-        const uint32_t mag = (uint32_t)fabsf(qc);
-        nib[i] = (sf == 0.0f) ? 0u : (mag | (qc < 0.0f ? 8u : 0u));
-      }
-      if (row_ok && sub == 0) {
-        if constexpr (MMA) {  // the split planes kernel 2 consumes: fp16 m, then E8M0 bytes
-          const int64_t Mp = (M + 3) & ~int64_t(3);
-          const uint32_t w = split_scale_word(__builtin_bit_cast(uint16_t, sh));
-          reinterpret_cast<uint16_t*>(sXv)[(int64_t)c * Mp + row] = (uint16_t)(w & 0xFFFFu);
-          reinterpret_cast<uint8_t*>(sXv)[(K >> 6) * Mp * 2 + (int64_t)c * Mp + row] = (uint8_t)(w >> 16);
+          for (int d = 0; d < 4; ++d) {
+            const int e0 = (d >> 1) * 8 + (d & 1);
+            float v[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              v[j] = __builtin_amdgcn_fmed3f(t[e0 + 2 * j] * 0x1p-9f, -7.0f * 0x1p-9f, 7.0f * 0x1p-9f);
+            int w = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+            w = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], w, true);
+            b[d] = (uint32_t)w;
+          }
+          *reinterpret_cast<uint4*>(qX + row * K + k0) = make_uint4(b[0], b[1], b[2], b[3]);
         } else {
-          reinterpret_cast<uint16_t*>(sXv)[(int64_t)c * M + row] = __builtin_bit_cast(uint16_t, sh);
+          uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float qc = __builtin_amdgcn_fmed3f(rintf(t[i]), -7.0f, 7.0f);
+            const uint32_t nib = (uint32_t)fabsf(qc) | (qc < 0.0f ? 8u : 0u);
+            if (i < 8) w0 |= nib << (4 * i);
+            else w1 |= nib << (4 * (i - 8));
+          }
+          *reinterpret_cast<uint2*>(qX + row * (K >> 1) + (k0 >> 1)) = make_uint2(w0, w1);
+        }
+        if (sub == 0) {
+          if constexpr (MMA) {  // the split planes kernel 2 consumes: fp16 m, then E8M0 bytes
+            const int64_t Mp = (M + 3) & ~int64_t(3);
+            const uint32_t w = split_scale_word(__builtin_bit_cast(uint16_t, sh));
+            reinterpret_cast<uint16_t*>(sXv)[(int64_t)c * Mp + row] = (uint16_t)(w & 0xFFFFu);
+            reinterpret_cast<uint8_t*>(sXv)[(K >> 6) * Mp * 2 + (int64_t)c * Mp + row] = (uint8_t)(w >> 16);
+          } else {
+            reinterpret_cast<uint16_t*>(sXv)[(int64_t)c * M + row] = __builtin_bit_cast(uint16_t, sh);
+          }
         }
       }
     } else {
       // MXFP4: e = smallest exponent with 6 * 2^e >= a (clamped to [-127, 127]);
-      // codes = E2M1 round-half-even of x * 2^-e (hardware convert, scale 1).
+      // codes = E2M1 round-half-even of x * 2^-e (hardware convert, scale 1), each
+      // pair converted straight into its byte of the packed word.
       const uint32_t ab = __float_as_uint(a);
       const int E = (int)((ab >> 23) & 0xFF);
       int e;
@@ -158,51 +191,46 @@ __global__ __launch_bounds__(64 * K1_WAVES) void k1_quant_lora_down(
       else e = (E - 127) - 2 + (((ab & 0x7FFFFFu) > 0x400000u) ? 1 : 0);
       e = e < -127 ? -127 : (e > 127 ? 127 : e);
       const float inv2e = __uint_as_float((uint32_t)(127 - e) << 23);
+      float y[16];
 #pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        uint32_t p = 0;
-        p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, xh[i] * inv2e, xh[i + 1] * inv2e, 1.0f, 0);
-        nib[i] = p & 0xF;
-        nib[i + 1] = (p >> 4) & 0xF;
-      }
-      if (row_ok && (sub & 1) == 0) {
-        const int64_t ld = MMA ? (M + 3) & ~int64_t(3) : M;  // MMA form: rows padded to 4
-        reinterpret_cast<uint8_t*>(sXv)[(int64_t)(2 * c + (sub >> 1)) * ld + row] = (uint8_t)(e + 127);
-      }
-    }
-    if (row_ok) {
-      if constexpr (MMA && FMT == 0) {
-        // one FP8 E4M3 byte per code (sign, exponent 0, mantissa |q|: value q * 2^-9),
-        // the operand form the GEMM consumes; [M][K] bytes, each 8-element block stored
-        // as its even elements then its odd ones (the order of the GEMM's own nibble
-        // expansion of the weights, which the two operands must share)
-        uint32_t b[4] = {0, 0, 0, 0};
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int d = (i >> 3) * 2 + (i & 1), pos = (i & 7) >> 1;
-          b[d] |= ((nib[i] & 7u) | ((nib[i] & 8u) << 4)) << (8 * pos);
-        }
-        *reinterpret_cast<uint4*>(qX + row * K + k0) = make_uint4(b[0], b[1], b[2], b[3]);
-      } else {
-        uint32_t w0 = 0, w1 = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          w0 |= (nib[2 * j] | (nib[2 * j + 1] << 4)) << (8 * j);
-          w1 |= (nib[8 + 2 * j] | (nib[8 + 2 * j + 1] << 4)) << (8 * j);
-        }
+      for (int i = 0; i < 16; ++i) y[i] = xh[i] * inv2e;
+      uint32_t w0 = 0, w1 = 0;  // the byte index operand must be a literal
+      w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, y[0], y[1], 1.0f, 0);
+      w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, y[2], y[3], 1.0f, 1);
+      w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, y[4], y[5], 1.0f, 2);
+      w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, y[6], y[7], 1.0f, 3);
+      w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, y[8], y[9], 1.0f, 0);
+      w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, y[10], y[11], 1.0f, 1);
+      w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, y[12], y[13], 1.0f, 2);
+      w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, y[14], y[15], 1.0f, 3);
+      if (row_ok) {
         *reinterpret_cast<uint2*>(qX + row * (K >> 1) + (k0 >> 1)) = make_uint2(w0, w1);
+        if ((sub & 1) == 0) {
+          const int64_t ld = MMA ? (M + 3) & ~int64_t(3) : M;  // MMA form: rows padded to 4
+          reinterpret_cast<uint8_t*>(sXv)[(int64_t)(2 * c + (sub >> 1)) * ld + row] = (uint8_t)(e + 127);
+        }
       }
     }
 
     if constexpr (NT > 0) {
-      const v8bf a0 = __builtin_bit_cast(v8bf, cxa);
-      const v8bf a1 = __builtin_bit_cast(v8bf, cxb);
+      // x = hi + lo as bf16 pairs, channels 0-7 of the lane in a*0, 8-15 in a*1
+      uint32_t hw[8], lw[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        hw[j] = pk_bf16(xh[2 * j], xh[2 * j + 1]);
+        lw[j] = pk_bf16(xh[2 * j] - bf16_lo_to_f32(hw[j]), xh[2 * j + 1] - bf16_hi_to_f32(hw[j]));
+      }
+      const v8bf a0h = __builtin_bit_cast(v8bf, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+      const v8bf a1h = __builtin_bit_cast(v8bf, make_uint4(hw[4], hw[5], hw[6], hw[7]));
+      const v8bf a0l = __builtin_bit_cast(v8bf, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+      const v8bf a1l = __builtin_bit_cast(v8bf, make_uint4(lw[4], lw[5], lw[6], lw[7]));
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, __builtin_bit_cast(v8bf, hA[t]), acc[t], 0, 0, 0);
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, __builtin_bit_cast(v8bf, hB[t]), acc[t], 0, 0, 0);
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, __builtin_bit_cast(v8bf, lA[t]), acc[t], 0, 0, 0);
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, __builtin_bit_cast(v8bf, lB[t]), acc[t], 0, 0, 0);
+        const v8bf bA = __builtin_bit_cast(v8bf, LA[t]), bB = __builtin_bit_cast(v8bf, LB[t]);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0h, bA, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1h, bB, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0l, bA, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1l, bB, acc[t], 0, 0, 0);
       }
     }
   }
@@ -215,8 +243,8 @@ __global__ __launch_bounds__(64 * K1_WAVES) void k1_quant_lora_down(
 #pragma unroll
       for (int i = 0; i < 4; ++i) red[wave][4 * sub + i][t * 16 + r16] = acc[t][i];
     __syncthreads();
-    // all NT * 16 columns are written; those past the rank are zero (their factor
-    // rows read as zeros)
+    // all NT * 16 columns are written; those past the rank are zero (their L1 rows read
+    // as zeros)
     constexpr int R16 = NT * 16;
     for (int idx = threadIdx.x; idx < 16 * R16; idx += 64 * K1_WAVES) {
       const int rr = idx / R16, cc = idx - rr * R16;
@@ -248,7 +276,7 @@ static hipError_t launch_k1_fmt(const KernelLayer& L, int64_t M, const uint16_t*
 #define K1_CASE(NTV)                                                                            \
   case NTV:                                                                                     \
     hipLaunchKernelGGL((k1_quant_lora_down<FMT, NTV, MMA>), grid, block, 0, st, X, ldx, M, L.K, \
-                       L.inv_s, L.Ld_hi, L.Ld_lo, L.rank, qX, sX, static_cast<float*>(lora_act));                    \
+                       L.inv_s, L.L1t, L.rank, qX, sX, static_cast<float*>(lora_act));                    \
     break;
   switch (nt) {
     K1_CASE(0) K1_CASE(1) K1_CASE(2) K1_CASE(3) K1_CASE(4)

@@ -627,20 +627,11 @@ svdq_status svdq_concat_lora(int64_t K, int64_t N, const float* s, int32_t rank,
   return ok();
 }
 
-svdq_status svdq_prepare_lowrank(int64_t K, int64_t N, int32_t rank, const float* inv_s, const uint16_t* L1t,
-                                 const uint16_t* L2, uint16_t* hi_out, uint16_t* lo_out, uint16_t* L2t_out) {
-  if (K < 1 || N < 1 || rank < 0) return fail(SVDQ_EINVAL, "need K >= 1, N >= 1 and rank >= 0");
+svdq_status svdq_prepare_lowrank(int64_t N, int32_t rank, const uint16_t* L2, uint16_t* L2t_out) {
+  if (N < 1 || rank < 0) return fail(SVDQ_EINVAL, "need N >= 1 and rank >= 0");
   if (rank > SVDQ_MAX_RANK) return fail(SVDQ_EUNSUPPORTED, "rank exceeds %d", SVDQ_MAX_RANK);
   if (rank == 0) return ok();
-  if (!inv_s || !L1t || !L2 || !hi_out || !lo_out || !L2t_out) return fail(SVDQ_EINVAL, "required pointer is NULL");
-  for (int64_t j = 0; j < rank; ++j)
-    for (int64_t k = 0; k < K; ++k) {
-      const float v = inv_s[k] * bf16_to_float(L1t[j * K + k]);
-      const uint16_t hb = double_to_bf16((double)v);
-      const float rem = v - bf16_to_float(hb);
-      hi_out[j * K + k] = hb;
-      lo_out[j * K + k] = double_to_bf16((double)rem);
-    }
+  if (!L2 || !L2t_out) return fail(SVDQ_EINVAL, "required pointer is NULL");
   const int64_t r16 = (rank + 15) / 16 * 16;
   for (int64_t n = 0; n < N; ++n)
     for (int64_t j = 0; j < r16; ++j) L2t_out[n * r16 + j] = j < rank ? L2[j * N + n] : (uint16_t)0;

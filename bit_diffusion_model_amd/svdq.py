@@ -32,8 +32,7 @@ class SvdqError(RuntimeError):
 class _Layer(ctypes.Structure):
     _fields_ = [
         ("K", ctypes.c_int64), ("N", ctypes.c_int64), ("rank", ctypes.c_int32), ("fmt", ctypes.c_int32),
-        ("inv_s", ctypes.c_void_p), ("Ld_hi", ctypes.c_void_p), ("Ld_lo", ctypes.c_void_p),
-        ("L2t", ctypes.c_void_p), ("qW", ctypes.c_void_p), ("sW", ctypes.c_void_p),
+        ("inv_s", ctypes.c_void_p), ("L1t", ctypes.c_void_p), ("L2t", ctypes.c_void_p), ("qW", ctypes.c_void_p), ("sW", ctypes.c_void_p),
     ]
 
 
@@ -63,7 +62,7 @@ def lib():
         "svdq_pack_weights": (I32, [I64, I64, P, P, F, I32, I32, P, P, P, P, P, P, P]),
         "svdq_quantize_weights": (I32, [I64, I64, P, I32, P, P]),
         "svdq_concat_lora": (I32, [I64, I64, P, I32, P, P, I32, P, P, F, P, P]),
-        "svdq_prepare_lowrank": (I32, [I64, I64, I32, P, P, P, P, P, P]),
+        "svdq_prepare_lowrank": (I32, [I64, I32, P, P]),
         "svdq_prepare_weights": (I32, [I64, I64, I32, P, P, P, P]),
         "svdq_quantize_act_lora_down": (I32, [P, I64, P, I64, I32, P, P, P, P]),
         "svdq_gemm_w4a4_lora_up": (I32, [P, I64, I32, P, P, P, P, I64, I32, P, ctypes.c_size_t, P]),
@@ -167,18 +166,13 @@ def r16(rank: int) -> int:
     return (rank + 15) // 16 * 16
 
 
-def prepare_lowrank(inv_s: np.ndarray, L1t: np.ndarray, L2: np.ndarray):
-    """Device layouts of the low-rank branch: (Ld_hi, Ld_lo [rank][K], L2t [N][R16])."""
-    inv = np.ascontiguousarray(inv_s, dtype=np.float32)
-    L1t = np.ascontiguousarray(L1t, dtype=np.uint16)
+def prepare_lowrank(L2: np.ndarray):
+    """Device layout of the up projection: L2t [N][R16] (L2 transposed, zero-padded)."""
     L2 = np.ascontiguousarray(L2, dtype=np.uint16)
-    r, K = L1t.shape
-    N = L2.shape[1]
-    hi = np.zeros((r, K), np.uint16)
-    lo = np.zeros((r, K), np.uint16)
+    r, N = L2.shape
     L2t = np.zeros((N, r16(r)), np.uint16)
-    _check(lib().svdq_prepare_lowrank(K, N, r, _ptr(inv), _ptr(L1t), _ptr(L2), _ptr(hi), _ptr(lo), _ptr(L2t)))
-    return hi, lo, L2t
+    _check(lib().svdq_prepare_lowrank(N, r, _ptr(L2), _ptr(L2t)))
+    return L2t
 
 
 def pad4(n: int) -> int:
@@ -240,17 +234,15 @@ class PackedLinear:
         self.device = device
         self.inv_s = _upload(np.asarray(inv_s, np.float32), device)
         if rank > 0:
-            hi, lo, L2t = prepare_lowrank(inv_s, L1t, L2)
-            self.Ld_hi = _upload(hi, device)
-            self.Ld_lo = _upload(lo, device)
-            self.L2t = _upload(L2t, device)
+            self.L1t = _upload(np.ascontiguousarray(L1t, dtype=np.uint16), device)
+            self.L2t = _upload(prepare_lowrank(L2), device)
         else:
-            self.Ld_hi = self.Ld_lo = self.L2t = None
+            self.L1t = self.L2t = None
         qk, sk = prepare_weights(self.K, self.N, self.fmt, qW, sW)
         self.qW = _upload(qk, device)
         self.sW = _upload(sk, device)
-        self._c = _Layer(self.K, self.N, self.rank, self.fmt, _dptr(self.inv_s), _dptr(self.Ld_hi),
-                         _dptr(self.Ld_lo), _dptr(self.L2t), _dptr(self.qW), _dptr(self.sW))
+        self._c = _Layer(self.K, self.N, self.rank, self.fmt, _dptr(self.inv_s), _dptr(self.L1t),
+                         _dptr(self.L2t), _dptr(self.qW), _dptr(self.sW))
 
     @classmethod
     def from_host_pack(cls, p: HostPack, device="cuda:0"):

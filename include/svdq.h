@@ -79,22 +79,21 @@ typedef enum { SVDQ_ACT_PACKED = 0, SVDQ_ACT_MMA = 1 } svdq_act_form;
  * svdq_prepare_weights for the kernels' layouts).
  * R16 below is rank rounded up to a multiple of 16.
  *   inv_s  [K]        fp32  reciprocal smoothing factor, fp32(1 / fp32(s))
- *   Ld_hi  [rank][K]  bf16  high part of (diag(inv_s) L1)^T
- *   Ld_lo  [rank][K]  bf16  low part, so Ld_hi + Ld_lo = diag(inv_s) L1 to ~2^-17
+ *   L1t    [rank][K]  bf16  down projection transposed (L1^T), as svdq_pack_weights
+ *                           writes it
  *   L2t    [N][R16]   bf16  up projection transposed (L2^T), columns >= rank zero
  *   qW     [N][K/2]   u8    residual codes, row n = output channel n along K, in the
  *                           kernel bit order of svdq_prepare_weights
  *   sW                group-major scales as svdq_prepare_weights writes them: INT4 the
  *                           fp16 mantissa and E8M0 planes, MXFP4 E8M0 bytes, rows
  *                           padded to Np (16-byte aligned)
- * Ld_hi/Ld_lo/L2t may be NULL iff rank == 0. */
+ * L1t/L2t may be NULL iff rank == 0. */
 typedef struct svdq_layer {
   int64_t K, N;
   int32_t rank;
   int32_t fmt; /* svdq_format */
   const float* inv_s;
-  const uint16_t* Ld_hi;
-  const uint16_t* Ld_lo;
+  const uint16_t* L1t;
   const uint16_t* L2t;
   const uint8_t* qW;
   const void* sW;
@@ -152,15 +151,11 @@ svdq_status svdq_concat_lora(int64_t K, int64_t N, const float* s, int32_t rank,
                              const uint16_t* A, const uint16_t* B, float lora_scale,
                              uint16_t* L1t_out, uint16_t* L2_out);
 
-/* Offline device layouts of the low-rank branch.  The runtime smoothing is folded into
- * the down projection, (X diag(s)^-1) L1 = X (diag(inv_s) L1): for j < rank, k < K,
- *   v = inv_s[k] * L1t[j][k] (fp32), hi = bf16_rne(v), lo = bf16_rne(v - hi);
- * and the up projection is transposed and zero-padded: L2t[n][j] = L2[j][n] (j < rank),
- * 0 (rank <= j < R16).  Host pointers; outputs hi_out, lo_out [rank][K], L2t_out
- * [N][R16] bf16. */
-svdq_status svdq_prepare_lowrank(int64_t K, int64_t N, int32_t rank, const float* inv_s,
-                                 const uint16_t* L1t, const uint16_t* L2, uint16_t* hi_out,
-                                 uint16_t* lo_out, uint16_t* L2t_out);
+/* Offline device layout of the up projection (the down projection L1t is used as
+ * svdq_pack_weights writes it): transposed and zero-padded, L2t[n][j] = L2[j][n]
+ * (j < rank), 0 (rank <= j < R16).  Host pointers; L2 [rank][N], L2t_out [N][R16] bf16.
+ * EINVAL on bad sizes or NULL pointers (rank 0: nothing to write, pointers unused). */
+svdq_status svdq_prepare_lowrank(int64_t N, int32_t rank, const uint16_t* L2, uint16_t* L2t_out);
 
 /* Offline device layout of the residual weights (host pointers).  The values are those
  * of svdq_pack_weights / svdq_quantize_weights; only their encoding changes.  Np = N
