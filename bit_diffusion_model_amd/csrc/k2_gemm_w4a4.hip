@@ -23,14 +23,19 @@
 //    activations as bf16 hi/lo pairs, so the main loop converts only the weights.
 //
 // Tiling: a 256-thread block (4 waves) owns a 128 x 128 output tile; wave w owns rows
-// 64*(w/2) .. +63 and columns 64*(w%2) .. +63, i.e. 2 x 2 MFMA tiles of 32 x 32; two or
-// more blocks share a CU, so one block's barrier and staging overlap another's math.
-// K advances in stages of SUB 64-wide sub-steps (one INT4 group, two FP4 groups each):
-// per stage the block stages both operand panels through LDS (double buffered, rows
-// padded so that 8 consecutive rows of 16-byte accesses hit distinct banks), the codes
-// are expanded once per block there, and one barrier covers SUB sub-steps of MFMAs and
-// rescales.  The next stage's global loads are issued before the current stage's math,
-// through buffer resources whose range check returns zeros past the end of the matrix.
+// 64*(w/2) .. +63 and columns 64*(w%2) .. +63, i.e. 2 x 2 MFMA tiles of 32 x 32; two
+// blocks share a CU, so one block's barrier and staging overlap another's math.  K
+// advances in stages of SUB 64-wide sub-steps (one INT4 group, two FP4 groups each),
+// one barrier per stage.  Two kernels implement this:
+//  * k2_stream (MMA activation form, the forward's path): both operand panels and
+//    their scales go global -> LDS with LDS-destination buffer loads into three
+//    rotating buffers, loads for stage k+2 in flight while stage k is computed; the
+//    weight codes stay 4-bit in LDS and each wave expands its own fragments.
+//  * k2_gemm (packed activation form): loads into registers one stage ahead, converts
+//    the codes to FP8 on the way into double-buffered, row-padded LDS.
+// Buffer resources' range checks return zeros past the end of either matrix, so no
+// loop has bounds branches.  The tiles of a last, partly filled round of resident
+// blocks are split along K; their partial tiles are summed by k2_fixup.
 //
 // 32x32x64 operand layout (measured): lane l supplies row/column l & 31; for FP4 it
 // holds the 32 consecutive K values 32*(l>>5).. with the block scale of that half; for
@@ -94,10 +99,13 @@ struct K2Sched {
   uint32_t tiles_n;  // tiles along N
   uint32_t full;     // tiles computed whole
   uint32_t split;    // parts per remaining tile (1: none remain)
-  float* partials;   // [remaining * split][4 waves][TI][TJ][16][64] fp32
+  float* partials;   // [remaining * split][16 sub-tiles][16][64] fp32
 };
-constexpr int PART_FLOATS = 4 * TI * TJ * 16 * 64;  // one partial tile
-static_assert(TI == 2 && TJ == 2, "k2_fixup and the rescale schedule assume a 2 x 2 wave tile");
+// One partial tile: the 16 32 x 32 sub-tiles of the 128 x 128 tile, sub-tile (r, c) (row
+// block r, column block c) at index 4 r + c, each 16 x 64 floats in the MFMA's lane
+// layout (accumulator a of lane l at a * 64 + l).
+constexpr int PART_FLOATS = 16 * 16 * 64;
+static_assert(TI == 2 && TJ == 2, "the rescale schedules assume a 2 x 2 wave tile");
 
 // One stage's global loads of one thread: INT4 activation codes as FP8 bytes take two
 // 16-byte pieces per sub-step, 4-bit codes one.
@@ -412,14 +420,15 @@ __global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
       for (int j = 0; j < TJ; ++j) store_sub(acc[i][j], Y, ldy, ydtype, m0, n0, rowsA, nlim, wm + i * 32, wn + j * 32, l32, kh);
   } else {
-    // partial tile, laid out per (wave, i, j): 16 x 64 floats, lane-contiguous
     float* P = sch.partials + (size_t)(blockIdx.x - sch.full) * PART_FLOATS;
 #pragma unroll
     for (int i = 0; i < TI; ++i)
 #pragma unroll
-      for (int j = 0; j < TJ; ++j)
+      for (int j = 0; j < TJ; ++j) {
+        const int st = ((wm >> 5) + i) * 4 + (wn >> 5) + j;
 #pragma unroll
-        for (int a = 0; a < 16; ++a) P[(((wave * TI + i) * TJ + j) * 16 + a) * 64 + lane] = acc[i][j][a];
+        for (int a = 0; a < 16; ++a) P[(st * 16 + a) * 64 + lane] = acc[i][j][a];
+      }
   }
 }
 
@@ -453,13 +462,21 @@ struct DLay {
   static_assert(BM * RA % 4096 == 0 && BN * RB % 4096 == 0, "whole 1 KB load chunks per wave");
 };
 
-// XOR swizzle of the 16-byte slot within a row of `slots` slots
+// XOR swizzle of the 16-byte slot within a row of `slots` slots.  An operand read
+// (ds_read_b128, one row per lane) is served 16 lanes, i.e. 16 consecutive rows, per
+// pass over the 64 banks (256 bytes): the rows of one pass that share their position
+// within 256 bytes must get different slots.  The functions also keep any 8
+// consecutive rows apart within 128 bytes.  (Measured: no bank conflicts; the plain
+// row & 7 / (row >> 1) & 3 patterns conflicted two ways.)
 __device__ __forceinline__ int swz(int row, int slots) {
-  return slots == 8 ? (row & 7) : (slots == 4 ? ((row >> 1) & 3) : ((row >> 2) & 1));
+  return slots == 8 ? ((row ^ (row >> 3)) & 7)
+                    : (slots == 4 ? (((row >> 1) ^ (row >> 2)) & 3) : (((row >> 2) ^ (row >> 3)) & 1));
 }
 
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t off) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, off, 0, 0, 0);
+// 16 bytes per lane global -> LDS; soff (wave-uniform) is added to the address: the
+// range check on voff alone still drops every row past the end of the panel
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
 }
 __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t off) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, off, 0, 0, 0);
@@ -515,23 +532,26 @@ __global__ __launch_bounds__(NTHREADS, WPE) __attribute__((amdgpu_waves_per_eu(W
   const __amdgpu_buffer_rsrc_t rSW = make_rsrc(sW, ng * Np * (FMT == 0 ? 3 : 1));
 
   // ---- loads of stage k into LDS buffer b (every wave issues D::NDW instructions) -------
+  // Per-lane source offsets within a stage are fixed (chunk n of 1 KB covers rows
+  // n * 1024 / R ..); the stage's offset along K goes in the scalar offset.
+  uint32_t voA[D::NA], voB[D::NBW];
+#pragma unroll
+  for (int q = 0; q < D::NA; ++q) {
+    const int pos = (wave + 4 * q) * 1024 + lane * 16;
+    const int row = pos / D::RA, ps = (pos % D::RA) / 16;
+    voA[q] = (uint32_t)row * Ka + (uint32_t)((ps ^ swz(row, D::RA / 16)) * 16);
+  }
+#pragma unroll
+  for (int q = 0; q < D::NBW; ++q) {
+    const int pos = (wave + 4 * q) * 1024 + lane * 16;
+    const int row = pos / D::RB, ps = (pos % D::RB) / 16;
+    voB[q] = (uint32_t)row * Kb + (uint32_t)((ps ^ swz(row, D::RB / 16)) * 16);
+  }
   auto issue = [&](int k, uint8_t* base) {
 #pragma unroll
-    for (int q = 0; q < D::NA; ++q) {  // A: chunk n covers rows n * 1024 / RA ..
-      const int n = wave + 4 * q;
-      const int pos = n * 1024 + lane * 16;
-      const int row = pos / D::RA, ps = (pos % D::RA) / 16;
-      const int ls = ps ^ swz(row, D::RA / 16);
-      dma16(rA, base + n * 1024, (uint32_t)row * Ka + (uint32_t)k * D::RA + ls * 16);
-    }
+    for (int q = 0; q < D::NA; ++q) dma16(rA, base + (wave + 4 * q) * 1024, voA[q], (uint32_t)k * D::RA);
 #pragma unroll
-    for (int q = 0; q < D::NBW; ++q) {
-      const int n = wave + 4 * q;
-      const int pos = n * 1024 + lane * 16;
-      const int row = pos / D::RB, ps = (pos % D::RB) / 16;
-      const int ls = ps ^ swz(row, D::RB / 16);
-      dma16(rB, base + D::B_OFF + n * 1024, (uint32_t)row * Kb + (uint32_t)k * D::RB + ls * 16);
-    }
+    for (int q = 0; q < D::NBW; ++q) dma16(rB, base + D::B_OFF + (wave + 4 * q) * 1024, voB[q], (uint32_t)k * D::RB);
     // scale loads: every wave issues one activation-side and one weight-side load; the
     // wave number picks the sub-step (w & 1) and, for INT4, the plane (m for waves 0-1,
     // E8M0 for waves 2-3), arithmetically (no branches, so the compiler keeps tracking
@@ -736,18 +756,17 @@ __global__ __launch_bounds__(NTHREADS, WPE) __attribute__((amdgpu_waves_per_eu(W
 #pragma unroll
       for (int j = 0; j < TJ; ++j)
 #pragma unroll
-        for (int a = 0; a < 16; ++a) P[(((wave * TI + i) * TJ + j) * 16 + a) * 64 + lane] = acc[i][j][a];
+        for (int a = 0; a < 16; ++a) P[((((wm >> 5) + i) * 4 + (wn >> 5) + j) * 16 + a) * 64 + lane] = acc[i][j][a];
   }
 }
 
 // Sum of the `split` partial tiles of one remaining tile, in part order (the result does
 // not depend on which part finished first), stored like a whole tile.  One 64-thread
-// block per 32 x 32 sub-tile: blockIdx.x = remaining tile * 16 + (wave, i, j).
+// block per 32 x 32 sub-tile: blockIdx.x = remaining tile * 16 + sub-tile index.
 __global__ __launch_bounds__(64) void k2_fixup(const float* __restrict__ partials, K2Sched sch, int64_t M,
                                                int64_t N, void* __restrict__ Y, int64_t ldy, int ydtype) {
   const int lane = threadIdx.x;
-  const uint32_t r = blockIdx.x >> 4, sub = blockIdx.x & 15;  // sub = (wave * TI + i) * TJ + j
-  const int w = (int)(sub >> 2), i = (int)((sub >> 1) & 1), j = (int)(sub & 1);
+  const uint32_t r = blockIdx.x >> 4, sub = blockIdx.x & 15;  // sub = 4 * row block + column block
   const uint32_t t = sch.full + r;
   const int64_t m0 = (int64_t)(t / sch.tiles_n) * BM, n0 = (int64_t)(t % sch.tiles_n) * BN;
   const float* P = partials + (size_t)r * sch.split * PART_FLOATS + (size_t)sub * 16 * 64 + lane;
@@ -760,7 +779,7 @@ __global__ __launch_bounds__(64) void k2_fixup(const float* __restrict__ partial
     for (int a = 0; a < 16; ++a) acc[a] += Q[a * 64];
   }
   const int64_t rowsA = M - m0 < BM ? M - m0 : BM;
-  store_sub(acc, Y, ldy, ydtype, m0, n0, rowsA, N, (w >> 1) * WM + i * 32, (w & 1) * WN + j * 32, lane & 31, lane >> 5);
+  store_sub(acc, Y, ldy, ydtype, m0, n0, rowsA, N, (int)(sub >> 2) * 32, (int)(sub & 3) * 32, lane & 31, lane >> 5);
 }
 
 }  // namespace
