@@ -71,10 +71,9 @@ static WsLayout ws_layout(const svdq_layer* L, int64_t M) {
   WsLayout w;
   w.qx = 0;
   w.sx = rup((size_t)M * (size_t)(f8 ? L->K : L->K / 2));
-  // MMA-form scales: rows padded to Mp = M rounded up to 4; INT4 as an fp16 plane and
-  // an E8M0 plane (3 bytes per group and row), MXFP4 E8M0 bytes
+  // MMA-form scales: rows padded to Mp = M rounded up to 4; INT4 fp32, MXFP4 E8M0 bytes
   const size_t Mp = ((size_t)M + 3) / 4 * 4;
-  w.la = w.sx + rup((size_t)(L->K / group_of(L->fmt)) * Mp * (f8 ? 3 : 1));
+  w.la = w.sx + rup((size_t)(L->K / group_of(L->fmt)) * Mp * (f8 ? 4 : 1));
   w.part = w.la + rup((size_t)M * (size_t)((L->rank + 15) / 16 * 16) * 4);
   KernelLayer kl{L->K, L->N, L->rank, L->fmt, nullptr, nullptr, nullptr, nullptr, nullptr};
   w.total = w.part + rup(plan_k2(kl, M, true).bytes);

@@ -41,16 +41,20 @@ __device__ __forceinline__ void nib8p_to_fp8(uint32_t d, uint32_t& lo, uint32_t&
   hi = __builtin_amdgcn_alignbit(d, d, 4) & 0x87878787u;
 }
 
-// An fp16 INT4 group scale s = m * 2^e (m in [1, 2)) as one word: bits 0-15 the fp16 m
-// (0 for s = 0), bits 16-23 the E8M0 byte of 2^(e + 9) (127 for s = 0).  2^-9 is the
-// value of FP8 code 1, so an MFMA with these block scales on both sides returns the
-// exact integer group sum times 2^(eX + eW).
-__device__ __forceinline__ uint32_t split_scale_word(uint32_t bits) {
-  const float f = (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
-  const uint32_t u = __float_as_uint(f);
+// An INT4 group scale s = m * 2^e (m in [1, 2)), given as fp32 bits (every fp16 value
+// is exact in fp32), as one word: bits 0-15 the fp16 m (0 for s = 0), bits 16-23 the
+// E8M0 byte of 2^(e + 9) (127 for s = 0).  2^-9 is the value of FP8 code 1, so an MFMA
+// with these block scales on both sides returns the exact integer group sum times
+// 2^(eX + eW).
+__device__ __forceinline__ uint32_t split_scale_f32(uint32_t u) {
+  const float f = __uint_as_float(u);
   const uint32_t m = f == 0.0f ? 0u : __builtin_bit_cast(uint16_t, (_Float16)__uint_as_float((u & 0x807FFFFFu) | (127u << 23)));
   const uint32_t eb = f == 0.0f ? 127u : ((u >> 23) & 0xFFu) + 9u;
   return m | (eb << 16);
+}
+// The same from fp16 bits.
+__device__ __forceinline__ uint32_t split_scale_word(uint32_t bits) {
+  return split_scale_f32(__float_as_uint((float)__builtin_bit_cast(_Float16, (uint16_t)bits)));
 }
 
 // Raw buffer resource over `bytes` bytes at p: loads beyond the range return zeros.

@@ -169,11 +169,9 @@ k1_quant_lora_down(const uint16_t* __restrict__ X, int64_t ldx, int64_t M, int64
           *reinterpret_cast<uint2*>(qX + row * (K >> 1) + (k0 >> 1)) = make_uint2(w0, w1);
         }
         if (sub == 0) {
-          if constexpr (MMA) {  // the split planes kernel 2 consumes: fp16 m, then E8M0 bytes
+          if constexpr (MMA) {  // the value as fp32, rows padded to 4
             const int64_t Mp = (M + 3) & ~int64_t(3);
-            const uint32_t w = split_scale_word(__builtin_bit_cast(uint16_t, sh));
-            reinterpret_cast<uint16_t*>(sXv)[(int64_t)c * Mp + row] = (uint16_t)(w & 0xFFFFu);
-            reinterpret_cast<uint8_t*>(sXv)[(K >> 6) * Mp * 2 + (int64_t)c * Mp + row] = (uint8_t)(w >> 16);
+            reinterpret_cast<float*>(sXv)[(int64_t)c * Mp + row] = sf;
           } else {
             reinterpret_cast<uint16_t*>(sXv)[(int64_t)c * M + row] = __builtin_bit_cast(uint16_t, sh);
           }

@@ -10,17 +10,17 @@
 //  * MXFP4: the E2M1 codes are the operands as stored and the E8M0 group scales are
 //    the hardware block scales; the MFMA accumulates the exact scaled products.
 //  * INT4: a sign-magnitude code q becomes the FP8 E4M3 byte (sign, exponent 0,
-//    mantissa |q|), whose value is q * 2^-9 (a subnormal; exact).  Each fp16 group
-//    scale s = m * 2^e (m in [1,2)) is split: 2^(e+9) goes to the MFMA's E8M0 block
-//    scale, so one MFMA yields the exact group sum times 2^(eX+eW) in fp32, and the
-//    epilogue adds it times the fp16 product mX*mW (v_pk_mul_f16 + v_fma_mix_f32).
-//    With per-group scales on both sides this per-element rescale is the VALU cost
-//    that bounds the INT4 path; moving the powers of two into the MFMA halves it.
-//    The weight scales arrive already split (one word: fp16 m, E8M0 byte), and the
-//    weight codes in a bit order that expands to FP8 with a mask and a rotate (both
-//    prepared once, offline).  In the fused forward path the activation side comes
-//    the same way from kernel 1: FP8 code bytes, split scales, and the low-rank
-//    activations as bf16 hi/lo pairs, so the main loop converts only the weights.
+//    mantissa |q|), whose value is q * 2^-9 (a subnormal; exact), so an MFMA with block
+//    scales 2^9 on both sides yields the exact integer group sum I in fp32.  The
+//    per-group rescale by s_X s_W is VALU work on every output and group, and it is
+//    what bounds the INT4 path.  The forward's kernel (k2_stream) applies fp32 scales:
+//    acc += (I * sW) * sX with v_mul_f32 and v_fmac_f32.  The packed-form kernel
+//    (k2_gemm) splits each scale s = m * 2^e (m in [1, 2)), puts 2^(e+9) into the
+//    MFMA's E8M0 block scales and adds the result times the fp16 product mX * mW
+//    (v_pk_mul_f16 + v_fma_mix_f32).  The weight codes come in a bit order that expands
+//    to FP8 with a mask and a rotate (prepared once, offline).  In the fused forward
+//    path the activation side comes from kernel 1 as FP8 code bytes, fp32 scales and
+//    bf16 hi/lo low-rank activations, so the main loop converts only the weights.
 //
 // Tiling: a 256-thread block (4 waves) owns a 128 x 128 output tile; wave w owns rows
 // 64*(w/2) .. +63 and columns 64*(w%2) .. +63, i.e. 2 x 2 MFMA tiles of 32 x 32; two
@@ -115,11 +115,10 @@ struct Stage {
   uint32_t s[SUB];
 };
 
-// MMA: the activation side arrives in kernel 1's operand form: INT4 codes as FP8 bytes
-// [M][K], each 8-element block in the order of the weights' expansion (even elements,
-// then odd ones), so the A panel is copied to LDS without conversion, and INT4 scales
-// as split words [K/64][M]; lora_act as bf16 rows [R16 hi][R16 lo] (both formats).
-template <int FMT, bool DEBUG, bool MMA, int SUB>
+// The packed activation form: 4-bit codes [M][K/2] (INT4 nibbles are expanded to FP8
+// on the way into LDS), scales [K/G][M] (INT4 fp16, split into mantissa and E8M0 block
+// scale here), lora_act fp32 [M][R16]; prepared weights (INT4 scales fp32).
+template <int FMT, bool DEBUG, int SUB>
 __global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void k2_gemm(
     const uint8_t* __restrict__ qX, const void* __restrict__ sXv, int64_t M,
     const uint8_t* __restrict__ qW, const void* __restrict__ sWv, int64_t N, int64_t K,
@@ -128,7 +127,6 @@ __global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 
     int64_t mbase, int64_t nbase, int64_t mlim, int64_t nlim, K2Sched sch, int32_t* __restrict__ dbg) {
   using S = Smem<FMT, SUB>;
   __shared__ S sm;
-  constexpr bool AF8 = MMA && FMT == 0;  // activation codes as FP8 bytes
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar
@@ -137,7 +135,7 @@ __global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 
   const int wm = (wave >> 1) * WM;
   const int wn = (wave & 1) * WN;
   const uint32_t Kb = (uint32_t)(K >> 1);      // bytes per 4-bit code row
-  const uint32_t Ka = AF8 ? (uint32_t)K : Kb;  // bytes per A row
+  const uint32_t Ka = Kb;                      // bytes per A row
   const int nstages = (int)(K >> 6) / SUB;     // the host picks SUB dividing K / 64
   // tile and stage range of this block; part < 0: the whole K
   uint32_t t = blockIdx.x;
@@ -159,24 +157,21 @@ __global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 
   const __amdgpu_buffer_rsrc_t rB = make_rsrc(qW + n0 * Kb, (uint32_t)rowsB * Kb);
   const int ng = FMT == 0 ? (int)(K >> 6) : (int)(K >> 5);  // scale groups along K
   // INT4 scale words are 4 bytes, except the public path's fp16 activation scales
-  const bool xs16 = FMT == 0 && !AF8 && wave < 2;
   // staging roles: thread t moves the pieces of row t & 127, half t >> 7, of the A and
   // the B panel, and one scale per sub-step: waves 0-1 of the X row t, waves 2-3 of the
   // W column t - 128.  The choice is wave-uniform, so it is made once, here.
   const bool xs = wave < 2;
-  // scale rows: the packed activation scales have stride M; the MMA-form activation
-  // scales and the prepared weight scales are padded to a multiple of 4, and INT4 ones
-  // are split into a plane of fp16 mantissas followed by a plane of E8M0 bytes
-  const uint32_t sstride = xs ? (uint32_t)(MMA ? (M + 3) & ~int64_t(3) : M) : (uint32_t)((N + 3) & ~int64_t(3));
-  const uint32_t sbytes = (uint32_t)ng * sstride * (FMT == 0 ? (xs16 ? 2 : 3) : 1);
-  const __amdgpu_buffer_rsrc_t rS = make_rsrc(xs ? sXv : sWv, DEBUG ? 0u : sbytes);
-  const uint32_t eplane = (uint32_t)ng * sstride * 2;  // INT4 E8M0 plane offset
+  // scale rows: the activation scales have stride M, the prepared weight scales are
+  // padded to a multiple of 4; INT4: activation fp16, weight fp32
+  const uint32_t sstride = xs ? (uint32_t)M : (uint32_t)((N + 3) & ~int64_t(3));
+  const uint32_t ssz = FMT == 0 ? (xs ? 2u : 4u) : 1u;
+  const __amdgpu_buffer_rsrc_t rS = make_rsrc(xs ? sXv : sWv, DEBUG ? 0u : (uint32_t)ng * sstride * ssz);
   const uint32_t sidx = xs ? (uint32_t)(m0 + tid) : (uint32_t)(n0 + tid - BM);
   const int ldrow = tid & 127, ldhalf = tid >> 7;
   // this thread's part of a stage row: 4-bit code bytes [SUB*16*half, +SUB*16) (INT4
   // FP8 activation bytes [SUB*32*half, +SUB*32)); in LDS, INT4 stores every code as a byte
   const uint32_t offB = (uint32_t)ldrow * Kb + ldhalf * SUB * 16;
-  const uint32_t offA = (uint32_t)ldrow * Ka + ldhalf * SUB * (AF8 ? 32 : 16);
+  const uint32_t offA = (uint32_t)ldrow * Ka + ldhalf * SUB * 16;
   const int ldsAB = ldrow * S::kPitch + ldhalf * SUB * (FMT == 0 ? 32 : 16);
 
   // Loads for stages past the end are harmless: they read zeros (range check) or codes
@@ -185,12 +180,7 @@ __global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 
     const uint32_t kb = (uint32_t)k * SUB * 32;  // 4-bit code bytes before stage k
 #pragma unroll
     for (int v = 0; v < SUB; ++v) {
-      if (AF8) {
-        st.a[2 * v] = buf_load16(rA, offA + 2 * kb + v * 32);
-        st.a[2 * v + 1] = buf_load16(rA, offA + 2 * kb + v * 32 + 16);
-      } else {
-        st.a[v] = buf_load16(rA, offA + kb + v * 16);
-      }
+      st.a[v] = buf_load16(rA, offA + kb + v * 16);
       st.b[v] = buf_load16(rB, offB + kb + v * 16);
     }
 #pragma unroll
@@ -199,8 +189,7 @@ __global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 
       if (DEBUG) {
         st.s[u] = 0;
       } else if (FMT == 0) {
-        if (xs16) st.s[u] = buf_load2(rS, (g * sstride + sidx) * 2);
-        else st.s[u] = buf_load2(rS, (g * sstride + sidx) * 2) | (buf_load1(rS, eplane + g * sstride + sidx) << 16);
+        st.s[u] = xs ? buf_load2(rS, (g * sstride + sidx) * 2) : buf_load4(rS, (g * sstride + sidx) * 4);
       } else {
         const uint32_t o0 = 2 * g * sstride + sidx;
         st.s[u] = buf_load1(rS, o0) | (buf_load1(rS, o0 + sstride) << 8);
@@ -218,18 +207,13 @@ __global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 
         const uint32_t bw[4] = {st.b[v].x, st.b[v].y, st.b[v].z, st.b[v].w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          if (!AF8) nib8_to_fp8(aw[i], a8[2 * i], a8[2 * i + 1]);
+          nib8_to_fp8(aw[i], a8[2 * i], a8[2 * i + 1]);
           nib8p_to_fp8(bw[i], b8[2 * i], b8[2 * i + 1]);
         }
         uint4* da = reinterpret_cast<uint4*>(A + v * 32);
         uint4* db = reinterpret_cast<uint4*>(B + v * 32);
-        if (AF8) {
-          da[0] = st.a[2 * v];
-          da[1] = st.a[2 * v + 1];
-        } else {
-          da[0] = make_uint4(a8[0], a8[1], a8[2], a8[3]);
-          da[1] = make_uint4(a8[4], a8[5], a8[6], a8[7]);
-        }
+        da[0] = make_uint4(a8[0], a8[1], a8[2], a8[3]);
+        da[1] = make_uint4(a8[4], a8[5], a8[6], a8[7]);
         db[0] = make_uint4(b8[0], b8[1], b8[2], b8[3]);
         db[1] = make_uint4(b8[4], b8[5], b8[6], b8[7]);
       } else {
@@ -242,7 +226,7 @@ __global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 
       if (FMT == 0) {
         uint32_t w;
         if (DEBUG) w = 0x3C00u | ((127u + 9u) << 16);  // m = 1, 2^9
-        else w = xs16 ? split_scale_word(st.s[u]) : st.s[u];
+        else w = xs ? split_scale_word(st.s[u]) : split_scale_f32(st.s[u]);
         sm.st[buf].m[u][tid] = __builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
         sm.st[buf].e[u][tid] = w >> 16;
       } else {
@@ -384,26 +368,19 @@ __global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 
         bl[j] = __builtin_bit_cast(v8bf, buf_load16(rU, (uint32_t)((wn + j * 32 + l32) * R16 + k0 + 8 * kh) * 2));
 #pragma unroll
       for (int i = 0; i < TI; ++i) {
-        v8bf ah, al;
-        if (MMA) {  // bf16 rows [R16 hi][R16 lo]
-          const uint32_t o = (uint32_t)((wm + i * 32 + l32) * 2 * R16 + k0 + 8 * kh) * 2;
-          ah = __builtin_bit_cast(v8bf, buf_load16(rL, o));
-          al = __builtin_bit_cast(v8bf, buf_load16(rL, o + R16 * 2));
-        } else {
-          const uint32_t o = (uint32_t)((wm + i * 32 + l32) * R16 + k0 + 8 * kh) * 4;
-          const uint4 v0 = buf_load16(rL, o), v1 = buf_load16(rL, o + 16);
-          const float v[8] = {__uint_as_float(v0.x), __uint_as_float(v0.y), __uint_as_float(v0.z), __uint_as_float(v0.w),
-                              __uint_as_float(v1.x), __uint_as_float(v1.y), __uint_as_float(v1.z), __uint_as_float(v1.w)};
-          uint16_t hi[8], lo[8];
+        const uint32_t o = (uint32_t)((wm + i * 32 + l32) * R16 + k0 + 8 * kh) * 4;
+        const uint4 v0 = buf_load16(rL, o), v1 = buf_load16(rL, o + 16);
+        const float v[8] = {__uint_as_float(v0.x), __uint_as_float(v0.y), __uint_as_float(v0.z), __uint_as_float(v0.w),
+                            __uint_as_float(v1.x), __uint_as_float(v1.y), __uint_as_float(v1.z), __uint_as_float(v1.w)};
+        uint16_t hi[8], lo[8];
 #pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            const uint32_t hb = f32_to_bf16_rne(v[u]);
-            hi[u] = (uint16_t)hb;
-            lo[u] = (uint16_t)f32_to_bf16_rne(v[u] - __uint_as_float(hb << 16));
-          }
-          ah = __builtin_bit_cast(v8bf, hi);
-          al = __builtin_bit_cast(v8bf, lo);
+        for (int u = 0; u < 8; ++u) {
+          const uint32_t hb = f32_to_bf16_rne(v[u]);
+          hi[u] = (uint16_t)hb;
+          lo[u] = (uint16_t)f32_to_bf16_rne(v[u] - __uint_as_float(hb << 16));
         }
+        const v8bf ah = __builtin_bit_cast(v8bf, hi);
+        const v8bf al = __builtin_bit_cast(v8bf, lo);
 #pragma unroll
         for (int j = 0; j < TJ; ++j) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl[j], acc[i][j], 0, 0, 0);
@@ -435,25 +412,29 @@ __global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 
 // ---------------------------------------------------------------------------------------
 // Kernel 2, streamed (MMA activation form): codes and scales go from global memory
 // straight into LDS with buffer loads that write LDS (each lane's 16 or 4 bytes land at
-// the instruction's LDS base + lane * size), so no register staging, no LDS store
-// instructions and no wait for a stage's data until it is needed.  NB = 3 LDS buffers:
-// the loads of stage k+2 are issued while stage k is computed; NB = 2: stage k+1's (less
-// LDS, for more blocks per CU).  One barrier per stage.
+// the instruction's LDS base + lane * size): no register staging and no LDS store
+// instructions.  Three LDS buffers rotate; a stage is two 64-wide sub-steps (K is a
+// multiple of 128), and the loads of stage k+2 are in flight while stage k is computed,
+// with one barrier per stage.
 // 16-byte slots of each operand row are XOR-swizzled with the row (rows are not padded:
-// a load instruction fills 1 KB contiguously), so that the 8 rows an MFMA operand read
-// takes at once fall on 8 different bank groups.  The weight codes stay 4-bit in LDS and
+// a load instruction fills 1 KB contiguously).  The weight codes stay 4-bit in LDS and
 // are expanded to FP8 after the read, per wave.
+// INT4 rescale: both MFMA block scales are 2^9, so the MFMA returns the exact integer
+// group sum I; the epilogue adds (I * sW) * sX with fp32 v_mul / v_fmac, which run at
+// twice the rate of the packed-fp16 and mixed-precision forms on gfx950 and issue
+// alongside the MFMA (measured; v_pk_mul_f16 does not overlap a running MFMA).
 
-template <int FMT, int SUB>
+// LDS layout of one stage
+template <int FMT>
 struct DLay {
-  static constexpr int RA = SUB * (FMT == 0 ? 64 : 32);  // A bytes per row and stage
-  static constexpr int RB = SUB * 32;                     // B (4-bit) bytes per row and stage
+  static constexpr int RA = 2 * (FMT == 0 ? 64 : 32);  // A bytes per row
+  static constexpr int RB = 2 * 32;                     // B (4-bit) bytes per row
   static constexpr int B_OFF = BM * RA;
   static constexpr int S_OFF = B_OFF + BN * RB;
-  // scales of one sub-step: INT4 X m [BM] fp16 | W m [BN] fp16 | X e (256 B) | W e (256 B);
-  // MXFP4 X e [2][BM] | W e [2][BN] (the sub-step's two 32-groups)
-  static constexpr int S_SUB = FMT == 0 ? 2 * BM + 2 * BN + 512 : 2 * BM + 2 * BN;
-  static constexpr int BUF = S_OFF + SUB * S_SUB;
+  // scales of one sub-step: INT4 X [BM] fp32 | W [BN] fp32; MXFP4 X e [2][BM] | W e [2][BN]
+  // (the sub-step's two 32-groups)
+  static constexpr int S_SUB = FMT == 0 ? 4 * BM + 4 * BN : 2 * BM + 2 * BN;
+  static constexpr int BUF = S_OFF + 2 * S_SUB;
   // load instructions per wave and stage
   static constexpr int NA = BM * RA / 1024 / 4;
   static constexpr int NBW = BN * RB / 1024 / 4;
@@ -469,8 +450,7 @@ struct DLay {
 // consecutive rows apart within 128 bytes.  (Measured: no bank conflicts; the plain
 // row & 7 / (row >> 1) & 3 patterns conflicted two ways.)
 __device__ __forceinline__ int swz(int row, int slots) {
-  return slots == 8 ? ((row ^ (row >> 3)) & 7)
-                    : (slots == 4 ? (((row >> 1) ^ (row >> 2)) & 3) : (((row >> 2) ^ (row >> 3)) & 1));
+  return slots == 8 ? ((row ^ (row >> 3)) & 7) : (((row >> 1) ^ (row >> 2)) & 3);
 }
 
 // 16 bytes per lane global -> LDS; soff (wave-uniform) is added to the address: the
@@ -482,25 +462,25 @@ __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uin
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, off, 0, 0, 0);
 }
 
-template <int N>
-__device__ __forceinline__ void wait_vm() {  // s_waitcnt vmcnt(N), other counters untouched
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+// s_waitcnt vmcnt(N) and lgkmcnt(L) (expcnt untouched; L = 15: untouched)
+template <int N, int L = 15>
+__device__ __forceinline__ void wait_cnt() {
+  static_assert(N >= 0 && N < 64 && L >= 0 && L < 16, "counter range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (L << 8));
 }
 
-template <int FMT, int SUB, int NB, int WPE>
-__global__ __launch_bounds__(NTHREADS, WPE) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void k2_stream(
+template <int FMT>
+__global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void k2_stream(
     const uint8_t* __restrict__ qX, const uint8_t* __restrict__ sX, int64_t M,
     const uint8_t* __restrict__ qW, const uint8_t* __restrict__ sW, int64_t N, int64_t K,
     const uint16_t* __restrict__ lora_act, const uint16_t* __restrict__ L2, int rank,
     void* __restrict__ Y, int64_t ldy, int ydtype, K2Sched sch) {
-  using D = DLay<FMT, SUB>;
-  // separate arrays, always addressed statically (the main loop is unrolled by NB), so
+  using D = DLay<FMT>;
+  // separate arrays, always addressed statically (the main loop is unrolled by 3), so
   // the compiler can tell a buffer's pending loads from reads of another
-  static_assert(NB == 2 || NB == 3, "two or three LDS buffers");
   __shared__ __attribute__((aligned(1024))) uint8_t lds0[D::BUF];
   __shared__ __attribute__((aligned(1024))) uint8_t lds1[D::BUF];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds2[NB == 3 ? D::BUF : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds2[D::BUF];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -510,7 +490,7 @@ __global__ __launch_bounds__(NTHREADS, WPE) __attribute__((amdgpu_waves_per_eu(W
   const int wn = (wave & 1) * WN;
   const uint32_t Kb = (uint32_t)(K >> 1);                  // 4-bit code bytes per row
   const uint32_t Ka = FMT == 0 ? (uint32_t)K : Kb;         // A bytes per row
-  const int nstages = (int)(K >> 6) / SUB;
+  const int nstages = (int)(K >> 7);
   uint32_t t = blockIdx.x;
   int part = -1, kbeg = 0, kend = nstages;
   if (t >= sch.full) {
@@ -528,10 +508,10 @@ __global__ __launch_bounds__(NTHREADS, WPE) __attribute__((amdgpu_waves_per_eu(W
   const __amdgpu_buffer_rsrc_t rB = make_rsrc(qW + n0 * Kb, (uint32_t)rowsB * Kb);
   const uint32_t ng = FMT == 0 ? (uint32_t)(K >> 6) : (uint32_t)(K >> 5);
   const uint32_t Mp = (uint32_t)((M + 3) & ~int64_t(3)), Np = (uint32_t)((N + 3) & ~int64_t(3));
-  const __amdgpu_buffer_rsrc_t rSX = make_rsrc(sX, ng * Mp * (FMT == 0 ? 3 : 1));
-  const __amdgpu_buffer_rsrc_t rSW = make_rsrc(sW, ng * Np * (FMT == 0 ? 3 : 1));
+  const __amdgpu_buffer_rsrc_t rSX = make_rsrc(sX, ng * Mp * (FMT == 0 ? 4 : 1));
+  const __amdgpu_buffer_rsrc_t rSW = make_rsrc(sW, ng * Np * (FMT == 0 ? 4 : 1));
 
-  // ---- loads of stage k into LDS buffer b (every wave issues D::NDW instructions) -------
+  // ---- loads of stage k into an LDS buffer (every wave issues D::NDW instructions) ------
   // Per-lane source offsets within a stage are fixed (chunk n of 1 KB covers rows
   // n * 1024 / R ..); the stage's offset along K goes in the scalar offset.
   uint32_t voA[D::NA], voB[D::NBW];
@@ -553,21 +533,19 @@ __global__ __launch_bounds__(NTHREADS, WPE) __attribute__((amdgpu_waves_per_eu(W
 #pragma unroll
     for (int q = 0; q < D::NBW; ++q) dma16(rB, base + D::B_OFF + (wave + 4 * q) * 1024, voB[q], (uint32_t)k * D::RB);
     // scale loads: every wave issues one activation-side and one weight-side load; the
-    // wave number picks the sub-step (w & 1) and, for INT4, the plane (m for waves 0-1,
-    // E8M0 for waves 2-3), arithmetically (no branches, so the compiler keeps tracking
-    // which buffer has loads pending).  Sub-steps past SUB repeat the last (same data).
+    // wave number picks the sub-step (w & 1) and, for INT4, the half of the 128 rows or
+    // columns (w >> 1), arithmetically (no branches, so the compiler keeps tracking which
+    // buffer has loads pending)
     {
-      const int u = SUB == 1 ? 0 : (wave & 1);
+      const int u = wave & 1;
       uint8_t* sb = base + D::S_OFF + u * D::S_SUB;
       if (FMT == 0) {
-        const uint32_t g = (uint32_t)(k * SUB + u);
-        const uint32_t ep = (uint32_t)wave >> 1;  // 0: m planes, 1: E8M0 planes
-        const uint32_t mx_ = (g * Mp + (uint32_t)m0) * 2, ex_ = ng * Mp * 2 + g * Mp + (uint32_t)m0;
-        const uint32_t mw_ = (g * Np + (uint32_t)n0) * 2, ew_ = ng * Np * 2 + g * Np + (uint32_t)n0;
-        dma4(rSX, sb + ep * (2 * BM + 2 * BN), mx_ + ep * (ex_ - mx_) + lane * 4);
-        dma4(rSW, sb + 2 * BM + ep * (2 * BN + 256), mw_ + ep * (ew_ - mw_) + lane * 4);
+        const uint32_t g = (uint32_t)(k * 2 + u);
+        const uint32_t h = (uint32_t)wave >> 1;
+        dma4(rSX, sb + h * 256, (g * Mp + (uint32_t)m0 + 64 * h) * 4 + lane * 4);
+        dma4(rSW, sb + 4 * BM + h * 256, (g * Np + (uint32_t)n0 + 64 * h) * 4 + lane * 4);
       } else {  // lanes 0-31 group 2g, lanes 32-63 group 2g+1
-        const uint32_t g2 = 2 * (uint32_t)(k * SUB + u) + (uint32_t)kh;
+        const uint32_t g2 = 2 * (uint32_t)(k * 2 + u) + (uint32_t)kh;
         dma4(rSX, sb, g2 * Mp + (uint32_t)m0 + l32 * 4);
         dma4(rSW, sb + 2 * BM, g2 * Np + (uint32_t)n0 + l32 * 4);
       }
@@ -580,142 +558,139 @@ __global__ __launch_bounds__(NTHREADS, WPE) __attribute__((amdgpu_waves_per_eu(W
 #pragma unroll
     for (int j = 0; j < TJ; ++j) acc[i][j] = v16f{};
 
-  // ---- one 64-wide sub-step u of the stage in LDS buffer b ------------------------------
-  auto compute = [&](const uint8_t* base, int u) {
+  // ---- the fragments of one sub-step u of a stage, read from LDS --------------------------
+  struct Frag {
+    uint4 a[TI][FMT == 0 ? 2 : 1];  // A: INT4 32 FP8 bytes, MXFP4 32 nibbles
+    uint4 b[TJ];                    // B: 32 4-bit codes
+    uint32_t sa[TI], sb[TJ];        // MXFP4: E8M0 block scales
+    float sw[TJ];                   // INT4: the weight scale of the lane's column
+  };
+  typedef float4 XS[TI][4];  // INT4: the activation scales of the lane's 16 rows of tile i
+  auto load = [&](const uint8_t* base, int u, Frag& f) {
     const uint8_t* sb = base + D::S_OFF + u * D::S_SUB;
-    v8i af[TI], bf[TJ];
-    uint32_t sa[TI], sbv[TJ];
 #pragma unroll
     for (int j = 0; j < TJ; ++j) {
       const int col = wn + j * 32 + l32;
       const int ls = u * 2 + kh;  // 4-bit bytes u*32 + kh*16
-      const uint4 x = *reinterpret_cast<const uint4*>(base + D::B_OFF + col * D::RB + ((ls ^ swz(col, D::RB / 16)) * 16));
-      if (FMT == 0) {
-        uint32_t w8[8];
-        const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) nib8p_to_fp8(xw[e], w8[2 * e], w8[2 * e + 1]);
-        bf[j] = v8i{(int)w8[0], (int)w8[1], (int)w8[2], (int)w8[3], (int)w8[4], (int)w8[5], (int)w8[6], (int)w8[7]};
-        sbv[j] = sb[2 * BM + 2 * BN + 256 + col];
+      f.b[j] = *reinterpret_cast<const uint4*>(base + D::B_OFF + col * D::RB + ((ls ^ swz(col, D::RB / 16)) * 16));
+      if constexpr (FMT == 0) {
+        f.sw[j] = reinterpret_cast<const float*>(sb + 4 * BM)[col];
       } else {
-        bf[j] = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
-        sbv[j] = sb[2 * BM + kh * BN + col];
+        f.sb[j] = sb[2 * BM + kh * BN + col];
       }
     }
 #pragma unroll
     for (int i = 0; i < TI; ++i) {
       const int row = wm + i * 32 + l32;
-      if (FMT == 0) {
+      if constexpr (FMT == 0) {
         const int ls0 = u * 4 + kh * 2;  // FP8 bytes u*64 + kh*32, two slots
         const int sw = swz(row, D::RA / 16);
-        const uint4 x0 = *reinterpret_cast<const uint4*>(base + row * D::RA + ((ls0 ^ sw) * 16));
-        const uint4 x1 = *reinterpret_cast<const uint4*>(base + row * D::RA + (((ls0 + 1) ^ sw) * 16));
-        af[i] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-        sa[i] = sb[2 * BM + 2 * BN + row];
+        f.a[i][0] = *reinterpret_cast<const uint4*>(base + row * D::RA + ((ls0 ^ sw) * 16));
+        f.a[i][1] = *reinterpret_cast<const uint4*>(base + row * D::RA + (((ls0 + 1) ^ sw) * 16));
       } else {
         const int ls = u * 2 + kh;
-        const uint4 x = *reinterpret_cast<const uint4*>(base + row * D::RA + ((ls ^ swz(row, D::RA / 16)) * 16));
-        af[i] = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
-        sa[i] = sb[kh * BM + row];
+        f.a[i][0] = *reinterpret_cast<const uint4*>(base + row * D::RA + ((ls ^ swz(row, D::RA / 16)) * 16));
+        f.sa[i] = sb[kh * BM + row];
       }
-    }
-    if (FMT == 0) {
-      const _Float16* xm = reinterpret_cast<const _Float16*>(sb);
-      const _Float16* wmn = reinterpret_cast<const _Float16*>(sb + 2 * BM);
-      h2 mw[TJ];
-#pragma unroll
-      for (int j = 0; j < TJ; ++j) {
-        const _Float16 m = wmn[wn + j * 32 + l32];
-        mw[j] = h2{m, m};
-      }
-      h2 mx[TI][8];
-#pragma unroll
-      for (int i = 0; i < TI; ++i)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint2 w = *reinterpret_cast<const uint2*>(&xm[wm + i * 32 + 8 * q + 4 * kh]);
-          mx[i][2 * q] = __builtin_bit_cast(h2, w.x);
-          mx[i][2 * q + 1] = __builtin_bit_cast(h2, w.y);
-        }
-      auto gs = [&](int i, int j) {
-        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], v16f{}, 0, 0, 0, (int)sa[i], 0,
-                                                               (int)sbv[j]);
-      };
-      auto epi = [&](int i, int j, const v16f& p) {
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const h2 sc = mx[i][q] * mw[j];
-          acc[i][j][2 * q] = fmaf(p[2 * q], (float)sc.x, acc[i][j][2 * q]);
-          acc[i][j][2 * q + 1] = fmaf(p[2 * q + 1], (float)sc.y, acc[i][j][2 * q + 1]);
-        }
-      };
-      // two group-sum MFMAs in flight: tile t+1's MFMA is issued ahead of tile t's rescale
-      v16f p0 = gs(0, 0);
-      v16f p1 = gs(0, 1);
-      epi(0, 0, p0);
-      p0 = gs(1, 0);
-      epi(0, 1, p1);
-      p1 = gs(1, 1);
-      epi(1, 0, p0);
-      epi(1, 1, p1);
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 24, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 24, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 48, 0);
-    } else {
-#pragma unroll
-      for (int i = 0; i < TI; ++i)
-#pragma unroll
-        for (int j = 0; j < TJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], 4, 4, 0, (int)sa[i], 0,
-                                                                     (int)sbv[j]);
     }
   };
 
+  // rows 8 q + 4 kh .. +3 of tile i: accumulator a of the lane is row 8 (a >> 2) + 4 kh + (a & 3)
+  auto load_xs = [&](const uint8_t* base, int u, XS& xs) {
+    const float* sx = reinterpret_cast<const float*>(base + D::S_OFF + u * D::S_SUB);
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) xs[i][q] = *reinterpret_cast<const float4*>(&sx[wm + i * 32 + 8 * q + 4 * kh]);
+  };
+
+  // ---- INT4: weight expansion, group-sum MFMA, rescale ----------------------------------
+  auto expand = [&](const Frag& f, v8i (&bf)[TJ]) {
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      uint32_t w8[8];
+      const uint32_t xw[4] = {f.b[j].x, f.b[j].y, f.b[j].z, f.b[j].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) nib8p_to_fp8(xw[e], w8[2 * e], w8[2 * e + 1]);
+      bf[j] = v8i{(int)w8[0], (int)w8[1], (int)w8[2], (int)w8[3], (int)w8[4], (int)w8[5], (int)w8[6], (int)w8[7]};
+    }
+  };
+  // both block scales 2^9 (E8M0 byte 136): FP8 code q is q * 2^-9, so the MFMA returns
+  // the exact integer group sum
+  auto gs = [&](const Frag& f, const v8i (&bf)[TJ], int i, int j) {
+    const uint4 x0 = f.a[i][0], x1 = f.a[i][FMT == 0 ? 1 : 0];
+    const v8i af = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf[j], v16f{}, 0, 0, 0, 136, 0, 136);
+  };
+  // acc += (I * sW) * sX: I * sW is exact (12 + 11 significant bits), one rounding per
+  // group in the fma
+  auto epi = [&](const Frag& f, const XS& xs, int i, int j, const v16f& p) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      acc[i][j][4 * q] = fmaf(p[4 * q] * f.sw[j], xs[i][q].x, acc[i][j][4 * q]);
+      acc[i][j][4 * q + 1] = fmaf(p[4 * q + 1] * f.sw[j], xs[i][q].y, acc[i][j][4 * q + 1]);
+      acc[i][j][4 * q + 2] = fmaf(p[4 * q + 2] * f.sw[j], xs[i][q].z, acc[i][j][4 * q + 2]);
+      acc[i][j][4 * q + 3] = fmaf(p[4 * q + 3] * f.sw[j], xs[i][q].w, acc[i][j][4 * q + 3]);
+    }
+  };
+  // ---- MXFP4: the MFMA accumulates the block-scaled products directly ---------------------
+  auto mma4 = [&](const Frag& f) {
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const v8i af = {(int)f.a[i][0].x, (int)f.a[i][0].y, (int)f.a[i][0].z, (int)f.a[i][0].w, 0, 0, 0, 0};
+        const v8i bf = {(int)f.b[j].x, (int)f.b[j].y, (int)f.b[j].z, (int)f.b[j].w, 0, 0, 0, 0};
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf, acc[i][j], 4, 4, 0, (int)f.sa[i], 0,
+                                                                   (int)f.sb[j]);
+      }
+  };
+
   // ---- main loop ------------------------------------------------------------------------
-  // Stage k's loads were issued NB-1 stages earlier into buffer (k - kbeg) % NB.  A wave
-  // waits for its own loads of stage k (with NB = 3 the loads of stage k+1 may stay in
-  // flight), the barrier makes every wave's loads visible and frees the buffer read
-  // during stage k-1, which then receives stage k+NB-1.  Every step issues a stage's
-  // loads: past the end, the last stage again (harmless, never read), so the count in
-  // flight is the same at every wait and the loop body has no branches.
+  // Stage k lives in buffer (k - kbeg) % 3.  Each wave waits for its own loads of stage k
+  // (those of stage k+1 stay in flight) and for its own LDS reads of stage k-1; the
+  // barrier then publishes stage k and frees stage k-1's buffer, which receives stage
+  // k+2.  Every stage issues one stage's loads: past the end the last stage again
+  // (harmless, never read), so the count in flight is the same at every wait and the
+  // loop body has no branches.
+  auto stage = [&](int kk, const uint8_t* cur, uint8_t* dst) {
+    wait_cnt<D::NDW, 0>();
+    __builtin_amdgcn_s_barrier();
+    issue(kk + 2 < kend ? kk + 2 : kend - 1, dst);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      Frag F;
+      load(cur, u, F);
+      if constexpr (FMT == 0) {
+        v8i bf[TJ];
+        XS mx;
+        load_xs(cur, u, mx);
+        expand(F, bf);
+        v16f p0 = gs(F, bf, 0, 0);
+        v16f p1 = gs(F, bf, 0, 1);
+        epi(F, mx, 0, 0, p0);
+        p0 = gs(F, bf, 1, 0);
+        epi(F, mx, 0, 1, p1);
+        p1 = gs(F, bf, 1, 1);
+        epi(F, mx, 1, 0, p0);
+        epi(F, mx, 1, 1, p1);
+      } else {
+        mma4(F);
+      }
+    }
+  };
   const int nk = kend - kbeg;
   int k = kbeg;
-  if constexpr (NB == 3) {
-    auto kstep = [&](int kk, const uint8_t* cur, uint8_t* nxt) {
-      wait_vm<D::NDW>();
-      __builtin_amdgcn_s_barrier();
-      issue(kk + 2 < kend ? kk + 2 : kend - 1, nxt);
-#pragma unroll
-      for (int u = 0; u < SUB; ++u) compute(cur, u);
-    };
-    issue(kbeg, lds0);
-    issue(kbeg + 1 < kend ? kbeg + 1 : kend - 1, lds1);
-    for (; k + 3 <= kend; k += 3) {
-      kstep(k, lds0, lds2);
-      kstep(k + 1, lds1, lds0);
-      kstep(k + 2, lds2, lds1);
-    }
-    if (nk % 3 >= 1) kstep(k, lds0, lds2);
-    if (nk % 3 == 2) kstep(k + 1, lds1, lds0);
-  } else {
-    auto kstep = [&](int kk, const uint8_t* cur, uint8_t* nxt) {
-      wait_vm<0>();
-      __builtin_amdgcn_s_barrier();
-      issue(kk + 1 < kend ? kk + 1 : kend - 1, nxt);
-#pragma unroll
-      for (int u = 0; u < SUB; ++u) compute(cur, u);
-    };
-    issue(kbeg, lds0);
-    for (; k + 2 <= kend; k += 2) {
-      kstep(k, lds0, lds1);
-      kstep(k + 1, lds1, lds0);
-    }
-    if (nk % 2) kstep(k, lds0, lds1);
+  issue(kbeg, lds0);
+  issue(kbeg + 1 < kend ? kbeg + 1 : kend - 1, lds1);
+  for (; k + 3 <= kend; k += 3) {
+    stage(k, lds0, lds2);
+    stage(k + 1, lds1, lds0);
+    stage(k + 2, lds2, lds1);
   }
-  wait_vm<0>();
+  if (nk % 3 >= 1) stage(k, lds0, lds2);
+  if (nk % 3 == 2) stage(k + 1, lds1, lds0);
+  wait_cnt<0, 0>();
 
   // ---- low-rank up projection: acc += lora_act[rows, :] L2[:, cols] ----------------------
   // v_mfma_f32_32x32x16_bf16 on lora_act's bf16 hi/lo rows ([M][R16 hi | R16 lo]) and L2t
@@ -787,21 +762,21 @@ __global__ __launch_bounds__(64) void k2_fixup(const float* __restrict__ partial
 // Sub-steps per stage: the largest of 2, 1 that divides K / 64.
 static int sub_of(int64_t K) { return (K >> 6) % 2 == 0 ? 2 : 1; }
 
-template <int FMT, bool MMA, int SUB>
+template <int FMT, int SUB>
 static void launch_k2_t(const KernelLayer& L, int64_t M, const uint8_t* qX, const void* sX,
                         const void* lora_act, void* Y, int64_t ldy, int ydtype, const K2Sched& sch,
                         uint32_t nblocks, hipStream_t st) {
-  hipLaunchKernelGGL((k2_gemm<FMT, false, MMA, SUB>), dim3(nblocks), dim3(NTHREADS), 0, st, qX, sX, M, L.qW,
+  hipLaunchKernelGGL((k2_gemm<FMT, false, SUB>), dim3(nblocks), dim3(NTHREADS), 0, st, qX, sX, M, L.qW,
                      L.sW, L.N, L.K, lora_act, L.L2t, L.rank, Y, ldy, ydtype, (int64_t)0, (int64_t)0, M, L.N, sch,
                      (int32_t*)nullptr);
 }
 
-template <int FMT, bool MMA, int SUB>
+template <int FMT, int SUB>
 static int blocks_per_cu() {
   static int n = 0;  // per kernel instance; the same on every MI355X device
   if (n == 0) {
     int v = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, k2_gemm<FMT, false, MMA, SUB>, NTHREADS, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, k2_gemm<FMT, false, SUB>, NTHREADS, 0) != hipSuccess ||
         v < 1)
       v = 1;
     n = v;
@@ -809,33 +784,21 @@ static int blocks_per_cu() {
   return n;
 }
 
-// Streamed-kernel configuration per format: LDS buffers and waves per SIMD.
 template <int FMT>
-struct SCfg {
-  static constexpr int NB = 3, WPE = 2;
-};
-
-template <int FMT, int SUB>
 static int stream_blocks_per_cu() {
   static int n = 0;
   if (n == 0) {
     int v = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, k2_stream<FMT, SUB, SCfg<FMT>::NB, SCfg<FMT>::WPE>,
-                                                     NTHREADS, 0) != hipSuccess ||
-        v < 1)
-      v = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, k2_stream<FMT>, NTHREADS, 0) != hipSuccess || v < 1) v = 1;
     n = v;
   }
   return n;
 }
 
 static int blocks_per_cu(int fmt, bool mma, int sub) {
-  if (mma) {
-    if (fmt == 0) return sub == 2 ? stream_blocks_per_cu<0, 2>() : stream_blocks_per_cu<0, 1>();
-    return sub == 2 ? stream_blocks_per_cu<1, 2>() : stream_blocks_per_cu<1, 1>();
-  }
-  if (fmt == 0) return sub == 2 ? blocks_per_cu<0, false, 2>() : blocks_per_cu<0, false, 1>();
-  return sub == 2 ? blocks_per_cu<1, false, 2>() : blocks_per_cu<1, false, 1>();
+  if (mma) return fmt == 0 ? stream_blocks_per_cu<0>() : stream_blocks_per_cu<1>();
+  if (fmt == 0) return sub == 2 ? blocks_per_cu<0, 2>() : blocks_per_cu<0, 1>();
+  return sub == 2 ? blocks_per_cu<1, 2>() : blocks_per_cu<1, 1>();
 }
 
 K2Plan plan_k2(const KernelLayer& L, int64_t M, bool mma) {
@@ -875,20 +838,15 @@ hipError_t launch_k2(const KernelLayer& L, int64_t M, const uint8_t* qX, const v
   const uint32_t T = p.tiles_m * p.tiles_n, rem = T - p.full;
   const K2Sched sch{p.tiles_n, p.full, p.split, static_cast<float*>(workspace)};
   const uint32_t nblocks = p.full + rem * p.split;
-#define K2_LAUNCH(F, SB) launch_k2_t<F, false, SB>(L, M, qX, sX, lora_act, Y, ldy, ydtype, sch, nblocks, st)
-#define K2_STREAM(F, SB)                                                                                   \
-  hipLaunchKernelGGL((k2_stream<F, SB, SCfg<F>::NB, SCfg<F>::WPE>), dim3(nblocks), dim3(NTHREADS), 0, st, qX, \
-                     static_cast<const uint8_t*>(sX), M, L.qW, static_cast<const uint8_t*>(L.sW), L.N, L.K, \
-                     static_cast<const uint16_t*>(lora_act), L.L2t, L.rank, Y, ldy, ydtype, sch)
+#define K2_LAUNCH(F, SB) launch_k2_t<F, SB>(L, M, qX, sX, lora_act, Y, ldy, ydtype, sch, nblocks, st)
+#define K2_STREAM(F)                                                                                        \
+  hipLaunchKernelGGL((k2_stream<F>), dim3(nblocks), dim3(NTHREADS), 0, st, qX, static_cast<const uint8_t*>(sX), M, \
+                     L.qW, static_cast<const uint8_t*>(L.sW), L.N, L.K, static_cast<const uint16_t*>(lora_act),   \
+                     L.L2t, L.rank, Y, ldy, ydtype, sch)
   const int sub = sub_of(L.K);
-  if (mma) {  // the activation side in MMA form: streamed kernel
-    if (L.fmt == 0) {
-      if (sub == 2) K2_STREAM(0, 2);
-      else K2_STREAM(0, 1);
-    } else {
-      if (sub == 2) K2_STREAM(1, 2);
-      else K2_STREAM(1, 1);
-    }
+  if (mma) {  // the activation side in MMA form: streamed kernel (K % 128 == 0: two sub-steps per stage)
+    if (L.fmt == 0) K2_STREAM(0);
+    else K2_STREAM(1);
   } else if (L.fmt == 0) {
     if (sub == 2) K2_LAUNCH(0, 2);
     else K2_LAUNCH(0, 1);
@@ -908,7 +866,7 @@ hipError_t launch_k2_debug(const KernelLayer& L, int64_t M, const uint8_t* qX, i
                            int64_t n0, int64_t mt, int64_t nt, int32_t* out, hipStream_t st) {
   const uint32_t tn = (uint32_t)((nt + BN - 1) / BN), tm = (uint32_t)((mt + BM - 1) / BM);
   const K2Sched sch{tn, tm * tn, 1, nullptr};
-  hipLaunchKernelGGL((k2_gemm<0, true, false, 1>), dim3(tm * tn), dim3(NTHREADS), 0, st, qX, (const void*)nullptr, M,
+  hipLaunchKernelGGL((k2_gemm<0, true, 1>), dim3(tm * tn), dim3(NTHREADS), 0, st, qX, (const void*)nullptr, M,
                      L.qW, (const void*)nullptr, L.N, L.K, (const void*)nullptr, (const uint16_t*)nullptr, 0,
                      (void*)nullptr, (int64_t)0, 0, m0, n0, m0 + mt, n0 + nt, sch, out);
   return hipGetLastError();

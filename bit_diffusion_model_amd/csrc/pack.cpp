@@ -669,40 +669,15 @@ svdq_status svdq_prepare_weights(int64_t K, int64_t N, int32_t fmt, const uint8_
     }
     std::memcpy(qW_out + 4 * w, &o, 4);
   }
-  // scales: fp16 s = m * 2^e, m in [1, 2) -> plane of fp16 m [groups][Np], then plane of
-  // E8M0 bytes e + 9 + 127 [groups][Np]; s = 0 (and padding) -> m = 0, byte 127
+  // scales: the fp16 value as fp32 (exact), [groups][Np], padding 0
   const uint16_t* s16 = static_cast<const uint16_t*>(sW);
-  uint16_t* om = static_cast<uint16_t*>(sW_out);
-  uint8_t* oe = static_cast<uint8_t*>(sW_out) + groups * Np * 2;
+  float* of = static_cast<float*>(sW_out);
   for (int64_t g = 0; g < groups; ++g)
     for (int64_t n = 0; n < Np; ++n) {
-      const int64_t o = g * Np + n;
       const uint16_t h = n < N ? s16[g * N + n] : (uint16_t)0;
       if (h & 0x8000u) return fail(SVDQ_ENUMERIC, "negative weight scale");
-      const uint32_t ex = (h >> 10) & 0x1F, mant = h & 0x3FF;
-      if (ex == 0x1F) return fail(SVDQ_ENUMERIC, "non-finite weight scale");
-      if (ex == 0 && mant == 0) {
-        om[o] = 0;
-        oe[o] = 127;
-        continue;
-      }
-      int e;
-      uint32_t m10;
-      if (ex != 0) {
-        e = (int)ex - 15;
-        m10 = mant;
-      } else {  // subnormal: mant * 2^-24, normalise
-        int sh = 0;
-        uint32_t mm = mant;
-        while (!(mm & 0x400u)) {
-          mm <<= 1;
-          ++sh;
-        }
-        e = -14 - sh;
-        m10 = mm & 0x3FF;
-      }
-      om[o] = (uint16_t)((15u << 10) | m10);
-      oe[o] = (uint8_t)(e + 9 + 127);
+      if (((h >> 10) & 0x1F) == 0x1F) return fail(SVDQ_ENUMERIC, "non-finite weight scale");
+      of[g * Np + n] = (float)f16_to_double(h);
     }
   return ok();
 }

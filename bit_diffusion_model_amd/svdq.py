@@ -180,13 +180,12 @@ def pad4(n: int) -> int:
 
 
 def prepare_weights(K: int, N: int, fmt: int, qW: np.ndarray, sW: np.ndarray):
-    """Kernel layout of the residual weights: (qW [N][K/2] u8, sW bytes: INT4 the fp16
-    mantissa plane [K/64][Np] then the E8M0 plane [K/64][Np]; MXFP4 E8M0 [K/32][Np];
-    Np = N rounded up to 4)."""
+    """Kernel layout of the residual weights: (qW [N][K/2] u8, sW bytes: INT4 fp32
+    [K/64][Np]; MXFP4 E8M0 [K/32][Np]; Np = N rounded up to 4)."""
     qW = np.ascontiguousarray(qW, dtype=np.uint8)
     sW = np.ascontiguousarray(sW)
     qo = np.empty_like(qW)
-    so = np.empty((K // GROUP[fmt]) * pad4(N) * (3 if fmt == INT4_G64 else 1), np.uint8)
+    so = np.empty((K // GROUP[fmt]) * pad4(N) * (4 if fmt == INT4_G64 else 1), np.uint8)
     _check(lib().svdq_prepare_weights(K, N, fmt, _ptr(qW), _ptr(sW), _ptr(qo), _ptr(so)))
     return qo, so
 
@@ -260,8 +259,8 @@ class PackedLinear:
         torch = _torch()
         mma8 = form == ACT_MMA and self.fmt == INT4_G64
         qX = torch.empty((M, self.K if mma8 else self.K // 2), dtype=torch.uint8, device=self.device)
-        if form == ACT_MMA:  # scale planes with rows padded to 4 (INT4: fp16 m, then E8M0)
-            sX = torch.empty((self.K // self.group) * pad4(M) * (3 if mma8 else 1), dtype=torch.uint8,
+        if form == ACT_MMA:  # scales with rows padded to 4: INT4 fp32, MXFP4 E8M0 bytes
+            sX = torch.empty((self.K // self.group) * pad4(M) * (4 if mma8 else 1), dtype=torch.uint8,
                              device=self.device)
         else:
             sdt = torch.int16 if self.fmt == INT4_G64 else torch.uint8

@@ -64,9 +64,7 @@ typedef enum { SVDQ_F32 = 0, SVDQ_BF16 = 1 } svdq_dtype;
  *           converting.  Mp = M rounded up to a multiple of 4.
  *           INT4: qX [M][K] one FP8 E4M3 byte per code (sign bit 7, magnitude in the
  *           mantissa bits: value q * 2^-9), each 8-code block stored as codes
- *           0,2,4,6,1,3,5,7; sX: for the fp16 scale s = m * 2^e (m in [1, 2)) the
- *           plane fp16 m [K/64][Mp] then the plane of E8M0 bytes of 2^(e+9)
- *           [K/64][Mp] (s = 0: m = 0, byte 127).
+ *           0,2,4,6,1,3,5,7; sX [K/64][Mp] fp32: the fp16 scale values.
  *           MXFP4: qX as PACKED; sX [K/32][Mp] E8M0 bytes.
  *           Both: lora_act rows of 2*R16 bf16, [R16 hi][R16 lo] with hi = bf16(v),
  *           lo = bf16(v - hi) of the fp32 value v. */
@@ -84,9 +82,8 @@ typedef enum { SVDQ_ACT_PACKED = 0, SVDQ_ACT_MMA = 1 } svdq_act_form;
  *   L2t    [N][R16]   bf16  up projection transposed (L2^T), columns >= rank zero
  *   qW     [N][K/2]   u8    residual codes, row n = output channel n along K, in the
  *                           kernel bit order of svdq_prepare_weights
- *   sW                group-major scales as svdq_prepare_weights writes them: INT4 the
- *                           fp16 mantissa and E8M0 planes, MXFP4 E8M0 bytes, rows
- *                           padded to Np (16-byte aligned)
+ *   sW                group-major scales as svdq_prepare_weights writes them: INT4
+ *                           fp32, MXFP4 E8M0 bytes, rows padded to Np (16-byte aligned)
  * L1t/L2t may be NULL iff rank == 0. */
 typedef struct svdq_layer {
   int64_t K, N;
@@ -166,9 +163,8 @@ svdq_status svdq_prepare_lowrank(int64_t N, int32_t rank, const uint16_t* L2, ui
  *          in bits 0-2 and sign in bit 7, code 2j+1's magnitude in bits 4-6, and in bit 3
  *          the sign of code 2j-1 (indices mod 8): a mask then yields the even codes and
  *          a 4-bit rotate plus the same mask the odd ones, as FP8 E4M3 bytes q * 2^-9.
- *          sW_out: the fp16 scale s = m * 2^e (m in [1, 2)) as two planes, fp16 m
- *          [K/64][Np] then E8M0 bytes of 2^(e+9) [K/64][Np] ((K/64) * Np * 3 bytes);
- *          s = 0 and padding give m = 0, byte 127.
+ *          sW_out: the fp16 scales as fp32 values [K/64][Np] ((K/64) * Np * 4 bytes),
+ *          padding 0.
  * EINVAL on bad sizes, ENUMERIC on a negative or non-finite scale. */
 svdq_status svdq_prepare_weights(int64_t K, int64_t N, int32_t fmt, const uint8_t* qW,
                                  const void* sW, uint8_t* qW_out, void* sW_out);

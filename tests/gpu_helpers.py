@@ -71,8 +71,8 @@ def bf16_rne_bits(v32):
 def decode_mma(qX, sX, la, fmt, K, rank):
     """Kernel 1's MMA-form outputs (device tensors) decoded per the header's description:
     INT4 codes from FP8 bytes (sign bit 7, magnitude bits 0-2; 8-code blocks stored as
-    codes 0,2,4,6,1,3,5,7) and scale values m * 2^(byte - 136) from the fp16 mantissa
-    plane and the E8M0 plane (rows padded to Mp); MXFP4 codes as stored and E8M0 bytes
+    codes 0,2,4,6,1,3,5,7) and fp32 scale values (rows padded to Mp); MXFP4 codes as
+    stored and E8M0 bytes
     (rows padded to Mp); lora_act rows [R16 hi][R16 lo] bf16.  Returns (codes or packed
     bytes, scales (float64 values [K/64][M] for INT4, bytes [K/32][M] for MXFP4), hi bits,
     lo bits)."""
@@ -87,10 +87,7 @@ def decode_mma(qX, sX, la, fmt, K, rank):
         codes = np.empty_like(v)
         codes[:, :, 0::2], codes[:, :, 1::2] = v[:, :, :4], v[:, :, 4:]
         G = K // 64
-        m = sb[:G * Mp * 2].view(np.float16).reshape(G, Mp)[:, :M].astype(np.float64)
-        e = sb[G * Mp * 2:G * Mp * 3].reshape(G, Mp)[:, :M].astype(np.int64) - 136
-        assert np.all((m == 0) | ((m >= 1) & (m < 2)))
-        out = codes.reshape(M, K), m * 2.0 ** e
+        out = codes.reshape(M, K), sb[:G * Mp * 4].view(np.float32).reshape(G, Mp)[:, :M].astype(np.float64)
     else:
         out = q, sb[:(K // 32) * Mp].reshape(K // 32, Mp)[:, :M]
     hi = lo = None

@@ -146,9 +146,8 @@ def test_prepare_lowrank_layouts():
 def test_prepare_weights_kernel_layout():
     """The kernel layout decodes back to the oracle's codes and scales: even codes by the
     mask 0x87, odd codes by a 4-bit rotate of the word and the same mask (FP8 E4M3 bytes
-    with zero exponent: magnitude in bits 0-2, sign in bit 7); each scale is
-    m * 2^(byte - 127 - 9) with m from the fp16 plane and the byte from the E8M0 plane,
-    m in [1, 2) or 0; padded rows hold m = 0, byte 127."""
+    with zero exponent: magnitude in bits 0-2, sign in bit 7); the scales are the fp16
+    values as fp32 [K/64][Np], padded rows 0."""
     rng = np.random.default_rng(11)
     K, N = 256, 39  # N not a multiple of 4: padded scale rows
     R = (rng.standard_normal((K, N)) * 10.0 ** rng.uniform(-9, 2, (1, N))).astype(np.float32)
@@ -168,12 +167,10 @@ def test_prepare_weights_kernel_layout():
     np.testing.assert_array_equal(dec.reshape(N, K), codes)
     Np = (N + 3) // 4 * 4
     G = K // 64
-    assert sk.size == G * Np * 3
-    mant = sk[:G * Np * 2].view(np.float16).reshape(G, Np).astype(np.float64)
-    e = sk[G * Np * 2:].reshape(G, Np).astype(np.int64) - 127 - 9
-    assert np.all((mant == 0) | ((mant >= 1) & (mant < 2)))
-    np.testing.assert_array_equal((mant * 2.0 ** e)[:, :N], sc.view(np.float16).astype(np.float64))
-    assert not mant[:, N:].any() and np.all(e[:, N:] == -9)
+    assert sk.size == G * Np * 4
+    sv = sk.view(np.float32).reshape(G, Np)
+    np.testing.assert_array_equal(sv[:, :N], sc.view(np.float16).astype(np.float32))
+    assert not sv[:, N:].any()
     c4, s4 = opack.quantize_residual(R, "mxfp4")
     qf, sf = svdq.prepare_weights(K, N, svdq.MXFP4_G32, opack.pack_codes(c4, "mxfp4"), s4)
     np.testing.assert_array_equal(qf, opack.pack_codes(c4, "mxfp4"))
@@ -229,6 +226,6 @@ def test_device_entry_points_validate_on_host():
     assert L.svdq_gemm_w4a4_lora_up(ref, 4, 0, 16, 16, 16, 16, 64, 0, 8, 1 << 20, None) == 1 and "workspace" in _err()
     assert L.svdq_linear_forward(ref, 4, 16, 256, 16, 64, 0, 256, 10, None) == 1 and "workspace" in _err()
     assert L.svdq_debug_group_sums(ref, 4, 16, 0, 0, 5, 4, 16, None) == 1 and "window" in _err()
-    # MMA form: FP8 codes (M*K bytes), fp16 + E8M0 scale planes (3 bytes per group and
-    # row), 2*R16 bf16 per row
-    assert L.svdq_workspace_bytes(ref, 100) >= 100 * 256 + 4 * 100 * 3 + 100 * 16 * 4
+    # MMA form: FP8 codes (M*K bytes), fp32 scales (4 bytes per group and row), 2*R16
+    # bf16 per row
+    assert L.svdq_workspace_bytes(ref, 100) >= 100 * 256 + 4 * 100 * 4 + 100 * 16 * 4
