@@ -76,7 +76,7 @@ def _pmc_means(path):
         name = r["Kernel_Name"]
         # kernel 2 of the timed forward: the INT4 streamed kernel on the MMA activation
         # form (the fixup launch is counted with it)
-        if "k2_stream<0," in name or "k2_fixup" in name:
+        if "k2_stream<0>" in name or "k2_fixup" in name:
             key = "k2" if "k2_stream" in name else "fixup"
         elif "copyBuffer" in name or "copy" in name.lower():
             key = "copy"
