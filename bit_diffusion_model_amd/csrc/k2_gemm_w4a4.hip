@@ -424,23 +424,48 @@ __global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 
 // twice the rate of the packed-fp16 and mixed-precision forms on gfx950 and issue
 // alongside the MFMA (measured; v_pk_mul_f16 does not overlap a running MFMA).
 
-// LDS layout of one stage
+// Block shape: a WGM x WGN grid of waves, each owning TI x TJ MFMA tiles of 32 x 32.
+template <int WGM_, int WGN_, int TI_, int TJ_>
+struct Shape {
+  static constexpr int WGM = WGM_, WGN = WGN_, TI = TI_, TJ = TJ_;
+  static constexpr int NW = WGM * WGN, NT = 64 * NW;
+  static constexpr int BM = 32 * TI * WGM, BN = 32 * TJ * WGN;
+  static constexpr int CB = BN / 32;                 // 32-wide column blocks per tile
+  static constexpr int PART = (BM / 32) * CB * 16 * 64;  // floats per partial tile
+};
+// INT4: 128 x 128, 4 waves of 64 x 64 (the rescale schedule's 2 x 2 MFMA tiles), two
+// blocks per CU (a 128 x 256 tile with one block per CU measured 6% slower: the waves
+// of one block meet at every barrier).  MXFP4: 256 x 256, 8 waves of 128 x 64, one block
+// per CU (no per-group VALU, so larger wave tiles; the panel loads bound this format,
+// and the larger tile halves their bytes per output).
+template <int FMT> struct SShape;
+template <> struct SShape<0> : Shape<2, 2, 2, 2> {};
+template <> struct SShape<1> : Shape<2, 4, 4, 2> {};
+
+// LDS layout of one stage of the streamed kernel
 template <int FMT>
 struct DLay {
+  using SH = SShape<FMT>;
+  static constexpr int BM = SH::BM, BN = SH::BN, NW = SH::NW;
   static constexpr int RA = 2 * (FMT == 0 ? 64 : 32);  // A bytes per row
   static constexpr int RB = 2 * 32;                     // B (4-bit) bytes per row
   static constexpr int B_OFF = BM * RA;
   static constexpr int S_OFF = B_OFF + BN * RB;
   // scales of one sub-step: INT4 X [BM] fp32 | W [BN] fp32; MXFP4 X e [2][BM] | W e [2][BN]
-  // (the sub-step's two 32-groups)
-  static constexpr int S_SUB = FMT == 0 ? 4 * BM + 4 * BN : 2 * BM + 2 * BN;
-  static constexpr int BUF = S_OFF + 2 * S_SUB;
+  // (the sub-step's two 32-groups); moved in 256-byte parts, one 4-byte load per lane
+  static constexpr int XB = FMT == 0 ? 4 * BM : 2 * BM, WB = FMT == 0 ? 4 * BN : 2 * BN;
+  static constexpr int S_SUB = XB + WB;
+  static constexpr int XP = XB / 256, WP = WB / 256, SPARTS = 2 * (XP + WP);  // per stage
+  static constexpr int NS = (SPARTS + NW - 1) / NW;  // scale loads per wave
+  // slots past SPARTS load a part again into a spare 256 bytes, so every wave issues NS
+  static constexpr int SPARE = S_OFF + 2 * S_SUB;
+  static constexpr int BUF = SPARE + (NS * NW > SPARTS ? 256 : 0);
   // load instructions per wave and stage
-  static constexpr int NA = BM * RA / 1024 / 4;
-  static constexpr int NBW = BN * RB / 1024 / 4;
-  static constexpr int NS = 2;  // scale loads per wave: one activation-side, one weight-side
+  static constexpr int NA = BM * RA / 1024 / NW;
+  static constexpr int NBW = BN * RB / 1024 / NW;
   static constexpr int NDW = NA + NBW + NS;
-  static_assert(BM * RA % 4096 == 0 && BN * RB % 4096 == 0, "whole 1 KB load chunks per wave");
+  static_assert(BM * RA % (1024 * NW) == 0 && BN * RB % (1024 * NW) == 0, "whole 1 KB load chunks per wave");
+  static_assert(XB % 256 == 0 && WB % 256 == 0, "whole 256-byte scale parts");
 };
 
 // XOR swizzle of the 16-byte slot within a row of `slots` slots.  An operand read
@@ -470,12 +495,14 @@ __device__ __forceinline__ void wait_cnt() {
 }
 
 template <int FMT>
-__global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void k2_stream(
+__global__ __launch_bounds__(SShape<FMT>::NT, 8 / SShape<FMT>::NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void k2_stream(
     const uint8_t* __restrict__ qX, const uint8_t* __restrict__ sX, int64_t M,
     const uint8_t* __restrict__ qW, const uint8_t* __restrict__ sW, int64_t N, int64_t K,
     const uint16_t* __restrict__ lora_act, const uint16_t* __restrict__ L2, int rank,
     void* __restrict__ Y, int64_t ldy, int ydtype, K2Sched sch) {
   using D = DLay<FMT>;
+  using SH = SShape<FMT>;
+  constexpr int TI = SH::TI, TJ = SH::TJ, BM = SH::BM, BN = SH::BN, NW = SH::NW;
   // separate arrays, always addressed statically (the main loop is unrolled by 3), so
   // the compiler can tell a buffer's pending loads from reads of another
   __shared__ __attribute__((aligned(1024))) uint8_t lds0[D::BUF];
@@ -486,8 +513,8 @@ __global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int kh = lane >> 5;
-  const int wm = (wave >> 1) * WM;
-  const int wn = (wave & 1) * WN;
+  const int wm = (wave / SH::WGN) * (32 * TI);
+  const int wn = (wave % SH::WGN) * (32 * TJ);
   const uint32_t Kb = (uint32_t)(K >> 1);                  // 4-bit code bytes per row
   const uint32_t Ka = FMT == 0 ? (uint32_t)K : Kb;         // A bytes per row
   const int nstages = (int)(K >> 7);
@@ -517,38 +544,45 @@ __global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 
   uint32_t voA[D::NA], voB[D::NBW];
 #pragma unroll
   for (int q = 0; q < D::NA; ++q) {
-    const int pos = (wave + 4 * q) * 1024 + lane * 16;
+    const int pos = (wave + NW * q) * 1024 + lane * 16;
     const int row = pos / D::RA, ps = (pos % D::RA) / 16;
     voA[q] = (uint32_t)row * Ka + (uint32_t)((ps ^ swz(row, D::RA / 16)) * 16);
   }
 #pragma unroll
   for (int q = 0; q < D::NBW; ++q) {
-    const int pos = (wave + 4 * q) * 1024 + lane * 16;
+    const int pos = (wave + NW * q) * 1024 + lane * 16;
     const int row = pos / D::RB, ps = (pos % D::RB) / 16;
     voB[q] = (uint32_t)row * Kb + (uint32_t)((ps ^ swz(row, D::RB / 16)) * 16);
   }
   auto issue = [&](int k, uint8_t* base) {
 #pragma unroll
-    for (int q = 0; q < D::NA; ++q) dma16(rA, base + (wave + 4 * q) * 1024, voA[q], (uint32_t)k * D::RA);
+    for (int q = 0; q < D::NA; ++q) dma16(rA, base + (wave + NW * q) * 1024, voA[q], (uint32_t)k * D::RA);
 #pragma unroll
-    for (int q = 0; q < D::NBW; ++q) dma16(rB, base + D::B_OFF + (wave + 4 * q) * 1024, voB[q], (uint32_t)k * D::RB);
-    // scale loads: every wave issues one activation-side and one weight-side load; the
-    // wave number picks the sub-step (w & 1) and, for INT4, the half of the 128 rows or
-    // columns (w >> 1), arithmetically (no branches, so the compiler keeps tracking which
-    // buffer has loads pending)
-    {
-      const int u = wave & 1;
-      uint8_t* sb = base + D::S_OFF + u * D::S_SUB;
-      if (FMT == 0) {
-        const uint32_t g = (uint32_t)(k * 2 + u);
-        const uint32_t h = (uint32_t)wave >> 1;
-        dma4(rSX, sb + h * 256, (g * Mp + (uint32_t)m0 + 64 * h) * 4 + lane * 4);
-        dma4(rSW, sb + 4 * BM + h * 256, (g * Np + (uint32_t)n0 + 64 * h) * 4 + lane * 4);
-      } else {  // lanes 0-31 group 2g, lanes 32-63 group 2g+1
-        const uint32_t g2 = 2 * (uint32_t)(k * 2 + u) + (uint32_t)kh;
-        dma4(rSX, sb, g2 * Mp + (uint32_t)m0 + l32 * 4);
-        dma4(rSW, sb + 2 * BM, g2 * Np + (uint32_t)n0 + l32 * 4);
+    for (int q = 0; q < D::NBW; ++q) dma16(rB, base + D::B_OFF + (wave + NW * q) * 1024, voB[q], (uint32_t)k * D::RB);
+    // scale parts: slot z = wave + NW r covers sub-step z / (XP + WP), part y of it
+    // (activation parts first); slots past the last part reload part 0 of sub-step 0
+    // into the spare bytes.  Everything is wave-uniform arithmetic (no branches, so the
+    // compiler keeps tracking which buffer has loads pending).
+#pragma unroll
+    for (int r = 0; r < D::NS; ++r) {
+      const int z0 = wave + NW * r;
+      const bool spare = z0 >= D::SPARTS;
+      const int z = spare ? 0 : z0;
+      const int u = z / (D::XP + D::WP), y = z % (D::XP + D::WP);
+      const bool wside = y >= D::XP;
+      const int yp = wside ? y - D::XP : y;
+      uint8_t* dst = spare ? base + D::SPARE : base + D::S_OFF + u * D::S_SUB + (wside ? D::XB : 0) + yp * 256;
+      const uint32_t pitch = wside ? Np : Mp, org = wside ? (uint32_t)n0 : (uint32_t)m0;
+      const uint32_t g = (uint32_t)(k * 2 + u);
+      uint32_t off;
+      if (FMT == 0) {  // fp32 values of rows yp * 64 + lane
+        off = (g * pitch + org + (uint32_t)(yp * 64 + lane)) * 4;
+      } else {  // bytes [gi][row] of the [2][B] region: byte yp * 256 + 4 lane ..
+        const int bpg = wside ? BN : BM;
+        const int b0 = yp * 256 + lane * 4;
+        off = (2 * g + (uint32_t)(b0 / bpg)) * pitch + org + (uint32_t)(b0 % bpg);
       }
+      dma4(wside ? rSW : rSX, dst, off);
     }
   };
 
@@ -574,9 +608,9 @@ __global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 
       const int ls = u * 2 + kh;  // 4-bit bytes u*32 + kh*16
       f.b[j] = *reinterpret_cast<const uint4*>(base + D::B_OFF + col * D::RB + ((ls ^ swz(col, D::RB / 16)) * 16));
       if constexpr (FMT == 0) {
-        f.sw[j] = reinterpret_cast<const float*>(sb + 4 * BM)[col];
+        f.sw[j] = reinterpret_cast<const float*>(sb + D::XB)[col];
       } else {
-        f.sb[j] = sb[2 * BM + kh * BN + col];
+        f.sb[j] = sb[D::XB + kh * BN + col];
       }
     }
 #pragma unroll
@@ -725,36 +759,39 @@ __global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
       for (int j = 0; j < TJ; ++j) store_sub(acc[i][j], Y, ldy, ydtype, m0, n0, rowsA, N, wm + i * 32, wn + j * 32, l32, kh);
   } else {
-    float* P = sch.partials + (size_t)(blockIdx.x - sch.full) * PART_FLOATS;
+    float* P = sch.partials + (size_t)(blockIdx.x - sch.full) * SH::PART;
 #pragma unroll
     for (int i = 0; i < TI; ++i)
 #pragma unroll
       for (int j = 0; j < TJ; ++j)
 #pragma unroll
-        for (int a = 0; a < 16; ++a) P[((((wm >> 5) + i) * 4 + (wn >> 5) + j) * 16 + a) * 64 + lane] = acc[i][j][a];
+        for (int a = 0; a < 16; ++a) P[((((wm >> 5) + i) * SH::CB + (wn >> 5) + j) * 16 + a) * 64 + lane] = acc[i][j][a];
   }
 }
 
 // Sum of the `split` partial tiles of one remaining tile, in part order (the result does
 // not depend on which part finished first), stored like a whole tile.  One 64-thread
-// block per 32 x 32 sub-tile: blockIdx.x = remaining tile * 16 + sub-tile index.
+// block per 32 x 32 sub-tile: blockIdx.x = remaining tile * sub-tiles + sub-tile index,
+// sub-tile = row block * CB + column block.
+template <int TBM, int TBN>
 __global__ __launch_bounds__(64) void k2_fixup(const float* __restrict__ partials, K2Sched sch, int64_t M,
                                                int64_t N, void* __restrict__ Y, int64_t ldy, int ydtype) {
+  constexpr int CB = TBN / 32, NSUB = (TBM / 32) * CB, PF = NSUB * 16 * 64;
   const int lane = threadIdx.x;
-  const uint32_t r = blockIdx.x >> 4, sub = blockIdx.x & 15;  // sub = 4 * row block + column block
+  const uint32_t r = blockIdx.x / NSUB, sub = blockIdx.x % NSUB;
   const uint32_t t = sch.full + r;
-  const int64_t m0 = (int64_t)(t / sch.tiles_n) * BM, n0 = (int64_t)(t % sch.tiles_n) * BN;
-  const float* P = partials + (size_t)r * sch.split * PART_FLOATS + (size_t)sub * 16 * 64 + lane;
+  const int64_t m0 = (int64_t)(t / sch.tiles_n) * TBM, n0 = (int64_t)(t % sch.tiles_n) * TBN;
+  const float* P = partials + (size_t)r * sch.split * PF + (size_t)sub * 16 * 64 + lane;
   v16f acc;
 #pragma unroll
   for (int a = 0; a < 16; ++a) acc[a] = P[a * 64];
   for (uint32_t p = 1; p < sch.split; ++p) {
-    const float* Q = P + (size_t)p * PART_FLOATS;
+    const float* Q = P + (size_t)p * PF;
 #pragma unroll
     for (int a = 0; a < 16; ++a) acc[a] += Q[a * 64];
   }
-  const int64_t rowsA = M - m0 < BM ? M - m0 : BM;
-  store_sub(acc, Y, ldy, ydtype, m0, n0, rowsA, N, (int)(sub >> 2) * 32, (int)(sub & 3) * 32, lane & 31, lane >> 5);
+  const int64_t rowsA = M - m0 < TBM ? M - m0 : TBM;
+  store_sub(acc, Y, ldy, ydtype, m0, n0, rowsA, N, (int)(sub / CB) * 32, (int)(sub % CB) * 32, lane & 31, lane >> 5);
 }
 
 }  // namespace
@@ -789,7 +826,8 @@ static int stream_blocks_per_cu() {
   static int n = 0;
   if (n == 0) {
     int v = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, k2_stream<FMT>, NTHREADS, 0) != hipSuccess || v < 1) v = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, k2_stream<FMT>, SShape<FMT>::NT, 0) != hipSuccess || v < 1)
+      v = 1;
     n = v;
   }
   return n;
@@ -801,10 +839,21 @@ static int blocks_per_cu(int fmt, bool mma, int sub) {
   return sub == 2 ? blocks_per_cu<1, 2>() : blocks_per_cu<1, 1>();
 }
 
+// Output tile of the kernel-2 variant for (format, activation form), and its partial
+// tile size in floats.
+static void tile_of(int fmt, bool mma, int& tbm, int& tbn, size_t& part) {
+  if (mma && fmt == 0) { tbm = SShape<0>::BM; tbn = SShape<0>::BN; part = SShape<0>::PART; }
+  else if (mma) { tbm = SShape<1>::BM; tbn = SShape<1>::BN; part = SShape<1>::PART; }
+  else { tbm = BM; tbn = BN; part = PART_FLOATS; }
+}
+
 K2Plan plan_k2(const KernelLayer& L, int64_t M, bool mma) {
   K2Plan p{};
-  p.tiles_m = (uint32_t)((M + BM - 1) / BM);
-  p.tiles_n = (uint32_t)((L.N + BN - 1) / BN);
+  int tbm, tbn;
+  size_t part;
+  tile_of(L.fmt, mma, tbm, tbn, part);
+  p.tiles_m = (uint32_t)((M + tbm - 1) / tbm);
+  p.tiles_n = (uint32_t)((L.N + tbn - 1) / tbn);
   const uint32_t T = p.tiles_m * p.tiles_n;
   p.full = T;
   p.split = 1;
@@ -812,7 +861,7 @@ K2Plan plan_k2(const KernelLayer& L, int64_t M, bool mma) {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
     return p;
-  const int sub = sub_of(L.K);
+  const int sub = mma ? 2 : sub_of(L.K);
   const uint32_t G = (uint32_t)cus * (uint32_t)blocks_per_cu(L.fmt, mma, sub);  // blocks resident at once
   const uint32_t R = T % G;  // tiles of the last, partly filled round
   const uint32_t nst = (uint32_t)(L.K >> 6) / (uint32_t)sub;  // stages
@@ -823,7 +872,7 @@ K2Plan plan_k2(const KernelLayer& L, int64_t M, bool mma) {
   if (R == 0 || S < 2) return p;
   p.full = T - R;
   p.split = S;
-  p.bytes = (size_t)R * S * PART_FLOATS * sizeof(float);
+  p.bytes = (size_t)R * S * part * sizeof(float);
   return p;
 }
 
@@ -840,7 +889,7 @@ hipError_t launch_k2(const KernelLayer& L, int64_t M, const uint8_t* qX, const v
   const uint32_t nblocks = p.full + rem * p.split;
 #define K2_LAUNCH(F, SB) launch_k2_t<F, SB>(L, M, qX, sX, lora_act, Y, ldy, ydtype, sch, nblocks, st)
 #define K2_STREAM(F)                                                                                        \
-  hipLaunchKernelGGL((k2_stream<F>), dim3(nblocks), dim3(NTHREADS), 0, st, qX, static_cast<const uint8_t*>(sX), M, \
+  hipLaunchKernelGGL((k2_stream<F>), dim3(nblocks), dim3(SShape<F>::NT), 0, st, qX, static_cast<const uint8_t*>(sX), M, \
                      L.qW, static_cast<const uint8_t*>(L.sW), L.N, L.K, static_cast<const uint16_t*>(lora_act),   \
                      L.L2t, L.rank, Y, ldy, ydtype, sch)
   const int sub = sub_of(L.K);
@@ -856,9 +905,17 @@ hipError_t launch_k2(const KernelLayer& L, int64_t M, const uint8_t* qX, const v
   }
 #undef K2_LAUNCH
 #undef K2_STREAM
-  if (rem > 0)
-    hipLaunchKernelGGL(k2_fixup, dim3(rem * 16), dim3(64), 0, st, static_cast<const float*>(workspace), sch, M,
-                       L.N, Y, ldy, ydtype);
+  if (rem > 0) {
+    const float* part = static_cast<const float*>(workspace);
+    if (mma && L.fmt == 0)
+      hipLaunchKernelGGL((k2_fixup<SShape<0>::BM, SShape<0>::BN>), dim3(rem * (SShape<0>::PART / 1024)), dim3(64), 0,
+                         st, part, sch, M, L.N, Y, ldy, ydtype);
+    else if (mma)
+      hipLaunchKernelGGL((k2_fixup<SShape<1>::BM, SShape<1>::BN>), dim3(rem * (SShape<1>::PART / 1024)), dim3(64), 0,
+                         st, part, sch, M, L.N, Y, ldy, ydtype);
+    else
+      hipLaunchKernelGGL((k2_fixup<BM, BN>), dim3(rem * 16), dim3(64), 0, st, part, sch, M, L.N, Y, ldy, ydtype);
+  }
   return hipGetLastError();
 }
 
