@@ -253,11 +253,11 @@ def main():
 
     G = lay.group
     k2_ops = float(M) * N * (2.0 * K + 2.0 * r)
-    # kernel 1's HBM bytes in MMA form: X (bf16), codes (INT4 FP8 bytes / MXFP4 nibbles),
-    # scales (INT4 fp32 / E8M0 bytes), lora_act (R16 x 4 bytes); the factor
-    # rows are re-read from L2 and not counted
+    # kernel 1's HBM bytes in MMA form: X (bf16), codes (INT4 FP6 operand words, 64 bytes
+    # per group / MXFP4 nibbles), scales (INT4 fp16 / E8M0 bytes), lora_act (R16 x 4
+    # bytes); the factor rows are re-read from L2 and not counted
     if fmt == svdq.INT4_G64:
-        k1_bytes = float(M) * (2 * K + K + (K // G) * 4 + 4 * svdq.r16(r))
+        k1_bytes = float(M) * (2 * K + K + (K // G) * 2 + 4 * svdq.r16(r))
     else:
         k1_bytes = float(M) * (2 * K + K // 2 + (K // G) + 4 * svdq.r16(r))
     peak = PEAK_MFMA_TOPS if fmt == svdq.INT4_G64 else PEAK_MFMA_FP4_TOPS

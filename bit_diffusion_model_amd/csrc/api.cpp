@@ -63,17 +63,18 @@ static size_t rup(size_t x) { return (x + 255) & ~size_t(255); }
 struct WsLayout {
   size_t qx, sx, la, part, total;
 };
-// The forward path's workspace: the activation side in MMA form (INT4 codes as FP8
-// bytes [M][K] and split scale planes; MXFP4 packed codes and E8M0 bytes; lora_act as
-// bf16 hi/lo rows, the bytes of fp32 [M][R16]), then kernel 2's partial tiles.
+// The forward path's workspace: the activation side in MMA form (INT4 FP6 operand
+// words, 64 bytes per token and group, and an fp16 scale plane; MXFP4 packed codes and
+// E8M0 bytes; lora_act as bf16 hi/lo rows, the bytes of fp32 [M][R16]), then kernel 2's
+// partial tiles.
 static WsLayout ws_layout(const svdq_layer* L, int64_t M) {
-  const bool f8 = L->fmt == SVDQ_INT4_G64;
+  const bool i4 = L->fmt == SVDQ_INT4_G64;
   WsLayout w;
   w.qx = 0;
-  w.sx = rup((size_t)M * (size_t)(f8 ? L->K : L->K / 2));
-  // MMA-form scales: rows padded to Mp = M rounded up to 4; INT4 fp32, MXFP4 E8M0 bytes
+  w.sx = rup((size_t)M * (size_t)(i4 ? L->K : L->K / 2));
+  // MMA-form scales: rows padded to Mp = M rounded up to 4; INT4 fp16, MXFP4 E8M0 bytes
   const size_t Mp = ((size_t)M + 3) / 4 * 4;
-  w.la = w.sx + rup((size_t)(L->K / group_of(L->fmt)) * Mp * (f8 ? 4 : 1));
+  w.la = w.sx + rup((size_t)(L->K / group_of(L->fmt)) * Mp * (i4 ? 2 : 1));
   w.part = w.la + rup((size_t)M * (size_t)((L->rank + 15) / 16 * 16) * 4);
   KernelLayer kl{L->K, L->N, L->rank, L->fmt, nullptr, nullptr, nullptr, nullptr, nullptr};
   w.total = w.part + rup(plan_k2(kl, M, true).bytes);

@@ -6,11 +6,14 @@
 namespace svdq {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v6i __attribute__((ext_vector_type(6)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
 
 constexpr int kMaxRank = 128;
 
@@ -32,29 +35,40 @@ __device__ __forceinline__ void nib8_to_fp8(uint32_t d, uint32_t& lo, uint32_t& 
   hi = ((d >> 4) & 0x07070707u) | (d & 0x80808080u);
 }
 
-// The same expansion for the kernel's weight layout, in which each byte j of the word
-// holds element 2j in bits 0-2 (magnitude) and 7 (sign), the magnitude of element 2j+1
-// in bits 4-6, and in bit 3 the sign of element 2j-1 (cyclically, of byte j-1's odd
-// element).  Then lo is a mask, and hi is the word rotated by 4 bits and masked.
-__device__ __forceinline__ void nib8p_to_fp8(uint32_t d, uint32_t& lo, uint32_t& hi) {
-  lo = d & 0x87878787u;
-  hi = __builtin_amdgcn_alignbit(d, d, 4) & 0x87878787u;
+// INT4 codes as matrix-core FP6 E2M3 operands: code q is the 6-bit field sign << 5 | |q|
+// (exponent 0: the value q / 8).  One operand half (32 codes of a group half) is six
+// words with field f at bit 6 f; field f carries k = 16 (f & 1) + (f >> 1) of the half.
+// Bits 3-4 of every field are zero, so the prepared weight layout stores the half in
+// four words w0..w3 with the info bits of words 2 and 5 on the zero bits of words
+// 0, 1 and 3, 4: w0 = f0 | (f2 & Z0), w1 = f1 | (f2 & Z1) (and w2, w3 from f3, f4, f5).
+constexpr uint32_t kZ0 = (3u << 3) | (3u << 9) | (3u << 15) | (3u << 21) | (3u << 27);
+constexpr uint32_t kZ1 = (3u << 1) | (3u << 7) | (3u << 13) | (3u << 19) | (3u << 25) | (1u << 31);
+__device__ __forceinline__ v8i expand_w6(uint4 w) {
+  return v8i{(int)(w.x & ~kZ0), (int)(w.y & ~kZ1), (int)((w.x & kZ0) | (w.y & kZ1)),
+             (int)(w.z & ~kZ0), (int)(w.w & ~kZ1), (int)((w.z & kZ0) | (w.w & kZ1)), 0, 0};
 }
 
-// An INT4 group scale s = m * 2^e (m in [1, 2)), given as fp32 bits (every fp16 value
-// is exact in fp32), as one word: bits 0-15 the fp16 m (0 for s = 0), bits 16-23 the
-// E8M0 byte of 2^(e + 9) (127 for s = 0).  2^-9 is the value of FP8 code 1, so an MFMA
-// with these block scales on both sides returns the exact integer group sum times
-// 2^(eX + eW).
-__device__ __forceinline__ uint32_t split_scale_f32(uint32_t u) {
-  const float f = __uint_as_float(u);
-  const uint32_t m = f == 0.0f ? 0u : __builtin_bit_cast(uint16_t, (_Float16)__uint_as_float((u & 0x807FFFFFu) | (127u << 23)));
-  const uint32_t eb = f == 0.0f ? 127u : ((u >> 23) & 0xFFu) + 9u;
-  return m | (eb << 16);
-}
-// The same from fp16 bits.
-__device__ __forceinline__ uint32_t split_scale_word(uint32_t bits) {
-  return split_scale_f32(__float_as_uint((float)__builtin_bit_cast(_Float16, (uint16_t)bits)));
+// 32 sign-magnitude nibbles of a group half in storage order (code 2j in the low nibble
+// of byte j) -> the six FP6 operand words: nibbles -> FP8 bytes q * 2^-9 -> fp32 ->
+// the FP6 converter (x / 2^-6 = q / 8, exact), which interleaves its two 16-value inputs
+// field by field (codes 0-15 in the even fields, 16-31 in the odd ones).
+__device__ __forceinline__ v6i nib32_to_fp6(uint4 d) {
+  const uint32_t dw[4] = {d.x, d.y, d.z, d.w};
+  v16f x0, x1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t lo, hi;
+    nib8_to_fp8(dw[i], lo, hi);  // lo: codes 8i + 0, 2, 4, 6; hi: 8i + 1, 3, 5, 7
+    const v2f a = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, false), b = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, true);
+    const v2f c = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false), e = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
+    const float v[8] = {a.x, c.x, a.y, c.y, b.x, e.x, b.y, e.y};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (i < 2) x0[8 * i + j] = v[j];
+      else x1[8 * (i - 2) + j] = v[j];
+    }
+  }
+  return __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(x0, x1, 0x1p-6f);
 }
 
 // Raw buffer resource over `bytes` bytes at p: loads beyond the range return zeros.

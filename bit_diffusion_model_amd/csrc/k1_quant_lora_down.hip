@@ -29,9 +29,13 @@
 // round(t) is the correctly rounded code unless x / s lies within 2^-17 of a half
 // integer.  Such lanes are flagged and, if any lane of the wave has one, the chunk takes
 // the exact correction (x - q * s is exact near s / 2, and ties go to even).  The MMA
-// form then converts t * 2^-9 with the hardware FP8 conversion (round to nearest even
-// on the E4M3 subnormal grid, whose step is 2^-9): the byte of code q, with no integer
-// conversion or bit packing.
+// form then converts t / 8 with the hardware FP6 conversion (round to nearest even on
+// the E2M3 subnormal grid, whose step is 1/8): the 6-bit field of code q, value q / 8.
+// The converter interleaves two 16-value inputs field by field, so the lanes of
+// quarters 2h and 2h+1 of a group (lanes l and l ^ 16) each convert their own 16 codes
+// twice, exchange halves with one row swap per word, and keep the even fields of the
+// even quarter and the odd fields of the odd quarter: field f of half h holds
+// k = 32 h + 16 (f & 1) + (f >> 1), the order kernel 2's weight operand uses.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -137,26 +141,31 @@ k1_quant_lora_down(const uint16_t* __restrict__ X, int64_t ldx, int64_t M, int64
           t[i] = q + (float)away * copysignf(1.0f, e);
         }
       }
+      // MMA form: a group half's 192-bit operand (six words), built by the lane pair of
+      // quarters 2h, 2h+1 together (every lane takes part in the row swap, valid row or
+      // not).  The clamp to +-7 only acts for subnormal fp16 scales; code 0 may carry
+      // either sign bit.
+      uint32_t fw[3] = {0u, 0u, 0u};
+      if constexpr (MMA) {
+        v16f tc;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) tc[i] = __builtin_amdgcn_fmed3f(t[i], -7.0f, 7.0f);
+        const v6i f6 = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(tc, tc, 8.0f);
+        // bits of the even fields (field 2i at bit 12 i) in words d and d + 3
+        constexpr uint32_t EV[3] = {0x3F03F03Fu, 0xF03F03F0u, 0x03F03F03u};
+#pragma unroll
+        for (int d = 0; d < 3; ++d) {
+          // even rows (quarters 0, 2) receive the odd row's word d, odd rows the even
+          // row's word d + 3
+          const auto r = __builtin_amdgcn_permlane16_swap((uint32_t)f6[d], (uint32_t)f6[d + 3], false, false);
+          fw[d] = (r[0] & EV[d]) | (r[1] & ~EV[d]);
+        }
+      }
       if (row_ok) {
         if constexpr (MMA) {
-          // one FP8 E4M3 byte per code (sign, exponent 0, mantissa |q|: value q * 2^-9),
-          // [M][K] bytes, each 8-element block stored as its even elements then its odd
-          // ones (the order of the GEMM's own nibble expansion of the weights, which the
-          // two operands must share).  The clamp to +-7 only acts for subnormal fp16
-          // scales; code 0 may carry either sign bit.
-          uint32_t b[4];
-#pragma unroll
-          for (int d = 0; d < 4; ++d) {
-            const int e0 = (d >> 1) * 8 + (d & 1);
-            float v[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              v[j] = __builtin_amdgcn_fmed3f(t[e0 + 2 * j] * 0x1p-9f, -7.0f * 0x1p-9f, 7.0f * 0x1p-9f);
-            int w = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
-            w = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], w, true);
-            b[d] = (uint32_t)w;
-          }
-          *reinterpret_cast<uint4*>(qX + row * K + k0) = make_uint4(b[0], b[1], b[2], b[3]);
+          // [M][K/64][64] bytes per token and group: quarter q stores 16 bytes at 16 q,
+          // words 0-2 (quarter 2h) or 3-5 (quarter 2h+1) of half h, then a zero word
+          *reinterpret_cast<uint4*>(qX + row * K + k0) = make_uint4(fw[0], fw[1], fw[2], 0u);
         } else {
           uint32_t w0 = 0, w1 = 0;
 #pragma unroll
@@ -169,9 +178,9 @@ k1_quant_lora_down(const uint16_t* __restrict__ X, int64_t ldx, int64_t M, int64
           *reinterpret_cast<uint2*>(qX + row * (K >> 1) + (k0 >> 1)) = make_uint2(w0, w1);
         }
         if (sub == 0) {
-          if constexpr (MMA) {  // the value as fp32, rows padded to 4
+          if constexpr (MMA) {  // fp16 bits, rows padded to 4
             const int64_t Mp = (M + 3) & ~int64_t(3);
-            reinterpret_cast<float*>(sXv)[(int64_t)c * Mp + row] = sf;
+            reinterpret_cast<uint16_t*>(sXv)[(int64_t)c * Mp + row] = __builtin_bit_cast(uint16_t, sh);
           } else {
             reinterpret_cast<uint16_t*>(sXv)[(int64_t)c * M + row] = __builtin_bit_cast(uint16_t, sh);
           }

@@ -55,13 +55,14 @@ constexpr int TI = WM / 32, TJ = WN / 32;
 
 template <int FMT, int SUB>
 struct Smem {
-  // operand bytes per row and 64-wide sub-step: INT4 expands 32 code bytes to 64 FP8
+  // operand bytes per row and 64-wide sub-step: INT4 holds each 32-code half as its six
+  // FP6 operand words in two 16-byte slots (words 0-2 | pad, 3-5 | pad)
   static constexpr int kSub = FMT == 0 ? 64 : 32;
   static constexpr int kPitch = SUB * kSub + 16;
   // one stage's panels and scales
   struct Stage {
-    _Float16 m[FMT == 0 ? SUB : 1][BM + BN];  // INT4 scale mantissas: X rows, then W columns
-    uint32_t e[SUB][BM + BN];  // E8M0 bytes (MXFP4: the sub-step's two groups in bytes 0, 1)
+    uint16_t m[FMT == 0 ? SUB : 1][BM + BN];  // INT4 fp16 scale bits: X rows, then W columns
+    uint32_t e[FMT == 0 ? 1 : SUB][BM + BN];  // MXFP4 E8M0 bytes (the sub-step's two groups in bytes 0, 1)
     uint8_t A[BM * kPitch];
     uint8_t B[BN * kPitch];
   } st[2];
@@ -107,17 +108,16 @@ struct K2Sched {
 constexpr int PART_FLOATS = 16 * 16 * 64;
 static_assert(TI == 2 && TJ == 2, "the rescale schedules assume a 2 x 2 wave tile");
 
-// One stage's global loads of one thread: INT4 activation codes as FP8 bytes take two
-// 16-byte pieces per sub-step, 4-bit codes one.
+// One stage's global loads of one thread: 16-byte pieces of 4-bit codes.
 template <int SUB>
 struct Stage {
   uint4 a[2 * SUB], b[SUB];
   uint32_t s[SUB];
 };
 
-// The packed activation form: 4-bit codes [M][K/2] (INT4 nibbles are expanded to FP8
-// on the way into LDS), scales [K/G][M] (INT4 fp16, split into mantissa and E8M0 block
-// scale here), lora_act fp32 [M][R16]; prepared weights (INT4 scales fp32).
+// The packed activation form: 4-bit codes [M][K/2] (INT4 nibbles are converted to FP6
+// operand words on the way into LDS, the weights' prepared words expanded), scales
+// [K/G][M] (INT4 fp16), lora_act fp32 [M][R16]; prepared weights (INT4 scales fp16).
 template <int FMT, bool DEBUG, int SUB>
 __global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void k2_gemm(
     const uint8_t* __restrict__ qX, const void* __restrict__ sXv, int64_t M,
@@ -156,20 +156,19 @@ __global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 
   const __amdgpu_buffer_rsrc_t rA = make_rsrc(qX + m0 * Ka, (uint32_t)rowsA * Ka);
   const __amdgpu_buffer_rsrc_t rB = make_rsrc(qW + n0 * Kb, (uint32_t)rowsB * Kb);
   const int ng = FMT == 0 ? (int)(K >> 6) : (int)(K >> 5);  // scale groups along K
-  // INT4 scale words are 4 bytes, except the public path's fp16 activation scales
   // staging roles: thread t moves the pieces of row t & 127, half t >> 7, of the A and
   // the B panel, and one scale per sub-step: waves 0-1 of the X row t, waves 2-3 of the
   // W column t - 128.  The choice is wave-uniform, so it is made once, here.
   const bool xs = wave < 2;
   // scale rows: the activation scales have stride M, the prepared weight scales are
-  // padded to a multiple of 4; INT4: activation fp16, weight fp32
+  // padded to a multiple of 4; INT4: fp16, MXFP4: E8M0 bytes
   const uint32_t sstride = xs ? (uint32_t)M : (uint32_t)((N + 3) & ~int64_t(3));
-  const uint32_t ssz = FMT == 0 ? (xs ? 2u : 4u) : 1u;
+  const uint32_t ssz = FMT == 0 ? 2u : 1u;
   const __amdgpu_buffer_rsrc_t rS = make_rsrc(xs ? sXv : sWv, DEBUG ? 0u : (uint32_t)ng * sstride * ssz);
   const uint32_t sidx = xs ? (uint32_t)(m0 + tid) : (uint32_t)(n0 + tid - BM);
   const int ldrow = tid & 127, ldhalf = tid >> 7;
-  // this thread's part of a stage row: 4-bit code bytes [SUB*16*half, +SUB*16) (INT4
-  // FP8 activation bytes [SUB*32*half, +SUB*32)); in LDS, INT4 stores every code as a byte
+  // this thread's part of a stage row: 4-bit code bytes [SUB*16*half, +SUB*16); in LDS,
+  // INT4 takes 32 bytes per 32-code half (its FP6 operand words)
   const uint32_t offB = (uint32_t)ldrow * Kb + ldhalf * SUB * 16;
   const uint32_t offA = (uint32_t)ldrow * Ka + ldhalf * SUB * 16;
   const int ldsAB = ldrow * S::kPitch + ldhalf * SUB * (FMT == 0 ? 32 : 16);
@@ -189,7 +188,7 @@ __global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 
       if (DEBUG) {
         st.s[u] = 0;
       } else if (FMT == 0) {
-        st.s[u] = xs ? buf_load2(rS, (g * sstride + sidx) * 2) : buf_load4(rS, (g * sstride + sidx) * 4);
+        st.s[u] = buf_load2(rS, (g * sstride + sidx) * 2);
       } else {
         const uint32_t o0 = 2 * g * sstride + sidx;
         st.s[u] = buf_load1(rS, o0) | (buf_load1(rS, o0 + sstride) << 8);
@@ -202,20 +201,14 @@ __global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
     for (int v = 0; v < SUB; ++v) {
       if (FMT == 0) {
-        uint32_t a8[8], b8[8];
-        const uint32_t aw[4] = {st.a[v].x, st.a[v].y, st.a[v].z, st.a[v].w};
-        const uint32_t bw[4] = {st.b[v].x, st.b[v].y, st.b[v].z, st.b[v].w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          nib8_to_fp8(aw[i], a8[2 * i], a8[2 * i + 1]);
-          nib8p_to_fp8(bw[i], b8[2 * i], b8[2 * i + 1]);
-        }
+        const v6i fa = nib32_to_fp6(st.a[v]);
+        const v8i fb = expand_w6(st.b[v]);
         uint4* da = reinterpret_cast<uint4*>(A + v * 32);
         uint4* db = reinterpret_cast<uint4*>(B + v * 32);
-        da[0] = make_uint4(a8[0], a8[1], a8[2], a8[3]);
-        da[1] = make_uint4(a8[4], a8[5], a8[6], a8[7]);
-        db[0] = make_uint4(b8[0], b8[1], b8[2], b8[3]);
-        db[1] = make_uint4(b8[4], b8[5], b8[6], b8[7]);
+        da[0] = make_uint4(fa[0], fa[1], fa[2], 0u);
+        da[1] = make_uint4(fa[3], fa[4], fa[5], 0u);
+        db[0] = make_uint4(fb[0], fb[1], fb[2], 0u);
+        db[1] = make_uint4(fb[3], fb[4], fb[5], 0u);
       } else {
         *reinterpret_cast<uint4*>(A + v * 16) = st.a[v];
         *reinterpret_cast<uint4*>(B + v * 16) = st.b[v];
@@ -224,11 +217,7 @@ __global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
     for (int u = 0; u < SUB; ++u) {
       if (FMT == 0) {
-        uint32_t w;
-        if (DEBUG) w = 0x3C00u | ((127u + 9u) << 16);  // m = 1, 2^9
-        else w = xs ? split_scale_word(st.s[u]) : split_scale_f32(st.s[u]);
-        sm.st[buf].m[u][tid] = __builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
-        sm.st[buf].e[u][tid] = w >> 16;
+        sm.st[buf].m[u][tid] = (uint16_t)st.s[u];
       } else {
         sm.st[buf].e[u][tid] = st.s[u];
       }
@@ -246,16 +235,15 @@ __global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 
   auto compute = [&](int buf, int u, int g) {
     v8i bf[TJ], af[TI];
     uint32_t sb[TJ], sa[TI];
-    _Float16 mw[TJ];
 #pragma unroll
     for (int j = 0; j < TJ; ++j) {
       const int col = wn + j * 32 + l32;
       if (FMT == 0) {
         const uint4* p = reinterpret_cast<const uint4*>(&sm.st[buf].B[col * S::kPitch + u * 64 + kh * 32]);
         const uint4 x0 = p[0], x1 = p[1];
-        bf[j] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-        sb[j] = sm.st[buf].e[u][BM + col];
-        mw[j] = sm.st[buf].m[u][BM + col];
+        bf[j] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x1.x, (int)x1.y, (int)x1.z, 0, 0};
+        const uint32_t w = sm.st[buf].m[u][BM + col];
+        sb[j] = kh ? 0u : w;  // the column scale enters the scale product once (k = 0)
       } else {
         const uint4 x0 = *reinterpret_cast<const uint4*>(&sm.st[buf].B[col * S::kPitch + u * 32 + kh * 16]);
         bf[j] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, 0, 0, 0, 0};
@@ -268,8 +256,8 @@ __global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 
       if (FMT == 0) {
         const uint4* p = reinterpret_cast<const uint4*>(&sm.st[buf].A[row * S::kPitch + u * 64 + kh * 32]);
         const uint4 x0 = p[0], x1 = p[1];
-        af[i] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-        sa[i] = sm.st[buf].e[u][row];
+        af[i] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x1.x, (int)x1.y, (int)x1.z, 0, 0};
+        sa[i] = sm.st[buf].m[u][row];
       } else {
         const uint4 x0 = *reinterpret_cast<const uint4*>(&sm.st[buf].A[row * S::kPitch + u * 32 + kh * 16]);
         af[i] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, 0, 0, 0, 0};
@@ -277,54 +265,45 @@ __global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 
       }
     }
     if (FMT == 0) {
-      // two group-sum MFMAs in flight: tile t+1's MFMA is issued ahead of tile t's rescale
+      // FP6 codes q / 8 with block scales 2^3 on both sides: the exact integer group sum
       auto gs = [&](int i, int j) {
-        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], v16f{}, 0, 0, 0, (int)sa[i], 0,
-                                                               (int)sb[j]);
+        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], v16f{}, 2, 2, 0, 130, 0, 130);
       };
-      h2 mx[TI][8];
-#pragma unroll
-      for (int i = 0; i < TI; ++i)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint2 w = *reinterpret_cast<const uint2*>(&sm.st[buf].m[u][wm + i * 32 + 8 * q + 4 * kh]);
-          mx[i][2 * q] = __builtin_bit_cast(h2, w.x);
-          mx[i][2 * q + 1] = __builtin_bit_cast(h2, w.y);
-        }
-      auto epi = [&](int i, int j, const v16f& p) {
-        if (DEBUG) {
-#pragma unroll
-          for (int a = 0; a < 16; ++a) {
-            const int64_t r = m0 + wm + i * 32 + 8 * (a >> 2) + 4 * kh + (a & 3);
-            const int64_t c = n0 + wn + j * 32 + l32;
-            if (r < mlim && c < nlim)
-              dbg[((int64_t)g * (mlim - mbase) + (r - mbase)) * (nlim - nbase) + (c - nbase)] = (int32_t)p[a];
-          }
-        } else {
-          const h2 mw2 = h2{mw[j], mw[j]};
-#pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            const h2 sc = mx[i][q] * mw2;
-            acc[i][j][2 * q] = fmaf(p[2 * q], (float)sc.x, acc[i][j][2 * q]);
-            acc[i][j][2 * q + 1] = fmaf(p[2 * q + 1], (float)sc.y, acc[i][j][2 * q + 1]);
-          }
-        }
+      // c = sX sW for the tile, exact (see k2_stream)
+      auto sc = [&](int i, int j) {
+        const v4h a = __builtin_bit_cast(v4h, make_uint2(sa[i], 0u));
+        const v4h b = __builtin_bit_cast(v4h, make_uint2(sb[j], 0u));
+        return __builtin_amdgcn_mfma_f32_32x32x8f16(a, b, v16f{}, 0, 0, 0);
       };
-      v16f p0 = gs(0, 0);
-      v16f p1 = gs(0, 1);
-      epi(0, 0, p0);
-      p0 = gs(1, 0);
-      epi(0, 1, p1);
-      p1 = gs(1, 1);
-      epi(1, 0, p0);
-      epi(1, 1, p1);
-      if (!DEBUG) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 24, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 24, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 48, 0);
+      if (DEBUG) {
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+          for (int j = 0; j < TJ; ++j) {
+            const v16f p = gs(i, j);
+#pragma unroll
+            for (int a = 0; a < 16; ++a) {
+              const int64_t r = m0 + wm + i * 32 + 8 * (a >> 2) + 4 * kh + (a & 3);
+              const int64_t c = n0 + wn + j * 32 + l32;
+              if (r < mlim && c < nlim)
+                dbg[((int64_t)g * (mlim - mbase) + (r - mbase)) * (nlim - nbase) + (c - nbase)] = (int32_t)p[a];
+            }
+          }
+      } else {
+        auto epi = [&](int i, int j, const v16f& p, const v16f& c) {
+#pragma unroll
+          for (int a = 0; a < 16; ++a) acc[i][j][a] = fmaf(p[a], c[a], acc[i][j][a]);
+        };
+        v16f c0 = sc(0, 0), p0 = gs(0, 0);
+        v16f c1 = sc(0, 1), p1 = gs(0, 1);
+        epi(0, 0, p0, c0);
+        c0 = sc(1, 0);
+        p0 = gs(1, 0);
+        epi(0, 1, p1, c1);
+        c1 = sc(1, 1);
+        p1 = gs(1, 1);
+        epi(1, 0, p0, c0);
+        epi(1, 1, p1, c1);
       }
     } else {
 #pragma unroll
@@ -451,9 +430,9 @@ struct DLay {
   static constexpr int RB = 2 * 32;                     // B (4-bit) bytes per row
   static constexpr int B_OFF = BM * RA;
   static constexpr int S_OFF = B_OFF + BN * RB;
-  // scales of one sub-step: INT4 X [BM] fp32 | W [BN] fp32; MXFP4 X e [2][BM] | W e [2][BN]
+  // scales of one sub-step: INT4 X [BM] fp16 | W [BN] fp16; MXFP4 X e [2][BM] | W e [2][BN]
   // (the sub-step's two 32-groups); moved in 256-byte parts, one 4-byte load per lane
-  static constexpr int XB = FMT == 0 ? 4 * BM : 2 * BM, WB = FMT == 0 ? 4 * BN : 2 * BN;
+  static constexpr int XB = 2 * BM, WB = 2 * BN;
   static constexpr int S_SUB = XB + WB;
   static constexpr int XP = XB / 256, WP = WB / 256, SPARTS = 2 * (XP + WP);  // per stage
   static constexpr int NS = (SPARTS + NW - 1) / NW;  // scale loads per wave
@@ -535,8 +514,8 @@ __global__ __launch_bounds__(SShape<FMT>::NT, 8 / SShape<FMT>::NW) __attribute__
   const __amdgpu_buffer_rsrc_t rB = make_rsrc(qW + n0 * Kb, (uint32_t)rowsB * Kb);
   const uint32_t ng = FMT == 0 ? (uint32_t)(K >> 6) : (uint32_t)(K >> 5);
   const uint32_t Mp = (uint32_t)((M + 3) & ~int64_t(3)), Np = (uint32_t)((N + 3) & ~int64_t(3));
-  const __amdgpu_buffer_rsrc_t rSX = make_rsrc(sX, ng * Mp * (FMT == 0 ? 4 : 1));
-  const __amdgpu_buffer_rsrc_t rSW = make_rsrc(sW, ng * Np * (FMT == 0 ? 4 : 1));
+  const __amdgpu_buffer_rsrc_t rSX = make_rsrc(sX, ng * Mp * (FMT == 0 ? 2 : 1));
+  const __amdgpu_buffer_rsrc_t rSW = make_rsrc(sW, ng * Np * (FMT == 0 ? 2 : 1));
 
   // ---- loads of stage k into an LDS buffer (every wave issues D::NDW instructions) ------
   // Per-lane source offsets within a stage are fixed (chunk n of 1 KB covers rows
@@ -575,8 +554,8 @@ __global__ __launch_bounds__(SShape<FMT>::NT, 8 / SShape<FMT>::NW) __attribute__
       const uint32_t pitch = wside ? Np : Mp, org = wside ? (uint32_t)n0 : (uint32_t)m0;
       const uint32_t g = (uint32_t)(k * 2 + u);
       uint32_t off;
-      if (FMT == 0) {  // fp32 values of rows yp * 64 + lane
-        off = (g * pitch + org + (uint32_t)(yp * 64 + lane)) * 4;
+      if (FMT == 0) {  // fp16 values of rows yp * 128 + 2 lane, + 1
+        off = (g * pitch + org) * 2 + (uint32_t)(yp * 256 + lane * 4);
       } else {  // bytes [gi][row] of the [2][B] region: byte yp * 256 + 4 lane ..
         const int bpg = wside ? BN : BM;
         const int b0 = yp * 256 + lane * 4;
@@ -594,12 +573,11 @@ __global__ __launch_bounds__(SShape<FMT>::NT, 8 / SShape<FMT>::NW) __attribute__
 
   // ---- the fragments of one sub-step u of a stage, read from LDS --------------------------
   struct Frag {
-    uint4 a[TI][FMT == 0 ? 2 : 1];  // A: INT4 32 FP8 bytes, MXFP4 32 nibbles
+    uint4 a[TI][FMT == 0 ? 2 : 1];  // A: INT4 FP6 operand (words 0-2 | pad, 3-5 | pad), MXFP4 32 nibbles
     uint4 b[TJ];                    // B: 32 4-bit codes
-    uint32_t sa[TI], sb[TJ];        // MXFP4: E8M0 block scales
-    float sw[TJ];                   // INT4: the weight scale of the lane's column
+    uint32_t sa[TI], sb[TJ];        // MXFP4: E8M0 block scales; INT4: fp16 scale bits of the
+                                    // lane's row / column (the column's 0 in lanes 32-63)
   };
-  typedef float4 XS[TI][4];  // INT4: the activation scales of the lane's 16 rows of tile i
   auto load = [&](const uint8_t* base, int u, Frag& f) {
     const uint8_t* sb = base + D::S_OFF + u * D::S_SUB;
 #pragma unroll
@@ -608,7 +586,8 @@ __global__ __launch_bounds__(SShape<FMT>::NT, 8 / SShape<FMT>::NW) __attribute__
       const int ls = u * 2 + kh;  // 4-bit bytes u*32 + kh*16
       f.b[j] = *reinterpret_cast<const uint4*>(base + D::B_OFF + col * D::RB + ((ls ^ swz(col, D::RB / 16)) * 16));
       if constexpr (FMT == 0) {
-        f.sw[j] = reinterpret_cast<const float*>(sb + D::XB)[col];
+        const uint32_t w = reinterpret_cast<const uint16_t*>(sb + D::XB)[col];
+        f.sb[j] = kh ? 0u : w;
       } else {
         f.sb[j] = sb[D::XB + kh * BN + col];
       }
@@ -617,10 +596,11 @@ __global__ __launch_bounds__(SShape<FMT>::NT, 8 / SShape<FMT>::NW) __attribute__
     for (int i = 0; i < TI; ++i) {
       const int row = wm + i * 32 + l32;
       if constexpr (FMT == 0) {
-        const int ls0 = u * 4 + kh * 2;  // FP8 bytes u*64 + kh*32, two slots
+        const int ls0 = u * 4 + kh * 2;  // operand half kh of sub-step u: bytes u*64 + kh*32, two slots
         const int sw = swz(row, D::RA / 16);
         f.a[i][0] = *reinterpret_cast<const uint4*>(base + row * D::RA + ((ls0 ^ sw) * 16));
         f.a[i][1] = *reinterpret_cast<const uint4*>(base + row * D::RA + (((ls0 + 1) ^ sw) * 16));
+        f.sa[i] = reinterpret_cast<const uint16_t*>(sb)[row];
       } else {
         const int ls = u * 2 + kh;
         f.a[i][0] = *reinterpret_cast<const uint4*>(base + row * D::RA + ((ls ^ swz(row, D::RA / 16)) * 16));
@@ -629,43 +609,31 @@ __global__ __launch_bounds__(SShape<FMT>::NT, 8 / SShape<FMT>::NW) __attribute__
     }
   };
 
-  // rows 8 q + 4 kh .. +3 of tile i: accumulator a of the lane is row 8 (a >> 2) + 4 kh + (a & 3)
-  auto load_xs = [&](const uint8_t* base, int u, XS& xs) {
-    const float* sx = reinterpret_cast<const float*>(base + D::S_OFF + u * D::S_SUB);
-#pragma unroll
-    for (int i = 0; i < TI; ++i)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) xs[i][q] = *reinterpret_cast<const float4*>(&sx[wm + i * 32 + 8 * q + 4 * kh]);
-  };
-
-  // ---- INT4: weight expansion, group-sum MFMA, rescale ----------------------------------
+  // ---- INT4: weight expansion, group-sum MFMA, scale products, rescale -------------------
   auto expand = [&](const Frag& f, v8i (&bf)[TJ]) {
 #pragma unroll
-    for (int j = 0; j < TJ; ++j) {
-      uint32_t w8[8];
-      const uint32_t xw[4] = {f.b[j].x, f.b[j].y, f.b[j].z, f.b[j].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) nib8p_to_fp8(xw[e], w8[2 * e], w8[2 * e + 1]);
-      bf[j] = v8i{(int)w8[0], (int)w8[1], (int)w8[2], (int)w8[3], (int)w8[4], (int)w8[5], (int)w8[6], (int)w8[7]};
-    }
+    for (int j = 0; j < TJ; ++j) bf[j] = expand_w6(f.b[j]);
   };
-  // both block scales 2^9 (E8M0 byte 136): FP8 code q is q * 2^-9, so the MFMA returns
-  // the exact integer group sum
+  // FP6 code q is q / 8 and both block scales are 2^3 (E8M0 byte 130), so the MFMA
+  // returns the exact integer group sum I
   auto gs = [&](const Frag& f, const v8i (&bf)[TJ], int i, int j) {
     const uint4 x0 = f.a[i][0], x1 = f.a[i][FMT == 0 ? 1 : 0];
-    const v8i af = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf[j], v16f{}, 0, 0, 0, 136, 0, 136);
+    const v8i af = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x1.x, (int)x1.y, (int)x1.z, 0, 0};
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf[j], v16f{}, 2, 2, 0, 130, 0, 130);
   };
-  // acc += (I * sW) * sX: I * sW is exact (12 + 11 significant bits), one rounding per
-  // group in the fma
-  auto epi = [&](const Frag& f, const XS& xs, int i, int j, const v16f& p) {
+  // c = sX sW for the 32 x 32 tile: an fp16 MFMA whose only nonzero k term is the pair of
+  // scales (k = 0 in lanes 0-31; the column scale is 0 in lanes 32-63), so every
+  // product is exact in fp32 (11 + 11 significant bits) and c has the accumulator layout
+  auto sc = [&](const Frag& f, int i, int j) {
+    const v4h a = __builtin_bit_cast(v4h, make_uint2(f.sa[i], 0u));
+    const v4h b = __builtin_bit_cast(v4h, make_uint2(f.sb[j], 0u));
+    return __builtin_amdgcn_mfma_f32_32x32x8f16(a, b, v16f{}, 0, 0, 0);
+  };
+  // acc += I * c: one rounding per group, the same value as (I * sW) * sX with the exact
+  // product I * sW
+  auto epi = [&](int i, int j, const v16f& p, const v16f& c) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      acc[i][j][4 * q] = fmaf(p[4 * q] * f.sw[j], xs[i][q].x, acc[i][j][4 * q]);
-      acc[i][j][4 * q + 1] = fmaf(p[4 * q + 1] * f.sw[j], xs[i][q].y, acc[i][j][4 * q + 1]);
-      acc[i][j][4 * q + 2] = fmaf(p[4 * q + 2] * f.sw[j], xs[i][q].z, acc[i][j][4 * q + 2]);
-      acc[i][j][4 * q + 3] = fmaf(p[4 * q + 3] * f.sw[j], xs[i][q].w, acc[i][j][4 * q + 3]);
-    }
+    for (int a = 0; a < 16; ++a) acc[i][j][a] = fmaf(p[a], c[a], acc[i][j][a]);
   };
   // ---- MXFP4: the MFMA accumulates the block-scaled products directly ---------------------
   auto mma4 = [&](const Frag& f) {
@@ -697,17 +665,18 @@ __global__ __launch_bounds__(SShape<FMT>::NT, 8 / SShape<FMT>::NW) __attribute__
       load(cur, u, F);
       if constexpr (FMT == 0) {
         v8i bf[TJ];
-        XS mx;
-        load_xs(cur, u, mx);
         expand(F, bf);
-        v16f p0 = gs(F, bf, 0, 0);
-        v16f p1 = gs(F, bf, 0, 1);
-        epi(F, mx, 0, 0, p0);
+        // two tiles in flight: tile t+1's MFMAs are issued ahead of tile t's rescale
+        v16f c0 = sc(F, 0, 0), p0 = gs(F, bf, 0, 0);
+        v16f c1 = sc(F, 0, 1), p1 = gs(F, bf, 0, 1);
+        epi(0, 0, p0, c0);
+        c0 = sc(F, 1, 0);
         p0 = gs(F, bf, 1, 0);
-        epi(F, mx, 0, 1, p1);
+        epi(0, 1, p1, c1);
+        c1 = sc(F, 1, 1);
         p1 = gs(F, bf, 1, 1);
-        epi(F, mx, 1, 0, p0);
-        epi(F, mx, 1, 1, p1);
+        epi(1, 0, p0, c0);
+        epi(1, 1, p1, c1);
       } else {
         mma4(F);
       }

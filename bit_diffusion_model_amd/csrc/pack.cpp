@@ -643,7 +643,6 @@ svdq_status svdq_prepare_weights(int64_t K, int64_t N, int32_t fmt, const uint8_
   svdq_status st = check_dims(K, N, fmt);
   if (st != SVDQ_OK) return st;
   if (!qW || !sW || !qW_out || !sW_out) return fail(SVDQ_EINVAL, "required pointer is NULL");
-  const int64_t words = N * (K / 8);
   const int64_t groups = K / group_of(fmt);
   const int64_t Np = (N + 3) / 4 * 4;  // scale rows padded to 4 bytes (fp16 rows: 8)
   if (fmt == SVDQ_MXFP4_G32) {
@@ -654,30 +653,41 @@ svdq_status svdq_prepare_weights(int64_t K, int64_t N, int32_t fmt, const uint8_
       for (int64_t n = 0; n < Np; ++n) o8[g * Np + n] = n < N ? s8[g * N + n] : (uint8_t)127;
     return ok();
   }
-  // codes: per 32-bit word (8 codes, code 2j in the low nibble of byte j), byte j of the
-  // output holds code 2j's magnitude in bits 0-2 and sign in bit 7, code 2j+1's
-  // magnitude in bits 4-6, and in bit 3 the sign of code 2j-1 (mod 8)
-  for (int64_t w = 0; w < words; ++w) {
-    uint32_t d;
-    std::memcpy(&d, qW + 4 * w, 4);
-    uint32_t o = 0;
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t lo = (d >> (8 * j)) & 0xF, hi = (d >> (8 * j + 4)) & 0xF;
-      const uint32_t hi_prev = (d >> (8 * ((j + 3) & 3) + 4)) & 0xF;
-      const uint32_t b = (lo & 7) | ((lo & 8) << 4) | ((hi & 7) << 4) | (hi_prev & 8);
-      o |= b << (8 * j);
+  // codes: kernel 2 multiplies INT4 codes as FP6 E2M3 values q / 8 (sign bit 5,
+  // exponent 0, mantissa |q|).  A matrix-core operand half holds the 32 codes of one
+  // group half as 6-bit fields at bit 6f of six words; field f carries k = 16 (f & 1) +
+  // (f >> 1) of the half (the order kernel 1's converter produces).  Bits 3-4 of every
+  // field are zero, and the info bits of words 2 and 5 sit exactly on the zero bits of
+  // words 0, 1 and 3, 4, so the 32 codes are stored in four words w0..w3:
+  //   w0 = f0 | (f2 & Z0), w1 = f1 | (f2 & Z1), w2 = f3 | (f5 & Z0), w3 = f4 | (f5 & Z1)
+  // and expanded with masks alone (f0 = w0 & ~Z0, f2 = (w0 & Z0) | (w1 & Z1), ...).
+  const uint32_t Z0 = (3u << 3) | (3u << 9) | (3u << 15) | (3u << 21) | (3u << 27);
+  const uint32_t Z1 = (3u << 1) | (3u << 7) | (3u << 13) | (3u << 19) | (3u << 25) | (1u << 31);
+  const int64_t rowb = K / 2;
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t h0 = 0; h0 < K; h0 += 32) {  // one group half: codes h0 .. h0 + 31
+      const uint8_t* src = qW + n * rowb + h0 / 2;
+      uint32_t f[6] = {0, 0, 0, 0, 0, 0};
+      for (int fi = 0; fi < 32; ++fi) {
+        const int k = 16 * (fi & 1) + (fi >> 1);
+        const uint32_t nib = (src[k >> 1] >> (4 * (k & 1))) & 0xFu;
+        const uint32_t v = (nib & 7u) | ((nib & 8u) << 2);  // sign bit 3 -> field bit 5
+        const uint64_t sh = (uint64_t)v << ((6 * fi) & 31);
+        f[(6 * fi) >> 5] |= (uint32_t)sh;
+        if ((6 * fi & 31) > 26) f[((6 * fi) >> 5) + 1] |= (uint32_t)(sh >> 32);
+      }
+      const uint32_t w[4] = {f[0] | (f[2] & Z0), f[1] | (f[2] & Z1), f[3] | (f[5] & Z0), f[4] | (f[5] & Z1)};
+      std::memcpy(qW_out + n * rowb + h0 / 2, w, 16);
     }
-    std::memcpy(qW_out + 4 * w, &o, 4);
-  }
-  // scales: the fp16 value as fp32 (exact), [groups][Np], padding 0
+  // scales: the fp16 bits, [groups][Np], padding 0
   const uint16_t* s16 = static_cast<const uint16_t*>(sW);
-  float* of = static_cast<float*>(sW_out);
+  uint16_t* o16 = static_cast<uint16_t*>(sW_out);
   for (int64_t g = 0; g < groups; ++g)
     for (int64_t n = 0; n < Np; ++n) {
       const uint16_t h = n < N ? s16[g * N + n] : (uint16_t)0;
       if (h & 0x8000u) return fail(SVDQ_ENUMERIC, "negative weight scale");
       if (((h >> 10) & 0x1F) == 0x1F) return fail(SVDQ_ENUMERIC, "non-finite weight scale");
-      of[g * Np + n] = (float)f16_to_double(h);
+      o16[g * Np + n] = h;
     }
   return ok();
 }

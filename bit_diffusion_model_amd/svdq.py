@@ -180,12 +180,12 @@ def pad4(n: int) -> int:
 
 
 def prepare_weights(K: int, N: int, fmt: int, qW: np.ndarray, sW: np.ndarray):
-    """Kernel layout of the residual weights: (qW [N][K/2] u8, sW bytes: INT4 fp32
+    """Kernel layout of the residual weights: (qW [N][K/2] u8, sW bytes: INT4 fp16
     [K/64][Np]; MXFP4 E8M0 [K/32][Np]; Np = N rounded up to 4)."""
     qW = np.ascontiguousarray(qW, dtype=np.uint8)
     sW = np.ascontiguousarray(sW)
     qo = np.empty_like(qW)
-    so = np.empty((K // GROUP[fmt]) * pad4(N) * (4 if fmt == INT4_G64 else 1), np.uint8)
+    so = np.empty((K // GROUP[fmt]) * pad4(N) * (2 if fmt == INT4_G64 else 1), np.uint8)
     _check(lib().svdq_prepare_weights(K, N, fmt, _ptr(qW), _ptr(sW), _ptr(qo), _ptr(so)))
     return qo, so
 
@@ -257,10 +257,10 @@ class PackedLinear:
     def alloc_act(self, M: int, form: int = ACT_PACKED):
         """Device buffers for kernel 1's outputs in the given activation form."""
         torch = _torch()
-        mma8 = form == ACT_MMA and self.fmt == INT4_G64
-        qX = torch.empty((M, self.K if mma8 else self.K // 2), dtype=torch.uint8, device=self.device)
-        if form == ACT_MMA:  # scales with rows padded to 4: INT4 fp32, MXFP4 E8M0 bytes
-            sX = torch.empty((self.K // self.group) * pad4(M) * (4 if mma8 else 1), dtype=torch.uint8,
+        mma6 = form == ACT_MMA and self.fmt == INT4_G64
+        qX = torch.empty((M, self.K if mma6 else self.K // 2), dtype=torch.uint8, device=self.device)
+        if form == ACT_MMA:  # scales with rows padded to 4: INT4 fp16, MXFP4 E8M0 bytes
+            sX = torch.empty((self.K // self.group) * pad4(M) * (2 if mma6 else 1), dtype=torch.uint8,
                              device=self.device)
         else:
             sdt = torch.int16 if self.fmt == INT4_G64 else torch.uint8

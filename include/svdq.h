@@ -62,9 +62,12 @@ typedef enum { SVDQ_F32 = 0, SVDQ_BF16 = 1 } svdq_dtype;
  *           lora_act [M][R16] fp32.
  *   MMA:    the matrix-core operand form, which kernel 2 streams into LDS without
  *           converting.  Mp = M rounded up to a multiple of 4.
- *           INT4: qX [M][K] one FP8 E4M3 byte per code (sign bit 7, magnitude in the
- *           mantissa bits: value q * 2^-9), each 8-code block stored as codes
- *           0,2,4,6,1,3,5,7; sX [K/64][Mp] fp32: the fp16 scale values.
+ *           INT4: qX [M][K] bytes, 64 per token and group: the codes as matrix-core
+ *           FP6 E2M3 operands, 6-bit fields sign << 5 | |q| (exponent 0: value q / 8).
+ *           Group half h (32 codes) is six 32-bit words w0..w5 holding field f at bit
+ *           6 f of their 192-bit concatenation, field f carrying k = 32 h + 16 (f & 1)
+ *           + (f >> 1) of the group; it is stored at byte 32 h as [w0 w1 w2 0 w3 w4 w5
+ *           0]; sX [K/64][Mp] fp16 bits.
  *           MXFP4: qX as PACKED; sX [K/32][Mp] E8M0 bytes.
  *           Both: lora_act rows of 2*R16 bf16, [R16 hi][R16 lo] with hi = bf16(v),
  *           lo = bf16(v - hi) of the fp32 value v. */
@@ -83,7 +86,7 @@ typedef enum { SVDQ_ACT_PACKED = 0, SVDQ_ACT_MMA = 1 } svdq_act_form;
  *   qW     [N][K/2]   u8    residual codes, row n = output channel n along K, in the
  *                           kernel bit order of svdq_prepare_weights
  *   sW                group-major scales as svdq_prepare_weights writes them: INT4
- *                           fp32, MXFP4 E8M0 bytes, rows padded to Np (16-byte aligned)
+ *                           fp16, MXFP4 E8M0 bytes, rows padded to Np (16-byte aligned)
  * L1t/L2t may be NULL iff rank == 0. */
 typedef struct svdq_layer {
   int64_t K, N;
@@ -158,13 +161,16 @@ svdq_status svdq_prepare_lowrank(int64_t N, int32_t rank, const uint16_t* L2, ui
  * of svdq_pack_weights / svdq_quantize_weights; only their encoding changes.  Np = N
  * rounded up to a multiple of 4; scale rows are padded to it.
  *   MXFP4: qW_out = qW; sW_out [K/32][Np] E8M0 bytes (padding 127).
- *   INT4:  qW_out [N][K/2]: each 32-bit word of 8 sign-magnitude codes (code 2j in the
- *          low nibble of byte j) is re-encoded so that byte j holds code 2j's magnitude
- *          in bits 0-2 and sign in bit 7, code 2j+1's magnitude in bits 4-6, and in bit 3
- *          the sign of code 2j-1 (indices mod 8): a mask then yields the even codes and
- *          a 4-bit rotate plus the same mask the odd ones, as FP8 E4M3 bytes q * 2^-9.
- *          sW_out: the fp16 scales as fp32 values [K/64][Np] ((K/64) * Np * 4 bytes),
- *          padding 0.
+ *   INT4:  qW_out [N][K/2]: each 16 bytes of a row (32 codes, a group half) become
+ *          four words v0..v3 from which masks alone give the half's six FP6 operand
+ *          words w0..w5 (fields and k order as in the MMA activation form below):
+ *          with Z0 = the bits 3-4 of fields 0-4 (0x18618618) and Z1 = bits 1-2, 7-8,
+ *          13-14, 19-20, 25-26 and 31 (0x86186186),
+ *            v0 = w0 | (w2 & Z0), v1 = w1 | (w2 & Z1), v2 = w3 | (w5 & Z0),
+ *            v3 = w4 | (w5 & Z1);
+ *          w0 = v0 & ~Z0, w1 = v1 & ~Z1, w2 = (v0 & Z0) | (v1 & Z1) (w3..w5 likewise),
+ *          since every field has zero exponent bits (bits 3-4).
+ *          sW_out: the fp16 scale bits [K/64][Np] ((K/64) * Np * 2 bytes), padding 0.
  * EINVAL on bad sizes, ENUMERIC on a negative or non-finite scale. */
 svdq_status svdq_prepare_weights(int64_t K, int64_t N, int32_t fmt, const uint8_t* qW,
                                  const void* sW, uint8_t* qW_out, void* sW_out);

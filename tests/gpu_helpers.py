@@ -68,26 +68,43 @@ def bf16_rne_bits(v32):
     return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
 
 
+def _fp6_fields(words6):
+    """[..., 6] uint32 words -> [..., 32] 6-bit fields (field f at bit 6 f)."""
+    w = words6.astype(np.uint64)
+    out = np.empty(words6.shape[:-1] + (32,), np.int64)
+    for f in range(32):
+        b, o = divmod(6 * f, 32)
+        v = w[..., b] >> np.uint64(o)
+        if o > 26:
+            v = v | (w[..., b + 1] << np.uint64(32 - o))
+        out[..., f] = (v & np.uint64(63)).astype(np.int64)
+    return out
+
+
 def decode_mma(qX, sX, la, fmt, K, rank):
     """Kernel 1's MMA-form outputs (device tensors) decoded per the header's description:
-    INT4 codes from FP8 bytes (sign bit 7, magnitude bits 0-2; 8-code blocks stored as
-    codes 0,2,4,6,1,3,5,7) and fp32 scale values (rows padded to Mp); MXFP4 codes as
-    stored and E8M0 bytes
-    (rows padded to Mp); lora_act rows [R16 hi][R16 lo] bf16.  Returns (codes or packed
-    bytes, scales (float64 values [K/64][M] for INT4, bytes [K/32][M] for MXFP4), hi bits,
-    lo bits)."""
+    INT4: per token and group 64 bytes, half h at byte 32 h as words [f0 f1 f2 0 f3 f4 f5
+    0]; the 192-bit f0..f5 hold 6-bit E2M3 fields (sign bit 5, exponent 0, |q| in bits
+    0-2), field f carrying k = 32 h + 16 (f & 1) + (f >> 1); fp16 scale bits [K/64][Mp].
+    MXFP4: codes as stored and E8M0 bytes [K/32][Mp].  lora_act rows [R16 hi][R16 lo]
+    bf16.  Returns (codes or packed bytes, scales (float64 values [K/64][M] for INT4,
+    bytes [K/32][M] for MXFP4), hi bits, lo bits)."""
     q = qX.cpu().numpy()
     M = q.shape[0]
     Mp = (M + 3) // 4 * 4
-    sb = sX.cpu().numpy().view(np.uint8).reshape(-1)
+    sb = None if sX is None else sX.cpu().numpy().view(np.uint8).reshape(-1)
     if fmt == "int4":
-        b = q.reshape(M, K // 8, 8).astype(np.int64)
-        v = (b & 7) * np.where(b & 0x80, -1, 1)
-        assert not (b & 0x78).any()
-        codes = np.empty_like(v)
-        codes[:, :, 0::2], codes[:, :, 1::2] = v[:, :, :4], v[:, :, 4:]
         G = K // 64
-        out = codes.reshape(M, K), sb[:G * Mp * 4].view(np.float32).reshape(G, Mp)[:, :M].astype(np.float64)
+        w = np.ascontiguousarray(q).view("<u4").reshape(M, G, 2, 8)
+        assert not w[..., 3].any() and not w[..., 7].any(), "padding words must be zero"
+        fl = _fp6_fields(w[..., [0, 1, 2, 4, 5, 6]])
+        assert not (fl & 0b011000).any(), "nonzero E2M3 exponent bits"
+        v = (fl & 7) * np.where(fl & 32, -1, 1)
+        kk = np.array([16 * (f & 1) + (f >> 1) for f in range(32)])
+        codes = np.empty_like(v)
+        codes[..., kk] = v
+        sv = None if sX is None else sb[:G * Mp * 2].view(np.float16).reshape(G, Mp)[:, :M].astype(np.float64)
+        out = codes.reshape(M, K), sv
     else:
         out = q, sb[:(K // 32) * Mp].reshape(K // 32, Mp)[:, :M]
     hi = lo = None

@@ -104,14 +104,10 @@ def test_forward_matches_oracle(shape):
     log(f"  max|err|/RMS = {e:.3e}")
     assert e <= TOL_Y
     if fmt == "int4":
-        # the forward path keeps the activation codes as FP8 E4M3 bytes (sign bit 7,
-        # magnitude in the mantissa bits), each 8-element block as even then odd elements
-        b = ws[:M * K].cpu().numpy().reshape(M, K // 8, 8)
-        q = (b & 7).astype(np.int64) * np.where(b & 0x80, -1, 1)
-        assert not (b & 0x78).any()
-        codes = np.empty_like(q)
-        codes[:, :, 0::2], codes[:, :, 1::2] = q[:, :, :4], q[:, :, 4:]
-        np.testing.assert_array_equal(codes.reshape(M, K), oforward.quantize_activations(wl.X, p["inv_s32"], fmt)[1])
+        # the forward path keeps the activation codes in MMA form (FP6 operand words) at
+        # the start of its workspace
+        codes = decode_mma(ws[:M * K].view(M, K), None, None, "int4", K, 0)[0]
+        np.testing.assert_array_equal(codes, oforward.quantize_activations(wl.X, p["inv_s32"], fmt)[1])
     # the two kernels called separately in MMA form, kernel 2 with its split workspace,
     # give the same bits as the forward; without the workspace (no split) the same bar
     X = to_dev_bf16(wl.X)

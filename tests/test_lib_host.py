@@ -143,11 +143,40 @@ def test_prepare_lowrank_layouts():
     assert not L2t[:, 5:].any()
 
 
+def fp6_fields(words6):
+    """[..., 6] uint32 words -> [..., 32] 6-bit fields, field f at bit 6 f of the 192-bit
+    little-endian concatenation."""
+    w = words6.astype(np.uint64)
+    out = np.empty(words6.shape[:-1] + (32,), np.int64)
+    for f in range(32):
+        b, o = divmod(6 * f, 32)
+        v = w[..., b] >> np.uint64(o)
+        if o > 26:
+            v = v | (w[..., b + 1] << np.uint64(32 - o))
+        out[..., f] = (v & np.uint64(63)).astype(np.int64)
+    return out
+
+
+def fp6_codes(fields):
+    """E2M3 fields with a zero exponent (sign bit 5, |q| in bits 0-2) -> codes q, in k
+    order: field f of a half carries k = 16 (f & 1) + (f >> 1)."""
+    assert not (fields & 0b011000).any(), "nonzero exponent bits"
+    v = (fields & 7) * np.where(fields & 32, -1, 1)
+    k = np.array([16 * (f & 1) + (f >> 1) for f in range(32)])
+    out = np.empty_like(v)
+    out[..., k] = v
+    return out
+
+
+Z0 = sum(3 << b for b in (3, 9, 15, 21, 27))
+Z1 = sum(3 << b for b in (1, 7, 13, 19, 25)) | (1 << 31)
+
+
 def test_prepare_weights_kernel_layout():
-    """The kernel layout decodes back to the oracle's codes and scales: even codes by the
-    mask 0x87, odd codes by a 4-bit rotate of the word and the same mask (FP8 E4M3 bytes
-    with zero exponent: magnitude in bits 0-2, sign in bit 7); the scales are the fp16
-    values as fp32 [K/64][Np], padded rows 0."""
+    """The kernel layout decodes back to the oracle's codes and scales: per 32-code group
+    half four words w0..w3 give the six FP6 operand words f0 = w0 & ~Z0, f1 = w1 & ~Z1,
+    f2 = (w0 & Z0) | (w1 & Z1) (f3..f5 likewise from w2, w3), whose fields are the codes
+    as E2M3 values q / 8; the scales are the fp16 bits [K/64][Np], padded rows 0."""
     rng = np.random.default_rng(11)
     K, N = 256, 39  # N not a multiple of 4: padded scale rows
     R = (rng.standard_normal((K, N)) * 10.0 ** rng.uniform(-9, 2, (1, N))).astype(np.float32)
@@ -157,19 +186,15 @@ def test_prepare_weights_kernel_layout():
     qW = opack.pack_codes(codes, "int4")
     assert (sc.view(np.uint16) & 0x7C00 == 0).any(), "want subnormal fp16 scales in the case"
     qk, sk = svdq.prepare_weights(K, N, svdq.INT4_G64, qW, sc)
-    words = qk.view("<u4").astype(np.uint64)
-    rot = ((words >> 4) | (words << 28)) & 0xFFFFFFFF
-    dec = np.empty((N, K // 8, 8), np.int64)
-    for src, off in ((words, 0), (rot, 1)):
-        for j in range(4):
-            b = (src >> (8 * j)) & 0x87
-            dec[:, :, 2 * j + off] = ((b & 7) * np.where(b & 0x80, -1, 1)).reshape(N, K // 8)
-    np.testing.assert_array_equal(dec.reshape(N, K), codes)
+    w = qk.view("<u4").reshape(N, K // 32, 4)
+    f = np.stack([w[..., 0] & ~np.uint32(Z0), w[..., 1] & ~np.uint32(Z1), (w[..., 0] & Z0) | (w[..., 1] & Z1),
+                  w[..., 2] & ~np.uint32(Z0), w[..., 3] & ~np.uint32(Z1), (w[..., 2] & Z0) | (w[..., 3] & Z1)], -1)
+    np.testing.assert_array_equal(fp6_codes(fp6_fields(f)).reshape(N, K), codes)
     Np = (N + 3) // 4 * 4
     G = K // 64
-    assert sk.size == G * Np * 4
-    sv = sk.view(np.float32).reshape(G, Np)
-    np.testing.assert_array_equal(sv[:, :N], sc.view(np.float16).astype(np.float32))
+    assert sk.size == G * Np * 2
+    sv = sk.view(np.uint16).reshape(G, Np)
+    np.testing.assert_array_equal(sv[:, :N], sc.view(np.uint16))
     assert not sv[:, N:].any()
     c4, s4 = opack.quantize_residual(R, "mxfp4")
     qf, sf = svdq.prepare_weights(K, N, svdq.MXFP4_G32, opack.pack_codes(c4, "mxfp4"), s4)
@@ -226,6 +251,6 @@ def test_device_entry_points_validate_on_host():
     assert L.svdq_gemm_w4a4_lora_up(ref, 4, 0, 16, 16, 16, 16, 64, 0, 8, 1 << 20, None) == 1 and "workspace" in _err()
     assert L.svdq_linear_forward(ref, 4, 16, 256, 16, 64, 0, 256, 10, None) == 1 and "workspace" in _err()
     assert L.svdq_debug_group_sums(ref, 4, 16, 0, 0, 5, 4, 16, None) == 1 and "window" in _err()
-    # MMA form: FP8 codes (M*K bytes), fp32 scales (4 bytes per group and row), 2*R16
-    # bf16 per row
-    assert L.svdq_workspace_bytes(ref, 100) >= 100 * 256 + 4 * 100 * 4 + 100 * 16 * 4
+    # MMA form: FP6 operand words (M*K bytes), fp16 scales (2 bytes per group and row),
+    # 2*R16 bf16 per row
+    assert L.svdq_workspace_bytes(ref, 100) >= 100 * 256 + 4 * 100 * 2 + 100 * 16 * 4
