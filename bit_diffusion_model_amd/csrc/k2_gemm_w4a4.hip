@@ -686,16 +686,9 @@ __global__ __launch_bounds__(SShape<FMT>::NT, 8 / SShape<FMT>::NW) __attribute__
   int k = kbeg;
   issue(kbeg, lds0);
   issue(kbeg + 1 < kend ? kbeg + 1 : kend - 1, lds1);
-  for (; k + 3 <= kend; k += 3) {
-    stage(k, lds0, lds2);
-    stage(k + 1, lds1, lds0);
-    stage(k + 2, lds2, lds1);
-  }
-  if (nk % 3 >= 1) stage(k, lds0, lds2);
-  if (nk % 3 == 2) stage(k + 1, lds1, lds0);
-  wait_cnt<0, 0>();
-
-  // ---- low-rank up projection: acc += lora_act[rows, :] L2[:, cols] ----------------------
+  // ---- low-rank up projection first: acc = lora_act[rows, :] L2[:, cols] ----------------
+  // It depends on nothing of the main loop, so it runs while the first two stages' loads
+  // are in flight (its own loads queue behind them) instead of after the last stage.
   // v_mfma_f32_32x32x16_bf16 on lora_act's bf16 hi/lo rows ([M][R16 hi | R16 lo]) and L2t
   // [N][R16]; rows past M / columns past N read zeros through the range check.
   if (rank > 0 && part <= 0) {
@@ -720,6 +713,15 @@ __global__ __launch_bounds__(SShape<FMT>::NT, 8 / SShape<FMT>::NW) __attribute__
       }
     }
   }
+
+  for (; k + 3 <= kend; k += 3) {
+    stage(k, lds0, lds2);
+    stage(k + 1, lds1, lds0);
+    stage(k + 2, lds2, lds1);
+  }
+  if (nk % 3 >= 1) stage(k, lds0, lds2);
+  if (nk % 3 == 2) stage(k + 1, lds1, lds0);
+  wait_cnt<0, 0>();
 
   // ---- store (or the partial tile) ------------------------------------------------------
   if (part < 0) {
