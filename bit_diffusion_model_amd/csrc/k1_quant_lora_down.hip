@@ -9,8 +9,8 @@
 // Figure 6(b)).  Activation scales are computed online (ch3chohch3 post, "量化方案").
 //
 // Work split: a block of 8 waves owns 16 consecutive tokens.  The K dimension is cut
-// into 64-wide chunks; wave w takes chunks w, w+8, ..., with the next chunk's X and
-// inv_s loads issued before the current chunk is processed.  Inside a chunk, lane l holds
+// into 64-wide chunks; wave w takes chunks w, w+8, ..., with the next chunk's X, inv_s
+// and L1 loads issued before the current chunk is processed.  Inside a chunk, lane l holds
 // token (l & 15) and the 16 consecutive channels 16 * (l >> 4) .. +15 (two 16-byte
 // loads of X).  One INT4 group (64) is therefore spread over the 4 lanes l, l^16,
 // l^32, l^48; one FP4 group (32) over lanes l, l^16.
@@ -76,41 +76,57 @@ k1_quant_lora_down(const uint16_t* __restrict__ X, int64_t ldx, int64_t M, int64
 #pragma unroll
   for (int t = 0; t < (NT > 0 ? NT : 1); ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  uint4 xa, xb, s0, s1, s2, s3;  // the current chunk's X and inv_s, loaded one chunk ahead
+  // One chunk ahead: X, the lane's own inv_s element (channel sub * 16 + r16: the 16
+  // lanes of a row hold the row's 16 channels, broadcast to the row where they are
+  // used) and the L1 fragments (rows past the rank read as zeros).
+  uint4 xa, xb, LAn[NT > 0 ? NT : 1], LBn[NT > 0 ? NT : 1];
+  uint32_t sv;
   auto fetch = [&](int c) {
     const uint32_t kx = xoff + (uint32_t)c * 128;
     xa = buf_load16(rX, kx);
     xb = buf_load16(rX, kx + 16);
-    const uint32_t ks = (uint32_t)(c * 64 + sub * 16) * 4;
-    s0 = buf_load16(rS, ks);
-    s1 = buf_load16(rS, ks + 16);
-    s2 = buf_load16(rS, ks + 32);
-    s3 = buf_load16(rS, ks + 48);
+    sv = buf_load4(rS, (uint32_t)(c * 64 + sub * 16 + r16) * 4);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const uint32_t o = (uint32_t)((t * 16 + r16) * K + (int64_t)c * 64 + sub * 16) * 2;
+      LAn[t] = buf_load16(rL, o);
+      LBn[t] = buf_load16(rL, o + 16);
+    }
   };
   if (wave < nchunks) fetch(wave);
 
   for (int c = wave; c < nchunks; c += K1_WAVES) {
     const int64_t k0 = (int64_t)c * 64 + sub * 16;
     const uint32_t xw[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
-    const uint32_t sw[16] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w,
-                             s2.x, s2.y, s2.z, s2.w, s3.x, s3.y, s3.z, s3.w};
-    if (c + K1_WAVES < nchunks) fetch(c + K1_WAVES);
-
-    // L1 fragments for this chunk (issued early); rows past the rank read as zeros
+    const int s_own = (int)sv;
     uint4 LA[NT > 0 ? NT : 1], LB[NT > 0 ? NT : 1];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const uint32_t o = (uint32_t)((t * 16 + r16) * K + k0) * 2;
-      LA[t] = buf_load16(rL, o);
-      LB[t] = buf_load16(rL, o + 16);
+      LA[t] = LAn[t];
+      LB[t] = LBn[t];
     }
+    if (c + K1_WAVES < nchunks) fetch(c + K1_WAVES);
 
+    // x * inv_s, inv_s of channel i from lane i of the row (DPP row_newbcast:i)
+#define K1_BC(i) __int_as_float(__builtin_amdgcn_update_dpp(0, s_own, 0x150 + (i), 0xF, 0xF, false))
     float xh[16];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      xh[2 * i] = bf16_lo_to_f32(xw[i]) * __uint_as_float(sw[2 * i]);
-      xh[2 * i + 1] = bf16_hi_to_f32(xw[i]) * __uint_as_float(sw[2 * i + 1]);
-    }
+    xh[0] = bf16_lo_to_f32(xw[0]) * K1_BC(0);
+    xh[1] = bf16_hi_to_f32(xw[0]) * K1_BC(1);
+    xh[2] = bf16_lo_to_f32(xw[1]) * K1_BC(2);
+    xh[3] = bf16_hi_to_f32(xw[1]) * K1_BC(3);
+    xh[4] = bf16_lo_to_f32(xw[2]) * K1_BC(4);
+    xh[5] = bf16_hi_to_f32(xw[2]) * K1_BC(5);
+    xh[6] = bf16_lo_to_f32(xw[3]) * K1_BC(6);
+    xh[7] = bf16_hi_to_f32(xw[3]) * K1_BC(7);
+    xh[8] = bf16_lo_to_f32(xw[4]) * K1_BC(8);
+    xh[9] = bf16_hi_to_f32(xw[4]) * K1_BC(9);
+    xh[10] = bf16_lo_to_f32(xw[5]) * K1_BC(10);
+    xh[11] = bf16_hi_to_f32(xw[5]) * K1_BC(11);
+    xh[12] = bf16_lo_to_f32(xw[6]) * K1_BC(12);
+    xh[13] = bf16_hi_to_f32(xw[6]) * K1_BC(13);
+    xh[14] = bf16_lo_to_f32(xw[7]) * K1_BC(14);
+    xh[15] = bf16_hi_to_f32(xw[7]) * K1_BC(15);
+#undef K1_BC
     float a = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(xh[i]));
