@@ -839,7 +839,10 @@ K2Plan plan_k2(const KernelLayer& L, int64_t M, bool mma) {
   uint32_t S = R ? G / R : 1;
   if (S * 4 > nst * sub) S = nst * sub / 4;  // parts of at least 4 sub-steps
   if (S > nst) S = nst;
-  if (S > 16) S = 16;
+  // At most 4 parts: the partial tiles are written and read back by the fixup, and beyond
+  // 4 parts that traffic costs more than the idle slots of the tail round it recovers
+  // (measured on the QKV and batch-2 layers: 2-4 parts 3-6 us faster than 16).
+  if (S > 4) S = 4;
   if (R == 0 || S < 2) return p;
   p.full = T - R;
   p.split = S;
