@@ -663,7 +663,13 @@ svdq_status svdq_prepare_weights(int64_t K, int64_t N, int32_t fmt, const uint8_
   // and expanded with masks alone (f0 = w0 & ~Z0, f2 = (w0 & Z0) | (w1 & Z1), ...).
   const uint32_t Z0 = (3u << 3) | (3u << 9) | (3u << 15) | (3u << 21) | (3u << 27);
   const uint32_t Z1 = (3u << 1) | (3u << 7) | (3u << 13) | (3u << 19) | (3u << 25) | (1u << 31);
+  // Placement: kernel 2 moves 128 K values (64 bytes of a column) per stage, so the
+  // 64-byte segments of columns 2j and 2j+1 for a stage share one 128-byte line:
+  // byte b of column n goes to (n / 2) K + (b / 64) 128 + (n % 2) 64 + b % 64.  With N
+  // odd, the last line pair's second half (a phantom column) is zero.
   const int64_t rowb = K / 2;
+  const int64_t N2 = N + (N & 1);
+  std::memset(qW_out, 0, (size_t)(N2 * rowb));
   for (int64_t n = 0; n < N; ++n)
     for (int64_t h0 = 0; h0 < K; h0 += 32) {  // one group half: codes h0 .. h0 + 31
       const uint8_t* src = qW + n * rowb + h0 / 2;
@@ -677,7 +683,8 @@ svdq_status svdq_prepare_weights(int64_t K, int64_t N, int32_t fmt, const uint8_
         if ((6 * fi & 31) > 26) f[((6 * fi) >> 5) + 1] |= (uint32_t)(sh >> 32);
       }
       const uint32_t w[4] = {f[0] | (f[2] & Z0), f[1] | (f[2] & Z1), f[3] | (f[5] & Z0), f[4] | (f[5] & Z1)};
-      std::memcpy(qW_out + n * rowb + h0 / 2, w, 16);
+      const int64_t b = h0 / 2;  // byte of the column
+      std::memcpy(qW_out + (n / 2) * K + (b / 64) * 128 + (n % 2) * 64 + b % 64, w, 16);
     }
   // scales: the fp16 bits, [groups][Np], padding 0
   const uint16_t* s16 = static_cast<const uint16_t*>(sW);

@@ -180,11 +180,12 @@ def pad4(n: int) -> int:
 
 
 def prepare_weights(K: int, N: int, fmt: int, qW: np.ndarray, sW: np.ndarray):
-    """Kernel layout of the residual weights: (qW [N][K/2] u8, sW bytes: INT4 fp16
-    [K/64][Np]; MXFP4 E8M0 [K/32][Np]; Np = N rounded up to 4)."""
+    """Kernel layout of the residual weights: (qW bytes: INT4 (N rounded up to 2) * K/2 in
+    column pairs, MXFP4 [N][K/2]; sW bytes: INT4 fp16 [K/64][Np]; MXFP4 E8M0 [K/32][Np];
+    Np = N rounded up to 4)."""
     qW = np.ascontiguousarray(qW, dtype=np.uint8)
     sW = np.ascontiguousarray(sW)
-    qo = np.empty_like(qW)
+    qo = np.empty(((N + 1) // 2 * 2 * (K // 2),), np.uint8) if fmt == INT4_G64 else np.empty_like(qW)
     so = np.empty((K // GROUP[fmt]) * pad4(N) * (2 if fmt == INT4_G64 else 1), np.uint8)
     _check(lib().svdq_prepare_weights(K, N, fmt, _ptr(qW), _ptr(sW), _ptr(qo), _ptr(so)))
     return qo, so

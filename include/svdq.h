@@ -83,8 +83,8 @@ typedef enum { SVDQ_ACT_PACKED = 0, SVDQ_ACT_MMA = 1 } svdq_act_form;
  *   L1t    [rank][K]  bf16  down projection transposed (L1^T), as svdq_pack_weights
  *                           writes it
  *   L2t    [N][R16]   bf16  up projection transposed (L2^T), columns >= rank zero
- *   qW     [N][K/2]   u8    residual codes, row n = output channel n along K, in the
- *                           kernel bit order of svdq_prepare_weights
+ *   qW                u8    residual codes along K per output channel, in the kernel
+ *                           layout of svdq_prepare_weights (INT4: column pairs)
  *   sW                group-major scales as svdq_prepare_weights writes them: INT4
  *                           fp16, MXFP4 E8M0 bytes, rows padded to Np (16-byte aligned)
  * L1t/L2t may be NULL iff rank == 0. */
@@ -161,15 +161,20 @@ svdq_status svdq_prepare_lowrank(int64_t N, int32_t rank, const uint16_t* L2, ui
  * of svdq_pack_weights / svdq_quantize_weights; only their encoding changes.  Np = N
  * rounded up to a multiple of 4; scale rows are padded to it.
  *   MXFP4: qW_out = qW; sW_out [K/32][Np] E8M0 bytes (padding 127).
- *   INT4:  qW_out [N][K/2]: each 16 bytes of a row (32 codes, a group half) become
- *          four words v0..v3 from which masks alone give the half's six FP6 operand
- *          words w0..w5 (fields and k order as in the MMA activation form below):
+ *   INT4:  qW_out: (N rounded up to 2) * K/2 bytes.  Each 16 bytes of a column (32
+ *          codes, a group half) become four words v0..v3 from which masks alone give
+ *          the half's six FP6 operand words w0..w5 (fields and k order as in the MMA
+ *          activation form below):
  *          with Z0 = the bits 3-4 of fields 0-4 (0x18618618) and Z1 = bits 1-2, 7-8,
  *          13-14, 19-20, 25-26 and 31 (0x86186186),
  *            v0 = w0 | (w2 & Z0), v1 = w1 | (w2 & Z1), v2 = w3 | (w5 & Z0),
  *            v3 = w4 | (w5 & Z1);
  *          w0 = v0 & ~Z0, w1 = v1 & ~Z1, w2 = (v0 & Z0) | (v1 & Z1) (w3..w5 likewise),
- *          since every field has zero exponent bits (bits 3-4).
+ *          since every field has zero exponent bits (bits 3-4).  Columns are stored
+ *          in pairs: byte b of column n (in the order above) is at
+ *          (n / 2) * K + (b / 64) * 128 + (n % 2) * 64 + b % 64, so the 64-byte
+ *          segments of columns 2j and 2j+1 for 128 consecutive K share a 128-byte line;
+ *          with N odd the last pair's second column is zero.
  *          sW_out: the fp16 scale bits [K/64][Np] ((K/64) * Np * 2 bytes), padding 0.
  * EINVAL on bad sizes, ENUMERIC on a negative or non-finite scale. */
 svdq_status svdq_prepare_weights(int64_t K, int64_t N, int32_t fmt, const uint8_t* qW,

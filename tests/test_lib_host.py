@@ -186,7 +186,12 @@ def test_prepare_weights_kernel_layout():
     qW = opack.pack_codes(codes, "int4")
     assert (sc.view(np.uint16) & 0x7C00 == 0).any(), "want subnormal fp16 scales in the case"
     qk, sk = svdq.prepare_weights(K, N, svdq.INT4_G64, qW, sc)
-    w = qk.view("<u4").reshape(N, K // 32, 4)
+    # column pairs: byte b of column n at (n // 2) K + (b // 64) 128 + (n % 2) 64 + b % 64
+    N2 = N + (N & 1)
+    assert qk.size == N2 * K // 2
+    pr = qk.reshape(N2 // 2, K // 128, 2, 64).transpose(0, 2, 1, 3).reshape(N2, K // 2)
+    assert not pr[N:].any(), "phantom column must be zero"
+    w = np.ascontiguousarray(pr[:N]).view("<u4").reshape(N, K // 32, 4)
     f = np.stack([w[..., 0] & ~np.uint32(Z0), w[..., 1] & ~np.uint32(Z1), (w[..., 0] & Z0) | (w[..., 1] & Z1),
                   w[..., 2] & ~np.uint32(Z0), w[..., 3] & ~np.uint32(Z1), (w[..., 2] & Z0) | (w[..., 3] & Z1)], -1)
     np.testing.assert_array_equal(fp6_codes(fp6_fields(f)).reshape(N, K), codes)
