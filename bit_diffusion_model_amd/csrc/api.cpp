@@ -64,14 +64,15 @@ struct WsLayout {
   size_t qx, sx, la, part, total;
 };
 // The forward path's workspace: the activation side in MMA form (INT4 FP6 operand
-// words, 64 bytes per token and group, and an fp16 scale plane; MXFP4 packed codes and
-// E8M0 bytes; lora_act as bf16 hi/lo rows, the bytes of fp32 [M][R16]), then kernel 2's
+// words, 64 bytes per token and group, and an fp16 scale plane; MXFP4 codes in token
+// pairs and E8M0 bytes; lora_act as bf16 hi/lo rows, the bytes of fp32 [M][R16]), then kernel 2's
 // partial tiles.
 static WsLayout ws_layout(const svdq_layer* L, int64_t M) {
   const bool i4 = L->fmt == SVDQ_INT4_G64;
   WsLayout w;
   w.qx = 0;
-  w.sx = rup((size_t)M * (size_t)(i4 ? L->K : L->K / 2));
+  // MXFP4 codes in token pairs: an odd M gets a pair's second row
+  w.sx = rup(i4 ? (size_t)M * (size_t)L->K : (size_t)((M + 1) & ~int64_t(1)) * (size_t)(L->K / 2));
   // MMA-form scales: rows padded to Mp = M rounded up to 4; INT4 fp16, MXFP4 E8M0 bytes
   const size_t Mp = ((size_t)M + 3) / 4 * 4;
   w.la = w.sx + rup((size_t)(L->K / group_of(L->fmt)) * Mp * (i4 ? 2 : 1));

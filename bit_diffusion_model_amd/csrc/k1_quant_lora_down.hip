@@ -227,7 +227,11 @@ k1_quant_lora_down(const uint16_t* __restrict__ X, int64_t ldx, int64_t M, int64
       w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, y[12], y[13], 1.0f, 2);
       w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, y[14], y[15], 1.0f, 3);
       if (row_ok) {
-        *reinterpret_cast<uint2*>(qX + row * (K >> 1) + (k0 >> 1)) = make_uint2(w0, w1);
+        const int64_t b = k0 >> 1;  // byte of the token's code row
+        // MMA form: token pairs, the 64-byte segments (128 K values, one kernel-2 stage)
+        // of tokens 2j and 2j+1 share a 128-byte line
+        uint8_t* dst = MMA ? qX + (row >> 1) * K + (b >> 6) * 128 + (row & 1) * 64 + (b & 63) : qX + row * (K >> 1) + b;
+        *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
         if ((sub & 1) == 0) {
           const int64_t ld = MMA ? (M + 3) & ~int64_t(3) : M;  // MMA form: rows padded to 4
           reinterpret_cast<uint8_t*>(sXv)[(int64_t)(2 * c + (sub >> 1)) * ld + row] = (uint8_t)(e + 127);

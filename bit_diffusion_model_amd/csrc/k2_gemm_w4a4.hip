@@ -154,11 +154,10 @@ __global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 
   const int64_t rowsA = mlim - m0 < BM ? mlim - m0 : BM;
   const int64_t rowsB = nlim - n0 < BN ? nlim - n0 : BN;
   const __amdgpu_buffer_rsrc_t rA = make_rsrc(qX + m0 * Ka, (uint32_t)rowsA * Ka);
-  // INT4 weights come in column pairs (two columns' 64-byte stage segments per 128-byte
-  // line), addressed from the start of the array (the debug window may start at an odd
-  // column); the range covers the pair of a last odd column
-  const __amdgpu_buffer_rsrc_t rB = FMT == 0 ? make_rsrc(qW, (uint32_t)((N + 1) & ~int64_t(1)) * Kb)
-                                             : make_rsrc(qW + n0 * Kb, (uint32_t)rowsB * Kb);
+  // The prepared weights come in column pairs (two columns' 64-byte stage segments per
+  // 128-byte line), addressed from the start of the array (the debug window may start at
+  // an odd column); the range covers the pair of a last odd column
+  const __amdgpu_buffer_rsrc_t rB = make_rsrc(qW, (uint32_t)((N + 1) & ~int64_t(1)) * Kb);
   const int ng = FMT == 0 ? (int)(K >> 6) : (int)(K >> 5);  // scale groups along K
   // staging roles: thread t moves the pieces of row t & 127, half t >> 7, of the A and
   // the B panel, and one scale per sub-step: waves 0-1 of the X row t, waves 2-3 of the
@@ -173,11 +172,10 @@ __global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 
   const int ldrow = tid & 127, ldhalf = tid >> 7;
   // this thread's part of a stage row: 4-bit code bytes [SUB*16*half, +SUB*16); in LDS,
   // INT4 takes 32 bytes per 32-code half (its FP6 operand words)
-  // INT4 column pairs: byte b of column c at (c / 2) 2 Kb + (b / 64) 128 + (c % 2) 64 + b % 64
+  // column pairs: byte b of column c at (c / 2) 2 Kb + (b / 64) 128 + (c % 2) 64 + b % 64
   // (a thread's pieces of a stage never cross a 64-byte segment)
-  const uint32_t cB = (uint32_t)(n0 + ldrow);  // INT4: absolute column
-  const uint32_t offB = FMT == 0 ? (cB >> 1) * 2 * Kb + (cB & 1) * 64 + ldhalf * SUB * 16
-                                 : (uint32_t)ldrow * Kb + ldhalf * SUB * 16;
+  const uint32_t cB = (uint32_t)(n0 + ldrow);  // absolute column
+  const uint32_t offB = (cB >> 1) * 2 * Kb + (cB & 1) * 64 + ldhalf * SUB * 16;
   const uint32_t offA = (uint32_t)ldrow * Ka + ldhalf * SUB * 16;
   const int ldsAB = ldrow * S::kPitch + ldhalf * SUB * (FMT == 0 ? 32 : 16);
 
@@ -185,7 +183,7 @@ __global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 
   // of another row into registers that are never stored.
   auto gload = [&](Stage<SUB>& st, int k) {
     const uint32_t kb = (uint32_t)k * SUB * 32;  // 4-bit code bytes before stage k
-    const uint32_t kbB = FMT == 0 ? (kb >> 6) * 128 + (kb & 63) : kb;
+    const uint32_t kbB = (kb >> 6) * 128 + (kb & 63);
 #pragma unroll
     for (int v = 0; v < SUB; ++v) {
       st.a[v] = buf_load16(rA, offA + kb + v * 16);
@@ -519,8 +517,10 @@ __global__ __launch_bounds__(SShape<FMT>::NT, 8 / SShape<FMT>::NW) __attribute__
   const int64_t n0 = (int64_t)(t % sch.tiles_n) * BN;
   const int64_t rowsA = M - m0 < BM ? M - m0 : BM;
   const int64_t rowsB = N - n0 < BN ? N - n0 : BN;
-  const __amdgpu_buffer_rsrc_t rA = make_rsrc(qX + m0 * Ka, (uint32_t)rowsA * Ka);
-  const __amdgpu_buffer_rsrc_t rB = make_rsrc(qW + n0 * Kb, (uint32_t)(FMT == 0 ? (rowsB + 1) & ~int64_t(1) : rowsB) * Kb);
+  // Row pairs: the weights (both formats) and the MXFP4 activations keep the 64-byte stage
+  // segments of rows 2j, 2j+1 in one 128-byte line; the ranges cover a last odd row's pair
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(qX + m0 * Ka, (uint32_t)(FMT == 1 ? (rowsA + 1) & ~int64_t(1) : rowsA) * Ka);
+  const __amdgpu_buffer_rsrc_t rB = make_rsrc(qW + n0 * Kb, (uint32_t)((rowsB + 1) & ~int64_t(1)) * Kb);
   const uint32_t ng = FMT == 0 ? (uint32_t)(K >> 6) : (uint32_t)(K >> 5);
   const uint32_t Mp = (uint32_t)((M + 3) & ~int64_t(3)), Np = (uint32_t)((N + 3) & ~int64_t(3));
   const __amdgpu_buffer_rsrc_t rSX = make_rsrc(sX, ng * Mp * (FMT == 0 ? 2 : 1));
@@ -534,22 +534,22 @@ __global__ __launch_bounds__(SShape<FMT>::NT, 8 / SShape<FMT>::NW) __attribute__
   for (int q = 0; q < D::NA; ++q) {
     const int pos = (wave + NW * q) * 1024 + lane * 16;
     const int row = pos / D::RA, ps = (pos % D::RA) / 16;
-    voA[q] = (uint32_t)row * Ka + (uint32_t)((ps ^ swz(row, D::RA / 16)) * 16);
+    const uint32_t sl = (uint32_t)((ps ^ swz(row, D::RA / 16)) * 16);
+    voA[q] = FMT == 1 ? (uint32_t)(row >> 1) * 2 * Ka + (uint32_t)(row & 1) * D::RA + sl : (uint32_t)row * Ka + sl;
   }
 #pragma unroll
   for (int q = 0; q < D::NBW; ++q) {
     const int pos = (wave + NW * q) * 1024 + lane * 16;
     const int row = pos / D::RB, ps = (pos % D::RB) / 16;
     const uint32_t sl = (uint32_t)((ps ^ swz(row, D::RB / 16)) * 16);
-    // INT4: column pairs, a stage's 64-byte segments of columns 2j, 2j+1 in one line
-    voB[q] = FMT == 0 ? (uint32_t)(row >> 1) * 2 * Kb + (uint32_t)(row & 1) * D::RB + sl : (uint32_t)row * Kb + sl;
+    voB[q] = (uint32_t)(row >> 1) * 2 * Kb + (uint32_t)(row & 1) * D::RB + sl;
   }
   auto issue = [&](int k, uint8_t* base) {
 #pragma unroll
-    for (int q = 0; q < D::NA; ++q) dma16(rA, base + (wave + NW * q) * 1024, voA[q], (uint32_t)k * D::RA);
+    for (int q = 0; q < D::NA; ++q) dma16(rA, base + (wave + NW * q) * 1024, voA[q], (uint32_t)k * (FMT == 1 ? 2 : 1) * D::RA);
 #pragma unroll
     for (int q = 0; q < D::NBW; ++q)
-      dma16(rB, base + D::B_OFF + (wave + NW * q) * 1024, voB[q], (uint32_t)k * (FMT == 0 ? 2 : 1) * D::RB);
+      dma16(rB, base + D::B_OFF + (wave + NW * q) * 1024, voB[q], (uint32_t)k * 2 * D::RB);
     // scale parts: slot z = wave + NW r covers sub-step z / (XP + WP), part y of it
     // (activation parts first); slots past the last part reload part 0 of sub-step 0
     // into the spare bytes.  Everything is wave-uniform arithmetic (no branches, so the

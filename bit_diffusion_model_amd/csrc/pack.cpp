@@ -646,7 +646,12 @@ svdq_status svdq_prepare_weights(int64_t K, int64_t N, int32_t fmt, const uint8_
   const int64_t groups = K / group_of(fmt);
   const int64_t Np = (N + 3) / 4 * 4;  // scale rows padded to 4 bytes (fp16 rows: 8)
   if (fmt == SVDQ_MXFP4_G32) {
-    std::memcpy(qW_out, qW, (size_t)(N * (K / 2)));
+    // codes as stored, columns in pairs (see the INT4 placement below)
+    const int64_t N2 = N + (N & 1);
+    std::memset(qW_out, 0, (size_t)(N2 * (K / 2)));
+    for (int64_t n = 0; n < N; ++n)
+      for (int64_t b = 0; b < K / 2; b += 64)
+        std::memcpy(qW_out + (n / 2) * K + (b / 64) * 128 + (n % 2) * 64, qW + n * (K / 2) + b, 64);
     const uint8_t* s8 = static_cast<const uint8_t*>(sW);
     uint8_t* o8 = static_cast<uint8_t*>(sW_out);
     for (int64_t g = 0; g < groups; ++g)

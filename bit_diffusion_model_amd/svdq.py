@@ -180,12 +180,12 @@ def pad4(n: int) -> int:
 
 
 def prepare_weights(K: int, N: int, fmt: int, qW: np.ndarray, sW: np.ndarray):
-    """Kernel layout of the residual weights: (qW bytes: INT4 (N rounded up to 2) * K/2 in
-    column pairs, MXFP4 [N][K/2]; sW bytes: INT4 fp16 [K/64][Np]; MXFP4 E8M0 [K/32][Np];
+    """Kernel layout of the residual weights: (qW bytes: (N rounded up to 2) * K/2 in
+    column pairs; sW bytes: INT4 fp16 [K/64][Np]; MXFP4 E8M0 [K/32][Np];
     Np = N rounded up to 4)."""
     qW = np.ascontiguousarray(qW, dtype=np.uint8)
     sW = np.ascontiguousarray(sW)
-    qo = np.empty(((N + 1) // 2 * 2 * (K // 2),), np.uint8) if fmt == INT4_G64 else np.empty_like(qW)
+    qo = np.empty(((N + 1) // 2 * 2 * (K // 2),), np.uint8)
     so = np.empty((K // GROUP[fmt]) * pad4(N) * (2 if fmt == INT4_G64 else 1), np.uint8)
     _check(lib().svdq_prepare_weights(K, N, fmt, _ptr(qW), _ptr(sW), _ptr(qo), _ptr(so)))
     return qo, so
@@ -259,7 +259,13 @@ class PackedLinear:
         """Device buffers for kernel 1's outputs in the given activation form."""
         torch = _torch()
         mma6 = form == ACT_MMA and self.fmt == INT4_G64
-        qX = torch.empty((M, self.K if mma6 else self.K // 2), dtype=torch.uint8, device=self.device)
+        if form == ACT_MMA and not mma6:
+            # MXFP4 MMA form: token pairs; the allocation holds the pair of an odd last
+            # token (M rounded up to 2 rows), the view has M rows
+            buf = torch.empty(((M + 1) // 2 * 2) * (self.K // 2), dtype=torch.uint8, device=self.device)
+            qX = buf[:M * (self.K // 2)].view(M, self.K // 2)
+        else:
+            qX = torch.empty((M, self.K if mma6 else self.K // 2), dtype=torch.uint8, device=self.device)
         if form == ACT_MMA:  # scales with rows padded to 4: INT4 fp16, MXFP4 E8M0 bytes
             sX = torch.empty((self.K // self.group) * pad4(M) * (2 if mma6 else 1), dtype=torch.uint8,
                              device=self.device)

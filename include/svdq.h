@@ -68,7 +68,9 @@ typedef enum { SVDQ_F32 = 0, SVDQ_BF16 = 1 } svdq_dtype;
  *           6 f of their 192-bit concatenation, field f carrying k = 32 h + 16 (f & 1)
  *           + (f >> 1) of the group; it is stored at byte 32 h as [w0 w1 w2 0 w3 w4 w5
  *           0]; sX [K/64][Mp] fp16 bits.
- *           MXFP4: qX as PACKED; sX [K/32][Mp] E8M0 bytes.
+ *           MXFP4: the PACKED codes in token pairs: byte b of token m's code row at
+ *           (m / 2) * K + (b / 64) * 128 + (m % 2) * 64 + b % 64 ((M rounded up to 2) *
+ *           K/2 bytes); sX [K/32][Mp] E8M0 bytes.
  *           Both: lora_act rows of 2*R16 bf16, [R16 hi][R16 lo] with hi = bf16(v),
  *           lo = bf16(v - hi) of the fp32 value v. */
 typedef enum { SVDQ_ACT_PACKED = 0, SVDQ_ACT_MMA = 1 } svdq_act_form;
@@ -160,7 +162,8 @@ svdq_status svdq_prepare_lowrank(int64_t N, int32_t rank, const uint16_t* L2, ui
 /* Offline device layout of the residual weights (host pointers).  The values are those
  * of svdq_pack_weights / svdq_quantize_weights; only their encoding changes.  Np = N
  * rounded up to a multiple of 4; scale rows are padded to it.
- *   MXFP4: qW_out = qW; sW_out [K/32][Np] E8M0 bytes (padding 127).
+ *   MXFP4: qW_out: the codes as stored, columns in pairs as for INT4 below ((N rounded
+ *          up to 2) * K/2 bytes); sW_out [K/32][Np] E8M0 bytes (padding 127).
  *   INT4:  qW_out: (N rounded up to 2) * K/2 bytes.  Each 16 bytes of a column (32
  *          codes, a group half) become four words v0..v3 from which masks alone give
  *          the half's six FP6 operand words w0..w5 (fields and k order as in the MMA

@@ -81,16 +81,23 @@ def _fp6_fields(words6):
     return out
 
 
-def decode_mma(qX, sX, la, fmt, K, rank):
+def decode_mma(qX, sX, la, fmt, K, rank, M=None):
     """Kernel 1's MMA-form outputs (device tensors) decoded per the header's description:
     INT4: per token and group 64 bytes, half h at byte 32 h as words [f0 f1 f2 0 f3 f4 f5
     0]; the 192-bit f0..f5 hold 6-bit E2M3 fields (sign bit 5, exponent 0, |q| in bits
     0-2), field f carrying k = 32 h + 16 (f & 1) + (f >> 1); fp16 scale bits [K/64][Mp].
-    MXFP4: codes as stored and E8M0 bytes [K/32][Mp].  lora_act rows [R16 hi][R16 lo]
-    bf16.  Returns (codes or packed bytes, scales (float64 values [K/64][M] for INT4,
-    bytes [K/32][M] for MXFP4), hi bits, lo bits)."""
+    MXFP4: codes in token pairs (byte b of token m at (m / 2) K + (b / 64) 128 + (m % 2)
+    64 + b % 64, M rounded up to 2 rows) and E8M0 bytes [K/32][Mp].  lora_act rows
+    [R16 hi][R16 lo] bf16.  Returns (codes or packed bytes [M][K/2], scales (float64
+    values [K/64][M] for INT4, bytes [K/32][M] for MXFP4), hi bits, lo bits)."""
     q = qX.cpu().numpy()
-    M = q.shape[0]
+    if M is None:
+        M = q.shape[0]
+    if fmt != "int4":  # token pairs reach past the M-row view when M is odd
+        import torch
+
+        full = torch.empty(0, dtype=torch.uint8, device=qX.device).set_(qX.untyped_storage())
+        q = full[qX.storage_offset():].cpu().numpy()
     Mp = (M + 3) // 4 * 4
     sb = None if sX is None else sX.cpu().numpy().view(np.uint8).reshape(-1)
     if fmt == "int4":
@@ -106,7 +113,10 @@ def decode_mma(qX, sX, la, fmt, K, rank):
         sv = None if sX is None else sb[:G * Mp * 2].view(np.float16).reshape(G, Mp)[:, :M].astype(np.float64)
         out = codes.reshape(M, K), sv
     else:
-        out = q, sb[:(K // 32) * Mp].reshape(K // 32, Mp)[:, :M]
+        M2 = (M + 1) // 2 * 2
+        pr = np.ascontiguousarray(q).reshape(-1)[:M2 * K // 2].reshape(M2 // 2, K // 128, 2, 64)
+        rows = pr.transpose(0, 2, 1, 3).reshape(M2, K // 2)[:M]
+        out = rows, sb[:(K // 32) * Mp].reshape(K // 32, Mp)[:, :M]
     hi = lo = None
     if rank:
         R16 = (rank + 15) // 16 * 16

@@ -59,7 +59,7 @@ def test_kernel1_codes_scales_lora(shape):
     # the MMA form: the same codes and scales re-encoded, lora_act as the bf16 hi/lo
     # split of the very fp32 values above
     qm, sm, lam = lay.quantize_act(X, form=svdq.ACT_MMA)
-    c_m, s_m, hi, lo = decode_mma(qm, sm, lam, fmt, K, r)
+    c_m, s_m, hi, lo = decode_mma(qm, sm, lam, fmt, K, r, M=M)
     if fmt == "int4":
         np.testing.assert_array_equal(c_m, codes)
         np.testing.assert_array_equal(s_m, sX_ref.view(np.float16).astype(np.float64))

@@ -203,7 +203,9 @@ def test_prepare_weights_kernel_layout():
     assert not sv[:, N:].any()
     c4, s4 = opack.quantize_residual(R, "mxfp4")
     qf, sf = svdq.prepare_weights(K, N, svdq.MXFP4_G32, opack.pack_codes(c4, "mxfp4"), s4)
-    np.testing.assert_array_equal(qf, opack.pack_codes(c4, "mxfp4"))
+    pf = qf.reshape(N2 // 2, K // 128, 2, 64).transpose(0, 2, 1, 3).reshape(N2, K // 2)
+    np.testing.assert_array_equal(pf[:N], opack.pack_codes(c4, "mxfp4"))
+    assert not pf[N:].any()
     sf = sf.reshape(K // 32, Np)
     np.testing.assert_array_equal(sf[:, :N], s4)
     assert np.all(sf[:, N:] == 127)
