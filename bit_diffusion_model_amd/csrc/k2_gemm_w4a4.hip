@@ -421,12 +421,13 @@ struct Shape {
 };
 // INT4: 128 x 128, 4 waves of 64 x 64 (the rescale schedule's 2 x 2 MFMA tiles), two
 // blocks per CU (a 128 x 256 tile with one block per CU measured 6% slower: the waves
-// of one block meet at every barrier).  MXFP4: 256 x 256, 8 waves of 128 x 64, one block
-// per CU (no per-group VALU, so larger wave tiles; the panel loads bound this format,
-// and the larger tile halves their bytes per output).
+// of one block meet at every barrier).  MXFP4: 256 x 128, 4 waves of 128 x 64, two blocks
+// per CU (no per-group VALU, so larger wave tiles; measured against 256 x 256 tiles of 8
+// waves, which halve the panel bytes per output but leave the QKV layer 2.53 rounds of
+// tiles in 3 rounds of one block per CU: 96 against 102 us).
 template <int FMT> struct SShape;
 template <> struct SShape<0> : Shape<2, 2, 2, 2> {};
-template <> struct SShape<1> : Shape<2, 4, 4, 2> {};
+template <> struct SShape<1> : Shape<2, 2, 4, 2> {};
 
 // LDS layout of one stage of the streamed kernel
 template <int FMT>
