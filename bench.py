@@ -237,19 +237,20 @@ def main():
     torch.cuda.synchronize()
     t_k1 = float(np.mean([e[3 * i].elapsed_time(e[3 * i + 1]) for i in range(nrep)])) * 1e-3
     t_k2 = float(np.mean([e[3 * i + 1].elapsed_time(e[3 * i + 2]) for i in range(nrep)])) * 1e-3
-    # low-rank overhead: the layer against a rank-0 layer with the same codes, timed in
-    # alternating blocks of 20 forwards (medians of 5), so both see the same clocks
-    fr, f0 = [], []
+    # low-rank overhead: the layer against a rank-0 layer with the same codes, and against
+    # the unfused baseline (the low-rank branch as kernels of its own), timed in alternating
+    # blocks of 20 forwards (medians of 5), so all three see the same clocks
+    fr, f0, fu = [], [], []
     for _ in range(5):
-        for lyr, wsp, out in ((lay, ws, fr), (lay0, ws0, f0)):
-            lyr.forward(X, ydt, Y, wsp)
+        for lyr, wsp, fused, out in ((lay, ws, True, fr), (lay0, ws0, True, f0), (lay, ws, False, fu)):
+            lyr.forward(X, ydt, Y, wsp, fused=fused)
             ev0.record()
             for _ in range(20):
-                lyr.forward(X, ydt, Y, wsp)
+                lyr.forward(X, ydt, Y, wsp, fused=fused)
             ev1.record()
             torch.cuda.synchronize()
             out.append(ev0.elapsed_time(ev1) / 20)
-    ms_r, ms0 = float(np.median(fr)), float(np.median(f0))
+    ms_r, ms0, ms_u = float(np.median(fr)), float(np.median(f0)), float(np.median(fu))
 
     G = lay.group
     k2_ops = float(M) * N * (2.0 * K + 2.0 * r)
@@ -275,7 +276,8 @@ def main():
         "kernels": {"k1_us": round(t_k1 * 1e6, 2), "k2_us": round(t_k2 * 1e6, 2),
                     "k1_GBps": round(k1_bytes / t_k1 / 1e9, 1), "k1_hbm_frac": round(k1_bytes / t_k1 / 1e9 / PEAK_HBM_GBS, 4),
                     "k2_TOPS": round(k2_tops, 2), "rank0_ms": round(ms0, 5),
-                    "fwd_ms_paired": round(ms_r, 5), "lowrank_overhead": round(ms_r / ms0 - 1.0, 4)},
+                    "fwd_ms_paired": round(ms_r, 5), "lowrank_overhead": round(ms_r / ms0 - 1.0, 4),
+                    "unfused_ms": round(ms_u, 5), "unfused_lowrank_overhead": round(ms_u / ms0 - 1.0, 4)},
     }
     if args.calib_copy:
         src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device=dev)

@@ -189,6 +189,35 @@ svdq_status svdq_linear_forward(const svdq_layer* layer, int64_t M, const uint16
   return run_k2(layer, M, SVDQ_ACT_MMA, qX, sX, la, Y, ldy, ydtype, base + w.part, w.total - w.part, stream);
 }
 
+svdq_status svdq_linear_forward_unfused(const svdq_layer* layer, int64_t M, const uint16_t* X, int64_t ldx,
+                                        void* Y, int64_t ldy, int32_t ydtype, void* workspace,
+                                        size_t ws_bytes, void* stream) {
+  KernelLayer kl;
+  svdq_status st = check_layer(layer, kl);
+  if (st != SVDQ_OK) return st;
+  if (M < 0) return fail(SVDQ_EINVAL, "M must be >= 0");
+  if (M == 0) return ok();
+  const WsLayout w = ws_layout(layer, M);
+  if (!workspace || ws_bytes < w.total) return fail(SVDQ_EINVAL, "workspace too small: need %zu bytes", w.total);
+  if (!aligned(workspace, 256)) return fail(SVDQ_EINVAL, "workspace must be 256-byte aligned");
+  uint8_t* base = static_cast<uint8_t*>(workspace);
+  uint8_t* qX = base + w.qx;
+  void* sX = base + w.sx;
+  void* la = base + w.la;
+  svdq_layer l0 = *layer;  // the 4-bit branch alone
+  l0.rank = 0;
+  st = run_k1(&l0, M, X, ldx, SVDQ_ACT_MMA, qX, sX, nullptr, stream);
+  if (st != SVDQ_OK) return st;
+  hipError_t e = hipSuccess;
+  if (kl.rank > 0 && (e = launch_k1_down(kl, M, X, ldx, la, (hipStream_t)stream)) != hipSuccess)
+    return fail(SVDQ_EHIP, "down-projection launch: %s", hipGetErrorString(e));
+  st = run_k2(&l0, M, SVDQ_ACT_MMA, qX, sX, nullptr, Y, ldy, ydtype, base + w.part, w.total - w.part, stream);
+  if (st != SVDQ_OK) return st;
+  if (kl.rank > 0 && (e = launch_lora_up(kl, M, la, Y, ldy, ydtype, (hipStream_t)stream)) != hipSuccess)
+    return fail(SVDQ_EHIP, "up-projection launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 svdq_status svdq_debug_group_sums(const svdq_layer* layer, int64_t M, const uint8_t* qX, int64_t m0,
                                   int64_t n0, int64_t mt, int64_t nt, int32_t* out, void* stream) {
   KernelLayer kl;

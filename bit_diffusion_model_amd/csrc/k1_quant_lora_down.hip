@@ -52,7 +52,9 @@ __device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
 }
 
 // Rank tiles 1 and 2 fit in 128 VGPRs, so two 8-wave blocks share a CU.
-template <int FMT, int NT, bool MMA>
+// QUANT = false: the down projection alone (lora_act only), the unfused baseline's
+// separate low-rank pass over X; qX and sX are not touched.
+template <int FMT, int NT, bool MMA, bool QUANT = true>
 __global__ __launch_bounds__(64 * K1_WAVES) __attribute__((amdgpu_waves_per_eu(NT == 1 || NT == 2 ? 4 : 2))) void
 k1_quant_lora_down(const uint16_t* __restrict__ X, int64_t ldx, int64_t M, int64_t K,
                    const float* __restrict__ inv_s, const uint16_t* __restrict__ L1t, int rank,
@@ -127,6 +129,7 @@ k1_quant_lora_down(const uint16_t* __restrict__ X, int64_t ldx, int64_t M, int64
     xh[14] = bf16_lo_to_f32(xw[7]) * K1_BC(14);
     xh[15] = bf16_hi_to_f32(xw[7]) * K1_BC(15);
 #undef K1_BC
+    if constexpr (QUANT) {
     float a = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(xh[i]));
@@ -238,6 +241,7 @@ k1_quant_lora_down(const uint16_t* __restrict__ X, int64_t ldx, int64_t M, int64
         }
       }
     }
+    }  // QUANT
 
     if constexpr (NT > 0) {
       // x = hi + lo as bf16 pairs, channels 0-7 of the lane in a*0, 8-15 in a*1
@@ -311,6 +315,22 @@ static hipError_t launch_k1_fmt(const KernelLayer& L, int64_t M, const uint16_t*
     default: return hipErrorInvalidValue;
   }
 #undef K1_CASE
+  return hipGetLastError();
+}
+
+hipError_t launch_k1_down(const KernelLayer& L, int64_t M, const uint16_t* X, int64_t ldx, void* lora_act,
+                          hipStream_t st) {
+  const dim3 grid((unsigned)((M + 15) / 16)), block(64 * K1_WAVES);
+#define K1D_CASE(NTV)                                                                                          \
+  case NTV:                                                                                                    \
+    hipLaunchKernelGGL((k1_quant_lora_down<0, NTV, true, false>), grid, block, 0, st, X, ldx, M, L.K, L.inv_s, \
+                       L.L1t, L.rank, (uint8_t*)nullptr, (void*)nullptr, static_cast<float*>(lora_act));       \
+    break;
+  switch ((L.rank + 15) / 16) {
+    K1D_CASE(1) K1D_CASE(2) K1D_CASE(3) K1D_CASE(4) K1D_CASE(5) K1D_CASE(6) K1D_CASE(7) K1D_CASE(8)
+    default: return hipErrorInvalidValue;
+  }
+#undef K1D_CASE
   return hipGetLastError();
 }
 

@@ -22,6 +22,13 @@ struct KernelLayer {
 hipError_t launch_k1(const KernelLayer& L, int64_t M, const uint16_t* X, int64_t ldx, uint8_t* qX,
                      void* sX, void* lora_act, bool mma, hipStream_t st);
 
+// The unfused baseline's two low-rank passes: lora_act = X_hat L1 alone (a second read
+// of X; MMA-form lora_act), and Y += lora_act L2 (a read and a write of Y).
+hipError_t launch_k1_down(const KernelLayer& L, int64_t M, const uint16_t* X, int64_t ldx, void* lora_act,
+                          hipStream_t st);
+hipError_t launch_lora_up(const KernelLayer& L, int64_t M, const void* lora_act, void* Y, int64_t ldy,
+                          int ydtype, hipStream_t st);
+
 // Work split of kernel 2 on the current device: tiles [0, full) whole, the remaining
 // tiles (those of a last, partly filled round of resident blocks) cut into `split` parts
 // along K whose fp32 partial tiles take `bytes` of workspace.

@@ -42,7 +42,7 @@ EXPORTS = [
     "svdq_last_error", "svdq_act_absmax", "svdq_weight_sizes", "svdq_pack_weights",
     "svdq_quantize_weights", "svdq_concat_lora", "svdq_prepare_lowrank", "svdq_prepare_weights",
     "svdq_quantize_act_lora_down", "svdq_gemm_w4a4_lora_up", "svdq_gemm_workspace_bytes", "svdq_workspace_bytes",
-    "svdq_linear_forward", "svdq_debug_group_sums",
+    "svdq_linear_forward", "svdq_linear_forward_unfused", "svdq_debug_group_sums",
 ]
 
 
@@ -69,6 +69,7 @@ def lib():
         "svdq_gemm_workspace_bytes": (ctypes.c_size_t, [P, I64, I32]),
         "svdq_workspace_bytes": (ctypes.c_size_t, [P, I64]),
         "svdq_linear_forward": (I32, [P, I64, P, I64, P, I64, I32, P, ctypes.c_size_t, P]),
+        "svdq_linear_forward_unfused": (I32, [P, I64, P, I64, P, I64, I32, P, ctypes.c_size_t, P]),
         "svdq_debug_group_sums": (I32, [P, I64, P, I64, I64, I64, I64, P, P]),
     }
     for name, (res, args) in sig.items():
@@ -310,16 +311,18 @@ class PackedLinear:
         n = lib().svdq_workspace_bytes(self.c_layer(), M)
         return torch.empty(max(n, 256), dtype=torch.uint8, device=self.device)
 
-    def forward(self, X, ydtype: int = F32, out=None, workspace=None):
-        """The public layer: svdq_linear_forward (kernel 1 then kernel 2)."""
+    def forward(self, X, ydtype: int = F32, out=None, workspace=None, fused: bool = True):
+        """The public layer: svdq_linear_forward (kernel 1 then kernel 2), or with
+        fused=False svdq_linear_forward_unfused (the low-rank branch as kernels of its own)."""
         torch = _torch()
         M = X.shape[0]
         if out is None:
             out = torch.empty((M, self.N), dtype=torch.float32 if ydtype == F32 else torch.bfloat16,
                               device=self.device)
         ws = workspace if workspace is not None else self.workspace(M)
-        _check(lib().svdq_linear_forward(self.c_layer(), M, _dptr(X), X.stride(0), _dptr(out), out.stride(0),
-                                         ydtype, _dptr(ws), ws.numel(), _stream()))
+        fn = lib().svdq_linear_forward if fused else lib().svdq_linear_forward_unfused
+        _check(fn(self.c_layer(), M, _dptr(X), X.stride(0), _dptr(out), out.stride(0), ydtype, _dptr(ws), ws.numel(),
+                  _stream()))
         return out
 
     def group_sums(self, qX, m0: int, n0: int, mt: int, nt: int):

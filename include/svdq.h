@@ -232,6 +232,20 @@ svdq_status svdq_linear_forward(const svdq_layer* layer, int64_t M, const uint16
                                 int64_t ldx, void* Y, int64_t ldy, int32_t ydtype,
                                 void* workspace, size_t ws_bytes, void* stream);
 
+/* The unfused baseline (jeonghoonpark.com "SVDQuant" review, section 4.3, Figure 6(a)):
+ * the same layer with the low-rank branch run as kernels of its own, the arrangement
+ * the fused path is measured against.  Four launches on `stream`: kernel 1 without the
+ * down projection, a down-projection kernel that reads X a second time (lora_act into
+ * the workspace), kernel 2 without the up projection (writes Q(X_hat) Q(R) to Y), and
+ * an up-projection kernel that reads Y back and writes Y + lora_act L2.  Arguments,
+ * workspace size (svdq_workspace_bytes) and errors as for svdq_linear_forward.  The
+ * codes and the 4-bit product are bit-identical to the fused path's; Y differs from it
+ * only by the rounding of the intermediate Y (bf16 output: rounded twice) and the order
+ * of the fp32 additions. */
+svdq_status svdq_linear_forward_unfused(const svdq_layer* layer, int64_t M, const uint16_t* X,
+                                        int64_t ldx, void* Y, int64_t ldy, int32_t ydtype,
+                                        void* workspace, size_t ws_bytes, void* stream);
+
 /* Diagnostic, same main loop as kernel 2 with an epilogue that stores the exact
  * integer group sums I[g][m][n] = sum_{k in group g} qX[m][k] qW[n][k] (INT4 only) for
  * the window rows [m0, m0+mt) x cols [n0, n0+nt).  out: device int32 [K/64][mt][nt].

@@ -180,3 +180,51 @@ def test_strided_activation_rows():
     assert Xd.stride(0) == 320
     Y = lay.forward(Xd).cpu().numpy().astype(np.float64)
     assert rel_err(Y, oforward.forward(wl.X, p)["Y"]) <= TOL_Y
+
+
+def _ws_lora_region(M, K, rank, fmt):
+    """Byte range of lora_act in the forward workspace: MMA-form qX, sX, lora_act in that
+    order, each starting on a 256-byte boundary."""
+    rup = lambda x: (x + 255) // 256 * 256
+    Mp = (M + 3) // 4 * 4
+    qx = M * K if fmt == "int4" else (M + 1) // 2 * 2 * (K // 2)
+    sx = (K // 64) * Mp * 2 if fmt == "int4" else (K // 32) * Mp
+    off = rup(qx) + rup(sx)
+    return off, off + M * ((rank + 15) // 16 * 16) * 4
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=_ids)
+def test_unfused_baseline_matches_oracle(shape):
+    """svdq_linear_forward_unfused: the low-rank branch as kernels of its own meets the
+    forward's bar, its lora_act is the fused kernel 1's bit for bit, and with rank 0 it is
+    the fused forward."""
+    M, K, N, r, fmt = shape
+    log(f"unfused {_ids(shape)}")
+    wl = random_layer(M, K, N, r, 7000 + M + K + N, fmt=fmt, x_out=3, w_out=2)
+    p = oracle_pack(wl)
+    lay = layer_from_oracle(p)
+    X = to_dev_bf16(wl.X)
+    Yref = oforward.forward(wl.X, p)["Y"]
+    wsf, wsu = lay.workspace(M), lay.workspace(M)
+    Yf = lay.forward(X, workspace=wsf).cpu().numpy()
+    Yu = lay.forward(X, workspace=wsu, fused=False).cpu().numpy()
+    e = rel_err(Yu.astype(np.float64), Yref)
+    log(f"  max|err|/RMS = {e:.3e}")
+    assert e <= TOL_Y
+    if r == 0:
+        np.testing.assert_array_equal(Yu, Yf)
+    else:
+        a, b = _ws_lora_region(M, K, r, fmt)
+        np.testing.assert_array_equal(wsu[a:b].cpu().numpy(), wsf[a:b].cpu().numpy())
+        # the same two fp32 terms added in another order
+        rms = np.sqrt(np.mean(Yref ** 2))
+        assert np.abs(Yu.astype(np.float64) - Yf).max() <= 1e-5 * rms
+    # bf16 output: the 4-bit term is rounded to bf16 in Y, then Y + lora_act L2 again
+    # (each rounding within 2^-8 relative: half a bf16 ulp), on top of the forward's bar
+    Yb = lay.forward(X, ydtype=svdq.BF16, fused=False).float().cpu().numpy().astype(np.float64)
+    o = oforward.forward(wl.X, p)
+    Yres = Yref - (o["lora_act"] @ np.asarray(p["L2b"], np.float64) if r else 0.0)
+    rms = np.sqrt(np.mean(Yref ** 2))
+    excess = np.abs(Yb - Yref) - (2.0 ** -8 * (np.abs(Yres) + np.abs(Yref)) + TOL_Y * rms)
+    log(f"  bf16 max|err|/RMS = {rel_err(Yb, Yref):.3e}, worst excess over the bound {excess.max() / rms:.3e} RMS")
+    assert excess.max() <= 0
