@@ -48,13 +48,13 @@ static svdq_status check_layer(const svdq_layer* L, KernelLayer& kl) {
   if (L->rank < 0 || L->rank > SVDQ_MAX_RANK)
     return fail(SVDQ_EUNSUPPORTED, "rank must be in [0, %d] (got %d)", SVDQ_MAX_RANK, (int)L->rank);
   if (!L->inv_s || !L->qW || !L->sW) return fail(SVDQ_EINVAL, "layer inv_s, qW and sW must be non-NULL");
-  if (L->rank > 0 && (!L->L1t || !L->L2t))
-    return fail(SVDQ_EINVAL, "layer L1t and L2t must be non-NULL when rank > 0");
+  if (L->rank > 0 && (!L->L1f || !L->L2t))
+    return fail(SVDQ_EINVAL, "layer L1f and L2t must be non-NULL when rank > 0");
   if (!aligned(L->sW, 16)) return fail(SVDQ_EINVAL, "layer sW must be 16-byte aligned");
   if (!aligned(L->inv_s, 16) || !aligned(L->qW, 16) ||
-      (L->rank > 0 && (!aligned(L->L1t, 16) || !aligned(L->L2t, 16))))
-    return fail(SVDQ_EINVAL, "layer inv_s, qW, L1t and L2t must be 16-byte aligned");
-  kl = KernelLayer{L->K, L->N, L->rank, L->fmt, L->inv_s, L->L1t, L->L2t, L->qW, L->sW};
+      (L->rank > 0 && (!aligned(L->L1f, 16) || !aligned(L->L2t, 16))))
+    return fail(SVDQ_EINVAL, "layer inv_s, qW, L1f and L2t must be 16-byte aligned");
+  kl = KernelLayer{L->K, L->N, L->rank, L->fmt, L->inv_s, L->L1f, L->L2t, L->qW, L->sW};
   return SVDQ_OK;
 }
 

@@ -11,19 +11,24 @@
 // Work split: a block of 8 waves owns 16 consecutive tokens.  The K dimension is cut
 // into 64-wide chunks; wave w takes chunks w, w+8, ..., with the next chunk's X, inv_s
 // and L1 loads issued before the current chunk is processed.  Inside a chunk, lane l holds
-// token (l & 15) and the 16 consecutive channels 16 * (l >> 4) .. +15 (two 16-byte
-// loads of X).  One INT4 group (64) is therefore spread over the 4 lanes l, l^16,
-// l^32, l^48; one FP4 group (32) over lanes l, l^16.
+// token (l & 15) and the 16 consecutive channels 16 * (l >> 4) .. +15.  One INT4 group
+// (64) is therefore spread over the 4 lanes l, l^16, l^32, l^48; one FP4 group (32)
+// over lanes l, l^16.  X is loaded row-contiguously instead (each 16-byte load covers 8
+// whole 128-byte lines of 8 tokens) and regrouped through a small per-wave LDS tile:
+// loads whose 4-lane groups straddle 4 lines were measured markedly slower.
 //
-// Down projection: X_hat L1 with L1 as the pack stores it (bf16, transposed to
-// [rank][K]).  The smoothed activations exist only in fp32 registers, so each is split
-// into a bf16 pair hi + lo (hi = bf16(x), lo = bf16(x - hi): x to ~2^-17) and the
-// pair feeds two v_mfma_f32_16x16x32_bf16 against the same L1 fragment, which keeps
-// the low-rank branch fp32-accurate with one read of L1 per chunk.  Lane l supplies
-// MFMA row l & 15 and k-block l >> 4: the lane's first 8 channels go to one MFMA and
-// the next 8 to a second, and the B operand (L1 rows, contiguous along K) uses the same
-// channel order.  Partial sums of the 8 waves are added through LDS at the end, in a
-// fixed order.
+// Down projection: X_hat L1 with L1 in bf16, prepared in fragment order: for one chunk
+// and one tile of 16 rank columns, the 32 bytes a lane needs (16 channels of one rank
+// column) are contiguous, so each 16-byte load reads whole 128-byte lines (the plain
+// [rank][K] rows made every load touch 16 half-used lines, and these loads, repeated by
+// every block of 16 tokens, cost more than the pass over X).  The smoothed activations
+// exist only in fp32 registers, so each is split into a bf16 pair hi + lo (hi = bf16(x),
+// lo = bf16(x - hi): x to ~2^-17) and the pair feeds two v_mfma_f32_16x16x32_bf16
+// against the same L1 fragment, which keeps the low-rank branch fp32-accurate with one
+// read of L1 per chunk.  Lane l supplies MFMA row l & 15 and k-block l >> 4: the lane's
+// first 8 channels go to one MFMA and the next 8 to a second, and the B operand uses
+// the same channel order.  Partial sums of the waves are added through LDS at the end,
+// in a fixed order.
 //
 // INT4 rounding: t = x * (1 / s) is within |x / s| * 2^-23 of the quotient x / s, so
 // round(t) is the correctly rounded code unless x / s lies within 2^-17 of a half
@@ -51,13 +56,13 @@ __device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// Rank tiles 1 and 2 fit in 128 VGPRs, so two 8-wave blocks share a CU.
+// Rank tiles 0-2 fit in 128 VGPRs, so two 8-wave blocks share a CU.
 // QUANT = false: the down projection alone (lora_act only), the unfused baseline's
 // separate low-rank pass over X; qX and sX are not touched.
 template <int FMT, int NT, bool MMA, bool QUANT = true>
-__global__ __launch_bounds__(64 * K1_WAVES) __attribute__((amdgpu_waves_per_eu(NT == 1 || NT == 2 ? 4 : 2))) void
+__global__ __launch_bounds__(64 * K1_WAVES) __attribute__((amdgpu_waves_per_eu(NT <= 2 ? 4 : 2))) void
 k1_quant_lora_down(const uint16_t* __restrict__ X, int64_t ldx, int64_t M, int64_t K,
-                   const float* __restrict__ inv_s, const uint16_t* __restrict__ L1t, int rank,
+                   const float* __restrict__ inv_s, const uint16_t* __restrict__ L1f, int rank,
                    uint8_t* __restrict__ qX, void* __restrict__ sXv, float* __restrict__ lora_act) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -71,8 +76,13 @@ k1_quant_lora_down(const uint16_t* __restrict__ X, int64_t ldx, int64_t M, int64
   const int64_t nrows = M - m0 < 16 ? M - m0 : 16;
   const __amdgpu_buffer_rsrc_t rX = make_rsrc(X + m0 * ldx, (uint32_t)(((nrows - 1) * ldx + K) * 2));
   const __amdgpu_buffer_rsrc_t rS = make_rsrc(inv_s, (uint32_t)(K * 4));
-  const uint32_t xoff = (uint32_t)(r16 * ldx + sub * 16) * 2;
-  const __amdgpu_buffer_rsrc_t rL = make_rsrc(L1t, (uint32_t)(rank * K * 2));
+  // X loads: lane l takes row 8 i + (l >> 3), 16-byte piece l & 7 of the chunk's 128
+  // bytes (load i = 0, 1), so each load reads 8 whole lines; the pieces are regrouped
+  // to the lane's (row l & 15, 32 bytes at 32 (l >> 4)) through a per-wave LDS tile.
+  const uint32_t xoff = (uint32_t)((lane >> 3) * ldx + (lane & 7) * 8) * 2;
+  const uint32_t xstep8 = (uint32_t)(8 * ldx * 2);
+  __shared__ uint4 xs[K1_WAVES][16][9];
+  const __amdgpu_buffer_rsrc_t rL = make_rsrc(L1f, (uint32_t)(NT * 16 * K * 2));
 
   v4f acc[NT > 0 ? NT : 1];
 #pragma unroll
@@ -80,17 +90,18 @@ k1_quant_lora_down(const uint16_t* __restrict__ X, int64_t ldx, int64_t M, int64
 
   // One chunk ahead: X, the lane's own inv_s element (channel sub * 16 + r16: the 16
   // lanes of a row hold the row's 16 channels, broadcast to the row where they are
-  // used) and the L1 fragments (rows past the rank read as zeros).
+  // used) and the L1 fragments (rows past the rank are zero in the prepared layout).
   uint4 xa, xb, LAn[NT > 0 ? NT : 1], LBn[NT > 0 ? NT : 1];
   uint32_t sv;
   auto fetch = [&](int c) {
     const uint32_t kx = xoff + (uint32_t)c * 128;
     xa = buf_load16(rX, kx);
-    xb = buf_load16(rX, kx + 16);
+    xb = buf_load16(rX, kx + xstep8);
     sv = buf_load4(rS, (uint32_t)(c * 64 + sub * 16 + r16) * 4);
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const uint32_t o = (uint32_t)((t * 16 + r16) * K + (int64_t)c * 64 + sub * 16) * 2;
+      // fragment order: lane l's 32 bytes of chunk c, rank tile t, contiguous
+      const uint32_t o = (uint32_t)(((c * NT + t) * 64 + lane) * 32);
       LAn[t] = buf_load16(rL, o);
       LBn[t] = buf_load16(rL, o + 16);
     }
@@ -99,7 +110,10 @@ k1_quant_lora_down(const uint16_t* __restrict__ X, int64_t ldx, int64_t M, int64
 
   for (int c = wave; c < nchunks; c += K1_WAVES) {
     const int64_t k0 = (int64_t)c * 64 + sub * 16;
-    const uint32_t xw[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+    xs[wave][lane >> 3][lane & 7] = xa;
+    xs[wave][8 + (lane >> 3)][lane & 7] = xb;
+    const uint4 ya = xs[wave][r16][2 * sub], yb = xs[wave][r16][2 * sub + 1];
+    const uint32_t xw[8] = {ya.x, ya.y, ya.z, ya.w, yb.x, yb.y, yb.z, yb.w};
     const int s_own = (int)sv;
     uint4 LA[NT > 0 ? NT : 1], LB[NT > 0 ? NT : 1];
 #pragma unroll
@@ -274,7 +288,7 @@ k1_quant_lora_down(const uint16_t* __restrict__ X, int64_t ldx, int64_t M, int64
 #pragma unroll
       for (int i = 0; i < 4; ++i) red[wave][4 * sub + i][t * 16 + r16] = acc[t][i];
     __syncthreads();
-    // all NT * 16 columns are written; those past the rank are zero (their L1 rows read
+    // all NT * 16 columns are written; those past the rank are zero (their L1 rows are
     // as zeros)
     constexpr int R16 = NT * 16;
     for (int idx = threadIdx.x; idx < 16 * R16; idx += 64 * K1_WAVES) {
@@ -302,12 +316,12 @@ k1_quant_lora_down(const uint16_t* __restrict__ X, int64_t ldx, int64_t M, int64
 template <int FMT, bool MMA>
 static hipError_t launch_k1_fmt(const KernelLayer& L, int64_t M, const uint16_t* X, int64_t ldx,
                                 uint8_t* qX, void* sX, void* lora_act, hipStream_t st) {
-  const dim3 grid((unsigned)((M + 15) / 16)), block(64 * K1_WAVES);
+  const dim3 grid((unsigned)((M + 15) / 16));
   const int nt = (L.rank + 15) / 16;
 #define K1_CASE(NTV)                                                                            \
   case NTV:                                                                                     \
-    hipLaunchKernelGGL((k1_quant_lora_down<FMT, NTV, MMA>), grid, block, 0, st, X, ldx, M, L.K, \
-                       L.inv_s, L.L1t, L.rank, qX, sX, static_cast<float*>(lora_act));                    \
+    hipLaunchKernelGGL((k1_quant_lora_down<FMT, NTV, MMA>), grid, dim3(64 * K1_WAVES), 0, st, X, ldx, M, L.K, \
+                       L.inv_s, L.L1f, L.rank, qX, sX, static_cast<float*>(lora_act));                    \
     break;
   switch (nt) {
     K1_CASE(0) K1_CASE(1) K1_CASE(2) K1_CASE(3) K1_CASE(4)
@@ -320,11 +334,11 @@ static hipError_t launch_k1_fmt(const KernelLayer& L, int64_t M, const uint16_t*
 
 hipError_t launch_k1_down(const KernelLayer& L, int64_t M, const uint16_t* X, int64_t ldx, void* lora_act,
                           hipStream_t st) {
-  const dim3 grid((unsigned)((M + 15) / 16)), block(64 * K1_WAVES);
+  const dim3 grid((unsigned)((M + 15) / 16));
 #define K1D_CASE(NTV)                                                                                          \
   case NTV:                                                                                                    \
-    hipLaunchKernelGGL((k1_quant_lora_down<0, NTV, true, false>), grid, block, 0, st, X, ldx, M, L.K, L.inv_s, \
-                       L.L1t, L.rank, (uint8_t*)nullptr, (void*)nullptr, static_cast<float*>(lora_act));       \
+    hipLaunchKernelGGL((k1_quant_lora_down<0, NTV, true, false>), grid, dim3(64 * K1_WAVES), 0, st, X, ldx, M, L.K, L.inv_s, \
+                       L.L1f, L.rank, (uint8_t*)nullptr, (void*)nullptr, static_cast<float*>(lora_act));       \
     break;
   switch ((L.rank + 15) / 16) {
     K1D_CASE(1) K1D_CASE(2) K1D_CASE(3) K1D_CASE(4) K1D_CASE(5) K1D_CASE(6) K1D_CASE(7) K1D_CASE(8)

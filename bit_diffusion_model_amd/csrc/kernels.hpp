@@ -10,7 +10,7 @@ struct KernelLayer {
   int rank;
   int fmt;  // 0 INT4 g64, 1 MXFP4 g32
   const float* inv_s;
-  const uint16_t* L1t;
+  const uint16_t* L1f;  // kernel 1's fragment order (svdq_prepare_lowrank_down)
   const uint16_t* L2t;
   const uint8_t* qW;
   const void* sW;

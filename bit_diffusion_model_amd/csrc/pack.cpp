@@ -627,6 +627,22 @@ svdq_status svdq_concat_lora(int64_t K, int64_t N, const float* s, int32_t rank,
   return ok();
 }
 
+svdq_status svdq_prepare_lowrank_down(int64_t K, int32_t rank, const uint16_t* L1t, uint16_t* L1f_out) {
+  if (K < 64 || K % 64 != 0 || rank < 0) return fail(SVDQ_EINVAL, "need K a positive multiple of 64 and rank >= 0");
+  if (rank > SVDQ_MAX_RANK) return fail(SVDQ_EUNSUPPORTED, "rank exceeds %d", SVDQ_MAX_RANK);
+  if (rank == 0) return ok();
+  if (!L1t || !L1f_out) return fail(SVDQ_EINVAL, "required pointer is NULL");
+  const int64_t nt = (rank + 15) / 16;
+  for (int64_t c = 0; c < K / 64; ++c)
+    for (int64_t t = 0; t < nt; ++t)
+      for (int64_t l = 0; l < 64; ++l) {
+        const int64_t j = t * 16 + (l & 15), k0 = c * 64 + (l >> 4) * 16;
+        uint16_t* dst = L1f_out + ((c * nt + t) * 64 + l) * 16;
+        for (int64_t e = 0; e < 16; ++e) dst[e] = j < rank ? L1t[j * K + k0 + e] : (uint16_t)0;
+      }
+  return ok();
+}
+
 svdq_status svdq_prepare_lowrank(int64_t N, int32_t rank, const uint16_t* L2, uint16_t* L2t_out) {
   if (N < 1 || rank < 0) return fail(SVDQ_EINVAL, "need N >= 1 and rank >= 0");
   if (rank > SVDQ_MAX_RANK) return fail(SVDQ_EUNSUPPORTED, "rank exceeds %d", SVDQ_MAX_RANK);

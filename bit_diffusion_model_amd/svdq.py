@@ -32,7 +32,7 @@ class SvdqError(RuntimeError):
 class _Layer(ctypes.Structure):
     _fields_ = [
         ("K", ctypes.c_int64), ("N", ctypes.c_int64), ("rank", ctypes.c_int32), ("fmt", ctypes.c_int32),
-        ("inv_s", ctypes.c_void_p), ("L1t", ctypes.c_void_p), ("L2t", ctypes.c_void_p), ("qW", ctypes.c_void_p), ("sW", ctypes.c_void_p),
+        ("inv_s", ctypes.c_void_p), ("L1f", ctypes.c_void_p), ("L2t", ctypes.c_void_p), ("qW", ctypes.c_void_p), ("sW", ctypes.c_void_p),
     ]
 
 
@@ -40,7 +40,8 @@ _lib = None
 
 EXPORTS = [
     "svdq_last_error", "svdq_act_absmax", "svdq_weight_sizes", "svdq_pack_weights",
-    "svdq_quantize_weights", "svdq_concat_lora", "svdq_prepare_lowrank", "svdq_prepare_weights",
+    "svdq_quantize_weights", "svdq_concat_lora", "svdq_prepare_lowrank_down", "svdq_prepare_lowrank",
+    "svdq_prepare_weights",
     "svdq_quantize_act_lora_down", "svdq_gemm_w4a4_lora_up", "svdq_gemm_workspace_bytes", "svdq_workspace_bytes",
     "svdq_linear_forward", "svdq_linear_forward_unfused", "svdq_debug_group_sums",
 ]
@@ -62,6 +63,7 @@ def lib():
         "svdq_pack_weights": (I32, [I64, I64, P, P, F, I32, I32, P, P, P, P, P, P, P]),
         "svdq_quantize_weights": (I32, [I64, I64, P, I32, P, P]),
         "svdq_concat_lora": (I32, [I64, I64, P, I32, P, P, I32, P, P, F, P, P]),
+        "svdq_prepare_lowrank_down": (I32, [I64, I32, P, P]),
         "svdq_prepare_lowrank": (I32, [I64, I32, P, P]),
         "svdq_prepare_weights": (I32, [I64, I64, I32, P, P, P, P]),
         "svdq_quantize_act_lora_down": (I32, [P, I64, P, I64, I32, P, P, P, P]),
@@ -167,6 +169,15 @@ def r16(rank: int) -> int:
     return (rank + 15) // 16 * 16
 
 
+def prepare_lowrank_down(L1t: np.ndarray):
+    """Device layout of the down projection: L1^T [rank][K] in kernel 1's fragment order
+    (R16 * K bf16, flat)."""
+    r, K = L1t.shape
+    L1f = np.zeros((r16(r) * K,), np.uint16)
+    _check(lib().svdq_prepare_lowrank_down(K, r, _ptr(np.ascontiguousarray(L1t, dtype=np.uint16)), _ptr(L1f)))
+    return L1f
+
+
 def prepare_lowrank(L2: np.ndarray):
     """Device layout of the up projection: L2t [N][R16] (L2 transposed, zero-padded)."""
     L2 = np.ascontiguousarray(L2, dtype=np.uint16)
@@ -235,14 +246,14 @@ class PackedLinear:
         self.device = device
         self.inv_s = _upload(np.asarray(inv_s, np.float32), device)
         if rank > 0:
-            self.L1t = _upload(np.ascontiguousarray(L1t, dtype=np.uint16), device)
+            self.L1f = _upload(prepare_lowrank_down(L1t), device)
             self.L2t = _upload(prepare_lowrank(L2), device)
         else:
-            self.L1t = self.L2t = None
+            self.L1f = self.L2t = None
         qk, sk = prepare_weights(self.K, self.N, self.fmt, qW, sW)
         self.qW = _upload(qk, device)
         self.sW = _upload(sk, device)
-        self._c = _Layer(self.K, self.N, self.rank, self.fmt, _dptr(self.inv_s), _dptr(self.L1t),
+        self._c = _Layer(self.K, self.N, self.rank, self.fmt, _dptr(self.inv_s), _dptr(self.L1f),
                          _dptr(self.L2t), _dptr(self.qW), _dptr(self.sW))
 
     @classmethod

@@ -78,24 +78,24 @@ typedef enum { SVDQ_ACT_PACKED = 0, SVDQ_ACT_MMA = 1 } svdq_act_form;
 #define SVDQ_MAX_RANK 128
 
 /* Device-resident description of one packed layer (all pointers device memory,
- * owned by the caller, produced by svdq_pack_weights, then svdq_prepare_lowrank and
- * svdq_prepare_weights for the kernels' layouts).
+ * owned by the caller, produced by svdq_pack_weights, then svdq_prepare_lowrank_down,
+ * svdq_prepare_lowrank and svdq_prepare_weights for the kernels' layouts).
  * R16 below is rank rounded up to a multiple of 16.
  *   inv_s  [K]        fp32  reciprocal smoothing factor, fp32(1 / fp32(s))
- *   L1t    [rank][K]  bf16  down projection transposed (L1^T), as svdq_pack_weights
- *                           writes it
+ *   L1f    R16 * K    bf16  down projection in kernel 1's fragment order, as
+ *                           svdq_prepare_lowrank_down writes it
  *   L2t    [N][R16]   bf16  up projection transposed (L2^T), columns >= rank zero
  *   qW                u8    residual codes along K per output channel, in the kernel
  *                           layout of svdq_prepare_weights (INT4: column pairs)
  *   sW                group-major scales as svdq_prepare_weights writes them: INT4
  *                           fp16, MXFP4 E8M0 bytes, rows padded to Np (16-byte aligned)
- * L1t/L2t may be NULL iff rank == 0. */
+ * L1f/L2t may be NULL iff rank == 0. */
 typedef struct svdq_layer {
   int64_t K, N;
   int32_t rank;
   int32_t fmt; /* svdq_format */
   const float* inv_s;
-  const uint16_t* L1t;
+  const uint16_t* L1f;
   const uint16_t* L2t;
   const uint8_t* qW;
   const void* sW;
@@ -153,8 +153,17 @@ svdq_status svdq_concat_lora(int64_t K, int64_t N, const float* s, int32_t rank,
                              const uint16_t* A, const uint16_t* B, float lora_scale,
                              uint16_t* L1t_out, uint16_t* L2_out);
 
-/* Offline device layout of the up projection (the down projection L1t is used as
- * svdq_pack_weights writes it): transposed and zero-padded, L2t[n][j] = L2[j][n]
+/* Offline device layout of the down projection: L1^T [rank][K] (as svdq_pack_weights
+ * writes it) reordered so that each 16-byte load of kernel 1 reads whole 128-byte lines.
+ * With NT = R16 / 16, chunk c = k / 64, rank tile t = j / 16, lane l = (j % 16) +
+ * 16 ((k % 64) / 16) and e = k % 16:
+ *   L1f[((c NT + t) 64 + l) 16 + e] = L1t[j][k] (j < rank), 0 (rank <= j < R16),
+ * i.e. for one chunk and rank tile, lane l's 16 consecutive channels of rank row j are
+ * 32 contiguous bytes.  Host pointers; L1t [rank][K], L1f_out R16 * K bf16.  EINVAL on
+ * bad sizes (K a positive multiple of 64) or NULL pointers (rank 0: nothing written). */
+svdq_status svdq_prepare_lowrank_down(int64_t K, int32_t rank, const uint16_t* L1t, uint16_t* L1f_out);
+
+/* Offline device layout of the up projection: transposed and zero-padded, L2t[n][j] = L2[j][n]
  * (j < rank), 0 (rank <= j < R16).  Host pointers; L2 [rank][N], L2t_out [N][R16] bf16.
  * EINVAL on bad sizes or NULL pointers (rank 0: nothing to write, pointers unused). */
 svdq_status svdq_prepare_lowrank(int64_t N, int32_t rank, const uint16_t* L2, uint16_t* L2t_out);

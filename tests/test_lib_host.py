@@ -143,6 +143,24 @@ def test_prepare_lowrank_layouts():
     assert not L2t[:, 5:].any()
 
 
+def test_prepare_lowrank_down_layout():
+    """L1f: for chunk c, rank tile t and lane l, the 16 channels 64 c + 16 (l >> 4) ..
+    of rank row 16 t + (l & 15) at element ((c NT + t) 64 + l) 16; rows past the rank
+    zero.  Checked by undoing the permutation with an independent index walk."""
+    rng = np.random.default_rng(3)
+    for rank, K in ((5, 128), (16, 192), (33, 256)):
+        L1t = rng.integers(1, 1 << 16, size=(rank, K), dtype=np.uint16)
+        f = svdq.prepare_lowrank_down(L1t)
+        R16 = (rank + 15) // 16 * 16
+        assert f.shape == (R16 * K,)
+        full = f.reshape(K // 64, R16 // 16, 4, 16, 16)  # c, t, l >> 4, l & 15, e
+        back = full.transpose(1, 3, 0, 2, 4).reshape(R16, K)  # [t, l & 15] rows, [c, l >> 4, e] columns
+        np.testing.assert_array_equal(back[:rank], L1t)
+        assert not back[rank:].any()
+    with pytest.raises(svdq.SvdqError):
+        svdq.prepare_lowrank_down(np.zeros((4, 96), np.uint16))  # K not a multiple of 64
+
+
 def fp6_fields(words6):
     """[..., 6] uint32 words -> [..., 32] 6-bit fields, field f at bit 6 f of the 192-bit
     little-endian concatenation."""
