@@ -48,13 +48,13 @@ static svdq_status check_layer(const svdq_layer* L, KernelLayer& kl) {
   if (L->rank < 0 || L->rank > SVDQ_MAX_RANK)
     return fail(SVDQ_EUNSUPPORTED, "rank must be in [0, %d] (got %d)", SVDQ_MAX_RANK, (int)L->rank);
   if (!L->inv_s || !L->qW || !L->sW) return fail(SVDQ_EINVAL, "layer inv_s, qW and sW must be non-NULL");
-  if (L->rank > 0 && (!L->L1f || !L->L2t))
-    return fail(SVDQ_EINVAL, "layer L1f and L2t must be non-NULL when rank > 0");
+  if (L->rank > 0 && (!L->L1f || !L->L2f))
+    return fail(SVDQ_EINVAL, "layer L1f and L2f must be non-NULL when rank > 0");
   if (!aligned(L->sW, 16)) return fail(SVDQ_EINVAL, "layer sW must be 16-byte aligned");
   if (!aligned(L->inv_s, 16) || !aligned(L->qW, 16) ||
-      (L->rank > 0 && (!aligned(L->L1f, 16) || !aligned(L->L2t, 16))))
-    return fail(SVDQ_EINVAL, "layer inv_s, qW, L1f and L2t must be 16-byte aligned");
-  kl = KernelLayer{L->K, L->N, L->rank, L->fmt, L->inv_s, L->L1f, L->L2t, L->qW, L->sW};
+      (L->rank > 0 && (!aligned(L->L1f, 16) || !aligned(L->L2f, 16))))
+    return fail(SVDQ_EINVAL, "layer inv_s, qW, L1f and L2f must be 16-byte aligned");
+  kl = KernelLayer{L->K, L->N, L->rank, L->fmt, L->inv_s, L->L1f, L->L2f, L->qW, L->sW};
   return SVDQ_OK;
 }
 
@@ -65,8 +65,8 @@ struct WsLayout {
 };
 // The forward path's workspace: the activation side in MMA form (INT4 FP6 operand
 // words, 64 bytes per token and group, and an fp16 scale plane; MXFP4 codes in token
-// pairs and E8M0 bytes; lora_act as bf16 hi/lo rows, the bytes of fp32 [M][R16]), then kernel 2's
-// partial tiles.
+// pairs and E8M0 bytes; lora_act as bf16 hi/lo pairs in fragment order, M rounded up to
+// 32 rows), then kernel 2's partial tiles.
 static WsLayout ws_layout(const svdq_layer* L, int64_t M) {
   const bool i4 = L->fmt == SVDQ_INT4_G64;
   WsLayout w;
@@ -76,7 +76,7 @@ static WsLayout ws_layout(const svdq_layer* L, int64_t M) {
   // MMA-form scales: rows padded to Mp = M rounded up to 4; INT4 fp16, MXFP4 E8M0 bytes
   const size_t Mp = ((size_t)M + 3) / 4 * 4;
   w.la = w.sx + rup((size_t)(L->K / group_of(L->fmt)) * Mp * (i4 ? 2 : 1));
-  w.part = w.la + rup((size_t)M * (size_t)((L->rank + 15) / 16 * 16) * 4);
+  w.part = w.la + rup((size_t)((M + 31) & ~int64_t(31)) * (size_t)((L->rank + 15) / 16 * 16) * 4);
   KernelLayer kl{L->K, L->N, L->rank, L->fmt, nullptr, nullptr, nullptr, nullptr, nullptr};
   w.total = w.part + rup(plan_k2(kl, M, true).bytes);
   return w;

@@ -299,12 +299,15 @@ k1_quant_lora_down(const uint16_t* __restrict__ X, int64_t ldx, int64_t M, int64
         for (int w = 0; w < K1_WAVES; ++w) v += red[w][rr][cc];
         if constexpr (MMA) {
           // the bf16 pair kernel 2's up-projection MFMA consumes, v = hi + lo to ~2^-17
-          // relative; row layout [R16 hi][R16 lo] (the same bytes as R16 fp32)
+          // relative, in its fragment order: 32-row blocks, k steps of 16, hi then lo
+          // (512 elements apart), the 64 lanes' 8 values (lane m % 32 + 32 (k / 8 % 2))
           const uint32_t hb = f32_to_bf16_rne(v);
           const uint32_t lb = f32_to_bf16_rne(v - __uint_as_float(hb << 16));
-          uint16_t* la = reinterpret_cast<uint16_t*>(lora_act) + (m0 + rr) * 2 * R16;
-          la[cc] = (uint16_t)hb;
-          la[R16 + cc] = (uint16_t)lb;
+          const int64_t m = m0 + rr;
+          uint16_t* la = reinterpret_cast<uint16_t*>(lora_act) +
+                         (((((m >> 5) * NT + (cc >> 4)) * 2) * 64 + (m & 31) + 32 * ((cc >> 3) & 1)) << 3) + (cc & 7);
+          la[0] = (uint16_t)hb;
+          la[512] = (uint16_t)lb;
         } else {
           lora_act[(m0 + rr) * R16 + cc] = v;
         }

@@ -340,18 +340,19 @@ __global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 
 
   // ---- low-rank up projection: acc += lora_act[rows, :] L2[:, cols] -------------------
   // v_mfma_f32_32x32x16_bf16 with a bf16 hi/lo split of lora_act (L2 is bf16 already).
-  // Both operands are rows of 16-padded arrays (lora_act [M][R16] fp32, L2t [N][R16]
-  // bf16): lane (row or column l & 31, kh) reads the 8 consecutive ranks 16 t + 8 kh..,
-  // and rows past M / columns past N read as zeros through the range check.
+  // lora_act is [M][R16] fp32 (lane (row l & 31, kh) reads the 8 consecutive ranks
+  // 16 t + 8 kh..), L2f is in fragment order (one 16-byte piece per lane, 1 KB per
+  // column block and k step); rows past M / columns past N read as zeros through the
+  // range check.
   if (rank > 0 && part <= 0) {  // once per tile: whole, or the first part
     const int R16 = (rank + 15) & ~15;
     const __amdgpu_buffer_rsrc_t rL = make_rsrc(static_cast<const uint8_t*>(lora_act) + m0 * R16 * 4, (uint32_t)(rowsA * R16 * 4));
-    const __amdgpu_buffer_rsrc_t rU = make_rsrc(L2 + n0 * R16, (uint32_t)(rowsB * R16 * 2));
+    const __amdgpu_buffer_rsrc_t rU = make_rsrc(L2 + n0 * R16, (uint32_t)(((rowsB + 31) & ~31) * R16 * 2));
     for (int k0 = 0; k0 < R16; k0 += 16) {
       v8bf bl[TJ];
 #pragma unroll
       for (int j = 0; j < TJ; ++j)
-        bl[j] = __builtin_bit_cast(v8bf, buf_load16(rU, (uint32_t)((wn + j * 32 + l32) * R16 + k0 + 8 * kh) * 2));
+        bl[j] = __builtin_bit_cast(v8bf, buf_load16(rU, (uint32_t)(((((wn >> 5) + j) * (R16 >> 4) + (k0 >> 4)) * 64 + lane) * 16)));
 #pragma unroll
       for (int i = 0; i < TI; ++i) {
         const uint32_t o = (uint32_t)((wm + i * 32 + l32) * R16 + k0 + 8 * kh) * 4;
@@ -702,22 +703,25 @@ __global__ __launch_bounds__(SShape<FMT>::NT, 8 / SShape<FMT>::NW) __attribute__
   // ---- low-rank up projection first: acc = lora_act[rows, :] L2[:, cols] ----------------
   // It depends on nothing of the main loop, so it runs while the first two stages' loads
   // are in flight (its own loads queue behind them) instead of after the last stage.
-  // v_mfma_f32_32x32x16_bf16 on lora_act's bf16 hi/lo rows ([M][R16 hi | R16 lo]) and L2t
-  // [N][R16]; rows past M / columns past N read zeros through the range check.
+  // v_mfma_f32_32x32x16_bf16 on lora_act's bf16 hi/lo pairs and L2f, both in fragment
+  // order: for a block of 32 rows (columns) and a k step of 16, the 64 lanes' operands
+  // are 1 KB contiguous (lora_act: hi, then lo), so every load reads whole lines.  The
+  // range covers whole 32-row blocks; rows past M hold whatever the workspace held
+  // (their outputs are not stored), columns past N are zero.
   if (rank > 0 && part <= 0) {
     const int R16 = (rank + 15) & ~15;
-    const __amdgpu_buffer_rsrc_t rL = make_rsrc(lora_act + m0 * 2 * R16, (uint32_t)(rowsA * R16 * 4));
-    const __amdgpu_buffer_rsrc_t rU = make_rsrc(L2 + n0 * R16, (uint32_t)(rowsB * R16 * 2));
+    const __amdgpu_buffer_rsrc_t rL = make_rsrc(lora_act + m0 * 2 * R16, (uint32_t)(((rowsA + 31) & ~31) * R16 * 4));
+    const __amdgpu_buffer_rsrc_t rU = make_rsrc(L2 + n0 * R16, (uint32_t)(((rowsB + 31) & ~31) * R16 * 2));
     for (int k0 = 0; k0 < R16; k0 += 16) {
       v8bf bl[TJ];
 #pragma unroll
       for (int j = 0; j < TJ; ++j)
-        bl[j] = __builtin_bit_cast(v8bf, buf_load16(rU, (uint32_t)((wn + j * 32 + l32) * R16 + k0 + 8 * kh) * 2));
+        bl[j] = __builtin_bit_cast(v8bf, buf_load16(rU, (uint32_t)(((((wn >> 5) + j) * (R16 >> 4) + (k0 >> 4)) * 64 + lane) * 16)));
 #pragma unroll
       for (int i = 0; i < TI; ++i) {
-        const uint32_t o = (uint32_t)((wm + i * 32 + l32) * 2 * R16 + k0 + 8 * kh) * 2;
+        const uint32_t o = (uint32_t)(((((wm >> 5) + i) * (R16 >> 4) + (k0 >> 4)) * 2 * 64 + lane) * 16);
         const v8bf ah = __builtin_bit_cast(v8bf, buf_load16(rL, o));
-        const v8bf al = __builtin_bit_cast(v8bf, buf_load16(rL, o + R16 * 2));
+        const v8bf al = __builtin_bit_cast(v8bf, buf_load16(rL, o + 64 * 16));
 #pragma unroll
         for (int j = 0; j < TJ; ++j) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl[j], acc[i][j], 0, 0, 0);
@@ -788,7 +792,7 @@ static void launch_k2_t(const KernelLayer& L, int64_t M, const uint8_t* qX, cons
                         const void* lora_act, void* Y, int64_t ldy, int ydtype, const K2Sched& sch,
                         uint32_t nblocks, hipStream_t st) {
   hipLaunchKernelGGL((k2_gemm<FMT, false, SUB>), dim3(nblocks), dim3(NTHREADS), 0, st, qX, sX, M, L.qW,
-                     L.sW, L.N, L.K, lora_act, L.L2t, L.rank, Y, ldy, ydtype, (int64_t)0, (int64_t)0, M, L.N, sch,
+                     L.sW, L.N, L.K, lora_act, L.L2f, L.rank, Y, ldy, ydtype, (int64_t)0, (int64_t)0, M, L.N, sch,
                      (int32_t*)nullptr);
 }
 
@@ -878,7 +882,7 @@ hipError_t launch_k2(const KernelLayer& L, int64_t M, const uint8_t* qX, const v
 #define K2_STREAM(F)                                                                                        \
   hipLaunchKernelGGL((k2_stream<F>), dim3(nblocks), dim3(SShape<F>::NT), 0, st, qX, static_cast<const uint8_t*>(sX), M, \
                      L.qW, static_cast<const uint8_t*>(L.sW), L.N, L.K, static_cast<const uint16_t*>(lora_act),   \
-                     L.L2t, L.rank, Y, ldy, ydtype, sch)
+                     L.L2f, L.rank, Y, ldy, ydtype, sch)
   const int sub = sub_of(L.K);
   if (mma) {  // the activation side in MMA form: streamed kernel (K % 128 == 0: two sub-steps per stage)
     if (L.fmt == 0) K2_STREAM(0);

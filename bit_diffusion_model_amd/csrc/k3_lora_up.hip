@@ -9,10 +9,11 @@
 //
 // Work split: a block of 4 waves owns a 128 x 128 tile of Y, wave w the 64 x 64 quarter
 // (w >> 1, w & 1) as 2 x 2 accumulators of v_mfma_f32_32x32x16_bf16.  lora_act arrives
-// as bf16 hi/lo rows ([M][R16 hi | R16 lo], x = hi + lo to ~2^-17 relative) and L2 as
-// L2t [N][R16] bf16; each accumulator takes the hi and the lo product, so the branch keeps
-// fp32 accuracy.  Consecutive blocks walk along N, so a block's lora_act rows and all of
-// L2t (N * R16 * 2 bytes) stay in cache; Y is read and written once.
+// as bf16 hi/lo pairs (x = hi + lo to ~2^-17 relative) and L2 as bf16, both in the
+// matrix core's fragment order (1 KB per 32-row block and k step); each accumulator
+// takes the hi and the lo product, so the branch keeps fp32 accuracy.  Consecutive
+// blocks walk along N, so a block's lora_act rows and all of L2f (N * R16 * 2 bytes)
+// stay in cache; Y is read and written once.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -52,7 +53,7 @@ __device__ __forceinline__ void add_sub(const v16f& acc, void* Y, int64_t ldy, i
 }
 
 __global__ __launch_bounds__(UP_THREADS) void k3_lora_up(const uint16_t* __restrict__ lora_act,
-                                                         const uint16_t* __restrict__ L2t, int rank, int64_t M,
+                                                         const uint16_t* __restrict__ L2f, int rank, int64_t M,
                                                          int64_t N, void* __restrict__ Y, int64_t ldy, int ydtype,
                                                          uint32_t tiles_n) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -61,9 +62,9 @@ __global__ __launch_bounds__(UP_THREADS) void k3_lora_up(const uint16_t* __restr
   const int64_t rowsA = M - m0 < UP_BM ? M - m0 : UP_BM, rowsB = N - n0 < UP_BN ? N - n0 : UP_BN;
   const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
   const int R16 = (rank + 15) & ~15;
-  // rows past M / columns past N read zeros through the range check
-  const __amdgpu_buffer_rsrc_t rL = make_rsrc(lora_act + m0 * 2 * R16, (uint32_t)(rowsA * R16 * 4));
-  const __amdgpu_buffer_rsrc_t rU = make_rsrc(L2t + n0 * R16, (uint32_t)(rowsB * R16 * 2));
+  // whole 32-row blocks: rows past M are never stored, columns past N are zero in L2f
+  const __amdgpu_buffer_rsrc_t rL = make_rsrc(lora_act + m0 * 2 * R16, (uint32_t)(((rowsA + 31) & ~31) * R16 * 4));
+  const __amdgpu_buffer_rsrc_t rU = make_rsrc(L2f + n0 * R16, (uint32_t)(((rowsB + 31) & ~31) * R16 * 2));
   v16f acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -73,12 +74,12 @@ __global__ __launch_bounds__(UP_THREADS) void k3_lora_up(const uint16_t* __restr
     v8bf bl[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j)
-      bl[j] = __builtin_bit_cast(v8bf, buf_load16(rU, (uint32_t)((wn + j * 32 + l32) * R16 + k0 + 8 * kh) * 2));
+      bl[j] = __builtin_bit_cast(v8bf, buf_load16(rU, (uint32_t)(((((wn >> 5) + j) * (R16 >> 4) + (k0 >> 4)) * 64 + lane) * 16)));
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const uint32_t o = (uint32_t)((wm + i * 32 + l32) * 2 * R16 + k0 + 8 * kh) * 2;
+      const uint32_t o = (uint32_t)(((((wm >> 5) + i) * (R16 >> 4) + (k0 >> 4)) * 2 * 64 + lane) * 16);
       const v8bf ah = __builtin_bit_cast(v8bf, buf_load16(rL, o));
-      const v8bf al = __builtin_bit_cast(v8bf, buf_load16(rL, o + R16 * 2));
+      const v8bf al = __builtin_bit_cast(v8bf, buf_load16(rL, o + 64 * 16));
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl[j], acc[i][j], 0, 0, 0);
@@ -98,7 +99,7 @@ hipError_t launch_lora_up(const KernelLayer& L, int64_t M, const void* lora_act,
                           int ydtype, hipStream_t st) {
   const uint32_t tiles_m = (uint32_t)((M + UP_BM - 1) / UP_BM), tiles_n = (uint32_t)((L.N + UP_BN - 1) / UP_BN);
   hipLaunchKernelGGL(k3_lora_up, dim3(tiles_m * tiles_n), dim3(UP_THREADS), 0, st,
-                     static_cast<const uint16_t*>(lora_act), L.L2t, L.rank, M, L.N, Y, ldy, ydtype, tiles_n);
+                     static_cast<const uint16_t*>(lora_act), L.L2f, L.rank, M, L.N, Y, ldy, ydtype, tiles_n);
   return hipGetLastError();
 }
 

@@ -11,13 +11,13 @@ struct KernelLayer {
   int fmt;  // 0 INT4 g64, 1 MXFP4 g32
   const float* inv_s;
   const uint16_t* L1f;  // kernel 1's fragment order (svdq_prepare_lowrank_down)
-  const uint16_t* L2t;
+  const uint16_t* L2f;  // kernel 2's fragment order (svdq_prepare_lowrank)
   const uint8_t* qW;
   const void* sW;
 };
 
-// mma: the activation side in the matrix-core operand form (INT4 codes as FP8 bytes
-// [M][K] and split scale words; lora_act as bf16 hi/lo rows) instead of the packed
+// mma: the activation side in the matrix-core operand form (INT4 FP6 operand words,
+// fp16 scales; lora_act as bf16 hi/lo pairs in fragment order) instead of the packed
 // storage form (4-bit codes [M][K/2], fp16 / E8M0 scales, fp32 lora_act).
 hipError_t launch_k1(const KernelLayer& L, int64_t M, const uint16_t* X, int64_t ldx, uint8_t* qX,
                      void* sX, void* lora_act, bool mma, hipStream_t st);

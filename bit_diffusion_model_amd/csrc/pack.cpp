@@ -643,14 +643,17 @@ svdq_status svdq_prepare_lowrank_down(int64_t K, int32_t rank, const uint16_t* L
   return ok();
 }
 
-svdq_status svdq_prepare_lowrank(int64_t N, int32_t rank, const uint16_t* L2, uint16_t* L2t_out) {
+svdq_status svdq_prepare_lowrank(int64_t N, int32_t rank, const uint16_t* L2, uint16_t* L2f_out) {
   if (N < 1 || rank < 0) return fail(SVDQ_EINVAL, "need N >= 1 and rank >= 0");
   if (rank > SVDQ_MAX_RANK) return fail(SVDQ_EUNSUPPORTED, "rank exceeds %d", SVDQ_MAX_RANK);
   if (rank == 0) return ok();
-  if (!L2 || !L2t_out) return fail(SVDQ_EINVAL, "required pointer is NULL");
-  const int64_t r16 = (rank + 15) / 16 * 16;
-  for (int64_t n = 0; n < N; ++n)
-    for (int64_t j = 0; j < r16; ++j) L2t_out[n * r16 + j] = j < rank ? L2[j * N + n] : (uint16_t)0;
+  if (!L2 || !L2f_out) return fail(SVDQ_EINVAL, "required pointer is NULL");
+  const int64_t S = (rank + 15) / 16, N32 = (N + 31) / 32 * 32;
+  for (int64_t n = 0; n < N32; ++n)
+    for (int64_t j = 0; j < S * 16; ++j) {
+      const int64_t e = ((((n >> 5) * S + (j >> 4)) * 64 + (n & 31) + 32 * ((j >> 3) & 1)) << 3) + (j & 7);
+      L2f_out[e] = (j < rank && n < N) ? L2[j * N + n] : (uint16_t)0;
+    }
   return ok();
 }
 

@@ -32,7 +32,7 @@ class SvdqError(RuntimeError):
 class _Layer(ctypes.Structure):
     _fields_ = [
         ("K", ctypes.c_int64), ("N", ctypes.c_int64), ("rank", ctypes.c_int32), ("fmt", ctypes.c_int32),
-        ("inv_s", ctypes.c_void_p), ("L1f", ctypes.c_void_p), ("L2t", ctypes.c_void_p), ("qW", ctypes.c_void_p), ("sW", ctypes.c_void_p),
+        ("inv_s", ctypes.c_void_p), ("L1f", ctypes.c_void_p), ("L2f", ctypes.c_void_p), ("qW", ctypes.c_void_p), ("sW", ctypes.c_void_p),
     ]
 
 
@@ -179,12 +179,13 @@ def prepare_lowrank_down(L1t: np.ndarray):
 
 
 def prepare_lowrank(L2: np.ndarray):
-    """Device layout of the up projection: L2t [N][R16] (L2 transposed, zero-padded)."""
+    """Device layout of the up projection: L2 in kernel 2's fragment order (N rounded
+    up to 32 times R16 bf16, flat)."""
     L2 = np.ascontiguousarray(L2, dtype=np.uint16)
     r, N = L2.shape
-    L2t = np.zeros((N, r16(r)), np.uint16)
-    _check(lib().svdq_prepare_lowrank(N, r, _ptr(L2), _ptr(L2t)))
-    return L2t
+    L2f = np.zeros(((N + 31) // 32 * 32 * r16(r),), np.uint16)
+    _check(lib().svdq_prepare_lowrank(N, r, _ptr(L2), _ptr(L2f)))
+    return L2f
 
 
 def pad4(n: int) -> int:
@@ -247,14 +248,14 @@ class PackedLinear:
         self.inv_s = _upload(np.asarray(inv_s, np.float32), device)
         if rank > 0:
             self.L1f = _upload(prepare_lowrank_down(L1t), device)
-            self.L2t = _upload(prepare_lowrank(L2), device)
+            self.L2f = _upload(prepare_lowrank(L2), device)
         else:
-            self.L1f = self.L2t = None
+            self.L1f = self.L2f = None
         qk, sk = prepare_weights(self.K, self.N, self.fmt, qW, sW)
         self.qW = _upload(qk, device)
         self.sW = _upload(sk, device)
         self._c = _Layer(self.K, self.N, self.rank, self.fmt, _dptr(self.inv_s), _dptr(self.L1f),
-                         _dptr(self.L2t), _dptr(self.qW), _dptr(self.sW))
+                         _dptr(self.L2f), _dptr(self.qW), _dptr(self.sW))
 
     @classmethod
     def from_host_pack(cls, p: HostPack, device="cuda:0"):
@@ -287,7 +288,9 @@ class PackedLinear:
         la = None
         if self.rank:
             if form == ACT_MMA:
-                la = torch.empty((M, 2 * r16(self.rank)), dtype=torch.int16, device=self.device)
+                # bf16 hi/lo pairs in fragment order, M rounded up to 32 rows
+                la = torch.empty(((M + 31) // 32 * 32 * 2 * r16(self.rank),), dtype=torch.int16,
+                                 device=self.device)
             else:
                 la = torch.empty((M, r16(self.rank)), dtype=torch.float32, device=self.device)
         return qX, sX, la

@@ -71,8 +71,12 @@ typedef enum { SVDQ_F32 = 0, SVDQ_BF16 = 1 } svdq_dtype;
  *           MXFP4: the PACKED codes in token pairs: byte b of token m's code row at
  *           (m / 2) * K + (b / 64) * 128 + (m % 2) * 64 + b % 64 ((M rounded up to 2) *
  *           K/2 bytes); sX [K/32][Mp] E8M0 bytes.
- *           Both: lora_act rows of 2*R16 bf16, [R16 hi][R16 lo] with hi = bf16(v),
- *           lo = bf16(v - hi) of the fp32 value v. */
+ *           Both: lora_act as bf16 pairs hi = bf16(v), lo = bf16(v - hi) of the fp32
+ *           value v, in the matrix core's fragment order (each 16-byte load of kernel
+ *           2 then reads whole lines): with S = R16 / 16, the hi (p = 0) and lo (p = 1)
+ *           halves of value (m, j) at bf16 element
+ *             ((((m / 32) S + j / 16) 2 + p) 64 + m % 32 + 32 ((j / 8) % 2)) 8 + j % 8,
+ *           (M rounded up to 32) * R16 * 2 elements; the rows past M are not written. */
 typedef enum { SVDQ_ACT_PACKED = 0, SVDQ_ACT_MMA = 1 } svdq_act_form;
 
 #define SVDQ_MAX_RANK 128
@@ -84,19 +88,20 @@ typedef enum { SVDQ_ACT_PACKED = 0, SVDQ_ACT_MMA = 1 } svdq_act_form;
  *   inv_s  [K]        fp32  reciprocal smoothing factor, fp32(1 / fp32(s))
  *   L1f    R16 * K    bf16  down projection in kernel 1's fragment order, as
  *                           svdq_prepare_lowrank_down writes it
- *   L2t    [N][R16]   bf16  up projection transposed (L2^T), columns >= rank zero
+ *   L2f    N32 * R16  bf16  up projection in kernel 2's fragment order, as
+ *                           svdq_prepare_lowrank writes it (N32 = N rounded up to 32)
  *   qW                u8    residual codes along K per output channel, in the kernel
  *                           layout of svdq_prepare_weights (INT4: column pairs)
  *   sW                group-major scales as svdq_prepare_weights writes them: INT4
  *                           fp16, MXFP4 E8M0 bytes, rows padded to Np (16-byte aligned)
- * L1f/L2t may be NULL iff rank == 0. */
+ * L1f/L2f may be NULL iff rank == 0. */
 typedef struct svdq_layer {
   int64_t K, N;
   int32_t rank;
   int32_t fmt; /* svdq_format */
   const float* inv_s;
   const uint16_t* L1f;
-  const uint16_t* L2t;
+  const uint16_t* L2f;
   const uint8_t* qW;
   const void* sW;
 } svdq_layer;
@@ -163,10 +168,14 @@ svdq_status svdq_concat_lora(int64_t K, int64_t N, const float* s, int32_t rank,
  * bad sizes (K a positive multiple of 64) or NULL pointers (rank 0: nothing written). */
 svdq_status svdq_prepare_lowrank_down(int64_t K, int32_t rank, const uint16_t* L1t, uint16_t* L1f_out);
 
-/* Offline device layout of the up projection: transposed and zero-padded, L2t[n][j] = L2[j][n]
- * (j < rank), 0 (rank <= j < R16).  Host pointers; L2 [rank][N], L2t_out [N][R16] bf16.
- * EINVAL on bad sizes or NULL pointers (rank 0: nothing to write, pointers unused). */
-svdq_status svdq_prepare_lowrank(int64_t N, int32_t rank, const uint16_t* L2, uint16_t* L2t_out);
+/* Offline device layout of the up projection: L2 [rank][N] in the matrix core's
+ * fragment order, so that each 16-byte load of kernel 2 reads whole lines.  With S =
+ * R16 / 16:
+ *   L2f[(((n / 32) S + j / 16) 64 + n % 32 + 32 ((j / 8) % 2)) 8 + j % 8] = L2[j][n]
+ * for j < rank and n < N, and 0 for rank <= j < R16 or N <= n < N32 (N rounded up to
+ * 32).  Host pointers; L2 [rank][N], L2f_out N32 * R16 bf16.  EINVAL on bad sizes or
+ * NULL pointers (rank 0: nothing to write, pointers unused). */
+svdq_status svdq_prepare_lowrank(int64_t N, int32_t rank, const uint16_t* L2, uint16_t* L2f_out);
 
 /* Offline device layout of the residual weights (host pointers).  The values are those
  * of svdq_pack_weights / svdq_quantize_weights; only their encoding changes.  Np = N

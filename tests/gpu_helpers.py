@@ -81,14 +81,27 @@ def _fp6_fields(words6):
     return out
 
 
+def decode_lora_mma(la, M, rank):
+    """MMA-form lora_act (device tensor of any integer dtype) -> (hi, lo) bf16 bits [M][R16]
+    of the written rows: element ((((m / 32) S + j / 16) 2 + p) 64 + m % 32 + 32 ((j / 8) %
+    2)) 8 + j % 8, S = R16 / 16, p = 0 hi, 1 lo."""
+    R16 = (rank + 15) // 16 * 16
+    M32 = (M + 31) // 32 * 32
+    l = la.cpu().numpy().view(np.uint16).reshape(-1)[:M32 * 2 * R16]
+    # [m / 32][j / 16][p][j / 8 % 2][m % 32][j % 8] -> [p][m][j]
+    l = l.reshape(M32 // 32, R16 // 16, 2, 2, 32, 8).transpose(2, 0, 4, 1, 3, 5).reshape(2, M32, R16)
+    return l[0, :M], l[1, :M]
+
+
 def decode_mma(qX, sX, la, fmt, K, rank, M=None):
     """Kernel 1's MMA-form outputs (device tensors) decoded per the header's description:
     INT4: per token and group 64 bytes, half h at byte 32 h as words [f0 f1 f2 0 f3 f4 f5
     0]; the 192-bit f0..f5 hold 6-bit E2M3 fields (sign bit 5, exponent 0, |q| in bits
     0-2), field f carrying k = 32 h + 16 (f & 1) + (f >> 1); fp16 scale bits [K/64][Mp].
     MXFP4: codes in token pairs (byte b of token m at (m / 2) K + (b / 64) 128 + (m % 2)
-    64 + b % 64, M rounded up to 2 rows) and E8M0 bytes [K/32][Mp].  lora_act rows
-    [R16 hi][R16 lo] bf16.  Returns (codes or packed bytes [M][K/2], scales (float64
+    64 + b % 64, M rounded up to 2 rows) and E8M0 bytes [K/32][Mp].  lora_act bf16 hi/lo
+    pairs in fragment order: element ((((m / 32) S + j / 16) 2 + p) 64 + m % 32 + 32 ((j /
+    8) % 2)) 8 + j % 8, S = R16 / 16, p = 0 hi, 1 lo.  Returns (codes or packed bytes [M][K/2], scales (float64
     values [K/64][M] for INT4, bytes [K/32][M] for MXFP4), hi bits, lo bits)."""
     q = qX.cpu().numpy()
     if M is None:
@@ -119,7 +132,5 @@ def decode_mma(qX, sX, la, fmt, K, rank, M=None):
         out = rows, sb[:(K // 32) * Mp].reshape(K // 32, Mp)[:, :M]
     hi = lo = None
     if rank:
-        R16 = (rank + 15) // 16 * 16
-        l = la.cpu().numpy().view(np.uint16).reshape(M, 2, R16)
-        hi, lo = l[:, 0, :], l[:, 1, :]
+        hi, lo = decode_lora_mma(la, M, rank)
     return out[0], out[1], hi, lo

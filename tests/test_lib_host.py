@@ -137,10 +137,17 @@ def test_prepare_lowrank_layouts():
     rng = np.random.default_rng(2)
     from bit_diffusion_model_amd.workloads import bf16_bits_from_f64
     L2 = bf16_bits_from_f64(rng.standard_normal((5, 40)))
-    L2t = svdq.prepare_lowrank(L2)
-    assert L2t.shape == (40, 16)
-    np.testing.assert_array_equal(L2t[:, :5], L2.T)
-    assert not L2t[:, 5:].any()
+    f = svdq.prepare_lowrank(L2)
+    # fragment order: [column block of 32][k step of 16][lane = n % 32 + 32 (j / 8 % 2)][j % 8]
+    assert f.shape == (64 * 16,)
+    back = f.reshape(2, 1, 2, 32, 8).transpose(0, 3, 1, 2, 4).reshape(64, 16)  # [n][j]
+    np.testing.assert_array_equal(back[:40, :5], L2.T)
+    assert not back[:, 5:].any() and not back[40:].any()
+    L2b = bf16_bits_from_f64(rng.standard_normal((37, 70)))  # three k steps, three column blocks
+    f = svdq.prepare_lowrank(L2b)
+    back = f.reshape(3, 3, 2, 32, 8).transpose(0, 3, 1, 2, 4).reshape(96, 48)
+    np.testing.assert_array_equal(back[:70, :37], L2b.T)
+    assert not back[:, 37:].any() and not back[70:].any()
 
 
 def test_prepare_lowrank_down_layout():
@@ -277,5 +284,5 @@ def test_device_entry_points_validate_on_host():
     assert L.svdq_linear_forward(ref, 4, 16, 256, 16, 64, 0, 256, 10, None) == 1 and "workspace" in _err()
     assert L.svdq_debug_group_sums(ref, 4, 16, 0, 0, 5, 4, 16, None) == 1 and "window" in _err()
     # MMA form: FP6 operand words (M*K bytes), fp16 scales (2 bytes per group and row),
-    # 2*R16 bf16 per row
-    assert L.svdq_workspace_bytes(ref, 100) >= 100 * 256 + 4 * 100 * 2 + 100 * 16 * 4
+    # 2*R16 bf16 per row, rows rounded up to 32
+    assert L.svdq_workspace_bytes(ref, 100) >= 100 * 256 + 4 * 100 * 2 + 128 * 16 * 4
