@@ -104,7 +104,7 @@ def write_traffic(fetch_csv, write_csv):
          "copy_fetch_factor": ffac, "copy_write_factor": wfac, "fetch_bytes": fetch_b, "write_bytes": write_b,
          "bytes_per_launch": fetch_b + write_b, "dispatches": f["k2"][1],
          "command": "rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -- "
-                    "python bench.py --steps 3 --warmup 1 --no-cpu-baseline --calib-copy"}
+                    "python bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-compare --calib-copy"}
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as fh:
         json.dump(d, fh, indent=1)
@@ -157,6 +157,9 @@ def main():
     ap.add_argument("--ydtype", default="f32", choices=["f32", "bf16"])
     ap.add_argument("--cpu-rows", type=int, default=4608)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-compare", action="store_true",
+                    help="skip the rank-0 and unfused comparison forwards (counter runs: only the "
+                         "timed layer's kernels are dispatched)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after timing, run one plain device copy of 512 MiB (counter calibration)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -241,7 +244,7 @@ def main():
     # the unfused baseline (the low-rank branch as kernels of its own), timed in alternating
     # blocks of 20 forwards (medians of 5), so all three see the same clocks
     fr, f0, fu = [], [], []
-    for _ in range(5):
+    for _ in range(0 if args.no_compare else 5):
         for lyr, wsp, fused, out in ((lay, ws, True, fr), (lay0, ws0, True, f0), (lay, ws, False, fu)):
             lyr.forward(X, ydt, Y, wsp, fused=fused)
             ev0.record()
@@ -250,7 +253,9 @@ def main():
             ev1.record()
             torch.cuda.synchronize()
             out.append(ev0.elapsed_time(ev1) / 20)
-    ms_r, ms0, ms_u = float(np.median(fr)), float(np.median(f0)), float(np.median(fu))
+    med = lambda v: float(np.median(v)) if v else float("nan")
+    rnd = lambda x, d: None if x != x else round(x, d)  # NaN (not measured) -> null
+    ms_r, ms0, ms_u = med(fr), med(f0), med(fu)
 
     G = lay.group
     k2_ops = float(M) * N * (2.0 * K + 2.0 * r)
@@ -275,9 +280,9 @@ def main():
                      "frac": round(k2_tops / peak, 4), "traffic": traffic},
         "kernels": {"k1_us": round(t_k1 * 1e6, 2), "k2_us": round(t_k2 * 1e6, 2),
                     "k1_GBps": round(k1_bytes / t_k1 / 1e9, 1), "k1_hbm_frac": round(k1_bytes / t_k1 / 1e9 / PEAK_HBM_GBS, 4),
-                    "k2_TOPS": round(k2_tops, 2), "rank0_ms": round(ms0, 5),
-                    "fwd_ms_paired": round(ms_r, 5), "lowrank_overhead": round(ms_r / ms0 - 1.0, 4),
-                    "unfused_ms": round(ms_u, 5), "unfused_lowrank_overhead": round(ms_u / ms0 - 1.0, 4)},
+                    "k2_TOPS": round(k2_tops, 2), "rank0_ms": rnd(ms0, 5),
+                    "fwd_ms_paired": rnd(ms_r, 5), "lowrank_overhead": rnd(ms_r / ms0 - 1.0, 4),
+                    "unfused_ms": rnd(ms_u, 5), "unfused_lowrank_overhead": rnd(ms_u / ms0 - 1.0, 4)},
     }
     if args.calib_copy:
         src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device=dev)
