@@ -13,7 +13,9 @@ Sources:
   ch3chohch3.github.io, section "量化方案", the truncation equation;
 * static artifacts (weight scales, smoothing factor, low-rank branch) fixed offline:
   ch3chohch3.github.io post, section "量化方案", item 1;
-* LoRA adapters used without re-quantizing R: SVDQuant abstract (chatpaper.ai).
+* LoRA adapters used without re-quantizing R: SVDQuant abstract (chatpaper.ai);
+* R optimised repeatedly rather than from a single split: jeonghoonpark.com "SVDQuant"
+  review, the discussion after "Limitation", item on accuracy (refine_split).
 """
 from __future__ import annotations
 
@@ -63,6 +65,63 @@ def quantize_residual(R32: np.ndarray, fmt: str):
     return codes, np.ascontiguousarray(sc.T)
 
 
+def dequant_residual(codes: np.ndarray, sW: np.ndarray, fmt: str) -> np.ndarray:
+    """deq(Q(R)) [K][N] in fp64 from codes [N][K] and group-major scales [K/G][N]."""
+    sc = np.ascontiguousarray(np.asarray(sW).T)  # [N][K/G]
+    if fmt == "int4":
+        D = quant.dequant_int4(codes, sc, quant.INT4_GROUP)
+    elif fmt == "mxfp4":
+        D = quant.dequant_mxfp4(codes, sc, quant.FP4_GROUP)
+    else:
+        raise ValueError(fmt)
+    return np.ascontiguousarray(D.T)
+
+
+def split_error(W_hat: np.ndarray, L1b: np.ndarray, L2b: np.ndarray, fmt: str):
+    """The split's weight error with the stored factors and the quantized residual:
+    R = W_hat - L1b L2b (fp64), codes and scales of fp32(R), and
+    E = ||W_hat - L1b L2b - deq(Q(R))||_F (the quantization error of the decomposition,
+    review section 4.1 measures errors in the Frobenius norm)."""
+    R = W_hat - L1b @ L2b
+    codes, sW = quantize_residual(R.astype(np.float32), fmt)
+    D = dequant_residual(codes, sW, fmt)
+    return dict(R=R, codes=codes, sW=sW, D=D, err=float(np.linalg.norm(R - D)))
+
+
+def refine_split(W_hat: np.ndarray, rank: int, fmt: str, iters: int, keep_iterates: bool = False):
+    """Iterative refinement of the split (jeonghoonpark.com "SVDQuant" review, the
+    discussion after "Limitation", item on accuracy: the low-rank split is not taken
+    once, R is optimised repeatedly to reduce the quantization error).
+
+    Reading (the page names no algorithm): alternate between the residual's quantized
+    value and the low-rank factors.  Iterate 0 is the plain split of svd_split.  Iterate
+    t >= 1 takes the rank-r split of W_hat - deq(Q(R_{t-1})) (the part of W_hat the
+    quantized residual does not already carry), rounds its factors to bf16 and sets
+    R_t = W_hat - L1b L2b, so W_hat = L1b L2b + R_t still holds exactly.  Each iterate's
+    error is split_error's E; the iterate with the smallest E is kept (the first on
+    ties), so refinement never returns a worse pack than the plain split.
+
+    Returns (best: dict with L1, L2, L1b, L2b, R, codes, sW, err; errors: list of the
+    iters + 1 iterates' E; index of the best iterate).  keep_iterates: best["iterates"]
+    lists every iterate's target and factors.
+    """
+    best, errors, best_t, its = None, [], 0, []
+    target = W_hat
+    for t in range(iters + 1):
+        sp = svd_split(target, rank)
+        ev = split_error(W_hat, sp["L1b"], sp["L2b"], fmt)
+        errors.append(ev["err"])
+        if keep_iterates:
+            its.append(dict(target=target, L1=sp["L1"], L2=sp["L2"], L1b=sp["L1b"], L2b=sp["L2b"], err=ev["err"]))
+        if best is None or ev["err"] < best["err"]:
+            best = dict(L1=sp["L1"], L2=sp["L2"], L1b=sp["L1b"], L2b=sp["L2b"], **ev)
+            best_t = t
+        target = W_hat - ev["D"]
+    if keep_iterates:
+        best["iterates"] = its
+    return best, errors, best_t
+
+
 def pack_codes(codes: np.ndarray, fmt: str) -> np.ndarray:
     """Nibble-pack 4-bit codes along the last axis (INT4 as sign-magnitude nibbles)."""
     if fmt == "int4":
@@ -70,10 +129,11 @@ def pack_codes(codes: np.ndarray, fmt: str) -> np.ndarray:
     return quant.pack_nibbles(codes)
 
 
-def pack_weights(W_bits: np.ndarray, act_absmax, alpha: float, rank: int, fmt: str):
+def pack_weights(W_bits: np.ndarray, act_absmax, alpha: float, rank: int, fmt: str, refine_iters: int = 0):
     """Offline pack of one layer: s, W_hat, SVD split, R quantization.
 
-    act_absmax None means no smoothing (s = 1).  Returns a dict with
+    act_absmax None means no smoothing (s = 1).  refine_iters > 0 takes the split from
+    refine_split (then also: errors, the iterates' E, and best_iter).  Returns a dict with
       s64, s32, inv_s32   smoothing factor (fp64, stored fp32, reciprocal fp32)
       L1b [K][r], L2b [r][N] bf16 values (fp64), and their bit patterns L1_bits, L2_bits
       R (fp64), R32 (fp32) the residual
@@ -90,6 +150,12 @@ def pack_weights(W_bits: np.ndarray, act_absmax, alpha: float, rank: int, fmt: s
         s64, s32, inv_s32 = quant.smoothing_factors(act_absmax, w_absmax, alpha)
     W_hat = smoothed_weight(W_bits, s32)
     sp = svd_split(W_hat, rank)
+    extra = {}
+    if refine_iters > 0:
+        best, errors, best_t = refine_split(W_hat, rank, fmt, refine_iters)
+        sigma = sp["sigma"]
+        sp = dict(L1=best["L1"], L2=best["L2"], L1b=best["L1b"], L2b=best["L2b"], R=best["R"], sigma=sigma)
+        extra = dict(errors=errors, best_iter=best_t)
     R32 = sp["R"].astype(np.float32)
     codesW, sW = quantize_residual(R32, fmt)
     return dict(
@@ -97,7 +163,7 @@ def pack_weights(W_bits: np.ndarray, act_absmax, alpha: float, rank: int, fmt: s
         L1=sp["L1"], L2=sp["L2"], L1b=sp["L1b"], L2b=sp["L2b"],
         L1_bits=bf16_value_to_bits(sp["L1b"]), L2_bits=bf16_value_to_bits(sp["L2b"]),
         R=sp["R"], R32=R32, sigma=sp["sigma"],
-        codesW=codesW, qW=pack_codes(codesW, fmt), sW=sW,
+        codesW=codesW, qW=pack_codes(codesW, fmt), sW=sW, **extra,
     )
 
 
