@@ -499,9 +499,90 @@ svdq_status svdq_quantize_weights(int64_t K, int64_t N, const float* R, int32_t 
   return ok();
 }
 
-svdq_status svdq_pack_weights(int64_t K, int64_t N, const uint16_t* W, const float* act_absmax, float alpha,
-                              int32_t rank, int32_t fmt, float* s_out, float* inv_s_out, uint16_t* L1t_out,
-                              uint16_t* L2_out, uint8_t* qW_out, void* sW_out, float* R_out) {
+}  // extern "C"
+
+namespace svdq {
+namespace {
+
+// Rank-r split of a target T [K][N] (fp64) from the Gram matrix of its smaller side:
+// L1 = U_r Sigma_r, L2 = V_r^T, both rounded to bf16 (bits into L1t_bits [rank][K],
+// L2_bits [rank][N]; values into L1 [K][rank], L2 [rank][N]).
+void split_rank(const double* T, int64_t K, int64_t N, int32_t rank, std::vector<double>& L1,
+                std::vector<double>& L2, uint16_t* L1t_bits, uint16_t* L2_bits) {
+  const bool left = K <= N;
+  const int64_t n = left ? K : N, L = left ? N : K;
+  std::vector<double> At;
+  const double* A = T;
+  if (!left) {
+    At.resize((size_t)N * K);
+    parallel_for(N, [&](int64_t c) {
+      for (int64_t k = 0; k < K; ++k) At[c * K + k] = T[k * N + c];
+    });
+    A = At.data();
+  }
+  std::vector<double> G((size_t)n * n);
+  gram(A, n, L, G.data());
+  std::vector<double> vals(rank), vecs((size_t)rank * n);
+  top_eigen(G.data(), n, rank, vals.data(), vecs.data());
+  const double smax = std::sqrt(std::max(vals[0], 0.0));
+  parallel_for(rank, [&](int64_t t) {
+    const double sig = std::sqrt(std::max(vals[t], 0.0));
+    const double* q = &vecs[(size_t)t * n];
+    const bool keep = sig > 1e-300 && sig > 1e-15 * smax;
+    if (left) {  // q = u_t;  L1[:,t] = sig u_t;  L2[t,:] = T^T u_t / sig
+      for (int64_t k = 0; k < K; ++k) L1[k * rank + t] = keep ? sig * q[k] : 0.0;
+      for (int64_t c = 0; c < N; ++c) {
+        double acc = 0.0;
+        if (keep)
+          for (int64_t k = 0; k < K; ++k) acc += T[k * N + c] * q[k];
+        L2[t * N + c] = keep ? acc / sig : 0.0;
+      }
+    } else {  // q = v_t;  L2[t,:] = v_t;  L1[:,t] = T v_t
+      for (int64_t c = 0; c < N; ++c) L2[t * N + c] = keep ? q[c] : 0.0;
+      for (int64_t k = 0; k < K; ++k) {
+        double acc = 0.0;
+        if (keep)
+          for (int64_t c = 0; c < N; ++c) acc += T[k * N + c] * q[c];
+        L1[k * rank + t] = acc;
+      }
+    }
+  });
+  for (int64_t k = 0; k < K; ++k)
+    for (int64_t t = 0; t < rank; ++t) {
+      const uint16_t b = double_to_bf16(L1[k * rank + t]);
+      L1t_bits[t * K + k] = b;
+      L1[k * rank + t] = bf16_to_double(b);
+    }
+  for (int64_t t = 0; t < rank; ++t)
+    for (int64_t c = 0; c < N; ++c) {
+      const uint16_t b = double_to_bf16(L2[t * N + c]);
+      L2_bits[t * N + c] = b;
+      L2[t * N + c] = bf16_to_double(b);
+    }
+}
+
+// deq(Q(R)) [K][N] from codes qW [N][K/2] and scales sW [K/G][N].
+void dequantize_residual(int64_t K, int64_t N, int fmt, const uint8_t* qW, const void* sW, double* D) {
+  static const double kE2M1[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+  const int G = group_of(fmt);
+  parallel_for(N, [&](int64_t n) {
+    for (int64_t k = 0; k < K; ++k) {
+      const uint8_t byte = qW[n * (K / 2) + k / 2];
+      const int nib = (k & 1) ? byte >> 4 : byte & 15;
+      const int64_t g = k / G;
+      double v;
+      if (fmt == SVDQ_INT4_G64) v = (double)(nib & 7) * f16_to_double(static_cast<const uint16_t*>(sW)[g * N + n]);
+      else v = std::ldexp(kE2M1[nib & 7], (int)static_cast<const uint8_t*>(sW)[g * N + n] - 127);
+      D[k * N + n] = (nib & 8) ? -v : v;
+    }
+  });
+}
+
+// The pack with `iters` refinement iterates after the plain split (iters = 0: the plain
+// split alone); each iterate's E into err_out[t] when given.
+svdq_status pack_impl(int64_t K, int64_t N, const uint16_t* W, const float* act_absmax, float alpha, int32_t rank,
+                      int32_t fmt, int32_t iters, float* s_out, float* inv_s_out, uint16_t* L1t_out, uint16_t* L2_out,
+                      uint8_t* qW_out, void* sW_out, float* R_out, double* err_out) {
   svdq_status st = check_dims(K, N, fmt);
   if (st != SVDQ_OK) return st;
   if (!W || !s_out || !inv_s_out || !qW_out || !sW_out) return fail(SVDQ_EINVAL, "required pointer is NULL");
@@ -509,6 +590,7 @@ svdq_status svdq_pack_weights(int64_t K, int64_t N, const uint16_t* W, const flo
   if (rank < 0 || rank > SVDQ_MAX_RANK || rank > std::min(K, N))
     return fail(SVDQ_EINVAL, "rank must be in [0, min(K, N, %d)]", SVDQ_MAX_RANK);
   if (rank > 0 && (!L1t_out || !L2_out)) return fail(SVDQ_EINVAL, "L1t_out and L2_out required when rank > 0");
+  if (iters < 0 || iters > 64) return fail(SVDQ_EINVAL, "iters must be in [0, 64]");
   for (int64_t i = 0; i < K * N; ++i)
     if (!std::isfinite(bf16_to_double(W[i]))) return fail(SVDQ_ENUMERIC, "W has a non-finite value at %lld", (long long)i);
   if (act_absmax)
@@ -535,73 +617,85 @@ svdq_status svdq_pack_weights(int64_t K, int64_t N, const uint16_t* W, const flo
     for (int64_t n = 0; n < N; ++n) What[k * N + n] = s * bf16_to_double(W[k * N + n]);
   });
 
-  // truncated SVD from the smaller Gram matrix
+  const int G = group_of(fmt);
+  const size_t nq = (size_t)N * (K / 2), ns = (size_t)(K / G) * N * (fmt == SVDQ_INT4_G64 ? 2 : 1);
   std::vector<double> L1((size_t)K * std::max(rank, 1)), L2((size_t)std::max(rank, 1) * N);
-  if (rank > 0) {
-    const bool left = K <= N;
-    const int64_t n = left ? K : N, L = left ? N : K;
-    std::vector<double> At;
-    const double* A = What.data();
-    if (!left) {
-      At.resize((size_t)N * K);
-      parallel_for(N, [&](int64_t c) {
-        for (int64_t k = 0; k < K; ++k) At[c * K + k] = What[k * N + c];
-      });
-      A = At.data();
-    }
-    std::vector<double> G((size_t)n * n);
-    gram(A, n, L, G.data());
-    std::vector<double> vals(rank), vecs((size_t)rank * n);
-    top_eigen(G.data(), n, rank, vals.data(), vecs.data());
-    const double smax = std::sqrt(std::max(vals[0], 0.0));
-    parallel_for(rank, [&](int64_t t) {
-      const double sig = std::sqrt(std::max(vals[t], 0.0));
-      const double* q = &vecs[(size_t)t * n];
-      const bool keep = sig > 1e-300 && sig > 1e-15 * smax;
-      if (left) {  // q = u_t;  L1[:,t] = sig u_t;  L2[t,:] = W_hat^T u_t / sig
-        for (int64_t k = 0; k < K; ++k) L1[k * rank + t] = keep ? sig * q[k] : 0.0;
-        for (int64_t c = 0; c < N; ++c) {
-          double acc = 0.0;
-          if (keep)
-            for (int64_t k = 0; k < K; ++k) acc += What[k * N + c] * q[k];
-          L2[t * N + c] = keep ? acc / sig : 0.0;
-        }
-      } else {  // q = v_t;  L2[t,:] = v_t;  L1[:,t] = W_hat v_t
-        for (int64_t c = 0; c < N; ++c) L2[t * N + c] = keep ? q[c] : 0.0;
-        for (int64_t k = 0; k < K; ++k) {
-          double acc = 0.0;
-          if (keep)
-            for (int64_t c = 0; c < N; ++c) acc += What[k * N + c] * q[c];
-          L1[k * rank + t] = acc;
-        }
-      }
-    });
-    // round the factors to bf16; R = W_hat - L1b L2b
-    for (int64_t k = 0; k < K; ++k)
-      for (int64_t t = 0; t < rank; ++t) {
-        const uint16_t b = double_to_bf16(L1[k * rank + t]);
-        L1t_out[t * K + k] = b;
-        L1[k * rank + t] = bf16_to_double(b);
-      }
-    for (int64_t t = 0; t < rank; ++t)
-      for (int64_t c = 0; c < N; ++c) {
-        const uint16_t b = double_to_bf16(L2[t * N + c]);
-        L2_out[t * N + c] = b;
-        L2[t * N + c] = bf16_to_double(b);
-      }
+  std::vector<uint16_t> b1((size_t)std::max(rank, 1) * K), b2((size_t)std::max(rank, 1) * N);
+  std::vector<double> Rd((size_t)K * N), D, T;
+  std::vector<float> R32((size_t)K * N);
+  std::vector<uint8_t> q(nq), sc(ns);
+  if (iters > 0) {
+    D.resize((size_t)K * N);
+    T.resize((size_t)K * N);
+  }
+  double best = 0.0;
+  for (int32_t it = 0; it <= iters; ++it) {
+    // iterate 0 splits W_hat; iterate t >= 1 splits W_hat - deq(Q(R_{t-1}))
+    const double* target = it == 0 ? What.data() : T.data();
+    if (rank > 0) split_rank(target, K, N, rank, L1, L2, b1.data(), b2.data());
+    // R = W_hat - L1b L2b with the rounded factors
     parallel_for(K, [&](int64_t k) {
       for (int64_t c = 0; c < N; ++c) {
         double acc = 0.0;
         for (int64_t t = 0; t < rank; ++t) acc += L1[k * rank + t] * L2[t * N + c];
-        What[k * N + c] -= acc;
+        Rd[k * N + c] = What[k * N + c] - acc;
       }
     });
+    for (size_t i = 0; i < R32.size(); ++i) R32[i] = (float)Rd[i];
+    quantize_residual(K, N, R32.data(), fmt, q.data(), sc.data());
+    double err = 0.0;
+    if (iters > 0 || err_out) {
+      if (D.empty()) D.resize((size_t)K * N);
+      dequantize_residual(K, N, fmt, q.data(), sc.data(), D.data());
+      std::vector<double> row(K);
+      parallel_for(K, [&](int64_t k) {
+        double a = 0.0;
+        for (int64_t c = 0; c < N; ++c) {
+          const double d = Rd[k * N + c] - D[k * N + c];
+          a += d * d;
+        }
+        row[k] = a;
+      });
+      for (int64_t k = 0; k < K; ++k) err += row[k];  // fixed order
+      err = std::sqrt(err);
+      if (err_out) err_out[it] = err;
+    }
+    if (it == 0 || err < best) {  // keep the first iterate with the smallest error
+      best = err;
+      if (rank > 0) {
+        std::memcpy(L1t_out, b1.data(), sizeof(uint16_t) * (size_t)rank * K);
+        std::memcpy(L2_out, b2.data(), sizeof(uint16_t) * (size_t)rank * N);
+      }
+      std::memcpy(qW_out, q.data(), nq);
+      std::memcpy(sW_out, sc.data(), ns);
+      if (R_out) std::memcpy(R_out, R32.data(), sizeof(float) * R32.size());
+    }
+    if (it < iters)
+      parallel_for(K, [&](int64_t k) {
+        for (int64_t c = 0; c < N; ++c) T[k * N + c] = What[k * N + c] - D[k * N + c];
+      });
   }
-  std::vector<float> R32((size_t)K * N);
-  for (size_t i = 0; i < R32.size(); ++i) R32[i] = (float)What[i];
-  if (R_out) std::memcpy(R_out, R32.data(), sizeof(float) * R32.size());
-  quantize_residual(K, N, R32.data(), fmt, qW_out, sW_out);
   return ok();
+}
+
+}  // namespace
+}  // namespace svdq
+
+extern "C" {
+
+svdq_status svdq_pack_weights(int64_t K, int64_t N, const uint16_t* W, const float* act_absmax, float alpha,
+                              int32_t rank, int32_t fmt, float* s_out, float* inv_s_out, uint16_t* L1t_out,
+                              uint16_t* L2_out, uint8_t* qW_out, void* sW_out, float* R_out) {
+  return pack_impl(K, N, W, act_absmax, alpha, rank, fmt, 0, s_out, inv_s_out, L1t_out, L2_out, qW_out, sW_out,
+                   R_out, nullptr);
+}
+
+svdq_status svdq_pack_weights_refined(int64_t K, int64_t N, const uint16_t* W, const float* act_absmax,
+                                      float alpha, int32_t rank, int32_t fmt, int32_t iters, float* s_out,
+                                      float* inv_s_out, uint16_t* L1t_out, uint16_t* L2_out, uint8_t* qW_out,
+                                      void* sW_out, float* R_out, double* err_out) {
+  return pack_impl(K, N, W, act_absmax, alpha, rank, fmt, iters, s_out, inv_s_out, L1t_out, L2_out, qW_out, sW_out,
+                   R_out, err_out);
 }
 
 svdq_status svdq_concat_lora(int64_t K, int64_t N, const float* s, int32_t rank, const uint16_t* L1t,

@@ -39,7 +39,7 @@ class _Layer(ctypes.Structure):
 _lib = None
 
 EXPORTS = [
-    "svdq_last_error", "svdq_act_absmax", "svdq_weight_sizes", "svdq_pack_weights",
+    "svdq_last_error", "svdq_act_absmax", "svdq_weight_sizes", "svdq_pack_weights", "svdq_pack_weights_refined",
     "svdq_quantize_weights", "svdq_concat_lora", "svdq_prepare_lowrank_down", "svdq_prepare_lowrank",
     "svdq_prepare_weights",
     "svdq_quantize_act_lora_down", "svdq_gemm_w4a4_lora_up", "svdq_gemm_workspace_bytes", "svdq_workspace_bytes",
@@ -61,6 +61,7 @@ def lib():
         "svdq_act_absmax": (I32, [I64, I64, P, I64, P]),
         "svdq_weight_sizes": (I32, [I64, I64, I32, P, P]),
         "svdq_pack_weights": (I32, [I64, I64, P, P, F, I32, I32, P, P, P, P, P, P, P]),
+        "svdq_pack_weights_refined": (I32, [I64, I64, P, P, F, I32, I32, I32, P, P, P, P, P, P, P, P]),
         "svdq_quantize_weights": (I32, [I64, I64, P, I32, P, P]),
         "svdq_concat_lora": (I32, [I64, I64, P, I32, P, P, I32, P, P, F, P, P]),
         "svdq_prepare_lowrank_down": (I32, [I64, I32, P, P]),
@@ -121,10 +122,13 @@ class HostPack:
     qW: np.ndarray      # u8 [N][K/2]
     sW: np.ndarray      # fp16 bits u16 or E8M0 u8 [K/G][N]
     R: Optional[np.ndarray] = None
+    errors: Optional[np.ndarray] = None  # refined packs: each iterate's split error E
 
 
 def pack_weights(W_bits: np.ndarray, act_absmax_: Optional[np.ndarray], alpha: float, rank: int,
-                 fmt: int, want_R: bool = False) -> HostPack:
+                 fmt: int, want_R: bool = False, refine_iters: int = 0) -> HostPack:
+    """svdq_pack_weights, or with refine_iters > 0 svdq_pack_weights_refined (the
+    iterates' errors in .errors)."""
     W = np.ascontiguousarray(W_bits, dtype=np.uint16)
     K, N = W.shape
     s = np.empty(K, np.float32)
@@ -136,6 +140,12 @@ def pack_weights(W_bits: np.ndarray, act_absmax_: Optional[np.ndarray], alpha: f
     sW = np.empty((K // G, N), np.uint16 if fmt == INT4_G64 else np.uint8)
     R = np.empty((K, N), np.float32) if want_R else None
     a = None if act_absmax_ is None else np.ascontiguousarray(act_absmax_, dtype=np.float32)
+    if refine_iters > 0:
+        errs = np.empty(refine_iters + 1, np.float64)
+        _check(lib().svdq_pack_weights_refined(K, N, _ptr(W), _ptr(a), float(alpha), rank, fmt, int(refine_iters),
+                                               _ptr(s), _ptr(inv), _ptr(L1t), _ptr(L2), _ptr(qW), _ptr(sW), _ptr(R),
+                                               _ptr(errs)))
+        return HostPack(K, N, rank, fmt, s, inv, L1t, L2, qW, sW, R, errs)
     _check(lib().svdq_pack_weights(K, N, _ptr(W), _ptr(a), float(alpha), rank, fmt, _ptr(s), _ptr(inv),
                                    _ptr(L1t), _ptr(L2), _ptr(qW), _ptr(sW), _ptr(R)))
     return HostPack(K, N, rank, fmt, s, inv, L1t, L2, qW, sW, R)

@@ -141,6 +141,21 @@ svdq_status svdq_pack_weights(int64_t K, int64_t N, const uint16_t* W, const flo
                               float* inv_s_out, uint16_t* L1t_out, uint16_t* L2_out,
                               uint8_t* qW_out, void* sW_out, float* R_out);
 
+/* Offline pack with iterative refinement of the split (jeonghoonpark.com "SVDQuant"
+ * review, the discussion after "Limitation", item on accuracy: R optimised repeatedly
+ * rather than taken from one split).  Iterate 0 is svdq_pack_weights' split; iterate
+ * t = 1..iters takes the rank-r split of W_hat - deq(Q(R_{t-1})), rounds its factors to
+ * bf16 and sets R_t = W_hat - L1 L2.  The outputs are those of the iterate with the
+ * smallest E = ||W_hat - L1 L2 - deq(Q(R))||_F (Frobenius norm, fp64; the first on ties),
+ * so the result is never worse than the plain split, and iters = 0 gives exactly
+ * svdq_pack_weights' outputs.  err_out: optional host double [iters + 1], the E of every
+ * iterate.  Each iterate costs about one plain pack.  Arguments, outputs and errors as
+ * for svdq_pack_weights; EINVAL for iters outside [0, 64]. */
+svdq_status svdq_pack_weights_refined(int64_t K, int64_t N, const uint16_t* W, const float* act_absmax,
+                                      float alpha, int32_t rank, int32_t fmt, int32_t iters, float* s_out,
+                                      float* inv_s_out, uint16_t* L1t_out, uint16_t* L2_out, uint8_t* qW_out,
+                                      void* sW_out, float* R_out, double* err_out);
+
 /* Quantize a given fp32 residual R [K][N] (host) per output column in groups along K:
  * the last step of svdq_pack_weights on its own.  Outputs as in svdq_pack_weights. */
 svdq_status svdq_quantize_weights(int64_t K, int64_t N, const float* R, int32_t fmt,

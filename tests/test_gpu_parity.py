@@ -229,3 +229,17 @@ def test_unfused_baseline_matches_oracle(shape):
     excess = np.abs(Yb - Yref) - (2.0 ** -8 * (np.abs(Yres) + np.abs(Yref)) + TOL_Y * rms)
     log(f"  bf16 max|err|/RMS = {rel_err(Yb, Yref):.3e}, worst excess over the bound {excess.max() / rms:.3e} RMS")
     assert excess.max() <= 0
+
+
+def test_refined_pack_forward():
+    """A pack from the refined split runs through the same kernels to the same bar."""
+    from oracle import pack as opack, quant as oquant
+
+    wl = random_layer(300, 384, 520, 16, 77, fmt="int4", x_out=3, w_out=2)
+    p = opack.pack_weights(wl.W, oquant.channel_absmax_cols(wl.calib), wl.alpha, 16, "int4", refine_iters=3)
+    log(f"refined pack: errors {p['errors']}, kept iterate {p['best_iter']}")
+    lay = layer_from_oracle(p)
+    Y = lay.forward(to_dev_bf16(wl.X)).cpu().numpy().astype(np.float64)
+    e = rel_err(Y, oforward.forward(wl.X, p)["Y"])
+    log(f"  max|err|/RMS = {e:.3e}")
+    assert e <= TOL_Y

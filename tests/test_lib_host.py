@@ -121,6 +121,60 @@ def test_pack_matches_oracle_subspace(K, N, r, fmt):
         np.testing.assert_array_equal(lib.sW, orc["sW"])
 
 
+def _lib_split_error(hp, W_bits, fmt):
+    """E = ||W_hat - L1 L2 - deq(Q(R))||_F of a library pack, recomputed by the oracle
+    from the pack's own s, factors, codes and scales."""
+    Wh = opack.smoothed_weight(W_bits, hp.s)
+    nib = oquant.unpack_nibbles(hp.qW)
+    sc = np.ascontiguousarray(hp.sW.T)
+    if fmt == "int4":
+        D = oquant.dequant_int4(oquant.nibble_to_int4(nib), sc)
+    else:
+        D = oquant.dequant_mxfp4(nib, sc)
+    P = bf16_to_f64(hp.L1t).T @ bf16_to_f64(hp.L2) if hp.rank else 0.0
+    return float(np.linalg.norm(Wh - P - D.T))
+
+
+@pytest.mark.parametrize("fmt", ["int4", "mxfp4"])
+def test_refined_pack(fmt):
+    """svdq_pack_weights_refined: iters = 0 is svdq_pack_weights bit for bit; with
+    iterations, the errors it reports follow the oracle's refinement, and the kept pack
+    attains the smallest of them."""
+    wl = random_layer(64, 256, 96, 8, 3, fmt=fmt, x_out=3, w_out=2)
+    a = svdq.act_absmax(wl.calib)
+    F = svdq.FMT[fmt]
+    plain = svdq.pack_weights(wl.W, a, wl.alpha, 8, F, want_R=True)
+    r0 = svdq.pack_weights(wl.W, a, wl.alpha, 8, F, want_R=True, refine_iters=1)
+    hp = svdq.pack_weights(wl.W, a, wl.alpha, 8, F, want_R=True, refine_iters=4)
+    assert r0.errors[0] == hp.errors[0]
+    assert r0.errors[0] == pytest.approx(_lib_split_error(plain, wl.W, fmt), rel=1e-9)
+    if np.argmin(r0.errors) == 0:
+        for f in ("L1t", "L2", "qW", "sW", "R"):
+            np.testing.assert_array_equal(getattr(r0, f), getattr(plain, f))
+    # the oracle's refinement on the same smoothed weight
+    orc = opack.pack_weights(wl.W, oquant.channel_absmax_cols(wl.calib), wl.alpha, 8, fmt, refine_iters=4)
+    np.testing.assert_allclose(hp.errors, orc["errors"], rtol=1e-4)
+    assert int(np.argmin(hp.errors)) == orc["best_iter"]
+    assert _lib_split_error(hp, wl.W, fmt) == pytest.approx(hp.errors.min(), rel=1e-9)
+    assert hp.errors.min() < hp.errors[0]
+    for bad in (-1, 65):
+        with pytest.raises(svdq.SvdqError):
+            _refined_raw(wl.W, a, wl.alpha, 8, F, bad)
+
+
+def _refined_raw(W, a, alpha, rank, F, iters):
+    K, N = W.shape
+    G = svdq.GROUP[F]
+    s, inv = np.empty(K, np.float32), np.empty(K, np.float32)
+    L1t, L2 = np.zeros((rank, K), np.uint16), np.zeros((rank, N), np.uint16)
+    qW = np.empty((N, K // 2), np.uint8)
+    sW = np.empty((K // G, N), np.uint16 if F == svdq.INT4_G64 else np.uint8)
+    W = np.ascontiguousarray(W, dtype=np.uint16)
+    svdq._check(svdq.lib().svdq_pack_weights_refined(K, N, svdq._ptr(W), svdq._ptr(a), float(alpha), rank, F, iters,
+                                                     svdq._ptr(s), svdq._ptr(inv), svdq._ptr(L1t), svdq._ptr(L2),
+                                                     svdq._ptr(qW), svdq._ptr(sW), None, None))
+
+
 def test_concat_lora_bit_exact():
     wl = random_layer(16, 256, 72, 8, 91, lora_rank=4)
     orc = opack.pack_weights(wl.W, oquant.channel_absmax_cols(wl.X), wl.alpha, wl.rank, "int4")
