@@ -336,6 +336,9 @@ def test_device_entry_points_validate_on_host():
     assert L.svdq_gemm_w4a4_lora_up(ctypes.byref(unal), 4, 0, 16, 16, 16, 16, 64, 0, None, 0, None) == 1 and "sW" in _err()
     assert L.svdq_gemm_w4a4_lora_up(ref, 4, 0, 16, 16, 16, 16, 64, 0, 8, 1 << 20, None) == 1 and "workspace" in _err()
     assert L.svdq_linear_forward(ref, 4, 16, 256, 16, 64, 0, 256, 10, None) == 1 and "workspace" in _err()
+    assert L.svdq_linear_forward_unfused(ref, 4, 16, 256, 16, 64, 0, 256, 10, None) == 1 and "workspace" in _err()
+    assert L.svdq_linear_forward_unfused(ref, 0, 16, 256, 16, 64, 0, None, 0, None) == 0  # M = 0: no-op
+    assert L.svdq_linear_forward_unfused(ref, -1, 16, 256, 16, 64, 0, None, 0, None) == 1
     assert L.svdq_debug_group_sums(ref, 4, 16, 0, 0, 5, 4, 16, None) == 1 and "window" in _err()
     # MMA form: FP6 operand words (M*K bytes), fp16 scales (2 bytes per group and row),
     # 2*R16 bf16 per row, rows rounded up to 32
