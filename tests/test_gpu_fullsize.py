@@ -8,7 +8,8 @@ the oracle:
 * kernel 2 (INT4): exact integer group sums on an interior window and on the ragged
   last tiles;
 * the layer output: sampled rows x columns (the oracle computes them one by one),
-  max |err| <= 2e-2 x RMS of the sampled reference.
+  max |err| <= 2e-2 x RMS of the sampled reference; the unfused baseline's output to
+  the same bar and within 1e-5 x RMS of the fused output everywhere.
 The pack artifacts come from the oracle's own pack (LAPACK SVD), so no oracle input
 comes from the HIP path.  The three workloads that share the QKV weight share one
 oracle SVD.
@@ -91,3 +92,10 @@ def test_full_size_layer(name):
     e = rel_err(Yg, out["Y"])
     log(f"  sampled output max|err|/RMS = {e:.3e}")
     assert e <= TOL_Y
+    # the unfused baseline at full size: the same bar, and the fused output up to the
+    # order of the two fp32 terms, on every element
+    Yu = lay.forward(X, fused=False)
+    eu = rel_err(Yu.cpu().numpy()[np.ix_(rows, cols)].astype(np.float64), out["Y"])
+    d = float((Yu - Y).abs().max()) / float(Y.double().pow(2).mean().sqrt())
+    log(f"  unfused baseline: sampled max|err|/RMS = {eu:.3e}, max|Y_unfused - Y|/RMS = {d:.3e}")
+    assert eu <= TOL_Y and d <= 1e-5
