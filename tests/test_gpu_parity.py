@@ -243,3 +243,36 @@ def test_refined_pack_forward():
     e = rel_err(Y, oforward.forward(wl.X, p)["Y"])
     log(f"  max|err|/RMS = {e:.3e}")
     assert e <= TOL_Y
+
+
+@pytest.mark.parametrize("ydtype", [svdq.F32, svdq.BF16], ids=["f32", "bf16"])
+def test_unfused_strided_rows_and_padded_output(ydtype):
+    """Both forwards with X rows strided past K and Y rows padded past N: the padding
+    columns of Y are never written (kernel 2's store and the up-projection kernel's
+    read-modify-write both mask columns >= N), and the two agree."""
+    import torch
+
+    M, K, N, r = 70, 256, 100, 16
+    wl = random_layer(M, K, N, r, 21, x_out=2)
+    p = oracle_pack(wl)
+    lay = layer_from_oracle(p)
+    Xp = np.zeros((M, K + 64), np.uint16)
+    Xp[:, :K] = wl.X
+    Xd = to_dev_bf16(Xp)[:, :K]
+    dt = torch.float32 if ydtype == svdq.F32 else torch.bfloat16
+    outs = []
+    for fused in (True, False):
+        Yfull = torch.full((M, N + 28), 7.0, dtype=dt, device="cuda:0")
+        Y = Yfull[:, :N]
+        lay.forward(Xd, ydtype=ydtype, out=Y, fused=fused)
+        assert bool((Yfull[:, N:] == 7.0).all()), "padding columns written"
+        outs.append(Y.float().cpu().numpy().astype(np.float64))
+    Yref = oforward.forward(wl.X, p)["Y"]
+    rms = np.sqrt(np.mean(Yref ** 2))
+    for Yg in outs:
+        if ydtype == svdq.F32:
+            assert rel_err(Yg, Yref) <= TOL_Y
+        else:  # bf16 output: half an ulp per rounding (two for the unfused form), on top of the bar
+            assert np.all(np.abs(Yg - Yref) <= 2.0 ** -7 * np.abs(Yref) + TOL_Y * rms)
+    if ydtype == svdq.F32:
+        assert np.abs(outs[0] - outs[1]).max() <= 1e-5 * rms
