@@ -175,7 +175,7 @@ def concat_lora(p: HostPack, A_bits: np.ndarray, B_bits: np.ndarray, scale: floa
 
 
 def r16(rank: int) -> int:
-    """rank rounded up to a multiple of 16 (padded width of lora_act and L2t)."""
+    """rank rounded up to a multiple of 16 (padded width of lora_act, L1f and L2f)."""
     return (rank + 15) // 16 * 16
 
 
