@@ -698,36 +698,54 @@ __global__ __launch_bounds__(SShape<FMT>::NT, 8 / SShape<FMT>::NW) __attribute__
   };
   const int nk = kend - kbeg;
   int k = kbeg;
-  issue(kbeg, lds0);
-  issue(kbeg + 1 < kend ? kbeg + 1 : kend - 1, lds1);
   // ---- low-rank up projection first: acc = lora_act[rows, :] L2[:, cols] ----------------
-  // It depends on nothing of the main loop, so it runs while the first two stages' loads
-  // are in flight (its own loads queue behind them) instead of after the last stage.
+  // It depends on nothing of the main loop.  The operands of its first two k steps are
+  // loaded before the first two stages' panels, so the MFMAs wait only for their own
+  // loads while the panels stay in flight (loaded after the panels, they would wait
+  // for those too: a wave's loads complete in issue order).
   // v_mfma_f32_32x32x16_bf16 on lora_act's bf16 hi/lo pairs and L2f, both in fragment
   // order: for a block of 32 rows (columns) and a k step of 16, the 64 lanes' operands
   // are 1 KB contiguous (lora_act: hi, then lo), so every load reads whole lines.  The
   // range covers whole 32-row blocks; rows past M hold whatever the workspace held
   // (their outputs are not stored), columns past N are zero.
-  if (rank > 0 && part <= 0) {
-    const int R16 = (rank + 15) & ~15;
-    const __amdgpu_buffer_rsrc_t rL = make_rsrc(lora_act + m0 * 2 * R16, (uint32_t)(((rowsA + 31) & ~31) * R16 * 4));
-    const __amdgpu_buffer_rsrc_t rU = make_rsrc(L2 + n0 * R16, (uint32_t)(((rowsB + 31) & ~31) * R16 * 2));
-    for (int k0 = 0; k0 < R16; k0 += 16) {
-      v8bf bl[TJ];
+  const bool lora = rank > 0 && part <= 0;  // once per tile: whole, or the first part
+  const int R16 = (rank + 15) & ~15;
+  const __amdgpu_buffer_rsrc_t rL = make_rsrc(lora_act + m0 * 2 * R16, (uint32_t)(((rowsA + 31) & ~31) * R16 * 4));
+  const __amdgpu_buffer_rsrc_t rU = make_rsrc(L2 + n0 * R16, (uint32_t)(((rowsB + 31) & ~31) * R16 * 2));
+  auto lora_load = [&](int s, v8bf (&b)[TJ], v8bf (&a)[TI][2]) {
 #pragma unroll
-      for (int j = 0; j < TJ; ++j)
-        bl[j] = __builtin_bit_cast(v8bf, buf_load16(rU, (uint32_t)(((((wn >> 5) + j) * (R16 >> 4) + (k0 >> 4)) * 64 + lane) * 16)));
+    for (int j = 0; j < TJ; ++j)
+      b[j] = __builtin_bit_cast(v8bf, buf_load16(rU, (uint32_t)(((((wn >> 5) + j) * (R16 >> 4) + s) * 64 + lane) * 16)));
 #pragma unroll
-      for (int i = 0; i < TI; ++i) {
-        const uint32_t o = (uint32_t)(((((wm >> 5) + i) * (R16 >> 4) + (k0 >> 4)) * 2 * 64 + lane) * 16);
-        const v8bf ah = __builtin_bit_cast(v8bf, buf_load16(rL, o));
-        const v8bf al = __builtin_bit_cast(v8bf, buf_load16(rL, o + 64 * 16));
+    for (int i = 0; i < TI; ++i) {
+      const uint32_t o = (uint32_t)(((((wm >> 5) + i) * (R16 >> 4) + s) * 2 * 64 + lane) * 16);
+      a[i][0] = __builtin_bit_cast(v8bf, buf_load16(rL, o));
+      a[i][1] = __builtin_bit_cast(v8bf, buf_load16(rL, o + 64 * 16));
+    }
+  };
+  auto lora_mma = [&](const v8bf (&b)[TJ], const v8bf (&a)[TI][2]) {
 #pragma unroll
-        for (int j = 0; j < TJ; ++j) {
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl[j], acc[i][j], 0, 0, 0);
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bl[j], acc[i][j], 0, 0, 0);
-        }
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i][0], b[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i][1], b[j], acc[i][j], 0, 0, 0);
       }
+  };
+  v8bf pb0[TJ], pa0[TI][2], pb1[TJ], pa1[TI][2];
+  if (lora) {
+    lora_load(0, pb0, pa0);
+    if (R16 > 16) lora_load(1, pb1, pa1);
+  }
+  issue(kbeg, lds0);
+  issue(kbeg + 1 < kend ? kbeg + 1 : kend - 1, lds1);
+  if (lora) {
+    lora_mma(pb0, pa0);
+    if (R16 > 16) lora_mma(pb1, pa1);
+    for (int s = 2; s < (R16 >> 4); ++s) {
+      v8bf b[TJ], a[TI][2];
+      lora_load(s, b, a);
+      lora_mma(b, a);
     }
   }
 
