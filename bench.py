@@ -76,7 +76,7 @@ def _pmc_means(path):
         name = r["Kernel_Name"]
         # kernel 2 of the timed forward: the INT4 streamed kernel on the MMA activation
         # form (the fixup launch is counted with it)
-        if "k2_stream<0>" in name or "k2_fixup" in name:
+        if "k2_stream<0" in name or "k2_fixup" in name:
             key = "k2" if "k2_stream" in name else "fixup"
         elif "copyBuffer" in name or "copy" in name.lower():
             key = "copy"
@@ -146,13 +146,126 @@ def cpu_baseline(wl_name, rows):
                       f"layer ({t:.1f} s); host {os.cpu_count()} logical CPUs"}
 
 
+PEAK_INT8_TOPS = PEAK_MFMA_TOPS
+
+
+def k1_algorithmic_bytes(M, K, G, r, int4):
+    """Kernel 1's algorithmic HBM bytes: per token 2K (bf16 X) + K/2 (4-bit codes) +
+    (K/G) x (2-byte fp16 / 1-byte E8M0 scale) + 4r (fp32 X_hat L1).  The factor rows are
+    re-read from cache and not counted; the wider operand form the forward writes is not
+    counted either."""
+    return float(M) * (2 * K + K // 2 + (K // G) * (2 if int4 else 1) + 4 * r)
+
+
+def measure(svdq, torch, wl_name, ydt, steps, warmup, warm_s, compare, log_prefix=""):
+    """Time one workload: the forward (kernel 1 + kernel 2) over `steps` steps after at
+    least `warmup` steps and `warm_s` seconds of warm-up, per-kernel HIP-event durations,
+    and (compare) the rank-0 and unfused forwards in alternating blocks."""
+    from bit_diffusion_model_amd.workloads import make
+
+    dev = "cuda:0"
+    wl = make(wl_name)
+    M, K, N = wl.M, wl.K, wl.N
+    fmt = svdq.FMT[wl.fmt]
+    log(f"[bench]{log_prefix} workload {wl_name} M={M} K={K} N={N} r={wl.total_rank} fmt={wl.fmt}; packing on host")
+    t0 = time.perf_counter()
+    hp = svdq.pack_weights(wl.W, svdq.act_absmax(wl.calib), wl.alpha, wl.rank, fmt)
+    if wl.lora_A is not None:
+        hp = svdq.concat_lora(hp, wl.lora_A, wl.lora_B)
+    log(f"[bench]{log_prefix} pack {time.perf_counter() - t0:.1f} s (offline, untimed)")
+    lay = svdq.PackedLinear.from_host_pack(hp, dev)
+    lay0 = svdq.PackedLinear(K, N, 0, fmt, hp.inv_s, hp.L1t[:0], hp.L2[:0], hp.qW, hp.sW, dev)
+    r = hp.rank
+    X = torch.from_numpy(wl.X.view(np.int16)).to(dev).view(torch.bfloat16)
+    Y = torch.empty((M, N), dtype=torch.float32 if ydt == svdq.F32 else torch.bfloat16, device=dev)
+    ws = lay.workspace(M)
+    ws0 = lay0.workspace(M)
+
+    def step():
+        lay.forward(X, ydt, Y, ws)
+
+    # warm-up: at least `warmup` steps and at least `warm_s` seconds (the clocks take a few
+    # tens of ms to settle)
+    n, t0 = 0, time.perf_counter()
+    while n < warmup or time.perf_counter() - t0 < warm_s:
+        for _ in range(10):
+            step()
+        n += 10
+        torch.cuda.synchronize()
+    log(f"[bench]{log_prefix} warmup {n} steps ({time.perf_counter() - t0:.2f} s); timing {steps} steps")
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / steps
+    ops = 2.0 * M * N * K + 2.0 * M * r * (K + N)
+    tops = ops / (ms * 1e-3) / 1e12
+    log(f"[bench]{log_prefix} {ms:.4f} ms/step (wall {wall / steps * 1e3:.4f}), {tops:.1f} TOPS")
+
+    # per-kernel durations, launched exactly as inside svdq_linear_forward (activation
+    # side in MMA form), with HIP events on the stream the kernels are launched on (torch's
+    # current stream, which the binding passes to the library)
+    qX, sX, la = lay.alloc_act(M, svdq.ACT_MMA)
+    gws = lay.gemm_workspace(M, svdq.ACT_MMA)
+    nrep = max(steps, 10)
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(3 * nrep)]
+    for i in range(nrep):
+        e[3 * i].record()
+        lay.quantize_act(X, (qX, sX, la), form=svdq.ACT_MMA)
+        e[3 * i + 1].record()
+        lay.gemm(qX, sX, la, ydt, Y, form=svdq.ACT_MMA, workspace=gws)
+        e[3 * i + 2].record()
+    torch.cuda.synchronize()
+    t_k1 = float(np.mean([e[3 * i].elapsed_time(e[3 * i + 1]) for i in range(nrep)])) * 1e-3
+    t_k2 = float(np.mean([e[3 * i + 1].elapsed_time(e[3 * i + 2]) for i in range(nrep)])) * 1e-3
+    # low-rank overhead: the layer against a rank-0 layer with the same codes, and against
+    # the unfused baseline (the low-rank branch as kernels of its own), timed in alternating
+    # blocks of 20 forwards (medians of 5), so all three see the same clocks
+    fr, f0, fu = [], [], []
+    for _ in range(5 if compare else 0):
+        for lyr, wsp, fused, out in ((lay, ws, True, fr), (lay0, ws0, True, f0), (lay, ws, False, fu)):
+            lyr.forward(X, ydt, Y, wsp, fused=fused)
+            ev0.record()
+            for _ in range(20):
+                lyr.forward(X, ydt, Y, wsp, fused=fused)
+            ev1.record()
+            torch.cuda.synchronize()
+            out.append(ev0.elapsed_time(ev1) / 20)
+    med = lambda v: float(np.median(v)) if v else float("nan")
+    rnd = lambda x, d: None if x != x else round(x, d)  # NaN (not measured) -> null
+    ms_r, ms0, ms_u = med(fr), med(f0), med(fu)
+
+    G = lay.group
+    k2_ops = float(M) * N * (2.0 * K + 2.0 * r)
+    k1_bytes = k1_algorithmic_bytes(M, K, G, r, fmt == svdq.INT4_G64)
+    k2_tops = k2_ops / t_k2 / 1e12
+    res = dict(wl=wl, M=M, K=K, N=N, r=r, fmt=fmt, ms=ms, tops=tops, t_k1=t_k1, t_k2=t_k2, k2_tops=k2_tops,
+               k1_bytes=k1_bytes, warm_steps=n)
+    res["kernels"] = {
+        "k1_us": round(t_k1 * 1e6, 2), "k2_us": round(t_k2 * 1e6, 2),
+        "k1_GBps": round(k1_bytes / t_k1 / 1e9, 1), "k1_hbm_frac": round(k1_bytes / t_k1 / 1e9 / PEAK_HBM_GBS, 4),
+        "k2_TOPS": round(k2_tops, 2),
+        # the INT4 contraction runs on the FP6 scaled MFMA (10.1 PF dense); against the
+        # INT8 peak (5.0 POP/s) that the INT4 format would use on an int8 matrix core
+        "k2_frac_fp6_fp4_peak": round(k2_tops / PEAK_MFMA_FP4_TOPS, 4),
+        "k2_frac_int8_peak": round(k2_tops / PEAK_INT8_TOPS, 4) if fmt == svdq.INT4_G64 else None,
+        "rank0_ms": rnd(ms0, 5), "fwd_ms_paired": rnd(ms_r, 5), "lowrank_overhead": rnd(ms_r / ms0 - 1.0, 4),
+        "unfused_ms": rnd(ms_u, 5), "unfused_lowrank_overhead": rnd(ms_u / ms0 - 1.0, 4)}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    # defaults: ~60 ms of warm-up (the clocks settle within a few tens of ms) and of
-    # timed work at C1
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--warm-seconds", type=float, default=0.3,
+                    help="minimum warm-up wall time, whatever --warmup says (clocks settle in tens of ms)")
     ap.add_argument("--workload", default="C1", choices=list(WORKLOADS))
     ap.add_argument("--ydtype", default="f32", choices=["f32", "bf16"])
     ap.add_argument("--cpu-rows", type=int, default=4608)
@@ -160,6 +273,8 @@ def main():
     ap.add_argument("--no-compare", action="store_true",
                     help="skip the rank-0 and unfused comparison forwards (counter runs: only the "
                          "timed layer's kernels are dispatched)")
+    ap.add_argument("--no-others", action="store_true",
+                    help="skip the other FLUX workloads (MLP fc1, fc2, MXFP4, batch 2 + LoRA)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after timing, run one plain device copy of 512 MiB (counter calibration)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -179,113 +294,45 @@ def main():
 
     import torch
     from bit_diffusion_model_amd import svdq
-    from bit_diffusion_model_amd.workloads import make
 
     svdq.lib()  # fail loudly if the HIP library is missing
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
-    dev = "cuda:0"
-    wl = make(args.workload)
-    M, K, N = wl.M, wl.K, wl.N
-    fmt = svdq.FMT[wl.fmt]
-    log(f"[bench] workload {args.workload} M={M} K={K} N={N} r={wl.rank} fmt={wl.fmt}; packing on host")
-    t0 = time.perf_counter()
-    hp = svdq.pack_weights(wl.W, svdq.act_absmax(wl.calib), wl.alpha, wl.rank, fmt)
-    if wl.lora_A is not None:
-        hp = svdq.concat_lora(hp, wl.lora_A, wl.lora_B)
-    log(f"[bench] pack {time.perf_counter() - t0:.1f} s (offline, untimed)")
-    lay = svdq.PackedLinear.from_host_pack(hp, dev)
-    lay0 = svdq.PackedLinear(K, N, 0, fmt, hp.inv_s, hp.L1t[:0], hp.L2[:0], hp.qW, hp.sW, dev)
-    r = hp.rank
-    X = torch.from_numpy(wl.X.view(np.int16)).to(dev).view(torch.bfloat16)
     ydt = svdq.F32 if args.ydtype == "f32" else svdq.BF16
-    Y = torch.empty((M, N), dtype=torch.float32 if ydt == svdq.F32 else torch.bfloat16, device=dev)
-    ws = lay.workspace(M)
-    ws0 = lay0.workspace(M)
-
-    def step():
-        lay.forward(X, ydt, Y, ws)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    log(f"[bench] warmup done; timing {args.steps} steps")
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record()
-    for _ in range(args.steps):
-        step()
-    ev1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = ev0.elapsed_time(ev1) / args.steps
-    ops = 2.0 * M * N * K + 2.0 * M * r * (K + N)
-    tops = ops / (ms * 1e-3) / 1e12
-    log(f"[bench] {ms:.4f} ms/step (wall {wall / args.steps * 1e3:.4f}), {tops:.1f} TOPS")
-
-    # per-kernel durations, launched exactly as inside svdq_linear_forward (activation
-    # side in MMA form), on the same (torch current) stream the events are recorded on
-    qX, sX, la = lay.alloc_act(M, svdq.ACT_MMA)
-    gws = lay.gemm_workspace(M, svdq.ACT_MMA)
-    nrep = max(args.steps, 10)
-    e = [torch.cuda.Event(enable_timing=True) for _ in range(3 * nrep)]
-    for i in range(nrep):
-        e[3 * i].record()
-        lay.quantize_act(X, (qX, sX, la), form=svdq.ACT_MMA)
-        e[3 * i + 1].record()
-        lay.gemm(qX, sX, la, ydt, Y, form=svdq.ACT_MMA, workspace=gws)
-        e[3 * i + 2].record()
-    torch.cuda.synchronize()
-    t_k1 = float(np.mean([e[3 * i].elapsed_time(e[3 * i + 1]) for i in range(nrep)])) * 1e-3
-    t_k2 = float(np.mean([e[3 * i + 1].elapsed_time(e[3 * i + 2]) for i in range(nrep)])) * 1e-3
-    # low-rank overhead: the layer against a rank-0 layer with the same codes, and against
-    # the unfused baseline (the low-rank branch as kernels of its own), timed in alternating
-    # blocks of 20 forwards (medians of 5), so all three see the same clocks
-    fr, f0, fu = [], [], []
-    for _ in range(0 if args.no_compare else 5):
-        for lyr, wsp, fused, out in ((lay, ws, True, fr), (lay0, ws0, True, f0), (lay, ws, False, fu)):
-            lyr.forward(X, ydt, Y, wsp, fused=fused)
-            ev0.record()
-            for _ in range(20):
-                lyr.forward(X, ydt, Y, wsp, fused=fused)
-            ev1.record()
-            torch.cuda.synchronize()
-            out.append(ev0.elapsed_time(ev1) / 20)
-    med = lambda v: float(np.median(v)) if v else float("nan")
-    rnd = lambda x, d: None if x != x else round(x, d)  # NaN (not measured) -> null
-    ms_r, ms0, ms_u = med(fr), med(f0), med(fu)
-
-    G = lay.group
-    k2_ops = float(M) * N * (2.0 * K + 2.0 * r)
-    # kernel 1's HBM bytes in MMA form: X (bf16), codes (INT4 FP6 operand words, 64 bytes
-    # per group / MXFP4 nibbles), scales (INT4 fp16 / E8M0 bytes), lora_act (R16 x 4
-    # bytes); the factor rows are re-read from L2 and not counted
-    if fmt == svdq.INT4_G64:
-        k1_bytes = float(M) * (2 * K + K + (K // G) * 2 + 4 * svdq.r16(r))
-    else:
-        k1_bytes = float(M) * (2 * K + K // 2 + (K // G) + 4 * svdq.r16(r))
-    peak = PEAK_MFMA_TOPS if fmt == svdq.INT4_G64 else PEAK_MFMA_FP4_TOPS
-    k2_tops = k2_ops / t_k2 / 1e12
+    m = measure(svdq, torch, args.workload, ydt, args.steps, args.warmup, args.warm_seconds, not args.no_compare)
+    fmt, M, K, N, r = m["fmt"], m["M"], m["K"], m["N"], m["r"]
+    k2_tops = m["k2_tops"]
+    peak = PEAK_MFMA_FP4_TOPS  # both formats run the FP6 / FP4 scaled MFMA (10.1 PF dense)
     traffic = traffic_entry() if args.workload == "C1" and ydt == svdq.F32 else None
     out = {
-        "metric": METRIC, "value": round(tops, 2), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "metric": METRIC, "value": round(m["tops"], 2), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(m["ms"], 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "int4" if fmt == svdq.INT4_G64 else "fp4-e2m1", "data": "synthetic",
         "config": {"workload": WORKLOADS[args.workload], "M": M, "K": K, "N": N, "rank": r,
                    "format": "INT4 g64 fp16 scales" if fmt == svdq.INT4_G64 else "MXFP4 g32 E8M0 scales",
                    "output": args.ydtype, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "achieved": round(k2_tops, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(k2_tops / peak, 4), "traffic": traffic},
-        "kernels": {"k1_us": round(t_k1 * 1e6, 2), "k2_us": round(t_k2 * 1e6, 2),
-                    "k1_GBps": round(k1_bytes / t_k1 / 1e9, 1), "k1_hbm_frac": round(k1_bytes / t_k1 / 1e9 / PEAK_HBM_GBS, 4),
-                    "k2_TOPS": round(k2_tops, 2), "rank0_ms": rnd(ms0, 5),
-                    "fwd_ms_paired": rnd(ms_r, 5), "lowrank_overhead": rnd(ms_r / ms0 - 1.0, 4),
-                    "unfused_ms": rnd(ms_u, 5), "unfused_lowrank_overhead": rnd(ms_u / ms0 - 1.0, 4)},
+                     "frac": round(k2_tops / peak, 4), "traffic": traffic,
+                     "kernel": "kernel 2 (W4A4 GEMM + rescale + low-rank up projection), "
+                               + ("INT4 on the FP6 scaled MFMA" if fmt == svdq.INT4_G64 else "MXFP4 scaled MFMA"),
+                     "frac_vs_int8_peak": (round(k2_tops / PEAK_INT8_TOPS, 4) if fmt == svdq.INT4_G64 else None)},
+        "kernels": m["kernels"],
     }
+    if not args.no_others:
+        others = {}
+        for name in ("C2a", "C2b", "C3", "C4"):
+            if name == args.workload:
+                continue
+            o = measure(svdq, torch, name, ydt, 50, 20, 0.1, not args.no_compare, log_prefix=f" [{name}]")
+            others[name] = {"workload": WORKLOADS[name], "M": o["M"], "K": o["K"], "N": o["N"], "rank": o["r"],
+                            "ms_per_step": round(o["ms"], 5), "TOPS": round(o["tops"], 2),
+                            "k2_frac_fp6_fp4_peak": o["kernels"]["k2_frac_fp6_fp4_peak"], **o["kernels"]}
+            del o
+            torch.cuda.empty_cache()
+        out["workloads"] = others
     if args.calib_copy:
-        src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device=dev)
+        src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device="cuda:0")
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()

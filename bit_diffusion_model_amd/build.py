@@ -17,7 +17,7 @@ BUILD = os.path.join(HERE, "_build")
 ARCH = "gfx950"
 
 DEVICE_SOURCES = ["k1_quant_lora_down.hip", "k2_gemm_w4a4.hip", "k3_lora_up.hip", "api.cpp"]
-HOST_SOURCES = ["pack.cpp"]
+HOST_SOURCES = ["pack.cpp", "status.cpp"]
 
 HIP_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",

@@ -2,9 +2,7 @@
 // entry points declared in include/svdq.h.
 #include <hip/hip_runtime.h>
 
-#include <cstdarg>
 #include <cstdio>
-#include <string>
 
 #include "../../include/svdq.h"
 #include "internal.hpp"
@@ -12,34 +10,7 @@
 
 namespace svdq {
 
-static thread_local std::string g_err;
-
-svdq_status fail(svdq_status st, const char* fmt, ...) {
-  char buf[512];
-  va_list ap;
-  va_start(ap, fmt);
-  vsnprintf(buf, sizeof buf, fmt, ap);
-  va_end(ap);
-  g_err = buf;
-  return st;
-}
-
-svdq_status ok() {
-  g_err.clear();
-  return SVDQ_OK;
-}
-
 static bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
-
-int group_of(int fmt) { return fmt == SVDQ_INT4_G64 ? 64 : 32; }
-
-svdq_status check_dims(int64_t K, int64_t N, int32_t fmt) {
-  if (fmt != SVDQ_INT4_G64 && fmt != SVDQ_MXFP4_G32)
-    return fail(SVDQ_EUNSUPPORTED, "unsupported format %d", (int)fmt);
-  if (K < 128 || K % 128 != 0) return fail(SVDQ_EINVAL, "K must be a positive multiple of 128 (got %lld)", (long long)K);
-  if (N < 1) return fail(SVDQ_EINVAL, "N must be >= 1 (got %lld)", (long long)N);
-  return SVDQ_OK;
-}
 
 static svdq_status check_layer(const svdq_layer* L, KernelLayer& kl) {
   if (!L) return fail(SVDQ_EINVAL, "layer is NULL");
@@ -87,8 +58,6 @@ static WsLayout ws_layout(const svdq_layer* L, int64_t M) {
 using namespace svdq;
 
 extern "C" {
-
-const char* svdq_last_error(void) { return g_err.c_str(); }
 
 size_t svdq_workspace_bytes(const svdq_layer* layer, int64_t M) {
   if (!layer || M < 0 || check_dims(layer->K, layer->N, layer->fmt) != SVDQ_OK) return 0;
@@ -141,7 +110,8 @@ static svdq_status run_k2(const svdq_layer* layer, int64_t M, int32_t form, cons
   if (!qX || !sX || !Y) return fail(SVDQ_EINVAL, "qX, sX and Y must be non-NULL");
   if (kl.rank > 0 && !lora_act) return fail(SVDQ_EINVAL, "lora_act must be non-NULL when rank > 0");
   if (ldy < kl.N) return fail(SVDQ_EINVAL, "ldy must be >= N");
-  if (ldy >= (int64_t(1) << 23)) return fail(SVDQ_EUNSUPPORTED, "ldy must be < 2^23 elements");
+  // the output stores address a tile's rows (up to 256) through a 32-bit range
+  if (ldy >= (int64_t(1) << 22)) return fail(SVDQ_EUNSUPPORTED, "ldy must be < 2^22 elements");
   if (!aligned(qX, 16) || !aligned(Y, ydtype == SVDQ_F32 ? 4 : 2) || !aligned(sX, 2) ||
       (lora_act && !aligned(lora_act, 16)))
     return fail(SVDQ_EINVAL, "qX and lora_act must be 16-byte aligned and Y aligned to its element size");
@@ -218,17 +188,18 @@ svdq_status svdq_linear_forward_unfused(const svdq_layer* layer, int64_t M, cons
   return ok();
 }
 
-svdq_status svdq_debug_group_sums(const svdq_layer* layer, int64_t M, const uint8_t* qX, int64_t m0,
-                                  int64_t n0, int64_t mt, int64_t nt, int32_t* out, void* stream) {
+svdq_status svdq_debug_group_sums(const svdq_layer* layer, int64_t M, int32_t form, const uint8_t* qX,
+                                  int64_t m0, int64_t n0, int64_t mt, int64_t nt, int32_t* out, void* stream) {
   KernelLayer kl;
   svdq_status st = check_layer(layer, kl);
   if (st != SVDQ_OK) return st;
   if (kl.fmt != SVDQ_INT4_G64) return fail(SVDQ_EUNSUPPORTED, "group sums are defined for INT4 only");
+  if ((st = check_form(form)) != SVDQ_OK) return st;
   if (!qX || !out) return fail(SVDQ_EINVAL, "qX and out must be non-NULL");
   if (m0 < 0 || n0 < 0 || mt < 1 || nt < 1 || m0 + mt > M || n0 + nt > kl.N)
     return fail(SVDQ_EINVAL, "window out of range");
   if (!aligned(qX, 16)) return fail(SVDQ_EINVAL, "qX must be 16-byte aligned");
-  hipError_t e = launch_k2_debug(kl, M, qX, m0, n0, mt, nt, out, (hipStream_t)stream);
+  hipError_t e = launch_k2_debug(kl, M, qX, form == SVDQ_ACT_MMA, m0, n0, mt, nt, out, (hipStream_t)stream);
   if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
   if (e != hipSuccess) return fail(SVDQ_EHIP, "group-sum kernel: %s", hipGetErrorString(e));
   return ok();

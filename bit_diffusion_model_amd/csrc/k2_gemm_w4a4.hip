@@ -9,39 +9,40 @@
 // Matrix cores: v_mfma_scale_f32_32x32x64_f8f6f4.
 //  * MXFP4: the E2M1 codes are the operands as stored and the E8M0 group scales are
 //    the hardware block scales; the MFMA accumulates the exact scaled products.
-//  * INT4: a sign-magnitude code q becomes the FP8 E4M3 byte (sign, exponent 0,
-//    mantissa |q|), whose value is q * 2^-9 (a subnormal; exact), so an MFMA with block
-//    scales 2^9 on both sides yields the exact integer group sum I in fp32.  The
-//    per-group rescale by s_X s_W is VALU work on every output and group, and it is
-//    what bounds the INT4 path.  The forward's kernel (k2_stream) applies fp32 scales:
-//    acc += (I * sW) * sX with v_mul_f32 and v_fmac_f32.  The packed-form kernel
-//    (k2_gemm) splits each scale s = m * 2^e (m in [1, 2)), puts 2^(e+9) into the
-//    MFMA's E8M0 block scales and adds the result times the fp16 product mX * mW
-//    (v_pk_mul_f16 + v_fma_mix_f32).  The weight codes come in a bit order that expands
-//    to FP8 with a mask and a rotate (prepared once, offline).  In the fused forward
-//    path the activation side comes from kernel 1 as FP8 code bytes, fp32 scales and
-//    bf16 hi/lo low-rank activations, so the main loop converts only the weights.
+//  * INT4: a sign-magnitude code q becomes the FP6 E2M3 field (sign, exponent 0,
+//    mantissa |q|), whose value is q / 8 (a subnormal; exact), so an MFMA with block
+//    scales 2^3 (E8M0 byte 130) on both sides yields the exact integer group sum I in
+//    fp32, at the FP6 rate.  The per-group rescale: a second MFMA
+//    (v_mfma_f32_32x32x8_f16) whose only nonzero k term is the pair of fp16 scales
+//    forms c = s_X s_W for the 32 x 32 tile exactly (11 x 11 significant bits) in the
+//    accumulator layout, and one v_fmac_f32 per output adds I * c.  The weight codes
+//    come in a bit order from which masks alone give the FP6 operand words (prepared
+//    once, offline).  In the forward the activation side comes from kernel 1 already in
+//    operand form (FP6 words, fp16 scales, bf16 hi/lo low-rank activations), so the main
+//    loop expands only the weights.
 //
-// Tiling: a 256-thread block (4 waves) owns a 128 x 128 output tile; wave w owns rows
-// 64*(w/2) .. +63 and columns 64*(w%2) .. +63, i.e. 2 x 2 MFMA tiles of 32 x 32; two
+// Tiling: 64-wide waves own 2 x 2 (INT4) or 4 x 2 (MXFP4) MFMA tiles of 32 x 32; two
 // blocks share a CU, so one block's barrier and staging overlap another's math.  K
-// advances in stages of SUB 64-wide sub-steps (one INT4 group, two FP4 groups each),
-// one barrier per stage.  Two kernels implement this:
+// advances in stages of 64-wide sub-steps (one INT4 group, two FP4 groups each), one
+// barrier per stage.  Two kernels implement this:
 //  * k2_stream (MMA activation form, the forward's path): both operand panels and
 //    their scales go global -> LDS with LDS-destination buffer loads into three
 //    rotating buffers, loads for stage k+2 in flight while stage k is computed; the
-//    weight codes stay 4-bit in LDS and each wave expands its own fragments.
-//  * k2_gemm (packed activation form): loads into registers one stage ahead, converts
-//    the codes to FP8 on the way into double-buffered, row-padded LDS.
+//    weight codes stay 4-bit in LDS and each wave expands its own fragments.  Its DEBUG
+//    instance runs the same loads, LDS layout, expansion and group-sum MFMA and stores
+//    each group's MFMA result instead of rescaling it (the exact group sums).
+//  * k2_gemm (packed activation form): 128 x 128 tiles of 4 waves; loads into registers
+//    one stage ahead, converts the activation nibbles to FP6 operand words on the way
+//    into double-buffered, row-padded LDS.
 // Buffer resources' range checks return zeros past the end of either matrix, so no
 // loop has bounds branches.  The tiles of a last, partly filled round of resident
 // blocks are split along K; their partial tiles are summed by k2_fixup.
 //
 // 32x32x64 operand layout (measured): lane l supplies row/column l & 31; for FP4 it
 // holds the 32 consecutive K values 32*(l>>5).. with the block scale of that half; for
-// FP8 the k order inside the lane differs but a group's single scale covers both
-// halves, so A and B only need the same byte order.  Output: lane l holds column
-// l & 31, rows 8*(a>>2) + 4*(l>>5) + (a&3) for accumulator a = 0..15.
+// FP6 the fields of a lane half pair field f of A with field f of B, so A and B only
+// need the same k order.  Output: lane l holds column l & 31, rows 8*(a>>2) + 4*(l>>5) +
+// (a&3) for accumulator a = 0..15.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -71,7 +72,8 @@ struct Smem {
 // Store one 32 x 32 accumulator (rows r_off.., columns c_off.. of the tile at m0, n0)
 // to Y through a resource over the tile's rows: rows past the end fall outside the range
 // and are dropped; columns past N are masked (they may be the caller's row padding).
-// The host guarantees 128 * ldy * 4 < 2^32.
+// The host guarantees (tile rows) * ldy * (element size) < 2^32 for every tile shape
+// (ldy < 2^22 elements).
 __device__ __forceinline__ void store_sub(const v16f& acc, void* Y, int64_t ldy, int ydtype, int64_t m0,
                                           int64_t n0, int64_t rowsA, int64_t nlim, int r_off, int c_off,
                                           int l32, int kh) {
@@ -405,11 +407,10 @@ __global__ __launch_bounds__(NTHREADS, 2) __attribute__((amdgpu_waves_per_eu(2, 
 // with one barrier per stage.
 // 16-byte slots of each operand row are XOR-swizzled with the row (rows are not padded:
 // a load instruction fills 1 KB contiguously).  The weight codes stay 4-bit in LDS and
-// are expanded to FP8 after the read, per wave.
-// INT4 rescale: both MFMA block scales are 2^9, so the MFMA returns the exact integer
-// group sum I; the epilogue adds (I * sW) * sX with fp32 v_mul / v_fmac, which run at
-// twice the rate of the packed-fp16 and mixed-precision forms on gfx950 and issue
-// alongside the MFMA (measured; v_pk_mul_f16 does not overlap a running MFMA).
+// are expanded to FP6 operand words after the read, per wave (masks only).
+// INT4 rescale: both MFMA block scales are 2^3, so the MFMA returns the exact integer
+// group sum I; a second MFMA forms c = s_X s_W exactly and the epilogue adds I * c with
+// one v_fmac_f32 per output and group.
 
 // Block shape: a WGM x WGN grid of waves, each owning TI x TJ MFMA tiles of 32 x 32.
 template <int WGM_, int WGN_, int TI_, int TJ_>
@@ -482,12 +483,20 @@ __device__ __forceinline__ void wait_cnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (L << 8));
 }
 
-template <int FMT>
+// The DEBUG instance's output: the exact INT4 group sums I[g][r][c] of the window rows
+// [m0, m0 + mt) x columns [n0, n0 + nt), int32 [K/64][mt][nt].
+struct K2Debug {
+  int32_t* out;
+  int64_t m0, n0, mt, nt;
+};
+
+template <int FMT, bool DEBUG = false>
 __global__ __launch_bounds__(SShape<FMT>::NT, 8 / SShape<FMT>::NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void k2_stream(
     const uint8_t* __restrict__ qX, const uint8_t* __restrict__ sX, int64_t M,
     const uint8_t* __restrict__ qW, const uint8_t* __restrict__ sW, int64_t N, int64_t K,
     const uint16_t* __restrict__ lora_act, const uint16_t* __restrict__ L2, int rank,
-    void* __restrict__ Y, int64_t ldy, int ydtype, K2Sched sch) {
+    void* __restrict__ Y, int64_t ldy, int ydtype, K2Sched sch, K2Debug dbg) {
+  static_assert(!DEBUG || FMT == 0, "group sums are defined for INT4");
   using D = DLay<FMT>;
   using SH = SShape<FMT>;
   constexpr int TI = SH::TI, TJ = SH::TJ, BM = SH::BM, BN = SH::BN, NW = SH::NW;
@@ -525,8 +534,9 @@ __global__ __launch_bounds__(SShape<FMT>::NT, 8 / SShape<FMT>::NW) __attribute__
   const __amdgpu_buffer_rsrc_t rB = make_rsrc(qW + n0 * Kb, (uint32_t)((rowsB + 1) & ~int64_t(1)) * Kb);
   const uint32_t ng = FMT == 0 ? (uint32_t)(K >> 6) : (uint32_t)(K >> 5);
   const uint32_t Mp = (uint32_t)((M + 3) & ~int64_t(3)), Np = (uint32_t)((N + 3) & ~int64_t(3));
-  const __amdgpu_buffer_rsrc_t rSX = make_rsrc(sX, ng * Mp * (FMT == 0 ? 2 : 1));
-  const __amdgpu_buffer_rsrc_t rSW = make_rsrc(sW, ng * Np * (FMT == 0 ? 2 : 1));
+  // DEBUG: no scales (empty ranges: the scale loads return zeros and touch no memory)
+  const __amdgpu_buffer_rsrc_t rSX = make_rsrc(sX, DEBUG ? 0u : ng * Mp * (FMT == 0 ? 2 : 1));
+  const __amdgpu_buffer_rsrc_t rSW = make_rsrc(sW, DEBUG ? 0u : ng * Np * (FMT == 0 ? 2 : 1));
 
   // ---- loads of stage k into an LDS buffer (every wave issues D::NDW instructions) ------
   // Per-lane source offsets within a stage are fixed (chunk n of 1 KB covers rows
@@ -677,7 +687,23 @@ __global__ __launch_bounds__(SShape<FMT>::NT, 8 / SShape<FMT>::NW) __attribute__
     for (int u = 0; u < 2; ++u) {
       Frag F;
       load(cur, u, F);
-      if constexpr (FMT == 0) {
+      if constexpr (DEBUG) {
+        v8i bf[TJ];
+        expand(F, bf);
+        const int64_t g = (int64_t)kk * 2 + u;
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+          for (int j = 0; j < TJ; ++j) {
+            const v16f p = gs(F, bf, i, j);
+            const int64_t c = n0 + wn + j * 32 + l32 - dbg.n0;
+#pragma unroll
+            for (int a = 0; a < 16; ++a) {
+              const int64_t r = m0 + wm + i * 32 + 8 * (a >> 2) + 4 * kh + (a & 3) - dbg.m0;
+              if (r >= 0 && r < dbg.mt && c >= 0 && c < dbg.nt) dbg.out[(g * dbg.mt + r) * dbg.nt + c] = (int32_t)p[a];
+            }
+          }
+      } else if constexpr (FMT == 0) {
         v8i bf[TJ];
         expand(F, bf);
         // two tiles in flight: tile t+1's MFMAs are issued ahead of tile t's rescale
@@ -708,7 +734,7 @@ __global__ __launch_bounds__(SShape<FMT>::NT, 8 / SShape<FMT>::NW) __attribute__
   // are 1 KB contiguous (lora_act: hi, then lo), so every load reads whole lines.  The
   // range covers whole 32-row blocks; rows past M hold whatever the workspace held
   // (their outputs are not stored), columns past N are zero.
-  const bool lora = rank > 0 && part <= 0;  // once per tile: whole, or the first part
+  const bool lora = !DEBUG && rank > 0 && part <= 0;  // once per tile: whole, or the first part
   const int R16 = (rank + 15) & ~15;
   const __amdgpu_buffer_rsrc_t rL = make_rsrc(lora_act + m0 * 2 * R16, (uint32_t)(((rowsA + 31) & ~31) * R16 * 4));
   const __amdgpu_buffer_rsrc_t rU = make_rsrc(L2 + n0 * R16, (uint32_t)(((rowsB + 31) & ~31) * R16 * 2));
@@ -757,6 +783,7 @@ __global__ __launch_bounds__(SShape<FMT>::NT, 8 / SShape<FMT>::NW) __attribute__
   if (nk % 3 >= 1) stage(k, lds0, lds2);
   if (nk % 3 == 2) stage(k + 1, lds1, lds0);
   wait_cnt<0, 0>();
+  if constexpr (DEBUG) return;
 
   // ---- store (or the partial tile) ------------------------------------------------------
   if (part < 0) {
@@ -900,7 +927,7 @@ hipError_t launch_k2(const KernelLayer& L, int64_t M, const uint8_t* qX, const v
 #define K2_STREAM(F)                                                                                        \
   hipLaunchKernelGGL((k2_stream<F>), dim3(nblocks), dim3(SShape<F>::NT), 0, st, qX, static_cast<const uint8_t*>(sX), M, \
                      L.qW, static_cast<const uint8_t*>(L.sW), L.N, L.K, static_cast<const uint16_t*>(lora_act),   \
-                     L.L2f, L.rank, Y, ldy, ydtype, sch)
+                     L.L2f, L.rank, Y, ldy, ydtype, sch, K2Debug{})
   const int sub = sub_of(L.K);
   if (mma) {  // the activation side in MMA form: streamed kernel (K % 128 == 0: two sub-steps per stage)
     if (L.fmt == 0) K2_STREAM(0);
@@ -928,8 +955,20 @@ hipError_t launch_k2(const KernelLayer& L, int64_t M, const uint8_t* qX, const v
   return hipGetLastError();
 }
 
-hipError_t launch_k2_debug(const KernelLayer& L, int64_t M, const uint8_t* qX, int64_t m0,
+hipError_t launch_k2_debug(const KernelLayer& L, int64_t M, const uint8_t* qX, bool mma, int64_t m0,
                            int64_t n0, int64_t mt, int64_t nt, int32_t* out, hipStream_t st) {
+  if (mma) {
+    // the forward's streamed kernel on its own schedule (the same K split of the tail
+    // round as the forward): every group of every window element is stored by exactly
+    // one block, so no fixup runs
+    K2Plan p = plan_k2(L, M, true);
+    const uint32_t T = p.tiles_m * p.tiles_n, rem = T - p.full;
+    const K2Sched sch{p.tiles_n, p.full, p.split, nullptr};
+    hipLaunchKernelGGL((k2_stream<0, true>), dim3(p.full + rem * p.split), dim3(SShape<0>::NT), 0, st, qX,
+                       (const uint8_t*)nullptr, M, L.qW, (const uint8_t*)nullptr, L.N, L.K, (const uint16_t*)nullptr,
+                       (const uint16_t*)nullptr, 0, (void*)nullptr, (int64_t)0, 0, sch, K2Debug{out, m0, n0, mt, nt});
+    return hipGetLastError();
+  }
   const uint32_t tn = (uint32_t)((nt + BN - 1) / BN), tm = (uint32_t)((mt + BM - 1) / BM);
   const K2Sched sch{tn, tm * tn, 1, nullptr};
   hipLaunchKernelGGL((k2_gemm<0, true, 1>), dim3(tm * tn), dim3(NTHREADS), 0, st, qX, (const void*)nullptr, M,

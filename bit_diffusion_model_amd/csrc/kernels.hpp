@@ -44,7 +44,9 @@ hipError_t launch_k2(const KernelLayer& L, int64_t M, const uint8_t* qX, const v
                      const void* lora_act, void* Y, int64_t ldy, int ydtype, bool mma,
                      void* workspace, size_t ws_bytes, hipStream_t st);
 
-hipError_t launch_k2_debug(const KernelLayer& L, int64_t M, const uint8_t* qX, int64_t m0,
+// Exact INT4 group sums of a window.  mma: the forward's streamed kernel on MMA-form
+// codes (its own schedule); otherwise the packed-form kernel.
+hipError_t launch_k2_debug(const KernelLayer& L, int64_t M, const uint8_t* qX, bool mma, int64_t m0,
                            int64_t n0, int64_t mt, int64_t nt, int32_t* out, hipStream_t st);
 
 }  // namespace svdq

@@ -73,7 +73,7 @@ def lib():
         "svdq_workspace_bytes": (ctypes.c_size_t, [P, I64]),
         "svdq_linear_forward": (I32, [P, I64, P, I64, P, I64, I32, P, ctypes.c_size_t, P]),
         "svdq_linear_forward_unfused": (I32, [P, I64, P, I64, P, I64, I32, P, ctypes.c_size_t, P]),
-        "svdq_debug_group_sums": (I32, [P, I64, P, I64, I64, I64, I64, P, P]),
+        "svdq_debug_group_sums": (I32, [P, I64, I32, P, I64, I64, I64, I64, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -349,10 +349,12 @@ class PackedLinear:
                   _stream()))
         return out
 
-    def group_sums(self, qX, m0: int, n0: int, mt: int, nt: int):
-        """Exact INT4 group sums I[g][m][n] for a window (diagnostic)."""
+    def group_sums(self, qX, m0: int, n0: int, mt: int, nt: int, form: int = ACT_PACKED, out=None):
+        """Exact INT4 group sums I[g][m][n] for a window (diagnostic); form ACT_MMA runs the
+        forward's own kernel 2 on MMA-form codes."""
         torch = _torch()
-        out = torch.empty((self.K // 64, mt, nt), dtype=torch.int32, device=self.device)
-        _check(lib().svdq_debug_group_sums(self.c_layer(), qX.shape[0], _dptr(qX), m0, n0, mt, nt, _dptr(out),
-                                           _stream()))
+        if out is None:
+            out = torch.empty((self.K // 64, mt, nt), dtype=torch.int32, device=self.device)
+        _check(lib().svdq_debug_group_sums(self.c_layer(), qX.shape[0], form, _dptr(qX), m0, n0, mt, nt,
+                                           _dptr(out), _stream()))
         return out

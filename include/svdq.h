@@ -236,10 +236,12 @@ svdq_status svdq_quantize_act_lora_down(const svdq_layer* layer, int64_t M, cons
  * low-rank up projection (lora_act L2) added in the epilogue (review section 4.3: up
  * projection fused with the 4-bit kernel).
  *   form, qX, sX, lora_act  as written by kernel 1 (device)
- *   Y                 device [M][ldy], fp32 or bf16 (ydtype); 128 * ldy * 4 < 2^32
+ *   Y                 device [M][ldy], fp32 or bf16 (ydtype); ldy < 2^22 elements
+ *                     (EUNSUPPORTED otherwise: a tile's rows are addressed through a
+ *                     32-bit range)
  *   workspace         optional device scratch (NULL / ws_bytes 0: none), 256-byte
  *                     aligned.  With at least svdq_gemm_workspace_bytes bytes, the
- *                     128 x 128 output tiles that would form a last, partly filled round
+ *                     output tiles that would form a last, partly filled round
  *                     of resident blocks are split along K, their fp32 partial tiles
  *                     kept there and added in a fixed order by a second kernel; the
  *                     result is deterministic for a given device and workspace choice.
@@ -257,10 +259,19 @@ size_t svdq_gemm_workspace_bytes(const svdq_layer* layer, int64_t M, int32_t for
  * aligned. */
 size_t svdq_workspace_bytes(const svdq_layer* layer, int64_t M);
 
-/* The public layer: kernel 1 then kernel 2 on `stream` with the activation side in
- * MMA form, intermediates in `workspace` (device, >= svdq_workspace_bytes, 256-byte
- * aligned).  The same launches as the two calls above with form = SVDQ_ACT_MMA and
- * kernel 2 given its split workspace: the results are identical bit for bit. */
+/* The public layer Y = Q(X diag(s)^-1) Q(R) + (X diag(s)^-1 L1) L2 (decomposition
+ * equation of the jeonghoonpark.com "SVDQuant" review, section 4.2), computed the way
+ * the review's section 4.3 ("Nunchaku", Figure 6(b)) fuses it: two kernels instead of
+ * four, the down projection sharing the quantization kernel's read of X and the up
+ * projection sharing the 4-bit GEMM's output tile.  Kernel 1 then kernel 2 on `stream`
+ * with the activation side in MMA form, intermediates in `workspace` (device, >=
+ * svdq_workspace_bytes, 256-byte aligned, caller-owned; its contents on entry do not
+ * matter).  The same launches as the two calls above with form = SVDQ_ACT_MMA and
+ * kernel 2 given its split workspace: the results are identical bit for bit.
+ *   X  device bf16 [M][ldx] (16-byte aligned rows); Y device [M][ldy], fp32 or bf16
+ *   (ydtype), overwritten; columns >= N of each Y row are not touched.
+ * M == 0 is a no-op.  EINVAL on NULL / misalignment / small workspace; EUNSUPPORTED on
+ * ldy >= 2^22; EHIP on launch error. */
 svdq_status svdq_linear_forward(const svdq_layer* layer, int64_t M, const uint16_t* X,
                                 int64_t ldx, void* Y, int64_t ldy, int32_t ydtype,
                                 void* workspace, size_t ws_bytes, void* stream);
@@ -279,11 +290,17 @@ svdq_status svdq_linear_forward_unfused(const svdq_layer* layer, int64_t M, cons
                                         int64_t ldx, void* Y, int64_t ldy, int32_t ydtype,
                                         void* workspace, size_t ws_bytes, void* stream);
 
-/* Diagnostic, same main loop as kernel 2 with an epilogue that stores the exact
- * integer group sums I[g][m][n] = sum_{k in group g} qX[m][k] qW[n][k] (INT4 only) for
- * the window rows [m0, m0+mt) x cols [n0, n0+nt).  out: device int32 [K/64][mt][nt].
+/* Diagnostic: the exact integer group sums I[g][m][n] = sum_{k in group g} qX[m][k]
+ * qW[n][k] (INT4 only; the review's section 3 product Q_X Q_W, taken per group) for the
+ * window rows [m0, m0+mt) x cols [n0, n0+nt).  out: device int32 [K/64][mt][nt].
+ *   form = SVDQ_ACT_MMA: qX in kernel 1's MMA form; the kernel is the one
+ *     svdq_linear_forward and svdq_gemm_w4a4_lora_up (MMA form) run, instantiated with
+ *     an epilogue that stores each group's MFMA result instead of rescaling it: the same
+ *     launch schedule (including the K split of the last round), loads, LDS layout,
+ *     weight expansion and group-sum instruction.
+ *   form = SVDQ_ACT_PACKED: qX packed [M][K/2]; the packed-form kernel 2's main loop.
  * Synchronous (waits for the stream) so it can be used from tests directly. */
-svdq_status svdq_debug_group_sums(const svdq_layer* layer, int64_t M, const uint8_t* qX,
+svdq_status svdq_debug_group_sums(const svdq_layer* layer, int64_t M, int32_t form, const uint8_t* qX,
                                   int64_t m0, int64_t n0, int64_t mt, int64_t nt, int32_t* out,
                                   void* stream);
 

@@ -55,6 +55,14 @@ def group_sums(cX: np.ndarray, cW: np.ndarray, G: int) -> np.ndarray:
     return out
 
 
+def code_product(cX: np.ndarray, cW: np.ndarray) -> np.ndarray:
+    """Sum over all groups of the integer group sums: the plain integer product of the
+    codes, sum_k qX[m,k] qW[n,k] (cX [M][K], cW [N][K]).  One fp64 matmul of
+    integer-valued matrices; every partial sum is far below 2^53, so it is exact.
+    This is what the 4-bit product of section 3 reduces to when every scale is 1."""
+    return np.rint(cX.astype(np.float64) @ cW.astype(np.float64).T).astype(np.int64)
+
+
 def residual_int4(cX, sX_bits, cW, sW_bits, rows=None, cols=None) -> np.ndarray:
     """Steps 4-5 (INT4): sum_g s_X[m,g] s_W[g,n] I[g,m,n] in fp64.
 

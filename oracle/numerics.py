@@ -24,10 +24,11 @@ def round_f64_to_bf16(x: np.ndarray) -> np.ndarray:
     Definition: bf16 has an 8-bit significand and fp32's exponent range, so the
     quantum of a value with binary exponent e is 2^(max(e, -126) - 7).  The value is
     divided by its quantum (exact: a power of two), rounded half-to-even with
-    ``np.rint`` and multiplied back.  Returns the bf16 *values* as fp64.
+    ``np.rint`` and multiplied back.  Zeros keep their sign.  Returns the bf16 *values*
+    as fp64.
     """
     x = np.asarray(x, dtype=np.float64)
-    out = np.zeros_like(x)
+    out = x * 0.0  # signed zeros stay as they are
     nz = x != 0
     _, e = np.frexp(x[nz])  # x = f * 2^e with f in [0.5, 1)  =>  binary exponent e-1
     q = np.ldexp(1.0, np.maximum(e - 1, -126) - 7)

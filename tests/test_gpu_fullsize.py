@@ -1,23 +1,31 @@
 """GPU parity at the full FLUX.1 layer sizes, in the launch configuration bench.py times.
 
 For every named workload (QKV, MLP fc1, MLP fc2, the MXFP4 variant of QKV, QKV at batch
-2 with a folded rank-16 LoRA) the HIP path runs on the full input and is compared with
-the oracle:
-* kernel 1: codes and scales bit-exact for every token, lora_act within its error
-  budget for every token;
-* kernel 2 (INT4): exact integer group sums on an interior window and on the ragged
-  last tiles;
-* the layer output: sampled rows x columns (the oracle computes them one by one),
-  max |err| <= 2e-2 x RMS of the sampled reference; the unfused baseline's output to
-  the same bar and within 1e-5 x RMS of the fused output everywhere.
-The pack artifacts come from the oracle's own pack (LAPACK SVD), so no oracle input
-comes from the HIP path.  The three workloads that share the QKV weight share one
-oracle SVD.
+2 with a folded rank-16 LoRA) the HIP path runs on the full input, every buffer it
+writes pre-filled with 0xFF bytes (NaN), and is compared with the oracle:
+* kernel 1, packed form: codes and scales bit-exact for every token, lora_act within its
+  error budget for every token;
+* kernel 1, MMA form (the forward's own workspace after svdq_linear_forward): codes and
+  scales decoded and bit-exact for every token, lora_act's bf16 hi/lo pairs the split of
+  the packed form's fp32 values;
+* kernel 2 (INT4): exact integer group sums from the forward's own streamed kernel, on
+  an interior window and on the ragged last tiles (debug instance), and from the timed
+  instance itself with unit weight scales: activation scales 1.0 on one group give that
+  group's sums, 1.0 on every group the plain integer product of the codes, every element;
+* the layer output: every element, max |err| <= 2e-2 x RMS of the oracle output; the
+  unfused baseline to the same bar and within 1e-5 x RMS of the fused output;
+* end to end: the library's own pack (svdq_pack_weights, svdq_concat_lora for the LoRA
+  workload, then the device layouts) through svdq_linear_forward, against the oracle's
+  pack through the oracle forward, every element, to the same bar.
+The oracle pack (LAPACK SVD) is what the kernel checks run on, so no oracle input comes
+from the HIP path.  The three workloads that share the QKV weight share one oracle SVD.
 """
 import numpy as np
 import pytest
 
-from gpu_helpers import TOL_Y, layer_from_oracle, log, lora_bound, oracle_k1, rel_err, to_dev_bf16
+from gpu_helpers import (TOL_Y, assert_finite, bf16_rne_bits, decode_mma, forward_sentinel, layer_from_oracle, log,
+                         lora_bound, mma_scales_int4, oracle_k1, rel_err, sentinel_act, sentinel_gemm_ws,
+                         sentinel_out, to_dev_bf16, unit_scale_layer)
 
 from bit_diffusion_model_amd import svdq
 from bit_diffusion_model_amd.workloads import make
@@ -51,51 +59,104 @@ def _pack_for(wl):
     return p
 
 
+def _check_y(Yd, Yref, what):
+    assert_finite(Yd)
+    e = rel_err(Yd.cpu().numpy().astype(np.float64), Yref)
+    log(f"  {what}: max|err|/RMS = {e:.3e} over all {Yref.size} outputs")
+    assert e <= TOL_Y
+    return e
+
+
 @pytest.mark.parametrize("name", ["C1", "C2a", "C2b", "C3", "C4"])
 def test_full_size_layer(name):
     import torch
 
     wl = make(name)
-    log(f"full-size {name}: M={wl.M} K={wl.K} N={wl.N} rank={wl.total_rank} {wl.fmt}")
+    M, K, N = wl.M, wl.K, wl.N
+    log(f"full-size {name}: M={M} K={K} N={N} rank={wl.total_rank} {wl.fmt}")
     p = _pack_for(wl)
     lay = layer_from_oracle(p)
     X = to_dev_bf16(wl.X)
-    qX, sX, la = lay.quantize_act(X)
+    r = p["rank"]
+
+    # ---- kernel 1, packed form
+    qX, sX, la = lay.quantize_act(X, out=sentinel_act(lay, M, svdq.ACT_PACKED))
     torch.cuda.synchronize()
     log("  kernel 1 done; oracle kernel 1")
     Xh, codes, sc, qX_ref, sX_ref, la_ref = oracle_k1(wl.X, p)
     np.testing.assert_array_equal(qX.cpu().numpy(), qX_ref)
     np.testing.assert_array_equal(sX.cpu().numpy().view(sX_ref.dtype), sX_ref)
-    r = p["rank"]
-    la_g = la.cpu().numpy().astype(np.float64)
+    la_g = la.cpu().numpy()
     assert not la_g[:, r:].any()
-    assert np.all(np.abs(la_g[:, :r] - la_ref) <= lora_bound(Xh, p["L1b"]))
-    log("  kernel 1 bit-exact; forward")
-    Y = lay.forward(X)  # the public entry point, same launch as bench.py
+    assert np.all(np.abs(la_g[:, :r].astype(np.float64) - la_ref) <= lora_bound(Xh, p["L1b"]))
+    del qX, sX, la
+    log("  kernel 1 (packed) bit-exact; forward")
+
+    # ---- the forward, every element
+    Y, ws = forward_sentinel(lay, X)
+    Yref = oforward.forward(wl.X, p)["Y"]
+    _check_y(Y, Yref, "forward")
+
+    # ---- kernel 1, MMA form, as the forward left it in its workspace
+    Mp = (M + 3) // 4 * 4
     if wl.fmt == "int4":
-        M, N = wl.M, wl.N
+        sx0 = (M * K + 255) // 256 * 256
+        la0 = sx0 + ((K // 64) * Mp * 2 + 255) // 256 * 256
+        c_m, s_m, hi, lo = decode_mma(ws[:M * K].view(M, K), ws[sx0:sx0 + (K // 64) * Mp * 2], ws[la0:], "int4", K,
+                                      r, M=M)
+        np.testing.assert_array_equal(c_m, codes)
+        np.testing.assert_array_equal(s_m, sX_ref.view(np.float16).astype(np.float64))
+    else:
+        nq = (M + 1) // 2 * 2 * (K // 2)
+        sx0 = (nq + 255) // 256 * 256
+        la0 = sx0 + ((K // 32) * Mp + 255) // 256 * 256
+        c_m, s_m, hi, lo = decode_mma(ws[:M * (K // 2)].view(M, K // 2), ws[sx0:sx0 + (K // 32) * Mp], ws[la0:],
+                                      "mxfp4", K, r, M=M)
+        np.testing.assert_array_equal(c_m, qX_ref)
+        np.testing.assert_array_equal(s_m, sX_ref)
+    np.testing.assert_array_equal(hi, bf16_rne_bits(la_g))
+    rem = la_g - (hi.astype(np.uint32) << 16).view(np.float32)
+    np.testing.assert_array_equal(lo, bf16_rne_bits(rem))
+    del ws, c_m, hi, lo, rem
+    log("  kernel 1 (MMA form, forward workspace) bit-exact")
+
+    # ---- kernel 2's exact group sums (INT4)
+    if wl.fmt == "int4":
+        qm, _, _ = lay.quantize_act(X, out=sentinel_act(lay, M, svdq.ACT_MMA), form=svdq.ACT_MMA)
         wins = [(M // 2 - 70, N // 2 - 90, 140, 180), (M - 77, N - 61, 77, 61)]
         for m0, n0, mt, nt in wins:
-            I = lay.group_sums(qX, m0, n0, mt, nt).cpu().numpy()
+            out = torch.full((K // 64, mt, nt), -(2 ** 31), dtype=torch.int32, device="cuda:0")
+            I = lay.group_sums(qm, m0, n0, mt, nt, form=svdq.ACT_MMA, out=out).cpu().numpy()
             I_ref = oforward.group_sums(codes[m0:m0 + mt], p["codesW"][n0:n0 + nt], 64)
             np.testing.assert_array_equal(I, I_ref)
-        log("  group sums exact")
-    rng = np.random.default_rng(7)
-    # random rows and columns, plus some from the last tile row and column (the tiles
-    # kernel 2 may split along K)
-    rows = np.unique(np.concatenate([rng.choice(wl.M, 48, replace=False), [0, wl.M - 1],
-                                     rng.choice(np.arange((wl.M - 1) // 128 * 128, wl.M), 8)]))
-    cols = np.unique(np.concatenate([rng.choice(wl.N, 48, replace=False), [0, wl.N - 1],
-                                     rng.choice(np.arange(wl.N // 2, wl.N), 8)]))
-    Yg = Y.cpu().numpy()[np.ix_(rows, cols)].astype(np.float64)
-    out = oforward.forward(wl.X, p, rows=rows, cols=cols)
-    e = rel_err(Yg, out["Y"])
-    log(f"  sampled output max|err|/RMS = {e:.3e}")
-    assert e <= TOL_Y
-    # the unfused baseline at full size: the same bar, and the fused output up to the
-    # order of the two fp32 terms, on every element
-    Yu = lay.forward(X, fused=False)
-    eu = rel_err(Yu.cpu().numpy()[np.ix_(rows, cols)].astype(np.float64), out["Y"])
-    d = float((Yu - Y).abs().max()) / float(Y.double().pow(2).mean().sqrt())
-    log(f"  unfused baseline: sampled max|err|/RMS = {eu:.3e}, max|Y_unfused - Y|/RMS = {d:.3e}")
-    assert eu <= TOL_Y and d <= 1e-5
+        log("  group sums exact (debug instance of the forward's kernel 2, two windows)")
+        lu = unit_scale_layer(p)
+        gws = sentinel_gemm_ws(lu, M, svdq.ACT_MMA)
+        G = K // 64
+        for g in sorted({0, 1, G // 2, G - 1}):
+            Yg = lu.gemm(qm, mma_scales_int4(M, K, [g]), None, out=sentinel_out(M, N), form=svdq.ACT_MMA,
+                         workspace=gws).cpu().numpy()
+            Ig = oforward.group_sums(codes[:, 64 * g:64 * g + 64], p["codesW"][:, 64 * g:64 * g + 64], 64)[0]
+            np.testing.assert_array_equal(Yg, Ig.astype(np.float32))
+        Ys = lu.gemm(qm, mma_scales_int4(M, K, range(G)), None, out=sentinel_out(M, N), form=svdq.ACT_MMA,
+                     workspace=gws).cpu().numpy()
+        np.testing.assert_array_equal(Ys, oforward.code_product(codes, p["codesW"]).astype(np.float32))
+        del qm, lu, gws, Ys
+        log(f"  timed kernel 2 with unit scales: groups {sorted({0, 1, G // 2, G - 1})} and their total exact, "
+            f"every element")
+
+    # ---- the unfused baseline, every element
+    Yu, _ = forward_sentinel(lay, X, fused=False)
+    _check_y(Yu, Yref, "unfused baseline")
+    d = float((Yu - Y).abs().max()) / float(np.sqrt(np.mean(Yref ** 2)))
+    log(f"  max|Y_unfused - Y|/RMS = {d:.3e}")
+    assert d <= 1e-5
+    del Yu, Y, lay
+
+    # ---- end to end: the library's pack through the forward, against oracle pack + oracle forward
+    calib = svdq.act_absmax(wl.calib)
+    hp = svdq.pack_weights(wl.W, calib, wl.alpha, wl.rank, svdq.FMT[wl.fmt])
+    if wl.lora_A is not None:
+        hp = svdq.concat_lora(hp, wl.lora_A, wl.lora_B)
+    Yl, _ = forward_sentinel(svdq.PackedLinear.from_host_pack(hp), X)
+    _check_y(Yl, Yref, "library pack -> forward vs oracle pack -> oracle forward")

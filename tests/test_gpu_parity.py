@@ -2,14 +2,24 @@
 
 Bar: bit-exact 4-bit codes, scales and INT4 integer group sums; lora_act within the
 arithmetic's error budget; Y within 2e-2 x RMS of the oracle output (fp32 output).
-Shapes span several 256 x 256 output tiles and 16-token kernel-1 tiles with ragged
-tails, K from 128 (the minimum) upward, ranks 0 / 1 / 8 / 48 / 128.
+Shapes span several output tiles and 16-token kernel-1 tiles with ragged tails, K from
+128 (the minimum) upward, ranks 0 / 1 / 8 / 48 / 128, and K long enough for kernel 2 to
+split its last round along K.
+
+Every output, activation and workspace buffer is filled with 0xFF bytes (NaN) before
+the kernels run, so an element no kernel wrote cannot pass as a value left over from
+an earlier allocation.  The exact integer group sums are taken from the forward's own
+kernel 2 twice: through its debug instance (same schedule, loads, LDS layout and
+group-sum MFMA; each group's result stored) and through the timed instance itself, fed
+weight scales 1.0 and activation scales 1.0 on one group and 0.0 on the others, so that
+its output is exactly that group's integer sums (and with 1.0 everywhere their sum).
 """
 import numpy as np
 import pytest
 
-from gpu_helpers import (TOL_Y, bf16_rne_bits, decode_lora_mma, decode_mma, layer_from_oracle, log, lora_bound,
-                         oracle_k1, oracle_pack, rel_err, to_dev_bf16)
+from gpu_helpers import (TOL_Y, assert_finite, bf16_rne_bits, decode_lora_mma, decode_mma, forward_sentinel,
+                         layer_from_oracle, log, lora_bound, mma_scales_int4, oracle_k1, oracle_pack, rel_err,
+                         sentinel_act, sentinel_gemm_ws, sentinel_out, to_dev_bf16, unit_scale_layer)
 
 from bit_diffusion_model_amd import svdq
 from bit_diffusion_model_amd.workloads import make, random_layer
@@ -45,7 +55,7 @@ def test_kernel1_codes_scales_lora(shape):
     p = oracle_pack(wl)
     lay = layer_from_oracle(p)
     X = to_dev_bf16(wl.X)
-    qX, sX, la = lay.quantize_act(X)
+    qX, sX, la = lay.quantize_act(X, out=sentinel_act(lay, M, svdq.ACT_PACKED))
     import torch
 
     torch.cuda.synchronize()
@@ -58,7 +68,7 @@ def test_kernel1_codes_scales_lora(shape):
         assert np.all(np.abs(la_g[:, :r] - la_ref) <= lora_bound(Xh, p["L1b"]))
     # the MMA form: the same codes and scales re-encoded, lora_act as the bf16 hi/lo
     # split of the very fp32 values above
-    qm, sm, lam = lay.quantize_act(X, form=svdq.ACT_MMA)
+    qm, sm, lam = lay.quantize_act(X, out=sentinel_act(lay, M, svdq.ACT_MMA), form=svdq.ACT_MMA)
     c_m, s_m, hi, lo = decode_mma(qm, sm, lam, fmt, K, r, M=M)
     if fmt == "int4":
         np.testing.assert_array_equal(c_m, codes)
@@ -74,20 +84,55 @@ def test_kernel1_codes_scales_lora(shape):
 
 
 @pytest.mark.parametrize("shape", [s for s in SHAPES if s[4] == "int4"], ids=_ids)
-def test_kernel2_group_sums_exact(shape):
+@pytest.mark.parametrize("form", [svdq.ACT_MMA, svdq.ACT_PACKED], ids=["mma", "packed"])
+def test_kernel2_group_sums_exact(shape, form):
+    """Exact integer group sums from kernel 2's debug instance: form MMA is the forward's
+    streamed kernel (same schedule and K split), form PACKED the packed-form kernel."""
+    import torch
+
     M, K, N, r, fmt = shape
-    log(f"groupsums {_ids(shape)}")
+    log(f"groupsums {_ids(shape)} form {form}")
     wl = random_layer(M, K, N, r, 7000 + M + K + N, fmt=fmt, x_out=3, w_out=2)
     p = oracle_pack(wl)
     lay = layer_from_oracle(p)
-    qX, sX, la = lay.quantize_act(to_dev_bf16(wl.X))
+    qX, sX, la = lay.quantize_act(to_dev_bf16(wl.X), out=sentinel_act(lay, M, form), form=form)
     _, codes, _, _, _, _ = oracle_k1(wl.X, p)
     I_ref = oforward.group_sums(codes, p["codesW"], 64)
-    I = lay.group_sums(qX, 0, 0, M, N).cpu().numpy()
+    out = torch.full((K // 64, M, N), -(2 ** 31), dtype=torch.int32, device="cuda:0")
+    I = lay.group_sums(qX, 0, 0, M, N, form=form, out=out).cpu().numpy()
     np.testing.assert_array_equal(I, I_ref)
     if M > 2 and N > 3:  # an interior window
-        I2 = lay.group_sums(qX, M // 3, N // 4, M - M // 3, N - N // 4).cpu().numpy()
+        I2 = lay.group_sums(qX, M // 3, N // 4, M - M // 3, N - N // 4, form=form).cpu().numpy()
         np.testing.assert_array_equal(I2, I_ref[:, M // 3:, N // 4:])
+
+
+@pytest.mark.parametrize("shape", [s for s in SHAPES if s[4] == "int4"], ids=_ids)
+def test_forward_kernel2_exact_with_unit_scales(shape):
+    """The forward's kernel 2 instance itself (the one svdq_linear_forward times), on kernel
+    1's MMA-form codes, with weight scales 1.0: activation scales 1.0 on group g only give
+    Y = I_g exactly (every group, so a K-split tail is covered), and 1.0 everywhere give
+    Y = sum_g I_g = the plain integer product of the codes."""
+    import torch
+
+    M, K, N, r, fmt = shape
+    log(f"unit scales {_ids(shape)}")
+    wl = random_layer(M, K, N, r, 7000 + M + K + N, fmt=fmt, x_out=3, w_out=2)
+    p = oracle_pack(wl)
+    lay = unit_scale_layer(p)
+    qX, _, _ = lay.quantize_act(to_dev_bf16(wl.X), out=sentinel_act(lay, M, svdq.ACT_MMA), form=svdq.ACT_MMA)
+    _, codes, _, _, _, _ = oracle_k1(wl.X, p)
+    I_ref = oforward.group_sums(codes, p["codesW"], 64)
+    G = K // 64
+    gws = sentinel_gemm_ws(lay, M, svdq.ACT_MMA)
+    for g in range(G):
+        Y = lay.gemm(qX, mma_scales_int4(M, K, [g]), None, out=sentinel_out(M, N), form=svdq.ACT_MMA,
+                     workspace=gws).cpu().numpy()
+        np.testing.assert_array_equal(Y, I_ref[g].astype(np.float32))
+    Y = lay.gemm(qX, mma_scales_int4(M, K, range(G)), None, out=sentinel_out(M, N), form=svdq.ACT_MMA,
+                 workspace=gws).cpu().numpy()
+    np.testing.assert_array_equal(Y, oforward.code_product(codes, p["codesW"]).astype(np.float32))
+    if K >= 768:
+        assert gws is not None, "expected kernel 2 to split this shape"
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=_ids)
@@ -97,36 +142,57 @@ def test_forward_matches_oracle(shape):
     wl = random_layer(M, K, N, r, 7000 + M + K + N, fmt=fmt, x_out=3, w_out=2)
     p = oracle_pack(wl)
     lay = layer_from_oracle(p)
-    ws = lay.workspace(M)
-    Y = lay.forward(to_dev_bf16(wl.X), workspace=ws).cpu().numpy().astype(np.float64)
+    Yd, ws = forward_sentinel(lay, to_dev_bf16(wl.X))
+    assert_finite(Yd)
+    Y = Yd.cpu().numpy().astype(np.float64)
     Yref = oforward.forward(wl.X, p)["Y"]
     e = rel_err(Y, Yref)
     log(f"  max|err|/RMS = {e:.3e}")
     assert e <= TOL_Y
+    # the forward keeps the activation side in MMA form at the start of its workspace:
+    # codes and scales bit-exact
+    Mp = (M + 3) // 4 * 4
+    _, codes_ref, _, qX_ref, sX_ref, _ = oracle_k1(wl.X, p)
     if fmt == "int4":
-        # the forward path keeps the activation codes in MMA form (FP6 operand words) at
-        # the start of its workspace
-        codes = decode_mma(ws[:M * K].view(M, K), None, None, "int4", K, 0)[0]
-        np.testing.assert_array_equal(codes, oforward.quantize_activations(wl.X, p["inv_s32"], fmt)[1])
+        sx0 = (M * K + 255) // 256 * 256
+        codes, sv = decode_mma(ws[:M * K].view(M, K), ws[sx0:sx0 + (K // 64) * Mp * 2], None, "int4", K, 0, M=M)[:2]
+        np.testing.assert_array_equal(codes, codes_ref)
+        np.testing.assert_array_equal(sv, sX_ref.view(np.float16).astype(np.float64))
+    else:
+        nq = (M + 1) // 2 * 2 * (K // 2)
+        sx0 = (nq + 255) // 256 * 256
+        rows, sb = decode_mma(ws[:M * (K // 2)].view(M, K // 2), ws[sx0:sx0 + (K // 32) * Mp], None, "mxfp4", K, 0,
+                              M=M)[:2]
+        np.testing.assert_array_equal(rows, qX_ref)
+        np.testing.assert_array_equal(sb, sX_ref)
     # the two kernels called separately in MMA form, kernel 2 with its split workspace,
     # give the same bits as the forward; without the workspace (no split) the same bar
     X = to_dev_bf16(wl.X)
-    qX, sX, la = lay.quantize_act(X, form=svdq.ACT_MMA)
-    gws = lay.gemm_workspace(M, svdq.ACT_MMA)
-    Y2 = lay.gemm(qX, sX, la, form=svdq.ACT_MMA, workspace=gws).cpu().numpy()
+    qX, sX, la = lay.quantize_act(X, out=sentinel_act(lay, M, svdq.ACT_MMA), form=svdq.ACT_MMA)
+    gws = sentinel_gemm_ws(lay, M, svdq.ACT_MMA)
+    Y2 = lay.gemm(qX, sX, la, out=sentinel_out(M, N), form=svdq.ACT_MMA, workspace=gws).cpu().numpy()
     np.testing.assert_array_equal(Y2, Y.astype(np.float32))
-    Yn = lay.gemm(qX, sX, la, form=svdq.ACT_MMA).cpu().numpy().astype(np.float64)
-    en = rel_err(Yn, Yref)
+    Ynd = lay.gemm(qX, sX, la, out=sentinel_out(M, N), form=svdq.ACT_MMA)
+    assert_finite(Ynd)
+    en = rel_err(Ynd.cpu().numpy().astype(np.float64), Yref)
     log(f"  unsplit kernel 2 max|err|/RMS = {en:.3e} (split workspace {0 if gws is None else gws.numel()} B)")
     assert en <= TOL_Y
     if K >= 768:
         assert gws is not None, "expected kernel 2 to split this shape"
     # the packed form meets the same bar
-    qX, sX, la = lay.quantize_act(X)
-    Yp = lay.gemm(qX, sX, la).cpu().numpy().astype(np.float64)
-    ep = rel_err(Yp, Yref)
+    qX, sX, la = lay.quantize_act(X, out=sentinel_act(lay, M, svdq.ACT_PACKED))
+    Ypd = lay.gemm(qX, sX, la, out=sentinel_out(M, N))
+    assert_finite(Ypd)
+    ep = rel_err(Ypd.cpu().numpy().astype(np.float64), Yref)
     log(f"  packed form max|err|/RMS = {ep:.3e}")
     assert ep <= TOL_Y
+
+
+def _fwd(lay, X, ydtype=svdq.F32, fused=True):
+    """The forward on sentinel-filled Y and workspace; every output written and finite."""
+    Y, _ = forward_sentinel(lay, X, ydtype, fused)
+    assert_finite(Y)
+    return Y
 
 
 def test_tiny_config_c0():
@@ -134,7 +200,7 @@ def test_tiny_config_c0():
     p = oracle_pack(wl)
     lay = layer_from_oracle(p)
     X = to_dev_bf16(wl.X)
-    Y = lay.forward(X).cpu().numpy().astype(np.float64)
+    Y = _fwd(lay, X).cpu().numpy().astype(np.float64)
     Yref = oforward.forward(wl.X, p)["Y"]
     e = rel_err(Y, Yref)
     log(f"C0 max|err|/RMS = {e:.3e}")
@@ -144,12 +210,12 @@ def test_tiny_config_c0():
 def test_rank0_and_zero_residual():
     wl = random_layer(200, 256, 300, 8, 99, x_out=3)
     p0 = oracle_pack(wl, rank=0)
-    Y = layer_from_oracle(p0).forward(to_dev_bf16(wl.X)).cpu().numpy().astype(np.float64)
+    Y = _fwd(layer_from_oracle(p0), to_dev_bf16(wl.X)).cpu().numpy().astype(np.float64)
     assert rel_err(Y, oforward.forward(wl.X, p0)["Y"]) <= TOL_Y
     p = dict(oracle_pack(wl))
     p["codesW"] = np.zeros_like(p["codesW"])
     p["qW"] = np.zeros_like(p["qW"])
-    Y = layer_from_oracle(p).forward(to_dev_bf16(wl.X)).cpu().numpy().astype(np.float64)
+    Y = _fwd(layer_from_oracle(p), to_dev_bf16(wl.X)).cpu().numpy().astype(np.float64)
     ref = oforward.forward(wl.X, p)["Y"]
     assert rel_err(Y, ref) <= 1e-3  # only the low-rank branch remains: fp32-accurate
 
@@ -159,13 +225,13 @@ def test_bf16_output_and_determinism():
     p = oracle_pack(wl)
     lay = layer_from_oracle(p)
     X = to_dev_bf16(wl.X)
-    Y32 = lay.forward(X)
-    Yb = lay.forward(X, ydtype=svdq.BF16).float().cpu().numpy().astype(np.float64)
+    Y32 = _fwd(lay, X)
+    Yb = _fwd(lay, X, ydtype=svdq.BF16).float().cpu().numpy().astype(np.float64)
     ref = oforward.forward(wl.X, p)["Y"]
     rms = np.sqrt(np.mean(ref ** 2))
     assert np.all(np.abs(Yb - ref) <= 2.0 ** -8 * np.abs(ref) + TOL_Y * rms)
     for _ in range(5):
-        assert np.array_equal(lay.forward(X).cpu().numpy(), Y32.cpu().numpy())
+        assert np.array_equal(_fwd(lay, X).cpu().numpy(), Y32.cpu().numpy())
 
 
 def test_strided_activation_rows():
@@ -178,7 +244,7 @@ def test_strided_activation_rows():
     Xp[:, :256] = wl.X
     Xd = to_dev_bf16(Xp)[:, :256]
     assert Xd.stride(0) == 320
-    Y = lay.forward(Xd).cpu().numpy().astype(np.float64)
+    Y = _fwd(lay, Xd).cpu().numpy().astype(np.float64)
     assert rel_err(Y, oforward.forward(wl.X, p)["Y"]) <= TOL_Y
 
 
@@ -205,9 +271,11 @@ def test_unfused_baseline_matches_oracle(shape):
     lay = layer_from_oracle(p)
     X = to_dev_bf16(wl.X)
     Yref = oforward.forward(wl.X, p)["Y"]
-    wsf, wsu = lay.workspace(M), lay.workspace(M)
-    Yf = lay.forward(X, workspace=wsf).cpu().numpy()
-    Yu = lay.forward(X, workspace=wsu, fused=False).cpu().numpy()
+    Yfd, wsf = forward_sentinel(lay, X)
+    Yud, wsu = forward_sentinel(lay, X, fused=False)
+    assert_finite(Yfd)
+    assert_finite(Yud)
+    Yf, Yu = Yfd.cpu().numpy(), Yud.cpu().numpy()
     e = rel_err(Yu.astype(np.float64), Yref)
     log(f"  max|err|/RMS = {e:.3e}")
     assert e <= TOL_Y
@@ -222,7 +290,7 @@ def test_unfused_baseline_matches_oracle(shape):
         assert np.abs(Yu.astype(np.float64) - Yf).max() <= 1e-5 * rms
     # bf16 output: the 4-bit term is rounded to bf16 in Y, then Y + lora_act L2 again
     # (each rounding within 2^-8 relative: half a bf16 ulp), on top of the forward's bar
-    Yb = lay.forward(X, ydtype=svdq.BF16, fused=False).float().cpu().numpy().astype(np.float64)
+    Yb = _fwd(lay, X, ydtype=svdq.BF16, fused=False).float().cpu().numpy().astype(np.float64)
     o = oforward.forward(wl.X, p)
     Yres = Yref - (o["lora_act"] @ np.asarray(p["L2b"], np.float64) if r else 0.0)
     rms = np.sqrt(np.mean(Yref ** 2))
@@ -239,7 +307,7 @@ def test_refined_pack_forward():
     p = opack.pack_weights(wl.W, oquant.channel_absmax_cols(wl.calib), wl.alpha, 16, "int4", refine_iters=3)
     log(f"refined pack: errors {p['errors']}, kept iterate {p['best_iter']}")
     lay = layer_from_oracle(p)
-    Y = lay.forward(to_dev_bf16(wl.X)).cpu().numpy().astype(np.float64)
+    Y = _fwd(lay, to_dev_bf16(wl.X)).cpu().numpy().astype(np.float64)
     e = rel_err(Y, oforward.forward(wl.X, p)["Y"])
     log(f"  max|err|/RMS = {e:.3e}")
     assert e <= TOL_Y
@@ -263,9 +331,11 @@ def test_unfused_strided_rows_and_padded_output(ydtype):
     outs = []
     for fused in (True, False):
         Yfull = torch.full((M, N + 28), 7.0, dtype=dt, device="cuda:0")
+        Yfull[:, :N] = float("nan")  # the sentinel: every element the forward must write
         Y = Yfull[:, :N]
         lay.forward(Xd, ydtype=ydtype, out=Y, fused=fused)
         assert bool((Yfull[:, N:] == 7.0).all()), "padding columns written"
+        assert_finite(Y)
         outs.append(Y.float().cpu().numpy().astype(np.float64))
     Yref = oforward.forward(wl.X, p)["Y"]
     rms = np.sqrt(np.mean(Yref ** 2))

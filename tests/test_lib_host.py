@@ -339,7 +339,11 @@ def test_device_entry_points_validate_on_host():
     assert L.svdq_linear_forward_unfused(ref, 4, 16, 256, 16, 64, 0, 256, 10, None) == 1 and "workspace" in _err()
     assert L.svdq_linear_forward_unfused(ref, 0, 16, 256, 16, 64, 0, None, 0, None) == 0  # M = 0: no-op
     assert L.svdq_linear_forward_unfused(ref, -1, 16, 256, 16, 64, 0, None, 0, None) == 1
-    assert L.svdq_debug_group_sums(ref, 4, 16, 0, 0, 5, 4, 16, None) == 1 and "window" in _err()
+    assert L.svdq_debug_group_sums(ref, 4, 1, 16, 0, 0, 5, 4, 16, None) == 1 and "window" in _err()
+    assert L.svdq_debug_group_sums(ref, 4, 0, 16, 0, 0, 5, 4, 16, None) == 1 and "window" in _err()
+    assert L.svdq_debug_group_sums(ref, 4, 3, 16, 0, 0, 4, 4, 16, None) == 2 and "form" in _err()
+    # the output rows of a tile are addressed through a 32-bit range: ldy below 2^22
+    assert L.svdq_gemm_w4a4_lora_up(ref, 4, 1, 16, 16, 16, 16, 1 << 22, 0, None, 0, None) == 2 and "ldy" in _err()
     # MMA form: FP6 operand words (M*K bytes), fp16 scales (2 bytes per group and row),
     # 2*R16 bf16 per row, rows rounded up to 32
     assert L.svdq_workspace_bytes(ref, 100) >= 100 * 256 + 4 * 100 * 2 + 128 * 16 * 4

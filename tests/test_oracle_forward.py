@@ -92,6 +92,19 @@ def test_group_sums_brute_force_and_bound():
     assert np.abs(I).max() <= 64 * 49
 
 
+def test_code_product_brute_force_and_group_sum_total():
+    """code_product = the plain integer product of the codes, by a Python double loop over
+    (m, n) with an explicit sum over k, and equal to the group sums added over groups."""
+    rng = np.random.default_rng(4)
+    M, N, K = 4, 5, 256
+    cX = rng.integers(-7, 8, (M, K)).astype(np.int8)
+    cW = rng.integers(-7, 8, (N, K)).astype(np.int8)
+    P = forward.code_product(cX, cW)
+    for m, n in itertools.product(range(M), range(N)):
+        assert P[m, n] == sum(int(cX[m, k]) * int(cW[n, k]) for k in range(K))
+    np.testing.assert_array_equal(P, forward.group_sums(cX, cW, 64).sum(axis=0))
+
+
 def test_rank0_reduces_to_dequantized_gemm():
     wl = random_layer(40, 256, 72, 0, 9, x_out=3)
     p = _pack(wl)
