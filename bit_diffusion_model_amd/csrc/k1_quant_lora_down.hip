@@ -154,7 +154,8 @@ k1_quant_lora_down(const uint16_t* __restrict__ X, int64_t ldx, int64_t M, int64
       a = wave_max_xor(a, 32);
       const _Float16 sh = (_Float16)fminf(a / 7.0f, 65504.0f);
       const float sf = (float)sh;
-      const float rcp = sf > 0.0f ? 1.0f / sf : 0.0f;  // s = 0: every x is 0, every code 0
+      // s = 0 (all-zero group, or one whose fp16 scale underflows): every code 0
+      const float rcp = sf > 0.0f ? 1.0f / sf : 0.0f;
       float t[16];
       float dev = 0.f;
 #pragma unroll
@@ -170,7 +171,8 @@ k1_quant_lora_down(const uint16_t* __restrict__ X, int64_t ldx, int64_t M, int64
           const float e = fmaf(-q, sf, xh[i]);
           const float ae = fabsf(e);
           const int odd = ((int)q) & 1;
-          const int away = (int)(ae > hs) | ((int)(ae == hs) & odd);
+          // with s = 0 the codes stay 0 (every nonzero x would test as beyond s / 2)
+          const int away = sf > 0.0f ? (int)(ae > hs) | ((int)(ae == hs) & odd) : 0;
           t[i] = q + (float)away * copysignf(1.0f, e);
         }
       }

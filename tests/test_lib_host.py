@@ -47,6 +47,8 @@ def test_residual_quantizer_bit_exact(fmt):
     R[:, 3] = 0.0
     R[5:70, 7] = np.float32(0.5) * (np.arange(65) % 15 - 7)  # exact ties at s = 1
     R[:64, 8] = (np.arange(64) - 32).astype(np.float32) / 4.0
+    R[:64, 9] = np.linspace(-1e-9, 1e-9, 64).astype(np.float32)  # the fp16 scale underflows to 0: codes 0
+    R[64:128, 9] = np.float32(1e6) * np.linspace(-1, 1, 64).astype(np.float32)  # the scale saturates
     codes, sc = opack.quantize_residual(R, fmt)
     qW, sW = svdq.quantize_weights(R, svdq.FMT[fmt])
     np.testing.assert_array_equal(qW, opack.pack_codes(codes, fmt))
