@@ -164,15 +164,15 @@ k1_quant_lora_down(const uint16_t* __restrict__ X, int64_t ldx, int64_t M, int64
         dev = fmaxf(dev, fabsf(t[i] - rintf(t[i])));
       }
       if (__builtin_amdgcn_ballot_w64(dev > 0.49999237f) != 0) {  // 0.5 - 2^-17
-        const float hs = 0.5f * sf;
+        // with s = 0 the codes stay 0: no |x - q s| exceeds an infinite half-scale
+        const float hs = sf > 0.0f ? 0.5f * sf : __builtin_inff();
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const float q = rintf(t[i]);
           const float e = fmaf(-q, sf, xh[i]);
           const float ae = fabsf(e);
           const int odd = ((int)q) & 1;
-          // with s = 0 the codes stay 0 (every nonzero x would test as beyond s / 2)
-          const int away = sf > 0.0f ? (int)(ae > hs) | ((int)(ae == hs) & odd) : 0;
+          const int away = (int)(ae > hs) | ((int)(ae == hs) & odd);
           t[i] = q + (float)away * copysignf(1.0f, e);
         }
       }
@@ -196,11 +196,18 @@ k1_quant_lora_down(const uint16_t* __restrict__ X, int64_t ldx, int64_t M, int64
           fw[d] = (r[0] & EV[d]) | (r[1] & ~EV[d]);
         }
       }
+      // the even quarter of each pair also takes word 3 (the odd quarter's first word), so
+      // a half is stored as [w0 w1 w2 w3 | w4 w5 0 0]: kernel 2 reads its six words as one
+      // 16-byte and one 8-byte load into an aligned run of registers
+      uint32_t w3 = 0u;
+      if constexpr (MMA) w3 = __builtin_amdgcn_permlane16_swap(fw[0], fw[0], false, false)[1];
       if (row_ok) {
         if constexpr (MMA) {
           // [M][K/64][64] bytes per token and group: quarter q stores 16 bytes at 16 q,
-          // words 0-2 (quarter 2h) or 3-5 (quarter 2h+1) of half h, then a zero word
-          *reinterpret_cast<uint4*>(qX + row * K + k0) = make_uint4(fw[0], fw[1], fw[2], 0u);
+          // words 0-3 of half h (quarter 2h) or words 4-5 and two zero words (quarter 2h+1)
+          const bool odd = (sub & 1) != 0;
+          *reinterpret_cast<uint4*>(qX + row * K + k0) =
+              odd ? make_uint4(fw[1], fw[2], 0u, 0u) : make_uint4(fw[0], fw[1], fw[2], w3);
         } else {
           uint32_t w0 = 0, w1 = 0;
 #pragma unroll

@@ -421,14 +421,17 @@ struct Shape {
   static constexpr int CB = BN / 32;                 // 32-wide column blocks per tile
   static constexpr int PART = (BM / 32) * CB * 16 * 64;  // floats per partial tile
 };
-// INT4: 128 x 128, 4 waves of 64 x 64 (the rescale schedule's 2 x 2 MFMA tiles), two
-// blocks per CU (a 128 x 256 tile with one block per CU measured 6% slower: the waves
-// of one block meet at every barrier).  MXFP4: 256 x 128, 4 waves of 128 x 64, two blocks
-// per CU (no per-group VALU, so larger wave tiles; measured against 256 x 256 tiles of 8
-// waves, which halve the panel bytes per output but leave the QKV layer 2.53 rounds of
-// tiles in 3 rounds of one block per CU: 96 against 102 us).
+// INT4: 128 x 128, 4 waves side by side, each 128 x 32 (four row tiles against one
+// column tile), two blocks per CU (a 128 x 256 tile with one block per CU measured 6%
+// slower: the waves of one block meet at every barrier).  The per-group rescale makes
+// VALU work the bound; a wave expands one weight fragment per group for four tiles
+// (half the expansion work of 64 x 64 waves, for a third more LDS operand reads).
+// MXFP4: 256 x 128, 4 waves of 128 x 64, two blocks per CU (no per-group VALU, so larger
+// wave tiles; measured against 256 x 256 tiles of 8 waves, which halve the panel bytes
+// per output but leave the QKV layer 2.53 rounds of tiles in 3 rounds of one block per
+// CU: 96 against 102 us).
 template <int FMT> struct SShape;
-template <> struct SShape<0> : Shape<2, 2, 2, 2> {};
+template <> struct SShape<0> : Shape<1, 4, 4, 1> {};
 template <> struct SShape<1> : Shape<2, 2, 4, 2> {};
 
 // LDS layout of one stage of the streamed kernel
@@ -597,7 +600,8 @@ __global__ __launch_bounds__(SShape<FMT>::NT, 8 / SShape<FMT>::NW) __attribute__
 
   // ---- the fragments of one sub-step u of a stage, read from LDS --------------------------
   struct Frag {
-    uint4 a[TI][FMT == 0 ? 2 : 1];  // A: INT4 FP6 operand (words 0-2 | pad, 3-5 | pad), MXFP4 32 nibbles
+    uint4 a[TI];                    // A: INT4 FP6 operand words 0-3 (4-5 in a4), MXFP4 32 nibbles
+    uint2 a4[FMT == 0 ? TI : 1];    // A: INT4 FP6 operand words 4-5
     uint4 b[TJ];                    // B: 32 4-bit codes
     uint32_t sa[TI], sb[TJ];        // MXFP4: E8M0 block scales; INT4: fp16 scale bits of the
                                     // lane's row / column (the column's 0 in lanes 32-63)
@@ -620,14 +624,16 @@ __global__ __launch_bounds__(SShape<FMT>::NT, 8 / SShape<FMT>::NW) __attribute__
     for (int i = 0; i < TI; ++i) {
       const int row = wm + i * 32 + l32;
       if constexpr (FMT == 0) {
-        const int ls0 = u * 4 + kh * 2;  // operand half kh of sub-step u: bytes u*64 + kh*32, two slots
+        // operand half kh of sub-step u: bytes u*64 + kh*32 in two slots, [w0 w1 w2 w3 |
+        // w4 w5 0 0]: a 16-byte and an 8-byte read into one aligned run of registers
+        const int ls0 = u * 4 + kh * 2;
         const int sw = swz(row, D::RA / 16);
-        f.a[i][0] = *reinterpret_cast<const uint4*>(base + row * D::RA + ((ls0 ^ sw) * 16));
-        f.a[i][1] = *reinterpret_cast<const uint4*>(base + row * D::RA + (((ls0 + 1) ^ sw) * 16));
+        f.a[i] = *reinterpret_cast<const uint4*>(base + row * D::RA + ((ls0 ^ sw) * 16));
+        f.a4[i] = *reinterpret_cast<const uint2*>(base + row * D::RA + (((ls0 + 1) ^ sw) * 16));
         f.sa[i] = reinterpret_cast<const uint16_t*>(sb)[row];
       } else {
         const int ls = u * 2 + kh;
-        f.a[i][0] = *reinterpret_cast<const uint4*>(base + row * D::RA + ((ls ^ swz(row, D::RA / 16)) * 16));
+        f.a[i] = *reinterpret_cast<const uint4*>(base + row * D::RA + ((ls ^ swz(row, D::RA / 16)) * 16));
         f.sa[i] = sb[kh * BM + row];
       }
     }
@@ -641,8 +647,9 @@ __global__ __launch_bounds__(SShape<FMT>::NT, 8 / SShape<FMT>::NW) __attribute__
   // FP6 code q is q / 8 and both block scales are 2^3 (E8M0 byte 130), so the MFMA
   // returns the exact integer group sum I
   auto gs = [&](const Frag& f, const v8i (&bf)[TJ], int i, int j) {
-    const uint4 x0 = f.a[i][0], x1 = f.a[i][FMT == 0 ? 1 : 0];
-    const v8i af = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x1.x, (int)x1.y, (int)x1.z, 0, 0};
+    const uint4 x0 = f.a[i];
+    const uint2 x1 = f.a4[FMT == 0 ? i : 0];
+    const v8i af = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, 0, 0};
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf[j], v16f{}, 2, 2, 0, 130, 0, 130);
   };
   // c = sX sW for the 32 x 32 tile: an fp16 MFMA whose only nonzero k term is the pair of
@@ -665,7 +672,7 @@ __global__ __launch_bounds__(SShape<FMT>::NT, 8 / SShape<FMT>::NW) __attribute__
     for (int i = 0; i < TI; ++i)
 #pragma unroll
       for (int j = 0; j < TJ; ++j) {
-        const v8i af = {(int)f.a[i][0].x, (int)f.a[i][0].y, (int)f.a[i][0].z, (int)f.a[i][0].w, 0, 0, 0, 0};
+        const v8i af = {(int)f.a[i].x, (int)f.a[i].y, (int)f.a[i].z, (int)f.a[i].w, 0, 0, 0, 0};
         const v8i bf = {(int)f.b[j].x, (int)f.b[j].y, (int)f.b[j].z, (int)f.b[j].w, 0, 0, 0, 0};
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf, acc[i][j], 4, 4, 0, (int)f.sa[i], 0,
                                                                    (int)f.sb[j]);
@@ -707,16 +714,18 @@ __global__ __launch_bounds__(SShape<FMT>::NT, 8 / SShape<FMT>::NW) __attribute__
         v8i bf[TJ];
         expand(F, bf);
         // two tiles in flight: tile t+1's MFMAs are issued ahead of tile t's rescale
-        v16f c0 = sc(F, 0, 0), p0 = gs(F, bf, 0, 0);
-        v16f c1 = sc(F, 0, 1), p1 = gs(F, bf, 0, 1);
-        epi(0, 0, p0, c0);
-        c0 = sc(F, 1, 0);
-        p0 = gs(F, bf, 1, 0);
-        epi(0, 1, p1, c1);
-        c1 = sc(F, 1, 1);
-        p1 = gs(F, bf, 1, 1);
-        epi(1, 0, p0, c0);
-        epi(1, 1, p1, c1);
+        constexpr int NTL = TI * TJ;
+        v16f c[2], p[2];
+        c[0] = sc(F, 0, 0);
+        p[0] = gs(F, bf, 0, 0);
+#pragma unroll
+        for (int t = 0; t < NTL; ++t) {
+          if (t + 1 < NTL) {
+            c[(t + 1) & 1] = sc(F, (t + 1) / TJ, (t + 1) % TJ);
+            p[(t + 1) & 1] = gs(F, bf, (t + 1) / TJ, (t + 1) % TJ);
+          }
+          epi(t / TJ, t % TJ, p[t & 1], c[t & 1]);
+        }
       } else {
         mma4(F);
       }

@@ -66,8 +66,8 @@ typedef enum { SVDQ_F32 = 0, SVDQ_BF16 = 1 } svdq_dtype;
  *           FP6 E2M3 operands, 6-bit fields sign << 5 | |q| (exponent 0: value q / 8).
  *           Group half h (32 codes) is six 32-bit words w0..w5 holding field f at bit
  *           6 f of their 192-bit concatenation, field f carrying k = 32 h + 16 (f & 1)
- *           + (f >> 1) of the group; it is stored at byte 32 h as [w0 w1 w2 0 w3 w4 w5
- *           0]; sX [K/64][Mp] fp16 bits.
+ *           + (f >> 1) of the group; it is stored at byte 32 h as [w0 w1 w2 w3 w4 w5
+ *           0 0]; sX [K/64][Mp] fp16 bits.
  *           MXFP4: the PACKED codes in token pairs: byte b of token m's code row at
  *           (m / 2) * K + (b / 64) * 128 + (m % 2) * 64 + b % 64 ((M rounded up to 2) *
  *           K/2 bytes); sX [K/32][Mp] E8M0 bytes.

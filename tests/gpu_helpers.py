@@ -95,7 +95,7 @@ def decode_lora_mma(la, M, rank):
 
 def decode_mma(qX, sX, la, fmt, K, rank, M=None):
     """Kernel 1's MMA-form outputs (device tensors) decoded per the header's description:
-    INT4: per token and group 64 bytes, half h at byte 32 h as words [f0 f1 f2 0 f3 f4 f5
+    INT4: per token and group 64 bytes, half h at byte 32 h as words [f0 f1 f2 f3 f4 f5 0
     0]; the 192-bit f0..f5 hold 6-bit E2M3 fields (sign bit 5, exponent 0, |q| in bits
     0-2), field f carrying k = 32 h + 16 (f & 1) + (f >> 1); fp16 scale bits [K/64][Mp].
     MXFP4: codes in token pairs (byte b of token m at (m / 2) K + (b / 64) 128 + (m % 2)
@@ -116,8 +116,8 @@ def decode_mma(qX, sX, la, fmt, K, rank, M=None):
     if fmt == "int4":
         G = K // 64
         w = np.ascontiguousarray(q).view("<u4").reshape(M, G, 2, 8)
-        assert not w[..., 3].any() and not w[..., 7].any(), "padding words must be zero"
-        fl = _fp6_fields(w[..., [0, 1, 2, 4, 5, 6]])
+        assert not w[..., 6].any() and not w[..., 7].any(), "padding words must be zero"
+        fl = _fp6_fields(w[..., :6])
         assert not (fl & 0b011000).any(), "nonzero E2M3 exponent bits"
         v = (fl & 7) * np.where(fl & 32, -1, 1)
         kk = np.array([16 * (f & 1) + (f >> 1) for f in range(32)])
