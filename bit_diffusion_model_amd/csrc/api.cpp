@@ -142,6 +142,13 @@ svdq_status svdq_gemm_w4a4_lora_up(const svdq_layer* layer, int64_t M, int32_t f
 svdq_status svdq_linear_forward(const svdq_layer* layer, int64_t M, const uint16_t* X, int64_t ldx,
                                 void* Y, int64_t ldy, int32_t ydtype, void* workspace,
                                 size_t ws_bytes, void* stream) {
+  return svdq::linear_forward(layer, M, X, ldx, Y, ldy, ydtype, workspace, ws_bytes, stream);
+}
+
+}  // extern "C"
+
+svdq_status svdq::linear_forward(const svdq_layer* layer, int64_t M, const uint16_t* X, int64_t ldx, void* Y,
+                                 int64_t ldy, int32_t ydtype, void* workspace, size_t ws_bytes, void* stream) {
   KernelLayer kl;
   svdq_status st = check_layer(layer, kl);
   if (st != SVDQ_OK) return st;
@@ -158,6 +165,8 @@ svdq_status svdq_linear_forward(const svdq_layer* layer, int64_t M, const uint16
   if (st != SVDQ_OK) return st;
   return run_k2(layer, M, SVDQ_ACT_MMA, qX, sX, la, Y, ldy, ydtype, base + w.part, w.total - w.part, stream);
 }
+
+extern "C" {
 
 svdq_status svdq_linear_forward_unfused(const svdq_layer* layer, int64_t M, const uint16_t* X, int64_t ldx,
                                         void* Y, int64_t ldy, int32_t ydtype, void* workspace,

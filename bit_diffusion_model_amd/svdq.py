@@ -43,8 +43,9 @@ EXPORTS = [
     "svdq_quantize_weights", "svdq_concat_lora", "svdq_prepare_lowrank_down", "svdq_prepare_lowrank",
     "svdq_prepare_weights",
     "svdq_quantize_act_lora_down", "svdq_gemm_w4a4_lora_up", "svdq_gemm_workspace_bytes", "svdq_workspace_bytes",
-    "svdq_linear_forward", "svdq_linear_forward_unfused", "svdq_debug_group_sums",
+    "svdq_linear_forward", "svdq_linear_forward_unfused", "svdq_debug_group_sums", "svdq_linear_forward_noalloc",
 ]
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 def lib():
@@ -74,6 +75,7 @@ def lib():
         "svdq_linear_forward": (I32, [P, I64, P, I64, P, I64, I32, P, ctypes.c_size_t, P]),
         "svdq_linear_forward_unfused": (I32, [P, I64, P, I64, P, I64, I32, P, ctypes.c_size_t, P]),
         "svdq_debug_group_sums": (I32, [P, I64, I32, P, I64, I64, I64, I64, P, P]),
+        "svdq_linear_forward_noalloc": (I32, [P, I64, P, I64, P, I64, I32, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -347,6 +349,18 @@ class PackedLinear:
         fn = lib().svdq_linear_forward if fused else lib().svdq_linear_forward_unfused
         _check(fn(self.c_layer(), M, _dptr(X), X.stride(0), _dptr(out), out.stride(0), ydtype, _dptr(ws), ws.numel(),
                   _stream()))
+        return out
+
+    def forward_noalloc(self, X, ydtype: int = F32, out=None):
+        """svdq_linear_forward_noalloc: the forward with its workspace in the library's fixed
+        device array (no workspace argument, nothing allocated by the library)."""
+        torch = _torch()
+        M = X.shape[0]
+        if out is None:
+            out = torch.empty((M, self.N), dtype=torch.float32 if ydtype == F32 else torch.bfloat16,
+                              device=self.device)
+        _check(lib().svdq_linear_forward_noalloc(self.c_layer(), M, _dptr(X), X.stride(0), _dptr(out), out.stride(0),
+                                                 ydtype, _stream()))
         return out
 
     def group_sums(self, qX, m0: int, n0: int, mt: int, nt: int, form: int = ACT_PACKED, out=None):

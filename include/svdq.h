@@ -276,6 +276,26 @@ svdq_status svdq_linear_forward(const svdq_layer* layer, int64_t M, const uint16
                                 int64_t ldx, void* Y, int64_t ldy, int32_t ydtype,
                                 void* workspace, size_t ws_bytes, void* stream);
 
+/* Size in bytes of the fixed device array svdq_linear_forward_noalloc uses as its
+ * workspace (one per device): 64 MiB, enough for every FLUX.1 layer workload of this
+ * library (the largest, the MLP fc2 layer at 4608 tokens, needs about 59 MB). */
+#define SVDQ_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* For callers that cannot allocate device memory (code under HIP stream capture, serving
+ * loops that must not call an allocator): svdq_linear_forward with its workspace in a
+ * fixed device array of the library (SVDQ_NOALLOC_SCRATCH_BYTES, one copy per device,
+ * held until the process ends) instead of a caller's buffer.  Same kernels, launches and
+ * results, bit for bit, as svdq_linear_forward.  The call allocates nothing: on its first
+ * call on a device it looks up that device's copy of the array (hipGetSymbolAddress).
+ * The array needs no clearing: every byte a call reads is written earlier in that call.
+ * Every call on one device shares that device's array, so calls that overlap on one
+ * device (other streams or threads without ordering between them) race and must not be
+ * made.  Arguments and errors as for svdq_linear_forward; EUNSUPPORTED, with nothing
+ * launched, when svdq_workspace_bytes(layer, M) exceeds SVDQ_NOALLOC_SCRATCH_BYTES. */
+svdq_status svdq_linear_forward_noalloc(const svdq_layer* layer, int64_t M, const uint16_t* X,
+                                        int64_t ldx, void* Y, int64_t ldy, int32_t ydtype,
+                                        void* stream);
+
 /* The unfused baseline (jeonghoonpark.com "SVDQuant" review, section 4.3, Figure 6(a)):
  * the same layer with the low-rank branch run as kernels of its own, the arrangement
  * the fused path is measured against.  Four launches on `stream`: kernel 1 without the
