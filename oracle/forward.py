@@ -23,13 +23,16 @@ from . import quant
 from .numerics import f16_to_f64
 
 
-def quantize_activations(X_bits: np.ndarray, inv_s32: np.ndarray, fmt: str):
-    """Steps 1-2.  Returns (X_hat fp32 [M][K], codes [M][K], scales [M][K/G])."""
+def quantize_activations(X_bits: np.ndarray, inv_s32: np.ndarray, fmt: str, S_X=None):
+    """Steps 1-2.  Returns (X_hat fp32 [M][K], codes [M][K], scales [M][K/G]); NVFP4
+    quantizes under the activations' tensor scale S_X."""
     Xh = quant.smooth_activations(X_bits, inv_s32)
     if fmt == "int4":
         codes, sc = quant.quantize_int4(Xh, quant.INT4_GROUP)
     elif fmt == "mxfp4":
         codes, sc = quant.quantize_mxfp4(Xh, quant.FP4_GROUP)
+    elif fmt == "nvfp4":
+        codes, sc = quant.quantize_nvfp4(Xh, S_X)
     else:
         raise ValueError(fmt)
     return Xh, codes, sc
@@ -109,6 +112,28 @@ def residual_mxfp4(cX, eX, cW, eW, rows=None, cols=None) -> np.ndarray:
     return Y
 
 
+def residual_nvfp4(cX, eX, S_X, cW, eW, S_W, rows=None, cols=None) -> np.ndarray:
+    """Steps 4-5 (NVFP4-style): S_X S_W sum_g sX[m,g] sW[g,n] sum_k vX vW in fp64.
+
+    cX [M][K] E2M1 codes, eX [M][K/16] E4M3 bytes; cW [N][K], eW [K/16][N]; S_X, S_W the
+    fp32 tensor scales.  Each group's dot product of E2M1 values is exact in fp64."""
+    G = quant.NV_GROUP
+    if rows is not None:
+        cX, eX = cX[rows], eX[rows]
+    if cols is not None:
+        cW, eW = cW[cols], eW[:, cols]
+    vX = quant.e2m1_value(cX)
+    vW = quant.e2m1_value(cW)
+    sX = quant.e4m3_value(eX)
+    sW = quant.e4m3_value(eW)
+    M, K = cX.shape
+    Y = np.zeros((M, cW.shape[0]))
+    for g in range(K // G):
+        Pg = vX[:, g * G:(g + 1) * G] @ vW[:, g * G:(g + 1) * G].T
+        Y += (sX[:, g][:, None] * sW[g][None, :]) * Pg
+    return Y * (np.float64(np.float32(S_X)) * np.float64(np.float32(S_W)))
+
+
 def forward(X_bits: np.ndarray, packed: dict, rows=None, cols=None) -> dict:
     """Full layer.  ``packed`` holds inv_s32, L1b [K][r], L2b [r][N], codesW [N][K],
     sW [K/G][N] and fmt (as produced by oracle.pack, or the same arrays from elsewhere).
@@ -116,10 +141,12 @@ def forward(X_bits: np.ndarray, packed: dict, rows=None, cols=None) -> dict:
     Returns dict(Xh, codesX, scalesX [M][K/G], lora_act [M][r], Y [rows][cols]).
     """
     fmt = packed["fmt"]
-    Xh, cX, sX = quantize_activations(X_bits, packed["inv_s32"], fmt)
+    Xh, cX, sX = quantize_activations(X_bits, packed["inv_s32"], fmt, packed.get("S_X"))
     la = lora_down(Xh, packed["L1b"]) if packed["L1b"].shape[1] else np.zeros((Xh.shape[0], 0))
     if fmt == "int4":
         Y = residual_int4(cX, sX, packed["codesW"], packed["sW"], rows, cols)
+    elif fmt == "nvfp4":
+        Y = residual_nvfp4(cX, sX, packed["S_X"], packed["codesW"], packed["sW"], packed["S_W"], rows, cols)
     else:
         Y = residual_mxfp4(cX, sX, packed["codesW"], packed["sW"], rows, cols)
     la_r = la if rows is None else la[rows]

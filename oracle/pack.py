@@ -49,29 +49,40 @@ def svd_split(W_hat: np.ndarray, rank: int):
     return dict(L1=L1, L2=L2, L1b=L1b, L2b=L2b, R=R, sigma=S)
 
 
+def residual_tensor_scale(R32: np.ndarray) -> np.float32:
+    """NVFP4-style level-2 scale of the residual: from its max |R| over the whole tensor."""
+    return quant.nvfp4_tensor_scale(np.abs(np.asarray(R32, dtype=np.float32)).max())
+
+
 def quantize_residual(R32: np.ndarray, fmt: str):
     """Quantize R [K x N] per output column n, in groups along K.
 
     Returns (codes [N][K], scales [K/G][N]): INT4 codes int8 with fp16 scale bits, or
-    E2M1 codes uint8 with E8M0 bytes.
+    E2M1 codes uint8 with E8M0 bytes (MXFP4) or E4M3 bytes (NVFP4, under the tensor scale
+    residual_tensor_scale(R32)).
     """
     Rt = np.ascontiguousarray(np.asarray(R32, dtype=np.float32).T)  # [N][K]
     if fmt == "int4":
         codes, sc = quant.quantize_int4(Rt, quant.INT4_GROUP)
     elif fmt == "mxfp4":
         codes, sc = quant.quantize_mxfp4(Rt, quant.FP4_GROUP)
+    elif fmt == "nvfp4":
+        codes, sc = quant.quantize_nvfp4(Rt, residual_tensor_scale(R32))
     else:
         raise ValueError(fmt)
     return codes, np.ascontiguousarray(sc.T)
 
 
-def dequant_residual(codes: np.ndarray, sW: np.ndarray, fmt: str) -> np.ndarray:
-    """deq(Q(R)) [K][N] in fp64 from codes [N][K] and group-major scales [K/G][N]."""
+def dequant_residual(codes: np.ndarray, sW: np.ndarray, fmt: str, S=None) -> np.ndarray:
+    """deq(Q(R)) [K][N] in fp64 from codes [N][K] and group-major scales [K/G][N]
+    (NVFP4: S is the tensor scale the codes were made under)."""
     sc = np.ascontiguousarray(np.asarray(sW).T)  # [N][K/G]
     if fmt == "int4":
         D = quant.dequant_int4(codes, sc, quant.INT4_GROUP)
     elif fmt == "mxfp4":
         D = quant.dequant_mxfp4(codes, sc, quant.FP4_GROUP)
+    elif fmt == "nvfp4":
+        D = quant.dequant_nvfp4(codes, sc, S)
     else:
         raise ValueError(fmt)
     return np.ascontiguousarray(D.T)
@@ -83,8 +94,9 @@ def split_error(W_hat: np.ndarray, L1b: np.ndarray, L2b: np.ndarray, fmt: str):
     E = ||W_hat - L1b L2b - deq(Q(R))||_F (the quantization error of the decomposition,
     review section 4.1 measures errors in the Frobenius norm)."""
     R = W_hat - L1b @ L2b
-    codes, sW = quantize_residual(R.astype(np.float32), fmt)
-    D = dequant_residual(codes, sW, fmt)
+    R32 = R.astype(np.float32)
+    codes, sW = quantize_residual(R32, fmt)
+    D = dequant_residual(codes, sW, fmt, residual_tensor_scale(R32) if fmt == "nvfp4" else None)
     return dict(R=R, codes=codes, sW=sW, D=D, err=float(np.linalg.norm(R - D)))
 
 
@@ -158,6 +170,14 @@ def pack_weights(W_bits: np.ndarray, act_absmax, alpha: float, rank: int, fmt: s
         extra = dict(errors=errors, best_iter=best_t)
     R32 = sp["R"].astype(np.float32)
     codesW, sW = quantize_residual(R32, fmt)
+    if fmt == "nvfp4":
+        # level-2 scales: the residual's, and the smoothed calibration activations' (max
+        # over channels of fp32(max|X_k| * inv_s_k), fixed offline like s itself)
+        extra["S_W"] = residual_tensor_scale(R32)
+        # without a calibration statistic (act_absmax None) the activations' level-2
+        # scale is 1; callers then set S_X themselves
+        extra["S_X"] = (np.float32(1.0) if act_absmax is None else quant.nvfp4_tensor_scale(
+            (np.asarray(act_absmax, np.float32) * inv_s32).astype(np.float32).max()))
     return dict(
         fmt=fmt, K=K, N=N, rank=rank, s64=s64, s32=s32, inv_s32=inv_s32, W_hat=W_hat,
         L1=sp["L1"], L2=sp["L2"], L1b=sp["L1b"], L2b=sp["L2b"],
