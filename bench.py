@@ -36,7 +36,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k2_gemm_int4_flux_qkv_traffic.jso
 
 WORKLOADS = {"C1": "FLUX.1 QKV projection", "C2a": "FLUX.1 MLP fc1", "C2b": "FLUX.1 MLP fc2",
              "C3": "FLUX.1 QKV projection, MXFP4", "C4": "FLUX.1 QKV projection at batch 2 + rank-16 LoRA",
-             "C0": "tiny layer"}
+             "C0": "tiny layer", "C1nv": "FLUX.1 QKV projection, NVFP4-style group-16 two-level scales"}
+PEAK_BF16_TOPS = 2500.0  # dense fp16 / bf16 MFMA, what the NVFP4 kernel 2 runs on
 
 
 def log(msg):
@@ -253,6 +254,10 @@ def measure(svdq, torch, wl_name, ydt, steps, warmup, warm_s, compare, log_prefi
         # the INT4 contraction runs on the FP6 scaled MFMA (10.1 PF dense); against the
         # INT8 peak (5.0 POP/s) that the INT4 format would use on an int8 matrix core
         "k2_frac_fp6_fp4_peak": round(k2_tops / PEAK_MFMA_FP4_TOPS, 4),
+        # against the peak of the matrix-core instruction kernel 2 runs (FP6/FP4 for INT4 and
+        # MXFP4, fp16 for NVFP4)
+        "k2_mfma_peak": PEAK_BF16_TOPS if fmt == svdq.NVFP4_G16 else PEAK_MFMA_FP4_TOPS,
+        "k2_frac_of_mfma_peak": round(k2_tops / (PEAK_BF16_TOPS if fmt == svdq.NVFP4_G16 else PEAK_MFMA_FP4_TOPS), 4),
         "k2_frac_int8_peak": round(k2_tops / PEAK_INT8_TOPS, 4) if fmt == svdq.INT4_G64 else None,
         "rank0_ms": rnd(ms0, 5), "fwd_ms_paired": rnd(ms_r, 5), "lowrank_overhead": rnd(ms_r / ms0 - 1.0, 4),
         "unfused_ms": rnd(ms_u, 5), "unfused_lowrank_overhead": rnd(ms_u / ms0 - 1.0, 4)}
@@ -310,7 +315,8 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(m["ms"], 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "int4" if fmt == svdq.INT4_G64 else "fp4-e2m1", "data": "synthetic",
         "config": {"workload": WORKLOADS[args.workload], "M": M, "K": K, "N": N, "rank": r,
-                   "format": "INT4 g64 fp16 scales" if fmt == svdq.INT4_G64 else "MXFP4 g32 E8M0 scales",
+                   "format": {svdq.INT4_G64: "INT4 g64 fp16 scales", svdq.MXFP4_G32: "MXFP4 g32 E8M0 scales",
+                              svdq.NVFP4_G16: "NVFP4-style g16 E4M3 + fp32 tensor scales"}[fmt],
                    "output": args.ydtype, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "achieved": round(k2_tops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(k2_tops / peak, 4), "traffic": traffic,
@@ -321,7 +327,7 @@ def main():
     }
     if not args.no_others:
         others = {}
-        for name in ("C2a", "C2b", "C3", "C4"):
+        for name in ("C2a", "C2b", "C3", "C4", "C1nv"):
             if name == args.workload:
                 continue
             o = measure(svdq, torch, name, ydt, 50, 20, 0.1, not args.no_compare, log_prefix=f" [{name}]")

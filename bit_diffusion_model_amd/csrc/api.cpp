@@ -25,7 +25,12 @@ static svdq_status check_layer(const svdq_layer* L, KernelLayer& kl) {
   if (!aligned(L->inv_s, 16) || !aligned(L->qW, 16) ||
       (L->rank > 0 && (!aligned(L->L1f, 16) || !aligned(L->L2f, 16))))
     return fail(SVDQ_EINVAL, "layer inv_s, qW, L1f and L2f must be 16-byte aligned");
-  kl = KernelLayer{L->K, L->N, L->rank, L->fmt, L->inv_s, L->L1f, L->L2f, L->qW, L->sW};
+  if (L->fmt == SVDQ_NVFP4_G16 && !(L->tscale_w > 0.f && L->tscale_x > 0.f && L->tscale_w < 3.0e38f &&
+                                    L->tscale_x < 3.0e38f))
+    return fail(SVDQ_EINVAL, "NVFP4 layer tensor scales must be positive and finite");
+  const bool nv = L->fmt == SVDQ_NVFP4_G16;
+  kl = KernelLayer{L->K, L->N, L->rank, L->fmt, L->inv_s, L->L1f, L->L2f, L->qW, L->sW, nv ? L->tscale_w : 1.f,
+                   nv ? L->tscale_x : 1.f};
   return SVDQ_OK;
 }
 
@@ -48,7 +53,7 @@ static WsLayout ws_layout(const svdq_layer* L, int64_t M) {
   const size_t Mp = ((size_t)M + 3) / 4 * 4;
   w.la = w.sx + rup((size_t)(L->K / group_of(L->fmt)) * Mp * (i4 ? 2 : 1));
   w.part = w.la + rup((size_t)((M + 31) & ~int64_t(31)) * (size_t)((L->rank + 15) / 16 * 16) * 4);
-  KernelLayer kl{L->K, L->N, L->rank, L->fmt, nullptr, nullptr, nullptr, nullptr, nullptr};
+  KernelLayer kl{L->K, L->N, L->rank, L->fmt, nullptr, nullptr, nullptr, nullptr, nullptr, 1.f, 1.f};
   w.total = w.part + rup(plan_k2(kl, M, true).bytes);
   return w;
 }
@@ -66,7 +71,7 @@ size_t svdq_workspace_bytes(const svdq_layer* layer, int64_t M) {
 
 size_t svdq_gemm_workspace_bytes(const svdq_layer* layer, int64_t M, int32_t form) {
   if (!layer || M < 1 || check_dims(layer->K, layer->N, layer->fmt) != SVDQ_OK) return 0;
-  KernelLayer kl{layer->K, layer->N, layer->rank, layer->fmt, nullptr, nullptr, nullptr, nullptr, nullptr};
+  KernelLayer kl{layer->K, layer->N, layer->rank, layer->fmt, nullptr, nullptr, nullptr, nullptr, nullptr, 1.f, 1.f};
   return plan_k2(kl, M, form == SVDQ_ACT_MMA).bytes;
 }
 
@@ -107,6 +112,8 @@ static svdq_status run_k2(const svdq_layer* layer, int64_t M, int32_t form, cons
   if (M < 0) return fail(SVDQ_EINVAL, "M must be >= 0");
   if (M == 0) return ok();
   if (ydtype != SVDQ_F32 && ydtype != SVDQ_BF16) return fail(SVDQ_EUNSUPPORTED, "unsupported output dtype %d", (int)ydtype);
+  if (kl.fmt == SVDQ_NVFP4_G16 && form != SVDQ_ACT_MMA)
+    return fail(SVDQ_EUNSUPPORTED, "NVFP4 kernel 2 runs on the MMA activation form only");
   if (!qX || !sX || !Y) return fail(SVDQ_EINVAL, "qX, sX and Y must be non-NULL");
   if (kl.rank > 0 && !lora_act) return fail(SVDQ_EINVAL, "lora_act must be non-NULL when rank > 0");
   if (ldy < kl.N) return fail(SVDQ_EINVAL, "ldy must be >= N");

@@ -71,6 +71,22 @@ __device__ __forceinline__ v6i nib32_to_fp6(uint4 d) {
   return __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(x0, x1, 0x1p-6f);
 }
 
+// Eight E2M1 codes (one dword, code 2j in the low nibble of byte j) times a group scale
+// s > 0 -> eight fp16 values, in code order, exact (at most 6 significant bits, binary
+// exponents -10 .. 11).  The scaled FP4 conversion applies only the exponent of its fp32
+// scale (2^floor(log2 s), measured), so the mantissa ratio s / 2^floor(log2 s) (1 to 1.875)
+// is applied after it with a packed fp16 multiply.  s = 0 gives zeros.
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ v8h nv_f16x8(uint32_t w, float s) {
+  const float r = __uint_as_float((__float_as_uint(s) & 0x007FFFFFu) | 0x3F800000u);
+  const h2 rr = {(_Float16)r, (_Float16)r};
+  const h2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s, 0) * rr;
+  const h2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s, 1) * rr;
+  const h2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s, 2) * rr;
+  const h2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s, 3) * rr;
+  return v8h{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+}
+
 // Raw buffer resource over `bytes` bytes at p: loads beyond the range return zeros.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);

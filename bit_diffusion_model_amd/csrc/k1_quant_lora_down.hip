@@ -42,19 +42,13 @@
 // even quarter and the odd fields of the odd quarter: field f of half h holds
 // k = 32 h + 16 (f & 1) + (f >> 1), the order kernel 2's weight operand uses.
 #include "common.hpp"
+#include "k1_parts.hpp"
 #include "kernels.hpp"
 
 namespace svdq {
 
 constexpr int K1_WAVES = 8;
 
-typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
-
-// fp32 pair -> bf16 pair bits, round to nearest even (element a in the low half)
-__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
-  const bf2 v = {(__bf16)a, (__bf16)b};
-  return __builtin_bit_cast(uint32_t, v);
-}
 
 // Rank tiles 0-2 fit in 128 VGPRs, so two 8-wave blocks share a CU.
 // QUANT = false: the down projection alone (lora_act only), the unfused baseline's
@@ -63,7 +57,8 @@ template <int FMT, int NT, bool MMA, bool QUANT = true>
 __global__ __launch_bounds__(64 * K1_WAVES) __attribute__((amdgpu_waves_per_eu(NT <= 2 ? 4 : 2))) void
 k1_quant_lora_down(const uint16_t* __restrict__ X, int64_t ldx, int64_t M, int64_t K,
                    const float* __restrict__ inv_s, const uint16_t* __restrict__ L1f, int rank,
-                   uint8_t* __restrict__ qX, void* __restrict__ sXv, float* __restrict__ lora_act) {
+                   uint8_t* __restrict__ qX, void* __restrict__ sXv, float* __restrict__ lora_act,
+                   float tsx, float r6x) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int r16 = lane & 15;
@@ -145,69 +140,24 @@ k1_quant_lora_down(const uint16_t* __restrict__ X, int64_t ldx, int64_t M, int64
 #undef K1_BC
     if constexpr (QUANT) {
     float a = 0.f;
+    if constexpr (FMT != 0) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(xh[i]));
-    a = wave_max_xor(a, 16);
+      for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(xh[i]));
+      // MXFP4: a 32-group spans lanes l, l ^ 16; NVFP4: the lane's 16 are one group
+      if constexpr (FMT == 1) a = wave_max_xor(a, 16);
+    }
 
     if constexpr (FMT == 0) {
       // INT4: s = fp16(fp32(a / 7)), saturating; q = round-half-even(x / s) exactly
-      a = wave_max_xor(a, 32);
-      const _Float16 sh = (_Float16)fminf(a / 7.0f, 65504.0f);
-      const float sf = (float)sh;
-      // s = 0 (all-zero group, or one whose fp16 scale underflows): every code 0
-      const float rcp = sf > 0.0f ? 1.0f / sf : 0.0f;
       float t[16];
-      float dev = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        t[i] = xh[i] * rcp;
-        dev = fmaxf(dev, fabsf(t[i] - rintf(t[i])));
-      }
-      if (__builtin_amdgcn_ballot_w64(dev > 0.49999237f) != 0) {  // 0.5 - 2^-17
-        // with s = 0 the codes stay 0: no |x - q s| exceeds an infinite half-scale
-        const float hs = sf > 0.0f ? 0.5f * sf : __builtin_inff();
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float q = rintf(t[i]);
-          const float e = fmaf(-q, sf, xh[i]);
-          const float ae = fabsf(e);
-          const int odd = ((int)q) & 1;
-          const int away = (int)(ae > hs) | ((int)(ae == hs) & odd);
-          t[i] = q + (float)away * copysignf(1.0f, e);
-        }
-      }
-      // MMA form: a group half's 192-bit operand (six words), built by the lane pair of
-      // quarters 2h, 2h+1 together (every lane takes part in the row swap, valid row or
-      // not).  The clamp to +-7 only acts for subnormal fp16 scales; code 0 may carry
-      // either sign bit.
-      uint32_t fw[3] = {0u, 0u, 0u};
-      if constexpr (MMA) {
-        v16f tc;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) tc[i] = __builtin_amdgcn_fmed3f(t[i], -7.0f, 7.0f);
-        const v6i f6 = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(tc, tc, 8.0f);
-        // bits of the even fields (field 2i at bit 12 i) in words d and d + 3
-        constexpr uint32_t EV[3] = {0x3F03F03Fu, 0xF03F03F0u, 0x03F03F03u};
-#pragma unroll
-        for (int d = 0; d < 3; ++d) {
-          // even rows (quarters 0, 2) receive the odd row's word d, odd rows the even
-          // row's word d + 3
-          const auto r = __builtin_amdgcn_permlane16_swap((uint32_t)f6[d], (uint32_t)f6[d + 3], false, false);
-          fw[d] = (r[0] & EV[d]) | (r[1] & ~EV[d]);
-        }
-      }
-      // the even quarter of each pair also takes word 3 (the odd quarter's first word), so
-      // a half is stored as [w0 w1 w2 w3 | w4 w5 0 0]: kernel 2 reads its six words as one
-      // 16-byte and one 8-byte load into an aligned run of registers
-      uint32_t w3 = 0u;
-      if constexpr (MMA) w3 = __builtin_amdgcn_permlane16_swap(fw[0], fw[0], false, false)[1];
+      const _Float16 sh = int4_quantize16(xh, t);
+      uint4 mw = make_uint4(0u, 0u, 0u, 0u);
+      if constexpr (MMA) mw = int4_mma_words(t, sub);  // every lane takes part in the swaps
       if (row_ok) {
         if constexpr (MMA) {
           // [M][K/64][64] bytes per token and group: quarter q stores 16 bytes at 16 q,
           // words 0-3 of half h (quarter 2h) or words 4-5 and two zero words (quarter 2h+1)
-          const bool odd = (sub & 1) != 0;
-          *reinterpret_cast<uint4*>(qX + row * K + k0) =
-              odd ? make_uint4(fw[1], fw[2], 0u, 0u) : make_uint4(fw[0], fw[1], fw[2], w3);
+          *reinterpret_cast<uint4*>(qX + row * K + k0) = mw;
         } else {
           uint32_t w0 = 0, w1 = 0;
 #pragma unroll
@@ -226,6 +176,40 @@ k1_quant_lora_down(const uint16_t* __restrict__ X, int64_t ldx, int64_t M, int64
           } else {
             reinterpret_cast<uint16_t*>(sXv)[(int64_t)c * M + row] = __builtin_bit_cast(uint16_t, sh);
           }
+        }
+      }
+    } else if constexpr (FMT == 2) {
+      // NVFP4: s = E4M3(fp32(a * r6)) (hardware conversion: round half to even; the
+      // input clamped to 448, the largest finite E4M3), sigma = fp32(s * S_X), codes =
+      // E2M1 of fp32(x * fp32(1 / sigma)) (hardware conversion, saturating at 6)
+      const float t = fminf(a * r6x, 448.0f);
+      const uint32_t sb = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(t, t, 0, false) & 0xFFu;
+      const float sigma = __builtin_amdgcn_cvt_f32_fp8((int)sb, 0) * tsx;
+      const float rcp = sigma > 0.0f ? 1.0f / sigma : 0.0f;
+      float y[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) y[i] = xh[i] * rcp;
+      uint32_t w0 = 0, w1 = 0;
+      w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, y[0], y[1], 1.0f, 0);
+      w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, y[2], y[3], 1.0f, 1);
+      w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, y[4], y[5], 1.0f, 2);
+      w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, y[6], y[7], 1.0f, 3);
+      w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, y[8], y[9], 1.0f, 0);
+      w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, y[10], y[11], 1.0f, 1);
+      w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, y[12], y[13], 1.0f, 2);
+      w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, y[14], y[15], 1.0f, 3);
+      if (row_ok) {
+        if constexpr (MMA) {
+          // token pairs; inside the 64-block, codes 16 sub + 0..7 at byte 4 sub and
+          // 16 sub + 8..15 at byte 16 + 4 sub (the bf16 matrix core's lane order)
+          uint8_t* blk = qX + (row >> 1) * K + (int64_t)(c >> 1) * 128 + (row & 1) * 64 + (c & 1) * 32;
+          *reinterpret_cast<uint32_t*>(blk + 4 * sub) = w0;
+          *reinterpret_cast<uint32_t*>(blk + 16 + 4 * sub) = w1;
+          const int64_t Mp = (M + 3) & ~int64_t(3);  // [K/64][Mp][4]
+          reinterpret_cast<uint8_t*>(sXv)[((int64_t)c * Mp + row) * 4 + sub] = (uint8_t)sb;
+        } else {
+          *reinterpret_cast<uint2*>(qX + row * (K >> 1) + (k0 >> 1)) = make_uint2(w0, w1);
+          reinterpret_cast<uint8_t*>(sXv)[(int64_t)(4 * c + sub) * M + row] = (uint8_t)sb;
         }
       }
     } else {
@@ -266,27 +250,7 @@ k1_quant_lora_down(const uint16_t* __restrict__ X, int64_t ldx, int64_t M, int64
     }
     }  // QUANT
 
-    if constexpr (NT > 0) {
-      // x = hi + lo as bf16 pairs, channels 0-7 of the lane in a*0, 8-15 in a*1
-      uint32_t hw[8], lw[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        hw[j] = pk_bf16(xh[2 * j], xh[2 * j + 1]);
-        lw[j] = pk_bf16(xh[2 * j] - bf16_lo_to_f32(hw[j]), xh[2 * j + 1] - bf16_hi_to_f32(hw[j]));
-      }
-      const v8bf a0h = __builtin_bit_cast(v8bf, make_uint4(hw[0], hw[1], hw[2], hw[3]));
-      const v8bf a1h = __builtin_bit_cast(v8bf, make_uint4(hw[4], hw[5], hw[6], hw[7]));
-      const v8bf a0l = __builtin_bit_cast(v8bf, make_uint4(lw[0], lw[1], lw[2], lw[3]));
-      const v8bf a1l = __builtin_bit_cast(v8bf, make_uint4(lw[4], lw[5], lw[6], lw[7]));
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const v8bf bA = __builtin_bit_cast(v8bf, LA[t]), bB = __builtin_bit_cast(v8bf, LB[t]);
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0h, bA, acc[t], 0, 0, 0);
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1h, bB, acc[t], 0, 0, 0);
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0l, bA, acc[t], 0, 0, 0);
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1l, bB, acc[t], 0, 0, 0);
-      }
-    }
+    lora_down16<NT>(acc, xh, LA, LB);
   }
 
   if constexpr (NT > 0) {
@@ -307,16 +271,7 @@ k1_quant_lora_down(const uint16_t* __restrict__ X, int64_t ldx, int64_t M, int64
 #pragma unroll
         for (int w = 0; w < K1_WAVES; ++w) v += red[w][rr][cc];
         if constexpr (MMA) {
-          // the bf16 pair kernel 2's up-projection MFMA consumes, v = hi + lo to ~2^-17
-          // relative, in its fragment order: 32-row blocks, k steps of 16, hi then lo
-          // (512 elements apart), the 64 lanes' 8 values (lane m % 32 + 32 (k / 8 % 2))
-          const uint32_t hb = f32_to_bf16_rne(v);
-          const uint32_t lb = f32_to_bf16_rne(v - __uint_as_float(hb << 16));
-          const int64_t m = m0 + rr;
-          uint16_t* la = reinterpret_cast<uint16_t*>(lora_act) +
-                         (((((m >> 5) * NT + (cc >> 4)) * 2) * 64 + (m & 31) + 32 * ((cc >> 3) & 1)) << 3) + (cc & 7);
-          la[0] = (uint16_t)hb;
-          la[512] = (uint16_t)lb;
+          store_lora_mma(reinterpret_cast<uint16_t*>(lora_act), m0 + rr, cc, NT, v);
         } else {
           lora_act[(m0 + rr) * R16 + cc] = v;
         }
@@ -330,10 +285,12 @@ static hipError_t launch_k1_fmt(const KernelLayer& L, int64_t M, const uint16_t*
                                 uint8_t* qX, void* sX, void* lora_act, hipStream_t st) {
   const dim3 grid((unsigned)((M + 15) / 16));
   const int nt = (L.rank + 15) / 16;
+  // NVFP4 level-2 scale of the activations and fp32(1 / fp32(6 S_X))
+  const float tsx = L.tscale_x, r6x = FMT == 2 ? 1.0f / (6.0f * L.tscale_x) : 0.0f;
 #define K1_CASE(NTV)                                                                            \
   case NTV:                                                                                     \
     hipLaunchKernelGGL((k1_quant_lora_down<FMT, NTV, MMA>), grid, dim3(64 * K1_WAVES), 0, st, X, ldx, M, L.K, \
-                       L.inv_s, L.L1f, L.rank, qX, sX, static_cast<float*>(lora_act));                    \
+                       L.inv_s, L.L1f, L.rank, qX, sX, static_cast<float*>(lora_act), tsx, r6x);          \
     break;
   switch (nt) {
     K1_CASE(0) K1_CASE(1) K1_CASE(2) K1_CASE(3) K1_CASE(4)
@@ -350,7 +307,7 @@ hipError_t launch_k1_down(const KernelLayer& L, int64_t M, const uint16_t* X, in
 #define K1D_CASE(NTV)                                                                                          \
   case NTV:                                                                                                    \
     hipLaunchKernelGGL((k1_quant_lora_down<0, NTV, true, false>), grid, dim3(64 * K1_WAVES), 0, st, X, ldx, M, L.K, L.inv_s, \
-                       L.L1f, L.rank, (uint8_t*)nullptr, (void*)nullptr, static_cast<float*>(lora_act));       \
+                       L.L1f, L.rank, (uint8_t*)nullptr, (void*)nullptr, static_cast<float*>(lora_act), 1.0f, 0.0f); \
     break;
   switch ((L.rank + 15) / 16) {
     K1D_CASE(1) K1D_CASE(2) K1D_CASE(3) K1D_CASE(4) K1D_CASE(5) K1D_CASE(6) K1D_CASE(7) K1D_CASE(8)
@@ -365,6 +322,9 @@ hipError_t launch_k1(const KernelLayer& L, int64_t M, const uint16_t* X, int64_t
   if (L.fmt == 0)
     return mma ? launch_k1_fmt<0, true>(L, M, X, ldx, qX, sX, lora_act, st)
                : launch_k1_fmt<0, false>(L, M, X, ldx, qX, sX, lora_act, st);
+  if (L.fmt == 2)
+    return mma ? launch_k1_fmt<2, true>(L, M, X, ldx, qX, sX, lora_act, st)
+               : launch_k1_fmt<2, false>(L, M, X, ldx, qX, sX, lora_act, st);
   return mma ? launch_k1_fmt<1, true>(L, M, X, ldx, qX, sX, lora_act, st)
              : launch_k1_fmt<1, false>(L, M, X, ldx, qX, sX, lora_act, st);
 }

@@ -43,6 +43,8 @@
 // FP6 the fields of a lane half pair field f of A with field f of B, so A and B only
 // need the same k order.  Output: lane l holds column l & 31, rows 8*(a>>2) + 4*(l>>5) +
 // (a&3) for accumulator a = 0..15.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -430,8 +432,11 @@ struct Shape {
 // wave tiles; measured against 256 x 256 tiles of 8 waves, which halve the panel bytes
 // per output but leave the QKV layer 2.53 rounds of tiles in 3 rounds of one block per
 // CU: 96 against 102 us).
+// NVFP4: 128 x 128, 4 waves of 64 x 64; its matrix-core work is fp16 (four 16-deep
+// MFMAs per 64 K, on operands dequantized in registers), which bounds it.
 template <int FMT> struct SShape;
 template <> struct SShape<0> : Shape<1, 4, 4, 1> {};
+template <> struct SShape<2> : Shape<2, 2, 2, 2> {};
 template <> struct SShape<1> : Shape<2, 2, 4, 2> {};
 
 // LDS layout of one stage of the streamed kernel
@@ -444,8 +449,10 @@ struct DLay {
   static constexpr int B_OFF = BM * RA;
   static constexpr int S_OFF = B_OFF + BN * RB;
   // scales of one sub-step: INT4 X [BM] fp16 | W [BN] fp16; MXFP4 X e [2][BM] | W e [2][BN]
-  // (the sub-step's two 32-groups); moved in 256-byte parts, one 4-byte load per lane
-  static constexpr int XB = 2 * BM, WB = 2 * BN;
+  // (the sub-step's two 32-groups); NVFP4 X [BM][4] | W [BN][4] E4M3 (four 16-groups);
+  // moved in 256-byte parts, one 4-byte load per lane
+  static constexpr int SPR = FMT == 2 ? 4 : 2;  // scale bytes per row and sub-step
+  static constexpr int XB = SPR * BM, WB = SPR * BN;
   static constexpr int S_SUB = XB + WB;
   static constexpr int XP = XB / 256, WP = WB / 256, SPARTS = 2 * (XP + WP);  // per stage
   static constexpr int NS = (SPARTS + NW - 1) / NW;  // scale loads per wave
@@ -498,8 +505,9 @@ __global__ __launch_bounds__(SShape<FMT>::NT, 8 / SShape<FMT>::NW) __attribute__
     const uint8_t* __restrict__ qX, const uint8_t* __restrict__ sX, int64_t M,
     const uint8_t* __restrict__ qW, const uint8_t* __restrict__ sW, int64_t N, int64_t K,
     const uint16_t* __restrict__ lora_act, const uint16_t* __restrict__ L2, int rank,
-    void* __restrict__ Y, int64_t ldy, int ydtype, K2Sched sch, K2Debug dbg) {
+    void* __restrict__ Y, int64_t ldy, int ydtype, K2Sched sch, K2Debug dbg, float sxw) {
   static_assert(!DEBUG || FMT == 0, "group sums are defined for INT4");
+  // NVFP4: sxw = fp32(S_X S_W), the product of the two tensor scales
   using D = DLay<FMT>;
   using SH = SShape<FMT>;
   constexpr int TI = SH::TI, TJ = SH::TJ, BM = SH::BM, BN = SH::BN, NW = SH::NW;
@@ -533,9 +541,9 @@ __global__ __launch_bounds__(SShape<FMT>::NT, 8 / SShape<FMT>::NW) __attribute__
   const int64_t rowsB = N - n0 < BN ? N - n0 : BN;
   // Row pairs: the weights (both formats) and the MXFP4 activations keep the 64-byte stage
   // segments of rows 2j, 2j+1 in one 128-byte line; the ranges cover a last odd row's pair
-  const __amdgpu_buffer_rsrc_t rA = make_rsrc(qX + m0 * Ka, (uint32_t)(FMT == 1 ? (rowsA + 1) & ~int64_t(1) : rowsA) * Ka);
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(qX + m0 * Ka, (uint32_t)(FMT != 0 ? (rowsA + 1) & ~int64_t(1) : rowsA) * Ka);
   const __amdgpu_buffer_rsrc_t rB = make_rsrc(qW + n0 * Kb, (uint32_t)((rowsB + 1) & ~int64_t(1)) * Kb);
-  const uint32_t ng = FMT == 0 ? (uint32_t)(K >> 6) : (uint32_t)(K >> 5);
+  const uint32_t ng = FMT == 0 ? (uint32_t)(K >> 6) : (FMT == 1 ? (uint32_t)(K >> 5) : (uint32_t)(K >> 4));
   const uint32_t Mp = (uint32_t)((M + 3) & ~int64_t(3)), Np = (uint32_t)((N + 3) & ~int64_t(3));
   // DEBUG: no scales (empty ranges: the scale loads return zeros and touch no memory)
   const __amdgpu_buffer_rsrc_t rSX = make_rsrc(sX, DEBUG ? 0u : ng * Mp * (FMT == 0 ? 2 : 1));
@@ -550,7 +558,7 @@ __global__ __launch_bounds__(SShape<FMT>::NT, 8 / SShape<FMT>::NW) __attribute__
     const int pos = (wave + NW * q) * 1024 + lane * 16;
     const int row = pos / D::RA, ps = (pos % D::RA) / 16;
     const uint32_t sl = (uint32_t)((ps ^ swz(row, D::RA / 16)) * 16);
-    voA[q] = FMT == 1 ? (uint32_t)(row >> 1) * 2 * Ka + (uint32_t)(row & 1) * D::RA + sl : (uint32_t)row * Ka + sl;
+    voA[q] = FMT != 0 ? (uint32_t)(row >> 1) * 2 * Ka + (uint32_t)(row & 1) * D::RA + sl : (uint32_t)row * Ka + sl;
   }
 #pragma unroll
   for (int q = 0; q < D::NBW; ++q) {
@@ -561,7 +569,7 @@ __global__ __launch_bounds__(SShape<FMT>::NT, 8 / SShape<FMT>::NW) __attribute__
   }
   auto issue = [&](int k, uint8_t* base) {
 #pragma unroll
-    for (int q = 0; q < D::NA; ++q) dma16(rA, base + (wave + NW * q) * 1024, voA[q], (uint32_t)k * (FMT == 1 ? 2 : 1) * D::RA);
+    for (int q = 0; q < D::NA; ++q) dma16(rA, base + (wave + NW * q) * 1024, voA[q], (uint32_t)k * (FMT != 0 ? 2 : 1) * D::RA);
 #pragma unroll
     for (int q = 0; q < D::NBW; ++q)
       dma16(rB, base + D::B_OFF + (wave + NW * q) * 1024, voB[q], (uint32_t)k * 2 * D::RB);
@@ -583,6 +591,8 @@ __global__ __launch_bounds__(SShape<FMT>::NT, 8 / SShape<FMT>::NW) __attribute__
       uint32_t off;
       if (FMT == 0) {  // fp16 values of rows yp * 128 + 2 lane, + 1
         off = (g * pitch + org) * 2 + (uint32_t)(yp * 256 + lane * 4);
+      } else if (FMT == 2) {  // [K/64][pitch][4]: the four E4M3 scales of row yp * 64 + lane
+        off = (g * pitch + org) * 4 + (uint32_t)(yp * 256 + lane * 4);
       } else {  // bytes [gi][row] of the [2][B] region: byte yp * 256 + 4 lane ..
         const int bpg = wside ? BN : BM;
         const int b0 = yp * 256 + lane * 4;
@@ -616,6 +626,8 @@ __global__ __launch_bounds__(SShape<FMT>::NT, 8 / SShape<FMT>::NW) __attribute__
       if constexpr (FMT == 0) {
         const uint32_t w = reinterpret_cast<const uint16_t*>(sb + D::XB)[col];
         f.sb[j] = kh ? 0u : w;
+      } else if constexpr (FMT == 2) {
+        f.sb[j] = reinterpret_cast<const uint32_t*>(sb + D::XB)[col];  // the column's four E4M3 scales
       } else {
         f.sb[j] = sb[D::XB + kh * BN + col];
       }
@@ -634,7 +646,8 @@ __global__ __launch_bounds__(SShape<FMT>::NT, 8 / SShape<FMT>::NW) __attribute__
       } else {
         const int ls = u * 2 + kh;
         f.a[i] = *reinterpret_cast<const uint4*>(base + row * D::RA + ((ls ^ swz(row, D::RA / 16)) * 16));
-        f.sa[i] = sb[kh * BM + row];
+        if constexpr (FMT == 2) f.sa[i] = reinterpret_cast<const uint32_t*>(sb)[row];
+        else f.sa[i] = sb[kh * BM + row];
       }
     }
   };
@@ -677,6 +690,38 @@ __global__ __launch_bounds__(SShape<FMT>::NT, 8 / SShape<FMT>::NW) __attribute__
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf, acc[i][j], 4, 4, 0, (int)f.sa[i], 0,
                                                                    (int)f.sb[j]);
       }
+  };
+
+  // ---- NVFP4: dequantize to fp16 in registers, fp16 MFMA --------------------------------
+  // K step s (16 deep) of the sub-step is group s: the lane's 16 bytes hold, per s, the
+  // four bytes of its eight codes k = 16 s + 8 kh .. +7 (the MMA-form lane order), and
+  // nv_f16x8 turns them into e2m1 * s_g in fp16, exact, so the MFMA accumulates exact
+  // products.
+  auto mma_nv_step = [&](const Frag& f, auto S) {
+    constexpr int s = decltype(S)::value;
+    v8h ab[TI], bb[TJ];
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      const float sc = __builtin_amdgcn_cvt_f32_fp8((int)f.sa[i], s);
+      const uint32_t w = s == 0 ? f.a[i].x : s == 1 ? f.a[i].y : s == 2 ? f.a[i].z : f.a[i].w;
+      ab[i] = nv_f16x8(w, sc);
+    }
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const float sc = __builtin_amdgcn_cvt_f32_fp8((int)f.sb[j], s);
+      const uint32_t w = s == 0 ? f.b[j].x : s == 1 ? f.b[j].y : s == 2 ? f.b[j].z : f.b[j].w;
+      bb[j] = nv_f16x8(w, sc);
+    }
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ab[i], bb[j], acc[i][j], 0, 0, 0);
+  };
+  auto mma_nv = [&](const Frag& f) {
+    mma_nv_step(f, std::integral_constant<int, 0>{});
+    mma_nv_step(f, std::integral_constant<int, 1>{});
+    mma_nv_step(f, std::integral_constant<int, 2>{});
+    mma_nv_step(f, std::integral_constant<int, 3>{});
   };
 
   // ---- main loop ------------------------------------------------------------------------
@@ -726,6 +771,8 @@ __global__ __launch_bounds__(SShape<FMT>::NT, 8 / SShape<FMT>::NW) __attribute__
           }
           epi(t / TJ, t % TJ, p[t & 1], c[t & 1]);
         }
+      } else if constexpr (FMT == 2) {
+        mma_nv(F);
       } else {
         mma4(F);
       }
@@ -744,6 +791,9 @@ __global__ __launch_bounds__(SShape<FMT>::NT, 8 / SShape<FMT>::NW) __attribute__
   // range covers whole 32-row blocks; rows past M hold whatever the workspace held
   // (their outputs are not stored), columns past N are zero.
   const bool lora = !DEBUG && rank > 0 && part <= 0;  // once per tile: whole, or the first part
+  // NVFP4 scales the 4-bit sum by S_X S_W after the main loop, so its low-rank term comes
+  // after that
+  const bool lora_pre = lora && FMT != 2;
   const int R16 = (rank + 15) & ~15;
   const __amdgpu_buffer_rsrc_t rL = make_rsrc(lora_act + m0 * 2 * R16, (uint32_t)(((rowsA + 31) & ~31) * R16 * 4));
   const __amdgpu_buffer_rsrc_t rU = make_rsrc(L2 + n0 * R16, (uint32_t)(((rowsB + 31) & ~31) * R16 * 2));
@@ -768,13 +818,13 @@ __global__ __launch_bounds__(SShape<FMT>::NT, 8 / SShape<FMT>::NW) __attribute__
       }
   };
   v8bf pb0[TJ], pa0[TI][2], pb1[TJ], pa1[TI][2];
-  if (lora) {
+  if (lora_pre) {
     lora_load(0, pb0, pa0);
     if (R16 > 16) lora_load(1, pb1, pa1);
   }
   issue(kbeg, lds0);
   issue(kbeg + 1 < kend ? kbeg + 1 : kend - 1, lds1);
-  if (lora) {
+  if (lora_pre) {
     lora_mma(pb0, pa0);
     if (R16 > 16) lora_mma(pb1, pa1);
     for (int s = 2; s < (R16 >> 4); ++s) {
@@ -793,6 +843,20 @@ __global__ __launch_bounds__(SShape<FMT>::NT, 8 / SShape<FMT>::NW) __attribute__
   if (nk % 3 == 2) stage(k + 1, lds1, lds0);
   wait_cnt<0, 0>();
   if constexpr (DEBUG) return;
+  if constexpr (FMT == 2) {
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+#pragma unroll
+        for (int a = 0; a < 16; ++a) acc[i][j][a] *= sxw;
+    if (lora)
+      for (int s = 0; s < (R16 >> 4); ++s) {
+        v8bf b[TJ], a[TI][2];
+        lora_load(s, b, a);
+        lora_mma(b, a);
+      }
+  }
 
   // ---- store (or the partial tile) ------------------------------------------------------
   if (part < 0) {
@@ -876,7 +940,7 @@ static int stream_blocks_per_cu() {
 }
 
 static int blocks_per_cu(int fmt, bool mma, int sub) {
-  if (mma) return fmt == 0 ? stream_blocks_per_cu<0>() : stream_blocks_per_cu<1>();
+  if (mma) return fmt == 0 ? stream_blocks_per_cu<0>() : (fmt == 2 ? stream_blocks_per_cu<2>() : stream_blocks_per_cu<1>());
   if (fmt == 0) return sub == 2 ? blocks_per_cu<0, 2>() : blocks_per_cu<0, 1>();
   return sub == 2 ? blocks_per_cu<1, 2>() : blocks_per_cu<1, 1>();
 }
@@ -885,6 +949,7 @@ static int blocks_per_cu(int fmt, bool mma, int sub) {
 // tile size in floats.
 static void tile_of(int fmt, bool mma, int& tbm, int& tbn, size_t& part) {
   if (mma && fmt == 0) { tbm = SShape<0>::BM; tbn = SShape<0>::BN; part = SShape<0>::PART; }
+  else if (mma && fmt == 2) { tbm = SShape<2>::BM; tbn = SShape<2>::BN; part = SShape<2>::PART; }
   else if (mma) { tbm = SShape<1>::BM; tbn = SShape<1>::BN; part = SShape<1>::PART; }
   else { tbm = BM; tbn = BN; part = PART_FLOATS; }
 }
@@ -936,10 +1001,11 @@ hipError_t launch_k2(const KernelLayer& L, int64_t M, const uint8_t* qX, const v
 #define K2_STREAM(F)                                                                                        \
   hipLaunchKernelGGL((k2_stream<F>), dim3(nblocks), dim3(SShape<F>::NT), 0, st, qX, static_cast<const uint8_t*>(sX), M, \
                      L.qW, static_cast<const uint8_t*>(L.sW), L.N, L.K, static_cast<const uint16_t*>(lora_act),   \
-                     L.L2f, L.rank, Y, ldy, ydtype, sch, K2Debug{})
+                     L.L2f, L.rank, Y, ldy, ydtype, sch, K2Debug{}, L.tscale_x * L.tscale_w)
   const int sub = sub_of(L.K);
   if (mma) {  // the activation side in MMA form: streamed kernel (K % 128 == 0: two sub-steps per stage)
     if (L.fmt == 0) K2_STREAM(0);
+    else if (L.fmt == 2) K2_STREAM(2);
     else K2_STREAM(1);
   } else if (L.fmt == 0) {
     if (sub == 2) K2_LAUNCH(0, 2);
@@ -954,6 +1020,9 @@ hipError_t launch_k2(const KernelLayer& L, int64_t M, const uint8_t* qX, const v
     const float* part = static_cast<const float*>(workspace);
     if (mma && L.fmt == 0)
       hipLaunchKernelGGL((k2_fixup<SShape<0>::BM, SShape<0>::BN>), dim3(rem * (SShape<0>::PART / 1024)), dim3(64), 0,
+                         st, part, sch, M, L.N, Y, ldy, ydtype);
+    else if (mma && L.fmt == 2)
+      hipLaunchKernelGGL((k2_fixup<SShape<2>::BM, SShape<2>::BN>), dim3(rem * (SShape<2>::PART / 1024)), dim3(64), 0,
                          st, part, sch, M, L.N, Y, ldy, ydtype);
     else if (mma)
       hipLaunchKernelGGL((k2_fixup<SShape<1>::BM, SShape<1>::BN>), dim3(rem * (SShape<1>::PART / 1024)), dim3(64), 0,
@@ -975,7 +1044,7 @@ hipError_t launch_k2_debug(const KernelLayer& L, int64_t M, const uint8_t* qX, b
     const K2Sched sch{p.tiles_n, p.full, p.split, nullptr};
     hipLaunchKernelGGL((k2_stream<0, true>), dim3(p.full + rem * p.split), dim3(SShape<0>::NT), 0, st, qX,
                        (const uint8_t*)nullptr, M, L.qW, (const uint8_t*)nullptr, L.N, L.K, (const uint16_t*)nullptr,
-                       (const uint16_t*)nullptr, 0, (void*)nullptr, (int64_t)0, 0, sch, K2Debug{out, m0, n0, mt, nt});
+                       (const uint16_t*)nullptr, 0, (void*)nullptr, (int64_t)0, 0, sch, K2Debug{out, m0, n0, mt, nt}, 1.0f);
     return hipGetLastError();
   }
   const uint32_t tn = (uint32_t)((nt + BN - 1) / BN), tm = (uint32_t)((mt + BM - 1) / BM);

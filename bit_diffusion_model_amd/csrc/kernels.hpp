@@ -8,12 +8,13 @@ namespace svdq {
 struct KernelLayer {
   int64_t K, N;
   int rank;
-  int fmt;  // 0 INT4 g64, 1 MXFP4 g32
+  int fmt;  // 0 INT4 g64, 1 MXFP4 g32, 2 NVFP4 g16
   const float* inv_s;
   const uint16_t* L1f;  // kernel 1's fragment order (svdq_prepare_lowrank_down)
   const uint16_t* L2f;  // kernel 2's fragment order (svdq_prepare_lowrank)
   const uint8_t* qW;
   const void* sW;
+  float tscale_w, tscale_x;  // NVFP4 tensor scales (1 otherwise)
 };
 
 // mma: the activation side in the matrix-core operand form (INT4 FP6 operand words,

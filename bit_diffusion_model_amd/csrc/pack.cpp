@@ -174,10 +174,76 @@ void quant_fp4_group(const float* v, int G, uint8_t* nib, uint8_t* e8) {
   *e8 = (uint8_t)(e + 127);
 }
 
-// Quantize R [K][N] (fp32, row-major) per column along K; write qW [N][K/2], sW [K/G][N].
-void quantize_residual(int64_t K, int64_t N, const float* R, int fmt, uint8_t* qW, void* sW) {
+// Non-negative x -> the nearest FP8 E4M3 value (bias 7, 3 mantissa bits, subnormals
+// m 2^-9), ties to the even mantissa, saturating at 448; returns the code byte.
+uint8_t e4m3_rne_sat(double x) {
+  if (!(x > 0.0)) return 0;
+  int e;
+  std::frexp(x, &e);  // x = f 2^e, f in [0.5, 1): binary exponent e - 1
+  const int be = std::max(e - 1, -6);
+  double r = std::nearbyint(std::ldexp(x, 3 - be));  // quanta of 2^(be - 3)
+  double v = std::ldexp(r, be - 3);
+  if (v >= 448.0) return 0x7E;
+  if (v < 0x1p-6) return (uint8_t)std::lrint(std::ldexp(v, 9));  // subnormal (or 0)
+  int re;
+  std::frexp(v, &re);
+  const int ex = re - 1;
+  const int mant = (int)std::lrint((std::ldexp(v, -ex) - 1.0) * 8.0);
+  return (uint8_t)(((ex + 7) << 3) | mant);
+}
+
+double e4m3_to_double(uint8_t b) {
+  const int E = (b >> 3) & 15, m = b & 7;
+  return E == 0 ? std::ldexp((double)m, -9) : std::ldexp(1.0 + m / 8.0, E - 7);
+}
+
+// E2M1 magnitude index of u >= 0: round half to even on {0, .5, 1, 1.5, 2, 3, 4, 6},
+// saturating at 6.
+int e2m1_index(double u) {
+  if (u <= 0.25) return 0;
+  if (u < 0.75) return 1;
+  if (u <= 1.25) return 2;
+  if (u < 1.75) return 3;
+  if (u <= 2.5) return 4;
+  if (u < 3.5) return 5;
+  if (u <= 5.0) return 6;
+  return 7;
+}
+
+// NVFP4 level-2 scale fp32(amax / 2688) (1 for amax = 0).
+float nv_tensor_scale(float amax) { return amax == 0.f ? 1.f : amax / 2688.0f; }
+
+// NVFP4 group of 16 under the tensor scale S (r6 = fp32(1 / fp32(6 S))): s =
+// E4M3(fp32(a r6)), sigma = fp32(s S), code = E2M1 of fp32(v * fp32(1 / sigma)).
+void quant_nv_group(const float* v, float S, float r6, uint8_t* nib, uint8_t* e4) {
+  float a = 0.f;
+  for (int i = 0; i < 16; ++i) a = std::max(a, std::fabs(v[i]));
+  const float t = a * r6;
+  const uint8_t sb = e4m3_rne_sat((double)t);
+  const float sigma = (float)e4m3_to_double(sb) * S;
+  const float rcp = sigma > 0.f ? 1.0f / sigma : 0.f;
+  for (int i = 0; i < 16; ++i) {
+    const float q = v[i] * rcp;
+    nib[i] = (uint8_t)((std::signbit(v[i]) ? 8 : 0) | e2m1_index(std::fabs((double)q)));
+  }
+  *e4 = sb;
+}
+
+// Quantize R [K][N] (fp32, row-major) per column along K; write qW [N][K/2], sW [K/G][N]
+// (NVFP4: then the fp32 tensor scale of R and the activations' S_X).
+void quantize_residual(int64_t K, int64_t N, const float* R, int fmt, uint8_t* qW, void* sW, float S_X = 1.f) {
   const int G = group_of(fmt);
   const int64_t ng = K / G;
+  float S = 1.f, r6 = 0.f;
+  if (fmt == SVDQ_NVFP4_G16) {
+    float amax = 0.f;
+    for (int64_t i = 0; i < K * N; ++i) amax = std::max(amax, std::fabs(R[i]));
+    S = nv_tensor_scale(amax);
+    r6 = 1.0f / (6.0f * S);
+    uint8_t* tail = static_cast<uint8_t*>(sW) + ng * N;
+    std::memcpy(tail, &S, 4);
+    std::memcpy(tail + 4, &S_X, 4);
+  }
   parallel_for((N + 63) / 64, [&](int64_t blk) {
     std::vector<float> col(K);
     std::vector<uint8_t> nib(K);
@@ -188,6 +254,10 @@ void quantize_residual(int64_t K, int64_t N, const float* R, int fmt, uint8_t* q
           uint16_t sb;
           quant_int4_group(&col[g * G], G, &nib[g * G], &sb);
           static_cast<uint16_t*>(sW)[g * N + n] = sb;
+        } else if (fmt == SVDQ_NVFP4_G16) {
+          uint8_t e4;
+          quant_nv_group(&col[g * G], S, r6, &nib[g * G], &e4);
+          static_cast<uint8_t*>(sW)[g * N + n] = e4;
         } else {
           uint8_t e8;
           quant_fp4_group(&col[g * G], G, &nib[g * G], &e8);
@@ -484,7 +554,8 @@ svdq_status svdq_weight_sizes(int64_t K, int64_t N, int32_t fmt, size_t* qW_byte
   if (st != SVDQ_OK) return st;
   if (!qW_bytes || !sW_bytes) return fail(SVDQ_EINVAL, "output pointers must be non-NULL");
   *qW_bytes = (size_t)N * (size_t)(K / 2);
-  *sW_bytes = (size_t)(K / group_of(fmt)) * (size_t)N * (fmt == SVDQ_INT4_G64 ? 2 : 1);
+  *sW_bytes = (size_t)(K / group_of(fmt)) * (size_t)N * (fmt == SVDQ_INT4_G64 ? 2 : 1) +
+              (fmt == SVDQ_NVFP4_G16 ? 8 : 0);
   return ok();
 }
 
@@ -565,6 +636,8 @@ void split_rank(const double* T, int64_t K, int64_t N, int32_t rank, std::vector
 void dequantize_residual(int64_t K, int64_t N, int fmt, const uint8_t* qW, const void* sW, double* D) {
   static const double kE2M1[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
   const int G = group_of(fmt);
+  float S = 1.f;
+  if (fmt == SVDQ_NVFP4_G16) std::memcpy(&S, static_cast<const uint8_t*>(sW) + (K / G) * N, 4);
   parallel_for(N, [&](int64_t n) {
     for (int64_t k = 0; k < K; ++k) {
       const uint8_t byte = qW[n * (K / 2) + k / 2];
@@ -572,6 +645,8 @@ void dequantize_residual(int64_t K, int64_t N, int fmt, const uint8_t* qW, const
       const int64_t g = k / G;
       double v;
       if (fmt == SVDQ_INT4_G64) v = (double)(nib & 7) * f16_to_double(static_cast<const uint16_t*>(sW)[g * N + n]);
+      else if (fmt == SVDQ_NVFP4_G16)
+        v = kE2M1[nib & 7] * e4m3_to_double(static_cast<const uint8_t*>(sW)[g * N + n]) * (double)S;
       else v = std::ldexp(kE2M1[nib & 7], (int)static_cast<const uint8_t*>(sW)[g * N + n] - 127);
       D[k * N + n] = (nib & 8) ? -v : v;
     }
@@ -618,7 +693,15 @@ svdq_status pack_impl(int64_t K, int64_t N, const uint16_t* W, const float* act_
   });
 
   const int G = group_of(fmt);
-  const size_t nq = (size_t)N * (K / 2), ns = (size_t)(K / G) * N * (fmt == SVDQ_INT4_G64 ? 2 : 1);
+  const size_t nq = (size_t)N * (K / 2),
+               ns = (size_t)(K / G) * N * (fmt == SVDQ_INT4_G64 ? 2 : 1) + (fmt == SVDQ_NVFP4_G16 ? 8 : 0);
+  // NVFP4: the activations' tensor scale from the smoothed calibration statistic
+  float S_X = 1.f;
+  if (fmt == SVDQ_NVFP4_G16 && act_absmax) {
+    float amax = 0.f;
+    for (int64_t k = 0; k < K; ++k) amax = std::max(amax, act_absmax[k] * inv_s_out[k]);
+    S_X = nv_tensor_scale(amax);
+  }
   std::vector<double> L1((size_t)K * std::max(rank, 1)), L2((size_t)std::max(rank, 1) * N);
   std::vector<uint16_t> b1((size_t)std::max(rank, 1) * K), b2((size_t)std::max(rank, 1) * N);
   std::vector<double> Rd((size_t)K * N), D, T;
@@ -642,7 +725,7 @@ svdq_status pack_impl(int64_t K, int64_t N, const uint16_t* W, const float* act_
       }
     });
     for (size_t i = 0; i < R32.size(); ++i) R32[i] = (float)Rd[i];
-    quantize_residual(K, N, R32.data(), fmt, q.data(), sc.data());
+    quantize_residual(K, N, R32.data(), fmt, q.data(), sc.data(), S_X);
     double err = 0.0;
     if (iters > 0 || err_out) {
       if (D.empty()) D.resize((size_t)K * N);
@@ -758,6 +841,34 @@ svdq_status svdq_prepare_weights(int64_t K, int64_t N, int32_t fmt, const uint8_
   if (!qW || !sW || !qW_out || !sW_out) return fail(SVDQ_EINVAL, "required pointer is NULL");
   const int64_t groups = K / group_of(fmt);
   const int64_t Np = (N + 3) / 4 * 4;  // scale rows padded to 4 bytes (fp16 rows: 8)
+  if (fmt == SVDQ_NVFP4_G16) {
+    // codes: column pairs as for MXFP4; inside each 64-block code k moves to nibble
+    // 2 (16 ((k / 8) % 2) + 4 (k / 16)) + k % 8, the lane order of the bf16 matrix core
+    const int64_t N2 = N + (N & 1);
+    std::memset(qW_out, 0, (size_t)(N2 * (K / 2)));
+    for (int64_t n = 0; n < N; ++n)
+      for (int64_t k0 = 0; k0 < K; k0 += 64) {
+        uint8_t blk[32] = {};
+        for (int k = 0; k < 64; ++k) {
+          const uint8_t byte = qW[n * (K / 2) + (k0 + k) / 2];
+          const uint8_t nib = (k & 1) ? byte >> 4 : byte & 15;
+          const int p = 2 * (16 * ((k >> 3) & 1) + 4 * (k >> 4)) + (k & 7);
+          blk[p >> 1] |= (uint8_t)(nib << (4 * (p & 1)));
+        }
+        const int64_t b = k0 / 2;
+        std::memcpy(qW_out + (n / 2) * K + (b / 64) * 128 + (n % 2) * 64 + b % 64, blk, 32);
+      }
+    // scales: [K/64][Np][4], the four groups of a 64-block contiguous per column
+    const uint8_t* s8 = static_cast<const uint8_t*>(sW);
+    uint8_t* o8 = static_cast<uint8_t*>(sW_out);
+    for (int64_t g = 0; g < groups; ++g)
+      for (int64_t n = 0; n < Np; ++n) {
+        const uint8_t e = n < N ? s8[g * N + n] : (uint8_t)0;
+        if (e >= 0x7F) return fail(SVDQ_ENUMERIC, "E4M3 weight scale out of range");
+        o8[((g / 4) * Np + n) * 4 + g % 4] = e;
+      }
+    return ok();
+  }
   if (fmt == SVDQ_MXFP4_G32) {
     // codes as stored, columns in pairs (see the INT4 placement below)
     const int64_t N2 = N + (N & 1);

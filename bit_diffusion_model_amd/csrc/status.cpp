@@ -26,10 +26,10 @@ svdq_status ok() {
   return SVDQ_OK;
 }
 
-int group_of(int fmt) { return fmt == SVDQ_INT4_G64 ? 64 : 32; }
+int group_of(int fmt) { return fmt == SVDQ_INT4_G64 ? 64 : (fmt == SVDQ_NVFP4_G16 ? 16 : 32); }
 
 svdq_status check_dims(int64_t K, int64_t N, int32_t fmt) {
-  if (fmt != SVDQ_INT4_G64 && fmt != SVDQ_MXFP4_G32)
+  if (fmt != SVDQ_INT4_G64 && fmt != SVDQ_MXFP4_G32 && fmt != SVDQ_NVFP4_G16)
     return fail(SVDQ_EUNSUPPORTED, "unsupported format %d", (int)fmt);
   if (K < 128 || K % 128 != 0) return fail(SVDQ_EINVAL, "K must be a positive multiple of 128 (got %lld)", (long long)K);
   if (N < 1) return fail(SVDQ_EINVAL, "N must be >= 1 (got %lld)", (long long)N);

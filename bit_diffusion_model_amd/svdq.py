@@ -17,11 +17,11 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsvdq.so")
 
-INT4_G64, MXFP4_G32 = 0, 1
+INT4_G64, MXFP4_G32, NVFP4_G16 = 0, 1, 2
 ACT_PACKED, ACT_MMA = 0, 1  # svdq_act_form
 F32, BF16 = 0, 1
-FMT = {"int4": INT4_G64, "mxfp4": MXFP4_G32}
-GROUP = {INT4_G64: 64, MXFP4_G32: 32}
+FMT = {"int4": INT4_G64, "mxfp4": MXFP4_G32, "nvfp4": NVFP4_G16}
+GROUP = {INT4_G64: 64, MXFP4_G32: 32, NVFP4_G16: 16}
 MAX_RANK = 128
 
 
@@ -33,6 +33,7 @@ class _Layer(ctypes.Structure):
     _fields_ = [
         ("K", ctypes.c_int64), ("N", ctypes.c_int64), ("rank", ctypes.c_int32), ("fmt", ctypes.c_int32),
         ("inv_s", ctypes.c_void_p), ("L1f", ctypes.c_void_p), ("L2f", ctypes.c_void_p), ("qW", ctypes.c_void_p), ("sW", ctypes.c_void_p),
+        ("tscale_w", ctypes.c_float), ("tscale_x", ctypes.c_float),
     ]
 
 
@@ -122,9 +123,11 @@ class HostPack:
     L1t: np.ndarray     # bf16 bits [rank][K]
     L2: np.ndarray      # bf16 bits [rank][N]
     qW: np.ndarray      # u8 [N][K/2]
-    sW: np.ndarray      # fp16 bits u16 or E8M0 u8 [K/G][N]
+    sW: np.ndarray      # fp16 bits u16, E8M0 u8 or E4M3 u8 [K/G][N]
     R: Optional[np.ndarray] = None
     errors: Optional[np.ndarray] = None  # refined packs: each iterate's split error E
+    tscale_w: float = 1.0  # NVFP4: the weights' and activations' fp32 tensor scales
+    tscale_x: float = 1.0
 
 
 def pack_weights(W_bits: np.ndarray, act_absmax_: Optional[np.ndarray], alpha: float, rank: int,
@@ -138,29 +141,48 @@ def pack_weights(W_bits: np.ndarray, act_absmax_: Optional[np.ndarray], alpha: f
     L1t = np.zeros((rank, K), np.uint16)
     L2 = np.zeros((rank, N), np.uint16)
     qW = np.empty((N, K // 2), np.uint8)
-    G = GROUP.get(fmt, 64)
-    sW = np.empty((K // G, N), np.uint16 if fmt == INT4_G64 else np.uint8)
+    sbuf, sW = _scale_buffer(K, N, fmt)
     R = np.empty((K, N), np.float32) if want_R else None
     a = None if act_absmax_ is None else np.ascontiguousarray(act_absmax_, dtype=np.float32)
+    errs = None
     if refine_iters > 0:
         errs = np.empty(refine_iters + 1, np.float64)
         _check(lib().svdq_pack_weights_refined(K, N, _ptr(W), _ptr(a), float(alpha), rank, fmt, int(refine_iters),
-                                               _ptr(s), _ptr(inv), _ptr(L1t), _ptr(L2), _ptr(qW), _ptr(sW), _ptr(R),
+                                               _ptr(s), _ptr(inv), _ptr(L1t), _ptr(L2), _ptr(qW), _ptr(sbuf), _ptr(R),
                                                _ptr(errs)))
-        return HostPack(K, N, rank, fmt, s, inv, L1t, L2, qW, sW, R, errs)
-    _check(lib().svdq_pack_weights(K, N, _ptr(W), _ptr(a), float(alpha), rank, fmt, _ptr(s), _ptr(inv),
-                                   _ptr(L1t), _ptr(L2), _ptr(qW), _ptr(sW), _ptr(R)))
-    return HostPack(K, N, rank, fmt, s, inv, L1t, L2, qW, sW, R)
+    else:
+        _check(lib().svdq_pack_weights(K, N, _ptr(W), _ptr(a), float(alpha), rank, fmt, _ptr(s), _ptr(inv),
+                                       _ptr(L1t), _ptr(L2), _ptr(qW), _ptr(sbuf), _ptr(R)))
+    tw, tx = _tscales(sbuf, K, N, fmt)
+    return HostPack(K, N, rank, fmt, s, inv, L1t, L2, qW, sW, R, errs, tw, tx)
 
 
-def quantize_weights(R: np.ndarray, fmt: int):
+def _scale_buffer(K: int, N: int, fmt: int):
+    """The pack's scale buffer (NVFP4: group scales, then the two fp32 tensor scales) and
+    its [K/G][N] view of the group scales."""
+    G = GROUP.get(fmt, 64)
+    if fmt == INT4_G64:
+        b = np.empty((K // G, N), np.uint16)
+        return b, b
+    b = np.empty((K // G) * N + (8 if fmt == NVFP4_G16 else 0), np.uint8)
+    return b, b[:(K // G) * N].reshape(K // G, N)
+
+
+def _tscales(sbuf, K: int, N: int, fmt: int):
+    if fmt != NVFP4_G16:
+        return 1.0, 1.0
+    t = sbuf[(K // 16) * N:].view(np.float32)
+    return float(t[0]), float(t[1])
+
+
+def quantize_weights(R: np.ndarray, fmt: int, with_tscale: bool = False):
+    """svdq_quantize_weights: (qW, sW) (and the NVFP4 weight tensor scale if asked)."""
     R = np.ascontiguousarray(R, dtype=np.float32)
     K, N = R.shape
     qW = np.empty((N, K // 2), np.uint8)
-    G = GROUP.get(fmt, 64)
-    sW = np.empty((K // G, N), np.uint16 if fmt == INT4_G64 else np.uint8)
-    _check(lib().svdq_quantize_weights(K, N, _ptr(R), fmt, _ptr(qW), _ptr(sW)))
-    return qW, sW
+    sbuf, sW = _scale_buffer(K, N, fmt)
+    _check(lib().svdq_quantize_weights(K, N, _ptr(R), fmt, _ptr(qW), _ptr(sbuf)))
+    return (qW, sW, _tscales(sbuf, K, N, fmt)[0]) if with_tscale else (qW, sW)
 
 
 def concat_lora(p: HostPack, A_bits: np.ndarray, B_bits: np.ndarray, scale: float = 1.0) -> HostPack:
@@ -173,7 +195,7 @@ def concat_lora(p: HostPack, A_bits: np.ndarray, B_bits: np.ndarray, scale: floa
     _check(lib().svdq_concat_lora(p.K, p.N, _ptr(p.s), p.rank, _ptr(np.ascontiguousarray(p.L1t)),
                                   _ptr(np.ascontiguousarray(p.L2)), lr, _ptr(A), _ptr(B), float(scale),
                                   _ptr(L1t), _ptr(L2)))
-    return HostPack(p.K, p.N, r, p.fmt, p.s, p.inv_s, L1t, L2, p.qW, p.sW, p.R)
+    return HostPack(p.K, p.N, r, p.fmt, p.s, p.inv_s, L1t, L2, p.qW, p.sW, p.R, None, p.tscale_w, p.tscale_x)
 
 
 def r16(rank: int) -> int:
@@ -206,8 +228,8 @@ def pad4(n: int) -> int:
 
 def prepare_weights(K: int, N: int, fmt: int, qW: np.ndarray, sW: np.ndarray):
     """Kernel layout of the residual weights: (qW bytes: (N rounded up to 2) * K/2 in
-    column pairs; sW bytes: INT4 fp16 [K/64][Np]; MXFP4 E8M0 [K/32][Np];
-    Np = N rounded up to 4)."""
+    column pairs; sW bytes: INT4 fp16 [K/64][Np]; MXFP4 E8M0 [K/32][Np]; NVFP4 E4M3
+    [K/64][Np][4]; Np = N rounded up to 4)."""
     qW = np.ascontiguousarray(qW, dtype=np.uint8)
     sW = np.ascontiguousarray(sW)
     qo = np.empty(((N + 1) // 2 * 2 * (K // 2),), np.uint8)
@@ -254,8 +276,10 @@ class PackedLinear:
     """A packed layer resident on the GPU, callable through the library's kernels."""
 
     def __init__(self, K: int, N: int, rank: int, fmt: int, inv_s: np.ndarray, L1t: np.ndarray,
-                 L2: np.ndarray, qW: np.ndarray, sW: np.ndarray, device="cuda:0"):
+                 L2: np.ndarray, qW: np.ndarray, sW: np.ndarray, device="cuda:0", tscale_w: float = 1.0,
+                 tscale_x: float = 1.0):
         self.K, self.N, self.rank, self.fmt = int(K), int(N), int(rank), int(fmt)
+        self.tscale_w, self.tscale_x = float(tscale_w), float(tscale_x)
         self.device = device
         self.inv_s = _upload(np.asarray(inv_s, np.float32), device)
         if rank > 0:
@@ -267,11 +291,11 @@ class PackedLinear:
         self.qW = _upload(qk, device)
         self.sW = _upload(sk, device)
         self._c = _Layer(self.K, self.N, self.rank, self.fmt, _dptr(self.inv_s), _dptr(self.L1f),
-                         _dptr(self.L2f), _dptr(self.qW), _dptr(self.sW))
+                         _dptr(self.L2f), _dptr(self.qW), _dptr(self.sW), self.tscale_w, self.tscale_x)
 
     @classmethod
     def from_host_pack(cls, p: HostPack, device="cuda:0"):
-        return cls(p.K, p.N, p.rank, p.fmt, p.inv_s, p.L1t, p.L2, p.qW, p.sW, device)
+        return cls(p.K, p.N, p.rank, p.fmt, p.inv_s, p.L1t, p.L2, p.qW, p.sW, device, p.tscale_w, p.tscale_x)
 
     @property
     def group(self) -> int:
@@ -291,7 +315,7 @@ class PackedLinear:
             qX = buf[:M * (self.K // 2)].view(M, self.K // 2)
         else:
             qX = torch.empty((M, self.K if mma6 else self.K // 2), dtype=torch.uint8, device=self.device)
-        if form == ACT_MMA:  # scales with rows padded to 4: INT4 fp16, MXFP4 E8M0 bytes
+        if form == ACT_MMA:  # scales with rows padded to 4: INT4 fp16, MXFP4 E8M0, NVFP4 E4M3 bytes
             sX = torch.empty((self.K // self.group) * pad4(M) * (2 if mma6 else 1), dtype=torch.uint8,
                              device=self.device)
         else:

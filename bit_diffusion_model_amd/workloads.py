@@ -73,7 +73,8 @@ class Workload:
     K: int
     N: int
     rank: int
-    fmt: str  # "int4" (INT4, group 64, fp16 scales) or "mxfp4" (E2M1, group 32, E8M0 scales)
+    fmt: str  # "int4" (INT4, group 64, fp16 scales), "mxfp4" (E2M1, group 32, E8M0 scales) or
+    #            "nvfp4" (E2M1, group 16, E4M3 scales under an fp32 tensor scale)
     alpha: float
     X: np.ndarray
     W: np.ndarray
@@ -85,7 +86,7 @@ class Workload:
 
     @property
     def group(self) -> int:
-        return 64 if self.fmt == "int4" else 32
+        return {"int4": 64, "mxfp4": 32, "nvfp4": 16}[self.fmt]
 
     @property
     def total_rank(self) -> int:
@@ -96,7 +97,7 @@ class Workload:
         return 2 * self.M * self.N * self.K
 
 
-CONFIG_NAMES = ["C0", "C1", "C2a", "C2b", "C3", "C4"]
+CONFIG_NAMES = ["C0", "C1", "C2a", "C2b", "C3", "C4", "C1nv"]
 
 
 def _streams(seed: int):
@@ -196,6 +197,8 @@ def make(name: str) -> Workload:
         return _c1(fmt="mxfp4", name="C3")
     if name == "C4":
         return _c4()
+    if name == "C1nv":  # the QKV layer in the group-16 two-level-scale format
+        return _c1(fmt="nvfp4", name="C1nv")
     raise KeyError(name)
 
 

@@ -31,6 +31,15 @@
  *    {0, 0.5, 1, 1.5, 2, 3, 4, 6}) with one E8M0 byte (2^(byte - 127)) per 32 values,
  *    the exponent being the smallest e with 6 * 2^e >= max|v|; round half to even on
  *    the E2M1 grid, sign bit kept.
+ *  - SVDQ_NVFP4_G16: the group-16, two-level-scale variant the ch3chohch3.github.io
+ *    post discusses in its section "个人见解": E2M1 codes as above, one FP8 E4M3 scale
+ *    per 16 values (bias 7, subnormals to 2^-9, largest finite 448) and one fp32 scale
+ *    S per tensor, S = fp32(max|v| / 2688) (1 for an all-zero tensor).  Per group:
+ *    s = E4M3(fp32(max|v| * fp32(1 / fp32(6 S)))) rounded half to even and saturating
+ *    at 448; codes = E2M1 of fp32(v * fp32(1 / fp32(s S))), half to even, saturating at
+ *    6, sign kept; a zero s gives sign-kept zero codes.  Value = S * s * e2m1(code).
+ *    The weights' S comes from the residual, the activations' from the smoothed
+ *    calibration statistic (fixed offline, like the smoothing factor).
  *  Two codes per byte: byte j of a row holds element 2j in the low nibble and
  *  element 2j+1 in the high nibble.  The quantizer formula is the review's section 3
  *  equation Q_X = round(X / s_X), s_X = max|X| / q_max (q_max 7 for INT4, 6 for FP4).
@@ -53,7 +62,7 @@ typedef enum {
   SVDQ_EHIP = 4          /* HIP runtime error reported at launch */
 } svdq_status;
 
-typedef enum { SVDQ_INT4_G64 = 0, SVDQ_MXFP4_G32 = 1 } svdq_format;
+typedef enum { SVDQ_INT4_G64 = 0, SVDQ_MXFP4_G32 = 1, SVDQ_NVFP4_G16 = 2 } svdq_format;
 typedef enum { SVDQ_F32 = 0, SVDQ_BF16 = 1 } svdq_dtype;
 
 /* How kernel 1 hands the activation side to kernel 2 (both calls must agree).
@@ -71,6 +80,11 @@ typedef enum { SVDQ_F32 = 0, SVDQ_BF16 = 1 } svdq_dtype;
  *           MXFP4: the PACKED codes in token pairs: byte b of token m's code row at
  *           (m / 2) * K + (b / 64) * 128 + (m % 2) * 64 + b % 64 ((M rounded up to 2) *
  *           K/2 bytes); sX [K/32][Mp] E8M0 bytes.
+ *           NVFP4: the codes in token pairs as for MXFP4, but inside each block of 64
+ *           K values code k is at nibble 2 (16 ((k / 8) % 2) + 4 (k / 16)) + (k % 8) of the
+ *           block's 32 bytes (the lane order of the bf16 matrix core: eight codes of one
+ *           group of 16 per lane and K step); sX [K/64][Mp][4]: the four E4M3 group scales
+ *           of a row and 64-block contiguous.
  *           Both: lora_act as bf16 pairs hi = bf16(v), lo = bf16(v - hi) of the fp32
  *           value v, in the matrix core's fragment order (each 16-byte load of kernel
  *           2 then reads whole lines): with S = R16 / 16, the hi (p = 0) and lo (p = 1)
@@ -104,6 +118,9 @@ typedef struct svdq_layer {
   const uint16_t* L2f;
   const uint8_t* qW;
   const void* sW;
+  /* NVFP4 only (host values, ignored otherwise): the weights' and the activations'
+   * fp32 tensor scales, as svdq_pack_weights writes them after the group scales */
+  float tscale_w, tscale_x;
 } svdq_layer;
 
 /* Thread-local description of the last failure in this thread ("" after success). */
@@ -117,7 +134,9 @@ const char* svdq_last_error(void);
  * EINVAL on NULL / M < 1 / K < 1 / ldx < K. */
 svdq_status svdq_act_absmax(int64_t M, int64_t K, const uint16_t* X, int64_t ldx, float* out);
 
-/* Sizes in bytes of the packed residual buffers for a K x N layer. */
+/* Sizes in bytes of the packed residual buffers for a K x N layer.  NVFP4: sW holds the
+ * E4M3 group scales [K/16][N] followed by two fp32 values, the weights' tensor scale and
+ * the activations' tensor scale. */
 svdq_status svdq_weight_sizes(int64_t K, int64_t N, int32_t fmt, size_t* qW_bytes,
                               size_t* sW_bytes);
 
@@ -133,7 +152,9 @@ svdq_status svdq_weight_sizes(int64_t K, int64_t N, int32_t fmt, size_t* qW_byte
  * (s = 1); alpha in [0,1]; 0 <= rank <= min(K, N, SVDQ_MAX_RANK).
  * Outputs (host, caller-allocated): s_out, inv_s_out [K] fp32; L1t_out [rank][K] bf16
  * (L1 transposed: row j = sigma_j u_j); L2_out [rank][N] bf16; qW_out [N][K/2];
- * sW_out [K/G][N]; R_out optional fp32 [K][N] (NULL to skip).
+ * sW_out [K/G][N] (NVFP4: then the two fp32 tensor scales, the activations' taken from
+ * max_k fp32(act_absmax[k] * inv_s[k]), 1 when act_absmax is NULL); R_out optional fp32
+ * [K][N] (NULL to skip).
  * Errors: EINVAL (NULL, K % 128 != 0, N < 1, alpha out of range, bad rank),
  * ENUMERIC (non-finite W or act_absmax), EUNSUPPORTED (fmt). */
 svdq_status svdq_pack_weights(int64_t K, int64_t N, const uint16_t* W, const float* act_absmax,
@@ -157,7 +178,8 @@ svdq_status svdq_pack_weights_refined(int64_t K, int64_t N, const uint16_t* W, c
                                       void* sW_out, float* R_out, double* err_out);
 
 /* Quantize a given fp32 residual R [K][N] (host) per output column in groups along K:
- * the last step of svdq_pack_weights on its own.  Outputs as in svdq_pack_weights. */
+ * the last step of svdq_pack_weights on its own.  Outputs as in svdq_pack_weights
+ * (NVFP4: the activations' tensor scale is written as 1). */
 svdq_status svdq_quantize_weights(int64_t K, int64_t N, const float* R, int32_t fmt,
                                   uint8_t* qW_out, void* sW_out);
 
@@ -212,6 +234,9 @@ svdq_status svdq_prepare_lowrank(int64_t N, int32_t rank, const uint16_t* L2, ui
  *          segments of columns 2j and 2j+1 for 128 consecutive K share a 128-byte line;
  *          with N odd the last pair's second column is zero.
  *          sW_out: the fp16 scale bits [K/64][Np] ((K/64) * Np * 2 bytes), padding 0.
+ *   NVFP4: qW_out: codes in column pairs as for MXFP4, each 64-block in the lane order
+ *          of the MMA activation form below; sW_out [K/64][Np][4] E4M3 bytes (padding
+ *          0).  The tensor scales are not copied: they go into svdq_layer. 
  * EINVAL on bad sizes, ENUMERIC on a negative or non-finite scale. */
 svdq_status svdq_prepare_weights(int64_t K, int64_t N, int32_t fmt, const uint8_t* qW,
                                  const void* sW, uint8_t* qW_out, void* sW_out);

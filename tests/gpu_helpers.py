@@ -31,7 +31,7 @@ def layer_from_oracle(p, device="cuda:0"):
     fmt = svdq.FMT[p["fmt"]]
     L1t = np.ascontiguousarray(p["L1_bits"].T)
     return svdq.PackedLinear(p["K"], p["N"], p["rank"], fmt, p["inv_s32"], L1t, p["L2_bits"], p["qW"],
-                             p["sW"], device)
+                             p["sW"], device, float(p.get("S_W", 1.0)), float(p.get("S_X", 1.0)))
 
 
 def to_dev_bf16(X_bits, device="cuda:0"):
@@ -42,7 +42,7 @@ def to_dev_bf16(X_bits, device="cuda:0"):
 
 def oracle_k1(X_bits, p):
     """Oracle kernel-1 outputs in the library's storage layout."""
-    Xh, codes, sc = oforward.quantize_activations(X_bits, p["inv_s32"], p["fmt"])
+    Xh, codes, sc = oforward.quantize_activations(X_bits, p["inv_s32"], p["fmt"], p.get("S_X"))
     qX = opack.pack_codes(codes, p["fmt"])
     sX = np.ascontiguousarray(sc.T)  # group-major [K/G][M]
     la = oforward.lora_down(Xh, p["L1b"]) if p["rank"] else None
@@ -129,7 +129,20 @@ def decode_mma(qX, sX, la, fmt, K, rank, M=None):
         M2 = (M + 1) // 2 * 2
         pr = np.ascontiguousarray(q).reshape(-1)[:M2 * K // 2].reshape(M2 // 2, K // 128, 2, 64)
         rows = pr.transpose(0, 2, 1, 3).reshape(M2, K // 2)[:M]
-        out = rows, sb[:(K // 32) * Mp].reshape(K // 32, Mp)[:, :M]
+        if fmt == "nvfp4":
+            # inside each 64-block code k sits at nibble 2 (16 ((k / 8) % 2) + 4 (k / 16)) + k % 8;
+            # scales [K/64][Mp][4]
+            nib = np.empty((M, K // 64, 64), np.uint8)
+            blk = rows.reshape(M, K // 64, 32)
+            for k in range(64):
+                pos = 2 * (16 * ((k >> 3) & 1) + 4 * (k >> 4)) + (k & 7)
+                nib[:, :, k] = (blk[:, :, pos >> 1] >> (4 * (pos & 1))) & 15
+            nib = nib.reshape(M, K)
+            rows = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+            sv = None if sX is None else sb[:(K // 64) * Mp * 4].reshape(K // 64, Mp, 4)[:, :M].transpose(0, 2, 1)
+            out = rows, (None if sv is None else sv.reshape(K // 16, M))
+        else:
+            out = rows, sb[:(K // 32) * Mp].reshape(K // 32, Mp)[:, :M]
     hi = lo = None
     if rank:
         hi, lo = decode_lora_mma(la, M, rank)

@@ -109,7 +109,20 @@ def _fp4_groups(rng):
     return out
 
 
-def _plain_pack(K, N, rank, fmt, seed):
+def _nv_groups(rng):
+    """NVFP4 cases (generated in groups of 32, i.e. two 16-groups): the FP4 cases without
+    the fp32-range ones (the tensor scale comes from the largest value, so they would zero
+    every other group), plus groups whose E4M3 scale is subnormal or rounds to zero."""
+    out = [c for c in _fp4_groups(rng) if c[0] not in ("huge", "e8m0_clamp_min_normal", "e8m0_clamp_denormal")]
+    v = rng.uniform(-1e-4, 1e-4, 32)
+    v[0] = 1e-4
+    out.append(("e4m3_subnormal_scale", bf16_bits_from_f64(v), True))
+    v = rng.uniform(-1e-7, 1e-7, 32)
+    out.append(("e4m3_scale_rounds_to_zero", bf16_bits_from_f64(v), True))
+    return out
+
+
+def _plain_pack(K, N, rank, fmt, seed, S_X=1.0):
     """A layer with smoothing factor 1 (X_hat = X): residual codes and scales from the
     oracle quantizer on a Gaussian R, bf16 low-rank factors."""
     rng = np.random.default_rng(seed)
@@ -117,9 +130,13 @@ def _plain_pack(K, N, rank, fmt, seed):
     codesW, sW = opack.quantize_residual(R, fmt)
     L1b = round_f64_to_bf16(0.05 * rng.standard_normal((K, rank)))
     L2b = round_f64_to_bf16(rng.standard_normal((rank, N)))
-    return dict(fmt=fmt, K=K, N=N, rank=rank, inv_s32=np.ones(K, np.float32), L1b=L1b, L2b=L2b,
-                L1_bits=bf16_value_to_bits(L1b), L2_bits=bf16_value_to_bits(L2b), codesW=codesW,
-                qW=opack.pack_codes(codesW, fmt), sW=sW)
+    p = dict(fmt=fmt, K=K, N=N, rank=rank, inv_s32=np.ones(K, np.float32), L1b=L1b, L2b=L2b,
+             L1_bits=bf16_value_to_bits(L1b), L2_bits=bf16_value_to_bits(L2b), codesW=codesW,
+             qW=opack.pack_codes(codesW, fmt), sW=sW)
+    if fmt == "nvfp4":
+        p["S_W"] = opack.residual_tensor_scale(R)
+        p["S_X"] = np.float32(S_X)
+    return p
 
 
 def _planted_X(cases, K, G, rows_per_case, rng):
@@ -142,7 +159,7 @@ _GEN = {}
 
 
 def _regen(name, G, rng):
-    gens = _GEN[G](rng)
+    gens = _GEN[G](rng) if name not in _NV_ONLY else _nv_groups(rng)
     for n, bits, _ in gens:
         if n == name:
             return bits
@@ -151,6 +168,7 @@ def _regen(name, G, rng):
 
 _GEN[64] = _int4_groups
 _GEN[32] = _fp4_groups
+_NV_ONLY = ("e4m3_subnormal_scale", "e4m3_scale_rounds_to_zero")
 
 
 def _oracle_side_checks(fmt, names, X, rows_per_case):
@@ -171,6 +189,15 @@ def _oracle_side_checks(fmt, names, X, rows_per_case):
         assert (s[rows["scale_saturates"]] == 65504.0).all()
         assert not codes[rows["scale_underflows_to_zero"]].any()
         return codes
+    if fmt == "nvfp4":
+        S = oquant.nvfp4_tensor_scale(np.abs(Xh).max())
+        codes, e = oquant.quantize_nvfp4(Xh, S)
+        sub = e[rows["e4m3_subnormal_scale"]]
+        assert ((sub > 0) & (sub < 8)).any(), "no subnormal E4M3 scale"
+        assert (e[rows["e4m3_scale_rounds_to_zero"]] == 0).all()
+        assert (codes[rows["neg_zero"]] == 0x8).all() and (codes[rows["zero"]] == 0).all()
+        assert (e[rows["grid_ties_e0"]] == 0x7E).any(), "a group at the tensor maximum takes scale 448"
+        return codes
     codes, e = oquant.quantize_mxfp4(Xh)
     assert (e[rows["e8m0_clamp_min_normal"]] == 0).all() and (e[rows["e8m0_clamp_denormal"]] == 0).all()
     assert (codes[rows["neg_zero"]] == 0x8).all() and (codes[rows["zero"]] == 0).all()
@@ -180,19 +207,20 @@ def _oracle_side_checks(fmt, names, X, rows_per_case):
     return codes
 
 
-@pytest.mark.parametrize("fmt", ["int4", "mxfp4"])
+@pytest.mark.parametrize("fmt", ["int4", "mxfp4", "nvfp4"])
 def test_planted_quantizer_edge_cases(fmt):
     import torch
 
     G = 64 if fmt == "int4" else 32
     K, N, rank, rpc = 256, 96, 16, 3
-    rng = np.random.default_rng(2024 if fmt == "int4" else 2025)
-    cases = _GEN[G](rng)
+    rng = np.random.default_rng({"int4": 2024, "mxfp4": 2025, "nvfp4": 2026}[fmt])
+    cases = _nv_groups(rng) if fmt == "nvfp4" else _GEN[G](rng)
     X, names, fwd = _planted_X(cases, K, G, rpc, rng)
     M = X.shape[0]
     log(f"edge cases {fmt}: {len(names)} cases x {rpc} rows, K={K}: {', '.join(names)}")
     _oracle_side_checks(fmt, names, X, rpc)
-    p = _plain_pack(K, N, rank, fmt, 31)
+    Xh = oquant.smooth_activations(X, np.ones(K, np.float32))
+    p = _plain_pack(K, N, rank, fmt, 31, S_X=oquant.nvfp4_tensor_scale(np.abs(Xh).max()))
     lay = layer_from_oracle(p)
     Xd = to_dev_bf16(X)
     Xh, codes, sc, qX_ref, sX_ref, la_ref = oracle_k1(X, p)

@@ -38,7 +38,7 @@ _svd_cache = {}
 
 def _pack_for(wl):
     """Oracle pack for a workload; the SVD split of a given (W, calibration) is shared."""
-    key = (wl.seed if wl.name != "C4" else 1001, wl.name in ("C1", "C3", "C4"), wl.K, wl.N)
+    key = (wl.seed if wl.name != "C4" else 1001, wl.name in ("C1", "C3", "C4", "C1nv"), wl.K, wl.N)
     if key not in _svd_cache:
         a = oquant.channel_absmax_cols(wl.calib)
         w = oquant.channel_absmax_rows(wl.W)
@@ -51,6 +51,9 @@ def _pack_for(wl):
     p = dict(fmt=wl.fmt, K=wl.K, N=wl.N, rank=wl.rank, s64=s64, s32=s32, inv_s32=inv,
              L1b=sp["L1b"], L2b=sp["L2b"], L1_bits=None, L2_bits=None,
              codesW=codesW, qW=opack.pack_codes(codesW, wl.fmt), sW=sW)
+    if wl.fmt == "nvfp4":  # the two level-2 scales, as the oracle pack sets them
+        p["S_W"] = opack.residual_tensor_scale(R32)
+        p["S_X"] = oquant.nvfp4_tensor_scale((oquant.channel_absmax_cols(wl.calib).astype(np.float32) * inv).max())
     from oracle.numerics import bf16_value_to_bits
     p["L1_bits"] = bf16_value_to_bits(p["L1b"])
     p["L2_bits"] = bf16_value_to_bits(p["L2b"])
@@ -67,7 +70,7 @@ def _check_y(Yd, Yref, what):
     return e
 
 
-@pytest.mark.parametrize("name", ["C1", "C2a", "C2b", "C3", "C4"])
+@pytest.mark.parametrize("name", ["C1", "C2a", "C2b", "C3", "C4", "C1nv"])
 def test_full_size_layer(name):
     import torch
 
@@ -109,9 +112,10 @@ def test_full_size_layer(name):
     else:
         nq = (M + 1) // 2 * 2 * (K // 2)
         sx0 = (nq + 255) // 256 * 256
-        la0 = sx0 + ((K // 32) * Mp + 255) // 256 * 256
-        c_m, s_m, hi, lo = decode_mma(ws[:M * (K // 2)].view(M, K // 2), ws[sx0:sx0 + (K // 32) * Mp], ws[la0:],
-                                      "mxfp4", K, r, M=M)
+        G = 32 if wl.fmt == "mxfp4" else 16
+        la0 = sx0 + ((K // G) * Mp + 255) // 256 * 256
+        c_m, s_m, hi, lo = decode_mma(ws[:M * (K // 2)].view(M, K // 2), ws[sx0:sx0 + (K // G) * Mp], ws[la0:],
+                                      wl.fmt, K, r, M=M)
         np.testing.assert_array_equal(c_m, qX_ref)
         np.testing.assert_array_equal(s_m, sX_ref)
     np.testing.assert_array_equal(hi, bf16_rne_bits(la_g))

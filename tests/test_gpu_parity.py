@@ -40,6 +40,11 @@ SHAPES = [  # M, K, N, rank, fmt
     # K long enough that kernel 2 splits its tiles along K (few tiles, >= 8 K steps)
     (200, 1024, 300, 8, "int4"),
     (130, 768, 260, 16, "mxfp4"),
+    # the group-16 two-level-scale variant
+    (64, 256, 256, 8, "nvfp4"),
+    (17, 128, 33, 1, "nvfp4"),
+    (300, 384, 520, 16, "nvfp4"),
+    (200, 1024, 300, 48, "nvfp4"),
 ]
 
 
@@ -161,7 +166,8 @@ def test_forward_matches_oracle(shape):
     else:
         nq = (M + 1) // 2 * 2 * (K // 2)
         sx0 = (nq + 255) // 256 * 256
-        rows, sb = decode_mma(ws[:M * (K // 2)].view(M, K // 2), ws[sx0:sx0 + (K // 32) * Mp], None, "mxfp4", K, 0,
+        G = 32 if fmt == "mxfp4" else 16
+        rows, sb = decode_mma(ws[:M * (K // 2)].view(M, K // 2), ws[sx0:sx0 + (K // G) * Mp], None, fmt, K, 0,
                               M=M)[:2]
         np.testing.assert_array_equal(rows, qX_ref)
         np.testing.assert_array_equal(sb, sX_ref)
@@ -179,7 +185,11 @@ def test_forward_matches_oracle(shape):
     assert en <= TOL_Y
     if K >= 768:
         assert gws is not None, "expected kernel 2 to split this shape"
-    # the packed form meets the same bar
+    # the packed form meets the same bar (kernel 2 on the NVFP4 format takes the MMA form only)
+    if fmt == "nvfp4":
+        with pytest.raises(svdq.SvdqError):
+            lay.gemm(qX, sX, la, out=sentinel_out(M, N), form=svdq.ACT_PACKED)
+        return
     qX, sX, la = lay.quantize_act(X, out=sentinel_act(lay, M, svdq.ACT_PACKED))
     Ypd = lay.gemm(qX, sX, la, out=sentinel_out(M, N))
     assert_finite(Ypd)

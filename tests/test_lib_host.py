@@ -39,7 +39,7 @@ def test_act_absmax_matches_oracle():
     np.testing.assert_array_equal(svdq.act_absmax(wl.X), oquant.channel_absmax_cols(wl.X).astype(np.float32))
 
 
-@pytest.mark.parametrize("fmt", ["int4", "mxfp4"])
+@pytest.mark.parametrize("fmt", ["int4", "mxfp4", "nvfp4"])
 def test_residual_quantizer_bit_exact(fmt):
     rng = np.random.default_rng(8)
     K, N = 256, 96
@@ -50,9 +50,40 @@ def test_residual_quantizer_bit_exact(fmt):
     R[:64, 9] = np.linspace(-1e-9, 1e-9, 64).astype(np.float32)  # the fp16 scale underflows to 0: codes 0
     R[64:128, 9] = np.float32(1e6) * np.linspace(-1, 1, 64).astype(np.float32)  # the scale saturates
     codes, sc = opack.quantize_residual(R, fmt)
-    qW, sW = svdq.quantize_weights(R, svdq.FMT[fmt])
+    qW, sW, tw = svdq.quantize_weights(R, svdq.FMT[fmt], with_tscale=True)
     np.testing.assert_array_equal(qW, opack.pack_codes(codes, fmt))
     np.testing.assert_array_equal(sW, sc)
+    if fmt == "nvfp4":
+        assert np.float32(tw) == opack.residual_tensor_scale(R)
+
+
+def test_nvfp4_pack_and_device_layout():
+    """The library's NVFP4 pack: codes are the oracle quantizer on the library's own R under
+    the library's tensor scales (both equal to the oracle's definitions), and the prepared
+    device layout decodes back to those codes and scales."""
+    wl = random_layer(64, 256, 200, 8, 3, fmt="nvfp4", x_out=3, w_out=2)
+    a = svdq.act_absmax(wl.calib)
+    hp = svdq.pack_weights(wl.W, a, wl.alpha, 8, svdq.NVFP4_G16, want_R=True)
+    codes, sc = opack.quantize_residual(hp.R, "nvfp4")
+    np.testing.assert_array_equal(hp.qW, opack.pack_codes(codes, "nvfp4"))
+    np.testing.assert_array_equal(hp.sW, sc)
+    assert np.float32(hp.tscale_w) == opack.residual_tensor_scale(hp.R)
+    assert np.float32(hp.tscale_x) == oquant.nvfp4_tensor_scale((a * hp.inv_s).astype(np.float32).max())
+    K, N = 256, 200
+    qo, so = svdq.prepare_weights(K, N, svdq.NVFP4_G16, hp.qW, hp.sW)
+    # column n's 64-byte stage segment at (n / 2) K + (b / 64) 128 + (n % 2) 64; inside each
+    # 64-block code k at nibble 2 (16 ((k / 8) % 2) + 4 (k / 16)) + k % 8
+    for n in (0, 1, 7, N - 1):
+        row = np.concatenate([qo[(n // 2) * K + (b // 64) * 128 + (n % 2) * 64:][:64] for b in range(0, K // 2, 64)])
+        nib = np.stack([row & 15, row >> 4], axis=1).reshape(-1)
+        for k0 in range(0, K, 64):
+            for k in range(64):
+                pos = 2 * (16 * ((k >> 3) & 1) + 4 * (k >> 4)) + (k & 7)
+                assert nib[k0 + pos] == codes[n, k0 + k]
+    Np = (N + 3) // 4 * 4
+    s4 = so.reshape(K // 64, Np, 4)
+    np.testing.assert_array_equal(s4[:, :N].transpose(0, 2, 1).reshape(K // 16, N), sc)
+    assert not s4[:, N:].any()
 
 
 @pytest.fixture(scope="module")
@@ -105,7 +136,8 @@ def test_pack_svd_split_properties(c0_both):
 
 
 @pytest.mark.parametrize("K,N,r,fmt", [(256, 640, 16, "int4"), (640 // 128 * 128 + 128, 200, 12, "mxfp4"),
-                                       (384, 384, 0, "int4"), (128, 64, 64, "int4")])
+                                       (384, 384, 0, "int4"), (128, 64, 64, "int4"), (256, 320, 16, "nvfp4"),
+                                       (256, 96, 0, "nvfp4")])
 def test_pack_matches_oracle_subspace(K, N, r, fmt):
     wl = random_layer(96, K, N, r, 4242 + K + N, fmt=fmt, x_out=3, w_out=2)
     a = svdq.act_absmax(wl.X)
@@ -131,13 +163,15 @@ def _lib_split_error(hp, W_bits, fmt):
     sc = np.ascontiguousarray(hp.sW.T)
     if fmt == "int4":
         D = oquant.dequant_int4(oquant.nibble_to_int4(nib), sc)
+    elif fmt == "nvfp4":
+        D = oquant.dequant_nvfp4(nib, sc, hp.tscale_w)
     else:
         D = oquant.dequant_mxfp4(nib, sc)
     P = bf16_to_f64(hp.L1t).T @ bf16_to_f64(hp.L2) if hp.rank else 0.0
     return float(np.linalg.norm(Wh - P - D.T))
 
 
-@pytest.mark.parametrize("fmt", ["int4", "mxfp4"])
+@pytest.mark.parametrize("fmt", ["int4", "mxfp4", "nvfp4"])
 def test_refined_pack(fmt):
     """svdq_pack_weights_refined: iters = 0 is svdq_pack_weights bit for bit; with
     iterations, the errors it reports follow the oracle's refinement, and the kept pack
@@ -170,7 +204,7 @@ def _refined_raw(W, a, alpha, rank, F, iters):
     s, inv = np.empty(K, np.float32), np.empty(K, np.float32)
     L1t, L2 = np.zeros((rank, K), np.uint16), np.zeros((rank, N), np.uint16)
     qW = np.empty((N, K // 2), np.uint8)
-    sW = np.empty((K // G, N), np.uint16 if F == svdq.INT4_G64 else np.uint8)
+    sW = svdq._scale_buffer(K, N, F)[0]
     W = np.ascontiguousarray(W, dtype=np.uint16)
     svdq._check(svdq.lib().svdq_pack_weights_refined(K, N, svdq._ptr(W), svdq._ptr(a), float(alpha), rank, F, iters,
                                                      svdq._ptr(s), svdq._ptr(inv), svdq._ptr(L1t), svdq._ptr(L2),
