@@ -67,49 +67,105 @@ def traffic_entry():
 CALIB_BYTES = 512 << 20
 
 
-def _pmc_means(path):
-    """Mean counter value per kernel-name prefix from a rocprofv3 counter CSV."""
+def _kernel_key(name):
+    """Which launch of the timed forward a rocprofv3 kernel name is: kernel 1, kernel 2
+    (the INT4 streamed kernel on the MMA activation form), kernel 2's K-split fixup, or
+    a device copy (the calibration copy is the largest of those)."""
+    if "k1_quant_lora_down" in name:
+        return "k1"
+    if "k2_stream<0" in name:
+        return "k2"
+    if "k2_fixup" in name:
+        return "fixup"
+    if "k2_" in name or "k3_" in name:
+        return None
+    return "copy" if "copy" in name.lower() else None
+
+
+def _pmc_table(path):
+    """{kernel key: {counter: (mean over dispatches, dispatches)}} from a rocprofv3
+    counter CSV; for the copy key the largest dispatch."""
     import csv
     import collections
 
-    acc = collections.defaultdict(list)
+    acc = collections.defaultdict(lambda: collections.defaultdict(list))
     for r in csv.DictReader(open(path)):
-        name = r["Kernel_Name"]
-        # kernel 2 of the timed forward: the INT4 streamed kernel on the MMA activation
-        # form (the fixup launch is counted with it)
-        if "k2_stream<0" in name or "k2_fixup" in name:
-            key = "k2" if "k2_stream" in name else "fixup"
-        elif "copyBuffer" in name or "copy" in name.lower():
-            key = "copy"
-        else:
-            key = None
+        key = _kernel_key(r["Kernel_Name"])
         if key:
-            acc[key].append(float(r["Counter_Value"]))
-    # the calibration copy is the largest copy dispatch (uploads may also use copy kernels)
-    return {k: ((max(v) if k == "copy" else sum(v) / len(v)), len(v)) for k, v in acc.items()}
+            acc[key][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    return {k: {c: ((max(v) if k == "copy" else sum(v) / len(v)), len(v)) for c, v in cs.items()}
+            for k, cs in acc.items()}
+
+
+PMC_COMMAND = ("rocprofv3 --pmc {counters} --output-format csv -d <dir> -o <name> -- python bench.py --steps 3 "
+               "--warmup 1 --warm-seconds 0 --no-cpu-baseline --no-compare --no-others --calib-copy")
 
 
 def write_traffic(fetch_csv, write_csv):
-    """Kernel 2's HBM traffic per launch: FETCH_SIZE and WRITE_SIZE (KiB per dispatch)
-    of kernel 2, each divided by the same counter's reading per byte for a plain copy of
-    CALIB_BYTES (read and written once each)."""
-    f = _pmc_means(fetch_csv)
-    w = _pmc_means(write_csv)
-    ffac = f["copy"][0] * 1024.0 / CALIB_BYTES
-    wfac = w["copy"][0] * 1024.0 / CALIB_BYTES
+    """HBM traffic per launch of kernel 1 and of kernel 2 (with its fixup): FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch), each divided by the same counter's reading per byte
+    for a plain copy of CALIB_BYTES (read and written once each)."""
+    f = _pmc_table(fetch_csv)
+    w = _pmc_table(write_csv)
+    ffac = f["copy"]["FETCH_SIZE"][0] * 1024.0 / CALIB_BYTES
+    wfac = w["copy"]["WRITE_SIZE"][0] * 1024.0 / CALIB_BYTES
+    val = lambda t, k, c: t.get(k, {}).get(c, (0.0, 0))[0]
     # the fixup launch runs once per kernel-2 launch
-    fetch_b = (f["k2"][0] + f.get("fixup", (0.0, 0))[0]) * 1024.0 / ffac
-    write_b = (w["k2"][0] + w.get("fixup", (0.0, 0))[0]) * 1024.0 / wfac
+    fetch_b = (val(f, "k2", "FETCH_SIZE") + val(f, "fixup", "FETCH_SIZE")) * 1024.0 / ffac
+    write_b = (val(w, "k2", "WRITE_SIZE") + val(w, "fixup", "WRITE_SIZE")) * 1024.0 / wfac
+    k1_f = val(f, "k1", "FETCH_SIZE") * 1024.0 / ffac
+    k1_w = val(w, "k1", "WRITE_SIZE") * 1024.0 / wfac
     d = {"kernel": "k2_stream<INT4> + k2_fixup", "workload": "FLUX.1 QKV projection M=4608 K=3072 N=9216 r=32, fp32 Y",
-         "k2_source_hash": source_hash(K2_SOURCES), "fetch_kib_raw": f["k2"][0], "write_kib_raw": w["k2"][0],
-         "copy_fetch_factor": ffac, "copy_write_factor": wfac, "fetch_bytes": fetch_b, "write_bytes": write_b,
-         "bytes_per_launch": fetch_b + write_b, "dispatches": f["k2"][1],
-         "command": "rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -- "
-                    "python bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-compare --calib-copy"}
+         "k2_source_hash": source_hash(K2_SOURCES), "fetch_kib_raw": val(f, "k2", "FETCH_SIZE"),
+         "write_kib_raw": val(w, "k2", "WRITE_SIZE"), "copy_fetch_factor": ffac, "copy_write_factor": wfac,
+         "fetch_bytes": fetch_b, "write_bytes": write_b, "bytes_per_launch": fetch_b + write_b,
+         "dispatches": f["k2"]["FETCH_SIZE"][1],
+         "k1": {"kernel": "k1_quant_lora_down<INT4, MMA form>", "fetch_bytes": k1_f, "write_bytes": k1_w,
+                "bytes_per_launch": k1_f + k1_w,
+                "algorithmic_bytes": k1_algorithmic_bytes(4608, 3072, 64, 32, True)},
+         "command": PMC_COMMAND.format(counters="FETCH_SIZE") + "; the same with --pmc WRITE_SIZE; then "
+                    "python bench.py --write-traffic <fetch csv> <write csv>"}
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as fh:
         json.dump(d, fh, indent=1)
     print(json.dumps(d))
+
+
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "k2_gemm_int4_flux_qkv_counters.json")
+N_XCD, N_CU, SIMD_PER_CU = 8, 256, 4
+
+
+def write_counters(a_csv, b_csv):
+    """Utilisation of kernels 1 and 2 from two rocprofv3 --pmc passes.  GRBM_GUI_ACTIVE is
+    summed over the 8 XCDs, so one XCD's active cycles are a eighth of it; the SQ busy
+    counters are summed over all 1024 SIMDs (SQ_ACTIVE_INST_VALU in units of 4 cycles,
+    one wave64 VALU issue), so each fraction below is per SIMD-cycle of the launch."""
+    a, b = _pmc_table(a_csv), _pmc_table(b_csv)
+    out = {"workload": "FLUX.1 QKV projection M=4608 K=3072 N=9216 r=32, INT4 g64, fp32 Y",
+           "k2_source_hash": source_hash(K2_SOURCES),
+           "commands": [PMC_COMMAND.format(counters=" ".join(sorted(a["k2"]))),
+                        PMC_COMMAND.format(counters=" ".join(sorted(b["k2"]))),
+                        "python bench.py --write-counters <pass A csv> <pass B csv>"],
+           "kernels": {}}
+    for key in ("k1", "k2"):
+        raw = {c: v[0] for c, v in a.get(key, {}).items()}
+        raw.update({c: v[0] for c, v in b.get(key, {}).items() if c != "GRBM_GUI_ACTIVE"})
+        cyc = raw["GRBM_GUI_ACTIVE"] / N_XCD
+        simd_cyc = cyc * N_CU * SIMD_PER_CU
+        g = lambda c: raw.get(c, float("nan"))
+        hits, miss = g("TCC_HIT_sum"), g("TCC_MISS_sum")
+        out["kernels"][key] = {
+            "raw_mean_per_dispatch": raw,
+            "active_cycles_per_xcd": cyc,
+            "mfma_busy_frac": g("SQ_VALU_MFMA_BUSY_CYCLES") / simd_cyc,
+            "valu_busy_frac": 4.0 * g("SQ_ACTIVE_INST_VALU") / simd_cyc,
+            "valu_mfma_coexec_frac": g("SQ_VALU_MFMA_COEXEC_CYCLES") / simd_cyc,
+            "valu_insts_per_mfma": g("SQ_INSTS_VALU") / max(g("SQ_INSTS_MFMA"), 1.0),
+            "lds_bank_conflict_cycles_per_lds_inst": g("SQ_LDS_BANK_CONFLICT") / max(g("SQ_INSTS_LDS"), 1.0),
+            "l2_hit_frac": hits / (hits + miss) if hits + miss > 0 else None}
+    with open(COUNTERS_FILE, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out))
 
 
 def cpu_baseline(wl_name, rows):
@@ -283,12 +339,18 @@ def main():
     ap.add_argument("--calib-copy", action="store_true",
                     help="after timing, run one plain device copy of 512 MiB (counter calibration)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="compute kernel 2's HBM bytes per launch from two rocprofv3 --pmc CSVs "
-                         "(FETCH_SIZE, WRITE_SIZE) of runs made with --calib-copy, write the "
+                    help="compute kernel 1's and kernel 2's HBM bytes per launch from two rocprofv3 "
+                         "--pmc CSVs (FETCH_SIZE, WRITE_SIZE) of runs made with --calib-copy, write the "
                          "summary JSON, and exit")
+    ap.add_argument("--write-counters", nargs=2, metavar=("PASS_A_CSV", "PASS_B_CSV"),
+                    help="summarise two rocprofv3 --pmc utilisation passes of kernels 1 and 2 (MFMA and "
+                         "VALU busy, co-issue, LDS, L2), write the summary JSON, and exit")
     args = ap.parse_args()
     if args.write_traffic:
         write_traffic(*args.write_traffic)
+        return
+    if args.write_counters:
+        write_counters(*args.write_counters)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
