@@ -155,3 +155,44 @@ def forward(X_bits: np.ndarray, packed: dict, rows=None, cols=None) -> dict:
     if L2.shape[0]:
         Y = Y + la_r @ L2c
     return dict(Xh=Xh, codesX=cX, scalesX=sX, lora_act=la, Y=Y)
+
+
+# ---------------------------------------------------------------------------------------
+# The chained MLP pair: fc2 consumes GELU of fc1's output.  The fusion that motivates
+# chaining the pair (the next layer's quantization done where the previous layer's output
+# tile is produced, so the 16-bit activation is not written and re-read) is the fused
+# kernel design of the review's section 4.3 ("Nunchaku", Figure 6(b)) and the cost named
+# in the ch3chohch3 post's "量化方案" section (16-bit activations reloaded from HBM).
+# Readings (the pages name neither the activation nor the hidden format):
+#   * the activation is GELU in its exact form x Phi(x), Phi the standard normal CDF;
+#   * the hidden activation G exists in the layers' 16-bit input format: one rounding of
+#     GELU(H) to bf16 (ties to even), H = fc1's output;
+#   * fc2 is the unchanged layer forward above, applied to G.
+
+def gelu_erf(h: np.ndarray) -> np.ndarray:
+    """GELU(h) = h Phi(h) with Phi(h) = erfc(-h / sqrt 2) / 2, in fp64 (erfc rather than
+    1 + erf keeps full relative accuracy in the negative tail)."""
+    from scipy.special import erfc
+
+    h = np.asarray(h, dtype=np.float64)
+    return h * (0.5 * erfc(-h / np.sqrt(2.0)))
+
+
+def mlp_hidden(X_bits: np.ndarray, packed1: dict) -> dict:
+    """fc1's forward, then G = bf16(GELU(H)).  Returns dict(H [M][N1] fp64, G_bits uint16
+    [M][N1], fc1 = fc1's forward dict)."""
+    from .numerics import bf16_value_to_bits, round_f64_to_bf16
+
+    f1 = forward(X_bits, packed1)
+    H = f1["Y"]
+    G_bits = bf16_value_to_bits(round_f64_to_bf16(gelu_erf(H)))
+    return dict(H=H, G_bits=G_bits, fc1=f1)
+
+
+def mlp_forward(X_bits: np.ndarray, packed1: dict, packed2: dict, cols=None) -> dict:
+    """The pair: Y = fc2(bf16(GELU(fc1(X)))).  Every token is independent, so a subset of
+    tokens is taken by passing those rows of X; cols selects fc2's output columns.
+    Returns dict(H, G_bits, fc2 = fc2's forward dict (its Y is the pair's output))."""
+    hid = mlp_hidden(X_bits, packed1)
+    f2 = forward(hid["G_bits"], packed2, cols=cols)
+    return dict(H=hid["H"], G_bits=hid["G_bits"], fc2=f2)
