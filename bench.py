@@ -320,6 +320,72 @@ def measure(svdq, torch, wl_name, ydt, steps, warmup, warm_s, compare, log_prefi
     return res
 
 
+def measure_mlp(svdq, torch, steps, warm_s):
+    """The chained FLUX.1 MLP pair (C2chain: 4608 tokens, 3072 -> 12288 -> 3072, rank 32,
+    INT4): svdq_mlp_forward chained against separate (two forwards, fc1 with the GELU
+    output), timed in alternating blocks of 20, and the chained step's kernels one by one
+    with HIP events on the launch stream."""
+    from bit_diffusion_model_amd.workloads import make_mlp
+
+    dev = "cuda:0"
+    d = make_mlp("C2chain")
+    M = d.M
+    log(f"[bench] [mlp] pair M={M} {d.fc1.K} -> {d.fc1.N} -> {d.fc2.N}; packing on host")
+    lays = []
+    for wl in (d.fc1, d.fc2):
+        hp = svdq.pack_weights(wl.W, svdq.act_absmax(wl.calib), wl.alpha, wl.rank, svdq.INT4_G64)
+        lays.append(svdq.PackedLinear.from_host_pack(hp, dev))
+    pair = svdq.MlpPair(*lays)
+    X = torch.from_numpy(d.fc1.X.view(np.int16)).to(dev).view(torch.bfloat16)
+    Y = torch.empty((M, d.fc2.N), dtype=torch.float32, device=dev)
+    wsc, wss = pair.workspace(M, svdq.MLP_CHAINED), pair.workspace(M, svdq.MLP_SEPARATE)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < warm_s:
+        for _ in range(5):
+            pair.forward(X, svdq.F32, Y, wsc, svdq.MLP_CHAINED)
+            pair.forward(X, svdq.F32, Y, wss, svdq.MLP_SEPARATE)
+        torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    tc, ts = [], []
+    for _ in range(max(steps // 20, 3)):
+        for mode, ws, out in ((svdq.MLP_CHAINED, wsc, tc), (svdq.MLP_SEPARATE, wss, ts)):
+            ev0.record()
+            for _ in range(20):
+                pair.forward(X, svdq.F32, Y, ws, mode)
+            ev1.record()
+            torch.cuda.synchronize()
+            out.append(ev0.elapsed_time(ev1) / 20)
+    # the chained path's kernels one by one
+    fc1, fc2 = pair.fc1, pair.fc2
+    a1 = fc1.alloc_act(M, svdq.ACT_MMA)
+    qX2, sX2, la2 = fc2.alloc_act(M, svdq.ACT_MMA)
+    part = torch.empty(((fc2.K // 128) * M * svdq.r16(fc2.rank),), dtype=torch.float32, device=dev)
+    gws = fc2.gemm_workspace(M, svdq.ACT_MMA)
+    nrep = 20
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(5 * nrep)]
+    for i in range(nrep):
+        e[5 * i].record()
+        fc1.quantize_act(X, a1, form=svdq.ACT_MMA)
+        e[5 * i + 1].record()
+        pair.chain_gemm(*a1, M, out=(qX2, sX2, part, None))
+        e[5 * i + 2].record()
+        pair.chain_reduce(part, M, out=la2)
+        e[5 * i + 3].record()
+        fc2.gemm(qX2, sX2, la2, svdq.F32, out=Y, form=svdq.ACT_MMA, workspace=gws)
+        e[5 * i + 4].record()
+    torch.cuda.synchronize()
+    us = [float(np.median([e[5 * i + k].elapsed_time(e[5 * i + k + 1]) for i in range(nrep)])) * 1e3 for k in range(4)]
+    ms_c, ms_s = float(np.median(tc)), float(np.median(ts))
+    ops = sum(2.0 * M * l.N * l.K + 2.0 * M * l.rank * (l.K + l.N) for l in (fc1, fc2))
+    log(f"[bench] [mlp] chained {ms_c:.4f} ms, separate {ms_s:.4f} ms")
+    return {"workload": "FLUX.1 MLP pair, chained (fc1 -> GELU -> fc2)", "M": M, "K1": fc1.K, "N1": fc1.N,
+            "N2": fc2.N, "rank": [fc1.rank, fc2.rank], "chained_ms": round(ms_c, 5), "separate_ms": round(ms_s, 5),
+            "chained_TOPS": round(ops / (ms_c * 1e-3) / 1e12, 2), "separate_TOPS": round(ops / (ms_s * 1e-3) / 1e12, 2),
+            "chained_speedup": round(ms_s / ms_c, 4),
+            "chained_kernels_us": {"fc1_k1": round(us[0], 2), "fc1_k2_chained": round(us[1], 2),
+                                   "lora_partials_sum": round(us[2], 2), "fc2_k2": round(us[3], 2)}}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -335,7 +401,8 @@ def main():
                     help="skip the rank-0 and unfused comparison forwards (counter runs: only the "
                          "timed layer's kernels are dispatched)")
     ap.add_argument("--no-others", action="store_true",
-                    help="skip the other FLUX workloads (MLP fc1, fc2, MXFP4, batch 2 + LoRA)")
+                    help="skip the other FLUX workloads (MLP fc1, fc2, MXFP4, batch 2 + LoRA, the chained "
+                         "MLP pair)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after timing, run one plain device copy of 512 MiB (counter calibration)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -399,6 +466,7 @@ def main():
             del o
             torch.cuda.empty_cache()
         out["workloads"] = others
+        out["mlp_pair"] = measure_mlp(svdq, torch, 100, 0.2)
     if args.calib_copy:
         src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device="cuda:0")
         dst = torch.empty_like(src)

@@ -111,7 +111,8 @@ static svdq_status run_k2(const svdq_layer* layer, int64_t M, int32_t form, cons
   if ((st = check_form(form)) != SVDQ_OK) return st;
   if (M < 0) return fail(SVDQ_EINVAL, "M must be >= 0");
   if (M == 0) return ok();
-  if (ydtype != SVDQ_F32 && ydtype != SVDQ_BF16) return fail(SVDQ_EUNSUPPORTED, "unsupported output dtype %d", (int)ydtype);
+  if (ydtype != SVDQ_F32 && ydtype != SVDQ_BF16 && ydtype != SVDQ_BF16_GELU)
+    return fail(SVDQ_EUNSUPPORTED, "unsupported output dtype %d", (int)ydtype);
   if (kl.fmt == SVDQ_NVFP4_G16 && form != SVDQ_ACT_MMA)
     return fail(SVDQ_EUNSUPPORTED, "NVFP4 kernel 2 runs on the MMA activation form only");
   if (!qX || !sX || !Y) return fail(SVDQ_EINVAL, "qX, sX and Y must be non-NULL");
@@ -183,6 +184,8 @@ svdq_status svdq_linear_forward_unfused(const svdq_layer* layer, int64_t M, cons
   if (st != SVDQ_OK) return st;
   if (M < 0) return fail(SVDQ_EINVAL, "M must be >= 0");
   if (M == 0) return ok();
+  // the separate up projection adds to Y, which an activation on the output would break
+  if (ydtype == SVDQ_BF16_GELU) return fail(SVDQ_EUNSUPPORTED, "the unfused forward has no GELU output");
   const WsLayout w = ws_layout(layer, M);
   if (!workspace || ws_bytes < w.total) return fail(SVDQ_EINVAL, "workspace too small: need %zu bytes", w.total);
   if (!aligned(workspace, 256)) return fail(SVDQ_EINVAL, "workspace must be 256-byte aligned");
@@ -219,6 +222,142 @@ svdq_status svdq_debug_group_sums(const svdq_layer* layer, int64_t M, int32_t fo
   if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
   if (e != hipSuccess) return fail(SVDQ_EHIP, "group-sum kernel: %s", hipGetErrorString(e));
   return ok();
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------------------
+// The chained MLP pair (fc1, GELU, fc2)
+
+namespace svdq {
+
+static svdq_status check_pair(const svdq_layer* fc1, const svdq_layer* fc2, KernelLayer& k1, KernelLayer& k2,
+                              bool chained) {
+  svdq_status st = check_layer(fc1, k1);
+  if (st != SVDQ_OK) return st;
+  if ((st = check_layer(fc2, k2)) != SVDQ_OK) return st;
+  if (k1.N != k2.K) return fail(SVDQ_EINVAL, "fc1's N (%lld) must equal fc2's K (%lld)", (long long)k1.N, (long long)k2.K);
+  if (chained && (k1.fmt != SVDQ_INT4_G64 || k2.fmt != SVDQ_INT4_G64))
+    return fail(SVDQ_EUNSUPPORTED, "the chained MLP pair runs INT4 layers");
+  return SVDQ_OK;
+}
+
+static size_t part_bytes(const svdq_layer* fc1, const svdq_layer* fc2, int64_t M) {
+  return (size_t)(fc1->N / 128) * (size_t)M * (size_t)((fc2->rank + 15) / 16 * 16) * sizeof(float);
+}
+
+struct MlpLayout {
+  WsLayout w1, w2;
+  size_t a1, part, g, fw, total;
+};
+// chained: [fc2's forward workspace: its activation side, then its kernel 2's partial
+// tiles] [fc1's activation side] [the down-projection partials]; separate: [G bf16
+// M x N1] [one forward workspace, fc1's then fc2's]
+static MlpLayout mlp_layout(const svdq_layer* fc1, const svdq_layer* fc2, int64_t M, int32_t mode) {
+  MlpLayout L{};
+  L.w1 = ws_layout(fc1, M);
+  L.w2 = ws_layout(fc2, M);
+  if (mode == SVDQ_MLP_CHAINED) {
+    L.a1 = L.w2.total;
+    L.part = L.a1 + rup(L.w1.part);
+    L.total = L.part + rup(part_bytes(fc1, fc2, M));
+  } else {
+    L.g = 0;
+    L.fw = rup((size_t)M * (size_t)fc1->N * 2);
+    L.total = L.fw + (L.w1.total > L.w2.total ? L.w1.total : L.w2.total);
+  }
+  return L;
+}
+
+static svdq_status run_chain_gemm(const svdq_layer* fc1, const svdq_layer* fc2, int64_t M, const uint8_t* qX,
+                                  const void* sX, const void* lora_act, uint8_t* qX2, void* sX2, float* lora_part,
+                                  uint16_t* hidden, int64_t ldh, void* stream) {
+  KernelLayer k1, k2;
+  svdq_status st = check_pair(fc1, fc2, k1, k2, true);
+  if (st != SVDQ_OK) return st;
+  if (M < 0) return fail(SVDQ_EINVAL, "M must be >= 0");
+  if (M == 0) return ok();
+  if (!qX || !sX || !qX2 || !sX2) return fail(SVDQ_EINVAL, "qX, sX, qX2 and sX2 must be non-NULL");
+  if (k1.rank > 0 && !lora_act) return fail(SVDQ_EINVAL, "lora_act must be non-NULL when fc1's rank > 0");
+  if (k2.rank > 0 && !lora_part) return fail(SVDQ_EINVAL, "lora_part must be non-NULL when fc2's rank > 0");
+  if (hidden && (ldh < k1.N || !aligned(hidden, 2))) return fail(SVDQ_EINVAL, "hidden needs ldh >= fc1's N");
+  if (!aligned(qX, 16) || !aligned(qX2, 16) || !aligned(sX, 2) || !aligned(sX2, 2) ||
+      (lora_act && !aligned(lora_act, 16)) || (lora_part && !aligned(lora_part, 16)))
+    return fail(SVDQ_EINVAL, "qX, qX2, lora_act and lora_part must be 16-byte aligned");
+  hipError_t e = launch_k2_chain(k1, k2, M, qX, sX, lora_act, qX2, sX2, lora_part, hidden, ldh, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(SVDQ_EHIP, "chained kernel 2 launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+static svdq_status run_chain_reduce(const svdq_layer* fc1, const svdq_layer* fc2, int64_t M, const float* lora_part,
+                                    void* lora_act2, void* stream) {
+  KernelLayer k1, k2;
+  svdq_status st = check_pair(fc1, fc2, k1, k2, true);
+  if (st != SVDQ_OK) return st;
+  if (M < 0) return fail(SVDQ_EINVAL, "M must be >= 0");
+  if (M == 0 || k2.rank == 0) return ok();
+  if (!lora_part || !lora_act2) return fail(SVDQ_EINVAL, "lora_part and lora_act2 must be non-NULL");
+  if (!aligned(lora_act2, 16)) return fail(SVDQ_EINVAL, "lora_act2 must be 16-byte aligned");
+  hipError_t e = launch_lora_reduce(k1, k2, M, lora_part, lora_act2, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(SVDQ_EHIP, "partial-sum launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace svdq
+
+extern "C" {
+
+svdq_status svdq_mlp_chain_gemm(const svdq_layer* fc1, const svdq_layer* fc2, int64_t M, const uint8_t* qX,
+                                const void* sX, const void* lora_act, uint8_t* qX2, void* sX2, float* lora_part,
+                                uint16_t* hidden, int64_t ldh, void* stream) {
+  return run_chain_gemm(fc1, fc2, M, qX, sX, lora_act, qX2, sX2, lora_part, hidden, ldh, stream);
+}
+
+svdq_status svdq_mlp_chain_reduce(const svdq_layer* fc1, const svdq_layer* fc2, int64_t M, const float* lora_part,
+                                  void* lora_act2, void* stream) {
+  return run_chain_reduce(fc1, fc2, M, lora_part, lora_act2, stream);
+}
+
+size_t svdq_mlp_workspace_bytes(const svdq_layer* fc1, const svdq_layer* fc2, int64_t M, int32_t mode) {
+  if (!fc1 || !fc2 || M < 0 || (mode != SVDQ_MLP_CHAINED && mode != SVDQ_MLP_SEPARATE)) return 0;
+  if (check_dims(fc1->K, fc1->N, fc1->fmt) != SVDQ_OK || check_dims(fc2->K, fc2->N, fc2->fmt) != SVDQ_OK) return 0;
+  return mlp_layout(fc1, fc2, M, mode).total;
+}
+
+svdq_status svdq_mlp_forward(const svdq_layer* fc1, const svdq_layer* fc2, int64_t M, const uint16_t* X,
+                             int64_t ldx, void* Y, int64_t ldy, int32_t ydtype, int32_t mode, void* workspace,
+                             size_t ws_bytes, void* stream) {
+  if (mode != SVDQ_MLP_CHAINED && mode != SVDQ_MLP_SEPARATE) return fail(SVDQ_EUNSUPPORTED, "unknown MLP mode %d", (int)mode);
+  KernelLayer k1, k2;
+  svdq_status st = check_pair(fc1, fc2, k1, k2, mode == SVDQ_MLP_CHAINED);
+  if (st != SVDQ_OK) return st;
+  if (M < 0) return fail(SVDQ_EINVAL, "M must be >= 0");
+  if (M == 0) return ok();
+  const MlpLayout L = mlp_layout(fc1, fc2, M, mode);
+  if (!workspace || ws_bytes < L.total) return fail(SVDQ_EINVAL, "workspace too small: need %zu bytes", L.total);
+  if (!aligned(workspace, 256)) return fail(SVDQ_EINVAL, "workspace must be 256-byte aligned");
+  uint8_t* base = static_cast<uint8_t*>(workspace);
+  if (mode == SVDQ_MLP_SEPARATE) {
+    uint16_t* G = reinterpret_cast<uint16_t*>(base + L.g);
+    st = svdq::linear_forward(fc1, M, X, ldx, G, k1.N, SVDQ_BF16_GELU, base + L.fw, L.total - L.fw, stream);
+    if (st != SVDQ_OK) return st;
+    return svdq::linear_forward(fc2, M, G, k1.N, Y, ldy, ydtype, base + L.fw, L.total - L.fw, stream);
+  }
+  uint8_t* a1 = base + L.a1;
+  uint8_t* qX1 = a1 + L.w1.qx;
+  void* sX1 = a1 + L.w1.sx;
+  void* la1 = k1.rank > 0 ? a1 + L.w1.la : nullptr;
+  uint8_t* qX2 = base + L.w2.qx;
+  void* sX2 = base + L.w2.sx;
+  void* la2 = k2.rank > 0 ? base + L.w2.la : nullptr;
+  float* part = k2.rank > 0 ? reinterpret_cast<float*>(base + L.part) : nullptr;
+  st = run_k1(fc1, M, X, ldx, SVDQ_ACT_MMA, qX1, sX1, la1, stream);
+  if (st != SVDQ_OK) return st;
+  st = run_chain_gemm(fc1, fc2, M, qX1, sX1, la1, qX2, sX2, part, nullptr, 0, stream);
+  if (st != SVDQ_OK) return st;
+  st = run_chain_reduce(fc1, fc2, M, part, la2, stream);
+  if (st != SVDQ_OK) return st;
+  return run_k2(fc2, M, SVDQ_ACT_MMA, qX2, sX2, la2, Y, ldy, ydtype, base + L.w2.part, L.w2.total - L.w2.part, stream);
 }
 
 }  // extern "C"

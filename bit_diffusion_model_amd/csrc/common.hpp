@@ -26,6 +26,18 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// An empty asm statement that reads v: v stays live (in its registers) up to this point.
+// Used after v_cvt_scalef32_2xpk16_fp6_f32, whose six result registers must not overlap
+// its 32 source registers: measured on gfx950, a result register allocated on top of a
+// source register at a higher position than its own is written before that source is
+// read (the instruction converts in passes), corrupting the codes that source carries.
+// The compiler does not mark the result early-clobber, so keeping the sources live past
+// the instruction is what keeps the allocator from overlapping them.
+template <typename T>
+__device__ __forceinline__ void keep_live(const T& v) {
+  asm volatile("" ::"v"(v));
+}
+
 // Expand 8 sign-magnitude 4-bit codes (one dword, element 2j in the low nibble of
 // byte j) into 8 FP8 E4M3 bytes whose value is q * 2^-9: with a zero exponent field
 // the E4M3 mantissa bits hold |q| directly (subnormal), and bit 7 is the sign.
@@ -68,7 +80,10 @@ __device__ __forceinline__ v6i nib32_to_fp6(uint4 d) {
       else x1[8 * (i - 2) + j] = v[j];
     }
   }
-  return __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(x0, x1, 0x1p-6f);
+  const v6i r = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(x0, x1, 0x1p-6f);
+  keep_live(x0);
+  keep_live(x1);
+  return r;
 }
 
 // Eight E2M1 codes (one dword, code 2j in the low nibble of byte j) times a group scale
@@ -85,6 +100,30 @@ __device__ __forceinline__ v8h nv_f16x8(uint32_t w, float s) {
   const h2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s, 2) * rr;
   const h2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s, 3) * rr;
   return v8h{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+}
+
+// GELU in its exact form, x Phi(x) with Phi(x) = erfc(-x / sqrt 2) / 2, in fp32.  erfc(z)
+// for z >= 0 by the Chebyshev fit of Numerical Recipes (Press et al., "Incomplete gamma
+// function, error function", routine erfcc; fractional error below 1.2e-7 for z >= 0):
+// erfc(z) = t exp(-z^2 + P(t)), t = 1 / (1 + z / 2), P a degree-9 polynomial; for x >= 0,
+// Phi(x) = 1 - erfc(x / sqrt 2) / 2.  Evaluated in fp32 the relative error of GELU stays
+// below 1e-5 (the exponential's argument reaches -z^2), far inside the bf16 rounding that
+// follows; the tail keeps its relative accuracy (no 1 + erf cancellation).
+__device__ __forceinline__ float gelu_erf(float x) {
+  const float z = fabsf(x) * 0.70710678118654752f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.5f, z, 1.0f));
+  float p = 0.17087277f;
+  p = fmaf(p, t, -0.82215223f);
+  p = fmaf(p, t, 1.48851587f);
+  p = fmaf(p, t, -1.13520398f);
+  p = fmaf(p, t, 0.27886807f);
+  p = fmaf(p, t, -0.18628806f);
+  p = fmaf(p, t, 0.09678418f);
+  p = fmaf(p, t, 0.37409196f);
+  p = fmaf(p, t, 1.00002368f);
+  p = fmaf(p, t, -1.26551223f);
+  const float h = 0.5f * t * __expf(fmaf(-z, z, p));  // erfc(|x| / sqrt 2) / 2
+  return x * (x >= 0.0f ? 1.0f - h : h);
 }
 
 // Raw buffer resource over `bytes` bytes at p: loads beyond the range return zeros.

@@ -61,6 +61,7 @@ __device__ __forceinline__ uint4 int4_mma_words(const float (&t)[16], int sub) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) tc[i] = __builtin_amdgcn_fmed3f(t[i], -7.0f, 7.0f);
   const v6i f6 = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(tc, tc, 8.0f);
+  keep_live(tc);
   // bits of the even fields (field 2i at bit 12 i) in words d and d + 3
   constexpr uint32_t EV[3] = {0x3F03F03Fu, 0xF03F03F0u, 0x03F03F03u};
   uint32_t fw[3];

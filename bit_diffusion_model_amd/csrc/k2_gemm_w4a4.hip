@@ -46,6 +46,7 @@
 #include <type_traits>
 
 #include "common.hpp"
+#include "k1_parts.hpp"
 #include "kernels.hpp"
 
 namespace svdq {
@@ -72,8 +73,8 @@ struct Smem {
 };
 
 // Store one 32 x 32 accumulator (rows r_off.., columns c_off.. of the tile at m0, n0)
-// to Y through a resource over the tile's rows: rows past the end fall outside the range
-// and are dropped; columns past N are masked (they may be the caller's row padding).
+// to Y (ydtype 0: fp32, 1: bf16, 2: bf16 of GELU(y)) through a resource over the
+// tile's rows: rows past the end fall outside the range and are dropped; columns past N are masked (they may be the caller's row padding).
 // The host guarantees (tile rows) * ldy * (element size) < 2^32 for every tile shape
 // (ldy < 2^22 elements).
 __device__ __forceinline__ void store_sub(const v16f& acc, void* Y, int64_t ldy, int ydtype, int64_t m0,
@@ -90,10 +91,14 @@ __device__ __forceinline__ void store_sub(const v16f& acc, void* Y, int64_t ldy,
 #pragma unroll
     for (int a = 0; a < 16; ++a)
       buf_store4(__float_as_uint(acc[a]), rY, o + (uint32_t)(8 * (a >> 2) + (a & 3)) * ystep);
-  } else {
+  } else if (ydtype == 1) {
 #pragma unroll
     for (int a = 0; a < 16; ++a)
       buf_store2((uint16_t)f32_to_bf16_rne(acc[a]), rY, o + (uint32_t)(8 * (a >> 2) + (a & 3)) * ystep);
+  } else {  // bf16 of GELU(y)
+#pragma unroll
+    for (int a = 0; a < 16; ++a)
+      buf_store2((uint16_t)f32_to_bf16_rne(gelu_erf(acc[a])), rY, o + (uint32_t)(8 * (a >> 2) + (a & 3)) * ystep);
   }
 }
 
@@ -500,13 +505,131 @@ struct K2Debug {
   int64_t m0, n0, mt, nt;
 };
 
-template <int FMT, bool DEBUG = false>
+// The chained MLP pair: the CHAIN instance (INT4 fc1, whole tiles) turns its finished
+// 128 x 128 tile H into fc2's activation side instead of storing it: G = bf16(GELU(H))
+// through LDS, then kernel 1's steps on G (smoothing by fc2's 1 / s, INT4 group-64 codes
+// and fp16 scales in the MMA form, down projection by fc2's L1).  The tile holds 128 of
+// fc2's input channels, two whole groups of every row, so the per-token group scales are
+// complete; the down projection over these 128 channels is a partial sum, stored per
+// column tile and summed over the tiles in a fixed order by k2_lora_reduce.
+struct K2Chain {
+  uint8_t* qX2;           // fc2 codes, MMA form [M][K2] (K2 = fc1's N)
+  uint16_t* sX2;          // fc2 fp16 scales [K2 / 64][Mp]
+  float* part;            // down-projection partials [K2 / 128][M][16 nt2]
+  const float* inv_s2;    // fc2 1 / s [K2]
+  const uint16_t* L1f2;   // fc2 L1 in kernel 1's fragment order
+  int nt2;                // fc2 rank tiles of 16
+  uint16_t* hidden;       // optional copy of G, bf16 [M][ldh] (NULL: not written)
+  int64_t ldh;
+};
+
+// Rows of a 64-channel half of the G tile in LDS: 128 bytes + 16, so the 16 rows read by
+// one 16-lane pass of a ds_read_b128 start 4 banks apart (36 r mod 64 for rows r = 0..15:
+// distinct multiples of 4).
+constexpr int GPITCH = 144;
+
+// The CHAIN instance's epilogue (see K2Chain).  acc: the INT4 wave tile (four 32 x 32
+// tiles, rows 0..127 of the block, columns wn..wn+31), the finished H including fc1's
+// low-rank term.  Steps:
+//  1. G = bf16(GELU(H)), rows past M as 0, into LDS (channels 0-63 of the tile in lds0,
+//     64-127 in lds1, GPITCH bytes per row), and into `hidden` when it is given;
+//  2. wave w takes the tile's tokens 32 w .. 32 w + 31 as two blocks of 16, in kernel 1's
+//     lane layout (lane l: token l & 15, channels 16 (l >> 4) .. +15 of a group), reads
+//     G, smooths it by fc2's 1 / s, and runs kernel 1's INT4 quantizer and MMA-form word
+//     builder and its bf16 hi / lo down projection;
+//  3. the down projection over the tile's 128 channels goes to part[tile column][token]
+//     (one 16-column rank tile at a time, so any fc2 rank runs in one instance).
+__device__ __forceinline__ void chain_epilogue(const v16f (&acc)[4][1], const K2Chain& ch, int64_t M, int64_t K2,
+                                               int64_t m0, int64_t n0, int64_t rowsA, uint8_t* lds0, uint8_t* lds1,
+                                               int wave, int lane, int wn, int l32, int kh, uint32_t Mp) {
+  // every wave has finished its reads of the last stage, and its own loads have landed
+  __syncthreads();
+  uint8_t* gw = wave < 2 ? lds0 : lds1;
+  const int cc = (wn & 63) + l32;
+  const bool dump = ch.hidden != nullptr;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int a = 0; a < 16; ++a) {
+      const int r = i * 32 + 8 * (a >> 2) + 4 * kh + (a & 3);
+      uint32_t b = f32_to_bf16_rne(gelu_erf(acc[i][0][a]));
+      if (r >= rowsA) b = 0u;
+      *reinterpret_cast<uint16_t*>(gw + r * GPITCH + cc * 2) = (uint16_t)b;
+      if (dump && r < rowsA) ch.hidden[(m0 + r) * ch.ldh + n0 + wn + l32] = (uint16_t)b;
+    }
+  __syncthreads();
+
+  const int r16 = lane & 15, sub = lane >> 4;
+  const int64_t c0 = n0 >> 6;  // fc2's group (chunk) index of the tile's first half
+  const __amdgpu_buffer_rsrc_t rI = make_rsrc(ch.inv_s2 + n0, 128u * 4u);
+  float is[2][16];
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 v = buf_load16(rI, (uint32_t)((g * 64 + sub * 16 + 4 * q) * 4));
+      is[g][4 * q] = __uint_as_float(v.x);
+      is[g][4 * q + 1] = __uint_as_float(v.y);
+      is[g][4 * q + 2] = __uint_as_float(v.z);
+      is[g][4 * q + 3] = __uint_as_float(v.w);
+    }
+  const int nt2 = ch.nt2;
+  const int64_t R16 = 16 * (int64_t)nt2;
+  const __amdgpu_buffer_rsrc_t rL = make_rsrc(ch.L1f2, (uint32_t)(R16 * K2 * 2));
+  float* part = ch.part + ((n0 >> 7) * M + m0) * R16;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int tb = (2 * wave + b) * 16;  // the token block's first row in the tile
+    const int tr = tb + r16;
+    const int64_t row = m0 + tr;
+    float xh[2][16];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const uint8_t* src = (g ? lds1 : lds0) + tr * GPITCH + sub * 32;
+      const uint4 p0 = *reinterpret_cast<const uint4*>(src), p1 = *reinterpret_cast<const uint4*>(src + 16);
+      const uint32_t w[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        xh[g][2 * j] = bf16_lo_to_f32(w[j]) * is[g][2 * j];
+        xh[g][2 * j + 1] = bf16_hi_to_f32(w[j]) * is[g][2 * j + 1];
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      float t[16];
+      const _Float16 sh = int4_quantize16(xh[g], t);
+      const uint4 mw = int4_mma_words(t, sub);  // every lane takes part in the swaps
+      if (tr < rowsA) {
+        *reinterpret_cast<uint4*>(ch.qX2 + row * K2 + n0 + g * 64 + sub * 16) = mw;
+        if (sub == 0) ch.sX2[(c0 + g) * (int64_t)Mp + row] = __builtin_bit_cast(uint16_t, sh);
+      }
+    }
+    for (int t = 0; t < nt2; ++t) {
+      v4f la[1] = {v4f{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const uint32_t o = (uint32_t)((((c0 + g) * nt2 + t) * 64 + lane) * 32);
+        const uint4 LA[1] = {buf_load16(rL, o)}, LB[1] = {buf_load16(rL, o + 16)};
+        lora_down16<1>(la, xh[g], LA, LB);
+      }
+      // the 16 x 16 result: lane l holds rank column 16 t + (l & 15), rows 4 (l >> 4) + i
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rr = tb + 4 * sub + i;
+        if (rr < rowsA) part[rr * R16 + 16 * t + r16] = la[0][i];
+      }
+    }
+  }
+}
+
+template <int FMT, bool DEBUG = false, bool CHAIN = false>
 __global__ __launch_bounds__(SShape<FMT>::NT, 8 / SShape<FMT>::NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void k2_stream(
     const uint8_t* __restrict__ qX, const uint8_t* __restrict__ sX, int64_t M,
     const uint8_t* __restrict__ qW, const uint8_t* __restrict__ sW, int64_t N, int64_t K,
     const uint16_t* __restrict__ lora_act, const uint16_t* __restrict__ L2, int rank,
-    void* __restrict__ Y, int64_t ldy, int ydtype, K2Sched sch, K2Debug dbg, float sxw) {
+    void* __restrict__ Y, int64_t ldy, int ydtype, K2Sched sch, K2Debug dbg, float sxw, K2Chain ch) {
   static_assert(!DEBUG || FMT == 0, "group sums are defined for INT4");
+  static_assert(!CHAIN || (FMT == 0 && !DEBUG), "the chained epilogue follows the INT4 layer");
   // NVFP4: sxw = fp32(S_X S_W), the product of the two tensor scales
   using D = DLay<FMT>;
   using SH = SShape<FMT>;
@@ -843,6 +966,10 @@ __global__ __launch_bounds__(SShape<FMT>::NT, 8 / SShape<FMT>::NW) __attribute__
   if (nk % 3 == 2) stage(k + 1, lds1, lds0);
   wait_cnt<0, 0>();
   if constexpr (DEBUG) return;
+  if constexpr (CHAIN) {
+    chain_epilogue(acc, ch, M, N, m0, n0, rowsA, lds0, lds1, wave, lane, wn, l32, kh, Mp);
+    return;
+  }
   if constexpr (FMT == 2) {
 #pragma unroll
     for (int i = 0; i < TI; ++i)
@@ -898,6 +1025,23 @@ __global__ __launch_bounds__(64) void k2_fixup(const float* __restrict__ partial
   }
   const int64_t rowsA = M - m0 < TBM ? M - m0 : TBM;
   store_sub(acc, Y, ldy, ydtype, m0, n0, rowsA, N, (int)(sub / CB) * 32, (int)(sub % CB) * 32, lane & 31, lane >> 5);
+}
+
+// Sum of the chained epilogue's per-column-tile partials of the down projection, in tile
+// order (the result does not depend on which tile finished first), stored in the MMA form
+// of lora_act (bf16 hi / lo pairs in fragment order) for fc2's kernel 2.  One thread per
+// (token, rank column).
+__global__ __launch_bounds__(256) void k2_lora_reduce(const float* __restrict__ part, int ntiles, int64_t M, int R16,
+                                                      uint16_t* __restrict__ la) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t total = M * R16;
+  if (idx >= total) return;
+  const int64_t m = idx / R16;
+  const int j = (int)(idx - m * R16);
+  float v = part[idx];
+#pragma unroll 8
+  for (int t = 1; t < ntiles; ++t) v += part[(int64_t)t * total + idx];
+  store_lora_mma(la, m, j, R16 >> 4, v);
 }
 
 }  // namespace
@@ -1001,7 +1145,7 @@ hipError_t launch_k2(const KernelLayer& L, int64_t M, const uint8_t* qX, const v
 #define K2_STREAM(F)                                                                                        \
   hipLaunchKernelGGL((k2_stream<F>), dim3(nblocks), dim3(SShape<F>::NT), 0, st, qX, static_cast<const uint8_t*>(sX), M, \
                      L.qW, static_cast<const uint8_t*>(L.sW), L.N, L.K, static_cast<const uint16_t*>(lora_act),   \
-                     L.L2f, L.rank, Y, ldy, ydtype, sch, K2Debug{}, L.tscale_x * L.tscale_w)
+                     L.L2f, L.rank, Y, ldy, ydtype, sch, K2Debug{}, L.tscale_x * L.tscale_w, K2Chain{})
   const int sub = sub_of(L.K);
   if (mma) {  // the activation side in MMA form: streamed kernel (K % 128 == 0: two sub-steps per stage)
     if (L.fmt == 0) K2_STREAM(0);
@@ -1033,6 +1177,31 @@ hipError_t launch_k2(const KernelLayer& L, int64_t M, const uint8_t* qX, const v
   return hipGetLastError();
 }
 
+hipError_t launch_k2_chain(const KernelLayer& L1, const KernelLayer& L2, int64_t M, const uint8_t* qX, const void* sX,
+                           const void* lora_act, uint8_t* qX2, void* sX2, float* part, uint16_t* hidden, int64_t ldh,
+                           hipStream_t st) {
+  // whole tiles only (the epilogue needs the finished tile): no K split
+  const uint32_t tiles_m = (uint32_t)((M + SShape<0>::BM - 1) / SShape<0>::BM);
+  const uint32_t tiles_n = (uint32_t)(L1.N / SShape<0>::BN);
+  const K2Sched sch{tiles_n, tiles_m * tiles_n, 1, nullptr};
+  const K2Chain ch{qX2, static_cast<uint16_t*>(sX2), part, L2.inv_s, L2.L1f, (L2.rank + 15) / 16, hidden, ldh};
+  hipLaunchKernelGGL((k2_stream<0, false, true>), dim3(tiles_m * tiles_n), dim3(SShape<0>::NT), 0, st, qX,
+                     static_cast<const uint8_t*>(sX), M, L1.qW, static_cast<const uint8_t*>(L1.sW), L1.N, L1.K,
+                     static_cast<const uint16_t*>(lora_act), L1.L2f, L1.rank, (void*)nullptr, (int64_t)0, 0, sch,
+                     K2Debug{}, 1.0f, ch);
+  return hipGetLastError();
+}
+
+hipError_t launch_lora_reduce(const KernelLayer& L1, const KernelLayer& L2, int64_t M, const float* part, void* la2,
+                              hipStream_t st) {
+  const int R16 = (L2.rank + 15) / 16 * 16;
+  if (R16 == 0 || M == 0) return hipSuccess;
+  const int64_t n = M * R16;
+  hipLaunchKernelGGL(k2_lora_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, part,
+                     (int)(L1.N / SShape<0>::BN), M, R16, static_cast<uint16_t*>(la2));
+  return hipGetLastError();
+}
+
 hipError_t launch_k2_debug(const KernelLayer& L, int64_t M, const uint8_t* qX, bool mma, int64_t m0,
                            int64_t n0, int64_t mt, int64_t nt, int32_t* out, hipStream_t st) {
   if (mma) {
@@ -1044,7 +1213,8 @@ hipError_t launch_k2_debug(const KernelLayer& L, int64_t M, const uint8_t* qX, b
     const K2Sched sch{p.tiles_n, p.full, p.split, nullptr};
     hipLaunchKernelGGL((k2_stream<0, true>), dim3(p.full + rem * p.split), dim3(SShape<0>::NT), 0, st, qX,
                        (const uint8_t*)nullptr, M, L.qW, (const uint8_t*)nullptr, L.N, L.K, (const uint16_t*)nullptr,
-                       (const uint16_t*)nullptr, 0, (void*)nullptr, (int64_t)0, 0, sch, K2Debug{out, m0, n0, mt, nt}, 1.0f);
+                       (const uint16_t*)nullptr, 0, (void*)nullptr, (int64_t)0, 0, sch, K2Debug{out, m0, n0, mt, nt}, 1.0f,
+                       K2Chain{});
     return hipGetLastError();
   }
   const uint32_t tn = (uint32_t)((nt + BN - 1) / BN), tm = (uint32_t)((mt + BM - 1) / BM);

@@ -39,11 +39,22 @@ struct K2Plan {
 };
 K2Plan plan_k2(const KernelLayer& L, int64_t M, bool mma);
 
-// ydtype: 0 fp32, 1 bf16.  mma: as for launch_k1.  workspace (device, may be NULL): used
+// ydtype: 0 fp32, 1 bf16, 2 bf16 of GELU(y).  mma: as for launch_k1.  workspace (device, may be NULL): used
 // for the split when it holds plan_k2's bytes; otherwise every tile is computed whole.
 hipError_t launch_k2(const KernelLayer& L, int64_t M, const uint8_t* qX, const void* sX,
                      const void* lora_act, void* Y, int64_t ldy, int ydtype, bool mma,
                      void* workspace, size_t ws_bytes, hipStream_t st);
+
+// The chained MLP pair, INT4: fc1's kernel 2 (MMA activation form, whole tiles) with
+// fc2's kernel 1 in its epilogue.  Writes fc2's MMA-form codes qX2 [M][K2] and fp16
+// scales sX2 [K2/64][Mp], the down-projection partials part [K2/128][M][R16(fc2)] and,
+// when hidden is non-NULL, G = bf16(GELU(H)) [M][ldh].  K2 = L1.N = L2.K.
+hipError_t launch_k2_chain(const KernelLayer& L1, const KernelLayer& L2, int64_t M, const uint8_t* qX, const void* sX,
+                           const void* lora_act, uint8_t* qX2, void* sX2, float* part, uint16_t* hidden, int64_t ldh,
+                           hipStream_t st);
+// fc2's lora_act (MMA form) = the sum of the partials over the K2/128 column tiles, in order.
+hipError_t launch_lora_reduce(const KernelLayer& L1, const KernelLayer& L2, int64_t M, const float* part, void* la2,
+                              hipStream_t st);
 
 // Exact INT4 group sums of a window.  mma: the forward's streamed kernel on MMA-form
 // codes (its own schedule); otherwise the packed-form kernel.

@@ -19,7 +19,8 @@ LIB_PATH = os.path.join(_HERE, "libsvdq.so")
 
 INT4_G64, MXFP4_G32, NVFP4_G16 = 0, 1, 2
 ACT_PACKED, ACT_MMA = 0, 1  # svdq_act_form
-F32, BF16 = 0, 1
+F32, BF16, BF16_GELU = 0, 1, 2  # svdq_dtype (BF16_GELU: bf16 of GELU(y))
+MLP_CHAINED, MLP_SEPARATE = 0, 1  # svdq_mlp_mode
 FMT = {"int4": INT4_G64, "mxfp4": MXFP4_G32, "nvfp4": NVFP4_G16}
 GROUP = {INT4_G64: 64, MXFP4_G32: 32, NVFP4_G16: 16}
 MAX_RANK = 128
@@ -45,6 +46,7 @@ EXPORTS = [
     "svdq_prepare_weights",
     "svdq_quantize_act_lora_down", "svdq_gemm_w4a4_lora_up", "svdq_gemm_workspace_bytes", "svdq_workspace_bytes",
     "svdq_linear_forward", "svdq_linear_forward_unfused", "svdq_debug_group_sums", "svdq_linear_forward_noalloc",
+    "svdq_mlp_workspace_bytes", "svdq_mlp_forward", "svdq_mlp_chain_gemm", "svdq_mlp_chain_reduce",
 ]
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
@@ -77,6 +79,10 @@ def lib():
         "svdq_linear_forward_unfused": (I32, [P, I64, P, I64, P, I64, I32, P, ctypes.c_size_t, P]),
         "svdq_debug_group_sums": (I32, [P, I64, I32, P, I64, I64, I64, I64, P, P]),
         "svdq_linear_forward_noalloc": (I32, [P, I64, P, I64, P, I64, I32, P]),
+        "svdq_mlp_workspace_bytes": (ctypes.c_size_t, [P, P, I64, I32]),
+        "svdq_mlp_forward": (I32, [P, P, I64, P, I64, P, I64, I32, I32, P, ctypes.c_size_t, P]),
+        "svdq_mlp_chain_gemm": (I32, [P, P, I64, P, P, P, P, P, P, P, I64, P]),
+        "svdq_mlp_chain_reduce": (I32, [P, P, I64, P, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -396,3 +402,55 @@ class PackedLinear:
         _check(lib().svdq_debug_group_sums(self.c_layer(), qX.shape[0], form, _dptr(qX), m0, n0, mt, nt,
                                            _dptr(out), _stream()))
         return out
+
+
+class MlpPair:
+    """Two packed layers with GELU between them, Y = fc2(bf16(GELU(fc1(X)))), through
+    svdq_mlp_forward (chained or separate) and the chained step's two calls."""
+
+    def __init__(self, fc1: PackedLinear, fc2: PackedLinear):
+        if fc1.N != fc2.K:
+            raise SvdqError("fc1's N must equal fc2's K")
+        self.fc1, self.fc2 = fc1, fc2
+        self.device = fc1.device
+
+    def workspace(self, M: int, mode: int = MLP_CHAINED):
+        n = lib().svdq_mlp_workspace_bytes(self.fc1.c_layer(), self.fc2.c_layer(), M, mode)
+        return _torch().empty(max(n, 256), dtype=torch_uint8(), device=self.device)
+
+    def forward(self, X, ydtype: int = F32, out=None, workspace=None, mode: int = MLP_CHAINED):
+        torch = _torch()
+        M = X.shape[0]
+        if out is None:
+            out = torch.empty((M, self.fc2.N), dtype=torch.float32 if ydtype == F32 else torch.bfloat16,
+                              device=self.device)
+        ws = workspace if workspace is not None else self.workspace(M, mode)
+        _check(lib().svdq_mlp_forward(self.fc1.c_layer(), self.fc2.c_layer(), M, _dptr(X), X.stride(0), _dptr(out),
+                                      out.stride(0), ydtype, mode, _dptr(ws), ws.numel(), _stream()))
+        return out
+
+    def chain_gemm(self, qX, sX, la, M: int, hidden: bool = False, out=None):
+        """fc1's kernel 2 with fc2's kernel 1 in its epilogue, on fc1's MMA-form activation
+        side.  Returns (qX2, sX2, lora_part, G or None)."""
+        torch = _torch()
+        K2 = self.fc2.K
+        if out is None:
+            qX2, sX2, _ = self.fc2.alloc_act(M, ACT_MMA)
+            part = (torch.empty(((K2 // 128) * M * r16(self.fc2.rank),), dtype=torch.float32, device=self.device)
+                    if self.fc2.rank else None)
+            G = torch.empty((M, K2), dtype=torch.bfloat16, device=self.device) if hidden else None
+        else:
+            qX2, sX2, part, G = out
+        _check(lib().svdq_mlp_chain_gemm(self.fc1.c_layer(), self.fc2.c_layer(), M, _dptr(qX), _dptr(sX), _dptr(la),
+                                         _dptr(qX2), _dptr(sX2), _dptr(part), _dptr(G),
+                                         K2 if G is None else G.stride(0), _stream()))
+        return qX2, sX2, part, G
+
+    def chain_reduce(self, part, M: int, out=None):
+        """fc2's MMA-form lora_act from the chained step's partials (None when rank 0)."""
+        if not self.fc2.rank:
+            return None
+        la2 = out if out is not None else self.fc2.alloc_act(M, ACT_MMA)[2]
+        _check(lib().svdq_mlp_chain_reduce(self.fc1.c_layer(), self.fc2.c_layer(), M, _dptr(part), _dptr(la2),
+                                           _stream()))
+        return la2

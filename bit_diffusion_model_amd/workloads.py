@@ -28,6 +28,9 @@ import numpy as np
 
 __all__ = [
     "Workload",
+    "MlpPair",
+    "mlp_pair",
+    "make_mlp",
     "CONFIG_NAMES",
     "make",
     "random_layer",
@@ -222,3 +225,59 @@ def random_layer(M: int, K: int, N: int, rank: int, seed: int, fmt: str = "int4"
         B = bf16_bits_from_f64(0.02 * st[_S_LB].standard_normal((lora_rank, N)))
     return Workload(f"rand{M}x{K}x{N}r{rank}", M, K, N, rank, fmt, alpha, X,
                     bf16_bits_from_f64(w), X, lora_A=A, lora_B=B, seed=seed)
+
+
+@dataclasses.dataclass
+class MlpPair:
+    """Data of a chained MLP pair fc1 -> GELU -> fc2.
+
+    fc1: the first layer's Workload (X is the pair's input).
+    fc2: the second layer's weights; its X and calib hold the calibration activations
+         for fc2's smoothing (GELU of the unquantized first layer on the first tokens:
+         the pair's actual fc2 input is computed by the layers themselves).
+    """
+
+    name: str
+    fc1: Workload
+    fc2: Workload
+
+    @property
+    def M(self) -> int:
+        return self.fc1.M
+
+
+def mlp_pair(M: int, K1: int, N1: int, N2: int, r1: int, r2: int, seed: int, x_out: Optional[int] = None,
+             h_out: Optional[int] = None, factor: float = 30.0, calib_rows: int = 512, name: str = "") -> MlpPair:
+    """A pair with the value structure of the FLUX MLP: fc1's input with x_out outlier
+    channels (x factor), fc1's weights N(0,1) scaled so that the hidden pre-activation H
+    is about N(0,1) per token (the scale is 1 / sqrt of the mean over tokens of sum_k x_k^2),
+    with h_out output columns x factor, so that fc2's input GELU(H) has that many outlier
+    channels; fc2's weights N(0,1).  Every draw fp64, rounded through fp32 to bf16."""
+    st = _streams(seed)
+    n_x = round(0.01 * K1) if x_out is None else x_out
+    n_h = round(0.01 * N1) if h_out is None else h_out
+    x, _ = _outlier_acts(st[_S_X], st[_S_XOUT], M, K1, n_x, factor)
+    X = bf16_bits_from_f64(x)
+    xv = bf16_bits_to_f32(X).astype(np.float64)
+    w1 = st[_S_W].standard_normal((K1, N1)) / math.sqrt(float(np.mean(np.sum(xv * xv, axis=1))))
+    if n_h:
+        hc = np.sort(st[_S_WOUT].choice(N1, n_h, replace=False))
+        w1[:, hc] *= factor
+    W1 = bf16_bits_from_f64(w1)
+    w2 = st[_S_LA].standard_normal((N1, N2))
+    Mc = min(calib_rows, M)
+    h = xv[:Mc] @ bf16_bits_to_f32(W1).astype(np.float64)
+    G = bf16_bits_from_f64(_gelu_erf(h))
+    fc1 = Workload(f"{name}fc1", M, K1, N1, r1, "int4", 0.5, X, W1, X, seed=seed,
+                   note="MLP fc1 of a chained pair")
+    fc2 = Workload(f"{name}fc2", Mc, N1, N2, r2, "int4", 0.5, G, bf16_bits_from_f64(w2), G, seed=seed,
+                   note="MLP fc2 of a chained pair; X / calib = GELU of the unquantized fc1 on the first tokens")
+    return MlpPair(name, fc1, fc2)
+
+
+def make_mlp(name: str) -> MlpPair:
+    """C2chain: the FLUX.1 MLP pair, 4608 tokens, 3072 -> 12288 -> 3072, rank 32 both,
+    31 input channels and 123 hidden channels x30 (as the independent fc1 / fc2 layers)."""
+    if name == "C2chain":
+        return mlp_pair(4608, 3072, 12288, 3072, 32, 32, seed=1005, name="C2chain ")
+    raise KeyError(name)

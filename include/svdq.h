@@ -63,7 +63,10 @@ typedef enum {
 } svdq_status;
 
 typedef enum { SVDQ_INT4_G64 = 0, SVDQ_MXFP4_G32 = 1, SVDQ_NVFP4_G16 = 2 } svdq_format;
-typedef enum { SVDQ_F32 = 0, SVDQ_BF16 = 1 } svdq_dtype;
+/* Output types of kernel 2: fp32, bf16, or bf16 of GELU(y) (the exact GELU y Phi(y),
+ * Phi the standard normal CDF, evaluated in fp32, then rounded once to bf16), the
+ * activation between the two layers of an MLP pair. */
+typedef enum { SVDQ_F32 = 0, SVDQ_BF16 = 1, SVDQ_BF16_GELU = 2 } svdq_dtype;
 
 /* How kernel 1 hands the activation side to kernel 2 (both calls must agree).
  *   PACKED: the format's storage form: qX [M][K/2] 4-bit codes (INT4 sign-magnitude
@@ -261,7 +264,7 @@ svdq_status svdq_quantize_act_lora_down(const svdq_layer* layer, int64_t M, cons
  * low-rank up projection (lora_act L2) added in the epilogue (review section 4.3: up
  * projection fused with the 4-bit kernel).
  *   form, qX, sX, lora_act  as written by kernel 1 (device)
- *   Y                 device [M][ldy], fp32 or bf16 (ydtype); ldy < 2^22 elements
+ *   Y                 device [M][ldy], svdq_dtype ydtype; ldy < 2^22 elements
  *                     (EUNSUPPORTED otherwise: a tile's rows are addressed through a
  *                     32-bit range)
  *   workspace         optional device scratch (NULL / ws_bytes 0: none), 256-byte
@@ -293,8 +296,8 @@ size_t svdq_workspace_bytes(const svdq_layer* layer, int64_t M);
  * svdq_workspace_bytes, 256-byte aligned, caller-owned; its contents on entry do not
  * matter).  The same launches as the two calls above with form = SVDQ_ACT_MMA and
  * kernel 2 given its split workspace: the results are identical bit for bit.
- *   X  device bf16 [M][ldx] (16-byte aligned rows); Y device [M][ldy], fp32 or bf16
- *   (ydtype), overwritten; columns >= N of each Y row are not touched.
+ *   X  device bf16 [M][ldx] (16-byte aligned rows); Y device [M][ldy], svdq_dtype
+ *   ydtype, overwritten; columns >= N of each Y row are not touched.
  * M == 0 is a no-op.  EINVAL on NULL / misalignment / small workspace; EUNSUPPORTED on
  * ldy >= 2^22; EHIP on launch error. */
 svdq_status svdq_linear_forward(const svdq_layer* layer, int64_t M, const uint16_t* X,
@@ -327,13 +330,66 @@ svdq_status svdq_linear_forward_noalloc(const svdq_layer* layer, int64_t M, cons
  * down projection, a down-projection kernel that reads X a second time (lora_act into
  * the workspace), kernel 2 without the up projection (writes Q(X_hat) Q(R) to Y), and
  * an up-projection kernel that reads Y back and writes Y + lora_act L2.  Arguments,
- * workspace size (svdq_workspace_bytes) and errors as for svdq_linear_forward.  The
+ * workspace size (svdq_workspace_bytes) and errors as for svdq_linear_forward, except
+ * that ydtype SVDQ_BF16_GELU is EUNSUPPORTED (the last kernel adds to Y).  The
  * codes and the 4-bit product are bit-identical to the fused path's; Y differs from it
  * only by the rounding of the intermediate Y (bf16 output: rounded twice) and the order
  * of the fp32 additions. */
 svdq_status svdq_linear_forward_unfused(const svdq_layer* layer, int64_t M, const uint16_t* X,
                                         int64_t ldx, void* Y, int64_t ldy, int32_t ydtype,
                                         void* workspace, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------- the chained MLP pair ---- */
+/* Two layers with GELU between them, Y = fc2(bf16(GELU(fc1(X)))), fc1.N == fc2.K.  The
+ * fused-kernel design of the jeonghoonpark.com "SVDQuant" review (section 4.3,
+ * "Nunchaku", Figure 6(b)) carried one step further, for the cost the ch3chohch3.github.io
+ * post "从 Smooth Quant 到 SVD Quant" names in its "量化方案" section (16-bit activations
+ * written and read back from HBM between kernels): fc1's kernel 2 runs fc2's kernel 1 on
+ * its finished output tile, so the 16-bit hidden activation G never goes to memory.
+ *   SVDQ_MLP_CHAINED: kernel 1 of fc1; fc1's kernel 2 with the chained epilogue (GELU,
+ *     smoothing by fc2's 1 / s, fc2's INT4 codes and fp16 scales in MMA form, and the
+ *     partial down projections by fc2's L1 over each 128-channel column tile); the
+ *     partials summed in column-tile order into fc2's lora_act; fc2's kernel 2.  INT4
+ *     layers only (EUNSUPPORTED otherwise).
+ *   SVDQ_MLP_SEPARATE: the two layers as two svdq_linear_forward calls, fc1's with
+ *     ydtype SVDQ_BF16_GELU into a bf16 G in the workspace (the baseline).
+ * Both modes compute G the same way, and fc2's codes and scales from equal G are equal;
+ * Y differs between them only by the fp32 summation order of fc2's down projection and
+ * of fc1's K-split tiles (the chained fc1 computes every tile whole). */
+typedef enum { SVDQ_MLP_CHAINED = 0, SVDQ_MLP_SEPARATE = 1 } svdq_mlp_mode;
+
+/* Workspace bytes of svdq_mlp_forward for M tokens in `mode` on the current device (0 on
+ * invalid arguments). */
+size_t svdq_mlp_workspace_bytes(const svdq_layer* fc1, const svdq_layer* fc2, int64_t M, int32_t mode);
+
+/* The pair on `stream`.  X device bf16 [M][ldx] (16-byte aligned rows); Y device
+ * [M][ldy] (svdq_dtype ydtype), overwritten; workspace device, >= svdq_mlp_workspace_bytes,
+ * 256-byte aligned, contents on entry irrelevant.  M == 0 is a no-op.  EINVAL on NULL /
+ * misalignment / small workspace / fc1.N != fc2.K; EUNSUPPORTED on a chained non-INT4
+ * pair or ldy >= 2^22; EHIP on launch error. */
+svdq_status svdq_mlp_forward(const svdq_layer* fc1, const svdq_layer* fc2, int64_t M, const uint16_t* X,
+                             int64_t ldx, void* Y, int64_t ldy, int32_t ydtype, int32_t mode, void* workspace,
+                             size_t ws_bytes, void* stream);
+
+/* The chained step alone: fc1's kernel 2 on fc1's MMA-form activation side (qX, sX,
+ * lora_act from svdq_quantize_act_lora_down with SVDQ_ACT_MMA), every output tile whole,
+ * with fc2's kernel 1 in its epilogue.  Writes (device):
+ *   qX2       fc2's codes in MMA form, [M][K2] bytes (K2 = fc1.N = fc2.K), 16-byte aligned
+ *   sX2       fc2's fp16 scales in MMA form, [K2/64][Mp] (Mp = M rounded up to 4)
+ *   lora_part fp32 [K2/128][M][R16], R16 = fc2.rank rounded up to 16: the down
+ *             projection of each token over each 128-channel column tile (unused when
+ *             fc2.rank == 0)
+ *   hidden    optional (NULL: not written): G = bf16(GELU(H)) [M][ldh], ldh >= K2
+ * INT4 layers only.  Errors as for svdq_gemm_w4a4_lora_up. */
+svdq_status svdq_mlp_chain_gemm(const svdq_layer* fc1, const svdq_layer* fc2, int64_t M, const uint8_t* qX,
+                                const void* sX, const void* lora_act, uint8_t* qX2, void* sX2, float* lora_part,
+                                uint16_t* hidden, int64_t ldh, void* stream);
+
+/* fc2's lora_act in MMA form (the layout svdq_quantize_act_lora_down writes with
+ * SVDQ_ACT_MMA, 16-byte aligned) = the sum of lora_part over the K2/128 column tiles, in
+ * tile order (deterministic).  No-op when fc2.rank == 0 or M == 0. */
+svdq_status svdq_mlp_chain_reduce(const svdq_layer* fc1, const svdq_layer* fc2, int64_t M, const float* lora_part,
+                                  void* lora_act2, void* stream);
 
 /* Diagnostic: the exact integer group sums I[g][m][n] = sum_{k in group g} qX[m][k]
  * qW[n][k] (INT4 only; the review's section 3 product Q_X Q_W, taken per group) for the

@@ -383,3 +383,32 @@ def test_device_entry_points_validate_on_host():
     # MMA form: FP6 operand words (M*K bytes), fp16 scales (2 bytes per group and row),
     # 2*R16 bf16 per row, rows rounded up to 32
     assert L.svdq_workspace_bytes(ref, 100) >= 100 * 256 + 4 * 100 * 2 + 128 * 16 * 4
+
+
+def test_mlp_entry_points_validate_on_host():
+    L = svdq.lib()
+    fc1 = svdq._Layer(256, 384, 8, 0, 16, 16, 16, 16, 16)  # fake aligned non-NULL pointers
+    fc2 = svdq._Layer(384, 64, 8, 0, 16, 16, 16, 16, 16)
+    r1, r2 = ctypes.byref(fc1), ctypes.byref(fc2)
+    # fc1.N must equal fc2.K
+    assert L.svdq_mlp_forward(r1, r1, 4, 16, 256, 16, 64, 0, 0, 256, 1 << 30, None) == 1 and "fc2's K" in _err()
+    assert L.svdq_mlp_forward(r1, r2, 4, 16, 256, 16, 64, 0, 5, 256, 1 << 30, None) == 2 and "mode" in _err()
+    assert L.svdq_mlp_forward(r1, r2, 0, 16, 256, 16, 64, 0, 0, None, 0, None) == 0  # M = 0: no-op
+    assert L.svdq_mlp_forward(r1, r2, 4, 16, 256, 16, 64, 0, 0, 256, 10, None) == 1 and "workspace" in _err()
+    # the chained pair runs INT4 layers; the separate mode takes any format
+    fx = svdq._Layer(384, 64, 8, 1, 16, 16, 16, 16, 16)
+    assert L.svdq_mlp_forward(r1, ctypes.byref(fx), 4, 16, 256, 16, 64, 0, 0, 256, 1 << 30, None) == 2
+    assert L.svdq_mlp_chain_gemm(r1, ctypes.byref(fx), 4, 16, 16, 16, 16, 16, 16, None, 0, None) == 2
+    assert L.svdq_mlp_chain_gemm(r1, r2, 4, 16, 16, 16, 16, 16, None, None, 0, None) == 1 and "lora_part" in _err()
+    assert L.svdq_mlp_chain_gemm(r1, r2, 4, 16, 16, 16, 16, 16, 16, 16, 100, None) == 1 and "ldh" in _err()
+    assert L.svdq_mlp_chain_reduce(r1, r2, 4, None, 16, None) == 1
+    # workspace sizes: chained holds fc2's activation side, fc1's and the partials
+    # (384/128 tiles x M x 16 fp32); separate holds the bf16 hidden M x 384
+    M = 100
+    wc = L.svdq_mlp_workspace_bytes(r1, r2, M, 0)
+    ws = L.svdq_mlp_workspace_bytes(r1, r2, M, 1)
+    assert wc >= L.svdq_workspace_bytes(r2, M) + M * 256 + 3 * M * 16 * 4
+    assert ws >= M * 384 * 2 + max(L.svdq_workspace_bytes(r1, M), L.svdq_workspace_bytes(r2, M))
+    assert L.svdq_mlp_workspace_bytes(r1, r2, M, 3) == 0
+    # the unfused forward has no GELU output
+    assert L.svdq_linear_forward_unfused(r1, 4, 16, 256, 16, 384, 2, 256, 1 << 30, None) == 2 and "GELU" in _err()
