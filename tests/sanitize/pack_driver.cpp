@@ -60,7 +60,7 @@ int main() {
   std::vector<float> a(K);
   EXPECT(svdq_act_absmax(M, K, X.data(), K, a.data()) == SVDQ_OK);
 
-  for (int fmt = 0; fmt < 2; ++fmt) {
+  for (int fmt = 0; fmt < 3; ++fmt) {  // INT4, MXFP4, NVFP4
     for (int rank : {0, 16}) {
       Pack p = alloc(K, N, rank, fmt, 0);
       EXPECT(svdq_pack_weights(K, N, W.data(), a.data(), 0.5f, rank, fmt, p.s.data(), p.inv.data(), p.L1t.data(),
@@ -79,9 +79,19 @@ int main() {
       // the quantizer alone on the pack's residual gives its codes
       std::vector<uint8_t> qW2(p.qW.size()), sW2(p.sW.size());
       EXPECT(svdq_quantize_weights(K, N, p.R.data(), fmt, qW2.data(), sW2.data()) == SVDQ_OK);
-      EXPECT(qW2 == p.qW && sW2 == p.sW);
+      if (fmt == 2) {  // NVFP4: the quantizer alone writes the activations' tensor scale as 1
+        const size_t n = sW2.size();
+        float sx = 0.f;
+        std::memcpy(&sx, sW2.data() + n - 4, 4);
+        EXPECT(qW2 == p.qW && std::memcmp(sW2.data(), p.sW.data(), n - 4) == 0 && sx == 1.0f);
+      } else {
+        EXPECT(qW2 == p.qW && sW2 == p.sW);
+      }
       // device layouts
-      std::vector<uint8_t> qo((size_t)(N + 1) / 2 * 2 * (K / 2)), so((size_t)(K / (fmt ? 32 : 64)) * ((N + 3) / 4 * 4) * (fmt ? 1 : 2));
+      // scale layouts: INT4 fp16 [K/64][Np], MXFP4 E8M0 [K/32][Np], NVFP4 E4M3 [K/64][Np][4]
+      const size_t Np = (size_t)(N + 3) / 4 * 4;
+      const size_t sbytes = fmt == 0 ? (size_t)(K / 64) * Np * 2 : fmt == 1 ? (size_t)(K / 32) * Np : (size_t)(K / 16) * Np;
+      std::vector<uint8_t> qo((size_t)(N + 1) / 2 * 2 * (K / 2)), so(sbytes);
       EXPECT(svdq_prepare_weights(K, N, fmt, p.qW.data(), p.sW.data(), qo.data(), so.data()) == SVDQ_OK);
       if (rank) {
         const int R16 = (rank + 15) / 16 * 16;
