@@ -280,7 +280,8 @@ static svdq_status run_chain_gemm(const svdq_layer* fc1, const svdq_layer* fc2, 
   if (!qX || !sX || !qX2 || !sX2) return fail(SVDQ_EINVAL, "qX, sX, qX2 and sX2 must be non-NULL");
   if (k1.rank > 0 && !lora_act) return fail(SVDQ_EINVAL, "lora_act must be non-NULL when fc1's rank > 0");
   if (k2.rank > 0 && !lora_part) return fail(SVDQ_EINVAL, "lora_part must be non-NULL when fc2's rank > 0");
-  if (hidden && (ldh < k1.N || !aligned(hidden, 2))) return fail(SVDQ_EINVAL, "hidden needs ldh >= fc1's N");
+  if (hidden && (ldh < k1.N || ldh % 8 != 0 || !aligned(hidden, 16)))
+    return fail(SVDQ_EINVAL, "hidden needs ldh >= fc1's N, ldh %% 8 == 0 and 16-byte alignment");
   if (!aligned(qX, 16) || !aligned(qX2, 16) || !aligned(sX, 2) || !aligned(sX2, 2) ||
       (lora_act && !aligned(lora_act, 16)) || (lora_part && !aligned(lora_part, 16)))
     return fail(SVDQ_EINVAL, "qX, qX2, lora_act and lora_part must be 16-byte aligned");

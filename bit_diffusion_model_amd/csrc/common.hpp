@@ -105,10 +105,11 @@ __device__ __forceinline__ v8h nv_f16x8(uint32_t w, float s) {
 // GELU in its exact form, x Phi(x) with Phi(x) = erfc(-x / sqrt 2) / 2, in fp32.  erfc(z)
 // for z >= 0 by the Chebyshev fit of Numerical Recipes (Press et al., "Incomplete gamma
 // function, error function", routine erfcc; fractional error below 1.2e-7 for z >= 0):
-// erfc(z) = t exp(-z^2 + P(t)), t = 1 / (1 + z / 2), P a degree-9 polynomial; for x >= 0,
-// Phi(x) = 1 - erfc(x / sqrt 2) / 2.  Evaluated in fp32 the relative error of GELU stays
-// below 1e-5 (the exponential's argument reaches -z^2), far inside the bf16 rounding that
-// follows; the tail keeps its relative accuracy (no 1 + erf cancellation).
+// erfc(z) = t exp(-z^2 + P(t)), t = 1 / (1 + z / 2), P a degree-9 polynomial whose
+// constant term here also carries -ln 2, so the exponential gives erfc / 2 directly; for
+// x >= 0, Phi(x) = 1 - erfc(x / sqrt 2) / 2.  Evaluated in fp32 the relative error of
+// GELU stays below 2e-5 (the exponential's argument reaches -z^2), far inside the bf16
+// rounding that follows; the tail keeps its relative accuracy (no 1 + erf cancellation).
 __device__ __forceinline__ float gelu_erf(float x) {
   const float z = fabsf(x) * 0.70710678118654752f;
   const float t = __builtin_amdgcn_rcpf(fmaf(0.5f, z, 1.0f));
@@ -121,9 +122,17 @@ __device__ __forceinline__ float gelu_erf(float x) {
   p = fmaf(p, t, 0.09678418f);
   p = fmaf(p, t, 0.37409196f);
   p = fmaf(p, t, 1.00002368f);
-  p = fmaf(p, t, -1.26551223f);
-  const float h = 0.5f * t * __expf(fmaf(-z, z, p));  // erfc(|x| / sqrt 2) / 2
+  p = fmaf(p, t, -1.95865941f);  // -1.26551223 - ln 2
+  const float h = t * __expf(fmaf(-z, z, p));  // erfc(|x| / sqrt 2) / 2
   return x * (x >= 0.0f ? 1.0f - h : h);
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+// bf16(GELU(a)) in the low half, bf16(GELU(b)) in the high half (hardware conversion,
+// round to nearest even)
+__device__ __forceinline__ uint32_t gelu_bf16x2(float a, float b) {
+  const bf16x2_t v = {(__bf16)gelu_erf(a), (__bf16)gelu_erf(b)};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // Raw buffer resource over `bytes` bytes at p: loads beyond the range return zeros.

@@ -95,10 +95,13 @@ __device__ __forceinline__ void store_sub(const v16f& acc, void* Y, int64_t ldy,
 #pragma unroll
     for (int a = 0; a < 16; ++a)
       buf_store2((uint16_t)f32_to_bf16_rne(acc[a]), rY, o + (uint32_t)(8 * (a >> 2) + (a & 3)) * ystep);
-  } else {  // bf16 of GELU(y)
+  } else {  // bf16 of GELU(y), converted as in the chained epilogue
 #pragma unroll
-    for (int a = 0; a < 16; ++a)
-      buf_store2((uint16_t)f32_to_bf16_rne(gelu_erf(acc[a])), rY, o + (uint32_t)(8 * (a >> 2) + (a & 3)) * ystep);
+    for (int a = 0; a < 16; a += 2) {
+      const uint32_t g2 = gelu_bf16x2(acc[a], acc[a + 1]);
+      buf_store2((uint16_t)g2, rY, o + (uint32_t)(8 * (a >> 2) + (a & 3)) * ystep);
+      buf_store2((uint16_t)(g2 >> 16), rY, o + (uint32_t)(8 * (a >> 2) + (a & 3) + 1) * ystep);
+    }
   }
 }
 
@@ -544,20 +547,28 @@ __device__ __forceinline__ void chain_epilogue(const v16f (&acc)[4][1], const K2
                                                int wave, int lane, int wn, int l32, int kh, uint32_t Mp) {
   // every wave has finished its reads of the last stage, and its own loads have landed
   __syncthreads();
-  uint8_t* gw = wave < 2 ? lds0 : lds1;
-  const int cc = (wn & 63) + l32;
-  const bool dump = ch.hidden != nullptr;
+  // Rows past M are not masked: their accumulators reach only those rows' own codes,
+  // scales and down projections (per-token groups; MFMA rows are independent), none of
+  // which is stored.  Two rows 8 q + j, 8 q + j + 1 share one bf16 conversion.
+  uint8_t* gw = (wave < 2 ? lds0 : lds1) + ((wn & 63) + l32) * 2 + 4 * kh * GPITCH;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int a = 0; a < 16; ++a) {
-      const int r = i * 32 + 8 * (a >> 2) + 4 * kh + (a & 3);
-      uint32_t b = f32_to_bf16_rne(gelu_erf(acc[i][0][a]));
-      if (r >= rowsA) b = 0u;
-      *reinterpret_cast<uint16_t*>(gw + r * GPITCH + cc * 2) = (uint16_t)b;
-      if (dump && r < rowsA) ch.hidden[(m0 + r) * ch.ldh + n0 + wn + l32] = (uint16_t)b;
+    for (int a = 0; a < 16; a += 2) {
+      const int r = i * 32 + 8 * (a >> 2) + (a & 3);
+      const uint32_t g2 = gelu_bf16x2(acc[i][0][a], acc[i][0][a + 1]);
+      *reinterpret_cast<uint16_t*>(gw + r * GPITCH) = (uint16_t)g2;
+      *reinterpret_cast<uint16_t*>(gw + (r + 1) * GPITCH) = (uint16_t)(g2 >> 16);
     }
   __syncthreads();
+  if (ch.hidden != nullptr) {  // the optional copy of G, 16 bytes per thread and step
+    for (int e = wave * 64 + lane; e < 128 * 16; e += 256) {
+      const int r = e >> 4, pc = e & 15;
+      if (r < rowsA)
+        *reinterpret_cast<uint4*>(ch.hidden + (m0 + r) * ch.ldh + n0 + 8 * pc) =
+            *reinterpret_cast<const uint4*>((pc < 8 ? lds0 : lds1) + r * GPITCH + (pc & 7) * 16);
+    }
+  }
 
   const int r16 = lane & 15, sub = lane >> 4;
   const int64_t c0 = n0 >> 6;  // fc2's group (chunk) index of the tile's first half
@@ -604,21 +615,36 @@ __device__ __forceinline__ void chain_epilogue(const v16f (&acc)[4][1], const K2
         if (sub == 0) ch.sX2[(c0 + g) * (int64_t)Mp + row] = __builtin_bit_cast(uint16_t, sh);
       }
     }
-    for (int t = 0; t < nt2; ++t) {
-      v4f la[1] = {v4f{0.f, 0.f, 0.f, 0.f}};
+    // rank tiles two at a time (one hi / lo split of the activations per pair), a last
+    // odd one alone
+    auto tiles = [&](auto NTc, int t0) {
+      constexpr int NT = decltype(NTc)::value;
+      v4f la[NT];
+#pragma unroll
+      for (int u = 0; u < NT; ++u) la[u] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
-        const uint32_t o = (uint32_t)((((c0 + g) * nt2 + t) * 64 + lane) * 32);
-        const uint4 LA[1] = {buf_load16(rL, o)}, LB[1] = {buf_load16(rL, o + 16)};
-        lora_down16<1>(la, xh[g], LA, LB);
-      }
-      // the 16 x 16 result: lane l holds rank column 16 t + (l & 15), rows 4 (l >> 4) + i
+        uint4 LA[NT], LB[NT];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int rr = tb + 4 * sub + i;
-        if (rr < rowsA) part[rr * R16 + 16 * t + r16] = la[0][i];
+        for (int u = 0; u < NT; ++u) {
+          const uint32_t o = (uint32_t)((((c0 + g) * nt2 + t0 + u) * 64 + lane) * 32);
+          LA[u] = buf_load16(rL, o);
+          LB[u] = buf_load16(rL, o + 16);
+        }
+        lora_down16<NT>(la, xh[g], LA, LB);
       }
-    }
+      // each 16 x 16 result: lane l holds rank column 16 t + (l & 15), rows 4 (l >> 4) + i
+#pragma unroll
+      for (int u = 0; u < NT; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int rr = tb + 4 * sub + i;
+          if (rr < rowsA) part[rr * R16 + 16 * (t0 + u) + r16] = la[u][i];
+        }
+    };
+    int t = 0;
+    for (; t + 2 <= nt2; t += 2) tiles(std::integral_constant<int, 2>{}, t);
+    if (t < nt2) tiles(std::integral_constant<int, 1>{}, t);
   }
 }
 
@@ -1039,7 +1065,7 @@ __global__ __launch_bounds__(256) void k2_lora_reduce(const float* __restrict__ 
   const int64_t m = idx / R16;
   const int j = (int)(idx - m * R16);
   float v = part[idx];
-#pragma unroll 8
+#pragma unroll 16
   for (int t = 1; t < ntiles; ++t) v += part[(int64_t)t * total + idx];
   store_lora_mma(la, m, j, R16 >> 4, v);
 }

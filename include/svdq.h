@@ -379,7 +379,8 @@ svdq_status svdq_mlp_forward(const svdq_layer* fc1, const svdq_layer* fc2, int64
  *   lora_part fp32 [K2/128][M][R16], R16 = fc2.rank rounded up to 16: the down
  *             projection of each token over each 128-channel column tile (unused when
  *             fc2.rank == 0)
- *   hidden    optional (NULL: not written): G = bf16(GELU(H)) [M][ldh], ldh >= K2
+ *   hidden    optional (NULL: not written): G = bf16(GELU(H)) [M][ldh], ldh >= K2, ldh a
+ *             multiple of 8, 16-byte aligned
  * INT4 layers only.  Errors as for svdq_gemm_w4a4_lora_up. */
 svdq_status svdq_mlp_chain_gemm(const svdq_layer* fc1, const svdq_layer* fc2, int64_t M, const uint8_t* qX,
                                 const void* sX, const void* lora_act, uint8_t* qX2, void* sX2, float* lora_part,
