@@ -95,6 +95,8 @@ static svdq_status run_k1(const svdq_layer* layer, int64_t M, const uint16_t* X,
   if (!X || !qX || !sX) return fail(SVDQ_EINVAL, "X, qX and sX must be non-NULL");
   if (kl.rank > 0 && !lora_act) return fail(SVDQ_EINVAL, "lora_act must be non-NULL when rank > 0");
   if (ldx < kl.K || ldx % 8 != 0) return fail(SVDQ_EINVAL, "ldx must be >= K and a multiple of 8");
+  // the scale planes are addressed through 32-bit buffer offsets
+  if (M * kl.K >= (int64_t(1) << 35)) return fail(SVDQ_EUNSUPPORTED, "M * K must be < 2^35");
   if (!aligned(X, 16) || !aligned(qX, 16) || !aligned(sX, 2) || (lora_act && !aligned(lora_act, 16)))
     return fail(SVDQ_EINVAL, "X, qX and lora_act must be 16-byte aligned");
   hipError_t e = launch_k1(kl, M, X, ldx, qX, sX, lora_act, form == SVDQ_ACT_MMA, (hipStream_t)stream);

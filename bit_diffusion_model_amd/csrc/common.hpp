@@ -8,6 +8,7 @@ namespace svdq {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v6i __attribute__((ext_vector_type(6)));
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v2i_t __attribute__((ext_vector_type(2)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
@@ -156,6 +157,18 @@ __device__ __forceinline__ uint32_t buf_load1(__amdgpu_buffer_rsrc_t r, uint32_t
 __device__ __forceinline__ void buf_store4(uint32_t v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
   __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, 0);
 }
+__device__ __forceinline__ void buf_store16(uint4 v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, v), r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_store8(uint2 v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2i_t, v), r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_store1(uint8_t v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b8(v, r, off, 0, 0);
+}
+// An offset no buffer of this library reaches: a store given it is dropped by the range
+// check, so a lane that must not store still issues the (unconditional) instruction.
+constexpr uint32_t kNoStore = 0xFFFFFFF0u;
 __device__ __forceinline__ void buf_store2(uint16_t v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
   __builtin_amdgcn_raw_buffer_store_b16(v, r, off, 0, 0);
 }

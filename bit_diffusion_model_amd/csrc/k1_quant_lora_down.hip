@@ -78,6 +78,20 @@ k1_quant_lora_down(const uint16_t* __restrict__ X, int64_t ldx, int64_t M, int64
   const uint32_t xstep8 = (uint32_t)(8 * ldx * 2);
   __shared__ uint4 xs[K1_WAVES][16][9];
   const __amdgpu_buffer_rsrc_t rL = make_rsrc(L1f, (uint32_t)(NT * 16 * K * 2));
+  // Code and scale stores go through buffer resources as unconditional instructions; a
+  // lane with nothing to store (a row past M, a lane that does not own the scale) gives
+  // the offset kNoStore, which the range check drops.  (With the stores under branches
+  // the compiler's wait counts at the top of the chunk loop no longer included them, so
+  // every chunk waited for the previous chunk's write acknowledgements.)  Code offsets
+  // are block-local: rows m0 .. (token pairs: pairs m0 / 2 ..; m0 is even).
+  const int64_t Mp = (M + 3) & ~int64_t(3);
+  const bool pairs = MMA && FMT != 0;
+  const __amdgpu_buffer_rsrc_t rQ = make_rsrc(
+      qX + (pairs ? (m0 >> 1) * K : m0 * (MMA && FMT == 0 ? K : K >> 1)),
+      (uint32_t)(pairs ? ((nrows + 1) >> 1) * K : nrows * (MMA && FMT == 0 ? K : K >> 1)));
+  const int64_t s_ld = MMA ? Mp : M;  // scale rows: padded to 4 in the MMA form
+  const int64_t s_bytes = FMT == 0 ? (K >> 6) * s_ld * 2 : (FMT == 1 ? (K >> 5) * s_ld : (K >> 4) * s_ld);
+  const __amdgpu_buffer_rsrc_t rSc = make_rsrc(sXv, (uint32_t)s_bytes);
 
   v4f acc[NT > 0 ? NT : 1];
 #pragma unroll
@@ -116,7 +130,9 @@ k1_quant_lora_down(const uint16_t* __restrict__ X, int64_t ldx, int64_t M, int64
       LA[t] = LAn[t];
       LB[t] = LBn[t];
     }
-    if (c + K1_WAVES < nchunks) fetch(c + K1_WAVES);
+    // unconditional (past the end the current chunk again, never used), so the loop has
+    // no branches around memory instructions
+    fetch(c + K1_WAVES < nchunks ? c + K1_WAVES : c);
 
     // x * inv_s, inv_s of channel i from lane i of the row (DPP row_newbcast:i)
 #define K1_BC(i) __int_as_float(__builtin_amdgcn_update_dpp(0, s_own, 0x150 + (i), 0xF, 0xF, false))
@@ -153,31 +169,24 @@ k1_quant_lora_down(const uint16_t* __restrict__ X, int64_t ldx, int64_t M, int64
       const _Float16 sh = int4_quantize16(xh, t);
       uint4 mw = make_uint4(0u, 0u, 0u, 0u);
       if constexpr (MMA) mw = int4_mma_words(t, sub);  // every lane takes part in the swaps
-      if (row_ok) {
-        if constexpr (MMA) {
-          // [M][K/64][64] bytes per token and group: quarter q stores 16 bytes at 16 q,
-          // words 0-3 of half h (quarter 2h) or words 4-5 and two zero words (quarter 2h+1)
-          *reinterpret_cast<uint4*>(qX + row * K + k0) = mw;
-        } else {
-          uint32_t w0 = 0, w1 = 0;
+      if constexpr (MMA) {
+        // [M][K/64][64] bytes per token and group: quarter q stores 16 bytes at 16 q, words
+        // 0-3 of half h (quarter 2h) or words 4-5 and two zero words (quarter 2h+1)
+        buf_store16(mw, rQ, row_ok ? (uint32_t)(r16 * K + k0) : kNoStore);
+      } else {
+        uint32_t w0 = 0, w1 = 0;
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float qc = __builtin_amdgcn_fmed3f(rintf(t[i]), -7.0f, 7.0f);
-            const uint32_t nib = (uint32_t)fabsf(qc) | (qc < 0.0f ? 8u : 0u);
-            if (i < 8) w0 |= nib << (4 * i);
-            else w1 |= nib << (4 * (i - 8));
-          }
-          *reinterpret_cast<uint2*>(qX + row * (K >> 1) + (k0 >> 1)) = make_uint2(w0, w1);
+        for (int i = 0; i < 16; ++i) {
+          const float qc = __builtin_amdgcn_fmed3f(rintf(t[i]), -7.0f, 7.0f);
+          const uint32_t nib = (uint32_t)fabsf(qc) | (qc < 0.0f ? 8u : 0u);
+          if (i < 8) w0 |= nib << (4 * i);
+          else w1 |= nib << (4 * (i - 8));
         }
-        if (sub == 0) {
-          if constexpr (MMA) {  // fp16 bits, rows padded to 4
-            const int64_t Mp = (M + 3) & ~int64_t(3);
-            reinterpret_cast<uint16_t*>(sXv)[(int64_t)c * Mp + row] = __builtin_bit_cast(uint16_t, sh);
-          } else {
-            reinterpret_cast<uint16_t*>(sXv)[(int64_t)c * M + row] = __builtin_bit_cast(uint16_t, sh);
-          }
-        }
+        buf_store8(make_uint2(w0, w1), rQ, row_ok ? (uint32_t)(r16 * (K >> 1) + (k0 >> 1)) : kNoStore);
       }
+      // fp16 scale bits [K/64][s_ld], from the lanes of quarter 0
+      buf_store2(__builtin_bit_cast(uint16_t, sh), rSc,
+                 row_ok && sub == 0 ? (uint32_t)(((int64_t)c * s_ld + row) * 2) : kNoStore);
     } else if constexpr (FMT == 2) {
       // NVFP4: s = E4M3(fp32(a * r6)) (hardware conversion: round half to even; the
       // input clamped to 448, the largest finite E4M3), sigma = fp32(s * S_X), codes =
@@ -198,19 +207,17 @@ k1_quant_lora_down(const uint16_t* __restrict__ X, int64_t ldx, int64_t M, int64
       w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, y[10], y[11], 1.0f, 1);
       w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, y[12], y[13], 1.0f, 2);
       w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, y[14], y[15], 1.0f, 3);
-      if (row_ok) {
-        if constexpr (MMA) {
-          // token pairs; inside the 64-block, codes 16 sub + 0..7 at byte 4 sub and
-          // 16 sub + 8..15 at byte 16 + 4 sub (the bf16 matrix core's lane order)
-          uint8_t* blk = qX + (row >> 1) * K + (int64_t)(c >> 1) * 128 + (row & 1) * 64 + (c & 1) * 32;
-          *reinterpret_cast<uint32_t*>(blk + 4 * sub) = w0;
-          *reinterpret_cast<uint32_t*>(blk + 16 + 4 * sub) = w1;
-          const int64_t Mp = (M + 3) & ~int64_t(3);  // [K/64][Mp][4]
-          reinterpret_cast<uint8_t*>(sXv)[((int64_t)c * Mp + row) * 4 + sub] = (uint8_t)sb;
-        } else {
-          *reinterpret_cast<uint2*>(qX + row * (K >> 1) + (k0 >> 1)) = make_uint2(w0, w1);
-          reinterpret_cast<uint8_t*>(sXv)[(int64_t)(4 * c + sub) * M + row] = (uint8_t)sb;
-        }
+      if constexpr (MMA) {
+        // token pairs; inside the 64-block, codes 16 sub + 0..7 at byte 4 sub and 16 sub +
+        // 8..15 at byte 16 + 4 sub (the bf16 matrix core's lane order)
+        const uint32_t blk = (uint32_t)((r16 >> 1) * K + (c >> 1) * 128 + (r16 & 1) * 64 + (c & 1) * 32);
+        buf_store4(w0, rQ, row_ok ? blk + 4 * sub : kNoStore);
+        buf_store4(w1, rQ, row_ok ? blk + 16 + 4 * sub : kNoStore);
+        // [K/64][Mp][4]
+        buf_store1((uint8_t)sb, rSc, row_ok ? (uint32_t)(((int64_t)c * s_ld + row) * 4 + sub) : kNoStore);
+      } else {
+        buf_store8(make_uint2(w0, w1), rQ, row_ok ? (uint32_t)(r16 * (K >> 1) + (k0 >> 1)) : kNoStore);
+        buf_store1((uint8_t)sb, rSc, row_ok ? (uint32_t)((int64_t)(4 * c + sub) * s_ld + row) : kNoStore);
       }
     } else {
       // MXFP4: e = smallest exponent with 6 * 2^e >= a (clamped to [-127, 127]);
@@ -236,17 +243,15 @@ k1_quant_lora_down(const uint16_t* __restrict__ X, int64_t ldx, int64_t M, int64
       w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, y[10], y[11], 1.0f, 1);
       w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, y[12], y[13], 1.0f, 2);
       w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, y[14], y[15], 1.0f, 3);
-      if (row_ok) {
-        const int64_t b = k0 >> 1;  // byte of the token's code row
-        // MMA form: token pairs, the 64-byte segments (128 K values, one kernel-2 stage)
-        // of tokens 2j and 2j+1 share a 128-byte line
-        uint8_t* dst = MMA ? qX + (row >> 1) * K + (b >> 6) * 128 + (row & 1) * 64 + (b & 63) : qX + row * (K >> 1) + b;
-        *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
-        if ((sub & 1) == 0) {
-          const int64_t ld = MMA ? (M + 3) & ~int64_t(3) : M;  // MMA form: rows padded to 4
-          reinterpret_cast<uint8_t*>(sXv)[(int64_t)(2 * c + (sub >> 1)) * ld + row] = (uint8_t)(e + 127);
-        }
-      }
+      const int64_t b = k0 >> 1;  // byte of the token's code row
+      // MMA form: token pairs, the 64-byte segments (128 K values, one kernel-2 stage) of
+      // tokens 2j and 2j+1 share a 128-byte line
+      const uint32_t dst = (uint32_t)(MMA ? (r16 >> 1) * K + (b >> 6) * 128 + (r16 & 1) * 64 + (b & 63)
+                                          : r16 * (K >> 1) + b);
+      buf_store8(make_uint2(w0, w1), rQ, row_ok ? dst : kNoStore);
+      // E8M0 bytes [K/32][s_ld], from the lanes of quarters 0 and 2
+      buf_store1((uint8_t)(e + 127), rSc,
+                 row_ok && (sub & 1) == 0 ? (uint32_t)((int64_t)(2 * c + (sub >> 1)) * s_ld + row) : kNoStore);
     }
     }  // QUANT
 

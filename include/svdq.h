@@ -255,7 +255,9 @@ svdq_status svdq_prepare_weights(int64_t K, int64_t N, int32_t fmt, const uint8_
  *   sX       device                       their group scales
  *   lora_act device                       X_hat L1, columns >= rank written as zero
  *                                         (unused when rank == 0)
- * M == 0 is a no-op.  EINVAL on NULL / misalignment / ldx < K; EHIP on launch error. */
+ * M == 0 is a no-op.  EINVAL on NULL / misalignment / ldx < K; EUNSUPPORTED when
+ * M * K >= 2^35 (the scale planes are addressed through 32-bit offsets); EHIP on launch
+ * error. */
 svdq_status svdq_quantize_act_lora_down(const svdq_layer* layer, int64_t M, const uint16_t* X,
                                         int64_t ldx, int32_t form, uint8_t* qX, void* sX,
                                         void* lora_act, void* stream);
