@@ -11,20 +11,26 @@ namespace svdq {
 
 // INT4 quantizer of a group (the review's section 3 equation Q_X = round(X / s_X), s_X =
 // max|X| / 7): s = fp16(fp32(a / 7)) with a the group's max |x| (saturating at 65504);
-// t[i] = round-half-even(x / s) exactly: t = x * (1 / s) is within |x / s| 2^-23 of the
-// quotient, so rint(t) is the correctly rounded code unless x / s lies within 2^-17 of a
-// half integer; then (if any lane of the wave has one) the exact residual x - q s decides,
-// ties to even.  s = 0 (an all-zero group, or one whose fp16 scale underflows) leaves
-// every code 0.  Returns s; t is not clamped.
+// the fp32 quotient a / 7 is formed as q0 = a * fp32(1/7) corrected by one fma with the
+// exact residual a - 7 q0, which gives the correctly rounded quotient for every
+// non-negative finite fp32 a (checked exhaustively).  t[i] = round-half-even(x / s)
+// exactly: t = x * rcp(s) (v_rcp_f32, within 1 ulp of 1 / s) is within |x / s| 2^-22 of
+// the quotient, so rint(t) is the correctly rounded code unless x / s lies within 2^-17
+// of a half integer; then (if any lane of the wave has one) the exact residual x - q s
+// decides, ties to even.  s = 0 (an all-zero group, or one whose fp16 scale underflows)
+// leaves every code 0.  Returns s; t is not clamped.
 __device__ __forceinline__ _Float16 int4_quantize16(const float (&xh)[16], float (&t)[16]) {
   float a = 0.f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(xh[i]));
   a = wave_max_xor(a, 16);
   a = wave_max_xor(a, 32);
-  const _Float16 sh = (_Float16)fminf(a / 7.0f, 65504.0f);
+  constexpr float kSeventh = 1.0f / 7.0f;
+  const float q0 = a * kSeventh;
+  const float a7 = fmaf(fmaf(-q0, 7.0f, a), kSeventh, q0);  // == fp32(a / 7)
+  const _Float16 sh = (_Float16)fminf(a7, 65504.0f);
   const float sf = (float)sh;
-  const float rcp = sf > 0.0f ? 1.0f / sf : 0.0f;
+  const float rcp = sf > 0.0f ? __builtin_amdgcn_rcpf(sf) : 0.0f;
   float dev = 0.f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {

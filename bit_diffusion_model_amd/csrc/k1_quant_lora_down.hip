@@ -30,7 +30,7 @@
 // the same channel order.  Partial sums of the waves are added through LDS at the end,
 // in a fixed order.
 //
-// INT4 rounding: t = x * (1 / s) is within |x / s| * 2^-23 of the quotient x / s, so
+// INT4 rounding: t = x * rcp(s) is within |x / s| * 2^-22 of the quotient x / s, so
 // round(t) is the correctly rounded code unless x / s lies within 2^-17 of a half
 // integer.  Such lanes are flagged and, if any lane of the wave has one, the chunk takes
 // the exact correction (x - q * s is exact near s / 2, and ties go to even).  The MMA
