@@ -136,6 +136,29 @@ class HostPack:
     tscale_x: float = 1.0
 
 
+_PACK_ARRAYS = ("s", "inv_s", "L1t", "L2", "qW", "sW", "R", "errors")
+
+
+def save_pack(p: HostPack, path: str) -> None:
+    """Write a pack's artifacts (the offline result: smoothing factors, low-rank factors,
+    residual codes and scales, and the NVFP4 tensor scales) to one .npz file; load_pack
+    reads them back bit for bit.  Plain arrays only (no pickled objects)."""
+    arrays = {k: getattr(p, k) for k in _PACK_ARRAYS if getattr(p, k) is not None}
+    meta = np.array([p.K, p.N, p.rank, p.fmt], dtype=np.int64)
+    tsc = np.array([p.tscale_w, p.tscale_x], dtype=np.float32)
+    np.savez(path, meta=meta, tscales=tsc, **arrays)
+
+
+def load_pack(path: str) -> HostPack:
+    """Read a pack written by save_pack (numpy's loader with pickles disallowed)."""
+    with np.load(path, allow_pickle=False) as z:
+        K, N, rank, fmt = (int(v) for v in z["meta"])
+        tw, tx = (float(v) for v in z["tscales"])
+        opt = {k: (z[k].copy() if k in z.files else None) for k in ("R", "errors")}
+        return HostPack(K, N, rank, fmt, z["s"].copy(), z["inv_s"].copy(), z["L1t"].copy(), z["L2"].copy(),
+                        z["qW"].copy(), z["sW"].copy(), opt["R"], opt["errors"], tw, tx)
+
+
 def pack_weights(W_bits: np.ndarray, act_absmax_: Optional[np.ndarray], alpha: float, rank: int,
                  fmt: int, want_R: bool = False, refine_iters: int = 0) -> HostPack:
     """svdq_pack_weights, or with refine_iters > 0 svdq_pack_weights_refined (the

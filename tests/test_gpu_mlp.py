@@ -210,3 +210,19 @@ def test_full_size_chained_pair():
         f"of which the oracle's own sensitivity to the hidden rounding is {sens:.2e}")
     assert e_own <= TOL_Y
     assert e_pair <= sens + TOL_Y
+
+
+def test_chained_pair_bitwise_deterministic():
+    """The chained pair (fixed-order partial sums, no atomics) gives the same bits over ten
+    calls."""
+    import torch
+
+    M, K1, N1, N2, r1, r2 = 300, 256, 640, 200, 16, 32
+    data = mlp_pair(M, K1, N1, N2, r1, r2, seed=77)
+    p1, p2 = _pack(data.fc1), _pack(data.fc2)
+    pair = svdq.MlpPair(layer_from_oracle(p1), layer_from_oracle(p2))
+    X = to_dev_bf16(data.fc1.X)
+    ws = pair.workspace(M)
+    Y0 = pair.forward(X, workspace=ws).clone()
+    for _ in range(9):
+        assert torch.equal(pair.forward(X, workspace=ws), Y0)

@@ -412,3 +412,32 @@ def test_mlp_entry_points_validate_on_host():
     assert L.svdq_mlp_workspace_bytes(r1, r2, M, 3) == 0
     # the unfused forward has no GELU output
     assert L.svdq_linear_forward_unfused(r1, 4, 16, 256, 16, 384, 2, 256, 1 << 30, None) == 2 and "GELU" in _err()
+
+
+@pytest.mark.parametrize("fmt", [svdq.INT4_G64, svdq.NVFP4_G16])
+def test_pack_save_load_round_trip(fmt, tmp_path):
+    """The offline artifacts written to one .npz and read back are the same bits."""
+    wl = random_layer(48, 256, 96, 8, 31)
+    p = svdq.pack_weights(wl.W, svdq.act_absmax(wl.X), wl.alpha, wl.rank, fmt, want_R=True)
+    path = str(tmp_path / "pack.npz")
+    svdq.save_pack(p, path)
+    q = svdq.load_pack(path)
+    assert (q.K, q.N, q.rank, q.fmt) == (p.K, p.N, p.rank, p.fmt)
+    assert (q.tscale_w, q.tscale_x) == (p.tscale_w, p.tscale_x)
+    for k in ("s", "inv_s", "L1t", "L2", "qW", "sW", "R"):
+        a, b = getattr(p, k), getattr(q, k)
+        assert a.dtype == b.dtype and a.shape == b.shape and a.tobytes() == b.tobytes(), k
+    assert q.errors is None
+
+
+def test_launch_failure_reports_hip_error():
+    """A launch that the HIP runtime refuses (here: no device in this container) returns
+    SVDQ_EHIP with the runtime's message, and nothing aborts."""
+    import torch
+
+    if torch.cuda.is_available():
+        pytest.skip("needs a host without a visible GPU")
+    L = svdq.lib()
+    lay = svdq._Layer(256, 64, 8, 0, 16, 16, 16, 16, 16)
+    assert L.svdq_quantize_act_lora_down(ctypes.byref(lay), 4, 16, 256, 1, 16, 16, 16, None) == 4
+    assert "kernel 1 launch" in _err()
