@@ -226,3 +226,29 @@ def test_chained_pair_bitwise_deterministic():
     Y0 = pair.forward(X, workspace=ws).clone()
     for _ in range(9):
         assert torch.equal(pair.forward(X, workspace=ws), Y0)
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
+def test_separate_mode_other_formats(fmt):
+    """The separate mode (two svdq_linear_forward calls, fc1 with the GELU output) runs any
+    format; the chained mode refuses non-INT4 layers."""
+    import torch
+
+    M, K1, N1, N2, r1, r2 = 130, 256, 384, 96, 16, 8
+    data = mlp_pair(M, K1, N1, N2, r1, r2, seed=515)
+    packs = [opack.pack_weights(w.W, oquant.channel_absmax_cols(w.calib), w.alpha, w.rank, fmt)
+             for w in (data.fc1, data.fc2)]
+    pair = svdq.MlpPair(layer_from_oracle(packs[0]), layer_from_oracle(packs[1]))
+    X = to_dev_bf16(data.fc1.X)
+    ws = pair.workspace(M, svdq.MLP_SEPARATE)
+    sentinel_fill(ws)
+    Y = torch.empty((M, N2), dtype=torch.float32, device="cuda:0")
+    sentinel_fill(Y)
+    pair.forward(X, svdq.F32, out=Y, workspace=ws, mode=svdq.MLP_SEPARATE)
+    torch.cuda.synchronize()
+    assert_finite(Y)
+    e = rel_err(Y.cpu().numpy().astype(np.float64), oforward.mlp_forward(data.fc1.X, packs[0], packs[1])["fc2"]["Y"])
+    log(f"  {fmt} separate pair: max|err|/RMS {e:.2e}")
+    assert e <= TOL_Y
+    with pytest.raises(svdq.SvdqError):
+        pair.forward(X, svdq.F32, out=Y, workspace=pair.workspace(M, svdq.MLP_CHAINED), mode=svdq.MLP_CHAINED)
