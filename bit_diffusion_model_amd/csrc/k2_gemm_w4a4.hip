@@ -1053,21 +1053,29 @@ __global__ __launch_bounds__(64) void k2_fixup(const float* __restrict__ partial
   store_sub(acc, Y, ldy, ydtype, m0, n0, rowsA, N, (int)(sub / CB) * 32, (int)(sub % CB) * 32, lane & 31, lane >> 5);
 }
 
-// Sum of the chained epilogue's per-column-tile partials of the down projection, in tile
-// order (the result does not depend on which tile finished first), stored in the MMA form
-// of lora_act (bf16 hi / lo pairs in fragment order) for fc2's kernel 2.  One thread per
-// (token, rank column).
+// Sum of the chained epilogue's per-column-tile partials of the down projection, stored
+// in the MMA form of lora_act (bf16 hi / lo pairs in fragment order) for fc2's kernel 2.
+// A block takes 64 (token, rank column) elements; wave w sums the tiles w, w + 4, ... of
+// each (64 consecutive floats per load), and wave 0 adds the four slices in wave order, so
+// the result does not depend on which tile or block finished first.
 __global__ __launch_bounds__(256) void k2_lora_reduce(const float* __restrict__ part, int ntiles, int64_t M, int R16,
                                                       uint16_t* __restrict__ la) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  __shared__ float red[4][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int64_t total = M * R16;
-  if (idx >= total) return;
-  const int64_t m = idx / R16;
-  const int j = (int)(idx - m * R16);
-  float v = part[idx];
-#pragma unroll 16
-  for (int t = 1; t < ntiles; ++t) v += part[(int64_t)t * total + idx];
-  store_lora_mma(la, m, j, R16 >> 4, v);
+  const int64_t idx = (int64_t)blockIdx.x * 64 + lane;
+  float v = 0.f;
+  if (idx < total) {
+#pragma unroll 4
+    for (int t = w; t < ntiles; t += 4) v += part[(int64_t)t * total + idx];
+  }
+  red[w][lane] = v;
+  __syncthreads();
+  if (w == 0 && idx < total) {
+    const float sum = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
+    const int64_t m = idx / R16;
+    store_lora_mma(la, m, (int)(idx - m * R16), R16 >> 4, sum);
+  }
 }
 
 }  // namespace
@@ -1223,7 +1231,7 @@ hipError_t launch_lora_reduce(const KernelLayer& L1, const KernelLayer& L2, int6
   const int R16 = (L2.rank + 15) / 16 * 16;
   if (R16 == 0 || M == 0) return hipSuccess;
   const int64_t n = M * R16;
-  hipLaunchKernelGGL(k2_lora_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, part,
+  hipLaunchKernelGGL(k2_lora_reduce, dim3((unsigned)((n + 63) / 64)), dim3(256), 0, st, part,
                      (int)(L1.N / SShape<0>::BN), M, R16, static_cast<uint16_t*>(la2));
   return hipGetLastError();
 }

@@ -351,7 +351,7 @@ svdq_status svdq_linear_forward_unfused(const svdq_layer* layer, int64_t M, cons
  *   SVDQ_MLP_CHAINED: kernel 1 of fc1; fc1's kernel 2 with the chained epilogue (GELU,
  *     smoothing by fc2's 1 / s, fc2's INT4 codes and fp16 scales in MMA form, and the
  *     partial down projections by fc2's L1 over each 128-channel column tile); the
- *     partials summed in column-tile order into fc2's lora_act; fc2's kernel 2.  INT4
+ *     partials summed in a fixed order into fc2's lora_act; fc2's kernel 2.  INT4
  *     layers only (EUNSUPPORTED otherwise).
  *   SVDQ_MLP_SEPARATE: the two layers as two svdq_linear_forward calls, fc1's with
  *     ydtype SVDQ_BF16_GELU into a bf16 G in the workspace (the baseline).
@@ -390,7 +390,8 @@ svdq_status svdq_mlp_chain_gemm(const svdq_layer* fc1, const svdq_layer* fc2, in
 
 /* fc2's lora_act in MMA form (the layout svdq_quantize_act_lora_down writes with
  * SVDQ_ACT_MMA, 16-byte aligned) = the sum of lora_part over the K2/128 column tiles, in
- * tile order (deterministic).  No-op when fc2.rank == 0 or M == 0. */
+ * a fixed order (tiles t = s mod 4 summed in tile order for each s, then the four sums
+ * in order of s), so the result is deterministic.  No-op when fc2.rank == 0 or M == 0. */
 svdq_status svdq_mlp_chain_reduce(const svdq_layer* fc1, const svdq_layer* fc2, int64_t M, const float* lora_part,
                                   void* lora_act2, void* stream);
 
