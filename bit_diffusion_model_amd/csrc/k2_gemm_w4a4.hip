@@ -21,16 +21,24 @@
 //    operand form (FP6 words, fp16 scales, bf16 hi/lo low-rank activations), so the main
 //    loop expands only the weights.
 //
-// Tiling: 64-wide waves own 2 x 2 (INT4) or 4 x 2 (MXFP4) MFMA tiles of 32 x 32; two
-// blocks share a CU, so one block's barrier and staging overlap another's math.  K
-// advances in stages of 64-wide sub-steps (one INT4 group, two FP4 groups each), one
-// barrier per stage.  Two kernels implement this:
+//  * NVFP4 (group 16, E4M3 scales under fp32 tensor scales): the scaled conversions take
+//    only a scale's exponent and the block-scaled MFMA only E8M0 per 32, so each code
+//    group is dequantized to fp16 in registers (exact) for v_mfma_f32_32x32x16_f16; the
+//    two tensor scales multiply the 4-bit sum once after the loop.
+//
+// Tiling: 64-wide waves own TI x TJ MFMA tiles of 32 x 32 (SShape: INT4 4 x 1 of a
+// 128 x 128 block, MXFP4 4 x 2 of 256 x 128, NVFP4 2 x 2 of 128 x 128; the packed-form
+// kernel 2 x 2); two blocks share a CU, so one block's barrier and staging overlap
+// another's math.  K advances in stages of 64-wide sub-steps, one barrier per stage.
+// Two kernels implement this:
 //  * k2_stream (MMA activation form, the forward's path): both operand panels and
 //    their scales go global -> LDS with LDS-destination buffer loads into three
 //    rotating buffers, loads for stage k+2 in flight while stage k is computed; the
 //    weight codes stay 4-bit in LDS and each wave expands its own fragments.  Its DEBUG
 //    instance runs the same loads, LDS layout, expansion and group-sum MFMA and stores
-//    each group's MFMA result instead of rescaling it (the exact group sums).
+//    each group's MFMA result instead of rescaling it (the exact group sums); its CHAIN
+//    instance (the MLP pair) runs the next layer's kernel 1 on the finished tile instead
+//    of storing it (chain_epilogue).
 //  * k2_gemm (packed activation form): 128 x 128 tiles of 4 waves; loads into registers
 //    one stage ahead, converts the activation nibbles to FP6 operand words on the way
 //    into double-buffered, row-padded LDS.
