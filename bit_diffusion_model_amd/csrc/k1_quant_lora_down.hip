@@ -12,8 +12,8 @@
 // into 64-wide chunks; wave w takes chunks w, w+8, ..., with the next chunk's X, inv_s
 // and L1 loads issued before the current chunk is processed.  Inside a chunk, lane l holds
 // token (l & 15) and the 16 consecutive channels 16 * (l >> 4) .. +15.  One INT4 group
-// (64) is therefore spread over the 4 lanes l, l^16, l^32, l^48; one FP4 group (32)
-// over lanes l, l^16.  X is loaded row-contiguously instead (each 16-byte load covers 8
+// (64) is therefore spread over the 4 lanes l, l^16, l^32, l^48; one MXFP4 group (32)
+// over lanes l, l^16; an NVFP4 group (16) is one lane's 16 values.  X is loaded row-contiguously instead (each 16-byte load covers 8
 // whole 128-byte lines of 8 tokens) and regrouped through a small per-wave LDS tile:
 // loads whose 4-lane groups straddle 4 lines were measured markedly slower.
 //
