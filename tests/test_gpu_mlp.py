@@ -41,6 +41,7 @@ SHAPES = [
     (17, 128, 128, 33, 0, 0),
     (129, 256, 256, 64, 8, 0),
     (64, 128, 512, 130, 0, 16),
+    (1, 128, 256, 16, 8, 16),
 ]
 
 
