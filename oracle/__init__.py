@@ -27,4 +27,4 @@ through their pinned parts (quantizers, group sums, SVD identities) and brute fo
 tiny shapes.
 """
 
-from . import numerics, quant, pack, forward  # noqa: F401
+from . import numerics, quant, pack, forward, weight_only  # noqa: F401
