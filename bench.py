@@ -386,6 +386,58 @@ def measure_mlp(svdq, torch, steps, warm_s):
                                    "lora_partials_sum": round(us[2], 2), "fc2_k2": round(us[3], 2)}}
 
 
+def measure_w4a16(svdq, torch, steps, warm_s, w4a4_ms, mxfp4_ms):
+    """The 4-bit weight-only baseline (svdq_w4a16_gemm) on the QKV shape: W's own INT4 g64
+    codes upcast to bf16 inside the kernel, bf16 MFMA, fp32 Y; the W4A4 layer's step time
+    over it is the layer-level analogue of the pages' speed-up over a weight-only baseline.
+    For context, a library bf16 GEMM (torch.matmul, hipBLASLt) on weights upcast beforehand,
+    which reads 16-bit weights and does no upcast: the floor of any weight-only layer."""
+    from bit_diffusion_model_amd.workloads import make
+
+    dev = "cuda:0"
+    wl = make("C1")
+    M, K, N = wl.M, wl.K, wl.N
+    lay = svdq.WeightOnlyLinear.from_weights(wl.W, dev)
+    X = torch.from_numpy(wl.X.view(np.int16)).to(dev).view(torch.bfloat16)
+    Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    # bf16(s q) [K][N] from the layer's own codes and scales, for the library GEMM only
+    q = lay.qW.to(torch.int32)
+    nib = torch.stack([q & 15, q >> 4], -1).reshape(N, K)
+    qv = torch.where(nib >= 8, 8 - nib, nib).float()
+    Wd = (qv.T * lay.sW.view(torch.float16).float().repeat_interleave(64, 0)).to(torch.bfloat16).contiguous()
+    Yb = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    fk = lambda: lay.forward(X, svdq.F32, Y)
+    fl = lambda: torch.matmul(X, Wd, out=Yb)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < warm_s:
+        for _ in range(5):
+            fk()
+            fl()
+        torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    tk, tl = [], []
+    for _ in range(max(steps // 20, 3)):
+        for f, out in ((fk, tk), (fl, tl)):
+            ev0.record()
+            for _ in range(20):
+                f()
+            ev1.record()
+            torch.cuda.synchronize()
+            out.append(ev0.elapsed_time(ev1) / 20)
+    ms, ms_l = float(np.median(tk)), float(np.median(tl))
+    flops = 2.0 * M * N * K
+    tf = flops / (ms * 1e-3) / 1e12
+    log(f"[bench] [w4a16] {ms:.4f} ms ({tf:.1f} TFLOP/s); library bf16 GEMM {ms_l:.4f} ms")
+    return {"workload": "FLUX.1 QKV projection, 4-bit weight-only (W4A16) baseline: INT4 g64 fp16 scales "
+                        "upcast to bf16 in the kernel, bf16 MFMA, fp32 output",
+            "M": M, "K": K, "N": N, "ms": round(ms, 5), "TFLOPs": round(tf, 2),
+            "frac_bf16_peak": round(tf / PEAK_BF16_TOPS, 4),
+            "w4a4_int4_speedup": round(ms / w4a4_ms, 4) if w4a4_ms else None,
+            "w4a4_mxfp4_speedup": round(ms / mxfp4_ms, 4) if mxfp4_ms else None,
+            "library_bf16_gemm_ms": round(ms_l, 5),
+            "library_bf16_gemm_TFLOPs": round(flops / (ms_l * 1e-3) / 1e12, 2)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -467,6 +519,8 @@ def main():
             torch.cuda.empty_cache()
         out["workloads"] = others
         out["mlp_pair"] = measure_mlp(svdq, torch, 100, 0.2)
+        out["w4a16"] = measure_w4a16(svdq, torch, 100, 0.2, m["ms"] if args.workload == "C1" else None,
+                                     others["C3"]["ms_per_step"] if "C3" in others else None)
     if args.calib_copy:
         src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device="cuda:0")
         dst = torch.empty_like(src)

@@ -16,7 +16,7 @@ OUT = os.path.join(HERE, "libsvdq.so")
 BUILD = os.path.join(HERE, "_build")
 ARCH = "gfx950"
 
-DEVICE_SOURCES = ["k1_quant_lora_down.hip", "k2_gemm_w4a4.hip", "k3_lora_up.hip", "api.cpp", "noalloc.hip"]
+DEVICE_SOURCES = ["k1_quant_lora_down.hip", "k2_gemm_w4a4.hip", "k3_lora_up.hip", "k4_w4a16.hip", "api.cpp", "noalloc.hip"]
 HOST_SOURCES = ["pack.cpp", "status.cpp"]
 
 HIP_FLAGS = [

@@ -209,6 +209,25 @@ svdq_status svdq_linear_forward_unfused(const svdq_layer* layer, int64_t M, cons
   return ok();
 }
 
+svdq_status svdq_w4a16_gemm(int64_t M, int64_t K, int64_t N, const uint16_t* X, int64_t ldx, const uint8_t* qW,
+                            const uint16_t* sW, void* Y, int64_t ldy, int32_t ydtype, void* stream) {
+  if (M < 0) return fail(SVDQ_EINVAL, "M must be >= 0");
+  if (K < 64 || K % 64 != 0 || N < 1) return fail(SVDQ_EINVAL, "K must be a positive multiple of 64 and N >= 1");
+  if (M == 0) return ok();
+  if (!X || !qW || !sW || !Y) return fail(SVDQ_EINVAL, "X, qW, sW and Y must be non-NULL");
+  if (ydtype != SVDQ_F32 && ydtype != SVDQ_BF16) return fail(SVDQ_EUNSUPPORTED, "unsupported output dtype %d", (int)ydtype);
+  if (ldx < K || ldx % 8 != 0) return fail(SVDQ_EINVAL, "ldx must be >= K and a multiple of 8");
+  if (ldy < N) return fail(SVDQ_EINVAL, "ldy must be >= N");
+  // a tile's rows of X and Y and the scale plane are addressed through 32-bit offsets
+  if (ldx >= (int64_t(1) << 22) || ldy >= (int64_t(1) << 22) || (K / 64) * N >= (int64_t(1) << 31))
+    return fail(SVDQ_EUNSUPPORTED, "ldx and ldy must be < 2^22 and K / 64 * N < 2^31");
+  if (!aligned(X, 16) || !aligned(qW, 16) || !aligned(sW, 2) || !aligned(Y, ydtype == SVDQ_F32 ? 4 : 2))
+    return fail(SVDQ_EINVAL, "X and qW must be 16-byte aligned, sW and Y aligned to their element size");
+  hipError_t e = launch_w4a16(M, K, N, X, ldx, qW, sW, Y, ldy, ydtype, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(SVDQ_EHIP, "weight-only kernel launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 svdq_status svdq_debug_group_sums(const svdq_layer* layer, int64_t M, int32_t form, const uint8_t* qX,
                                   int64_t m0, int64_t n0, int64_t mt, int64_t nt, int32_t* out, void* stream) {
   KernelLayer kl;

@@ -61,4 +61,9 @@ hipError_t launch_lora_reduce(const KernelLayer& L1, const KernelLayer& L2, int6
 hipError_t launch_k2_debug(const KernelLayer& L, int64_t M, const uint8_t* qX, bool mma, int64_t m0,
                            int64_t n0, int64_t mt, int64_t nt, int32_t* out, hipStream_t st);
 
+// The 4-bit weight-only baseline: Y = X bf16(s_W q_W) on the bf16 matrix core.  X bf16
+// [M][ldx]; qW storage-form INT4 codes [N][K/2]; sW fp16 [K/64][N]; ydtype 0 fp32, 1 bf16.
+hipError_t launch_w4a16(int64_t M, int64_t K, int64_t N, const uint16_t* X, int64_t ldx, const uint8_t* qW,
+                        const uint16_t* sW, void* Y, int64_t ldy, int ydtype, hipStream_t st);
+
 }  // namespace svdq

@@ -47,6 +47,7 @@ EXPORTS = [
     "svdq_quantize_act_lora_down", "svdq_gemm_w4a4_lora_up", "svdq_gemm_workspace_bytes", "svdq_workspace_bytes",
     "svdq_linear_forward", "svdq_linear_forward_unfused", "svdq_debug_group_sums", "svdq_linear_forward_noalloc",
     "svdq_mlp_workspace_bytes", "svdq_mlp_forward", "svdq_mlp_chain_gemm", "svdq_mlp_chain_reduce",
+    "svdq_w4a16_gemm",
 ]
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
@@ -83,6 +84,7 @@ def lib():
         "svdq_mlp_forward": (I32, [P, P, I64, P, I64, P, I64, I32, I32, P, ctypes.c_size_t, P]),
         "svdq_mlp_chain_gemm": (I32, [P, P, I64, P, P, P, P, P, P, P, I64, P]),
         "svdq_mlp_chain_reduce": (I32, [P, P, I64, P, P, P]),
+        "svdq_w4a16_gemm": (I32, [I64, I64, I64, P, I64, P, P, P, I64, I32, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -477,3 +479,32 @@ class MlpPair:
         _check(lib().svdq_mlp_chain_reduce(self.fc1.c_layer(), self.fc2.c_layer(), M, _dptr(part), _dptr(la2),
                                            _stream()))
         return la2
+
+
+class WeightOnlyLinear:
+    """The 4-bit weight-only baseline (svdq_w4a16_gemm): W's own INT4 codes and fp16 group
+    scales on the GPU, upcast to bf16 inside the kernel."""
+
+    def __init__(self, K: int, N: int, qW: np.ndarray, sW: np.ndarray, device="cuda:0"):
+        self.K, self.N, self.device = int(K), int(N), device
+        self.qW = _upload(np.asarray(qW, np.uint8), device)
+        self.sW = _upload(np.asarray(sW, np.uint16), device)
+
+    @classmethod
+    def from_weights(cls, W_bits: np.ndarray, device="cuda:0") -> "WeightOnlyLinear":
+        """Quantize W (bf16 bits [K][N]) with the library's INT4 group quantizer
+        (svdq_quantize_weights) and upload the codes and scales."""
+        W = np.ascontiguousarray(W_bits, dtype=np.uint16)
+        Wf = (W.astype(np.uint32) << 16).view(np.float32)
+        qW, sW = quantize_weights(Wf, INT4_G64)
+        return cls(W.shape[0], W.shape[1], qW, sW, device)
+
+    def forward(self, X, ydtype: int = F32, out=None):
+        torch = _torch()
+        M = X.shape[0]
+        if out is None:
+            out = torch.empty((M, self.N), dtype=torch.float32 if ydtype == F32 else torch.bfloat16,
+                              device=self.device)
+        _check(lib().svdq_w4a16_gemm(M, self.K, self.N, _dptr(X), X.stride(0), _dptr(self.qW), _dptr(self.sW),
+                                     _dptr(out), out.stride(0), ydtype, _stream()))
+        return out

@@ -341,6 +341,28 @@ svdq_status svdq_linear_forward_unfused(const svdq_layer* layer, int64_t M, cons
                                         int64_t ldx, void* Y, int64_t ldy, int32_t ydtype,
                                         void* workspace, size_t ws_bytes, void* stream);
 
+/* The 4-bit weight-only baseline (W4A16): the weights stored as 4-bit codes and upcast
+ * to the activations' 16-bit type before a 16-bit product, the arrangement the method's
+ * speed-up is measured against (jeonghoonpark.com "SVDQuant" review, section 3
+ * "Quantization Preliminary", on operands of unequal bit width; chatpaper.ai SVDQuant
+ * abstract, the 3.0x over a 4-bit weight-only baseline).
+ *   Y[m][n] = sum_k X[m][k] Wd[k][n],  Wd[k][n] = bf16(sW[k/64][n] * q[n][k])
+ * (the exact product of scale and code rounded once to bf16, nearest, ties to even),
+ * accumulated in fp32 on the bf16 matrix core; no smoothing and no low-rank branch.
+ *   X   device bf16 [M][ldx], 16-byte aligned, ldx % 8 == 0, ldx >= K
+ *   qW  device INT4 codes of W in the storage form of svdq_quantize_weights / pack
+ *       ([N][K/2], sign-magnitude nibbles, code 2j in the low nibble of byte j; make
+ *       them with svdq_quantize_weights on W itself), 16-byte aligned
+ *   sW  device fp16 scale bits [K/64][N]
+ *   Y   device [M][ldy], fp32 (SVDQ_F32) or bf16 (SVDQ_BF16)
+ * All buffers are the caller's; one launch on `stream`.  M == 0 is a no-op.  EINVAL on
+ * NULL, misalignment, K not a positive multiple of 64, N < 1, ldx < K or ldy < N;
+ * EUNSUPPORTED for another ydtype or ldx / ldy >= 2^22 or K/64 * N >= 2^31; EHIP on
+ * launch error. */
+svdq_status svdq_w4a16_gemm(int64_t M, int64_t K, int64_t N, const uint16_t* X, int64_t ldx,
+                            const uint8_t* qW, const uint16_t* sW, void* Y, int64_t ldy,
+                            int32_t ydtype, void* stream);
+
 /* ---------------------------------------------------- the chained MLP pair ---- */
 /* Two layers with GELU between them, Y = fc2(bf16(GELU(fc1(X)))), fc1.N == fc2.K.  The
  * fused-kernel design of the jeonghoonpark.com "SVDQuant" review (section 4.3,

@@ -414,6 +414,27 @@ def test_mlp_entry_points_validate_on_host():
     assert L.svdq_linear_forward_unfused(r1, 4, 16, 256, 16, 384, 2, 256, 1 << 30, None) == 2 and "GELU" in _err()
 
 
+def test_w4a16_gemm_validates_on_host():
+    """The weight-only baseline's argument checks (fake aligned device pointers: every call
+    below is refused before any launch)."""
+    L = svdq.lib()
+    g = L.svdq_w4a16_gemm
+    # M, K, N, X, ldx, qW, sW, Y, ldy, ydtype, stream
+    assert g(0, 256, 64, 16, 256, 16, 16, 16, 64, 0, None) == 0  # M = 0: no-op
+    assert g(-1, 256, 64, 16, 256, 16, 16, 16, 64, 0, None) == 1
+    assert g(4, 100, 64, 16, 256, 16, 16, 16, 64, 0, None) == 1 and "multiple of 64" in _err()
+    assert g(4, 256, 0, 16, 256, 16, 16, 16, 64, 0, None) == 1
+    assert g(4, 256, 64, None, 256, 16, 16, 16, 64, 0, None) == 1 and "non-NULL" in _err()
+    assert g(4, 256, 64, 16, 128, 16, 16, 16, 64, 0, None) == 1 and "ldx" in _err()
+    assert g(4, 256, 64, 16, 260, 16, 16, 16, 64, 0, None) == 1 and "ldx" in _err()
+    assert g(4, 256, 64, 16, 256, 16, 16, 16, 32, 0, None) == 1 and "ldy" in _err()
+    assert g(4, 256, 64, 16, 256, 16, 16, 16, 64, 2, None) == 2 and "dtype" in _err()
+    assert g(4, 256, 64, 16, 1 << 22, 16, 16, 16, 64, 0, None) == 2 and "2^22" in _err()
+    assert g(4, 256, 64, 18, 256, 16, 16, 16, 64, 0, None) == 1 and "aligned" in _err()
+    assert g(4, 256, 64, 16, 256, 24, 16, 16, 64, 0, None) == 1 and "aligned" in _err()
+    assert g(4, 256, 64, 16, 256, 16, 16, 18, 64, 0, None) == 1 and "aligned" in _err()  # fp32 Y
+
+
 @pytest.mark.parametrize("fmt", [svdq.INT4_G64, svdq.NVFP4_G16])
 def test_pack_save_load_round_trip(fmt, tmp_path):
     """The offline artifacts written to one .npz and read back are the same bits."""
@@ -441,3 +462,5 @@ def test_launch_failure_reports_hip_error():
     lay = svdq._Layer(256, 64, 8, 0, 16, 16, 16, 16, 16)
     assert L.svdq_quantize_act_lora_down(ctypes.byref(lay), 4, 16, 256, 1, 16, 16, 16, None) == 4
     assert "kernel 1 launch" in _err()
+    assert L.svdq_w4a16_gemm(4, 256, 64, 16, 256, 16, 16, 16, 64, 0, None) == 4
+    assert "weight-only kernel launch" in _err()
