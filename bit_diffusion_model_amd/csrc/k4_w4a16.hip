@@ -19,10 +19,9 @@
 //    consecutive rows fall in distinct bank groups;
 //  * the weight codes of a stage (256 columns x 32 bytes) go global -> LDS the same way,
 //    two stages ahead, and each lane's scale into a register; each lane upcasts 32 codes
-//    once per block (not once per wave): nibbles ->
-//    FP8 E4M3 subnormals q 2^-9 -> fp32 (exact) -> times 2^9 s (exact: q s has at most
-//    14 significant bits) -> bf16, round to nearest even (the hardware conversion) ->
-//    the stage's LDS tile;
+//    of one column once per block (not once per wave): nibbles -> FP8 E4M3 subnormals
+//    q 2^-9 -> fp32 (exact) -> times 2^9 s (exact: q s has at most 14 significant bits)
+//    -> bf16, round to nearest even (the hardware conversion) -> the stage's LDS tile;
 //  * two LDS buffers of 64 KB, one barrier per stage: it publishes stage k and frees the
 //    other buffer for stage k+1's loads and upcast.
 // Rows past M read as zeros and are not stored; columns past N have zero codes (their
@@ -49,7 +48,6 @@ __device__ __forceinline__ int swz8(int row) { return (row ^ (row >> 3)) & 7; }
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t voff, uint32_t soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
 }
-
 
 // s_waitcnt vmcnt(N) lgkmcnt(0)
 template <int N>
