@@ -99,3 +99,30 @@ def test_w4a16_deterministic():
     a = lay.forward(X).cpu()
     b = lay.forward(X).cpu()
     assert torch.equal(a, b)
+
+
+def test_w4a16_planted_scales_and_codes():
+    """Codes and scales set directly: every code -7..7 and the negative-zero nibble, scales
+    0, the smallest fp16 subnormal, the largest subnormal, 1 and the saturated 65504, and
+    scale products that are bf16 ties; X with magnitudes that keep every product finite."""
+    import torch
+
+    rng = np.random.default_rng(21)
+    M, K, N = 70, 384, 136
+    codes = rng.integers(-7, 8, size=(N, K)).astype(np.int8)
+    nib = (np.where(codes < 0, 8, 0) | np.abs(codes)).astype(np.uint8)
+    zero = codes == 0
+    nib[zero & (rng.random((N, K)) < 0.5)] = 8  # -0: sign bit with magnitude 0
+    qW = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+    special = np.array([0x0000, 0x0001, 0x03FF, 0x3C00, 0x7BFF, 0x3C04, 0x3C0C, 0x3C02], np.uint16)
+    sW = rng.integers(0x2000, 0x4800, size=(K // 64, N)).astype(np.uint16)
+    sW.flat[:: 5] = special[np.arange(sW.size)[:: 5] % special.size]
+    X = (rng.standard_normal((M, K)) * 0.5).astype(np.float32)
+    Xb = (X.view(np.uint32) >> 16).astype(np.uint16)  # truncated to bf16: any bf16 input
+    lay = svdq.WeightOnlyLinear(K, N, qW, sW)
+    Y = _run(lay, Xb, svdq.F32, 8, 4)
+    ref = owo.forward(Xb, codes, sW)
+    assert np.isfinite(Y).all()
+    bound = _bound(Xb, owo.upcast(codes, sW), K, ref, False)
+    err = np.abs(Y - ref)
+    assert (err <= bound).all(), f"max err/bound {np.max(err / bound):.3g}"
