@@ -3,9 +3,11 @@
 //   {"what": ..., "waves_per_simd": ..., "cycles": ...}    cycles per unit at 2.4 GHz
 //   {"what": ..., "bytes_per_cycle_cu": ...}              per CU at 2.4 GHz
 //   {"what": "mfma_32x32x4_2b_f16_layout", "ok": 0|1}    operand / result layout probe
+//   {"what": "cross_...", "nv": ..., "cycles_per_iter": ...}  per SIMD at 2.4 GHz
 // Units: one MFMA (MFMA chains), one VALU instruction (VALU only), one MFMA plus its
 // VALU (same-wave overlap), one tile and group (the INT4 rescale pattern: group-sum
-// MFMA, scale-product MFMA, 16 v_fmac).
+// MFMA, scale-product MFMA, 16 v_fmac); cross_*: one iteration of two FP6 MFMAs in one
+// wave and / or nv v_fmac in another wave of the same SIMD.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -172,7 +174,9 @@ static void layout_2b() {
 template <int NB, bool L2>
 __global__ __launch_bounds__(256) void kdma(const uint8_t* __restrict__ src, size_t per_wave, int reps, float* out) {
   __shared__ __attribute__((aligned(1024))) uint8_t ring[4][NB][1024];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // wave-uniform (readfirstlane): a per-lane wave index makes the buffer resource look
+  // divergent, and the compiler then wraps every load in a waterfall loop
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const size_t gw = (size_t)blockIdx.x * 4 + wave;
   const uint8_t* base = L2 ? src + (gw % 64) * 32768 : src + gw * per_wave;
   const int bytes = L2 ? 32768 : (int)per_wave;
@@ -188,6 +192,33 @@ __global__ __launch_bounds__(256) void kdma(const uint8_t* __restrict__ src, siz
   __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
   __syncthreads();
   out[gw * 64 + lane] = (float)ring[wave][lane % NB][lane];
+}
+
+// The same stream through registers: 16-byte buffer loads (8 in flight per wave), each
+// written to LDS with ds_write_b128 once it has arrived (the asm store keeps the compiler
+// from dropping the otherwise unread LDS data).
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+__global__ __launch_bounds__(256) void kreg(const uint8_t* __restrict__ src, int reps, float* out) {
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[4][8][1024];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const size_t gw = (size_t)blockIdx.x * 4 + wave;
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(src + (gw % 64) * 32768), (short)0, 32768, 0x00020000);
+  v4u reg[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) reg[j] = __builtin_amdgcn_raw_buffer_load_b128(r, (uint32_t)(j * 1024 + lane * 16), 0, 0);
+  for (int i = 8; i < reps; i += 8) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      asm volatile("ds_write_b128 %0, %1" ::"v"((uint32_t)(uintptr_t)&ring[wave][j][lane * 16]), "v"(reg[j]) : "memory");
+      reg[j] = __builtin_amdgcn_raw_buffer_load_b128(r, (uint32_t)(((i + j) % 32) * 1024 + lane * 16), 0, 0);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    asm volatile("ds_write_b128 %0, %1" ::"v"((uint32_t)(uintptr_t)&ring[wave][j][lane * 16]), "v"(reg[j]) : "memory");
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  out[gw * 64 + lane] = (float)ring[wave][lane % 8][lane];
 }
 
 struct DmaArg {
@@ -212,6 +243,70 @@ static void dma(const uint8_t* src, size_t total, int blocks_per_cu) {
   const double bytes = L2 ? (double)a.reps * 1024 * a.blocks * 4 : (double)a.per_wave * a.blocks * 4;
   printf("{\"what\": \"lds_dma_%s_%d_in_flight_%d_blocks\", \"bytes_per_cycle_cu\": %.1f}\n", L2 ? "l2" : "hbm", NB,
          blocks_per_cu, bytes / (ms * 1e-3) / 256 / 2.4e9);
+}
+
+static void launch_reg(void* p) {
+  const DmaArg* a = static_cast<const DmaArg*>(p);
+  hipLaunchKernelGGL(kreg, dim3(a->blocks), dim3(256), 0, 0, a->src, a->reps, a->out);
+}
+
+static void regload(const uint8_t* src, int blocks_per_cu) {
+  DmaArg a{src, 0, 4096, 256 * blocks_per_cu, nullptr};
+  CHECK(hipMalloc(&a.out, (size_t)a.blocks * 4 * 64 * sizeof(float)));
+  const float ms = best_ms(launch_reg, &a);
+  CHECK(hipFree(a.out));
+  const double bytes = (double)a.reps * 1024 * a.blocks * 4;
+  printf("{\"what\": \"reg_load_ds_write_l2_8_in_flight_%d_blocks\", \"bytes_per_cycle_cu\": %.1f}\n", blocks_per_cu,
+         bytes / (ms * 1e-3) / 256 / 2.4e9);
+}
+
+// MFMA and VALU in different waves of one SIMD: a block of 8 waves, wave w on SIMD w % 4;
+// waves 0-3 run FP6 MFMA chains (two per iteration), waves 4-7 NV v_fmac per iteration.
+// role 0: the wave exits at once.
+template <int NV>
+__global__ __launch_bounds__(512) void kcross(float* out, int roleA, int roleB) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int role = wave < 4 ? roleA : roleB;
+  float s = 0.f;
+  if (role == 1) {
+    v8i a = {lane, 3, 5, 7, 9, 11, 0, 0}, b = {lane * 3, 1, 2, 3, 4, 5, 0, 0};
+    v16f acc0 = {}, acc1 = {};
+    for (int it = 0; it < ITER; ++it) {
+      acc0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc0, 2, 2, 0, 130, 0, 130);
+      acc1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc1, 2, 2, 0, 130, 0, 130);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s += acc0[i] + acc1[i];
+  } else if (role == 2) {
+    float x[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) x[i] = (float)(lane + i) * 1e-3f;
+    for (int it = 0; it < ITER; ++it) {
+#pragma unroll
+      for (int i = 0; i < NV; ++i) x[i % 32] = fmaf(x[i % 32], 1.0001f, 1e-9f);
+    }
+#pragma unroll
+    for (int i = 0; i < 32; ++i) s += x[i];
+  }
+  out[blockIdx.x * 512 + threadIdx.x] = s;
+}
+
+struct CrossArg {
+  float* out;
+  int ra, rb;
+};
+template <int NV>
+static void launch_cross(void* p) {
+  const CrossArg* c = static_cast<const CrossArg*>(p);
+  hipLaunchKernelGGL((kcross<NV>), dim3(256), dim3(512), 0, 0, c->out, c->ra, c->rb);
+}
+template <int NV>
+static void cross(const char* what, int ra, int rb) {
+  CrossArg a{nullptr, ra, rb};
+  CHECK(hipMalloc(&a.out, (size_t)256 * 512 * sizeof(float)));
+  const float ms = best_ms(launch_cross<NV>, &a);
+  CHECK(hipFree(a.out));
+  printf("{\"what\": \"%s\", \"nv\": %d, \"cycles_per_iter\": %.1f}\n", what, NV, ms * 1e-3 * 2.4e9 / ITER);
 }
 
 // ds_read_b128 bandwidth: consecutive lanes read consecutive 16-byte slots
@@ -275,7 +370,12 @@ int main() {
   dma<8, false>(src, total, 1);
   dma<8, true>(src, total, 1);
   dma<8, true>(src, total, 2);
+  regload(src, 1);
+  regload(src, 2);
   CHECK(hipFree(src));
+  cross<16>("cross_mfma_only", 1, 0);
+  cross<16>("cross_valu_only", 0, 2);
+  cross<16>("cross_mfma_and_valu_waves", 1, 2);
   lds(4);
   lds(8);
   lds(16);

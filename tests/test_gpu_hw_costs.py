@@ -8,7 +8,11 @@ wide margins (the printed numbers are the measurement).
   rescale's v_fmac count bounds kernel 2);
 * the two-block v_mfma_f32_32x32x4_2b_f16 has the documented operand / result layout;
 * LDS-destination buffer loads and ds_read_b128 deliver far more than kernel 2 moves (so
-  the loads' bandwidth is not its bound).
+  the loads' bandwidth is not its bound), and 16-byte loads staged through registers
+  reach the same L2 -> CU rate as the LDS-destination loads (no faster path to LDS);
+* an FP6 MFMA stream in one wave and a v_fmac stream in another wave of the same SIMD
+  only partly overlap: each MFMA takes VALU issue cycles from the other wave (why the
+  INT4 rescale's VALU work and its MFMAs add up rather than overlap).
 """
 import json
 import os
@@ -40,3 +44,8 @@ def test_hardware_costs():
     assert [x for x in rows if x["what"] == "mfma_32x32x4_2b_f16_layout"][0]["ok"] == 1
     assert bw["lds_dma_l2_8_in_flight_2_blocks"] > 20
     assert bw["ds_read_b128_8_waves_per_cu"] > 64
+    reg, lds_dma = bw["reg_load_ds_write_l2_8_in_flight_2_blocks"], bw["lds_dma_l2_8_in_flight_2_blocks"]
+    assert 0.5 < reg / lds_dma < 2.0
+    cr = {x["what"]: x["cycles_per_iter"] for x in rows if x["what"].startswith("cross_")}
+    m, v, both = cr["cross_mfma_only"], cr["cross_valu_only"], cr["cross_mfma_and_valu_waves"]
+    assert max(m, v) * 1.15 < both < m + v
