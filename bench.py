@@ -198,9 +198,32 @@ def cpu_baseline(wl_name, rows):
     oforward.forward(X, packed)
     t = time.perf_counter() - t0
     ops = 2.0 * rows * N * K + 2.0 * rows * r * (K + N)
+    # the same on one BLAS thread, on a sixteenth of the rows
+    rows1 = max(rows // 16, 1)
+    t1 = None
+    try:
+        from threadpoolctl import threadpool_limits
+
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            oforward.forward(wl.X[:rows1], packed)
+            t1 = time.perf_counter() - t0
+    except Exception:  # pragma: no cover
+        pass
+    ops1 = 2.0 * rows1 * N * K + 2.0 * rows1 * r * (K + N)
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            model = next((l.split(":", 1)[1].strip() for l in fh if l.startswith("model name")), "")
+    except OSError:  # pragma: no cover
+        pass
     return {"value": ops / t / 1e12, "unit": "TOPS", "cores": int(cores), "kind": "oracle",
             "sample": f"oracle forward on {rows} of {wl.M} tokens x all {N} outputs of the {WORKLOADS[wl_name]} "
-                      f"layer ({t:.1f} s); host {os.cpu_count()} logical CPUs"}
+                      f"layer ({t:.1f} s); host {os.cpu_count()} logical CPUs ({model})",
+            "single_thread": (None if t1 is None else
+                              {"value": ops1 / t1 / 1e12, "unit": "TOPS", "cores": 1,
+                               "sample": f"oracle forward on {rows1} tokens x all {N} outputs, one BLAS thread "
+                                         f"({t1:.1f} s)"})}
 
 
 PEAK_INT8_TOPS = PEAK_MFMA_TOPS
@@ -214,10 +237,22 @@ def k1_algorithmic_bytes(M, K, G, r, int4):
     return float(M) * (2 * K + K // 2 + (K // G) * (2 if int4 else 1) + 4 * r)
 
 
-def measure(svdq, torch, wl_name, ydt, steps, warmup, warm_s, compare, log_prefix=""):
+def percentiles_us(ms_list):
+    v = np.asarray(ms_list) * 1e3
+    return {"p10": round(float(np.percentile(v, 10)), 2), "median": round(float(np.median(v)), 2),
+            "p90": round(float(np.percentile(v, 90)), 2), "n": int(v.size)}
+
+
+COLD_BYTES = 512 << 20  # written between cold forwards: twice the 256 MB Infinity Cache, 16 x the L2s
+
+
+def measure(svdq, torch, wl_name, ydt, steps, warmup, warm_s, compare, log_prefix="", dist=False):
     """Time one workload: the forward (kernel 1 + kernel 2) over `steps` steps after at
     least `warmup` steps and `warm_s` seconds of warm-up, per-kernel HIP-event durations,
-    and (compare) the rank-0 and unfused forwards in alternating blocks."""
+    (compare) the rank-0 and unfused forwards in alternating blocks, and (dist) single
+    forwards one by one, warm (back to back) and cold (after a 512 MiB write that evicts
+    the packed weights and the activations from the L2 and Infinity caches), as
+    p10 / median / p90."""
     from bit_diffusion_model_amd.workloads import make
 
     dev = "cuda:0"
@@ -229,7 +264,8 @@ def measure(svdq, torch, wl_name, ydt, steps, warmup, warm_s, compare, log_prefi
     hp = svdq.pack_weights(wl.W, svdq.act_absmax(wl.calib), wl.alpha, wl.rank, fmt)
     if wl.lora_A is not None:
         hp = svdq.concat_lora(hp, wl.lora_A, wl.lora_B)
-    log(f"[bench]{log_prefix} pack {time.perf_counter() - t0:.1f} s (offline, untimed)")
+    pack_s = time.perf_counter() - t0
+    log(f"[bench]{log_prefix} pack {pack_s:.1f} s (offline, untimed)")
     lay = svdq.PackedLinear.from_host_pack(hp, dev)
     lay0 = svdq.PackedLinear(K, N, 0, fmt, hp.inv_s, hp.L1t[:0], hp.L2[:0], hp.qW, hp.sW, dev)
     r = hp.rank
@@ -297,6 +333,30 @@ def measure(svdq, torch, wl_name, ydt, steps, warmup, warm_s, compare, log_prefi
     rnd = lambda x, d: None if x != x else round(x, d)  # NaN (not measured) -> null
     ms_r, ms0, ms_u = med(fr), med(f0), med(fu)
 
+    fwd_dist = None
+    if dist:
+        nw, nc = 100, 20
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * nw)]
+        for i in range(nw):
+            ev[2 * i].record()
+            step()
+            ev[2 * i + 1].record()
+        torch.cuda.synchronize()
+        warm_ms = [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(nw)]
+        scratch = torch.empty(COLD_BYTES, dtype=torch.uint8, device=dev)
+        cold_ms = []
+        for i in range(nc):
+            scratch.fill_(i & 255)
+            ev[0].record()
+            step()
+            ev[1].record()
+            torch.cuda.synchronize()
+            cold_ms.append(ev[0].elapsed_time(ev[1]))
+        del scratch
+        fwd_dist = {"warm_fwd_us": percentiles_us(warm_ms), "cold_fwd_us": percentiles_us(cold_ms),
+                    "cold_eviction": f"{COLD_BYTES >> 20} MiB written before each cold forward"}
+        log(f"[bench]{log_prefix} single forwards: warm {fwd_dist['warm_fwd_us']}, cold {fwd_dist['cold_fwd_us']}")
+
     G = lay.group
     k2_ops = float(M) * N * (2.0 * K + 2.0 * r)
     k1_bytes = k1_algorithmic_bytes(M, K, G, r, fmt == svdq.INT4_G64)
@@ -316,7 +376,10 @@ def measure(svdq, torch, wl_name, ydt, steps, warmup, warm_s, compare, log_prefi
         "k2_frac_of_mfma_peak": round(k2_tops / (PEAK_BF16_TOPS if fmt == svdq.NVFP4_G16 else PEAK_MFMA_FP4_TOPS), 4),
         "k2_frac_int8_peak": round(k2_tops / PEAK_INT8_TOPS, 4) if fmt == svdq.INT4_G64 else None,
         "rank0_ms": rnd(ms0, 5), "fwd_ms_paired": rnd(ms_r, 5), "lowrank_overhead": rnd(ms_r / ms0 - 1.0, 4),
-        "unfused_ms": rnd(ms_u, 5), "unfused_lowrank_overhead": rnd(ms_u / ms0 - 1.0, 4)}
+        "unfused_ms": rnd(ms_u, 5), "unfused_lowrank_overhead": rnd(ms_u / ms0 - 1.0, 4),
+        "host_pack_s": round(pack_s, 2)}
+    if fwd_dist:
+        res["kernels"].update(fwd_dist)
     return res
 
 
@@ -486,7 +549,8 @@ def main():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
     ydt = svdq.F32 if args.ydtype == "f32" else svdq.BF16
-    m = measure(svdq, torch, args.workload, ydt, args.steps, args.warmup, args.warm_seconds, not args.no_compare)
+    m = measure(svdq, torch, args.workload, ydt, args.steps, args.warmup, args.warm_seconds, not args.no_compare,
+                dist=not args.no_compare)
     fmt, M, K, N, r = m["fmt"], m["M"], m["K"], m["N"], m["r"]
     k2_tops = m["k2_tops"]
     peak = PEAK_MFMA_FP4_TOPS  # both formats run the FP6 / FP4 scaled MFMA (10.1 PF dense)
