@@ -67,13 +67,14 @@ def traffic_entry():
 CALIB_BYTES = 512 << 20
 
 
-def _kernel_key(name):
+def _kernel_key(name, fmt=0):
     """Which launch of the timed forward a rocprofv3 kernel name is: kernel 1, kernel 2
-    (the INT4 streamed kernel on the MMA activation form), kernel 2's K-split fixup, or
-    a device copy (the calibration copy is the largest of those)."""
+    (the streamed kernel of format fmt on the MMA activation form: 0 INT4, 1 MXFP4),
+    kernel 2's K-split fixup, or a device copy (the calibration copy is the largest of
+    those)."""
     if "k1_quant_lora_down" in name:
         return "k1"
-    if "k2_stream<0" in name:
+    if f"k2_stream<{fmt}" in name:
         return "k2"
     if "k2_fixup" in name:
         return "fixup"
@@ -82,7 +83,7 @@ def _kernel_key(name):
     return "copy" if "copy" in name.lower() else None
 
 
-def _pmc_table(path):
+def _pmc_table(path, fmt=0):
     """{kernel key: {counter: (mean over dispatches, dispatches)}} from a rocprofv3
     counter CSV; for the copy key the largest dispatch."""
     import csv
@@ -90,7 +91,7 @@ def _pmc_table(path):
 
     acc = collections.defaultdict(lambda: collections.defaultdict(list))
     for r in csv.DictReader(open(path)):
-        key = _kernel_key(r["Kernel_Name"])
+        key = _kernel_key(r["Kernel_Name"], fmt)
         if key:
             acc[key][r["Counter_Name"]].append(float(r["Counter_Value"]))
     return {k: {c: ((max(v) if k == "copy" else sum(v) / len(v)), len(v)) for c, v in cs.items()}
@@ -132,20 +133,25 @@ def write_traffic(fetch_csv, write_csv):
 
 
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "k2_gemm_int4_flux_qkv_counters.json")
+COUNTERS_FILE_MX = os.path.join(ROOT, "profiles", "k2_gemm_mxfp4_flux_qkv_counters.json")
 N_XCD, N_CU, SIMD_PER_CU = 8, 256, 4
 
 
-def write_counters(a_csv, b_csv):
+def write_counters(a_csv, b_csv, workload="C1"):
     """Utilisation of kernels 1 and 2 from two rocprofv3 --pmc passes.  GRBM_GUI_ACTIVE is
     summed over the 8 XCDs, so one XCD's active cycles are a eighth of it; the SQ busy
     counters are summed over all 1024 SIMDs (SQ_ACTIVE_INST_VALU in units of 4 cycles,
     one wave64 VALU issue), so each fraction below is per SIMD-cycle of the launch."""
-    a, b = _pmc_table(a_csv), _pmc_table(b_csv)
-    out = {"workload": "FLUX.1 QKV projection M=4608 K=3072 N=9216 r=32, INT4 g64, fp32 Y",
+    mx = workload == "C3"
+    fmt = 1 if mx else 0
+    a, b = _pmc_table(a_csv, fmt), _pmc_table(b_csv, fmt)
+    wflag = " --workload C3" if mx else ""
+    out = {"workload": "FLUX.1 QKV projection M=4608 K=3072 N=9216 r=32, "
+                       + ("MXFP4 g32" if mx else "INT4 g64") + ", fp32 Y",
            "k2_source_hash": source_hash(K2_SOURCES),
-           "commands": [PMC_COMMAND.format(counters=" ".join(sorted(a["k2"]))),
-                        PMC_COMMAND.format(counters=" ".join(sorted(b["k2"]))),
-                        "python bench.py --write-counters <pass A csv> <pass B csv>"],
+           "commands": [PMC_COMMAND.format(counters=" ".join(sorted(a["k2"]))) + wflag,
+                        PMC_COMMAND.format(counters=" ".join(sorted(b["k2"]))) + wflag,
+                        "python bench.py --write-counters <pass A csv> <pass B csv>" + wflag],
            "kernels": {}}
     for key in ("k1", "k2"):
         raw = {c: v[0] for c, v in a.get(key, {}).items()}
@@ -163,7 +169,7 @@ def write_counters(a_csv, b_csv):
             "valu_insts_per_mfma": g("SQ_INSTS_VALU") / max(g("SQ_INSTS_MFMA"), 1.0),
             "lds_bank_conflict_cycles_per_lds_inst": g("SQ_LDS_BANK_CONFLICT") / max(g("SQ_INSTS_LDS"), 1.0),
             "l2_hit_frac": hits / (hits + miss) if hits + miss > 0 else None}
-    with open(COUNTERS_FILE, "w") as fh:
+    with open(COUNTERS_FILE_MX if mx else COUNTERS_FILE, "w") as fh:
         json.dump(out, fh, indent=1)
     print(json.dumps(out))
 
@@ -532,7 +538,7 @@ def main():
         write_traffic(*args.write_traffic)
         return
     if args.write_counters:
-        write_counters(*args.write_counters)
+        write_counters(*args.write_counters, workload=args.workload)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
