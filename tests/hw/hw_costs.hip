@@ -4,6 +4,7 @@
 //   {"what": ..., "bytes_per_cycle_cu": ...}              per CU at 2.4 GHz
 //   {"what": "mfma_32x32x4_2b_f16_layout", "ok": 0|1}    operand / result layout probe
 //   {"what": "cross_...", "nv": ..., "cycles_per_iter": ...}  per SIMD at 2.4 GHz
+//   {"what": "valu_<instruction>", "waves_per_simd": ..., "cycles": ...}  per instruction
 // Units: one MFMA (MFMA chains), one VALU instruction (VALU only), one MFMA plus its
 // VALU (same-wave overlap), one tile and group (the INT4 rescale pattern: group-sum
 // MFMA, scale-product MFMA, 16 v_fmac); cross_*: one iteration of two FP6 MFMAs in one
@@ -111,6 +112,37 @@ static float best_ms(void (*launch)(void*), void* arg) {
   return best;
 }
 
+// VALU issue cost of one instruction class: 32 independent registers per lane, one
+// instruction of the class on each per iteration (inline asm, so the instruction is the
+// one named).  OP: 0 v_fmac_f32, 1 v_mul_f32, 2 v_and_b32, 3 v_add_f32, 4 v_fma_mix_f32,
+// 5 v_pk_mul_f16, 6 v_lshlrev_b32, 7 v_alignbit_b32, 8 v_cvt_f32_f16.
+template <int OP>
+__global__ void kvalu(float* out, int seed) {
+  const int lane = threadIdx.x & 63;
+  uint32_t x[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) x[i] = __float_as_uint((float)(lane + i + seed) * 1e-3f);
+  const uint32_t y = __float_as_uint(1.0001f), z = __float_as_uint(1e-9f);
+  for (int it = 0; it < ITER; ++it) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      if constexpr (OP == 0) asm volatile("v_fmac_f32 %0, %1, %2" : "+v"(x[i]) : "v"(y), "v"(z));
+      else if constexpr (OP == 1) asm volatile("v_mul_f32 %0, %0, %1" : "+v"(x[i]) : "v"(y));
+      else if constexpr (OP == 2) asm volatile("v_and_b32 %0, %0, %1" : "+v"(x[i]) : "v"(y));
+      else if constexpr (OP == 3) asm volatile("v_add_f32 %0, %0, %1" : "+v"(x[i]) : "v"(z));
+      else if constexpr (OP == 4) asm volatile("v_fma_mix_f32 %0, %0, %1, %2" : "+v"(x[i]) : "v"(y), "v"(z));
+      else if constexpr (OP == 5) asm volatile("v_pk_mul_f16 %0, %0, %1" : "+v"(x[i]) : "v"(y));
+      else if constexpr (OP == 6) asm volatile("v_lshlrev_b32 %0, 1, %0" : "+v"(x[i]));
+      else if constexpr (OP == 7) asm volatile("v_alignbit_b32 %0, %0, %1, 8" : "+v"(x[i]) : "v"(y));
+      else asm volatile("v_cvt_f32_f16 %0, %0" : "+v"(x[i]));
+    }
+  }
+  uint32_t s = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) s ^= x[i];
+  out[blockIdx.x * blockDim.x + threadIdx.x] = (float)s;
+}
+
 struct CostArg {
   float* out;
   int blocks;
@@ -119,6 +151,26 @@ template <int MODE, int NV>
 static void launch_cost(void* p) {
   const CostArg* c = static_cast<const CostArg*>(p);
   hipLaunchKernelGGL((kcost<MODE, NV>), dim3(c->blocks), dim3(256), 0, 0, c->out, 1);
+}
+
+template <int OP>
+static void launch_valu(void* p) {
+  const CostArg* c = static_cast<const CostArg*>(p);
+  hipLaunchKernelGGL((kvalu<OP>), dim3(c->blocks), dim3(256), 0, 0, c->out, 1);
+}
+template <int OP>
+static void valu_cost(const char* what, int blocks_per_cu) {
+  CostArg a{nullptr, 256 * blocks_per_cu};
+  CHECK(hipMalloc(&a.out, (size_t)a.blocks * 256 * sizeof(float)));
+  const float ms = best_ms(launch_valu<OP>, &a);
+  CHECK(hipFree(a.out));
+  const double cycles = ms * 1e-3 * 2.4e9 / ((double)ITER * blocks_per_cu * 32);
+  printf("{\"what\": \"valu_%s\", \"waves_per_simd\": %d, \"cycles\": %.1f}\n", what, blocks_per_cu, cycles);
+}
+template <int OP>
+static void valu_both(const char* what) {
+  valu_cost<OP>(what, 2);
+  valu_cost<OP>(what, 8);
 }
 
 // waves_per_simd = blocks per CU (4 waves per block, one per SIMD)
@@ -376,6 +428,15 @@ int main() {
   cross<16>("cross_mfma_only", 1, 0);
   cross<16>("cross_valu_only", 0, 2);
   cross<16>("cross_mfma_and_valu_waves", 1, 2);
+  valu_both<0>("v_fmac_f32");
+  valu_both<1>("v_mul_f32");
+  valu_both<2>("v_and_b32");
+  valu_both<3>("v_add_f32");
+  valu_both<4>("v_fma_mix_f32");
+  valu_both<5>("v_pk_mul_f16");
+  valu_both<6>("v_lshlrev_b32");
+  valu_both<7>("v_alignbit_b32");
+  valu_both<8>("v_cvt_f32_f16");
   lds(4);
   lds(8);
   lds(16);

@@ -49,3 +49,8 @@ def test_hardware_costs():
     cr = {x["what"]: x["cycles_per_iter"] for x in rows if x["what"].startswith("cross_")}
     m, v, both = cr["cross_mfma_only"], cr["cross_valu_only"], cr["cross_mfma_and_valu_waves"]
     assert max(m, v) * 1.15 < both < m + v
+    # the double-rate VALU class (fp32 fma / mul / add, bitwise and) against the single-rate
+    # class (mixed-precision fma, shifts, conversions) that the kernels' inner loops avoid
+    fast = [cyc[("valu_" + n, 8)] for n in ("v_fmac_f32", "v_mul_f32", "v_and_b32", "v_add_f32")]
+    slow = [cyc[("valu_" + n, 8)] for n in ("v_fma_mix_f32", "v_lshlrev_b32", "v_cvt_f32_f16")]
+    assert max(fast) * 1.2 < min(slow)
