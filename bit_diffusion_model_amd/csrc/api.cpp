@@ -38,11 +38,14 @@ static size_t rup(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct WsLayout {
   size_t qx, sx, la, part, total;
+  int k1parts;
 };
 // The forward path's workspace: the activation side in MMA form (INT4 FP6 operand
 // words, 64 bytes per token and group, and an fp16 scale plane; MXFP4 codes in token
 // pairs and E8M0 bytes; lora_act as bf16 hi/lo pairs in fragment order, M rounded up to
-// 32 rows), then kernel 2's partial tiles.
+// 32 rows), then one region that holds kernel 1's per-part down-projection sums (when
+// it is cut along K) and, after kernel 1's second step has added them, kernel 2's
+// partial tiles.
 static WsLayout ws_layout(const svdq_layer* L, int64_t M) {
   const bool i4 = L->fmt == SVDQ_INT4_G64;
   WsLayout w;
@@ -54,7 +57,10 @@ static WsLayout ws_layout(const svdq_layer* L, int64_t M) {
   w.la = w.sx + rup((size_t)(L->K / group_of(L->fmt)) * Mp * (i4 ? 2 : 1));
   w.part = w.la + rup((size_t)((M + 31) & ~int64_t(31)) * (size_t)((L->rank + 15) / 16 * 16) * 4);
   KernelLayer kl{L->K, L->N, L->rank, L->fmt, nullptr, nullptr, nullptr, nullptr, nullptr, 1.f, 1.f};
-  w.total = w.part + rup(plan_k2(kl, M, true).bytes);
+  w.k1parts = k1_parts(kl, M);
+  const size_t k1b = w.k1parts > 1 ? (size_t)w.k1parts * (size_t)M * (size_t)((L->rank + 15) / 16 * 16) * 4 : 0;
+  const size_t k2b = plan_k2(kl, M, true).bytes;
+  w.total = w.part + rup(k1b > k2b ? k1b : k2b);
   return w;
 }
 
@@ -85,7 +91,8 @@ static svdq_status check_form(int32_t form) {
 }
 
 static svdq_status run_k1(const svdq_layer* layer, int64_t M, const uint16_t* X, int64_t ldx,
-                          int32_t form, uint8_t* qX, void* sX, void* lora_act, void* stream) {
+                          int32_t form, uint8_t* qX, void* sX, void* lora_act, void* stream, int parts = 1,
+                          float* part_out = nullptr) {
   KernelLayer kl;
   svdq_status st = check_layer(layer, kl);
   if (st != SVDQ_OK) return st;
@@ -99,7 +106,8 @@ static svdq_status run_k1(const svdq_layer* layer, int64_t M, const uint16_t* X,
   if (M * kl.K >= (int64_t(1) << 35)) return fail(SVDQ_EUNSUPPORTED, "M * K must be < 2^35");
   if (!aligned(X, 16) || !aligned(qX, 16) || !aligned(sX, 2) || (lora_act && !aligned(lora_act, 16)))
     return fail(SVDQ_EINVAL, "X, qX and lora_act must be 16-byte aligned");
-  hipError_t e = launch_k1(kl, M, X, ldx, qX, sX, lora_act, form == SVDQ_ACT_MMA, (hipStream_t)stream);
+  hipError_t e = launch_k1(kl, M, X, ldx, qX, sX, lora_act, form == SVDQ_ACT_MMA, (hipStream_t)stream, parts,
+                           part_out);
   if (e != hipSuccess) return fail(SVDQ_EHIP, "kernel 1 launch: %s", hipGetErrorString(e));
   return ok();
 }
@@ -171,7 +179,8 @@ svdq_status svdq::linear_forward(const svdq_layer* layer, int64_t M, const uint1
   uint8_t* qX = base + w.qx;
   void* sX = base + w.sx;
   void* la = kl.rank > 0 ? base + w.la : nullptr;
-  st = run_k1(layer, M, X, ldx, SVDQ_ACT_MMA, qX, sX, la, stream);
+  st = run_k1(layer, M, X, ldx, SVDQ_ACT_MMA, qX, sX, la, stream, w.k1parts,
+              reinterpret_cast<float*>(base + w.part));
   if (st != SVDQ_OK) return st;
   return run_k2(layer, M, SVDQ_ACT_MMA, qX, sX, la, Y, ldy, ydtype, base + w.part, w.total - w.part, stream);
 }

@@ -285,7 +285,8 @@ svdq_status svdq_gemm_w4a4_lora_up(const svdq_layer* layer, int64_t M, int32_t f
 size_t svdq_gemm_workspace_bytes(const svdq_layer* layer, int64_t M, int32_t form);
 
 /* Bytes of device workspace svdq_linear_forward needs for M rows on the current device:
- * the MMA-form qX, sX and lora_act and kernel 2's split workspace, each 256-byte
+ * the MMA-form qX, sX and lora_act, then one region for kernel 1's per-part sums (when
+ * it is cut along K) and, after them, kernel 2's split workspace; each 256-byte
  * aligned. */
 size_t svdq_workspace_bytes(const svdq_layer* layer, int64_t M);
 
@@ -297,7 +298,12 @@ size_t svdq_workspace_bytes(const svdq_layer* layer, int64_t M);
  * with the activation side in MMA form, intermediates in `workspace` (device, >=
  * svdq_workspace_bytes, 256-byte aligned, caller-owned; its contents on entry do not
  * matter).  The same launches as the two calls above with form = SVDQ_ACT_MMA and
- * kernel 2 given its split workspace: the results are identical bit for bit.
+ * kernel 2 given its split workspace, and the results identical bit for bit, except at
+ * K >= 8192 with rank > 0 and at most two 16-token blocks per compute unit
+ * (ceil(M / 16) <= 2 x CUs): there kernel 1 runs cut into 4 contiguous ranges of its
+ * 64-wide chunks, one block per range, and a second small kernel adds the ranges' fp32
+ * down-projection sums in range order.  Codes and scales are the same; lora_act differs
+ * from the one-pass kernel only in the order of its fp32 additions (deterministic).
  *   X  device bf16 [M][ldx] (16-byte aligned rows); Y device [M][ldy], svdq_dtype
  *   ydtype, overwritten; columns >= N of each Y row are not touched.
  * M == 0 is a no-op.  EINVAL on NULL / misalignment / small workspace; EUNSUPPORTED on

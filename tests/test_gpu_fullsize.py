@@ -118,11 +118,25 @@ def test_full_size_layer(name):
                                       wl.fmt, K, r, M=M)
         np.testing.assert_array_equal(c_m, qX_ref)
         np.testing.assert_array_equal(s_m, sX_ref)
-    np.testing.assert_array_equal(hi, bf16_rne_bits(la_g))
-    rem = la_g - (hi.astype(np.uint32) << 16).view(np.float32)
-    np.testing.assert_array_equal(lo, bf16_rne_bits(rem))
+    split_k1 = wl.total_rank > 0 and K >= 8192 and \
+        (M + 15) // 16 <= 2 * torch.cuda.get_device_properties(0).multi_processor_count
+    if split_k1:
+        # the forward cut kernel 1 along K: its fp32 down-projection sums came in another
+        # order than the one-pass packed call's, so hi + lo is held to the error budget
+        v = (hi.astype(np.uint32) << 16).view(np.float32).astype(np.float64) + \
+            (lo.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        assert np.all(np.abs(v[:, :r] - la_ref) <= lora_bound(Xh, p["L1b"]) + 2.0 ** -16 * np.abs(la_ref))
+        assert np.all(np.abs(v[:, :r] - la_g[:, :r]) <= 2.0 ** -14 * np.abs(la_g[:, :r]) +
+                      2 * lora_bound(Xh, p["L1b"]))
+        assert not v[:, r:].any()
+        rem = None
+        log("  kernel 1 (MMA form, forward workspace, cut along K) codes and scales bit-exact, lora_act in budget")
+    else:
+        np.testing.assert_array_equal(hi, bf16_rne_bits(la_g))
+        rem = la_g - (hi.astype(np.uint32) << 16).view(np.float32)
+        np.testing.assert_array_equal(lo, bf16_rne_bits(rem))
+        log("  kernel 1 (MMA form, forward workspace) bit-exact")
     del ws, c_m, hi, lo, rem
-    log("  kernel 1 (MMA form, forward workspace) bit-exact")
 
     # ---- kernel 2's exact group sums (INT4)
     if wl.fmt == "int4":
@@ -154,7 +168,10 @@ def test_full_size_layer(name):
     _check_y(Yu, Yref, "unfused baseline")
     d = float((Yu - Y).abs().max()) / float(np.sqrt(np.mean(Yref ** 2)))
     log(f"  max|Y_unfused - Y|/RMS = {d:.3e}")
-    assert d <= 1e-5
+    # the unfused branch's down projection is one pass over K; where the forward cut
+    # kernel 1 along K the two add the same fp32 terms in another order (K = 12288:
+    # measured 2.1e-5)
+    assert d <= (1e-4 if split_k1 else 1e-5)
     del Yu, Y, lay
 
     # ---- end to end: the library's pack through the forward, against oracle pack + oracle forward

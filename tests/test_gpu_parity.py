@@ -140,6 +140,70 @@ def test_forward_kernel2_exact_with_unit_scales(shape):
         assert gws is not None, "expected kernel 2 to split this shape"
 
 
+@pytest.mark.parametrize("shape", [(100, 8320, 96, 32, "int4"), (100, 8192, 96, 32, "mxfp4"),
+                                   (37, 8192, 64, 16, "nvfp4")], ids=_ids)
+def test_forward_long_k_split(shape):
+    """At K >= 8192 (and at most two 16-token blocks per CU) the forward cuts kernel 1's
+    chunks along K into 4 ranges (K = 8320: 130 chunks, ranges of 32 and 33) and adds the
+    ranges' down-projection sums in a second step.  Codes and scales stay bit-exact;
+    lora_act keeps the arithmetic's error budget (only the order of its fp32 additions
+    differs from the single-pass kernel 1); Y meets the bar; repeated calls give the same
+    bits."""
+    import torch
+
+    M, K, N, r, fmt = shape
+    log(f"forward, kernel 1 cut along K: {_ids(shape)}")
+    wl = random_layer(M, K, N, r, 9100 + M + K + N, fmt=fmt, x_out=3, w_out=2)
+    p = oracle_pack(wl)
+    lay = layer_from_oracle(p)
+    X = to_dev_bf16(wl.X)
+    Yd, ws = forward_sentinel(lay, X)
+    assert_finite(Yd)
+    Yref = oforward.forward(wl.X, p)["Y"]
+    e = rel_err(Yd.cpu().numpy().astype(np.float64), Yref)
+    log(f"  max|err|/RMS = {e:.3e}")
+    assert e <= TOL_Y
+    Xh, _, _, qX_ref, sX_ref, la_ref = oracle_k1(wl.X, p)
+    Mp = (M + 3) // 4 * 4
+    if fmt == "int4":
+        sx0 = (M * K + 255) // 256 * 256
+        la0 = sx0 + ((K // 64) * Mp * 2 + 255) // 256 * 256
+        c_m, s_m, hi, lo = decode_mma(ws[:M * K].view(M, K), ws[sx0:sx0 + (K // 64) * Mp * 2], ws[la0:], fmt, K, r,
+                                      M=M)
+        _, codes_ref, _, _, _, _ = oracle_k1(wl.X, p)
+        np.testing.assert_array_equal(c_m, codes_ref)
+        np.testing.assert_array_equal(s_m, sX_ref.view(np.float16).astype(np.float64))
+    else:
+        G = 32 if fmt == "mxfp4" else 16
+        nq = (M + 1) // 2 * 2 * (K // 2)
+        sx0 = (nq + 255) // 256 * 256
+        la0 = sx0 + ((K // G) * Mp + 255) // 256 * 256
+        c_m, s_m, hi, lo = decode_mma(ws[:M * (K // 2)].view(M, K // 2), ws[sx0:sx0 + (K // G) * Mp], ws[la0:], fmt,
+                                      K, r, M=M)
+        np.testing.assert_array_equal(c_m, qX_ref)
+        np.testing.assert_array_equal(s_m, sX_ref)
+    # hi + lo carries the fp32 sum to 2^-17 of its size
+    v = (hi.astype(np.uint32) << 16).view(np.float32).astype(np.float64) + \
+        (lo.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    R16 = (r + 15) // 16 * 16
+    assert not v[:, r:].any()
+    err = np.abs(v[:, :r] - la_ref)
+    assert np.all(err <= lora_bound(Xh, p["L1b"]) + 2.0 ** -16 * np.abs(la_ref)), float(err.max())
+    assert v.shape == (M, R16)
+    # against the two kernels called one after the other (kernel 1 in one pass)
+    qX, sX, la = lay.quantize_act(X, out=sentinel_act(lay, M, svdq.ACT_MMA), form=svdq.ACT_MMA)
+    Y2 = lay.gemm(qX, sX, la, out=sentinel_out(M, N), form=svdq.ACT_MMA,
+                  workspace=sentinel_gemm_ws(lay, M, svdq.ACT_MMA)).cpu().numpy().astype(np.float64)
+    Yg = Yd.cpu().numpy().astype(np.float64)
+    e2 = rel_err(Yg, Y2)
+    log(f"  forward against the one-pass kernel 1 path: max|dY|/RMS = {e2:.2e}")
+    # the same fp32 terms of the down projection added in another order (the outlier
+    # channels make single terms large against the sums: measured 2.5e-5 at K = 8320)
+    assert e2 <= 1e-4
+    Y3 = lay.forward(X, workspace=ws)
+    assert torch.equal(Y3, Yd)
+
+
 @pytest.mark.parametrize("shape", SHAPES, ids=_ids)
 def test_forward_matches_oracle(shape):
     M, K, N, r, fmt = shape
