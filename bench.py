@@ -312,16 +312,26 @@ def measure(svdq, torch, wl_name, ydt, steps, warmup, warm_s, compare, log_prefi
     qX, sX, la = lay.alloc_act(M, svdq.ACT_MMA)
     gws = lay.gemm_workspace(M, svdq.ACT_MMA)
     nrep = max(steps, 10)
-    e = [torch.cuda.Event(enable_timing=True) for _ in range(3 * nrep)]
+    k1_parts = lay.forward_k1_parts(M)
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(4 * nrep)]
     for i in range(nrep):
-        e[3 * i].record()
+        e[4 * i].record()
         lay.quantize_act(X, (qX, sX, la), form=svdq.ACT_MMA)
-        e[3 * i + 1].record()
+        e[4 * i + 1].record()
         lay.gemm(qX, sX, la, ydt, Y, form=svdq.ACT_MMA, workspace=gws)
-        e[3 * i + 2].record()
+        e[4 * i + 2].record()
+        if k1_parts > 1:
+            step()
+        e[4 * i + 3].record()
     torch.cuda.synchronize()
-    t_k1 = float(np.mean([e[3 * i].elapsed_time(e[3 * i + 1]) for i in range(nrep)])) * 1e-3
-    t_k2 = float(np.mean([e[3 * i + 1].elapsed_time(e[3 * i + 2]) for i in range(nrep)])) * 1e-3
+    t_k1 = float(np.mean([e[4 * i].elapsed_time(e[4 * i + 1]) for i in range(nrep)])) * 1e-3
+    t_k2 = float(np.mean([e[4 * i + 1].elapsed_time(e[4 * i + 2]) for i in range(nrep)])) * 1e-3
+    t_k1_one_pass = t_k1
+    if k1_parts > 1:
+        # the forward cuts kernel 1 along K (no entry point launches that form alone): its
+        # share of the forward is the forward's time less kernel 2's
+        t_fwd = float(np.mean([e[4 * i + 2].elapsed_time(e[4 * i + 3]) for i in range(nrep)])) * 1e-3
+        t_k1 = t_fwd - t_k2
     # low-rank overhead: the layer against a rank-0 layer with the same codes, and against
     # the unfused baseline (the low-rank branch as kernels of its own), timed in alternating
     # blocks of 20 forwards (medians of 5), so all three see the same clocks
@@ -370,7 +380,8 @@ def measure(svdq, torch, wl_name, ydt, steps, warmup, warm_s, compare, log_prefi
     res = dict(wl=wl, M=M, K=K, N=N, r=r, fmt=fmt, ms=ms, tops=tops, t_k1=t_k1, t_k2=t_k2, k2_tops=k2_tops,
                k1_bytes=k1_bytes, warm_steps=n)
     res["kernels"] = {
-        "k1_us": round(t_k1 * 1e6, 2), "k2_us": round(t_k2 * 1e6, 2),
+        "k1_us": round(t_k1 * 1e6, 2), "k2_us": round(t_k2 * 1e6, 2), "k1_forward_parts": k1_parts,
+        "k1_one_pass_us": round(t_k1_one_pass * 1e6, 2),
         "k1_GBps": round(k1_bytes / t_k1 / 1e9, 1), "k1_hbm_frac": round(k1_bytes / t_k1 / 1e9 / PEAK_HBM_GBS, 4),
         "k2_TOPS": round(k2_tops, 2),
         # the INT4 contraction runs on the FP6 scaled MFMA (10.1 PF dense); against the

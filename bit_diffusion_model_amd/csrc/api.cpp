@@ -75,6 +75,11 @@ size_t svdq_workspace_bytes(const svdq_layer* layer, int64_t M) {
   return ws_layout(layer, M).total;
 }
 
+int32_t svdq_forward_k1_parts(const svdq_layer* layer, int64_t M) {
+  if (!layer || M < 0 || check_dims(layer->K, layer->N, layer->fmt) != SVDQ_OK) return 0;
+  return ws_layout(layer, M).k1parts;
+}
+
 size_t svdq_gemm_workspace_bytes(const svdq_layer* layer, int64_t M, int32_t form) {
   if (!layer || M < 1 || check_dims(layer->K, layer->N, layer->fmt) != SVDQ_OK) return 0;
   KernelLayer kl{layer->K, layer->N, layer->rank, layer->fmt, nullptr, nullptr, nullptr, nullptr, nullptr, 1.f, 1.f};

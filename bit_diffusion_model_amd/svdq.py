@@ -47,7 +47,7 @@ EXPORTS = [
     "svdq_quantize_act_lora_down", "svdq_gemm_w4a4_lora_up", "svdq_gemm_workspace_bytes", "svdq_workspace_bytes",
     "svdq_linear_forward", "svdq_linear_forward_unfused", "svdq_debug_group_sums", "svdq_linear_forward_noalloc",
     "svdq_mlp_workspace_bytes", "svdq_mlp_forward", "svdq_mlp_chain_gemm", "svdq_mlp_chain_reduce",
-    "svdq_w4a16_gemm",
+    "svdq_w4a16_gemm", "svdq_forward_k1_parts",
 ]
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
@@ -76,6 +76,7 @@ def lib():
         "svdq_gemm_w4a4_lora_up": (I32, [P, I64, I32, P, P, P, P, I64, I32, P, ctypes.c_size_t, P]),
         "svdq_gemm_workspace_bytes": (ctypes.c_size_t, [P, I64, I32]),
         "svdq_workspace_bytes": (ctypes.c_size_t, [P, I64]),
+        "svdq_forward_k1_parts": (I32, [P, I64]),
         "svdq_linear_forward": (I32, [P, I64, P, I64, P, I64, I32, P, ctypes.c_size_t, P]),
         "svdq_linear_forward_unfused": (I32, [P, I64, P, I64, P, I64, I32, P, ctypes.c_size_t, P]),
         "svdq_debug_group_sums": (I32, [P, I64, I32, P, I64, I64, I64, I64, P, P]),
@@ -391,6 +392,10 @@ class PackedLinear:
         torch = _torch()
         n = lib().svdq_workspace_bytes(self.c_layer(), M)
         return torch.empty(max(n, 256), dtype=torch.uint8, device=self.device)
+
+    def forward_k1_parts(self, M: int) -> int:
+        """svdq_forward_k1_parts: the K ranges the forward cuts kernel 1 into (1: one pass)."""
+        return int(lib().svdq_forward_k1_parts(self.c_layer(), M))
 
     def forward(self, X, ydtype: int = F32, out=None, workspace=None, fused: bool = True):
         """The public layer: svdq_linear_forward (kernel 1 then kernel 2), or with

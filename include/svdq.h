@@ -290,6 +290,12 @@ size_t svdq_gemm_workspace_bytes(const svdq_layer* layer, int64_t M, int32_t for
  * aligned. */
 size_t svdq_workspace_bytes(const svdq_layer* layer, int64_t M);
 
+/* The number of contiguous K ranges svdq_linear_forward cuts kernel 1 into for M rows on
+ * the current device (1: one pass; 4 at K >= 8192 with rank > 0 and ceil(M / 16) <= 2 x
+ * CUs), for callers that time or reproduce the forward's launches.  Returns 0 for a
+ * NULL layer, bad dimensions or M < 0. */
+int32_t svdq_forward_k1_parts(const svdq_layer* layer, int64_t M);
+
 /* The public layer Y = Q(X diag(s)^-1) Q(R) + (X diag(s)^-1 L1) L2 (decomposition
  * equation of the jeonghoonpark.com "SVDQuant" review, section 4.2), computed the way
  * the review's section 4.3 ("Nunchaku", Figure 6(b)) fuses it: two kernels instead of

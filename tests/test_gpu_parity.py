@@ -156,6 +156,8 @@ def test_forward_long_k_split(shape):
     wl = random_layer(M, K, N, r, 9100 + M + K + N, fmt=fmt, x_out=3, w_out=2)
     p = oracle_pack(wl)
     lay = layer_from_oracle(p)
+    assert lay.forward_k1_parts(M) == 4
+    assert lay.forward_k1_parts(64 * torch.cuda.get_device_properties(0).multi_processor_count) == 1
     X = to_dev_bf16(wl.X)
     Yd, ws = forward_sentinel(lay, X)
     assert_finite(Yd)

@@ -383,6 +383,11 @@ def test_device_entry_points_validate_on_host():
     # MMA form: FP6 operand words (M*K bytes), fp16 scales (2 bytes per group and row),
     # 2*R16 bf16 per row, rows rounded up to 32
     assert L.svdq_workspace_bytes(ref, 100) >= 100 * 256 + 4 * 100 * 2 + 128 * 16 * 4
+    # kernel 1 in one pass at short K; the query refuses what the workspace size refuses
+    assert L.svdq_forward_k1_parts(ref, 100) == 1
+    assert L.svdq_forward_k1_parts(None, 100) == 0 and L.svdq_forward_k1_parts(ref, -1) == 0
+    bad = svdq._Layer(100, 64, 8, 0, 16, 16, 16, 16, 16)  # K not a multiple of 128
+    assert L.svdq_forward_k1_parts(ctypes.byref(bad), 4) == 0
 
 
 def test_mlp_entry_points_validate_on_host():
