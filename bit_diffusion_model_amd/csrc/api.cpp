@@ -111,6 +111,8 @@ static svdq_status run_k1(const svdq_layer* layer, int64_t M, const uint16_t* X,
   if (M * kl.K >= (int64_t(1) << 35)) return fail(SVDQ_EUNSUPPORTED, "M * K must be < 2^35");
   if (!aligned(X, 16) || !aligned(qX, 16) || !aligned(sX, 2) || (lora_act && !aligned(lora_act, 16)))
     return fail(SVDQ_EINVAL, "X, qX and lora_act must be 16-byte aligned");
+  // at rank 0 the cut needs no workspace, so every kernel-1 launch takes it
+  if (kl.rank == 0) parts = k1_parts(kl, M);
   hipError_t e = launch_k1(kl, M, X, ldx, qX, sX, lora_act, form == SVDQ_ACT_MMA, (hipStream_t)stream, parts,
                            part_out);
   if (e != hipSuccess) return fail(SVDQ_EHIP, "kernel 1 launch: %s", hipGetErrorString(e));

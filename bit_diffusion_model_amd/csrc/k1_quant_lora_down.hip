@@ -315,7 +315,7 @@ template <int FMT, bool MMA>
 static hipError_t launch_k1_fmt(const KernelLayer& L, int64_t M, const uint16_t* X, int64_t ldx,
                                 uint8_t* qX, void* sX, void* lora_act, int parts, float* part_out, hipStream_t st) {
   const int nt = (L.rank + 15) / 16;
-  if (nt == 0 || !part_out || parts < 1) parts = 1;
+  if (parts < 1 || (nt > 0 && !part_out)) parts = 1;  // rank 0: nothing to add across parts
   const dim3 grid((unsigned)((M + 15) / 16 * parts));
   // NVFP4 level-2 scale of the activations and fp32(1 / fp32(6 S_X))
   const float tsx = L.tscale_x, r6x = FMT == 2 ? 1.0f / (6.0f * L.tscale_x) : 0.0f;
@@ -331,7 +331,7 @@ static hipError_t launch_k1_fmt(const KernelLayer& L, int64_t M, const uint16_t*
     default: return hipErrorInvalidValue;
   }
 #undef K1_CASE
-  if (parts > 1) {
+  if (parts > 1 && nt > 0) {
     const int64_t total = M * nt * 16;
     hipLaunchKernelGGL((k1_lora_sum<MMA>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, part_out, parts,
                        M, nt * 16, static_cast<float*>(lora_act));
@@ -372,8 +372,9 @@ int k1_parts(const KernelLayer& L, int64_t M) {
   // Long K only: there each block of 16 tokens walks many chunks, and the blocks past one
   // per CU double the time of the CUs that hold them; cut into 4 parts, every CU holds
   // about the same number of part blocks.  At short K the fixed cost of the extra launch
-  // and the partial sums outweighs that.
-  if (L.rank <= 0 || L.K < 8192) return 1;
+  // and the partial sums outweighs that.  (At rank 0 there is nothing to add across the
+  // parts.)
+  if (L.K < 8192) return 1;
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
                                                hipSuccess || cus < 1)

@@ -20,10 +20,11 @@ struct KernelLayer {
 // mma: the activation side in the matrix-core operand form (INT4 FP6 operand words,
 // fp16 scales; lora_act as bf16 hi/lo pairs in fragment order) instead of the packed
 // storage form (4-bit codes [M][K/2], fp16 / E8M0 scales, fp32 lora_act).
-// parts > 1 (with part_out, device, parts * M * R16 fp32, R16 = rank rounded up to 16):
-// the chunks along K are cut into `parts` ranges, one block per range and 16 tokens, whose
-// fp32 down-projection sums are added in part order by a second kernel (codes and scales
-// are the same as unsplit; lora_act differs only in the order of its fp32 additions).
+// parts > 1 (with part_out, device, parts * M * R16 fp32, R16 = rank rounded up to 16;
+// not needed at rank 0): the chunks along K are cut into `parts` ranges, one block per
+// range and 16 tokens, whose fp32 down-projection sums are added in part order by a second
+// kernel (codes and scales are the same as unsplit; lora_act differs only in the order of
+// its fp32 additions).
 hipError_t launch_k1(const KernelLayer& L, int64_t M, const uint16_t* X, int64_t ldx, uint8_t* qX,
                      void* sX, void* lora_act, bool mma, hipStream_t st, int parts = 1, float* part_out = nullptr);
 // The number of parts the forward uses for kernel 1 (1: unsplit).

@@ -255,6 +255,8 @@ svdq_status svdq_prepare_weights(int64_t K, int64_t N, int32_t fmt, const uint8_
  *   sX       device                       their group scales
  *   lora_act device                       X_hat L1, columns >= rank written as zero
  *                                         (unused when rank == 0)
+ * One launch (at rank 0, K >= 8192 and ceil(M / 16) <= 2 x CUs: the chunks of 64 along K
+ * cut into 4 contiguous ranges, one block each, the same codes and scales).
  * M == 0 is a no-op.  EINVAL on NULL / misalignment / ldx < K; EUNSUPPORTED when
  * M * K >= 2^35 (the scale planes are addressed through 32-bit offsets); EHIP on launch
  * error. */
@@ -291,9 +293,9 @@ size_t svdq_gemm_workspace_bytes(const svdq_layer* layer, int64_t M, int32_t for
 size_t svdq_workspace_bytes(const svdq_layer* layer, int64_t M);
 
 /* The number of contiguous K ranges svdq_linear_forward cuts kernel 1 into for M rows on
- * the current device (1: one pass; 4 at K >= 8192 with rank > 0 and ceil(M / 16) <= 2 x
- * CUs), for callers that time or reproduce the forward's launches.  Returns 0 for a
- * NULL layer, bad dimensions or M < 0. */
+ * the current device (1: one pass; 4 at K >= 8192 and ceil(M / 16) <= 2 x CUs), for
+ * callers that time or reproduce the forward's launches.  Returns 0 for a NULL layer,
+ * bad dimensions or M < 0. */
 int32_t svdq_forward_k1_parts(const svdq_layer* layer, int64_t M);
 
 /* The public layer Y = Q(X diag(s)^-1) Q(R) + (X diag(s)^-1 L1) L2 (decomposition
@@ -309,7 +311,9 @@ int32_t svdq_forward_k1_parts(const svdq_layer* layer, int64_t M);
  * (ceil(M / 16) <= 2 x CUs): there kernel 1 runs cut into 4 contiguous ranges of its
  * 64-wide chunks, one block per range, and a second small kernel adds the ranges' fp32
  * down-projection sums in range order.  Codes and scales are the same; lora_act differs
- * from the one-pass kernel only in the order of its fp32 additions (deterministic).
+ * from the one-pass kernel only in the order of its fp32 additions (deterministic).  (At
+ * rank 0 kernel 1 has no sums to add, and svdq_quantize_act_lora_down takes the same
+ * cut itself.)
  *   X  device bf16 [M][ldx] (16-byte aligned rows); Y device [M][ldy], svdq_dtype
  *   ydtype, overwritten; columns >= N of each Y row are not touched.
  * M == 0 is a no-op.  EINVAL on NULL / misalignment / small workspace; EUNSUPPORTED on
