@@ -324,7 +324,7 @@ svdq_status svdq_linear_forward(const svdq_layer* layer, int64_t M, const uint16
 
 /* Size in bytes of the fixed device array svdq_linear_forward_noalloc uses as its
  * workspace (one per device): 64 MiB, enough for every FLUX.1 layer workload of this
- * library (the largest, the MLP fc2 layer at 4608 tokens, needs about 59 MB). */
+ * library (the largest, the MLP fc2 layer at 4608 tokens, needs about 62 MB). */
 #define SVDQ_NOALLOC_SCRATCH_BYTES (64u << 20)
 
 /* For callers that cannot allocate device memory (code under HIP stream capture, serving
