@@ -334,7 +334,8 @@ def _ws_lora_region(M, K, rank, fmt):
     rup = lambda x: (x + 255) // 256 * 256
     Mp = (M + 3) // 4 * 4
     qx = M * K if fmt == "int4" else (M + 1) // 2 * 2 * (K // 2)
-    sx = (K // 64) * Mp * 2 if fmt == "int4" else (K // 32) * Mp
+    # scale planes: INT4 fp16 [K/64][Mp], MXFP4 E8M0 [K/32][Mp], NVFP4 E4M3 [K/64][Mp][4]
+    sx = {"int4": (K // 64) * Mp * 2, "mxfp4": (K // 32) * Mp, "nvfp4": (K // 16) * Mp}[fmt]
     off = rup(qx) + rup(sx)
     return off, off + (M + 31) // 32 * 32 * ((rank + 15) // 16 * 16) * 4
 
