@@ -518,6 +518,54 @@ def measure_w4a16(svdq, torch, steps, warm_s, w4a4_ms, mxfp4_ms):
             "library_bf16_gemm_TFLOPs": round(flops / (ms_l * 1e-3) / 1e12, 2)}
 
 
+def k1_sweep(svdq, torch):
+    """Kernel 1 alone (svdq_quantize_act_lora_down, MMA form) against the token count, per
+    format, at K = 3072: random N(0,1) bf16 tokens, unit smoothing factors and random bf16
+    down-projection factors (kernel 1's work does not depend on the values).  Best of 5
+    blocks of 50 back-to-back launches, HIP events on the launch stream, in us."""
+    rng = np.random.default_rng(7)
+    K, N = 3072, 256
+
+    def bf(a):
+        return ((a.astype(np.float32).view(np.uint32) + 0x8000) >> 16).astype(np.uint16)
+
+    def layer(rank, fmt):
+        L1t = bf(rng.standard_normal((rank, K)) * 0.02) if rank else None
+        L2 = bf(rng.standard_normal((rank, N)) * 0.02) if rank else None
+        qW = np.zeros((K, N // 2), np.uint8)
+        sW = {svdq.INT4_G64: np.ones((K // 64, N), np.float16).view(np.uint16),
+              svdq.MXFP4_G32: np.full((K // 32, N), 127, np.uint8),
+              svdq.NVFP4_G16: np.full((K // 16, N), 0x38, np.uint8)}[fmt]
+        return svdq.PackedLinear(K, N, rank, fmt, np.ones(K, np.float32), L1t, L2, qW, sW)
+
+    stream = torch.cuda.current_stream()
+    res = {}
+    for name, rank, fmt in (("int4_r32", 32, svdq.INT4_G64), ("int4_r0", 0, svdq.INT4_G64),
+                            ("mxfp4_r32", 32, svdq.MXFP4_G32), ("nvfp4_r32", 32, svdq.NVFP4_G16)):
+        lay = layer(rank, fmt)
+        row = {}
+        for M in (256, 2048, 4096, 4608, 8192, 9216):
+            X = torch.randn(M, K, device="cuda:0").to(torch.bfloat16).view(torch.int16)
+            bufs = lay.alloc_act(M, svdq.ACT_MMA)
+            for _ in range(20):
+                lay.quantize_act(X, bufs, form=svdq.ACT_MMA)
+            best = float("inf")
+            for _ in range(5):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(50):
+                    lay.quantize_act(X, bufs, form=svdq.ACT_MMA)
+                e1.record(stream)
+                e1.synchronize()
+                best = min(best, e0.elapsed_time(e1) * 1000 / 50)
+            row[str(M)] = round(best, 2)
+            log(f"[k1 sweep] {name} M={M} ({(M + 15) // 16} blocks of 16 tokens): {best:.2f} us")
+            del X, bufs
+        res[name] = row
+    return {"k1_sweep_us": res, "K": K, "blocks": "ceil(M / 16), 8 waves each",
+            "note": "kernel 1 alone, MMA form, best of 5 x 50 back-to-back launches"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -541,6 +589,9 @@ def main():
                     help="compute kernel 1's and kernel 2's HBM bytes per launch from two rocprofv3 "
                          "--pmc CSVs (FETCH_SIZE, WRITE_SIZE) of runs made with --calib-copy, write the "
                          "summary JSON, and exit")
+    ap.add_argument("--k1-sweep", action="store_true",
+                    help="time kernel 1 alone per format against the token count (K = 3072), print one "
+                         "JSON line and exit")
     ap.add_argument("--write-counters", nargs=2, metavar=("PASS_A_CSV", "PASS_B_CSV"),
                     help="summarise two rocprofv3 --pmc utilisation passes of kernels 1 and 2 (MFMA and "
                          "VALU busy, co-issue, LDS, L2), write the summary JSON, and exit")
@@ -565,6 +616,9 @@ def main():
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
+    if args.k1_sweep:
+        print(json.dumps(k1_sweep(svdq, torch)), flush=True)
+        return
     ydt = svdq.F32 if args.ydtype == "f32" else svdq.BF16
     m = measure(svdq, torch, args.workload, ydt, args.steps, args.warmup, args.warm_seconds, not args.no_compare,
                 dist=not args.no_compare)

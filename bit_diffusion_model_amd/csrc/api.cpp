@@ -38,7 +38,7 @@ static size_t rup(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct WsLayout {
   size_t qx, sx, la, part, total;
-  int k1parts;
+  int k1parts, k1full;
 };
 // The forward path's workspace: the activation side in MMA form (INT4 FP6 operand
 // words, 64 bytes per token and group, and an fp16 scale plane; MXFP4 codes in token
@@ -57,8 +57,12 @@ static WsLayout ws_layout(const svdq_layer* L, int64_t M) {
   w.la = w.sx + rup((size_t)(L->K / group_of(L->fmt)) * Mp * (i4 ? 2 : 1));
   w.part = w.la + rup((size_t)((M + 31) & ~int64_t(31)) * (size_t)((L->rank + 15) / 16 * 16) * 4);
   KernelLayer kl{L->K, L->N, L->rank, L->fmt, nullptr, nullptr, nullptr, nullptr, nullptr, 1.f, 1.f};
-  w.k1parts = k1_parts(kl, M);
-  const size_t k1b = w.k1parts > 1 ? (size_t)w.k1parts * (size_t)M * (size_t)((L->rank + 15) / 16 * 16) * 4 : 0;
+  const K1Cut cut = k1_cut(kl, M);
+  w.k1parts = cut.parts;
+  w.k1full = cut.full;
+  const size_t k1b = w.k1parts > 1 ? (size_t)w.k1parts * (size_t)(M - 16 * (int64_t)w.k1full) *
+                                         (size_t)((L->rank + 15) / 16 * 16) * 4
+                                   : 0;
   const size_t k2b = plan_k2(kl, M, true).bytes;
   w.total = w.part + rup(k1b > k2b ? k1b : k2b);
   return w;
@@ -97,7 +101,7 @@ static svdq_status check_form(int32_t form) {
 
 static svdq_status run_k1(const svdq_layer* layer, int64_t M, const uint16_t* X, int64_t ldx,
                           int32_t form, uint8_t* qX, void* sX, void* lora_act, void* stream, int parts = 1,
-                          float* part_out = nullptr) {
+                          float* part_out = nullptr, int full = 0) {
   KernelLayer kl;
   svdq_status st = check_layer(layer, kl);
   if (st != SVDQ_OK) return st;
@@ -112,9 +116,13 @@ static svdq_status run_k1(const svdq_layer* layer, int64_t M, const uint16_t* X,
   if (!aligned(X, 16) || !aligned(qX, 16) || !aligned(sX, 2) || (lora_act && !aligned(lora_act, 16)))
     return fail(SVDQ_EINVAL, "X, qX and lora_act must be 16-byte aligned");
   // at rank 0 the cut needs no workspace, so every kernel-1 launch takes it
-  if (kl.rank == 0) parts = k1_parts(kl, M);
+  if (kl.rank == 0) {
+    const K1Cut cut = k1_cut(kl, M);
+    parts = cut.parts;
+    full = cut.full;
+  }
   hipError_t e = launch_k1(kl, M, X, ldx, qX, sX, lora_act, form == SVDQ_ACT_MMA, (hipStream_t)stream, parts,
-                           part_out);
+                           part_out, full);
   if (e != hipSuccess) return fail(SVDQ_EHIP, "kernel 1 launch: %s", hipGetErrorString(e));
   return ok();
 }
@@ -187,7 +195,7 @@ svdq_status svdq::linear_forward(const svdq_layer* layer, int64_t M, const uint1
   void* sX = base + w.sx;
   void* la = kl.rank > 0 ? base + w.la : nullptr;
   st = run_k1(layer, M, X, ldx, SVDQ_ACT_MMA, qX, sX, la, stream, w.k1parts,
-              reinterpret_cast<float*>(base + w.part));
+              reinterpret_cast<float*>(base + w.part), w.k1full);
   if (st != SVDQ_OK) return st;
   return run_k2(layer, M, SVDQ_ACT_MMA, qX, sX, la, Y, ldy, ydtype, base + w.part, w.total - w.part, stream);
 }

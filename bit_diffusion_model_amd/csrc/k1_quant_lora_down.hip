@@ -10,9 +10,10 @@
 //
 // Work split: a block of 8 waves owns 16 consecutive tokens.  The K dimension is cut
 // into 64-wide chunks; wave w takes chunks w, w+8, ..., with the next chunk's X, inv_s
-// and L1 loads issued before the current chunk is processed.  (At long K the chunks can
+// and L1 loads issued before the current chunk is processed.  (The chunks of a block can
 // also be cut into a few contiguous ranges, one block each, with the down-projection
-// sums of the ranges added by a second small kernel.)  Inside a chunk, lane l holds
+// sums of the ranges added by a second small kernel: every block at long K, and at
+// short K only the blocks of a last, partly filled round of one block per CU.)  Inside a chunk, lane l holds
 // token (l & 15) and the 16 consecutive channels 16 * (l >> 4) .. +15.  One INT4 group
 // (64) is therefore spread over the 4 lanes l, l^16, l^32, l^48; one MXFP4 group (32)
 // over lanes l, l^16; an NVFP4 group (16) is one lane's 16 values.  X is loaded row-contiguously instead (each 16-byte load covers 8
@@ -60,20 +61,25 @@ __global__ __launch_bounds__(64 * K1_WAVES) __attribute__((amdgpu_waves_per_eu(N
 k1_quant_lora_down(const uint16_t* __restrict__ X, int64_t ldx, int64_t M, int64_t K,
                    const float* __restrict__ inv_s, const uint16_t* __restrict__ L1f, int rank,
                    uint8_t* __restrict__ qX, void* __restrict__ sXv, float* __restrict__ lora_act,
-                   float tsx, float r6x, int parts, float* __restrict__ part_out) {
+                   float tsx, float r6x, int parts, float* __restrict__ part_out, int full) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int r16 = lane & 15;
   const int sub = lane >> 4;
-  // parts > 1: block b takes tokens 16 (b / parts) .. and part b % parts of the chunks;
-  // its down-projection sums go to part_out and k1_lora_sum adds the parts
-  const int part = (int)(blockIdx.x % (uint32_t)parts);
-  const int64_t m0 = (int64_t)(blockIdx.x / (uint32_t)parts) * 16;
+  // Blocks [0, full) each take 16 tokens over all of K; after them, parts > 1 blocks per
+  // remaining 16 tokens: block full + t takes tokens 16 (full + t / parts) .. and part
+  // t % parts of the chunks, and its down-projection sums go to part_out (rows from token
+  // 16 full on), which k1_lora_sum adds up.
+  const bool cut = blockIdx.x >= (uint32_t)full;
+  const uint32_t tb = blockIdx.x - (uint32_t)full;
+  const int np = cut ? parts : 1;
+  const int part = cut ? (int)(tb % (uint32_t)parts) : 0;
+  const int64_t m0 = cut ? ((int64_t)full + tb / (uint32_t)parts) * 16 : (int64_t)blockIdx.x * 16;
   const int64_t row = m0 + r16;
   const bool row_ok = row < M;
   const int nch = (int)(K >> 6);
-  const int cbeg = (int)(((int64_t)part * nch) / parts);
-  const int nchunks = (int)(((int64_t)(part + 1) * nch) / parts);  // end of the block's chunks
+  const int cbeg = (int)(((int64_t)part * nch) / np);
+  const int nchunks = (int)(((int64_t)(part + 1) * nch) / np);  // end of the block's chunks
   // rows past M read as zeros through the range check
   const int64_t nrows = M - m0 < 16 ? M - m0 : 16;
   const __amdgpu_buffer_rsrc_t rX = make_rsrc(X + m0 * ldx, (uint32_t)(((nrows - 1) * ldx + K) * 2));
@@ -282,8 +288,9 @@ k1_quant_lora_down(const uint16_t* __restrict__ X, int64_t ldx, int64_t M, int64
         float v = 0.f;
 #pragma unroll
         for (int w = 0; w < K1_WAVES; ++w) v += red[w][rr][cc];
-        if (parts > 1) {
-          part_out[((int64_t)part * M + m0 + rr) * R16 + cc] = v;
+        if (np > 1) {
+          const int64_t mc = (int64_t)full * 16;  // first row of the cut blocks
+          part_out[((int64_t)part * (M - mc) + (m0 - mc) + rr) * R16 + cc] = v;
         } else if constexpr (MMA) {
           store_lora_mma(reinterpret_cast<uint16_t*>(lora_act), m0 + rr, cc, NT, v);
         } else {
@@ -294,36 +301,43 @@ k1_quant_lora_down(const uint16_t* __restrict__ X, int64_t ldx, int64_t M, int64
   }
 }
 
-// The K-split form's second step: lora_act[m][j] = sum over p of part_out[p][m][j], in
-// part order (the result does not depend on which block finished first), stored like
-// the unsplit kernel's epilogue stores it.
+// The K-split form's second step, for the rows m0 .. M-1 of the cut blocks:
+// lora_act[m][j] = sum over p of part_out[p][m - m0][j], in part order (the result does not
+// depend on which block finished first), stored like the unsplit kernel's epilogue.
 template <bool MMA>
-__global__ __launch_bounds__(256) void k1_lora_sum(const float* __restrict__ part_out, int parts, int64_t M, int R16,
-                                                   float* __restrict__ lora_act) {
-  const int64_t total = M * R16;
+__global__ __launch_bounds__(256) void k1_lora_sum(const float* __restrict__ part_out, int parts, int64_t m0,
+                                                   int64_t M, int R16, float* __restrict__ lora_act) {
+  const int64_t total = (M - m0) * R16;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= total) return;
   float v = part_out[idx];
   for (int p = 1; p < parts; ++p) v += part_out[(int64_t)p * total + idx];
-  const int64_t m = idx / R16;
-  const int j = (int)(idx - m * R16);
+  const int64_t m = m0 + idx / R16;
+  const int j = (int)(idx % R16);
   if constexpr (MMA) store_lora_mma(reinterpret_cast<uint16_t*>(lora_act), m, j, R16 >> 4, v);
-  else lora_act[idx] = v;
+  else lora_act[m * R16 + j] = v;
 }
 
 template <int FMT, bool MMA>
 static hipError_t launch_k1_fmt(const KernelLayer& L, int64_t M, const uint16_t* X, int64_t ldx,
-                                uint8_t* qX, void* sX, void* lora_act, int parts, float* part_out, hipStream_t st) {
+                                uint8_t* qX, void* sX, void* lora_act, int parts, float* part_out, int full,
+                                hipStream_t st) {
   const int nt = (L.rank + 15) / 16;
+  const int64_t nb = (M + 15) / 16;
   if (parts < 1 || (nt > 0 && !part_out)) parts = 1;  // rank 0: nothing to add across parts
-  const dim3 grid((unsigned)((M + 15) / 16 * parts));
+  if (full < 0) full = 0;
+  if (parts == 1 || full >= nb) {
+    parts = 1;
+    full = (int)nb;
+  }
+  const dim3 grid((unsigned)(full + (nb - full) * parts));
   // NVFP4 level-2 scale of the activations and fp32(1 / fp32(6 S_X))
   const float tsx = L.tscale_x, r6x = FMT == 2 ? 1.0f / (6.0f * L.tscale_x) : 0.0f;
 #define K1_CASE(NTV)                                                                            \
   case NTV:                                                                                     \
     hipLaunchKernelGGL((k1_quant_lora_down<FMT, NTV, MMA>), grid, dim3(64 * K1_WAVES), 0, st, X, ldx, M, L.K, \
                        L.inv_s, L.L1f, L.rank, qX, sX, static_cast<float*>(lora_act), tsx, r6x, parts,    \
-                       part_out);                                                                          \
+                       part_out, full);                                                                    \
     break;
   switch (nt) {
     K1_CASE(0) K1_CASE(1) K1_CASE(2) K1_CASE(3) K1_CASE(4)
@@ -332,9 +346,9 @@ static hipError_t launch_k1_fmt(const KernelLayer& L, int64_t M, const uint16_t*
   }
 #undef K1_CASE
   if (parts > 1 && nt > 0) {
-    const int64_t total = M * nt * 16;
+    const int64_t m0 = (int64_t)full * 16, total = (M - m0) * nt * 16;
     hipLaunchKernelGGL((k1_lora_sum<MMA>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, part_out, parts,
-                       M, nt * 16, static_cast<float*>(lora_act));
+                       m0, M, nt * 16, static_cast<float*>(lora_act));
   }
   return hipGetLastError();
 }
@@ -346,7 +360,7 @@ hipError_t launch_k1_down(const KernelLayer& L, int64_t M, const uint16_t* X, in
   case NTV:                                                                                                    \
     hipLaunchKernelGGL((k1_quant_lora_down<0, NTV, true, false>), grid, dim3(64 * K1_WAVES), 0, st, X, ldx, M, L.K, L.inv_s, \
                        L.L1f, L.rank, (uint8_t*)nullptr, (void*)nullptr, static_cast<float*>(lora_act), 1.0f, 0.0f, 1, \
-                       (float*)nullptr);                                                                            \
+                       (float*)nullptr, (int)((M + 15) / 16));                                                      \
     break;
   switch ((L.rank + 15) / 16) {
     K1D_CASE(1) K1D_CASE(2) K1D_CASE(3) K1D_CASE(4) K1D_CASE(5) K1D_CASE(6) K1D_CASE(7) K1D_CASE(8)
@@ -357,30 +371,44 @@ hipError_t launch_k1_down(const KernelLayer& L, int64_t M, const uint16_t* X, in
 }
 
 hipError_t launch_k1(const KernelLayer& L, int64_t M, const uint16_t* X, int64_t ldx, uint8_t* qX,
-                     void* sX, void* lora_act, bool mma, hipStream_t st, int parts, float* part_out) {
+                     void* sX, void* lora_act, bool mma, hipStream_t st, int parts, float* part_out, int full) {
   if (L.fmt == 0)
-    return mma ? launch_k1_fmt<0, true>(L, M, X, ldx, qX, sX, lora_act, parts, part_out, st)
-               : launch_k1_fmt<0, false>(L, M, X, ldx, qX, sX, lora_act, parts, part_out, st);
+    return mma ? launch_k1_fmt<0, true>(L, M, X, ldx, qX, sX, lora_act, parts, part_out, full, st)
+               : launch_k1_fmt<0, false>(L, M, X, ldx, qX, sX, lora_act, parts, part_out, full, st);
   if (L.fmt == 2)
-    return mma ? launch_k1_fmt<2, true>(L, M, X, ldx, qX, sX, lora_act, parts, part_out, st)
-               : launch_k1_fmt<2, false>(L, M, X, ldx, qX, sX, lora_act, parts, part_out, st);
-  return mma ? launch_k1_fmt<1, true>(L, M, X, ldx, qX, sX, lora_act, parts, part_out, st)
-             : launch_k1_fmt<1, false>(L, M, X, ldx, qX, sX, lora_act, parts, part_out, st);
+    return mma ? launch_k1_fmt<2, true>(L, M, X, ldx, qX, sX, lora_act, parts, part_out, full, st)
+               : launch_k1_fmt<2, false>(L, M, X, ldx, qX, sX, lora_act, parts, part_out, full, st);
+  return mma ? launch_k1_fmt<1, true>(L, M, X, ldx, qX, sX, lora_act, parts, part_out, full, st)
+             : launch_k1_fmt<1, false>(L, M, X, ldx, qX, sX, lora_act, parts, part_out, full, st);
 }
 
-int k1_parts(const KernelLayer& L, int64_t M) {
-  // Long K only: there each block of 16 tokens walks many chunks, and the blocks past one
-  // per CU double the time of the CUs that hold them; cut into 4 parts, every CU holds
-  // about the same number of part blocks.  At short K the fixed cost of the extra launch
-  // and the partial sums outweighs that.  (At rank 0 there is nothing to add across the
-  // parts.)
-  if (L.K < 8192) return 1;
+K1Cut k1_cut(const KernelLayer& L, int64_t M) {
+  // Long K: every block of 16 tokens walks many chunks, and the blocks past one per CU
+  // double the time of the CUs that hold them; cut into 4 parts, every CU holds about the
+  // same number of part blocks.  Short K with a last, partly filled round of one block per
+  // CU (the FLUX.1 layers' 4608 tokens: 288 blocks on 256 CUs): the blocks of the full
+  // rounds stay whole and only the last round's blocks are cut, into as many parts (at
+  // most 8, at least one chunk each) as fit one part block per CU beside the others.  Otherwise the fixed cost of
+  // the second step outweighs the balance.  (At rank 0 there is nothing to add across
+  // the parts.)
+  const int64_t nb = (M + 15) / 16;
+  K1Cut c{(int)nb, 1};
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
                                                hipSuccess || cus < 1)
-    return 1;
-  if ((M + 15) / 16 > 2 * (int64_t)cus) return 1;
-  return 4;
+    return c;
+  if (L.K >= 8192) {
+    if (nb <= 2 * (int64_t)cus) c = K1Cut{0, 4};
+    return c;
+  }
+  const int64_t rem = nb % cus;
+  if (nb < cus || rem == 0 || 2 * rem > cus) return c;
+  int p = (int)(cus / rem) < 8 ? (int)(cus / rem) : 8;
+  if (p > L.K / 64) p = (int)(L.K / 64);  // at least one chunk per range
+  if (p < 2) return c;
+  return K1Cut{(int)(nb - rem), p};
 }
+
+int k1_parts(const KernelLayer& L, int64_t M) { return k1_cut(L, M).parts; }
 
 }  // namespace svdq

@@ -20,14 +20,21 @@ struct KernelLayer {
 // mma: the activation side in the matrix-core operand form (INT4 FP6 operand words,
 // fp16 scales; lora_act as bf16 hi/lo pairs in fragment order) instead of the packed
 // storage form (4-bit codes [M][K/2], fp16 / E8M0 scales, fp32 lora_act).
-// parts > 1 (with part_out, device, parts * M * R16 fp32, R16 = rank rounded up to 16;
-// not needed at rank 0): the chunks along K are cut into `parts` ranges, one block per
-// range and 16 tokens, whose fp32 down-projection sums are added in part order by a second
+// parts > 1 (with part_out, device, parts * (M - 16 full) * R16 fp32, R16 = rank rounded
+// up to 16; not needed at rank 0): the first `full` blocks of 16 tokens run over all of K,
+// and the chunks along K of every later block of 16 tokens are cut into `parts` ranges,
+// one block per range, whose fp32 down-projection sums are added in part order by a second
 // kernel (codes and scales are the same as unsplit; lora_act differs only in the order of
 // its fp32 additions).
 hipError_t launch_k1(const KernelLayer& L, int64_t M, const uint16_t* X, int64_t ldx, uint8_t* qX,
-                     void* sX, void* lora_act, bool mma, hipStream_t st, int parts = 1, float* part_out = nullptr);
-// The number of parts the forward uses for kernel 1 (1: unsplit).
+                     void* sX, void* lora_act, bool mma, hipStream_t st, int parts = 1, float* part_out = nullptr,
+                     int full = 0);
+// How the forward cuts kernel 1: blocks [0, full) whole, the rest in `parts` K ranges each
+// (parts == 1: one pass).
+struct K1Cut {
+  int full, parts;
+};
+K1Cut k1_cut(const KernelLayer& L, int64_t M);
 int k1_parts(const KernelLayer& L, int64_t M);
 
 // The unfused baseline's two low-rank passes: lora_act = X_hat L1 alone (a second read

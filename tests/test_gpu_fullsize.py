@@ -118,10 +118,10 @@ def test_full_size_layer(name):
                                       wl.fmt, K, r, M=M)
         np.testing.assert_array_equal(c_m, qX_ref)
         np.testing.assert_array_equal(s_m, sX_ref)
-    split_k1 = wl.total_rank > 0 and K >= 8192 and \
-        (M + 15) // 16 <= 2 * torch.cuda.get_device_properties(0).multi_processor_count
+    split_k1 = wl.total_rank > 0 and lay.forward_k1_parts(M) > 1
     if split_k1:
-        # the forward cut kernel 1 along K: its fp32 down-projection sums came in another
+        # the forward cut kernel 1 along K (all blocks at K >= 8192; the blocks of a last,
+        # partly filled round at 4608 tokens): its fp32 down-projection sums came in another
         # order than the one-pass packed call's, so hi + lo is held to the error budget
         v = (hi.astype(np.uint32) << 16).view(np.float32).astype(np.float64) + \
             (lo.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
