@@ -13,7 +13,7 @@
 // and L1 loads issued before the current chunk is processed.  (The chunks of a block can
 // also be cut into a few contiguous ranges, one block each, with the down-projection
 // sums of the ranges added by a second small kernel: every block at long K, and at
-// short K only the blocks of a last, partly filled round of one block per CU.)  Inside a chunk, lane l holds
+// short K and rank 0 only the blocks of a last, partly filled round of one block per CU.)  Inside a chunk, lane l holds
 // token (l & 15) and the 16 consecutive channels 16 * (l >> 4) .. +15.  One INT4 group
 // (64) is therefore spread over the 4 lanes l, l^16, l^32, l^48; one MXFP4 group (32)
 // over lanes l, l^16; an NVFP4 group (16) is one lane's 16 values.  X is loaded row-contiguously instead (each 16-byte load covers 8
@@ -310,8 +310,14 @@ __global__ __launch_bounds__(256) void k1_lora_sum(const float* __restrict__ par
   const int64_t total = (M - m0) * R16;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= total) return;
-  float v = part_out[idx];
-  for (int p = 1; p < parts; ++p) v += part_out[(int64_t)p * total + idx];
+  // all parts' loads issued together (parts <= 8), then added in part order
+  float w[8];
+#pragma unroll
+  for (int p = 0; p < 8; ++p) w[p] = p < parts ? part_out[(int64_t)p * total + idx] : 0.0f;
+  float v = w[0];
+#pragma unroll
+  for (int p = 1; p < 8; ++p)
+    if (p < parts) v += w[p];
   const int64_t m = m0 + idx / R16;
   const int j = (int)(idx % R16);
   if constexpr (MMA) store_lora_mma(reinterpret_cast<uint16_t*>(lora_act), m, j, R16 >> 4, v);
@@ -324,6 +330,7 @@ static hipError_t launch_k1_fmt(const KernelLayer& L, int64_t M, const uint16_t*
                                 hipStream_t st) {
   const int nt = (L.rank + 15) / 16;
   const int64_t nb = (M + 15) / 16;
+  if (parts > 8) return hipErrorInvalidValue;  // k1_lora_sum adds at most 8 ranges
   if (parts < 1 || (nt > 0 && !part_out)) parts = 1;  // rank 0: nothing to add across parts
   if (full < 0) full = 0;
   if (parts == 1 || full >= nb) {
@@ -385,12 +392,12 @@ hipError_t launch_k1(const KernelLayer& L, int64_t M, const uint16_t* X, int64_t
 K1Cut k1_cut(const KernelLayer& L, int64_t M) {
   // Long K: every block of 16 tokens walks many chunks, and the blocks past one per CU
   // double the time of the CUs that hold them; cut into 4 parts, every CU holds about the
-  // same number of part blocks.  Short K with a last, partly filled round of one block per
-  // CU (the FLUX.1 layers' 4608 tokens: 288 blocks on 256 CUs): the blocks of the full
-  // rounds stay whole and only the last round's blocks are cut, into as many parts (at
-  // most 8, at least one chunk each) as fit one part block per CU beside the others.  Otherwise the fixed cost of
-  // the second step outweighs the balance.  (At rank 0 there is nothing to add across
-  // the parts.)
+  // same number of part blocks.  Short K at rank 0 (no sums to add across the parts) with
+  // a last, partly filled round of one block per CU (the FLUX.1 layers' 4608 tokens: 288
+  // blocks on 256 CUs): the blocks of the full rounds stay whole and only the last
+  // round's blocks are cut, into as many parts (at most 8, at least one chunk each) as fit
+  // one part block per CU beside the others.  At short K and rank > 0 the second step
+  // (~5 us) costs as much as the balance gains, so kernel 1 runs in one pass.
   const int64_t nb = (M + 15) / 16;
   K1Cut c{(int)nb, 1};
   int dev = 0, cus = 0;
@@ -402,7 +409,7 @@ K1Cut k1_cut(const KernelLayer& L, int64_t M) {
     return c;
   }
   const int64_t rem = nb % cus;
-  if (nb < cus || rem == 0 || 2 * rem > cus) return c;
+  if (L.rank > 0 || nb < cus || rem == 0 || 2 * rem > cus) return c;
   int p = (int)(cus / rem) < 8 ? (int)(cus / rem) : 8;
   if (p > L.K / 64) p = (int)(L.K / 64);  // at least one chunk per range
   if (p < 2) return c;

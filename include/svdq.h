@@ -295,10 +295,10 @@ size_t svdq_workspace_bytes(const svdq_layer* layer, int64_t M);
 /* The number of contiguous K ranges svdq_linear_forward cuts kernel 1's blocks of 16
  * tokens into for M rows on the current device (1: one pass), for callers that time or
  * reproduce the forward's launches.  At K >= 8192 with ceil(M / 16) <= 2 x CUs every block
- * is cut, into 4; at shorter K, when the blocks leave a last round of one block per CU at
- * most half full, only that round's blocks are cut, into min(8, CUs / blocks in it)
- * ranges (the FLUX.1 layers' 4608 tokens on 256 CUs: 32 blocks, 8 ranges).  Returns 0
- * for a NULL layer, bad dimensions or M < 0. */
+ * is cut, into 4; at shorter K and rank 0, when the blocks leave a last round of one block
+ * per CU at most half full, only that round's blocks are cut, into min(8, CUs / blocks in
+ * it, K / 64) ranges (the FLUX.1 layers' 4608 tokens on 256 CUs: 32 blocks, 8 ranges).
+ * Returns 0 for a NULL layer, bad dimensions or M < 0. */
 int32_t svdq_forward_k1_parts(const svdq_layer* layer, int64_t M);
 
 /* The public layer Y = Q(X diag(s)^-1) Q(R) + (X diag(s)^-1 L1) L2 (decomposition
